@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the wave-tick hot path on one MI355X.
+
+One step = one steady-state tick of the streaming rollout at the Wan-1.3B-like
+4-step shape (S = 4: five 4680-token chunks incl. the store, 12 heads x 128,
+bf16, 3 clean history chunks in 64-token pages of a 4096-page pool):
+  page-table alloc of the store chunk's pages (host) -> page ids to the device
+  -> wf_store_paged (store K/V into its pages) -> history table to the device
+  -> wf_attn_tick (all five query chunks, one launch) -> commit (promote the
+  store chunk, evict the oldest history chunk, host).
+Inputs are resident in HBM before the timed region (seeded device RNG).
+
+Prints one JSON line. `value` = useful TFLOP/s of the whole step (mask-true
+query-key pairs x 4*D flops x H); `roofline` = the attention kernel alone,
+timed with HIP events on its launch stream; `cpu_baseline` = the fp64 CPU
+oracle on a bounded sample of the same tick.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="wan13_4step",
+                    choices=["wan13_4step", "wan13_5step", "wan14b_4step"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+                    help="approximate CPU seconds for the oracle sample")
+    ap.add_argument("--rotate", type=int, default=4, help="distinct live-input sets cycled")
+    return ap.parse_args()
+
+
+class Rollout:
+    """Device state of a steady-state rollout: pools, page table, live inputs."""
+
+    def __init__(self, cfg, rotate: int, dev):
+        import torch
+
+        from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+        self.torch, self.wf, self.cfg, self.dev = torch, wfattn, cfg, dev
+        S, T, H, D, P = cfg.S, cfg.T, cfg.H, cfg.D, cfg.P
+        self.order = inputs.initial_free_order(cfg)
+        self.pt = wfattn.PageTable(cfg.num_pages, P, T, cfg.n_hist,
+                                   initial_free_order=self.order)
+        self.k_pool = torch.zeros((cfg.num_pages, P, H, D), dtype=torch.bfloat16, device=dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.ppc = self.pt.ppc
+        # ring of pinned host slots for the per-step page-id uploads
+        self.nslot = 8
+        self.ids_host = torch.empty((self.nslot, self.ppc), dtype=torch.int32, pin_memory=True)
+        self.hist_host = torch.empty((self.nslot, cfg.n_hist * self.ppc), dtype=torch.int32,
+                                     pin_memory=True)
+        self.ids_dev = torch.empty((self.nslot, self.ppc), dtype=torch.int32, device=dev)
+        self.hist_dev = torch.empty((self.nslot, cfg.n_hist, self.ppc), dtype=torch.int32,
+                                    device=dev)
+        self.slot_ev = [None] * self.nslot
+        self.step_i = 0
+        # history: n_hist clean chunks written through the store path
+        for c in range(cfg.n_hist):
+            hk, hv, _ = inputs.draw_live_torch(cfg, 2000 + c, dev)
+            ids = torch.from_numpy(self.pt.alloc_chunk()).to(dev)
+            wfattn.wf_store_paged(hk[0], hv[0], self.k_pool, self.v_pool, ids)
+            self.pt.commit()
+        self.live = [inputs.draw_live_torch(cfg, inputs.rollout_seed(i), dev)
+                     for i in range(rotate)]
+        self.o = torch.empty_like(self.live[0][0])
+        self.scale = 1.0 / float(np.sqrt(D))
+        self.mask = (1 << (S + 1)) - 1
+        torch.cuda.synchronize()
+
+    def step(self, attn_events=None):
+        torch, wf, cfg = self.torch, self.wf, self.cfg
+        slot = self.step_i % self.nslot
+        if self.slot_ev[slot] is not None:
+            self.slot_ev[slot].synchronize()
+        q, k, v = self.live[self.step_i % len(self.live)]
+        self.step_i += 1
+        S = cfg.S
+        ids = self.pt.alloc_chunk()
+        self.ids_host[slot].numpy()[:] = ids
+        self.ids_dev[slot].copy_(self.ids_host[slot], non_blocking=True)
+        wf.wf_store_paged(k[S], v[S], self.k_pool, self.v_pool, self.ids_dev[slot])
+        hist = self.pt.export()
+        self.hist_host[slot].numpy()[:] = hist.reshape(-1)
+        self.hist_dev[slot].view(-1).copy_(self.hist_host[slot], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.slot_ev[slot] = ev
+        if attn_events is not None:
+            attn_events[0].record()
+        wf.wf_attn_tick(q, k, v, self.o, S, self.mask, self.scale, self.k_pool, self.v_pool,
+                        self.hist_dev[slot])
+        if attn_events is not None:
+            attn_events[1].record()
+        self.pt.commit()
+
+
+def cpu_baseline(cfg, budget_s: float) -> dict:
+    """fp64 oracle on a bounded sample of one steady tick: all stages, heads
+    0..n-1, every query row; n grows while the budget allows."""
+    import oracle
+    from wavefront_causal_attention_wf_amd import inputs
+
+    cores = len(os.sched_getaffinity(0))
+    x = inputs.draw_tick(cfg)
+    model = oracle.FifoPageModel(cfg.num_pages, cfg.P, cfg.T, cfg.n_hist,
+                                 initial_free_order=inputs.initial_free_order(cfg))
+    store = oracle.PageStore(cfg.P, cfg.H, cfg.D)
+    for c in range(cfg.n_hist):
+        store.write_chunk(model.alloc_chunk(), x.hist_k_bits[c], x.hist_v_bits[c])
+        model.commit()
+    hist = model.export()
+    mask = (1 << (cfg.S + 1)) - 1
+    per_head = oracle.useful_flops(cfg.S, mask, cfg.n_hist, cfg.T, 1, cfg.D)
+    done_flops, spent, heads = 0, 0.0, 0
+    while heads < cfg.H:
+        t0 = time.perf_counter()
+        oracle.attention_tick_paged(x.q_bits, x.k_bits, x.v_bits, store, hist, cfg.S, mask,
+                                    1.0 / np.sqrt(cfg.D), heads=[heads])
+        dt = time.perf_counter() - t0
+        spent += dt
+        done_flops += per_head
+        heads += 1
+        log(f"oracle head {heads - 1}: {dt:.1f} s")
+        if spent + dt > budget_s:
+            break
+    return {"value": done_flops / spent / 1e12, "unit": "TFLOP/s (useful)", "cores": cores,
+            "kind": "oracle",
+            "sample": f"one full tick of {cfg.name} (all {cfg.S + 1} query chunks, all "
+                      f"{cfg.T} rows) restricted to heads 0..{heads - 1} of {cfg.H}; "
+                      f"{done_flops / 1e9:.1f} GFLOP useful in {spent:.1f} s, numpy float64, "
+                      f"heads run one at a time (BLAS threads = {cores})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the sharding design is described in DESIGN.md)"}))
+        sys.exit(2)
+    import torch
+
+    from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+    cfg = inputs.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"config {cfg.name}: S={cfg.S} T={cfg.T} H={cfg.H} D={cfg.D} P={cfg.P} "
+        f"n_hist={cfg.n_hist} pool={cfg.num_pages}")
+    ro = Rollout(cfg, args.rotate, dev)
+    mask = (1 << (cfg.S + 1)) - 1
+    flops = wfattn.wf_tick_useful_flops(cfg.S, mask, cfg.T, cfg.H, cfg.D, cfg.n_hist, P=cfg.P,
+                                        num_pages=cfg.num_pages)
+    for _ in range(args.warmup):
+        ro.step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        ro.step(ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}); "
+        f"attn kernel mean {attn_ms.mean():.3f} ms p10 {np.percentile(attn_ms, 10):.3f} "
+        f"p90 {np.percentile(attn_ms, 90):.3f}")
+
+    value = flops * args.steps / (total_ms * 1e-3) / 1e12
+    achieved = flops / (attn_ms.mean() * 1e-3) / 1e12
+    out = {
+        "metric": "wave-attn TFLOP/s (useful) + ticks/s, % bf16 MFMA peak, 1xMI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 0.5^2) bf16 Q/K/V, seeded page permutation)",
+        "config": {"workload": f"{cfg.name}: one steady wave tick, S={cfg.S} (width "
+                               f"{cfg.S + 1} incl. store), T={cfg.T}, H={cfg.H}, D={cfg.D}, "
+                               f"{cfg.n_hist} history chunks in P={cfg.P} pages of a "
+                               f"{cfg.num_pages}-page pool",
+                   "global_batch": 1, "seq_len": cfg.T * (cfg.S + 1), "parallelism": "none"},
+        "ticks_per_s": round(1e3 / ms_step, 2),
+        "useful_tflop_per_tick": round(flops / 1e12, 4),
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "wf_attn_tick",
+                     "kernel_ms_mean": round(float(attn_ms.mean()), 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * wf_attn.h — C ABI of libwfattn.so: one wave tick of chunk-wise causal
+ * wavefront attention on an AMD Instinct MI355X (gfx950).
+ *
+ * Citations name pages of "Wave Forcing: Towards Speed-of-Light Streaming Video
+ * Generation": [summary] = the structured summary page (picx.dev);
+ * [full text] = the full-text page (paperpeel.com).
+ *
+ * The method ([summary] Methodology 1, [full text] Eq. (4), Eq. (5), Appendix
+ * B.3): at tick k the S denoising stages hold chunks Z_k^(0) .. Z_{k-S+1}^(S-1)
+ * and the store holds B_{k-S} as stage S. Every chunk's queries attend, in one
+ * softmax, to: clean history chunks (anchor first, oldest first), the live store,
+ * then the live chunks at stages j >= s (itself first). Chunks at noisier stages
+ * j < s are never read. The store's K/V is written straight into history pages
+ * and becomes history after the tick ([full text] §4.2, Appendix B.3, Eq. (13)).
+ *
+ * Conventions shared by every call:
+ *  - Tensors are bf16 (bit pattern uint16), C-contiguous, head-interleaved:
+ *      live q/k/v/o  [S+1][T][H][D]       chunk slot s = stage s, slot S = store
+ *      K pool, V pool [num_pages][P][H][D] one page = P consecutive tokens of one
+ *                                          chunk, all heads; page bytes contiguous
+ *      page tables    int32, device memory
+ *  - The caller owns all device memory and the stream; the library allocates no
+ *    device memory and keeps no pointer after a call returns. Device calls are
+ *    stream-ordered and asynchronous: a WF_OK return means "validated and
+ *    enqueued".
+ *  - Every argument is validated on the host before anything is launched. On any
+ *    error nothing is launched, no output and no page-table state changes, and
+ *    wf_last_error() describes the problem. C++ exceptions never cross the ABI.
+ *  - Page ids inside device page tables are trusted for speed; with the
+ *    environment variable WF_CHECK_PAGES=1 the library copies them to the host
+ *    (synchronising the stream) and range-checks them first.
+ */
+#ifndef WF_ATTN_H_
+#define WF_ATTN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t wf_status;
+#define WF_OK 0
+#define WF_EINVAL (-1)       /* bad shape, pointer, alignment, mask or index      */
+#define WF_ENOMEM (-2)       /* page pool exhausted                              */
+#define WF_EHIP (-3)         /* a HIP runtime call or kernel launch failed        */
+#define WF_EUNSUPPORTED (-4) /* valid but outside what the kernels implement      */
+#define WF_ESTATE (-5)       /* call out of order (commit without alloc, ...)     */
+
+#define WF_MAX_STAGES 8      /* S + 1 <= 8 chunk slots per tick                   */
+#define WF_MAX_SEGMENTS 32   /* history chunks + live chunks one query may see    */
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* wf_last_error(void);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t wf_abi_version(void);
+#define WF_ABI_VERSION 1
+
+/* ------------------------------------------------------------------------ */
+/* Page table: host-only state for one request's attention pages.            */
+/* [full text] Appendix B.3 (promotion of the live store page, persistent     */
+/* anchor), Appendix B.8 / Eq. (13) (fixed-capacity K/V arrays, bounded       */
+/* history). Policy (the pages give none): FIFO free list — allocation pops   */
+/* ceil(T/P) ids from the front, an evicted chunk's ids are appended to the   */
+/* back in page order. Eviction removes the oldest history chunk, or the      */
+/* oldest after the anchor when pin_anchor != 0. One handle must not be used  */
+/* from two threads at once.                                                  */
+/* ------------------------------------------------------------------------ */
+typedef struct wf_page_table wf_page_table;
+
+/* num_pages, page_size (P), chunk_tokens (T), window_chunks (history capacity,
+ * >= 2 when pin_anchor) must be positive. initial_free_order: host array of
+ * num_pages distinct ids in [0, num_pages), or NULL for 0..num_pages-1.
+ * *out receives a new handle (freed with wf_page_table_destroy). */
+wf_status wf_page_table_create(int32_t num_pages, int32_t page_size, int32_t chunk_tokens,
+                               int32_t window_chunks, int32_t pin_anchor,
+                               const int32_t* initial_free_order, wf_page_table** out);
+void wf_page_table_destroy(wf_page_table* pt);
+
+/* Pages per chunk, ceil(T/P). */
+wf_status wf_page_table_pages_per_chunk(const wf_page_table* pt, int32_t* out);
+
+/* Allocate the pages of the store chunk about to be written (the live store U).
+ * out_ids: host int32[capacity], capacity >= pages per chunk. WF_ENOMEM when the
+ * free list is short, WF_ESTATE when a live chunk is already allocated. */
+wf_status wf_page_table_alloc_chunk(wf_page_table* pt, int32_t* out_ids, int32_t capacity);
+
+/* Promote the live chunk to history; if history then exceeds the window, evict
+ * one chunk and return its ids to the free list. evicted_ids (host, may be NULL
+ * when capacity is 0) receives the evicted ids, *n_evicted their count (0 or
+ * pages per chunk). WF_ESTATE without a live chunk. */
+wf_status wf_page_table_commit(wf_page_table* pt, int32_t* evicted_ids, int32_t capacity,
+                               int32_t* n_evicted);
+
+/* History page lists, oldest chunk first: out = host int32[n_hist][ppc]
+ * (capacity in int32 elements). *n_hist_chunks receives the chunk count. This
+ * is the table wf_attn_tick reads once the caller has copied it to the device. */
+wf_status wf_page_table_export(const wf_page_table* pt, int32_t* out, int32_t capacity,
+                               int32_t* n_hist_chunks);
+
+wf_status wf_page_table_num_free(const wf_page_table* pt, int32_t* out);
+
+/* ------------------------------------------------------------------------ */
+/* wf_store_paged — write the store chunk's K and V into its pages.          */
+/* [full text] §4.2 and Appendix B.3: K/V goes directly into its final        */
+/* attention slots. Token t -> slot t % P of page page_ids[t / P]; slots past */
+/* token T-1 in the last page are written as zero. Bit-exact copy.            */
+/* k_src, v_src: device bf16 [T][H][D]; k_pool, v_pool: device bf16           */
+/* [num_pages][P][H][D]; page_ids: device int32 [ceil(T/P)], each in          */
+/* [0, num_pages). All pointers 16-byte aligned; H*D*2 a multiple of 16 bytes. */
+/* ------------------------------------------------------------------------ */
+wf_status wf_store_paged(const void* k_src, const void* v_src, void* k_pool, void* v_pool,
+                         const int32_t* page_ids, int32_t T, int32_t H, int32_t D,
+                         int32_t num_pages, int32_t P, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* wf_gather_paged — diagnostic inverse of the store: copy n_chunks chunks    */
+/* from pool pages into contiguous k_dst, v_dst bf16 [n_chunks][T][H][D].     */
+/* page_ids: device int32 [n_chunks][ceil(T/P)]. Same alignment rules.        */
+/* ------------------------------------------------------------------------ */
+wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t* page_ids,
+                          int32_t n_chunks, void* k_dst, void* v_dst, int32_t T, int32_t H,
+                          int32_t D, int32_t num_pages, int32_t P, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* wf_attn_tick — all S+1 query chunks of one tick in a single launch.        */
+/* For each active stage s and head h:                                        */
+/*   O_s = softmax(scale * Q_s K_ctx(s)^T) V_ctx(s), where ctx(s) is, in the  */
+/*   Eq. (5) order: history chunks c = hist_first[s] .. n_hist-1 (read through */
+/*   hist_pages), the live store (slot S) if active, then live chunks         */
+/*   j = s .. S-1 that are active. For s = S the live part is the store only.  */
+/* Mask [summary] / [full text] Eq. (4): M_WF(s, j) = 1[j >= s]. Chunks with   */
+/* j < s are never enumerated (block skip), so their K/V is never read.        */
+/* Arithmetic: bf16 MFMA products, fp32 accumulation and softmax state, P     */
+/* rounded to bf16 for the P.V product, bf16 output (round to nearest even).  */
+/* ------------------------------------------------------------------------ */
+typedef struct wf_tick_desc {
+  int32_t S;              /* denoising stages, 0..7; slot S is the store           */
+  uint32_t active_mask;   /* bit s set = slot s occupied; bits above S must be 0    */
+  int32_t T, H, D;        /* tokens per chunk (>= 0), heads (>= 1), head dim 64|128 */
+  float scale;            /* softmax scale (> 0, finite), e.g. 1/sqrt(D)            */
+  const void* q;          /* device bf16 [S+1][T][H][D]                             */
+  const void* k;          /* device bf16 [S+1][T][H][D]                             */
+  const void* v;          /* device bf16 [S+1][T][H][D]                             */
+  void* o;                /* device bf16 [S+1][T][H][D]; rows of inactive slots are */
+                          /* left untouched                                          */
+  const void* k_pool;     /* device bf16 [num_pages][P][H][D] (NULL iff n_hist = 0) */
+  const void* v_pool;     /* device bf16 [num_pages][P][H][D] (NULL iff n_hist = 0) */
+  int32_t num_pages, P;   /* pool size in pages; tokens per page (multiple of 16)   */
+  const int32_t* hist_pages; /* device int32 [n_hist][ceil(T/P)], oldest first      */
+  int32_t n_hist;         /* clean history chunks, n_hist + S + 1 <= 32            */
+  int32_t hist_first[WF_MAX_STAGES]; /* per slot: first visible history chunk,     */
+                          /* 0 = all, n_hist = none (per-rank history budgets)      */
+} wf_tick_desc;
+
+wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);
+
+/* Useful FLOPs of one call with this descriptor: 4*D*H per visible
+ * (query, key) pair (Q.K^T plus P.V), exponentials not counted. Host only. */
+wf_status wf_tick_useful_flops(const wf_tick_desc* desc, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WF_ATTN_H_ */

@@ -182,20 +182,18 @@ def attention_tick(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     heads = list(range(H)) if heads is None else list(heads)
     rows = np.arange(T) if rows is None else np.asarray(rows)
 
-    qf, kf, vf = as_f64(q), as_f64(k), as_f64(v)
-    hkf, hvf = as_f64(hist_k), as_f64(hist_v)
-    D = qf.shape[3]
+    D = q.shape[3]
     masks = {s: token_mask(s, S, active_mask, n_hist, T, _hf(hist_first, s)) for s in stages}
     out = {s: np.zeros((len(rows), len(heads), D), dtype=np.float64) for s in stages}
 
     def one_head(hi: int) -> None:
         h = heads[hi]
-        K = _key_matrix(kf, hkf, h, S)
-        V = _key_matrix(vf, hvf, h, S)
+        K = as_f64(_key_matrix(k, hist_k, h, S))
+        V = as_f64(_key_matrix(v, hist_v, h, S))
         for s in stages:
             for r0 in range(0, len(rows), row_group):
                 rr = rows[r0:r0 + row_group]
-                Q = qf[s, rr, h, :]
+                Q = as_f64(q[s, rr, h, :])
                 sc = (Q @ K.T) * scale
                 mask2d = np.tile(masks[s], (len(rr), 1))      # materialised mask
                 sc = np.where(mask2d, sc, -np.inf)

@@ -1,0 +1,494 @@
+// wf_attn_tick: every query chunk of one wave tick in a single launch.
+//
+// "Wave Forcing: Towards Speed-of-Light Streaming Video Generation":
+//   summary page, Methodology 1 — tick sets F_k, W_k (store = stage S) and the
+//     ordered context C_{k,s} = anchor + history + live store + live j >= s;
+//   full text Eq. (4) — wave mask M_WF(s, j) = 1[j >= s];
+//   full text Eq. (5), Appendix B.3 — context order and store visibility
+//     (history + itself);
+//   summary page, Methodology 3 — rank s reads N_s = N_prefix + (S - s) N_C
+//     keys, so stage 0 is the heaviest.
+//
+// Design (gfx950, wave64, MFMA):
+//  * One workgroup = 4 waves = 128 query rows of one (stage, head); each wave
+//    owns 32 query rows. The context of the stage is a virtual key sequence
+//    (history chunks through the page table, live store, live j >= s) cut into
+//    64-key tiles that may straddle chunk boundaries; noisier chunks j < s are
+//    simply not in the sequence (block-sparse skip), so only the very last tile
+//    can be partial.
+//  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: the query is the
+//    MFMA column, so each lane holds one query row's scores and output and the
+//    softmax needs only one cross-lane exchange (lane l <-> l+32) per tile.
+//    K rows are fed to the MFMA in a bit-2/bit-3-swapped order so that the score
+//    registers already are the P operand of the P.V product (no shuffles).
+//  * K tile [64 keys][D] and V^T tile [D][64 keys] in LDS, XOR-swizzled so the
+//    16-byte MFMA operand reads are bank-conflict free; V is transposed in
+//    registers (v_perm_b32) on its way to LDS. Global loads of tile i+1 are in
+//    flight while tile i is computed (double-buffered LDS, one barrier a tile).
+//  * Online softmax in the exp2 domain (log2 e folded into the scale), fp32
+//    state; the running max is only raised when a tile exceeds it by more than
+//    8 (in log2 units), so the O rescale is rare (exact: numerator and
+//    denominator share the same reference).
+//  * Workgroups are ordered heavy stage first (stage 0 has the most keys).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "wf_internal.h"
+
+namespace wf {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int KT = 64;              // keys per tile
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int QROWS = 32 * NWAVES;  // query rows per workgroup
+constexpr float kLazyTau = 8.0f;    // raise the running max only beyond this (log2 units)
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* hist_pages;
+  int32_t T, H, P, ppc;
+  uint32_t p_magic;       // floor(2^32 / P) + 1: t / P == umulhi(t, p_magic) for t*P < 2^32
+  float c;                // scale * log2(e)
+  int32_t ntq;            // query tiles per chunk
+  int32_t items_per_stage;  // H * ntq
+  int8_t stage_of_rank[WF_MAX_STAGES];  // work order, heaviest stage first
+  int8_t nseg[WF_MAX_STAGES];
+  // per stage: segment code >= 0 is live slot j, < 0 is history chunk (-code - 1)
+  int8_t seg[WF_MAX_STAGES][WF_MAX_SEGMENTS];
+};
+
+__device__ __forceinline__ int swap_bits23(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+// XOR swizzle of the 16-byte column of K row `row` (values 0..7).
+__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+
+// Address of row t of segment `code` for head h (K or V, selected by the bases).
+__device__ __forceinline__ const uint16_t* row_ptr(const AttnParams& p, const uint16_t* live,
+                                                   const uint16_t* pool, int code, int t, int h,
+                                                   int D) {
+  if (code >= 0) return live + ((int64_t(code) * p.T + t) * p.H + h) * D;
+  const int c = -code - 1;
+  const uint32_t pg = __umulhi(uint32_t(t), p.p_magic);
+  const int slot = t - int(pg) * p.P;
+  const int64_t page = p.hist_pages[int64_t(c) * p.ppc + pg];
+  return pool + ((page * p.P + slot) * p.H + h) * D;
+}
+
+template <int D>
+struct TileLoader {
+  static constexpr int DC = D / 8;                       // 16-byte chunks per row
+  static constexpr int NK = KT * DC / NTHREADS;          // K chunks per thread
+  static constexpr int NV = KT * DC / NTHREADS;          // V keys per thread
+  static constexpr int KROW_STEP = NTHREADS / DC;
+  static constexpr int VKG = KT / NV;                    // key groups
+
+  uint4 kreg[NK];
+  uint4 vreg[NV];
+
+  // Locate key `r` of the tile that starts at (seg0, t0) of a stage's virtual
+  // sequence; returns false past the end.
+  __device__ __forceinline__ static bool locate(const AttnParams& p, int r, int seg0, int t0,
+                                                int nseg, int& seg, int& t) {
+    seg = seg0;
+    t = t0 + r;
+    while (t >= p.T) {
+      t -= p.T;
+      ++seg;
+    }
+    return seg < nseg;
+  }
+
+  __device__ __forceinline__ void load(const AttnParams& p, const int8_t* segs, int nseg,
+                                       int seg0, int t0, int h) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int r = tid / DC + KROW_STEP * i;
+      int seg, t;
+      if (locate(p, r, seg0, t0, nseg, seg, t)) {
+        const uint16_t* src = row_ptr(p, p.k, p.k_pool, segs[seg], t, h, D);
+        kreg[i] = reinterpret_cast<const uint4*>(src)[tid % DC];
+      } else {
+        kreg[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    const int kg = tid % VKG;
+    const int dc = tid / VKG;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int seg, t;
+      if (locate(p, NV * kg + i, seg0, t0, nseg, seg, t)) {
+        const uint16_t* src = row_ptr(p, p.v, p.v_pool, segs[seg], t, h, D);
+        vreg[i] = reinterpret_cast<const uint4*>(src)[dc];
+      } else {
+        vreg[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vt) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int r = tid / DC + KROW_STEP * i;
+      const int col = (tid % DC) ^ kswz(r);
+      *reinterpret_cast<uint4*>(ks + r * D + col * 8) = kreg[i];
+    }
+    // V^T: row d = 8*dc + dd holds keys NV*kg .. NV*kg+NV-1 (contiguous).
+    const int kg = tid % VKG;
+    const int dc = tid / VKG;
+    const int key0 = NV * kg;
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int d = 8 * dc + dd;
+      const int byte = key0 * 2;
+      const int col = (byte >> 4) ^ (d & 7);
+      uint16_t* dst = vt + d * KT + col * 8 + ((byte & 15) >> 1);
+      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[NV / 2];
+#pragma unroll
+      for (int m = 0; m < NV / 2; ++m) {
+        const uint32_t a = reinterpret_cast<const uint32_t*>(&vreg[2 * m])[dd >> 1];
+        const uint32_t b = reinterpret_cast<const uint32_t*>(&vreg[2 * m + 1])[dd >> 1];
+        w[m] = __builtin_amdgcn_perm(b, a, sel);
+      }
+      if constexpr (NV == 4) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = w[0];
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float xlane32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xlane32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
+                          amdgpu_waves_per_eu(2, 2))) void
+attn_tick_kernel(const AttnParams p) {
+  constexpr int KS = D / 16;  // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * KT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 31;
+  const int g = lane >> 5;
+
+  // ---- work item: heaviest stage first, then head, then query tile --------
+  const int b = blockIdx.x;
+  const int rank = b / p.items_per_stage;
+  const int rem = b - rank * p.items_per_stage;
+  const int h = rem / p.ntq;
+  const int qt = rem - h * p.ntq;
+  const int s = p.stage_of_rank[rank];
+  const int nseg = p.nseg[s];
+  const int8_t* segs = p.seg[s];
+  const int T = p.T;
+  const int nkeys = nseg * T;
+  const int ntiles = (nkeys + KT - 1) / KT;
+  const int last_valid = nkeys - (ntiles - 1) * KT;
+
+  const int q0w = qt * QROWS + wave * 32;  // first query row of this wave
+  const bool wave_active = q0w < T;
+  const int qrow = q0w + r;
+
+  // ---- Q^T operand: lane holds query qrow, head dims 16*ks + 8*g .. +7 -----
+  bf16x8 qf[KS];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(p.q + ((int64_t(s) * T + qrow) * p.H + h) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 u = (qrow < T) ? qp[2 * ks + g] : make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // per-lane LDS read offsets (elements)
+  const int krow0 = swap_bits23(r);          // K row feeding MFMA row r of block 0
+  const int kx = kswz(krow0);                // same swizzle for block 1 (row + 32)
+  const int vrow_sw = r & 7;
+
+  TileLoader<D> ld;
+  int seg0 = 0, t0 = 0;
+  ld.load(p, segs, nseg, seg0, t0, h);
+  ld.store(ks_lds[0], vt_lds[0]);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const bool has_next = it + 1 < ntiles;
+    if (has_next) {
+      t0 += KT;
+      while (t0 >= T) {
+        t0 -= T;
+        ++seg0;
+      }
+      ld.load(p, segs, nseg, seg0, t0, h);
+    }
+
+    if (wave_active) {
+      const uint16_t* kb = ks_lds[buf];
+      const uint16_t* vb = vt_lds[buf];
+      // ---- S^T = K Q^T : two 32-key blocks --------------------------------
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const int row = krow0 + 32 * blk;
+          const int col = (2 * kk + g) ^ kx;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + row * D + col * 8);
+          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[blk], 0, 0, 0);
+        }
+      }
+      // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
+      if (it == ntiles - 1 && last_valid < KT) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int key = 32 * blk + 16 * (x >> 3) + 8 * g + (x & 7);
+            if (key >= last_valid) sacc[blk][x] = -INFINITY;
+          }
+      }
+      // ---- online softmax (exp2 domain) ------------------------------------
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
+      mx = xlane32_max(mx) * p.c;
+      const bool raise = mx > m_run + kLazyTau;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) oacc[i][x] *= alpha;
+      }
+      bf16x8 pb[4];
+      float lsum = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], p.c, -m_run));
+          lsum += e;
+          pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(e);
+        }
+      l_run += lsum;
+      // ---- O^T += V^T P^T : four 16-key steps ---------------------------
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int d = 32 * db + r;
+          const int col = (2 * kk + g) ^ vrow_sw;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + d * KT + col * 8);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
+        }
+      }
+    }
+
+    if (has_next) ld.store(ks_lds[buf ^ 1], vt_lds[buf ^ 1]);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l, bf16 ----------------------------------------
+  if (wave_active && qrow < T) {
+    const float inv = 1.0f / xlane32_sum(l_run);
+    uint16_t* op = p.o + ((int64_t(s) * T + qrow) * p.H + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * db + 8 * i + 4 * g;
+        bf16x4 v4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(oacc[db][4 * i + j] * inv);
+        *reinterpret_cast<uint2*>(op + d) = __builtin_bit_cast(uint2, v4);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct StagePlan {
+  int n_active = 0;
+  int order[WF_MAX_STAGES];
+  int nseg[WF_MAX_STAGES];
+  int8_t seg[WF_MAX_STAGES][WF_MAX_SEGMENTS];
+  int64_t keys[WF_MAX_STAGES];
+};
+
+// Segments of each active slot's context in the Eq. (5) order.
+void plan_stages(const wf_tick_desc& d, StagePlan& pl) {
+  std::memset(&pl, 0, sizeof(pl));
+  const int S = d.S;
+  const uint32_t A = d.active_mask;
+  for (int s = 0; s <= S; ++s) {
+    if (!((A >> s) & 1u)) continue;
+    int n = 0;
+    for (int c = d.hist_first[s]; c < d.n_hist; ++c) pl.seg[s][n++] = int8_t(-c - 1);
+    if ((A >> S) & 1u) pl.seg[s][n++] = int8_t(S);  // live store (self when s == S)
+    for (int j = s; j < S; ++j)
+      if ((A >> j) & 1u) pl.seg[s][n++] = int8_t(j);
+    pl.nseg[s] = n;
+    pl.keys[s] = int64_t(n) * d.T;
+    pl.order[pl.n_active++] = s;
+  }
+  std::stable_sort(pl.order, pl.order + pl.n_active,
+                   [&](int a, int b) { return pl.keys[a] > pl.keys[b]; });
+}
+
+int32_t validate_tick(const wf_tick_desc* d) {
+  if (!d) return fail(WF_EINVAL, "wf_attn_tick: desc is NULL");
+  if (d->S < 0 || d->S > WF_MAX_STAGES - 1)
+    return fail(WF_EINVAL, "wf_attn_tick: S = %d outside [0, %d]", d->S, WF_MAX_STAGES - 1);
+  const uint32_t all = (2u << d->S) - 1u;
+  if (d->active_mask & ~all)
+    return fail(WF_EINVAL, "wf_attn_tick: active_mask 0x%x has bits above S = %d",
+                d->active_mask, d->S);
+  if (d->T < 0 || d->H <= 0)
+    return fail(WF_EINVAL, "wf_attn_tick: bad sizes T = %d H = %d", d->T, d->H);
+  if (d->D != 64 && d->D != 128)
+    return fail(WF_EUNSUPPORTED, "wf_attn_tick: head dim D = %d (supported: 64, 128)", d->D);
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale))
+    return fail(WF_EINVAL, "wf_attn_tick: scale must be positive and finite");
+  if (d->n_hist < 0) return fail(WF_EINVAL, "wf_attn_tick: n_hist = %d", d->n_hist);
+  if (d->n_hist + d->S + 1 > WF_MAX_SEGMENTS)
+    return fail(WF_EUNSUPPORTED, "wf_attn_tick: n_hist + S + 1 = %d exceeds %d",
+                d->n_hist + d->S + 1, WF_MAX_SEGMENTS);
+  for (int s = 0; s <= d->S; ++s)
+    if (d->hist_first[s] < 0 || d->hist_first[s] > d->n_hist)
+      return fail(WF_EINVAL, "wf_attn_tick: hist_first[%d] = %d outside [0, %d]", s,
+                  d->hist_first[s], d->n_hist);
+  if (d->T == 0 || d->active_mask == 0) return WF_OK;
+  if (!d->q || !d->k || !d->v || !d->o)
+    return fail(WF_EINVAL, "wf_attn_tick: q, k, v and o must be non-NULL");
+  if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(d->o))
+    return fail(WF_EINVAL, "wf_attn_tick: q, k, v and o must be 16-byte aligned");
+  if (int64_t(d->T) > (int64_t(1) << 24))
+    return fail(WF_EUNSUPPORTED, "wf_attn_tick: T = %d too large", d->T);
+  if (d->n_hist > 0) {
+    if (!d->k_pool || !d->v_pool || !d->hist_pages)
+      return fail(WF_EINVAL, "wf_attn_tick: n_hist > 0 needs k_pool, v_pool and hist_pages");
+    if (!aligned16(d->k_pool) || !aligned16(d->v_pool))
+      return fail(WF_EINVAL, "wf_attn_tick: pools must be 16-byte aligned");
+    if (d->P <= 0 || d->P % 16 != 0)
+      return fail(WF_EINVAL, "wf_attn_tick: page size P = %d must be a positive multiple of 16",
+                  d->P);
+    if (d->num_pages <= 0) return fail(WF_EINVAL, "wf_attn_tick: num_pages = %d", d->num_pages);
+    const int64_t ppc = (int64_t(d->T) + d->P - 1) / d->P;
+    if (int64_t(d->n_hist) * ppc > d->num_pages)
+      return fail(WF_EINVAL, "wf_attn_tick: n_hist * ceil(T/P) = %lld exceeds num_pages = %d",
+                  static_cast<long long>(int64_t(d->n_hist) * ppc), d->num_pages);
+    if (int64_t(d->T) * d->P >= (int64_t(1) << 32))
+      return fail(WF_EUNSUPPORTED, "wf_attn_tick: T * P too large");
+  }
+  return WF_OK;
+}
+
+}  // namespace
+}  // namespace wf
+
+extern "C" wf_status wf_tick_useful_flops(const wf_tick_desc* desc, double* out) {
+  using namespace wf;
+  try {
+    if (!out) return fail(WF_EINVAL, "wf_tick_useful_flops: out is NULL");
+    int32_t st = validate_tick(desc);
+    if (st != WF_OK) return st;
+    StagePlan pl;
+    plan_stages(*desc, pl);
+    double pairs = 0;
+    for (int i = 0; i < pl.n_active; ++i) pairs += double(desc->T) * double(pl.keys[pl.order[i]]);
+    *out = 4.0 * desc->D * desc->H * pairs;
+    return WF_OK;
+  } catch (...) {
+    return fail(WF_EINVAL, "wf_tick_useful_flops: internal error");
+  }
+}
+
+extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) {
+  using namespace wf;
+  try {
+    int32_t st = validate_tick(desc);
+    if (st != WF_OK) return st;
+    const wf_tick_desc& d = *desc;
+    if (d.T == 0 || d.active_mask == 0) return WF_OK;
+    StagePlan pl;
+    plan_stages(d, pl);
+    const int32_t ppc = d.n_hist > 0 ? int32_t((int64_t(d.T) + d.P - 1) / d.P) : 0;
+    if (d.n_hist > 0 && check_pages_enabled()) {
+      st = check_device_pages(d.hist_pages, int64_t(d.n_hist) * ppc, d.num_pages, stream,
+                              "wf_attn_tick");
+      if (st != WF_OK) return st;
+    }
+    AttnParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = static_cast<const uint16_t*>(d.q);
+    p.k = static_cast<const uint16_t*>(d.k);
+    p.v = static_cast<const uint16_t*>(d.v);
+    p.o = static_cast<uint16_t*>(d.o);
+    p.k_pool = static_cast<const uint16_t*>(d.k_pool);
+    p.v_pool = static_cast<const uint16_t*>(d.v_pool);
+    p.hist_pages = d.hist_pages;
+    p.T = d.T;
+    p.H = d.H;
+    p.P = d.n_hist > 0 ? d.P : 16;
+    p.ppc = ppc;
+    p.p_magic = uint32_t((uint64_t(1) << 32) / uint64_t(p.P) + 1);
+    p.c = float(double(d.scale) * 1.4426950408889634);
+    p.ntq = (d.T + QROWS - 1) / QROWS;
+    p.items_per_stage = d.H * p.ntq;
+    for (int i = 0; i < pl.n_active; ++i) p.stage_of_rank[i] = int8_t(pl.order[i]);
+    for (int s = 0; s <= d.S; ++s) {
+      p.nseg[s] = int8_t(pl.nseg[s]);
+      for (int i = 0; i < pl.nseg[s]; ++i) p.seg[s][i] = pl.seg[s][i];
+    }
+    const int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
+    if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
+    if (d.D == 128)
+      attn_tick_kernel<128><<<dim3(unsigned(blocks)), NTHREADS, 0, stream>>>(p);
+    else
+      attn_tick_kernel<64><<<dim3(unsigned(blocks)), NTHREADS, 0, stream>>>(p);
+    return check_launch("wf_attn_tick");
+  } catch (...) {
+    return fail(WF_EINVAL, "wf_attn_tick: internal error");
+  }
+}

@@ -156,3 +156,39 @@ def draw_live(cfg: TickConfig, seed: int) -> tuple:
 def rollout_seed(k: int) -> int:
     """Seed of rollout tick k's live Q/K/V."""
     return 1000 + k
+
+
+def draw_live_torch(cfg: TickConfig, seed: int, device, T: Optional[int] = None):
+    """Live q, k, v of one tick drawn on the device with torch's seeded generator:
+    bf16 [S+1][T][H][D] ~ N(0, std^2) (normal in fp32, then rounded to bf16).
+
+    Used where hundreds of ticks are needed (streaming rollout, timing); any
+    oracle check on these inputs reads host copies of the same tensors.
+    """
+    import torch
+
+    T = cfg.T if T is None else T
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shape = (cfg.S + 1, T, cfg.H, cfg.D)
+    out = []
+    for _ in range(3):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        x.mul_(cfg.std)
+        out.append(x.to(torch.bfloat16))
+    return tuple(out)
+
+
+def to_device_bf16(bits: np.ndarray, device):
+    """uint16 bf16 bit patterns -> torch bfloat16 tensor on `device` (bit copy)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def bf16_tensor_bits(t) -> np.ndarray:
+    """torch bfloat16 tensor -> host uint16 bit patterns (bit copy)."""
+    import torch
+
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,263 @@
+"""Thin Python binding over libwfattn.so (include/wf_attn.h).
+
+Argument marshalling only: tensors are passed as device pointers
+(`tensor.data_ptr()`), the stream is torch's current HIP stream unless one is
+given, and every step of the computation runs in the library's HIP kernels.
+There is no fallback: importing this module raises if the library has not
+been built, and every non-OK status raises WfError with the library's text.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .build_lib import LIB_PATH
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first "
+                      "(python -m wavefront_causal_attention_wf_amd.build_lib)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+WF_OK = 0
+STATUS_NAMES = {0: "WF_OK", -1: "WF_EINVAL", -2: "WF_ENOMEM", -3: "WF_EHIP",
+                -4: "WF_EUNSUPPORTED", -5: "WF_ESTATE"}
+MAX_STAGES = 8
+MAX_SEGMENTS = 32
+
+_i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
+_vp = ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class WfError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.wf_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+
+
+class WfTickDesc(ctypes.Structure):
+    """Mirror of wf_tick_desc."""
+    _fields_ = [("S", _i32), ("active_mask", _u32), ("T", _i32), ("H", _i32), ("D", _i32),
+                ("scale", ctypes.c_float),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp),
+                ("k_pool", _vp), ("v_pool", _vp), ("num_pages", _i32), ("P", _i32),
+                ("hist_pages", _vp), ("n_hist", _i32), ("hist_first", _i32 * MAX_STAGES)]
+
+
+_lib.wf_last_error.restype = ctypes.c_char_p
+_lib.wf_last_error.argtypes = []
+_lib.wf_abi_version.restype = _i32
+_lib.wf_page_table_create.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32p, ctypes.POINTER(_vp)]
+_lib.wf_page_table_destroy.argtypes = [_vp]
+_lib.wf_page_table_destroy.restype = None
+_lib.wf_page_table_pages_per_chunk.argtypes = [_vp, _i32p]
+_lib.wf_page_table_alloc_chunk.argtypes = [_vp, _i32p, _i32]
+_lib.wf_page_table_commit.argtypes = [_vp, _i32p, _i32, _i32p]
+_lib.wf_page_table_export.argtypes = [_vp, _i32p, _i32, _i32p]
+_lib.wf_page_table_num_free.argtypes = [_vp, _i32p]
+_lib.wf_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
+_lib.wf_gather_paged.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
+_lib.wf_attn_tick.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
+_lib.wf_tick_useful_flops.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_double)]
+for _f in ("wf_page_table_create", "wf_page_table_pages_per_chunk", "wf_page_table_alloc_chunk",
+           "wf_page_table_commit", "wf_page_table_export", "wf_page_table_num_free",
+           "wf_store_paged", "wf_gather_paged", "wf_attn_tick", "wf_tick_useful_flops"):
+    getattr(_lib, _f).restype = _i32
+
+EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
+                    "wf_page_table_destroy", "wf_page_table_pages_per_chunk",
+                    "wf_page_table_alloc_chunk", "wf_page_table_commit", "wf_page_table_export",
+                    "wf_page_table_num_free", "wf_store_paged", "wf_gather_paged",
+                    "wf_attn_tick", "wf_tick_useful_flops")
+
+
+def _check(status: int, where: str) -> None:
+    if status != WF_OK:
+        raise WfError(status, where)
+
+
+def abi_version() -> int:
+    return int(_lib.wf_abi_version())
+
+
+def library():
+    """The loaded ctypes library (for tests that call symbols directly)."""
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(x) -> Optional[int]:
+    """Device pointer of a tensor (anything with data_ptr()), an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check_bf16(name, t):
+    import torch
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 bit patterns (bfloat16/int16/uint16), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# page table (host)
+# ---------------------------------------------------------------------------
+class PageTable:
+    """wf_page_table_*: FIFO free list + rolling history window (host state)."""
+
+    def __init__(self, num_pages: int, page_size: int, chunk_tokens: int, window_chunks: int,
+                 pin_anchor: bool = False, initial_free_order: Optional[Sequence[int]] = None):
+        self._h = _vp()
+        order_p = None
+        if initial_free_order is not None:
+            self._order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            order_p = self._order.ctypes.data_as(_i32p)
+        _check(_lib.wf_page_table_create(num_pages, page_size, chunk_tokens, window_chunks,
+                                         int(bool(pin_anchor)), order_p, ctypes.byref(self._h)),
+               "wf_page_table_create")
+        n = _i32()
+        _check(_lib.wf_page_table_pages_per_chunk(self._h, ctypes.byref(n)),
+               "wf_page_table_pages_per_chunk")
+        self.ppc = n.value
+        self.window = window_chunks
+
+    def close(self) -> None:
+        if self._h:
+            _lib.wf_page_table_destroy(self._h)
+            self._h = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_chunk(self) -> np.ndarray:
+        out = np.empty(self.ppc, np.int32)
+        _check(_lib.wf_page_table_alloc_chunk(self._h, out.ctypes.data_as(_i32p), self.ppc),
+               "wf_page_table_alloc_chunk")
+        return out
+
+    def commit(self) -> np.ndarray:
+        ev = np.empty(self.ppc, np.int32)
+        n = _i32()
+        _check(_lib.wf_page_table_commit(self._h, ev.ctypes.data_as(_i32p), self.ppc,
+                                         ctypes.byref(n)), "wf_page_table_commit")
+        return ev[: n.value].copy()
+
+    def export(self, out: Optional[np.ndarray] = None) -> np.ndarray:
+        """History page lists [n_hist][ppc], oldest first (int32)."""
+        cap = (self.window + 1) * self.ppc
+        buf = np.empty(cap, np.int32) if out is None else out
+        n = _i32()
+        _check(_lib.wf_page_table_export(self._h, buf.ctypes.data_as(_i32p), buf.size,
+                                         ctypes.byref(n)), "wf_page_table_export")
+        return buf[: n.value * self.ppc].reshape(n.value, self.ppc)
+
+    def num_free(self) -> int:
+        n = _i32()
+        _check(_lib.wf_page_table_num_free(self._h, ctypes.byref(n)), "wf_page_table_num_free")
+        return n.value
+
+
+# ---------------------------------------------------------------------------
+# device calls
+# ---------------------------------------------------------------------------
+def wf_store_paged(k_src, v_src, k_pool, v_pool, page_ids, stream=None) -> None:
+    """Scatter one chunk's K/V [T][H][D] into pool pages [num_pages][P][H][D]."""
+    for n, t in (("k_src", k_src), ("v_src", v_src), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _check_bf16(n, t)
+    T, H, D = k_src.shape
+    num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    _check(_lib.wf_store_paged(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(v_pool),
+                               _ptr(page_ids), T, H, D, num_pages, P, _stream(stream)),
+           "wf_store_paged")
+
+
+def wf_gather_paged(k_pool, v_pool, page_ids, k_dst, v_dst, stream=None) -> None:
+    """Copy n chunks out of pool pages into contiguous [n][T][H][D]."""
+    for n, t in (("k_pool", k_pool), ("v_pool", v_pool), ("k_dst", k_dst), ("v_dst", v_dst)):
+        _check_bf16(n, t)
+    n_chunks, T, H, D = k_dst.shape
+    num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    _check(_lib.wf_gather_paged(_ptr(k_pool), _ptr(v_pool), _ptr(page_ids), n_chunks,
+                                _ptr(k_dst), _ptr(v_dst), T, H, D, num_pages, P,
+                                _stream(stream)), "wf_gather_paged")
+
+
+def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: float,
+                   q=None, k=None, v=None, o=None, k_pool=None, v_pool=None,
+                   num_pages: int = 0, P: int = 0, hist_pages=None, n_hist: int = 0,
+                   hist_first: Optional[Sequence[int]] = None) -> WfTickDesc:
+    d = WfTickDesc()
+    d.S, d.active_mask, d.T, d.H, d.D, d.scale = S, active_mask, T, H, D, scale
+    d.q, d.k, d.v, d.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
+    d.k_pool, d.v_pool = _ptr(k_pool), _ptr(v_pool)
+    d.num_pages, d.P = num_pages, P
+    d.hist_pages, d.n_hist = _ptr(hist_pages), n_hist
+    hf = [0] * MAX_STAGES if hist_first is None else list(hist_first) + [0] * (MAX_STAGES - len(hist_first))
+    for i in range(MAX_STAGES):
+        d.hist_first[i] = int(hf[i])
+    return d
+
+
+def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None, v_pool=None,
+                 hist_pages=None, hist_first: Optional[Sequence[int]] = None,
+                 stream=None) -> None:
+    """One tick: q, k, v, o [S+1][T][H][D]; pools [num_pages][P][H][D];
+    hist_pages int32 [n_hist][ceil(T/P)] on the device."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bf16(n, t)
+    _, T, H, D = q.shape
+    n_hist, num_pages, P = 0, 0, 0
+    if hist_pages is not None and hist_pages.numel() > 0:
+        n_hist = hist_pages.shape[0]
+        num_pages, P = k_pool.shape[0], k_pool.shape[1]
+        _check_bf16("k_pool", k_pool)
+        _check_bf16("v_pool", v_pool)
+    d = make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
+                       k_pool if n_hist else None, v_pool if n_hist else None, num_pages, P,
+                       hist_pages if n_hist else None, n_hist, hist_first)
+    _check(_lib.wf_attn_tick(ctypes.byref(d), _stream(stream)), "wf_attn_tick")
+
+
+def wf_attn_tick_desc(desc: WfTickDesc, stream=None) -> None:
+    """Raw call with a prepared descriptor (used by the bench and the error tests)."""
+    _check(_lib.wf_attn_tick(ctypes.byref(desc), _stream(stream)), "wf_attn_tick")
+
+
+def wf_tick_useful_flops(S: int, active_mask: int, T: int, H: int, D: int, n_hist: int = 0,
+                         hist_first: Optional[Sequence[int]] = None, P: int = 16,
+                         num_pages: int = 0) -> float:
+    """Useful FLOPs the library counts for a tick (host only; no device pointers needed
+    beyond non-NULL placeholders)."""
+    fake = 16  # aligned non-NULL placeholder: nothing is dereferenced by this call
+    d = make_tick_desc(S, active_mask, T, H, D, 1.0, fake, fake, fake, fake,
+                       fake if n_hist else None, fake if n_hist else None,
+                       max(num_pages, n_hist * -(-T // P)) if n_hist else 0, P if n_hist else 0,
+                       fake if n_hist else None, n_hist, hist_first)
+    out = ctypes.c_double()
+    _check(_lib.wf_tick_useful_flops(ctypes.byref(d), ctypes.byref(out)), "wf_tick_useful_flops")
+    return out.value
