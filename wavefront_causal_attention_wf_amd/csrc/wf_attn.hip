@@ -21,10 +21,13 @@
 //    softmax needs only one cross-lane exchange (lane l <-> l+32) per tile.
 //    K rows are fed to the MFMA in a bit-2/bit-3-swapped order so that the score
 //    registers already are the P operand of the P.V product (no shuffles).
-//  * K tile [64 keys][D] and V^T tile [D][64 keys] in LDS, XOR-swizzled so the
-//    16-byte MFMA operand reads are bank-conflict free; V is transposed in
-//    registers (v_perm_b32) on its way to LDS. Global loads of tile i+1 are in
-//    flight while tile i is computed (double-buffered LDS, one barrier a tile).
+//  * K and V tiles [64 keys][D] stream from global memory straight into LDS
+//    (16-byte direct loads, no register staging), double-buffered: the loads of
+//    tile i+1 are in flight while tile i is computed, one barrier per tile. Row
+//    addresses come from a per-tile segment lookup and, for history, from the
+//    page table copied into LDS once per workgroup. Both tiles are XOR-swizzled
+//    per row; V^T operands are fetched with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16), so V needs no transpose on its way in.
 //  * Online softmax in the exp2 domain (log2 e folded into the scale), fp32
 //    state; the running max is only raised when a tile exceeds it by more than
 //    8 (in log2 units), so the O rescale is rare (exact: numerator and
@@ -33,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -64,6 +68,7 @@ struct AttnParams {
   float c;                // scale * log2(e)
   int32_t ntq;            // query tiles per chunk
   int32_t items_per_stage;  // H * ntq
+  int32_t n_page_ids;     // n_hist * ppc entries of hist_pages (copied to LDS)
   int8_t stage_of_rank[WF_MAX_STAGES];  // work order, heaviest stage first
   int8_t nseg[WF_MAX_STAGES];
   // per stage: segment code >= 0 is live slot j, < 0 is history chunk (-code - 1)
@@ -73,107 +78,20 @@ struct AttnParams {
 __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
-// XOR swizzle of the 16-byte column of K row `row` (values 0..7).
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
 
-// Address of row t of segment `code` for head h (K or V, selected by the bases).
-__device__ __forceinline__ const uint16_t* row_ptr(const AttnParams& p, const uint16_t* live,
-                                                   const uint16_t* pool, int code, int t, int h,
-                                                   int D) {
-  if (code >= 0) return live + ((int64_t(code) * p.T + t) * p.H + h) * D;
-  const int c = -code - 1;
-  const uint32_t pg = __umulhi(uint32_t(t), p.p_magic);
-  const int slot = t - int(pg) * p.P;
-  const int64_t page = p.hist_pages[int64_t(c) * p.ppc + pg];
-  return pool + ((page * p.P + slot) * p.H + h) * D;
-}
-
+// XOR swizzle (16-byte chunk index) of K tile row `row`. The MFMA operand reads
+// touch rows {0..3, 8..11} (+4, +16, ...) at one logical chunk; the swizzle maps
+// any such 8 rows to distinct chunks mod 8 and rows 0..15 to distinct chunks
+// mod 16 (D = 128), so the reads are bank-conflict free.
 template <int D>
-struct TileLoader {
-  static constexpr int DC = D / 8;                       // 16-byte chunks per row
-  static constexpr int NK = KT * DC / NTHREADS;          // K chunks per thread
-  static constexpr int NV = KT * DC / NTHREADS;          // V keys per thread
-  static constexpr int KROW_STEP = NTHREADS / DC;
-  static constexpr int VKG = KT / NV;                    // key groups
-
-  uint4 kreg[NK];
-  uint4 vreg[NV];
-
-  // Locate key `r` of the tile that starts at (seg0, t0) of a stage's virtual
-  // sequence; returns false past the end.
-  __device__ __forceinline__ static bool locate(const AttnParams& p, int r, int seg0, int t0,
-                                                int nseg, int& seg, int& t) {
-    seg = seg0;
-    t = t0 + r;
-    while (t >= p.T) {
-      t -= p.T;
-      ++seg;
-    }
-    return seg < nseg;
-  }
-
-  __device__ __forceinline__ void load(const AttnParams& p, const int8_t* segs, int nseg,
-                                       int seg0, int t0, int h) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int r = tid / DC + KROW_STEP * i;
-      int seg, t;
-      if (locate(p, r, seg0, t0, nseg, seg, t)) {
-        const uint16_t* src = row_ptr(p, p.k, p.k_pool, segs[seg], t, h, D);
-        kreg[i] = reinterpret_cast<const uint4*>(src)[tid % DC];
-      } else {
-        kreg[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    const int kg = tid % VKG;
-    const int dc = tid / VKG;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int seg, t;
-      if (locate(p, NV * kg + i, seg0, t0, nseg, seg, t)) {
-        const uint16_t* src = row_ptr(p, p.v, p.v_pool, segs[seg], t, h, D);
-        vreg[i] = reinterpret_cast<const uint4*>(src)[dc];
-      } else {
-        vreg[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vt) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int r = tid / DC + KROW_STEP * i;
-      const int col = (tid % DC) ^ kswz(r);
-      *reinterpret_cast<uint4*>(ks + r * D + col * 8) = kreg[i];
-    }
-    // V^T: row d = 8*dc + dd holds keys NV*kg .. NV*kg+NV-1 (contiguous).
-    const int kg = tid % VKG;
-    const int dc = tid / VKG;
-    const int key0 = NV * kg;
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int d = 8 * dc + dd;
-      const int byte = key0 * 2;
-      const int col = (byte >> 4) ^ (d & 7);
-      uint16_t* dst = vt + d * KT + col * 8 + ((byte & 15) >> 1);
-      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t w[NV / 2];
-#pragma unroll
-      for (int m = 0; m < NV / 2; ++m) {
-        const uint32_t a = reinterpret_cast<const uint32_t*>(&vreg[2 * m])[dd >> 1];
-        const uint32_t b = reinterpret_cast<const uint32_t*>(&vreg[2 * m + 1])[dd >> 1];
-        w[m] = __builtin_amdgcn_perm(b, a, sel);
-      }
-      if constexpr (NV == 4) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = w[0];
-      }
-    }
-  }
-};
+__device__ __forceinline__ int kswz(int row) {
+  int x = (row & 3) | ((row >> 1) & 4);
+  if constexpr (D == 128) x |= (row << 1) & 8;
+  return x;
+}
+// XOR swizzle of V tile row `row`: the transposed reads fetch 32 contiguous bytes
+// from 4 consecutive rows; this puts those 4 pieces in distinct 32-byte slots.
+__device__ __forceinline__ int vswz(int row) { return 2 * (row & 3); }
 
 __device__ __forceinline__ float xlane32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -184,18 +102,118 @@ __device__ __forceinline__ float xlane32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Segments of the stage's virtual key sequence, resolved once per workgroup into
+// LDS: base row pointers of K and V for head h, and for history chunks the index
+// of the chunk's first page id in the page table (-1 for live chunks).
+struct SegTable {
+  const uint16_t* kbase[WF_MAX_SEGMENTS];
+  const uint16_t* vbase[WF_MAX_SEGMENTS];
+  int32_t hist_off[WF_MAX_SEGMENTS];
+};
+
+template <int D>
+__device__ __forceinline__ void fill_seg_table(const AttnParams& p, int s, int h, SegTable& st) {
+  const int i = threadIdx.x;
+  if (i < p.nseg[s]) {
+    const int code = p.seg[s][i];
+    if (code >= 0) {
+      const int64_t off = (int64_t(code) * p.T * p.H + h) * D;
+      st.kbase[i] = p.k + off;
+      st.vbase[i] = p.v + off;
+      st.hist_off[i] = -1;
+    } else {
+      st.kbase[i] = p.k_pool + int64_t(h) * D;
+      st.vbase[i] = p.v_pool + int64_t(h) * D;
+      st.hist_off[i] = (-code - 1) * p.ppc;
+    }
+  }
+}
+
+// Tile loads straight from global memory into LDS (16 bytes per lane). Wave w
+// fills K and V rows [16w, 16w+16) of the tile; one wave instruction writes
+// 1 KB = RPI whole rows, lane l landing at chunk l % DC of row l / DC, so each
+// lane fetches the logical chunk that the row swizzle maps to that position.
+template <int D>
+struct DirectLoader {
+  static constexpr int DC = D / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / DC;  // rows per wave instruction
+  static constexpr int NI = 16 / RPI;  // instructions per wave per tensor
+
+  __device__ __forceinline__ static void issue(const AttnParams& p, const int32_t* pages,
+                                               const SegTable& st, int nseg, int seg0, int t0,
+                                               uint16_t* kbuf, uint16_t* vbuf, int wave,
+                                               int lane) {
+    const int T = p.T;
+    const int64_t HD = int64_t(p.H) * D;
+    const int pc = lane % DC;
+    const bool fast = T >= KT;  // a tile then spans at most two segments
+    const int seg1 = seg0 + 1 < nseg ? seg0 + 1 : seg0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = wave * 16 + RPI * i + lane / DC;
+      int t = t0 + row;
+      int seg = seg0;
+      if (fast) {
+        if (t >= T) {
+          t -= T;
+          seg = seg0 + 1;
+        }
+      } else {
+        while (t >= T) {
+          t -= T;
+          ++seg;
+        }
+      }
+      const bool valid = seg < nseg;
+      const int sg = valid ? seg : seg1;
+      const int hoff = st.hist_off[sg];
+      int64_t ridx = t;
+      if (hoff >= 0) {
+        const uint32_t pg = __umulhi(uint32_t(t), p.p_magic);
+        const int slot = t - int(pg) * p.P;
+        ridx = int64_t(pages[hoff + int(pg)]) * p.P + slot;
+      }
+      const int koff = (pc ^ kswz<D>(row)) * 8;
+      const int voff = (pc ^ vswz(row)) * 8;
+      uint16_t* kdst = kbuf + (wave * 16 + RPI * i) * D;
+      uint16_t* vdst = vbuf + (wave * 16 + RPI * i) * D;
+      if (valid) {
+        __builtin_amdgcn_global_load_lds(st.kbase[sg] + ridx * HD + koff, (lds_void*)kdst, 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds(st.vbase[sg] + ridx * HD + voff, (lds_void*)vdst, 16, 0,
+                                         0);
+      } else {
+        // past the last key: zero V (P is 0 there and 0 * garbage may be NaN)
+        *reinterpret_cast<uint4*>(vdst + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(kdst + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+};
+
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 attn_tick_kernel(const AttnParams p) {
   constexpr int KS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * KT];
+  // Two K and two V tile buffers as four distinct LDS objects: the loop is
+  // unrolled by two so that every access names its buffer statically, which
+  // lets the compiler see that reads of one buffer never alias the in-flight
+  // direct loads into the other (no spurious wait on those loads mid-tile).
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[KT * D];
+  __shared__ SegTable seg_tab;
+  extern __shared__ int32_t pages_lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31;
   const int g = lane >> 5;
 
@@ -207,11 +225,15 @@ attn_tick_kernel(const AttnParams p) {
   const int qt = rem - h * p.ntq;
   const int s = p.stage_of_rank[rank];
   const int nseg = p.nseg[s];
-  const int8_t* segs = p.seg[s];
   const int T = p.T;
   const int nkeys = nseg * T;
   const int ntiles = (nkeys + KT - 1) / KT;
   const int last_valid = nkeys - (ntiles - 1) * KT;
+
+  // page table of the history into LDS (read by every tile's address math)
+  for (int i = tid; i < p.n_page_ids; i += NTHREADS) pages_lds[i] = p.hist_pages[i];
+  fill_seg_table<D>(p, s, h, seg_tab);
+  __syncthreads();
 
   const int q0w = qt * QROWS + wave * 32;  // first query row of this wave
   const bool wave_active = q0w < T;
@@ -235,31 +257,31 @@ attn_tick_kernel(const AttnParams p) {
   float l_run = 0.f;
 
   // per-lane LDS read offsets (elements)
-  const int krow0 = swap_bits23(r);          // K row feeding MFMA row r of block 0
-  const int kx = kswz(krow0);                // same swizzle for block 1 (row + 32)
-  const int vrow_sw = r & 7;
+  const int krow0 = swap_bits23(r);   // K row feeding MFMA row r of block 0 (+32: block 1)
+  const int kx = kswz<D>(krow0);      // same swizzle for row + 32
+  const int a16 = lane & 15;          // lane within its 16-lane group (transposed V reads)
+  const int vrow = 8 * g + (a16 >> 2);
+  const int vx = 2 * ((a16 >> 2) & 3);
+  const int vcx = 2 * ((lane >> 4) & 1) + ((a16 >> 1) & 1);
+  const int vsub = 4 * (a16 & 1);
 
-  TileLoader<D> ld;
   int seg0 = 0, t0 = 0;
-  ld.load(p, segs, nseg, seg0, t0, h);
-  ld.store(ks_lds[0], vt_lds[0]);
+  DirectLoader<D>::issue(p, pages_lds, seg_tab, nseg, seg0, t0, k_lds0, v_lds0, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's tile loads have landed
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) {
+  // One tile: prefetch tile it+1 into (kn, vn) while computing tile it from (kb, vb).
+  auto step = [&](int it, const uint16_t* kb, const uint16_t* vb, uint16_t* kn, uint16_t* vn) {
+    if (it + 1 < ntiles) {
       t0 += KT;
       while (t0 >= T) {
         t0 -= T;
         ++seg0;
       }
-      ld.load(p, segs, nseg, seg0, t0, h);
+      DirectLoader<D>::issue(p, pages_lds, seg_tab, nseg, seg0, t0, kn, vn, wave, lane);
     }
 
     if (wave_active) {
-      const uint16_t* kb = ks_lds[buf];
-      const uint16_t* vb = vt_lds[buf];
       // ---- S^T = K Q^T : two 32-key blocks --------------------------------
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -311,21 +333,28 @@ attn_tick_kernel(const AttnParams p) {
           pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(e);
         }
       l_run += lsum;
-      // ---- O^T += V^T P^T : four 16-key steps ---------------------------
+      // ---- O^T += V^T P^T : four 16-key steps, V^T via transposed reads ----
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = 32 * db + r;
-          const int col = (2 * kk + g) ^ vrow_sw;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + d * KT + col * 8);
+          const int col = ((4 * db + vcx) ^ vx) * 8 + vsub;
+          const uint16_t* a0 = vb + (16 * kk + vrow) * D + col;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0 + 4 * D));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
         }
       }
     }
 
-    if (has_next) ld.store(ks_lds[buf ^ 1], vt_lds[buf ^ 1]);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): next tile's loads have landed
     __syncthreads();
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, k_lds0, v_lds0, k_lds1, v_lds1);
+    if (it + 1 < ntiles) step(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
   // ---- epilogue: O = O^T / l, bf16 ----------------------------------------
@@ -374,6 +403,28 @@ void plan_stages(const wf_tick_desc& d, StagePlan& pl) {
   }
   std::stable_sort(pl.order, pl.order + pl.n_active,
                    [&](int a, int b) { return pl.keys[a] > pl.keys[b]; });
+}
+
+// LDS budget for the page table: static K/V buffers take 64 KB (D = 128); the
+// table is sized to the call and may use up to 32 KB more.
+constexpr size_t kMaxPageTableLds = 32 * 1024;
+
+template <int D>
+int32_t launch_attn(const AttnParams& p, unsigned blocks, size_t dyn_lds, hipStream_t stream) {
+  // The dynamic-LDS limit is raised once per device.
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "wf_attn_tick: hipGetDevice");
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_tick_kernel<D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxPageTableLds));
+    if (e != hipSuccess) return hip_fail(e, "wf_attn_tick: hipFuncSetAttribute");
+    attr_set.fetch_or(bit, std::memory_order_acq_rel);
+  }
+  attn_tick_kernel<D><<<dim3(blocks), NTHREADS, dyn_lds, stream>>>(p);
+  return WF_OK;
 }
 
 int32_t validate_tick(const wf_tick_desc* d) {
@@ -476,6 +527,7 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     p.c = float(double(d.scale) * 1.4426950408889634);
     p.ntq = (d.T + QROWS - 1) / QROWS;
     p.items_per_stage = d.H * p.ntq;
+    p.n_page_ids = d.n_hist * ppc;
     for (int i = 0; i < pl.n_active; ++i) p.stage_of_rank[i] = int8_t(pl.order[i]);
     for (int s = 0; s <= d.S; ++s) {
       p.nseg[s] = int8_t(pl.nseg[s]);
@@ -483,10 +535,15 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     }
     const int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
+    const size_t dyn_lds = size_t(p.n_page_ids) * sizeof(int32_t);
+    if (dyn_lds > kMaxPageTableLds)
+      return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %zu bytes of LDS",
+                  p.n_page_ids, kMaxPageTableLds);
     if (d.D == 128)
-      attn_tick_kernel<128><<<dim3(unsigned(blocks)), NTHREADS, 0, stream>>>(p);
+      st = launch_attn<128>(p, unsigned(blocks), dyn_lds, stream);
     else
-      attn_tick_kernel<64><<<dim3(unsigned(blocks)), NTHREADS, 0, stream>>>(p);
+      st = launch_attn<64>(p, unsigned(blocks), dyn_lds, stream);
+    if (st != WF_OK) return st;
     return check_launch("wf_attn_tick");
   } catch (...) {
     return fail(WF_EINVAL, "wf_attn_tick: internal error");
