@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle sample")
     ap.add_argument("--rotate", type=int, default=4, help="distinct live-input sets cycled")
+    ap.add_argument("--mode", default="tick", choices=["tick", "attn", "store", "copy"],
+                    help="tick: the full hot path (default, prints the JSON line); attn / "
+                         "store: only that kernel, --steps launches (for profilers); copy: "
+                         "a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -117,6 +121,73 @@ class Rollout:
         self.pt.commit()
 
 
+def store_bandwidth(cfg, dev, launches: int = 24, rotation: int = 8) -> dict:
+    """wf_store_paged alone, rotating over `rotation` distinct source chunks and
+    page sets (working set > the 256 MB last-level cache), HIP events on its stream."""
+    import torch
+
+    from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+    T, H, D, P = cfg.T, cfg.H, cfg.D, cfg.P
+    ppc = cfg.ppc
+    pool_pages = max(cfg.num_pages, rotation * ppc)
+    kp = torch.zeros((pool_pages, P, H, D), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    srcs = [inputs.draw_live_torch(cfg, 3000 + i, dev, T=T)[0] for i in range(rotation)]
+    ksrc = [x[0].clone() for x in srcs]
+    vsrc = [x[1].clone() for x in srcs]
+    del srcs
+    order = torch.from_numpy(inputs.initial_free_order(
+        inputs.TickConfig("rot", S=0, T=T, H=H, D=D, P=P, n_hist=0, num_pages=pool_pages,
+                          std=0.5, bf16_inputs=True, page_order="permutation")))
+    ids = [order[i * ppc:(i + 1) * ppc].to(torch.int32).to(dev) for i in range(rotation)]
+    for i in range(rotation):  # warm
+        wfattn.wf_store_paged(ksrc[i], vsrc[i], kp, vp, ids[i])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(launches):
+        j = i % rotation
+        wfattn.wf_store_paged(ksrc[j], vsrc[j], kp, vp, ids[j])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / launches
+    nbytes = 2 * (T * H * D * 2) + 2 * (ppc * P * H * D * 2)   # read K,V + write whole pages
+    return {"kernel": "wf_store_paged", "us_mean": round(ms * 1e3, 2),
+            "bytes": nbytes, "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "rotation": rotation}
+
+
+def profile_mode(args, cfg, dev) -> None:
+    """Launch-only loops for profilers (no JSON line)."""
+    import torch
+
+    from wavefront_causal_attention_wf_amd import wfattn
+
+    if args.mode == "copy":
+        n = 1 << 29  # 2^29 bf16 = 1 GiB
+        x = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
+        y = torch.empty_like(x)
+        for _ in range(args.steps):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log(f"copy: {args.steps} x 1 GiB read + 1 GiB write")
+        return
+    if args.mode == "store":
+        r = store_bandwidth(cfg, dev, launches=args.steps)
+        log(f"store: {r}")
+        return
+    ro = Rollout(cfg, 1, dev)
+    q, k, v = ro.live[0]
+    hist = torch.from_numpy(ro.pt.export().copy()).to(dev)
+    mask = (1 << (cfg.S + 1)) - 1
+    for _ in range(args.steps):
+        wfattn.wf_attn_tick(q, k, v, ro.o, cfg.S, mask, ro.scale, ro.k_pool, ro.v_pool, hist)
+    torch.cuda.synchronize()
+    log(f"attn: {args.steps} launches")
+
+
 def cpu_baseline(cfg, budget_s: float) -> dict:
     """fp64 oracle on a bounded sample of one steady tick: all stages, heads
     0..n-1, every query row; n grows while the budget allows."""
@@ -168,6 +239,9 @@ def main():
     dev = torch.device("cuda:0")
     log(f"config {cfg.name}: S={cfg.S} T={cfg.T} H={cfg.H} D={cfg.D} P={cfg.P} "
         f"n_hist={cfg.n_hist} pool={cfg.num_pages}")
+    if args.mode != "tick":
+        profile_mode(args, cfg, dev)
+        return
     ro = Rollout(cfg, args.rotate, dev)
     mask = (1 << (cfg.S + 1)) - 1
     flops = wfattn.wf_tick_useful_flops(cfg.S, mask, cfg.T, cfg.H, cfg.D, cfg.n_hist, P=cfg.P,
@@ -224,6 +298,8 @@ def main():
                      "traffic": None, "kernel": "wf_attn_tick",
                      "kernel_ms_mean": round(float(attn_ms.mean()), 4)},
     }
+    out["store"] = store_bandwidth(cfg, dev)
+    log(f"store: {out['store']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_s)

@@ -54,6 +54,8 @@ constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int QROWS = 32 * NWAVES;  // query rows per workgroup
 constexpr float kLazyTau = 8.0f;    // raise the running max only beyond this (log2 units)
+constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kXcdTable = 512;      // max (stage, head) groups in the XCD table
 
 struct AttnParams {
   const uint16_t* q;
@@ -69,6 +71,13 @@ struct AttnParams {
   int32_t ntq;            // query tiles per chunk
   int32_t items_per_stage;  // H * ntq
   int32_t n_page_ids;     // n_hist * ppc entries of hist_pages (copied to LDS)
+  // XCD-aware order: block b runs on XCD b % 8 (round-robin dispatch); its
+  // (b / 8)-th item is query tile (b / 8) % ntq of group xcd_groups[x][(b / 8) / ntq],
+  // group = rank * H + head. Blocks past an XCD's list exit at once.
+  int32_t use_xcd;
+  int32_t xcd_stride;
+  int16_t xcd_n[kNumXcd];
+  int16_t xcd_groups[kXcdTable];
   int8_t stage_of_rank[WF_MAX_STAGES];  // work order, heaviest stage first
   int8_t nseg[WF_MAX_STAGES];
   // per stage: segment code >= 0 is live slot j, < 0 is history chunk (-code - 1)
@@ -219,10 +228,22 @@ attn_tick_kernel(const AttnParams p) {
 
   // ---- work item: heaviest stage first, then head, then query tile --------
   const int b = blockIdx.x;
-  const int rank = b / p.items_per_stage;
-  const int rem = b - rank * p.items_per_stage;
-  const int h = rem / p.ntq;
-  const int qt = rem - h * p.ntq;
+  int rank, h, qt;
+  if (p.use_xcd) {
+    const int x = b & (kNumXcd - 1);
+    const int k = b / kNumXcd;
+    const int gi = k / p.ntq;
+    if (gi >= p.xcd_n[x]) return;  // whole block: this XCD's list is shorter
+    const int grp = p.xcd_groups[x * p.xcd_stride + gi];
+    qt = k - gi * p.ntq;
+    rank = grp / p.H;
+    h = grp - rank * p.H;
+  } else {
+    rank = b / p.items_per_stage;
+    const int rem = b - rank * p.items_per_stage;
+    h = rem / p.ntq;
+    qt = rem - h * p.ntq;
+  }
   const int s = p.stage_of_rank[rank];
   const int nseg = p.nseg[s];
   const int T = p.T;
@@ -282,18 +303,39 @@ attn_tick_kernel(const AttnParams p) {
     }
 
     if (wave_active) {
-      // ---- S^T = K Q^T : two 32-key blocks --------------------------------
+      // ---- S^T = K Q^T : two 32-key blocks, K operands one step ahead ------
+      auto kload = [&](int kk, bf16x8* dst) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+          dst[blk] = *reinterpret_cast<const bf16x8*>(kb + (krow0 + 32 * blk) * D +
+                                                      ((2 * kk + g) ^ kx) * 8);
+      };
+      // V^T operand of one 16-key step for all DB blocks: two transposed reads each
+      auto vload = [&](int kk, bf16x8* dst) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint16_t* a0 = vb + (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(a0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(a0 + 4 * D));
+          dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      };
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      bf16x8 ka[2][2];
+      kload(0, ka[0]);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) kload(kk + 1, ka[(kk + 1) & 1]);
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          const int row = krow0 + 32 * blk;
-          const int col = (2 * kk + g) ^ kx;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + row * D + col * 8);
-          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[blk], 0, 0, 0);
-        }
+        for (int blk = 0; blk < 2; ++blk)
+          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk & 1][blk], qf[kk], sacc[blk],
+                                                              0, 0, 0);
       }
+      // the first V^T operands load while the softmax runs
+      bf16x8 va[2][DB];
+      vload(0, va[0]);
       // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
       if (it == ntiles - 1 && last_valid < KT) {
 #pragma unroll
@@ -333,18 +375,14 @@ attn_tick_kernel(const AttnParams p) {
           pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(e);
         }
       l_run += lsum;
-      // ---- O^T += V^T P^T : four 16-key steps, V^T via transposed reads ----
+      // ---- O^T += V^T P^T : four 16-key steps, operands one step ahead ------
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        if (kk + 1 < 4) vload(kk + 1, va[(kk + 1) & 1]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int col = ((4 * db + vcx) ^ vx) * 8 + vsub;
-          const uint16_t* a0 = vb + (16 * kk + vrow) * D + col;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a0 + 4 * D));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kk], oacc[db], 0, 0, 0);
-        }
+        for (int db = 0; db < DB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0,
+                                                             0, 0);
       }
     }
 
@@ -403,6 +441,40 @@ void plan_stages(const wf_tick_desc& d, StagePlan& pl) {
   }
   std::stable_sort(pl.order, pl.order + pl.n_active,
                    [&](int a, int b) { return pl.keys[a] > pl.keys[b]; });
+}
+
+// XCD-aware work order. The (stage, head) groups, heaviest stage first, are
+// dealt to the 8 XCDs by longest-processing-time (each to the least-loaded XCD),
+// so every XCD gets about the same number of keys to stream and the query tiles
+// of one group run together on one XCD and share its L2. Falls back to the
+// plain order when the table does not fit.
+void plan_xcd_order(const StagePlan& pl, int H, AttnParams& p, int64_t& blocks) {
+  p.use_xcd = 0;
+  const int G = pl.n_active * H;
+  if (G > kXcdTable) return;
+  int16_t lists[kNumXcd][kXcdTable];
+  int n[kNumXcd] = {0};
+  int64_t load[kNumXcd] = {0};
+  for (int rank = 0; rank < pl.n_active; ++rank) {
+    const int64_t w = pl.keys[pl.order[rank]];
+    for (int h = 0; h < H; ++h) {
+      int best = 0;
+      for (int x = 1; x < kNumXcd; ++x)
+        if (load[x] < load[best]) best = x;
+      lists[best][n[best]++] = int16_t(rank * H + h);
+      load[best] += w;
+    }
+  }
+  int stride = 0;
+  for (int x = 0; x < kNumXcd; ++x) stride = std::max(stride, n[x]);
+  if (stride * kNumXcd > kXcdTable) return;
+  p.use_xcd = 1;
+  p.xcd_stride = stride;
+  for (int x = 0; x < kNumXcd; ++x) {
+    p.xcd_n[x] = int16_t(n[x]);
+    for (int i = 0; i < n[x]; ++i) p.xcd_groups[x * stride + i] = lists[x][i];
+  }
+  blocks = int64_t(kNumXcd) * stride * p.ntq;
 }
 
 // LDS budget for the page table: static K/V buffers take 64 KB (D = 128); the
@@ -533,7 +605,8 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
       p.nseg[s] = int8_t(pl.nseg[s]);
       for (int i = 0; i < pl.nseg[s]; ++i) p.seg[s][i] = pl.seg[s][i];
     }
-    const int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
+    int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
+    plan_xcd_order(pl, d.H, p, blocks);
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
     const size_t dyn_lds = size_t(p.n_page_ids) * sizeof(int32_t);
     if (dyn_lds > kMaxPageTableLds)
