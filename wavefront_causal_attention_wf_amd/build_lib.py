@@ -25,7 +25,10 @@ SOURCES = ["wf_attn.hip", "wf_paged.hip", "wf_page_table.cpp", "wf_error.cpp"]
 # Packed-FP32 VALU forms are kept out of the generated code (the device pass
 # honours the flag; the host pass only warns that it does not know it).
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA results in VGPRs: the softmax reads the score accumulators with
+             # VALU ops, and the query fragments go to AGPRs instead.
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

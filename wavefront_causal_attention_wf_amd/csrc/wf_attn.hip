@@ -141,69 +141,111 @@ __device__ __forceinline__ void fill_seg_table(const AttnParams& p, int s, int h
   }
 }
 
+// The (at most two, when T >= 64) segments a tile touches, in scalar
+// registers; refreshed only when the tile start moves into a new segment.
+struct SegPair {
+  const uint16_t* k[2];
+  const uint16_t* v[2];
+  int32_t hoff[2];
+  int32_t seg0;
+};
+
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(x >> 32));
+  return reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
+}
+
+// Segments past the end of the context map to segment 0: tile rows beyond the
+// last key then read a finite row of the first segment; their scores are masked
+// to -inf, so their P is exactly 0 and they add nothing.
+__device__ __forceinline__ void load_seg_pair(const SegTable& st, int nseg, int seg0,
+                                              SegPair& sp) {
+  const int s0 = seg0 < nseg ? seg0 : 0;
+  const int s1 = seg0 + 1 < nseg ? seg0 + 1 : 0;
+  sp.k[0] = uniform_ptr(st.kbase[s0]);
+  sp.v[0] = uniform_ptr(st.vbase[s0]);
+  sp.hoff[0] = __builtin_amdgcn_readfirstlane(st.hist_off[s0]);
+  sp.k[1] = uniform_ptr(st.kbase[s1]);
+  sp.v[1] = uniform_ptr(st.vbase[s1]);
+  sp.hoff[1] = __builtin_amdgcn_readfirstlane(st.hist_off[s1]);
+  sp.seg0 = seg0;
+}
+
 // Tile loads straight from global memory into LDS (16 bytes per lane). Wave w
 // fills K and V rows [16w, 16w+16) of the tile; one wave instruction writes
 // 1 KB = RPI whole rows, lane l landing at chunk l % DC of row l / DC, so each
 // lane fetches the logical chunk that the row swizzle maps to that position.
-template <int D>
-struct DirectLoader {
+// prepare() resolves this lane's rows and starts the page-id reads; emit(i)
+// issues the two loads of row group i, so the caller can spread them between
+// MFMAs. Rows past the last key (every row, when there is no next tile) read
+// a row of segment 0 instead: every wave issues the same loads each tile, with
+// no branch.
+template <int D, bool kSmallT>
+struct TileLoads {
   static constexpr int DC = D / 8;     // 16-byte chunks per row
   static constexpr int RPI = 64 / DC;  // rows per wave instruction
   static constexpr int NI = 16 / RPI;  // instructions per wave per tensor
 
-  __device__ __forceinline__ static void issue(const AttnParams& p, const int32_t* pages,
-                                               const SegTable& st, int nseg, int seg0, int t0,
-                                               uint16_t* kbuf, uint16_t* vbuf, int wave,
-                                               int lane) {
+  const uint16_t* kp[NI];
+  const uint16_t* vp[NI];
+  int32_t t[NI];      // token within the segment's chunk
+  int32_t hoff[NI];   // first page-table entry of the chunk (-1: live chunk)
+  int32_t pg[NI];     // page of the token within the chunk
+  int32_t page[NI];   // pool page id (history chunks)
+
+  __device__ __forceinline__ void prepare(const AttnParams& p, const int32_t* pages,
+                                          const SegTable& st, const SegPair& sp, int nseg,
+                                          int seg0, int t0, int wave, int lane) {
     const int T = p.T;
-    const int64_t HD = int64_t(p.H) * D;
-    const int pc = lane % DC;
-    const bool fast = T >= KT;  // a tile then spans at most two segments
-    const int seg1 = seg0 + 1 < nseg ? seg0 + 1 : seg0;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = wave * 16 + RPI * i + lane / DC;
-      int t = t0 + row;
-      int seg = seg0;
-      if (fast) {
-        if (t >= T) {
-          t -= T;
-          seg = seg0 + 1;
-        }
+      int tt = t0 + row;
+      if constexpr (!kSmallT) {
+        // T >= KT: the tile spans at most this segment and the next
+        const bool second = tt >= T;
+        tt = second ? tt - T : tt;
+        kp[i] = second ? sp.k[1] : sp.k[0];
+        vp[i] = second ? sp.v[1] : sp.v[0];
+        hoff[i] = second ? sp.hoff[1] : sp.hoff[0];
       } else {
-        while (t >= T) {
-          t -= T;
-          ++seg;
+        int sg = seg0;
+        while (tt >= T) {
+          tt -= T;
+          ++sg;
         }
+        sg = sg < nseg ? sg : 0;
+        kp[i] = st.kbase[sg];
+        vp[i] = st.vbase[sg];
+        hoff[i] = st.hist_off[sg];
       }
-      const bool valid = seg < nseg;
-      const int sg = valid ? seg : seg1;
-      const int hoff = st.hist_off[sg];
-      int64_t ridx = t;
-      if (hoff >= 0) {
-        const uint32_t pg = __umulhi(uint32_t(t), p.p_magic);
-        const int slot = t - int(pg) * p.P;
-        ridx = int64_t(pages[hoff + int(pg)]) * p.P + slot;
-      }
-      const int koff = (pc ^ kswz<D>(row)) * 8;
-      const int voff = (pc ^ vswz(row)) * 8;
-      uint16_t* kdst = kbuf + (wave * 16 + RPI * i) * D;
-      uint16_t* vdst = vbuf + (wave * 16 + RPI * i) * D;
-      if (valid) {
-        __builtin_amdgcn_global_load_lds(st.kbase[sg] + ridx * HD + koff, (lds_void*)kdst, 16, 0,
-                                         0);
-        __builtin_amdgcn_global_load_lds(st.vbase[sg] + ridx * HD + voff, (lds_void*)vdst, 16, 0,
-                                         0);
-      } else {
-        // past the last key: zero V (P is 0 there and 0 * garbage may be NaN)
-        *reinterpret_cast<uint4*>(vdst + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(kdst + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
-      }
+      t[i] = tt;
+      pg[i] = int(__umulhi(uint32_t(tt), p.p_magic));
+      page[i] = pages[hoff[i] >= 0 ? hoff[i] + pg[i] : 0];
     }
+  }
+
+  __device__ __forceinline__ void emit(int i, const AttnParams& p, uint16_t* kbuf,
+                                       uint16_t* vbuf, int wave, int lane) const {
+    const uint32_t HD = uint32_t(p.H) * D;
+    const int pc = lane % DC;
+    const int row = wave * 16 + RPI * i + lane / DC;
+    // row of the source tensor: pool row page*P + (t - pg*P) for history, t for
+    // live chunks (pool rows fit in 31 bits, checked on the host)
+    const uint32_t ridx = uint32_t(t[i]) + (hoff[i] >= 0 ? uint32_t(page[i] - pg[i]) * p.P : 0u);
+    const uint64_t off = uint64_t(ridx) * HD;
+    uint16_t* kdst = kbuf + (wave * 16 + RPI * i) * D;
+    uint16_t* vdst = vbuf + (wave * 16 + RPI * i) * D;
+    __builtin_amdgcn_global_load_lds(kp[i] + off + (pc ^ kswz<D>(row)) * 8, (lds_void*)kdst, 16,
+                                     0, 0);
+    __builtin_amdgcn_global_load_lds(vp[i] + off + (pc ^ vswz(row)) * 8, (lds_void*)vdst, 16, 0,
+                                     0);
   }
 };
 
-template <int D>
+template <int D, bool kSmallT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 attn_tick_kernel(const AttnParams p) {
@@ -286,53 +328,80 @@ attn_tick_kernel(const AttnParams p) {
   const int vcx = 2 * ((lane >> 4) & 1) + ((a16 >> 1) & 1);
   const int vsub = 4 * (a16 & 1);
 
-  int seg0 = 0, t0 = 0;
-  DirectLoader<D>::issue(p, pages_lds, seg_tab, nseg, seg0, t0, k_lds0, v_lds0, wave, lane);
+  // position (segment, token) of the next tile to load, and its segment pair
+  int seg_n = 0, t_n = 0;
+  SegPair sp;
+  load_seg_pair(seg_tab, nseg, 0, sp);
+  auto advance = [&]() {
+    t_n += KT;
+    while (t_n >= T) {
+      t_n -= T;
+      ++seg_n;
+    }
+    if (!kSmallT && seg_n != sp.seg0) load_seg_pair(seg_tab, nseg, seg_n, sp);
+  };
+  {
+    TileLoads<D, kSmallT> ld;
+    ld.prepare(p, pages_lds, seg_tab, sp, nseg, seg_n, t_n, wave, lane);
+#pragma unroll
+    for (int i = 0; i < TileLoads<D, kSmallT>::NI; ++i) ld.emit(i, p, k_lds0, v_lds0, wave, lane);
+    advance();
+  }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's tile loads have landed
   __syncthreads();
 
-  // One tile: prefetch tile it+1 into (kn, vn) while computing tile it from (kb, vb).
+  // One tile: compute tile it from (kb, vb); the loads of tile it+1 (dummy rows
+  // past the end) go to (kn, vn), spread between the S^T MFMAs.
   auto step = [&](int it, const uint16_t* kb, const uint16_t* vb, uint16_t* kn, uint16_t* vn) {
-    if (it + 1 < ntiles) {
-      t0 += KT;
-      while (t0 >= T) {
-        t0 -= T;
-        ++seg0;
-      }
-      DirectLoader<D>::issue(p, pages_lds, seg_tab, nseg, seg0, t0, kn, vn, wave, lane);
-    }
-
-    if (wave_active) {
-      // ---- S^T = K Q^T : two 32-key blocks, K operands one step ahead ------
+    constexpr int NI = TileLoads<D, kSmallT>::NI;
+    TileLoads<D, kSmallT> ld;
+    if (!wave_active) {
+      ld.prepare(p, pages_lds, seg_tab, sp, nseg, seg_n, t_n, wave, lane);
+      advance();
+#pragma unroll
+      for (int i = 0; i < NI; ++i) ld.emit(i, p, kn, vn, wave, lane);
+    } else {
+      // ---- S^T = K Q^T: two 32-key blocks; K operands two k-steps ahead, one
+      // row of next-tile loads after each k-step (scheduling fences keep the
+      // interleave)
       auto kload = [&](int kk, bf16x8* dst) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
-          dst[blk] = *reinterpret_cast<const bf16x8*>(kb + (krow0 + 32 * blk) * D +
-                                                      ((2 * kk + g) ^ kx) * 8);
+          dst[blk] = *reinterpret_cast<const bf16x8*>(
+              kb + ((krow0 + 32 * blk) * D + ((2 * kk + g) ^ kx) * 8));
       };
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      bf16x8 ka[3][2];
+      kload(0, ka[0]);
+      kload(1, ka[1]);
+      ld.prepare(p, pages_lds, seg_tab, sp, nseg, seg_n, t_n, wave, lane);
+      advance();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
+                                                              0, 0, 0);
+        if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
+        if (kk < NI) ld.emit(kk, p, kn, vn, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // V^T operand of one 16-key step for all DB blocks: two transposed reads each
+      // (Each LDS address is one offset added to the buffer: the compiler tags
+      // LDS accesses with the buffer they touch only through a short chain of
+      // address steps, and untagged reads would wait for every tile load.)
       auto vload = [&](int kk, bf16x8* dst) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* a0 = vb + (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
+          const int e0 = (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(a0));
+              (__attribute__((address_space(3))) i16x4*)(vb + e0));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(a0 + 4 * D));
+              (__attribute__((address_space(3))) i16x4*)(vb + (e0 + 4 * D)));
           dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       };
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      bf16x8 ka[2][2];
-      kload(0, ka[0]);
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        if (kk + 1 < KS) kload(kk + 1, ka[(kk + 1) & 1]);
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk & 1][blk], qf[kk], sacc[blk],
-                                                              0, 0, 0);
-      }
       // the first V^T operands load while the softmax runs
       bf16x8 va[2][DB];
       vload(0, va[0]);
@@ -481,21 +550,22 @@ void plan_xcd_order(const StagePlan& pl, int H, AttnParams& p, int64_t& blocks) 
 // table is sized to the call and may use up to 32 KB more.
 constexpr size_t kMaxPageTableLds = 32 * 1024;
 
-template <int D>
+// Chunks of at least one tile (T >= 64) put every tile in at most two segments.
+template <int D, bool kSmallT>
 int32_t launch_attn(const AttnParams& p, unsigned blocks, size_t dyn_lds, hipStream_t stream) {
-  // The dynamic-LDS limit is raised once per device.
+  // The dynamic-LDS limit is raised once per device and instantiation.
   static std::atomic<uint64_t> attr_set{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "wf_attn_tick: hipGetDevice");
   const uint64_t bit = uint64_t(1) << (dev & 63);
   if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_tick_kernel<D>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_tick_kernel<D, kSmallT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxPageTableLds));
     if (e != hipSuccess) return hip_fail(e, "wf_attn_tick: hipFuncSetAttribute");
     attr_set.fetch_or(bit, std::memory_order_acq_rel);
   }
-  attn_tick_kernel<D><<<dim3(blocks), NTHREADS, dyn_lds, stream>>>(p);
+  attn_tick_kernel<D, kSmallT><<<dim3(blocks), NTHREADS, dyn_lds, stream>>>(p);
   return WF_OK;
 }
 
@@ -543,6 +613,9 @@ int32_t validate_tick(const wf_tick_desc* d) {
                   static_cast<long long>(int64_t(d->n_hist) * ppc), d->num_pages);
     if (int64_t(d->T) * d->P >= (int64_t(1) << 32))
       return fail(WF_EUNSUPPORTED, "wf_attn_tick: T * P too large");
+    if (int64_t(d->num_pages) * d->P >= (int64_t(1) << 31))
+      return fail(WF_EUNSUPPORTED, "wf_attn_tick: num_pages * P = %lld pool rows exceed 2^31",
+                  static_cast<long long>(int64_t(d->num_pages) * d->P));
   }
   return WF_OK;
 }
@@ -608,14 +681,18 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
     plan_xcd_order(pl, d.H, p, blocks);
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
-    const size_t dyn_lds = size_t(p.n_page_ids) * sizeof(int32_t);
+    // at least one entry: tile rows of live segments still read (and ignore) entry 0
+    const size_t dyn_lds = size_t(std::max(p.n_page_ids, 1)) * sizeof(int32_t);
     if (dyn_lds > kMaxPageTableLds)
       return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %zu bytes of LDS",
                   p.n_page_ids, kMaxPageTableLds);
+    const bool small_t = d.T < KT;
     if (d.D == 128)
-      st = launch_attn<128>(p, unsigned(blocks), dyn_lds, stream);
+      st = small_t ? launch_attn<128, true>(p, unsigned(blocks), dyn_lds, stream)
+                   : launch_attn<128, false>(p, unsigned(blocks), dyn_lds, stream);
     else
-      st = launch_attn<64>(p, unsigned(blocks), dyn_lds, stream);
+      st = small_t ? launch_attn<64, true>(p, unsigned(blocks), dyn_lds, stream)
+                   : launch_attn<64, false>(p, unsigned(blocks), dyn_lds, stream);
     if (st != WF_OK) return st;
     return check_launch("wf_attn_tick");
   } catch (...) {
