@@ -202,7 +202,10 @@ def attention_tick(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                 l = p.sum(axis=1, keepdims=True)
                 out[s][r0:r0 + len(rr), hi, :] = (p @ V) / l
 
-    nthreads = threads or min(len(heads), len(os.sched_getaffinity(0)))
+    # Heads run on a thread pool only when each head is heavy; for a few sampled
+    # rows the matrix products' own threads are faster than nesting pools.
+    nthreads = threads or (min(len(heads), len(os.sched_getaffinity(0)))
+                           if len(rows) >= 1024 else 1)
     if nthreads <= 1 or len(heads) == 1:
         for hi in range(len(heads)):
             one_head(hi)

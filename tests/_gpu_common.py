@@ -116,13 +116,15 @@ def oracle_tick(t: Tick, stages=None, heads=None, rows=None) -> Dict[int, np.nda
 def compare(got_o: torch.Tensor, want: Dict[int, np.ndarray], heads=None, rows=None,
             atol=ATOL, rel=REL_L2, label="") -> float:
     """Per (stage, head): max-abs <= atol and rel-L2 <= rel. Returns the worst rel-L2."""
+    if rows is not None:  # select the sampled rows on the device before the copy
+        idx = torch.as_tensor(np.asarray(rows), dtype=torch.long, device=got_o.device)
+        got_o = got_o.index_select(1, idx)
     g = got_o.float().cpu().numpy().astype(np.float64)
     worst = 0.0
     for s, w in want.items():
         H = w.shape[1]
         hs = list(range(H)) if heads is None else list(heads)
-        rr = np.arange(w.shape[0]) if rows is None else np.asarray(rows)
-        gs = g[s][rr][:, hs, :]
+        gs = g[s][:, hs, :]
         assert np.isfinite(gs).all(), f"{label} stage {s}: non-finite outputs"
         for hi in range(len(hs)):
             d = gs[:, hi] - w[:, hi]

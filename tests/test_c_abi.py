@@ -1,0 +1,307 @@
+"""Host-side checks of the C-ABI library (no GPU needed): the shared library
+loads and exports every function include/wf_attn.h declares; the C page table
+matches the oracle's FIFO window model call for call, also under AddressSanitizer
+and UBSan; argument validation rejects bad calls before touching the device;
+the useful-FLOP count equals the oracle's mask count."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.page_model import PageModelError
+from wavefront_causal_attention_wf_amd import build_lib, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wf_attn.h")
+
+CODES = {"EINVAL": -1, "ENOMEM": -2, "EHIP": -3, "EUNSUPPORTED": -4, "ESTATE": -5}
+
+
+def _wfattn():
+    if not os.path.exists(build_lib.LIB_PATH):
+        build_lib.build()
+    from wavefront_causal_attention_wf_amd import wfattn
+    return wfattn
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(wf_[a-z0-9_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_exports_every_header_function():
+    wf = _wfattn()
+    names = header_functions()
+    assert len(names) >= 13, names
+    lib = wf.library()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in wf_attn.h but not exported"
+    assert sorted(wf.EXPORTED_SYMBOLS) == names
+    assert wf.abi_version() == 1
+    nm = subprocess.run(["nm", "-D", "--defined-only", build_lib.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r" T (wf_[a-z0-9_]+)$", nm, flags=re.M))
+    assert exported == set(names)
+
+
+# ---------------------------------------------------------------------------
+# page table: C vs oracle model
+# ---------------------------------------------------------------------------
+def _schedule(wf, N, P, T, W, pin, order, ticks):
+    c = wf.PageTable(N, P, T, W, pin_anchor=pin, initial_free_order=order)
+    m = oracle.FifoPageModel(N, P, T, W, pin_anchor=pin, initial_free_order=order)
+    assert c.ppc == m.ppc
+    for k in range(ticks):
+        assert c.alloc_chunk().tolist() == m.alloc_chunk()
+        assert c.num_free() == m.num_free()
+        assert c.commit().tolist() == m.commit()
+        assert c.export().tolist() == m.export()
+        assert c.num_free() == m.num_free()
+    c.close()
+
+
+@pytest.mark.parametrize("pin", [False, True])
+def test_page_table_matches_model_rollout(pin):
+    """120-tick rollout at the 4680-token, 64-token-page shape (74 pages per
+    chunk, the last one ragged), window 3, permuted pool of 4096 pages."""
+    wf = _wfattn()
+    cfg = inputs.CONFIGS["wan13_4step"]
+    order = inputs.initial_free_order(cfg)
+    _schedule(wf, cfg.num_pages, cfg.P, cfg.T, 3, pin, order, 120)
+
+
+@pytest.mark.parametrize("N,P,T,W", [(12, 16, 64, 2), (9, 16, 40, 2), (64, 16, 17, 5), (4, 4, 4, 1)])
+def test_page_table_matches_model_small(N, P, T, W):
+    wf = _wfattn()
+    order = np.random.default_rng(N * 31 + W).permutation(N)
+    _schedule(wf, N, P, T, W, False, order, 30)
+    if W >= 2:
+        _schedule(wf, N, P, T, W, True, None, 30)
+
+
+def test_page_table_errors_leave_state_unchanged():
+    wf = _wfattn()
+    for bad in [(0, 16, 64, 2), (8, 0, 64, 2), (8, 16, 0, 2), (8, 16, 64, 0)]:
+        with pytest.raises(wf.WfError) as e:
+            wf.PageTable(*bad)
+        assert e.value.status == CODES["EINVAL"]
+    with pytest.raises(wf.WfError) as e:
+        wf.PageTable(8, 16, 64, 1, pin_anchor=True)
+    assert e.value.status == CODES["EINVAL"]
+    with pytest.raises(wf.WfError) as e:
+        wf.PageTable(4, 16, 64, 2, initial_free_order=[0, 1, 1, 3])
+    assert e.value.status == CODES["EINVAL"]
+    with pytest.raises(wf.WfError) as e:
+        wf.PageTable(4, 16, 64, 2, initial_free_order=[0, 1, 2, 4])
+    assert e.value.status == CODES["EINVAL"]
+
+    pt = wf.PageTable(10, 16, 40, 2)  # 3 pages per chunk
+    with pytest.raises(wf.WfError) as e:
+        pt.commit()
+    assert e.value.status == CODES["ESTATE"]
+    ids = pt.alloc_chunk()
+    with pytest.raises(wf.WfError) as e:
+        pt.alloc_chunk()
+    assert e.value.status == CODES["ESTATE"]
+    assert pt.num_free() == 7
+    pt.commit()
+    pt.alloc_chunk()
+    pt.commit()
+    pt.alloc_chunk()
+    before = (pt.export().tolist(), pt.num_free())
+    pt.commit()  # evicts the first chunk
+    assert pt.export().tolist()[0] != ids.tolist()
+    pt.alloc_chunk()
+    pt.commit()
+    # 10 pages, window 2: 6 resident, 4 free; one more live chunk leaves 1
+    pt.alloc_chunk()
+    assert pt.num_free() == 1
+    pt.commit()
+    assert pt.num_free() == 4
+    del before
+
+    small = wf.PageTable(5, 16, 40, 2)  # room for one chunk, then ENOMEM
+    small.alloc_chunk()
+    small.commit()
+    state = (small.export().tolist(), small.num_free())
+    with pytest.raises(wf.WfError) as e:
+        small.alloc_chunk()
+    assert e.value.status == CODES["ENOMEM"]
+    assert (small.export().tolist(), small.num_free()) == state
+    assert "free pages" in wf.last_error()
+
+
+def _driver_script(N, P, T, W, pin, order, ticks, caps):
+    lines = [f"create {N} {P} {T} {W} {int(pin)} {1 if order is not None else 0}"
+             + ("" if order is None else " " + " ".join(str(int(x)) for x in order)), "ppc"]
+    for k in range(ticks):
+        cap_a, cap_c, cap_e = caps(k)
+        lines += [f"alloc {cap_a}", "free", f"commit {cap_c}", f"export {cap_e}", "free"]
+    return "\n".join(lines) + "\n"
+
+
+def _model_replay(N, P, T, W, pin, order, ticks, caps):
+    """Expected driver output, from the oracle model and the documented error rules."""
+    out = []
+    try:
+        m = oracle.FifoPageModel(N, P, T, W, pin_anchor=pin, initial_free_order=order)
+        out.append("create 0")
+    except PageModelError as e:
+        return [f"create {CODES[e.code]}"]
+    out.append(f"ppc 0 {m.ppc}")
+    for k in range(ticks):
+        cap_a, cap_c, cap_e = caps(k)
+        if cap_a < m.ppc:
+            out.append(f"alloc {CODES['EINVAL']}")
+        else:
+            try:
+                ids = m.alloc_chunk()
+                out.append("alloc 0 " + " ".join(map(str, ids)))
+            except PageModelError as e:
+                out.append(f"alloc {CODES[e.code]}")
+        out.append(f"free 0 {m.num_free()}")
+        will_evict = m.live is not None and len(m.history) + 1 > m.window
+        if m.live is None:
+            out.append(f"commit {CODES['ESTATE']} -1")
+        elif will_evict and 0 < cap_c < m.ppc:
+            out.append(f"commit {CODES['EINVAL']} -1")
+        else:
+            ev = m.commit()
+            shown = " " + " ".join(map(str, ev)) if (cap_c > 0 and ev) else ""
+            out.append(f"commit 0 {len(ev)}{shown}")
+        need = len(m.history) * m.ppc
+        if need > 0 and cap_e < need:
+            out.append(f"export {CODES['EINVAL']} -1")
+        else:
+            flat = [p for c in m.export() for p in c]
+            out.append(f"export 0 {len(m.history)}" + ("".join(f" {p}" for p in flat)))
+        out.append(f"free 0 {m.num_free()}")
+    return out
+
+
+def test_page_table_under_sanitizers(tmp_path):
+    """The page table built with g++ -fsanitize=address,undefined, driven through
+    a long schedule with interleaved error calls; output equals the model's."""
+    exe = str(tmp_path / "page_table_driver")
+    try:
+        build_lib.build_host_page_table_test(exe)
+    except RuntimeError as e:
+        pytest.skip(f"sanitizer build unavailable: {e}")
+    cases = [
+        (4096, 64, 4680, 3, False, inputs.initial_free_order(inputs.CONFIGS["wan13_4step"]), 60,
+         lambda k: (74, 74, 4 * 74)),
+        (4096, 64, 4680, 3, True, None, 60, lambda k: (74, 74 if k % 3 else 0, 4 * 74)),
+        (10, 16, 40, 2, False, np.random.default_rng(3).permutation(10), 40,
+         lambda k: (3 if k % 5 else 2, 3 if k % 7 else 1, 6 if k % 4 else 3)),
+        (5, 16, 40, 2, True, None, 12, lambda k: (3, 3, 9)),
+    ]
+    for N, P, T, W, pin, order, ticks, caps in cases:
+        script = _driver_script(N, P, T, W, pin, order, ticks, caps)
+        res = subprocess.run([exe], input=script, capture_output=True, text=True, timeout=120)
+        assert res.returncode == 0, res.stderr[-2000:]
+        got = res.stdout.strip().splitlines()
+        want = _model_replay(N, P, T, W, pin, order, ticks, caps)
+        assert got == want
+
+
+# ---------------------------------------------------------------------------
+# validation (returns before any device work) and the FLOP count
+# ---------------------------------------------------------------------------
+def _desc(wf, **kw):
+    a = dict(S=4, active_mask=0x1F, T=4680, H=12, D=128, scale=1.0 / np.sqrt(128), q=None, k=None,
+             v=None, o=None, k_pool=None, v_pool=None, num_pages=4096, P=64, hist_pages=None,
+             n_hist=0)
+    a.update(kw)
+    return wf.make_tick_desc(a["S"], a["active_mask"], a["T"], a["H"], a["D"], a["scale"], a["q"],
+                             a["k"], a["v"], a["o"], a["k_pool"], a["v_pool"], a["num_pages"],
+                             a["P"], a["hist_pages"], a["n_hist"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=8, active_mask=1), "EINVAL"),
+    (dict(S=-1, active_mask=0), "EINVAL"),
+    (dict(S=2, active_mask=0x10), "EINVAL"),
+    (dict(T=-1), "EINVAL"),
+    (dict(H=0), "EINVAL"),
+    (dict(D=96), "EUNSUPPORTED"),
+    (dict(scale=0.0), "EINVAL"),
+    (dict(scale=float("inf")), "EINVAL"),
+    (dict(n_hist=-1), "EINVAL"),
+    (dict(n_hist=28), "EUNSUPPORTED"),
+])
+def test_tick_validation(kw, code):
+    wf = _wfattn()
+    d = _desc(wf, **kw)
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_attn_tick_desc(d, stream=0)
+    assert e.value.status == CODES[code]
+    with pytest.raises(wf.WfError) as e:
+        wf.tick_useful_flops_desc(d)
+    assert e.value.status == CODES[code]
+
+
+def test_tick_validation_pointers_and_pool():
+    wf = _wfattn()
+    # missing tensors for a non-empty tick
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_attn_tick_desc(_desc(wf), stream=0)
+    assert e.value.status == CODES["EINVAL"]
+    fake = 1 << 20  # never dereferenced: validation fails first
+    base = dict(q=fake, k=fake, v=fake, o=fake)
+    with pytest.raises(wf.WfError) as e:  # misaligned q
+        wf.wf_attn_tick_desc(_desc(wf, **{**base, "q": fake + 2}), stream=0)
+    assert e.value.status == CODES["EINVAL"]
+    with pytest.raises(wf.WfError) as e:  # history without pools
+        wf.wf_attn_tick_desc(_desc(wf, **base, n_hist=3), stream=0)
+    assert e.value.status == CODES["EINVAL"]
+    pools = dict(k_pool=fake, v_pool=fake, hist_pages=fake)
+    with pytest.raises(wf.WfError) as e:  # page size not a multiple of 16
+        wf.wf_attn_tick_desc(_desc(wf, **base, **pools, n_hist=3, P=40), stream=0)
+    assert e.value.status == CODES["EINVAL"]
+    with pytest.raises(wf.WfError) as e:  # pool too small for the history
+        wf.wf_attn_tick_desc(_desc(wf, **base, **pools, n_hist=3, num_pages=100), stream=0)
+    assert e.value.status == CODES["EINVAL"]
+    with pytest.raises(wf.WfError) as e:  # page table larger than the LDS budget
+        wf.wf_attn_tick_desc(_desc(wf, **base, **pools, n_hist=3, P=16, T=60000,
+                                   num_pages=40000), stream=0)
+    assert e.value.status == CODES["EUNSUPPORTED"]
+    # empty ticks are accepted without touching the device
+    wf.wf_attn_tick_desc(_desc(wf, T=0), stream=0)
+    wf.wf_attn_tick_desc(_desc(wf, active_mask=0), stream=0)
+
+
+def test_store_gather_validation():
+    wf = _wfattn()
+    lib = wf.library()
+    fake = 1 << 20
+    # NULL sources, bad sizes, misalignment: all rejected on the host
+    assert lib.wf_store_paged(None, fake, fake, fake, fake, 64, 2, 64, 8, 16, None) == CODES["EINVAL"]
+    assert lib.wf_store_paged(fake, fake, fake, fake, fake, 64, 1, 4, 8, 16, None) == CODES["EINVAL"]
+    assert lib.wf_store_paged(fake, fake, fake, fake, fake, -1, 2, 64, 8, 16, None) == CODES["EINVAL"]
+    assert lib.wf_store_paged(fake + 2, fake, fake, fake, fake, 64, 2, 64, 8, 16, None) == CODES["EINVAL"]
+    assert lib.wf_store_paged(fake, fake, fake, fake, fake, 64, 2, 64, 2, 16, None) == CODES["EINVAL"]
+    assert lib.wf_gather_paged(fake, fake, None, 1, fake, fake, 64, 2, 64, 8, 16, None) == CODES["EINVAL"]
+    assert lib.wf_gather_paged(fake, fake, fake, -1, fake, fake, 64, 2, 64, 8, 16, None) == CODES["EINVAL"]
+    # zero-size calls are no-ops
+    assert lib.wf_store_paged(None, None, None, None, None, 0, 2, 64, 8, 16, None) == 0
+    assert lib.wf_gather_paged(None, None, None, 3, None, None, 0, 2, 64, 8, 16, None) == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan13_4step", "wan13_5step", "wan14b_4step"])
+def test_useful_flops_matches_oracle(name):
+    wf = _wfattn()
+    c = inputs.CONFIGS[name]
+    full = (1 << (c.S + 1)) - 1
+    for mask in {full, full & ~1, 1 << c.S, full >> 1, 0b101 & full}:
+        got = wf.wf_tick_useful_flops(c.S, mask, c.T, c.H, c.D, c.n_hist, P=c.P,
+                                      num_pages=c.num_pages)
+        want = oracle.useful_flops(c.S, mask, c.n_hist, c.T, c.H, c.D)
+        assert got == want, (name, mask)
+    if name == "wan13_4step":
+        assert abs(wf.wf_tick_useful_flops(c.S, full, c.T, c.H, c.D, c.n_hist, P=c.P,
+                                           num_pages=c.num_pages) - 4.037e12) < 1e9

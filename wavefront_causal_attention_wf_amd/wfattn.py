@@ -92,6 +92,11 @@ def library():
     return _lib
 
 
+def last_error() -> str:
+    """Text of the calling thread's last failed call."""
+    return _lib.wf_last_error().decode(errors="replace")
+
+
 # ---------------------------------------------------------------------------
 # marshalling helpers
 # ---------------------------------------------------------------------------
@@ -258,6 +263,11 @@ def wf_tick_useful_flops(S: int, active_mask: int, T: int, H: int, D: int, n_his
                        fake if n_hist else None, fake if n_hist else None,
                        max(num_pages, n_hist * -(-T // P)) if n_hist else 0, P if n_hist else 0,
                        fake if n_hist else None, n_hist, hist_first)
+    return tick_useful_flops_desc(d)
+
+
+def tick_useful_flops_desc(desc: WfTickDesc) -> float:
     out = ctypes.c_double()
-    _check(_lib.wf_tick_useful_flops(ctypes.byref(d), ctypes.byref(out)), "wf_tick_useful_flops")
+    _check(_lib.wf_tick_useful_flops(ctypes.byref(desc), ctypes.byref(out)),
+           "wf_tick_useful_flops")
     return out.value
