@@ -50,12 +50,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KT = 64;              // keys per tile
-constexpr int NWAVES = 4;
+#ifndef WF_NWAVES
+#define WF_NWAVES 8
+#endif
+constexpr int NWAVES = WF_NWAVES;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int QROWS = 32 * NWAVES;  // query rows per workgroup
 constexpr float kLazyTau = 8.0f;    // raise the running max only beyond this (log2 units)
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kXcdTable = 512;      // max (stage, head) groups in the XCD table
+// History page table held in LDS (ids of all history pages of one tick).
+constexpr int kMaxPageIds = 8192;
 
 struct AttnParams {
   const uint16_t* q;
@@ -66,11 +71,13 @@ struct AttnParams {
   const uint16_t* v_pool;
   const int32_t* hist_pages;
   int32_t T, H, P, ppc;
+  int32_t tps;            // tiles per chunk, ceil(T / 64)
+  int32_t t_last;         // keys in a chunk's last tile, T - 64 * (tps - 1)
   uint32_t p_magic;       // floor(2^32 / P) + 1: t / P == umulhi(t, p_magic) for t*P < 2^32
   float c;                // scale * log2(e)
   int32_t ntq;            // query tiles per chunk
   int32_t items_per_stage;  // H * ntq
-  int32_t n_page_ids;     // n_hist * ppc entries of hist_pages (copied to LDS)
+  int32_t n_page_ids;     // n_hist * ppc entries of hist_pages
   // XCD-aware order: block b runs on XCD b % 8 (round-robin dispatch); its
   // (b / 8)-th item is query tile (b / 8) % ntq of group xcd_groups[x][(b / 8) / ntq],
   // group = rank * H + head. Blocks past an XCD's list exit at once.
@@ -78,10 +85,12 @@ struct AttnParams {
   int32_t xcd_stride;
   int16_t xcd_n[kNumXcd];
   int16_t xcd_groups[kXcdTable];
-  int8_t stage_of_rank[WF_MAX_STAGES];  // work order, heaviest stage first
-  int8_t nseg[WF_MAX_STAGES];
+  // (32-bit entries: the kernel reads them with scalar loads, which are
+  // dword-granular; a narrower type would turn them into vector loads)
+  int32_t stage_of_rank[WF_MAX_STAGES];  // work order, heaviest stage first
+  int32_t nseg[WF_MAX_STAGES];
   // per stage: segment code >= 0 is live slot j, < 0 is history chunk (-code - 1)
-  int8_t seg[WF_MAX_STAGES][WF_MAX_SEGMENTS];
+  int32_t seg[WF_MAX_STAGES][WF_MAX_SEGMENTS];
 };
 
 __device__ __forceinline__ int swap_bits23(int r) {
@@ -114,153 +123,168 @@ __device__ __forceinline__ float xlane32_sum(float x) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Segments of the stage's virtual key sequence, resolved once per workgroup into
-// LDS: base row pointers of K and V for head h, and for history chunks the index
-// of the chunk's first page id in the page table (-1 for live chunks).
-struct SegTable {
-  const uint16_t* kbase[WF_MAX_SEGMENTS];
-  const uint16_t* vbase[WF_MAX_SEGMENTS];
-  int32_t hist_off[WF_MAX_SEGMENTS];
-};
-
-template <int D>
-__device__ __forceinline__ void fill_seg_table(const AttnParams& p, int s, int h, SegTable& st) {
-  const int i = threadIdx.x;
-  if (i < p.nseg[s]) {
-    const int code = p.seg[s][i];
-    if (code >= 0) {
-      const int64_t off = (int64_t(code) * p.T * p.H + h) * D;
-      st.kbase[i] = p.k + off;
-      st.vbase[i] = p.v + off;
-      st.hist_off[i] = -1;
-    } else {
-      st.kbase[i] = p.k_pool + int64_t(h) * D;
-      st.vbase[i] = p.v_pool + int64_t(h) * D;
-      st.hist_off[i] = (-code - 1) * p.ppc;
-    }
-  }
+// LDS destination of a direct tile load, passed through an empty asm so that the
+// compiler no longer knows which LDS buffer the load writes. It then inserts no
+// waits of its own for these loads before LDS reads (which it would place
+// conservatively, draining loads meant to stay in flight); the kernel orders
+// them itself with tile_barrier(). Every LDS read is of a buffer whose loads
+// have landed and been published by that barrier.
+__device__ __forceinline__ lds_void* opaque_lds(const uint16_t* p) {
+  uint32_t a = uint32_t(reinterpret_cast<uintptr_t>((const lds_void*)p));
+  asm volatile("" : "+s"(a));
+  return reinterpret_cast<lds_void*>(uintptr_t(a));
 }
 
-// The (at most two, when T >= 64) segments a tile touches, in scalar
-// registers; refreshed only when the tile start moves into a new segment.
-struct SegPair {
-  const uint16_t* k[2];
-  const uint16_t* v[2];
-  int32_t hoff[2];
-  int32_t seg0;
-};
+typedef const __attribute__((address_space(4))) int32_t* const_i32p;
 
-__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
-  const uint64_t x = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(x >> 32));
-  return reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
-}
+// Tile loads straight from global memory into LDS (16 bytes per lane).
+//
+// The stage's key sequence is walked segment by segment (a segment = one chunk
+// of T keys: a history chunk through its pages, or a live chunk), each cut into
+// tps = ceil(T / 64) tiles of 64 keys; only the last tile of a segment is
+// partial (its rows past the chunk re-read the chunk's last key and are masked
+// in the softmax). Wave w fills rows [RW*w, RW*w + RW) of the K and V tiles; one
+// wave instruction writes 1 KB = RPI whole rows, lane l landing at chunk l % DC
+// of row l / DC, so each lane fetches the logical chunk that the row swizzle
+// maps to that position.
+//
+// kFast (page size a multiple of 64, and every live chunk): a tile is 64
+// consecutive rows of one page or chunk, so its source is one uniform base
+// (scalar registers; the page id comes from a scalar load of the page table)
+// plus a fixed per-lane offset, and a tile costs no vector address math.
+// Otherwise history tiles resolve each lane's page through the page table in
+// LDS. prepare() resolves the next tile and advances the cursor; emit(i) issues
+// the two loads of row group i, so the caller can spread them between MFMAs.
+// Past the last tile the cursor reads tile 0 again (finite, masked).
+template <int D, bool kFast>
+struct TileLoader {
+  static constexpr int DC = D / 8;        // 16-byte chunks per row
+  static constexpr int RPI = 64 / DC;     // rows per wave instruction
+  static constexpr int RW = KT / NWAVES;  // tile rows loaded by each wave
+  static constexpr int NI = RW / RPI;     // instructions per wave per tensor
 
-// Segments past the end of the context map to segment 0: tile rows beyond the
-// last key then read a finite row of the first segment; their scores are masked
-// to -inf, so their P is exactly 0 and they add nothing.
-__device__ __forceinline__ void load_seg_pair(const SegTable& st, int nseg, int seg0,
-                                              SegPair& sp) {
-  const int s0 = seg0 < nseg ? seg0 : 0;
-  const int s1 = seg0 + 1 < nseg ? seg0 + 1 : 0;
-  sp.k[0] = uniform_ptr(st.kbase[s0]);
-  sp.v[0] = uniform_ptr(st.vbase[s0]);
-  sp.hoff[0] = __builtin_amdgcn_readfirstlane(st.hist_off[s0]);
-  sp.k[1] = uniform_ptr(st.kbase[s1]);
-  sp.v[1] = uniform_ptr(st.vbase[s1]);
-  sp.hoff[1] = __builtin_amdgcn_readfirstlane(st.hist_off[s1]);
-  sp.seg0 = seg0;
-}
+  // per lane (bytes): row offset + swizzled column, full and last-tile rows
+  uint32_t koff[NI], voff[NI], koff_r[NI], voff_r[NI];
+  int32_t row[NI];
+  // cursor: next tile to resolve
+  int seg, m;
+  // resolved tile: uniform bases (+ the per-lane offsets), or for per-lane
+  // history tiles the pool bases of head h and each lane's pool row
+  const char* kb;
+  const char* vb;
+  bool ragged;
+  bool per_lane;
+  uint32_t prow[NI];
 
-// Tile loads straight from global memory into LDS (16 bytes per lane). Wave w
-// fills K and V rows [16w, 16w+16) of the tile; one wave instruction writes
-// 1 KB = RPI whole rows, lane l landing at chunk l % DC of row l / DC, so each
-// lane fetches the logical chunk that the row swizzle maps to that position.
-// prepare() resolves this lane's rows and starts the page-id reads; emit(i)
-// issues the two loads of row group i, so the caller can spread them between
-// MFMAs. Rows past the last key (every row, when there is no next tile) read
-// a row of segment 0 instead: every wave issues the same loads each tile, with
-// no branch.
-template <int D, bool kSmallT>
-struct TileLoads {
-  static constexpr int DC = D / 8;     // 16-byte chunks per row
-  static constexpr int RPI = 64 / DC;  // rows per wave instruction
-  static constexpr int NI = 16 / RPI;  // instructions per wave per tensor
-
-  const uint16_t* kp[NI];
-  const uint16_t* vp[NI];
-  int32_t t[NI];      // token within the segment's chunk
-  int32_t hoff[NI];   // first page-table entry of the chunk (-1: live chunk)
-  int32_t pg[NI];     // page of the token within the chunk
-  int32_t page[NI];   // pool page id (history chunks)
-
-  __device__ __forceinline__ void prepare(const AttnParams& p, const int32_t* pages,
-                                          const SegTable& st, const SegPair& sp, int nseg,
-                                          int seg0, int t0, int wave, int lane) {
-    const int T = p.T;
+  __device__ __forceinline__ void init(const AttnParams& p, int wave, int lane) {
+    const uint32_t row_bytes = uint32_t(p.H) * D * 2;
+    const int pc = lane % DC;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = wave * 16 + RPI * i + lane / DC;
-      int tt = t0 + row;
-      if constexpr (!kSmallT) {
-        // T >= KT: the tile spans at most this segment and the next
-        const bool second = tt >= T;
-        tt = second ? tt - T : tt;
-        kp[i] = second ? sp.k[1] : sp.k[0];
-        vp[i] = second ? sp.v[1] : sp.v[0];
-        hoff[i] = second ? sp.hoff[1] : sp.hoff[0];
-      } else {
-        int sg = seg0;
-        while (tt >= T) {
-          tt -= T;
-          ++sg;
-        }
-        sg = sg < nseg ? sg : 0;
-        kp[i] = st.kbase[sg];
-        vp[i] = st.vbase[sg];
-        hoff[i] = st.hist_off[sg];
+      row[i] = wave * RW + RPI * i + lane / DC;
+      const int rr = row[i] < p.t_last ? row[i] : p.t_last - 1;
+      const uint32_t kc = uint32_t(pc ^ kswz<D>(row[i])) * 16;
+      const uint32_t vc = uint32_t(pc ^ vswz(row[i])) * 16;
+      koff[i] = uint32_t(row[i]) * row_bytes + kc;
+      voff[i] = uint32_t(row[i]) * row_bytes + vc;
+      koff_r[i] = uint32_t(rr) * row_bytes + kc;
+      voff_r[i] = uint32_t(rr) * row_bytes + vc;
+    }
+    seg = 0;
+    m = 0;
+  }
+
+  __device__ __forceinline__ void prepare(const AttnParams& p, const int32_t* pages_lds, int s,
+                                          int h, int nseg) {
+    const int sg = seg < nseg ? seg : 0;
+    const int mm = seg < nseg ? m : 0;
+    const int code = p.seg[s][sg];
+    const int64_t t0 = int64_t(KT) * mm;  // first token of the tile within the chunk
+    ragged = mm == p.tps - 1;
+    per_lane = false;
+    if (code >= 0) {  // live chunk `code` of the tick's q/k/v
+      const int64_t e = ((int64_t(code) * p.T + t0) * p.H + h) * D;
+      kb = reinterpret_cast<const char*>(p.k + e);
+      vb = reinterpret_cast<const char*>(p.v + e);
+    } else if constexpr (kFast) {  // history chunk: one page holds the whole tile
+      const int c = -code - 1;
+      const int pid = ((const_i32p)p.hist_pages)[c * p.ppc + int(t0 / p.P)];
+      const int64_t prow = int64_t(pid) * p.P + (t0 % p.P);
+      const int64_t e = (prow * p.H + h) * D;
+      kb = reinterpret_cast<const char*>(p.k_pool + e);
+      vb = reinterpret_cast<const char*>(p.v_pool + e);
+    } else {  // history chunk, pages smaller than or not aligned to a tile
+      const int c = -code - 1;
+      per_lane = true;
+      kb = reinterpret_cast<const char*>(p.k_pool + int64_t(h) * D);
+      vb = reinterpret_cast<const char*>(p.v_pool + int64_t(h) * D);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int rr = ragged && row[i] >= p.t_last ? p.t_last - 1 : row[i];
+        const uint32_t tok = uint32_t(t0) + uint32_t(rr);
+        const uint32_t pg = __umulhi(tok, p.p_magic);
+        const int32_t pid = pages_lds[c * p.ppc + int(pg)];
+        // pool rows fit in 31 bits (checked on the host)
+        prow[i] = uint32_t(pid) * uint32_t(p.P) + (tok - pg * uint32_t(p.P));
       }
-      t[i] = tt;
-      pg[i] = int(__umulhi(uint32_t(tt), p.p_magic));
-      page[i] = pages[hoff[i] >= 0 ? hoff[i] + pg[i] : 0];
+    }
+    if (++m == p.tps) {
+      m = 0;
+      ++seg;
     }
   }
 
   __device__ __forceinline__ void emit(int i, const AttnParams& p, uint16_t* kbuf,
-                                       uint16_t* vbuf, int wave, int lane) const {
-    const uint32_t HD = uint32_t(p.H) * D;
-    const int pc = lane % DC;
-    const int row = wave * 16 + RPI * i + lane / DC;
-    // row of the source tensor: pool row page*P + (t - pg*P) for history, t for
-    // live chunks (pool rows fit in 31 bits, checked on the host)
-    const uint32_t ridx = uint32_t(t[i]) + (hoff[i] >= 0 ? uint32_t(page[i] - pg[i]) * p.P : 0u);
-    const uint64_t off = uint64_t(ridx) * HD;
-    uint16_t* kdst = kbuf + (wave * 16 + RPI * i) * D;
-    uint16_t* vdst = vbuf + (wave * 16 + RPI * i) * D;
-    __builtin_amdgcn_global_load_lds(kp[i] + off + (pc ^ kswz<D>(row)) * 8, (lds_void*)kdst, 16,
-                                     0, 0);
-    __builtin_amdgcn_global_load_lds(vp[i] + off + (pc ^ vswz(row)) * 8, (lds_void*)vdst, 16, 0,
-                                     0);
+                                       uint16_t* vbuf, int wave) const {
+    lds_void* kdst = opaque_lds(kbuf + (wave * RW + RPI * i) * D);
+    lds_void* vdst = opaque_lds(vbuf + (wave * RW + RPI * i) * D);
+    const char* ks;
+    const char* vs;
+    if (!kFast && per_lane) {
+      const uint32_t row_bytes = uint32_t(p.H) * D * 2;
+      const uint64_t o = uint64_t(prow[i]) * row_bytes;
+      const uint32_t rb = uint32_t(row[i]) * row_bytes;
+      ks = kb + o + (koff[i] - rb);
+      vs = vb + o + (voff[i] - rb);
+    } else {
+      ks = kb + (ragged ? koff_r[i] : koff[i]);
+      vs = vb + (ragged ? voff_r[i] : voff[i]);
+    }
+    __builtin_amdgcn_global_load_lds(ks, kdst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vs, vdst, 16, 0, 0);
   }
 };
 
-template <int D, bool kSmallT>
+// End of a tile: this wave's tile loads except the newest N have landed in LDS
+// and its LDS reads are done, then all waves meet. (__syncthreads() would also
+// wait for the newest loads: its fence drains every outstanding memory op.)
+// The asm's memory clobber keeps LDS accesses on their side of the barrier.
+template <int N>
+__device__ __forceinline__ void tile_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt: vmcnt(N) (bits 3:0 and 15:14), expcnt(7) (no wait), lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int D, bool kFast>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 attn_tick_kernel(const AttnParams p) {
   constexpr int KS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  // Two K and two V tile buffers as four distinct LDS objects: the loop is
-  // unrolled by two so that every access names its buffer statically, which
-  // lets the compiler see that reads of one buffer never alias the in-flight
-  // direct loads into the other (no spurious wait on those loads mid-tile).
+  using Loader = TileLoader<D, kFast>;
+  constexpr int NI = Loader::NI;
+  // Three K and three V tile buffers as six distinct LDS objects; the loop is
+  // unrolled by three so that every access names its buffer statically. Tile
+  // it+2 is loaded while tile it is computed.
   __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t k_lds1[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds2[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds0[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[KT * D];
-  __shared__ SegTable seg_tab;
-  extern __shared__ int32_t pages_lds[];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds2[KT * D];
+  __shared__ int32_t pages_lds[kFast ? 1 : kMaxPageIds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,14 +313,12 @@ attn_tick_kernel(const AttnParams p) {
   const int s = p.stage_of_rank[rank];
   const int nseg = p.nseg[s];
   const int T = p.T;
-  const int nkeys = nseg * T;
-  const int ntiles = (nkeys + KT - 1) / KT;
-  const int last_valid = nkeys - (ntiles - 1) * KT;
+  const int ntiles = nseg * p.tps;
 
-  // page table of the history into LDS (read by every tile's address math)
-  for (int i = tid; i < p.n_page_ids; i += NTHREADS) pages_lds[i] = p.hist_pages[i];
-  fill_seg_table<D>(p, s, h, seg_tab);
-  __syncthreads();
+  if constexpr (!kFast) {  // page table of the history into LDS
+    for (int i = tid; i < p.n_page_ids; i += NTHREADS) pages_lds[i] = p.hist_pages[i];
+    __syncthreads();
+  }
 
   const int q0w = qt * QROWS + wave * 32;  // first query row of this wave
   const bool wave_active = q0w < T;
@@ -328,42 +350,40 @@ attn_tick_kernel(const AttnParams p) {
   const int vcx = 2 * ((lane >> 4) & 1) + ((a16 >> 1) & 1);
   const int vsub = 4 * (a16 & 1);
 
-  // position (segment, token) of the next tile to load, and its segment pair
-  int seg_n = 0, t_n = 0;
-  SegPair sp;
-  load_seg_pair(seg_tab, nseg, 0, sp);
-  auto advance = [&]() {
-    t_n += KT;
-    while (t_n >= T) {
-      t_n -= T;
-      ++seg_n;
-    }
-    if (!kSmallT && seg_n != sp.seg0) load_seg_pair(seg_tab, nseg, seg_n, sp);
-  };
-  {
-    TileLoads<D, kSmallT> ld;
-    ld.prepare(p, pages_lds, seg_tab, sp, nseg, seg_n, t_n, wave, lane);
+  Loader ld;
+  ld.init(p, wave, lane);
+  ld.prepare(p, pages_lds, s, h, nseg);
 #pragma unroll
-    for (int i = 0; i < TileLoads<D, kSmallT>::NI; ++i) ld.emit(i, p, k_lds0, v_lds0, wave, lane);
-    advance();
-  }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's tile loads have landed
-  __syncthreads();
+  for (int i = 0; i < NI; ++i) ld.emit(i, p, k_lds0, v_lds0, wave);
+  ld.prepare(p, pages_lds, s, h, nseg);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) ld.emit(i, p, k_lds1, v_lds1, wave);
+  ld.prepare(p, pages_lds, s, h, nseg);  // tile 2, issued by the first step
+  tile_barrier<2 * NI>();  // tile 0 has landed (tile 1 may still be in flight)
 
-  // One tile: compute tile it from (kb, vb); the loads of tile it+1 (dummy rows
-  // past the end) go to (kn, vn), spread between the S^T MFMAs.
+  // keys of the computed tile that are real: 64, the chunk's remainder on a
+  // segment's last tile, 0 past the end (the loop runs in groups of three)
+  int m_c = 0;
+  auto valid_keys = [&](int it) {
+    const int v = it >= ntiles ? 0 : (m_c == p.tps - 1 ? p.t_last : KT);
+    if (++m_c == p.tps) m_c = 0;
+    return v;
+  };
+
+  // One tile: compute tile it from (kb, vb); the loads of tile it+2 go to
+  // (kn, vn), spread between the S^T MFMAs; tile it+3 is resolved for the next.
   auto step = [&](int it, const uint16_t* kb, const uint16_t* vb, uint16_t* kn, uint16_t* vn) {
-    constexpr int NI = TileLoads<D, kSmallT>::NI;
-    TileLoads<D, kSmallT> ld;
+    const int valid = valid_keys(it);
     if (!wave_active) {
-      ld.prepare(p, pages_lds, seg_tab, sp, nseg, seg_n, t_n, wave, lane);
-      advance();
 #pragma unroll
-      for (int i = 0; i < NI; ++i) ld.emit(i, p, kn, vn, wave, lane);
+      for (int i = 0; i < NI; ++i) ld.emit(i, p, kn, vn, wave);
+      ld.prepare(p, pages_lds, s, h, nseg);
     } else {
       // ---- S^T = K Q^T: two 32-key blocks; K operands two k-steps ahead, one
-      // row of next-tile loads after each k-step (scheduling fences keep the
-      // interleave)
+      // row group of next-tile loads after each k-step (scheduling fences keep
+      // the interleave). Each LDS address is one offset added to the buffer:
+      // the compiler tags LDS accesses with the buffer they touch only through
+      // a short chain of address steps.
       auto kload = [&](int kk, bf16x8* dst) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
@@ -374,8 +394,6 @@ attn_tick_kernel(const AttnParams p) {
       bf16x8 ka[3][2];
       kload(0, ka[0]);
       kload(1, ka[1]);
-      ld.prepare(p, pages_lds, seg_tab, sp, nseg, seg_n, t_n, wave, lane);
-      advance();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
@@ -384,13 +402,11 @@ attn_tick_kernel(const AttnParams p) {
           sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
                                                               0, 0, 0);
         if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
-        if (kk < NI) ld.emit(kk, p, kn, vn, wave, lane);
+        if (kk < NI) ld.emit(kk, p, kn, vn, wave);
         __builtin_amdgcn_sched_barrier(0);
       }
+      ld.prepare(p, pages_lds, s, h, nseg);
       // V^T operand of one 16-key step for all DB blocks: two transposed reads each
-      // (Each LDS address is one offset added to the buffer: the compiler tags
-      // LDS accesses with the buffer they touch only through a short chain of
-      // address steps, and untagged reads would wait for every tile load.)
       auto vload = [&](int kk, bf16x8* dst) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -406,13 +422,13 @@ attn_tick_kernel(const AttnParams p) {
       bf16x8 va[2][DB];
       vload(0, va[0]);
       // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
-      if (it == ntiles - 1 && last_valid < KT) {
+      if (valid < KT) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int x = 0; x < 16; ++x) {
             const int key = 32 * blk + 16 * (x >> 3) + 8 * g + (x & 7);
-            if (key >= last_valid) sacc[blk][x] = -INFINITY;
+            if (key >= valid) sacc[blk][x] = -INFINITY;
           }
       }
       // ---- online softmax (exp2 domain) ------------------------------------
@@ -455,13 +471,15 @@ attn_tick_kernel(const AttnParams p) {
       }
     }
 
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): next tile's loads have landed
-    __syncthreads();
+    tile_barrier<2 * NI>();  // tile it+1 has landed; tile it+2 may still be in flight
   };
 
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, k_lds0, v_lds0, k_lds1, v_lds1);
-    if (it + 1 < ntiles) step(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+  // Whole groups of three (a tile past the end is fully masked and adds
+  // nothing), so that each step names its buffers statically.
+  for (int it = 0; it < ntiles; it += 3) {
+    step(it, k_lds0, v_lds0, k_lds2, v_lds2);
+    step(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    step(it + 2, k_lds2, v_lds2, k_lds1, v_lds1);
   }
 
   // ---- epilogue: O = O^T / l, bf16 ----------------------------------------
@@ -546,26 +564,11 @@ void plan_xcd_order(const StagePlan& pl, int H, AttnParams& p, int64_t& blocks) 
   blocks = int64_t(kNumXcd) * stride * p.ntq;
 }
 
-// LDS budget for the page table: static K/V buffers take 64 KB (D = 128); the
-// table is sized to the call and may use up to 32 KB more.
-constexpr size_t kMaxPageTableLds = 32 * 1024;
-
-// Chunks of at least one tile (T >= 64) put every tile in at most two segments.
-template <int D, bool kSmallT>
-int32_t launch_attn(const AttnParams& p, unsigned blocks, size_t dyn_lds, hipStream_t stream) {
-  // The dynamic-LDS limit is raised once per device and instantiation.
-  static std::atomic<uint64_t> attr_set{0};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "wf_attn_tick: hipGetDevice");
-  const uint64_t bit = uint64_t(1) << (dev & 63);
-  if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_tick_kernel<D, kSmallT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxPageTableLds));
-    if (e != hipSuccess) return hip_fail(e, "wf_attn_tick: hipFuncSetAttribute");
-    attr_set.fetch_or(bit, std::memory_order_acq_rel);
-  }
-  attn_tick_kernel<D, kSmallT><<<dim3(blocks), NTHREADS, dyn_lds, stream>>>(p);
+// kFast: every tile is one uniform span of a page or live chunk (page size a
+// multiple of 64, or no history); otherwise history tiles resolve per lane.
+template <int D, bool kFast>
+int32_t launch_attn(const AttnParams& p, unsigned blocks, hipStream_t stream) {
+  attn_tick_kernel<D, kFast><<<dim3(blocks), NTHREADS, 0, stream>>>(p);
   return WF_OK;
 }
 
@@ -668,31 +671,31 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     p.H = d.H;
     p.P = d.n_hist > 0 ? d.P : 16;
     p.ppc = ppc;
+    p.tps = (d.T + KT - 1) / KT;
+    p.t_last = d.T - KT * (p.tps - 1);
     p.p_magic = uint32_t((uint64_t(1) << 32) / uint64_t(p.P) + 1);
     p.c = float(double(d.scale) * 1.4426950408889634);
     p.ntq = (d.T + QROWS - 1) / QROWS;
     p.items_per_stage = d.H * p.ntq;
     p.n_page_ids = d.n_hist * ppc;
-    for (int i = 0; i < pl.n_active; ++i) p.stage_of_rank[i] = int8_t(pl.order[i]);
+    for (int i = 0; i < pl.n_active; ++i) p.stage_of_rank[i] = pl.order[i];
     for (int s = 0; s <= d.S; ++s) {
-      p.nseg[s] = int8_t(pl.nseg[s]);
+      p.nseg[s] = pl.nseg[s];
       for (int i = 0; i < pl.nseg[s]; ++i) p.seg[s][i] = pl.seg[s][i];
     }
     int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
     plan_xcd_order(pl, d.H, p, blocks);
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
-    // at least one entry: tile rows of live segments still read (and ignore) entry 0
-    const size_t dyn_lds = size_t(std::max(p.n_page_ids, 1)) * sizeof(int32_t);
-    if (dyn_lds > kMaxPageTableLds)
-      return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %zu bytes of LDS",
-                  p.n_page_ids, kMaxPageTableLds);
-    const bool small_t = d.T < KT;
+    const bool fast = d.n_hist == 0 || d.P % KT == 0;
+    if (!fast && p.n_page_ids > kMaxPageIds)  // the per-lane path keeps the table in LDS
+      return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %d (page sizes "
+                  "that are a multiple of 64 have no such limit)", p.n_page_ids, kMaxPageIds);
     if (d.D == 128)
-      st = small_t ? launch_attn<128, true>(p, unsigned(blocks), dyn_lds, stream)
-                   : launch_attn<128, false>(p, unsigned(blocks), dyn_lds, stream);
+      st = fast ? launch_attn<128, true>(p, unsigned(blocks), stream)
+                : launch_attn<128, false>(p, unsigned(blocks), stream);
     else
-      st = small_t ? launch_attn<64, true>(p, unsigned(blocks), dyn_lds, stream)
-                   : launch_attn<64, false>(p, unsigned(blocks), dyn_lds, stream);
+      st = fast ? launch_attn<64, true>(p, unsigned(blocks), stream)
+                : launch_attn<64, false>(p, unsigned(blocks), stream);
     if (st != WF_OK) return st;
     return check_launch("wf_attn_tick");
   } catch (...) {
