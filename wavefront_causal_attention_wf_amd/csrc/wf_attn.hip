@@ -97,19 +97,28 @@ __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// XOR swizzle (16-byte chunk index) of K tile row `row`. The MFMA operand reads
-// touch rows {0..3, 8..11} (+4, +16, ...) at one logical chunk; the swizzle maps
-// any such 8 rows to distinct chunks mod 8 and rows 0..15 to distinct chunks
-// mod 16 (D = 128), so the reads are bank-conflict free.
+// XOR swizzles (on the 16-byte chunk index) of K and V tile rows, chosen so
+// that the MFMA operand reads are free of LDS bank conflicts whether the LDS
+// serves 128 or 256 bytes per clock (8 or 16 lanes of a 16-byte read, 16 or 32
+// lanes of an 8-byte read, per pass):
+//  * K: a read touches rows {0..3, 8..11} (+4, +16, ...) at one logical chunk;
+//    any 8 such rows land in distinct chunks mod 8, and for D = 128 rows 0..15
+//    in distinct chunks mod 16; for D = 64 (two rows per 256 bytes) the 8 rows
+//    of one parity among 0..15 land in distinct chunks.
+//  * V (transposed reads): a pass reads 32 contiguous bytes (16 lanes) or 64
+//    bytes (32 lanes) from each of 4 consecutive rows; the row swizzle places
+//    those pieces in distinct bank ranges.
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
-  int x = (row & 3) | ((row >> 1) & 4);
-  if constexpr (D == 128) x |= (row << 1) & 8;
-  return x;
+  if constexpr (D == 128) return (row & 3) | ((row >> 1) & 4) | ((row << 1) & 8);
+  return (row & 3) ^ ((row >> 2) & 1) ^ ((row >> 1) & 4);
 }
-// XOR swizzle of V tile row `row`: the transposed reads fetch 32 contiguous bytes
-// from 4 consecutive rows; this puts those 4 pieces in distinct 32-byte slots.
-__device__ __forceinline__ int vswz(int row) { return 2 * (row & 3); }
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  const int q = row & 3;
+  if constexpr (D == 128) return (4 * q) ^ (2 * (q >> 1));
+  return 2 * q;
+}
 
 __device__ __forceinline__ float xlane32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -184,7 +193,7 @@ struct TileLoader {
       row[i] = wave * RW + RPI * i + lane / DC;
       const int rr = row[i] < p.t_last ? row[i] : p.t_last - 1;
       const uint32_t kc = uint32_t(pc ^ kswz<D>(row[i])) * 16;
-      const uint32_t vc = uint32_t(pc ^ vswz(row[i])) * 16;
+      const uint32_t vc = uint32_t(pc ^ vswz<D>(row[i])) * 16;
       koff[i] = uint32_t(row[i]) * row_bytes + kc;
       voff[i] = uint32_t(row[i]) * row_bytes + vc;
       koff_r[i] = uint32_t(rr) * row_bytes + kc;
@@ -346,7 +355,7 @@ attn_tick_kernel(const AttnParams p) {
   const int kx = kswz<D>(krow0);      // same swizzle for row + 32
   const int a16 = lane & 15;          // lane within its 16-lane group (transposed V reads)
   const int vrow = 8 * g + (a16 >> 2);
-  const int vx = 2 * ((a16 >> 2) & 3);
+  const int vx = vswz<D>(vrow);
   const int vcx = 2 * ((lane >> 4) & 1) + ((a16 >> 1) & 1);
   const int vsub = 4 * (a16 & 1);
 
