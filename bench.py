@@ -32,6 +32,51 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# HBM traffic of the attention kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes (scaled by a plain-copy calibration), recorded with a hash of the
+# kernel's sources and build flags; reported only while that hash still matches.
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "wf_attn_tick_wan13_4step_counters.md")
+
+
+def attn_kernel_hash() -> str:
+    """sha256 of the attention kernel's sources (comments and whitespace removed)
+    and the build flags."""
+    import hashlib
+    import re
+
+    from wavefront_causal_attention_wf_amd import build_lib
+
+    h = hashlib.sha256()
+    paths = [os.path.join(build_lib.CSRC, "wf_attn.hip"), os.path.join(build_lib.CSRC, "wf_internal.h"),
+             os.path.join(build_lib.INCLUDE, "wf_attn.h")]
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    h.update(" ".join(build_lib.HIP_FLAGS).encode())
+    return h.hexdigest()
+
+
+def recorded_traffic(config_name: str):
+    """(bytes per launch, note) from the committed counter summary, or (None, why)."""
+    if config_name != "wan13_4step":
+        return None, "counters recorded for wan13_4step only"
+    try:
+        text = open(COUNTERS_FILE).read()
+    except OSError:
+        return None, "no counter summary"
+    vals = {}
+    for line in text.splitlines():
+        line = line.strip().strip("`")
+        if ":" in line and line.split(":", 1)[0] in ("kernel_sha256", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            vals[k] = v.strip()
+    if vals.get("kernel_sha256") != attn_kernel_hash():
+        return None, "kernel changed since the counters were taken"
+    return int(vals["traffic_bytes_per_launch"]), "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -48,6 +93,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle sample")
     ap.add_argument("--rotate", type=int, default=4, help="distinct live-input sets cycled")
+    ap.add_argument("--kernel-hash", action="store_true",
+                    help="print the attention kernel's source hash (recorded with its counters)")
     ap.add_argument("--mode", default="tick", choices=["tick", "attn", "store", "copy"],
                     help="tick: the full hot path (default, prints the JSON line); attn / "
                          "store: only that kernel, --steps launches (for profilers); copy: "
@@ -227,6 +274,9 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
 
 def main():
     args = parse()
+    if args.kernel_hash:
+        print(attn_kernel_hash())
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the sharding design is described in DESIGN.md)"}))
@@ -270,6 +320,7 @@ def main():
         f"attn kernel mean {attn_ms.mean():.3f} ms p10 {np.percentile(attn_ms, 10):.3f} "
         f"p90 {np.percentile(attn_ms, 90):.3f}")
 
+    traffic, traffic_note = recorded_traffic(cfg.name)
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
     achieved = flops / (attn_ms.mean() * 1e-3) / 1e12
     out = {
@@ -295,7 +346,8 @@ def main():
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "wf_attn_tick",
+                     "traffic": traffic, "traffic_note": traffic_note,
+                     "kernel": "wf_attn_tick",
                      "kernel_ms_mean": round(float(attn_ms.mean()), 4)},
     }
     out["store"] = store_bandwidth(cfg, dev)

@@ -10,29 +10,34 @@
 //     keys, so stage 0 is the heaviest.
 //
 // Design (gfx950, wave64, MFMA):
-//  * One workgroup = 4 waves = 128 query rows of one (stage, head); each wave
-//    owns 32 query rows. The context of the stage is a virtual key sequence
-//    (history chunks through the page table, live store, live j >= s) cut into
-//    64-key tiles that may straddle chunk boundaries; noisier chunks j < s are
-//    simply not in the sequence (block-sparse skip), so only the very last tile
-//    can be partial.
+//  * One workgroup = 8 waves = 256 query rows of one (stage, head); each wave
+//    owns 32 query rows (two waves per SIMD, one workgroup per CU). The context
+//    of the stage is walked chunk by chunk (history chunks through the page
+//    table, live store, live j >= s), each chunk cut into ceil(T/64) tiles of
+//    64 keys whose last one is masked past T; noisier chunks j < s are not in
+//    the walk at all (block-sparse skip).
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: the query is the
 //    MFMA column, so each lane holds one query row's scores and output and the
 //    softmax needs only one cross-lane exchange (lane l <-> l+32) per tile.
 //    K rows are fed to the MFMA in a bit-2/bit-3-swapped order so that the score
 //    registers already are the P operand of the P.V product (no shuffles).
 //  * K and V tiles [64 keys][D] stream from global memory straight into LDS
-//    (16-byte direct loads, no register staging), double-buffered: the loads of
-//    tile i+1 are in flight while tile i is computed, one barrier per tile. Row
-//    addresses come from a per-tile segment lookup and, for history, from the
-//    page table copied into LDS once per workgroup. Both tiles are XOR-swizzled
-//    per row; V^T operands are fetched with the gfx950 transposing LDS read
-//    (ds_read_b64_tr_b16), so V needs no transpose on its way in.
+//    (16-byte direct loads, no register staging) into three buffers: the loads
+//    of tile i+2 are issued between the Q.K^T MFMAs of tile i, and a tile ends
+//    with one barrier that waits only for tile i+1. With pages of a multiple of
+//    64 tokens a tile is one contiguous span of a page or a live chunk: its
+//    base is a scalar (the page id comes from a scalar load of the page table)
+//    and each lane adds a fixed offset. Rows are XOR-swizzled so that the MFMA
+//    operand reads are free of LDS bank conflicts; V^T operands are fetched
+//    with the gfx950 transposing LDS read (ds_read_b64_tr_b16), so V needs no
+//    transpose on its way in.
 //  * Online softmax in the exp2 domain (log2 e folded into the scale), fp32
 //    state; the running max is only raised when a tile exceeds it by more than
 //    8 (in log2 units), so the O rescale is rare (exact: numerator and
 //    denominator share the same reference).
-//  * Workgroups are ordered heavy stage first (stage 0 has the most keys).
+//  * Work order: (stage, head) groups, heaviest stage first, dealt to the 8
+//    XCDs so that each XCD streams about the same number of keys and the query
+//    tiles of a group share that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
