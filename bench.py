@@ -169,8 +169,12 @@ class Rollout:
 
 
 def store_bandwidth(cfg, dev, launches: int = 24, rotation: int = 8) -> dict:
-    """wf_store_paged alone, rotating over `rotation` distinct source chunks and
-    page sets (working set > the 256 MB last-level cache), HIP events on its stream."""
+    """wf_store_paged and wf_gather_paged alone, HIP events on their stream.
+
+    cold: rotating over `rotation` distinct source chunks and page sets (working
+    set above the 256 MB last-level cache); warm: one chunk and page set
+    repeated; copy: a plain device-to-device copy of the store's byte count (the
+    achievable ceiling for a read+write stream of that size)."""
     import torch
 
     from wavefront_causal_attention_wf_amd import inputs, wfattn
@@ -188,22 +192,45 @@ def store_bandwidth(cfg, dev, launches: int = 24, rotation: int = 8) -> dict:
         inputs.TickConfig("rot", S=0, T=T, H=H, D=D, P=P, n_hist=0, num_pages=pool_pages,
                           std=0.5, bf16_inputs=True, page_order="permutation")))
     ids = [order[i * ppc:(i + 1) * ppc].to(torch.int32).to(dev) for i in range(rotation)]
-    for i in range(rotation):  # warm
-        wfattn.wf_store_paged(ksrc[i], vsrc[i], kp, vp, ids[i])
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(launches):
-        j = i % rotation
-        wfattn.wf_store_paged(ksrc[j], vsrc[j], kp, vp, ids[j])
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / launches
+    kd = torch.empty((1, T, H, D), dtype=torch.bfloat16, device=dev)
+    vd = torch.empty_like(kd)
+
+    def timed(fn) -> float:
+        for i in range(rotation):  # warm
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(launches):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / launches
+
+    store_cold = timed(lambda i: wfattn.wf_store_paged(ksrc[i % rotation], vsrc[i % rotation],
+                                                       kp, vp, ids[i % rotation]))
+    store_warm = timed(lambda i: wfattn.wf_store_paged(ksrc[0], vsrc[0], kp, vp, ids[0]))
+    gather_cold = timed(lambda i: wfattn.wf_gather_paged(kp, vp, ids[i % rotation], kd, vd))
     nbytes = 2 * (T * H * D * 2) + 2 * (ppc * P * H * D * 2)   # read K,V + write whole pages
-    return {"kernel": "wf_store_paged", "us_mean": round(ms * 1e3, 2),
-            "bytes": nbytes, "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "rotation": rotation}
+    gbytes = 4 * (T * H * D * 2)   # read the K,V tokens from their pages + write them
+    # a copy of nbytes / 2 bytes moves nbytes (read + write)
+    csrc = [torch.empty(nbytes // 4, dtype=torch.int16, device=dev) for _ in range(rotation)]
+    cdst = [torch.empty_like(x) for x in csrc]
+    copy_cold = timed(lambda i: cdst[i % rotation].copy_(csrc[i % rotation]))
+
+    def rate(nb, ms):
+        return round(nb / (ms * 1e-3) / 1e9, 1)
+
+    return {"kernel": "wf_store_paged", "us_mean": round(store_cold * 1e3, 2),
+            "bytes": nbytes, "gb_per_s": rate(nbytes, store_cold),
+            "frac_hbm_peak": round(rate(nbytes, store_cold) / PEAK_HBM_GBS, 4),
+            "rotation": rotation,
+            "warm_us_mean": round(store_warm * 1e3, 2), "warm_gb_per_s": rate(nbytes, store_warm),
+            "copy_same_bytes_us": round(copy_cold * 1e3, 2),
+            "copy_same_bytes_gb_per_s": rate(nbytes, copy_cold),
+            "gather": {"kernel": "wf_gather_paged", "us_mean": round(gather_cold * 1e3, 2),
+                       "bytes": gbytes, "gb_per_s": rate(gbytes, gather_cold),
+                       "frac_hbm_peak": round(rate(gbytes, gather_cold) / PEAK_HBM_GBS, 4)}}
 
 
 def profile_mode(args, cfg, dev) -> None:

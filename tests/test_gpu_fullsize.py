@@ -90,10 +90,10 @@ def run_tick(cfg, pages: MirroredPages, q, k, v, mask: int) -> torch.Tensor:
     return o
 
 
-def oracle_rows(cfg, pages: MirroredPages, q, k, v, mask: int, rows):
+def oracle_rows(cfg, pages: MirroredPages, q, k, v, mask: int, rows, heads=None):
     return oracle.attention_tick_paged(bits(q), bits(k), bits(v), pages.store,
                                        pages.model.export(), cfg.S, mask, 1.0 / np.sqrt(cfg.D),
-                                       rows=rows)
+                                       rows=rows, heads=heads)
 
 
 @pytest.mark.parametrize("name", ["wan13_4step", "wan13_5step", "wan14b_4step"])
@@ -127,12 +127,14 @@ def test_streaming_rollout_120_ticks():
 
     Every tick: page ids, evictions and exported tables equal the oracle model;
     the stored chunk's pool pages equal the oracle store bit for bit; every
-    output is finite. On a spread of ticks (fill, first eviction, recycled
-    pages, last) the outputs match the oracle on sampled rows."""
+    output is finite; head 0 matches the oracle on sampled rows. On a spread of
+    ticks (fill, first eviction, recycled pages, last) every head matches on
+    sampled rows, and on ticks 0-3 and the last, head 0 matches on every row."""
     cfg = inputs.CONFIGS["rollout120"]
     S = cfg.S
     pages = MirroredPages(cfg, cfg.window)
     check_at = {0, 1, S - 1, S, S + 1, S + 3, S + 4, 40, 61, 90, cfg.ticks - 1}
+    all_rows_at = {0, 1, 2, 3, cfg.ticks - 1}
     for t in range(cfg.ticks):
         mask = oracle.active_mask_for_tick(t, S)
         q, k, v = inputs.draw_live_torch(cfg, inputs.rollout_seed(t), DEV)
@@ -145,12 +147,20 @@ def test_streaming_rollout_120_ticks():
         for s in range(S + 1):
             if (mask >> s) & 1:
                 assert torch.isfinite(o[s].float()).all(), f"tick {t} stage {s}"
+        if t in all_rows_at:
+            want = oracle_rows(cfg, pages, q, k, v, mask, None, heads=[0])
+            worst0 = compare(o, want, heads=[0], label=f"tick {t} head 0 all rows")
+        else:
+            rows0 = sample_rows(cfg.T, seed=10_000 + t, n_random=4)
+            want = oracle_rows(cfg, pages, q, k, v, mask, rows0, heads=[0])
+            worst0 = compare(o, want, heads=[0], rows=rows0, label=f"tick {t} head 0")
         if t in check_at:
             rows = sample_rows(cfg.T, seed=t, n_random=6)
             want = oracle_rows(cfg, pages, q, k, v, mask, rows)
             worst = compare(o, want, rows=rows, label=f"tick {t}")
             say(f"[rollout] tick {t}: mask {mask:#x}, history "
-                f"{len(pages.model.export())} chunks, worst rel-L2 {worst:.2e}")
+                f"{len(pages.model.export())} chunks, worst rel-L2 {worst:.2e} (all heads, "
+                f"sampled rows), {worst0:.2e} (head 0)")
         if store_on:
             pages.commit()
     # every page still resident matches the oracle store
