@@ -139,8 +139,8 @@ wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t*
 /* Errors: WF_EINVAL for bad sizes, masks, pointers (NULL or not 16-byte      */
 /* aligned), P not a positive multiple of 16, n_hist*ceil(T/P) > num_pages;   */
 /* WF_EUNSUPPORTED for D not 64/128, n_hist + S + 1 > 32, T > 2^24,           */
-/* T*P >= 2^32, num_pages*P >= 2^31, and, only when P is not a multiple of    */
-/* 64, n_hist*ceil(T/P) > 8192 (those page tables are staged in LDS);         */
+/* T*P >= 2^32, num_pages*P >= 2^31, n_hist*ceil(T/P) > 8192 (the page       */
+/* table is staged in LDS);                                                   */
 /* WF_EHIP if the launch fails. T = 0 or active_mask = 0 is a no-op.          */
 /* ------------------------------------------------------------------------ */
 typedef struct wf_tick_desc {

@@ -64,8 +64,10 @@ constexpr int QROWS = 32 * NWAVES;  // query rows per workgroup
 constexpr float kLazyTau = 8.0f;    // raise the running max only beyond this (log2 units)
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kXcdTable = 512;      // max (stage, head) groups in the XCD table
-// History page table held in LDS (ids of all history pages of one tick).
+// History page table held in LDS (ids of all history pages of one tick) when
+// pages are not a multiple of 64 tokens; otherwise a table of tile sources.
 constexpr int kMaxPageIds = 8192;
+constexpr int kMaxTiles = 2560;  // 64-key tiles per (stage, head): 40 KB of sources
 
 struct AttnParams {
   const uint16_t* q;
@@ -149,8 +151,6 @@ __device__ __forceinline__ lds_void* opaque_lds(const uint16_t* p) {
   return reinterpret_cast<lds_void*>(uintptr_t(a));
 }
 
-typedef const __attribute__((address_space(4))) int32_t* const_i32p;
-
 // Tile loads straight from global memory into LDS (16 bytes per lane).
 //
 // The stage's key sequence is walked segment by segment (a segment = one chunk
@@ -170,6 +170,70 @@ typedef const __attribute__((address_space(4))) int32_t* const_i32p;
 // LDS. prepare() resolves the next tile and advances the cursor; emit(i) issues
 // the two loads of row group i, so the caller can spread them between MFMAs.
 // Past the last tile the cursor reads tile 0 again (finite, masked).
+// Loop-invariant scalars of a launch, read from the kernel arguments once and
+// kept in scalar registers (readfirstlane makes them values the compiler will
+// not re-load from the argument buffer inside the loop: scalar-memory loads
+// there would force waits that drain every LDS read in flight).
+struct Uniforms {
+  const char* k;
+  const char* v;
+  const char* k_pool;
+  const char* v_pool;
+  int32_t T, H, P, ppc, tps, t_last;
+  uint32_t p_magic, row_bytes;
+  float c;  // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ int32_t uniform_i32(int32_t x) {
+  return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ const char* uniform_ptr(const void* ptr) {
+  const uint64_t x = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(x >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+}
+
+template <int D>
+__device__ __forceinline__ Uniforms load_uniforms(const AttnParams& p, int h) {
+  Uniforms u;
+  u.T = uniform_i32(p.T);
+  u.H = uniform_i32(p.H);
+  u.P = uniform_i32(p.P);
+  u.ppc = uniform_i32(p.ppc);
+  u.tps = uniform_i32(p.tps);
+  u.t_last = uniform_i32(p.t_last);
+  u.p_magic = uint32_t(uniform_i32(int32_t(p.p_magic)));
+  u.row_bytes = uint32_t(u.H) * D * 2;
+  u.c = __builtin_bit_cast(float, uniform_i32(__builtin_bit_cast(int32_t, p.c)));
+  // head h's column block of every tensor
+  u.k = uniform_ptr(p.k + int64_t(h) * D);
+  u.v = uniform_ptr(p.v + int64_t(h) * D);
+  u.k_pool = uniform_ptr(p.k_pool + int64_t(h) * D);
+  u.v_pool = uniform_ptr(p.v_pool + int64_t(h) * D);
+  return u;
+}
+
+// Tile loads straight from global memory into LDS (16 bytes per lane).
+//
+// The stage's key sequence is walked segment by segment (a segment = one chunk
+// of T keys: a history chunk through its pages, or a live chunk), each cut into
+// tps = ceil(T / 64) tiles of 64 keys; only the last tile of a segment is
+// partial (its rows past the chunk re-read the chunk's last key and are masked
+// in the softmax). Wave w fills rows [RW*w, RW*w + RW) of the K and V tiles; one
+// wave instruction writes 1 KB = RPI whole rows, lane l landing at chunk l % DC
+// of row l / DC, so each lane fetches the logical chunk that the row swizzle
+// maps to that position.
+//
+// kFast (page size a multiple of 64, and every live chunk): a tile is 64
+// consecutive rows of one page or chunk, so its source is one uniform base
+// (scalar registers; the page id is one broadcast read of the page table in
+// LDS) plus a fixed per-lane offset, and a tile costs no vector address math.
+// Otherwise history tiles resolve each lane's page through the page table.
+// The segment's code is read (a scalar load) only when the cursor enters a new
+// segment. prepare() resolves the next tile and advances the cursor; emit(i)
+// issues the two loads of row group i, so the caller can spread them between
+// MFMAs. Past the last tile the cursor reads tile 0 again (finite, masked).
 template <int D, bool kFast>
 struct TileLoader {
   static constexpr int DC = D / 8;        // 16-byte chunks per row
@@ -182,6 +246,11 @@ struct TileLoader {
   int32_t row[NI];
   // cursor: next tile to resolve
   int seg, m;
+  // the cursor's segment: index, history chunk (-1: live), chunk bases
+  int cur_seg;
+  int hist_c;
+  const char* seg_k;
+  const char* seg_v;
   // resolved tile: uniform bases (+ the per-lane offsets), or for per-lane
   // history tiles the pool bases of head h and each lane's pool row
   const char* kb;
@@ -190,74 +259,106 @@ struct TileLoader {
   bool per_lane;
   uint32_t prow[NI];
 
-  __device__ __forceinline__ void init(const AttnParams& p, int wave, int lane) {
-    const uint32_t row_bytes = uint32_t(p.H) * D * 2;
+  __device__ __forceinline__ void init(const Uniforms& u, int wave, int lane) {
     const int pc = lane % DC;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       row[i] = wave * RW + RPI * i + lane / DC;
-      const int rr = row[i] < p.t_last ? row[i] : p.t_last - 1;
+      const int rr = row[i] < u.t_last ? row[i] : u.t_last - 1;
       const uint32_t kc = uint32_t(pc ^ kswz<D>(row[i])) * 16;
       const uint32_t vc = uint32_t(pc ^ vswz<D>(row[i])) * 16;
-      koff[i] = uint32_t(row[i]) * row_bytes + kc;
-      voff[i] = uint32_t(row[i]) * row_bytes + vc;
-      koff_r[i] = uint32_t(rr) * row_bytes + kc;
-      voff_r[i] = uint32_t(rr) * row_bytes + vc;
+      koff[i] = uint32_t(row[i]) * u.row_bytes + kc;
+      voff[i] = uint32_t(row[i]) * u.row_bytes + vc;
+      koff_r[i] = uint32_t(rr) * u.row_bytes + kc;
+      voff_r[i] = uint32_t(rr) * u.row_bytes + vc;
     }
     seg = 0;
     m = 0;
+    cur_seg = -1;
   }
 
-  __device__ __forceinline__ void prepare(const AttnParams& p, const int32_t* pages_lds, int s,
-                                          int h, int nseg) {
+  // kFast: the sources of tile t are entry t of a table built once per
+  // workgroup in LDS: K base (bit 0 = last, partial tile of its chunk) and V
+  // base. The entry of the next tile is read one tile ahead, so resolving a
+  // tile waits for nothing.
+  int next_t;
+  uint4 pre;
+
+  __device__ __forceinline__ void start_table(const uint4* tab) {
+    next_t = 0;
+    pre = tab[0];
+  }
+
+  __device__ __forceinline__ void prepare_table(const uint4* tab, int ntiles) {
+    const uint64_t kr = (uint64_t(uint32_t(uniform_i32(int32_t(pre.y)))) << 32) |
+                        uint32_t(uniform_i32(int32_t(pre.x)));
+    const uint64_t vr = (uint64_t(uint32_t(uniform_i32(int32_t(pre.w)))) << 32) |
+                        uint32_t(uniform_i32(int32_t(pre.z)));
+    ragged = kr & 1;
+    kb = reinterpret_cast<const char*>(kr & ~uint64_t(1));
+    vb = reinterpret_cast<const char*>(vr);
+    per_lane = false;
+    ++next_t;
+    pre = tab[next_t < ntiles ? next_t : 0];
+  }
+
+  __device__ __forceinline__ void prepare(const AttnParams& p, const Uniforms& u,
+                                          const int32_t* pages_lds, int s, int nseg) {
     const int sg = seg < nseg ? seg : 0;
     const int mm = seg < nseg ? m : 0;
-    const int code = p.seg[s][sg];
-    const int64_t t0 = int64_t(KT) * mm;  // first token of the tile within the chunk
-    ragged = mm == p.tps - 1;
-    per_lane = false;
-    if (code >= 0) {  // live chunk `code` of the tick's q/k/v
-      const int64_t e = ((int64_t(code) * p.T + t0) * p.H + h) * D;
-      kb = reinterpret_cast<const char*>(p.k + e);
-      vb = reinterpret_cast<const char*>(p.v + e);
-    } else if constexpr (kFast) {  // history chunk: one page holds the whole tile
-      const int c = -code - 1;
-      const int pid = ((const_i32p)p.hist_pages)[c * p.ppc + int(t0 / p.P)];
-      const int64_t prow = int64_t(pid) * p.P + (t0 % p.P);
-      const int64_t e = (prow * p.H + h) * D;
-      kb = reinterpret_cast<const char*>(p.k_pool + e);
-      vb = reinterpret_cast<const char*>(p.v_pool + e);
-    } else {  // history chunk, pages smaller than or not aligned to a tile
-      const int c = -code - 1;
-      per_lane = true;
-      kb = reinterpret_cast<const char*>(p.k_pool + int64_t(h) * D);
-      vb = reinterpret_cast<const char*>(p.v_pool + int64_t(h) * D);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int rr = ragged && row[i] >= p.t_last ? p.t_last - 1 : row[i];
-        const uint32_t tok = uint32_t(t0) + uint32_t(rr);
-        const uint32_t pg = __umulhi(tok, p.p_magic);
-        const int32_t pid = pages_lds[c * p.ppc + int(pg)];
-        // pool rows fit in 31 bits (checked on the host)
-        prow[i] = uint32_t(pid) * uint32_t(p.P) + (tok - pg * uint32_t(p.P));
+    if (sg != cur_seg) {  // entering a segment: its code, once
+      cur_seg = sg;
+      const int code = uniform_i32(p.seg[s][sg]);
+      if (code >= 0) {  // live chunk `code` of the tick's q/k/v
+        hist_c = -1;
+        const uint64_t e = uint64_t(code) * uint64_t(u.T) * u.row_bytes;
+        seg_k = u.k + e;
+        seg_v = u.v + e;
+      } else {
+        hist_c = -code - 1;
       }
     }
-    if (++m == p.tps) {
+    const uint32_t t0 = uint32_t(KT) * uint32_t(mm);  // first token of the tile in the chunk
+    ragged = mm == u.tps - 1;
+    per_lane = false;
+    if (hist_c < 0) {
+      kb = seg_k + uint64_t(t0) * u.row_bytes;
+      vb = seg_v + uint64_t(t0) * u.row_bytes;
+    } else if constexpr (kFast) {  // history chunk: one page holds the whole tile
+      const uint32_t pg = t0 / uint32_t(u.P);
+      const int pid = uniform_i32(pages_lds[hist_c * u.ppc + int(pg)]);
+      const uint64_t prow = uint64_t(uint32_t(pid)) * uint32_t(u.P) + (t0 - pg * uint32_t(u.P));
+      kb = u.k_pool + prow * u.row_bytes;
+      vb = u.v_pool + prow * u.row_bytes;
+    } else {  // history chunk, pages smaller than or not aligned to a tile
+      per_lane = true;
+      kb = u.k_pool;
+      vb = u.v_pool;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int rr = ragged && row[i] >= u.t_last ? u.t_last - 1 : row[i];
+        const uint32_t tok = t0 + uint32_t(rr);
+        const uint32_t pg = __umulhi(tok, u.p_magic);
+        const int32_t pid = pages_lds[hist_c * u.ppc + int(pg)];
+        // pool rows fit in 31 bits (checked on the host)
+        prow[i] = uint32_t(pid) * uint32_t(u.P) + (tok - pg * uint32_t(u.P));
+      }
+    }
+    if (++m == u.tps) {
       m = 0;
       ++seg;
     }
   }
 
-  __device__ __forceinline__ void emit(int i, const AttnParams& p, uint16_t* kbuf,
-                                       uint16_t* vbuf, int wave) const {
+  __device__ __forceinline__ void emit(int i, const Uniforms& u, uint16_t* kbuf, uint16_t* vbuf,
+                                       int wave) const {
     lds_void* kdst = opaque_lds(kbuf + (wave * RW + RPI * i) * D);
     lds_void* vdst = opaque_lds(vbuf + (wave * RW + RPI * i) * D);
     const char* ks;
     const char* vs;
     if (!kFast && per_lane) {
-      const uint32_t row_bytes = uint32_t(p.H) * D * 2;
-      const uint64_t o = uint64_t(prow[i]) * row_bytes;
-      const uint32_t rb = uint32_t(row[i]) * row_bytes;
+      const uint64_t o = uint64_t(prow[i]) * u.row_bytes;
+      const uint32_t rb = uint32_t(row[i]) * u.row_bytes;
       ks = kb + o + (koff[i] - rb);
       vs = vb + o + (voff[i] - rb);
     } else {
@@ -269,15 +370,18 @@ struct TileLoader {
   }
 };
 
-// End of a tile: this wave's tile loads except the newest N have landed in LDS
-// and its LDS reads are done, then all waves meet. (__syncthreads() would also
-// wait for the newest loads: its fence drains every outstanding memory op.)
-// The asm's memory clobber keeps LDS accesses on their side of the barrier.
+// End of a slot: this wave's tile loads except the newest N have landed in
+// LDS, then all waves meet. (__syncthreads() would also wait for the newest
+// loads: its fence drains every outstanding memory op.) LDS reads are not
+// waited for: every operand read of a tile buffer has been consumed by an MFMA
+// before the slot ends, and the only other LDS read that may still be in flight
+// is of the tile-source table, which is never written after the start. The
+// asm's memory clobber keeps LDS accesses on their side of the barrier.
 template <int N>
 __device__ __forceinline__ void tile_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  // s_waitcnt: vmcnt(N) (bits 3:0 and 15:14), expcnt(7) (no wait), lgkmcnt(0)
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  // s_waitcnt: vmcnt(N) (bits 3:0 and 15:14), expcnt(7) and lgkmcnt(15): no wait
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("s_barrier" ::: "memory");
 }
 
@@ -299,6 +403,7 @@ attn_tick_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds2[KT * D];
   __shared__ int32_t pages_lds[kFast ? 1 : kMaxPageIds];
+  __shared__ uint4 tile_tab[kFast ? kMaxTiles : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -329,10 +434,34 @@ attn_tick_kernel(const AttnParams p) {
   const int T = p.T;
   const int ntiles = nseg * p.tps;
 
-  if constexpr (!kFast) {  // page table of the history into LDS
+  const Uniforms u = load_uniforms<D>(p, h);
+  if constexpr (kFast) {
+    // sources of every tile of this (stage, head), one thread per tile
+    for (int t = tid; t < ntiles; t += NTHREADS) {
+      const int sg = t / u.tps;
+      const int mm = t - sg * u.tps;
+      const int code = p.seg[s][sg];
+      const uint32_t t0 = uint32_t(KT) * uint32_t(mm);
+      uint64_t kr, vr;
+      if (code >= 0) {  // live chunk `code`
+        const uint64_t e = (uint64_t(code) * uint32_t(u.T) + t0) * u.row_bytes;
+        kr = reinterpret_cast<uint64_t>(u.k + e);
+        vr = reinterpret_cast<uint64_t>(u.v + e);
+      } else {  // history chunk: the tile is rows t0 % P .. of one page
+        const int c = -code - 1;
+        const uint32_t pg = t0 / uint32_t(u.P);
+        const int pid = p.hist_pages[c * u.ppc + int(pg)];
+        const uint64_t prow = uint64_t(uint32_t(pid)) * uint32_t(u.P) + (t0 - pg * uint32_t(u.P));
+        kr = reinterpret_cast<uint64_t>(u.k_pool + prow * u.row_bytes);
+        vr = reinterpret_cast<uint64_t>(u.v_pool + prow * u.row_bytes);
+      }
+      kr |= (mm == u.tps - 1) ? 1u : 0u;  // bases are 16-byte aligned: bit 0 is free
+      tile_tab[t] = make_uint4(uint32_t(kr), uint32_t(kr >> 32), uint32_t(vr), uint32_t(vr >> 32));
+    }
+  } else {  // page table of the history into LDS
     for (int i = tid; i < p.n_page_ids; i += NTHREADS) pages_lds[i] = p.hist_pages[i];
-    __syncthreads();
   }
+  __syncthreads();
 
   const int q0w = qt * QROWS + wave * 32;  // first query row of this wave
   const bool wave_active = q0w < T;
@@ -365,136 +494,263 @@ attn_tick_kernel(const AttnParams p) {
   const int vsub = 4 * (a16 & 1);
 
   Loader ld;
-  ld.init(p, wave, lane);
-  ld.prepare(p, pages_lds, s, h, nseg);
+  ld.init(u, wave, lane);
+  auto resolve = [&]() __attribute__((always_inline)) {
+    if constexpr (kFast) ld.prepare_table(tile_tab, ntiles);
+    else ld.prepare(p, u, pages_lds, s, nseg);
+  };
+  if constexpr (kFast) ld.start_table(tile_tab);
+  resolve();
 #pragma unroll
-  for (int i = 0; i < NI; ++i) ld.emit(i, p, k_lds0, v_lds0, wave);
-  ld.prepare(p, pages_lds, s, h, nseg);
+  for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds0, v_lds0, wave);
+  resolve();
 #pragma unroll
-  for (int i = 0; i < NI; ++i) ld.emit(i, p, k_lds1, v_lds1, wave);
-  ld.prepare(p, pages_lds, s, h, nseg);  // tile 2, issued by the first step
+  for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds1, v_lds1, wave);
+  resolve();  // tile 2, issued in the first loop slot
   tile_barrier<2 * NI>();  // tile 0 has landed (tile 1 may still be in flight)
 
-  // keys of the computed tile that are real: 64, the chunk's remainder on a
-  // segment's last tile, 0 past the end (the loop runs in groups of three)
-  int m_c = 0;
-  auto valid_keys = [&](int it) {
-    const int v = it >= ntiles ? 0 : (m_c == p.tps - 1 ? p.t_last : KT);
-    if (++m_c == p.tps) m_c = 0;
-    return v;
+  // Keys of tile j that are real: 64, the chunk's remainder on a segment's last
+  // tile, 0 past the end (the loop runs in groups of three tiles).
+  auto valid_keys = [&](int j) __attribute__((always_inline)) {
+    if (j >= ntiles) return 0;
+    const int m = j - (j / u.tps) * u.tps;
+    return m == u.tps - 1 ? u.t_last : KT;
   };
 
-  // One tile: compute tile it from (kb, vb); the loads of tile it+2 go to
-  // (kn, vn), spread between the S^T MFMAs; tile it+3 is resolved for the next.
-  auto step = [&](int it, const uint16_t* kb, const uint16_t* vb, uint16_t* kn, uint16_t* vn) {
-    const int valid = valid_keys(it);
-    if (!wave_active) {
+  f32x16 sacc[2];
+  bf16x8 pb[4];
+
+  // S^T = K Q^T for one tile: two 32-key blocks, K operands two k-steps ahead.
+  // With (kn, vn), this wave's loads of the next tile to fetch are issued one
+  // row group per k-step between the MFMAs (scheduling fences keep the
+  // interleave). Each LDS address is one offset added to the buffer: the
+  // compiler tags LDS accesses with the buffer they touch only through a short
+  // chain of address steps.
+  auto qk = [&](const uint16_t* kb, uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
+    auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) ld.emit(i, p, kn, vn, wave);
-      ld.prepare(p, pages_lds, s, h, nseg);
-    } else {
-      // ---- S^T = K Q^T: two 32-key blocks; K operands two k-steps ahead, one
-      // row group of next-tile loads after each k-step (scheduling fences keep
-      // the interleave). Each LDS address is one offset added to the buffer:
-      // the compiler tags LDS accesses with the buffer they touch only through
-      // a short chain of address steps.
-      auto kload = [&](int kk, bf16x8* dst) {
+      for (int blk = 0; blk < 2; ++blk)
+        dst[blk] = *reinterpret_cast<const bf16x8*>(
+            kb + ((krow0 + 32 * blk) * D + ((2 * kk + g) ^ kx) * 8));
+    };
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
+    bf16x8 ka[3][2];
+    kload(0, ka[0]);
+    kload(1, ka[1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-          dst[blk] = *reinterpret_cast<const bf16x8*>(
-              kb + ((krow0 + 32 * blk) * D + ((2 * kk + g) ^ kx) * 8));
-      };
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      bf16x8 ka[3][2];
-      kload(0, ka[0]);
-      kload(1, ka[1]);
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
+                                                            0, 0, 0);
+      if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
+      if (kn != nullptr && kk < NI) ld.emit(kk, u, kn, vn, wave);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
-                                                              0, 0, 0);
-        if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
-        if (kk < NI) ld.emit(kk, p, kn, vn, wave);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      ld.prepare(p, pages_lds, s, h, nseg);
-      // V^T operand of one 16-key step for all DB blocks: two transposed reads each
-      auto vload = [&](int kk, bf16x8* dst) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int e0 = (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vb + e0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(vb + (e0 + 4 * D)));
-          dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-      };
-      // the first V^T operands load while the softmax runs
-      bf16x8 va[2][DB];
-      vload(0, va[0]);
-      // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
-      if (valid < KT) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int key = 32 * blk + 16 * (x >> 3) + 8 * g + (x & 7);
-            if (key >= valid) sacc[blk][x] = -INFINITY;
-          }
-      }
-      // ---- online softmax (exp2 domain) ------------------------------------
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
-#pragma unroll
-      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
-      mx = xlane32_max(mx) * p.c;
-      const bool raise = mx > m_run + kLazyTau;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = raise ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) oacc[i][x] *= alpha;
-      }
-      bf16x8 pb[4];
-      float lsum = 0.f;
+    }
+    if (kn != nullptr) resolve();
+  };
+
+  // Online softmax of the scores of tile j (exp2 domain): P as bf16 into pb.
+  // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int valid = valid_keys(j);
+    if (valid < KT) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], p.c, -m_run));
-          lsum += e;
-          pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(e);
+          const int key = 32 * blk + 16 * (x >> 3) + 8 * g + (x & 7);
+          if (key >= valid) sacc[blk][x] = -INFINITY;
         }
-      l_run += lsum;
-      // ---- O^T += V^T P^T : four 16-key steps, operands one step ahead ------
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk + 1 < 4) vload(kk + 1, va[(kk + 1) & 1]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0,
-                                                             0, 0);
-      }
     }
-
-    tile_barrier<2 * NI>();  // tile it+1 has landed; tile it+2 may still be in flight
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
+#pragma unroll
+    for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
+    mx = xlane32_max(mx) * u.c;
+    const bool raise = mx > m_run + kLazyTau;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) oacc[i][x] *= alpha;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], u.c, -m_run));
+        lsum += e;
+        pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(e);
+      }
+    l_run += lsum;
   };
 
-  // Whole groups of three (a tile past the end is fully masked and adds
-  // nothing), so that each step names its buffers statically.
-  for (int it = 0; it < ntiles; it += 3) {
-    step(it, k_lds0, v_lds0, k_lds2, v_lds2);
-    step(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
-    step(it + 2, k_lds2, v_lds2, k_lds1, v_lds1);
+  // O^T += V^T P^T for one tile: four 16-key steps, V^T operands (two
+  // transposed LDS reads per 32-row block) one step ahead.
+  auto pv = [&](const uint16_t* vb) __attribute__((always_inline)) {
+    auto vload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int e0 = (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + e0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + (e0 + 4 * D)));
+        dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    bf16x8 va[2][DB];
+    vload(0, va[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) vload(kk + 1, va[(kk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0,
+                                                           0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // G(j): O^T += V^T P^T of tile j and S^T = K Q^T of tile j+1, interleaved
+  // MFMA by MFMA so that consecutive MFMAs never share an accumulator (the
+  // score blocks recur every fourth MFMA, the output blocks every eighth).
+  // Operands: K two k-steps ahead, V one 16-key step ahead; with (kn, vn) this
+  // wave's loads of the next tile to fetch go out one row group per k-step.
+  auto gphase = [&](const uint16_t* vb, const uint16_t* kb, uint16_t* kn, uint16_t* vn)
+      __attribute__((always_inline)) {
+    auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        dst[blk] = *reinterpret_cast<const bf16x8*>(
+            kb + ((krow0 + 32 * blk) * D + ((2 * kk + g) ^ kx) * 8));
+    };
+    auto vload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int e0 = (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + e0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + (e0 + 4 * D)));
+        dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    constexpr int PV_PER_STEP = 4 * DB / KS;  // P.V MFMAs per Q.K^T k-step
+    f32x16 snew[2] = {f32x16{}, f32x16{}};
+    bf16x8 ka[3][2];
+    bf16x8 va[2][DB];
+    kload(0, ka[0]);
+    kload(1, ka[1]);
+    vload(0, va[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      // P.V MFMAs number PV_PER_STEP*t .. : 16-key step kk, output blocks db
+      const int pv0 = PV_PER_STEP * t;
+      const int kk = pv0 / DB;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        snew[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], snew[blk], 0,
+                                                            0, 0);
+        const int q = pv0 + blk * PV_PER_STEP / 2;
+#pragma unroll
+        for (int e = 0; e < PV_PER_STEP / 2; ++e) {
+          const int db = (q + e) % DB;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0,
+                                                             0, 0);
+        }
+      }
+      // operands of later steps go out after this step's MFMAs, so that each
+      // wait is for reads issued at least one step earlier
+      if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
+      if (pv0 % DB == 0 && kk + 1 < 4) vload(kk + 1, va[(kk + 1) & 1]);
+      if (kn != nullptr && t < NI) ld.emit(t, u, kn, vn, wave);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sacc[0] = snew[0];
+    sacc[1] = snew[1];
+  };
+
+  auto issue_all = [&](uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
+    resolve();
+  };
+
+  // Ping-pong: waves 0..3 (group A) and 4..7 (group B) share the four SIMDs
+  // one to one and run the same sequence one slot apart, so that while one
+  // wave of a SIMD runs MFMAs (G(j): P.V of tile j, then Q.K^T of tile j+1)
+  // the other runs the VALU softmax S of its current tile; a block-wide
+  // barrier ends every slot:
+  //   slot 0: A: Q.K^T(0)      B: -
+  //   slot 1: A: S(0)          B: Q.K^T(0)
+  //   slot 2: A: G(0)          B: S(0)
+  //   slot 3: A: S(1)          B: G(0)      ...
+  // In slot 2j+2 each wave issues its loads of tile j+2 (A inside the MFMAs of
+  // G(j), B before S(j)); they land by the end of slot 2j+3. Tile t lives in
+  // buffer t % 3 from its first use (slot 2t) to its last (slot 2t+3).
+  const bool grp_a = wave < NWAVES / 2;
+  // end of a slot: loads issued in this slot may stay in flight only in even
+  // slots, which for A are the Q.K^T slots and for B the softmax slots
+  auto end_qk_slot = [&]() __attribute__((always_inline)) {
+    if (grp_a) tile_barrier<2 * NI>();
+    else tile_barrier<0>();
+  };
+  auto end_s_slot = [&]() __attribute__((always_inline)) {
+    if (grp_a) tile_barrier<0>();
+    else tile_barrier<2 * NI>();
+  };
+
+  if (!grp_a) tile_barrier<2 * NI>();  // B sits out slot 0
+  if (wave_active) qk(k_lds0, nullptr, nullptr);
+  end_qk_slot();
+  if (wave_active) softmax(0);
+  if (!grp_a) issue_all(k_lds2, v_lds2);  // B: tile 2
+  end_s_slot();
+
+  // G(j) then S(j+1); (vb, kb): V of tile j and K of tile j+1; (kg, vg): where
+  // A's loads of tile j+2 go; (ks, vs): where B's loads of tile j+3 go.
+  auto slot_pair = [&](int j, const uint16_t* vb, const uint16_t* kb, uint16_t* kg, uint16_t* vg,
+                       uint16_t* ks, uint16_t* vs) __attribute__((always_inline)) {
+    if (wave_active) {
+      // the MFMA phase wins issue arbitration over the other wave's softmax
+      __builtin_amdgcn_s_setprio(1);
+      gphase(vb, kb, grp_a ? kg : nullptr, vg);
+      __builtin_amdgcn_s_setprio(0);
+    } else if (grp_a) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) ld.emit(i, u, kg, vg, wave);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    end_qk_slot();
+    if (wave_active) softmax(j + 1);
+    // B's loads go out after its softmax, when A's burst from the start of its
+    // MFMA slot has drained; A resolves its next tile here, off its MFMA slot
+    if (!grp_a) issue_all(ks, vs);
+    else resolve();
+    __builtin_amdgcn_sched_barrier(0);
+    end_s_slot();
+  };
+
+  for (int j = 0; j < ntiles; j += 3) {
+    slot_pair(j, v_lds0, k_lds1, k_lds2, v_lds2, k_lds0, v_lds0);
+    slot_pair(j + 1, v_lds1, k_lds2, k_lds0, v_lds0, k_lds1, v_lds1);
+    slot_pair(j + 2, v_lds2, k_lds0, k_lds1, v_lds1, k_lds2, v_lds2);
   }
+  if (grp_a) tile_barrier<0>();  // A's share of B's last slot
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
 
   // ---- epilogue: O = O^T / l, bf16 ----------------------------------------
   if (wave_active && qrow < T) {
@@ -701,9 +957,16 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     plan_xcd_order(pl, d.H, p, blocks);
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
     const bool fast = d.n_hist == 0 || d.P % KT == 0;
-    if (!fast && p.n_page_ids > kMaxPageIds)  // the per-lane path keeps the table in LDS
-      return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %d (page sizes "
-                  "that are a multiple of 64 have no such limit)", p.n_page_ids, kMaxPageIds);
+    if (fast) {  // the kernel keeps a table of tile sources in LDS
+      int max_seg = 0;
+      for (int i = 0; i < pl.n_active; ++i) max_seg = std::max(max_seg, pl.nseg[pl.order[i]]);
+      if (int64_t(max_seg) * p.tps > kMaxTiles)
+        return fail(WF_EUNSUPPORTED, "wf_attn_tick: %d chunks of %d tiles exceed %d tiles", max_seg,
+                    p.tps, kMaxTiles);
+    } else if (p.n_page_ids > kMaxPageIds) {  // the kernel keeps the page table in LDS
+      return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %d", p.n_page_ids,
+                  kMaxPageIds);
+    }
     if (d.D == 128)
       st = fast ? launch_attn<128, true>(p, unsigned(blocks), stream)
                 : launch_attn<128, false>(p, unsigned(blocks), stream);
