@@ -66,8 +66,8 @@ constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dealt round-ro
 constexpr int kXcdTable = 512;      // max (stage, head) groups in the XCD table
 // History page table held in LDS (ids of all history pages of one tick) when
 // pages are not a multiple of 64 tokens; otherwise a table of tile sources.
-constexpr int kMaxPageIds = 8192;
-constexpr int kMaxTiles = 2560;  // 64-key tiles per (stage, head): 40 KB of sources
+constexpr int kMaxPageIds = 4096;
+constexpr int kMaxTiles = 1536;  // 64-key tiles per (stage, head): 24 KB of sources
 
 struct AttnParams {
   const uint16_t* q;
@@ -399,9 +399,11 @@ attn_tick_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t k_lds1[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t k_lds2[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds3[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds0[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds2[KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds3[KT * D];
   __shared__ int32_t pages_lds[kFast ? 1 : kMaxPageIds];
   __shared__ uint4 tile_tab[kFast ? kMaxTiles : 1];
 
@@ -506,8 +508,16 @@ attn_tick_kernel(const AttnParams p) {
   resolve();
 #pragma unroll
   for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds1, v_lds1, wave);
-  resolve();  // tile 2, issued in the first loop slot
-  tile_barrier<2 * NI>();  // tile 0 has landed (tile 1 may still be in flight)
+  resolve();
+  const bool grp_a = wave < NWAVES / 2;
+  if (!grp_a) {  // B: tile 2 as well (A issues it in its first MFMA slot)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds2, v_lds2, wave);
+    resolve();
+  }
+  // tile 0 has landed (A: tile 1 may still be in flight; B: tiles 1 and 2)
+  if (grp_a) tile_barrier<2 * NI>();
+  else tile_barrier<4 * NI>();
 
   // Keys of tile j that are real: 64, the chunk's remainder on a segment's last
   // tile, 0 past the end (the loop runs in groups of three tiles).
@@ -648,7 +658,8 @@ attn_tick_kernel(const AttnParams p) {
       }
     };
     constexpr int PV_PER_STEP = 4 * DB / KS;  // P.V MFMAs per Q.K^T k-step
-    f32x16 snew[2] = {f32x16{}, f32x16{}};
+    sacc[0] = f32x16{};  // the previous scores were consumed by the last softmax
+    sacc[1] = f32x16{};
     bf16x8 ka[3][2];
     bf16x8 va[2][DB];
     kload(0, ka[0]);
@@ -662,7 +673,7 @@ attn_tick_kernel(const AttnParams p) {
       const int kk = pv0 / DB;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        snew[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], snew[blk], 0,
+        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], sacc[blk], 0,
                                                             0, 0);
         const int q = pv0 + blk * PV_PER_STEP / 2;
 #pragma unroll
@@ -679,75 +690,65 @@ attn_tick_kernel(const AttnParams p) {
       if (kn != nullptr && t < NI) ld.emit(t, u, kn, vn, wave);
       __builtin_amdgcn_sched_barrier(0);
     }
-    sacc[0] = snew[0];
-    sacc[1] = snew[1];
   };
 
-  auto issue_all = [&](uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
-    resolve();
-  };
 
   // Ping-pong: waves 0..3 (group A) and 4..7 (group B) share the four SIMDs
   // one to one and run the same sequence one slot apart, so that while one
-  // wave of a SIMD runs MFMAs (G(j): P.V of tile j, then Q.K^T of tile j+1)
-  // the other runs the VALU softmax S of its current tile; a block-wide
-  // barrier ends every slot:
+  // wave of a SIMD runs MFMAs (G(j): P.V of tile j, then Q.K^T of tile j+1,
+  // interleaved) the other runs the VALU softmax S of its current tile; a
+  // block-wide barrier ends every slot:
   //   slot 0: A: Q.K^T(0)      B: -
   //   slot 1: A: S(0)          B: Q.K^T(0)
   //   slot 2: A: G(0)          B: S(0)
   //   slot 3: A: S(1)          B: G(0)      ...
-  // In slot 2j+2 each wave issues its loads of tile j+2 (A inside the MFMAs of
-  // G(j), B before S(j)); they land by the end of slot 2j+3. Tile t lives in
-  // buffer t % 3 from its first use (slot 2t) to its last (slot 2t+3).
-  const bool grp_a = wave < NWAVES / 2;
-  // end of a slot: loads issued in this slot may stay in flight only in even
-  // slots, which for A are the Q.K^T slots and for B the softmax slots
+  // Tile t lives in buffer t % 4 from its first use (slot 2t) to its last
+  // (slot 2t+3). Each wave issues its loads inside its MFMA slot: A those of
+  // tile j+2 in G(j) (slot 2j+2, needed from slot 2j+4), B those of tile j+3
+  // in G(j) (slot 2j+3, needed from slot 2j+6); B loads tiles 0-2 up front.
+  // A's loads of a slot pair land by its end; B's by the end of the next pair.
   auto end_qk_slot = [&]() __attribute__((always_inline)) {
-    if (grp_a) tile_barrier<2 * NI>();
-    else tile_barrier<0>();
+    tile_barrier<2 * NI>();
   };
   auto end_s_slot = [&]() __attribute__((always_inline)) {
     if (grp_a) tile_barrier<0>();
     else tile_barrier<2 * NI>();
   };
 
-  if (!grp_a) tile_barrier<2 * NI>();  // B sits out slot 0
+  if (!grp_a) tile_barrier<4 * NI>();  // B sits out slot 0
   if (wave_active) qk(k_lds0, nullptr, nullptr);
-  end_qk_slot();
+  end_qk_slot();  // B: tile 1 has landed (tile 2 may be in flight)
   if (wave_active) softmax(0);
-  if (!grp_a) issue_all(k_lds2, v_lds2);  // B: tile 2
   end_s_slot();
 
-  // G(j) then S(j+1); (vb, kb): V of tile j and K of tile j+1; (kg, vg): where
-  // A's loads of tile j+2 go; (ks, vs): where B's loads of tile j+3 go.
-  auto slot_pair = [&](int j, const uint16_t* vb, const uint16_t* kb, uint16_t* kg, uint16_t* vg,
-                       uint16_t* ks, uint16_t* vs) __attribute__((always_inline)) {
+  // G(j) then S(j+1); (vb, kb): V of tile j and K of tile j+1; (kn, vn): where
+  // this wave's loads go (A: tile j+2, B: tile j+3).
+  auto slot_pair = [&](int j, const uint16_t* vb, const uint16_t* kb, uint16_t* ka_, uint16_t* va_,
+                       uint16_t* kb_, uint16_t* vb_) __attribute__((always_inline)) {
+    uint16_t* kn = grp_a ? ka_ : kb_;
+    uint16_t* vn = grp_a ? va_ : vb_;
     if (wave_active) {
       // the MFMA phase wins issue arbitration over the other wave's softmax
       __builtin_amdgcn_s_setprio(1);
-      gphase(vb, kb, grp_a ? kg : nullptr, vg);
+      gphase(vb, kb, kn, vn);
       __builtin_amdgcn_s_setprio(0);
-    } else if (grp_a) {
+    } else {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) ld.emit(i, u, kg, vg, wave);
+      for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
     }
     __builtin_amdgcn_sched_barrier(0);
     end_qk_slot();
     if (wave_active) softmax(j + 1);
-    // B's loads go out after its softmax, when A's burst from the start of its
-    // MFMA slot has drained; A resolves its next tile here, off its MFMA slot
-    if (!grp_a) issue_all(ks, vs);
-    else resolve();
+    resolve();  // the next tile this wave loads, off the MFMA slot
     __builtin_amdgcn_sched_barrier(0);
     end_s_slot();
   };
 
-  for (int j = 0; j < ntiles; j += 3) {
-    slot_pair(j, v_lds0, k_lds1, k_lds2, v_lds2, k_lds0, v_lds0);
-    slot_pair(j + 1, v_lds1, k_lds2, k_lds0, v_lds0, k_lds1, v_lds1);
-    slot_pair(j + 2, v_lds2, k_lds0, k_lds1, v_lds1, k_lds2, v_lds2);
+  for (int j = 0; j < ntiles; j += 4) {
+    slot_pair(j, v_lds0, k_lds1, k_lds2, v_lds2, k_lds3, v_lds3);
+    slot_pair(j + 1, v_lds1, k_lds2, k_lds3, v_lds3, k_lds0, v_lds0);
+    slot_pair(j + 2, v_lds2, k_lds3, k_lds0, v_lds0, k_lds1, v_lds1);
+    slot_pair(j + 3, v_lds3, k_lds0, k_lds1, v_lds1, k_lds2, v_lds2);
   }
   if (grp_a) tile_barrier<0>();  // A's share of B's last slot
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
