@@ -139,8 +139,10 @@ wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t*
 /* Errors: WF_EINVAL for bad sizes, masks, pointers (NULL or not 16-byte      */
 /* aligned), P not a positive multiple of 16, n_hist*ceil(T/P) > num_pages;   */
 /* WF_EUNSUPPORTED for D not 64/128, n_hist + S + 1 > 32, T > 2^24,           */
-/* T*P >= 2^32, num_pages*P >= 2^31, n_hist*ceil(T/P) > 8192 (the page       */
-/* table is staged in LDS);                                                   */
+/* T*P >= 2^32, num_pages*P >= 2^31, and tables the kernel stages in LDS    */
+/* that would not fit: with P a multiple of 64, more than 1536 64-key tiles   */
+/* in one slot's context (segments * ceil(T/64)); otherwise                   */
+/* n_hist*ceil(T/P) > 4096 page ids;                                          */
 /* WF_EHIP if the launch fails. T = 0 or active_mask = 0 is a no-op.          */
 /* ------------------------------------------------------------------------ */
 typedef struct wf_tick_desc {

@@ -270,6 +270,10 @@ def test_tick_validation_pointers_and_pool():
         wf.wf_attn_tick_desc(_desc(wf, **base, **pools, n_hist=3, P=16, T=60000,
                                    num_pages=40000), stream=0)
     assert e.value.status == CODES["EUNSUPPORTED"]
+    with pytest.raises(wf.WfError) as e:  # tile-source table larger than the LDS budget
+        wf.wf_attn_tick_desc(_desc(wf, **base, **pools, n_hist=25, num_pages=2000), stream=0)
+    assert e.value.status == CODES["EUNSUPPORTED"]
+    assert "tiles" in wf.last_error()
     # empty ticks are accepted without touching the device
     wf.wf_attn_tick_desc(_desc(wf, T=0), stream=0)
     wf.wf_attn_tick_desc(_desc(wf, active_mask=0), stream=0)
