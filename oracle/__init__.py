@@ -11,12 +11,16 @@ from the Wave Forcing pages:
   * page_model: a dict-based page store and a FIFO free-list / rolling-window
     model of the clean K/V history;
   * brute_force: per-query visible-key lists built by the rule, summed with
-    math.fsum (tiny shapes only).
+    math.fsum (tiny shapes only);
+  * rope: rotary position embedding of a chunk's keys over its latent grid,
+    the anchor's re-rotation after a window shift, and correctly rounded
+    float64 -> bf16 conversion of the rotated keys.
 
 Parity status: every function is pinned by the `-m "not gpu"` tests in
-tests/test_oracle_pins.py and tests/test_page_model.py (brute force, a library
-attention routine for the dense special case, mask invariances, closed forms
-and hand-derived tables under tests/golden/). No function is "parity unpinned".
+tests/test_oracle_pins.py, tests/test_page_model.py and tests/test_rope_oracle.py
+(brute force, a library attention routine for the dense special case, mask
+invariances, closed forms, rotation invariants, hand-derived tables under
+tests/golden/ and a library bf16 conversion). No function is "parity unpinned".
 """
 from .wave_attention import (  # noqa: F401
     decode_bf16,
@@ -29,8 +33,18 @@ from .wave_attention import (  # noqa: F401
     token_mask,
     attention_tick,
     attention_tick_paged,
+    attention_tick_fully_paged,
     keys_per_stage,
     useful_flops,
 )
 from .page_model import PageStore, FifoPageModel, PageModelError  # noqa: F401
 from .brute_force import brute_force_tick  # noqa: F401
+from .rope import (  # noqa: F401
+    default_split,
+    token_coords,
+    pair_axis_and_frequency,
+    rope_angles,
+    rope,
+    anchor_frame0,
+    round_to_bf16_bits,
+)

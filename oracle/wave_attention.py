@@ -224,6 +224,26 @@ def attention_tick_paged(q, k, v, store, hist_pages: Sequence[Sequence[int]], S:
     return attention_tick(q, k, v, hk, hv, S, active_mask, scale, **kw)
 
 
+def attention_tick_fully_paged(q, store, hist_pages: Sequence[Sequence[int]],
+                               live_pages: Sequence[Optional[Sequence[int]]], S: int,
+                               active_mask: int, scale: float, **kw) -> Dict[int, np.ndarray]:
+    """Same as attention_tick with every K/V segment read from the page store: the
+    history through hist_pages and live slot j through live_pages[j] (None for a
+    slot that is not active). [full text] Appendix B.8, Eq. (13): the K/V arrays
+    hold the anchor, the bounded history, the live store and the denoising chunks."""
+    T, H, D = q.shape[1], q.shape[2], q.shape[3]
+    hk, hv = store.gather(hist_pages, T)
+    lk = np.zeros((S + 1, T, H, D), np.uint16)
+    lv = np.zeros_like(lk)
+    for j in range(S + 1):
+        if (active_mask >> j) & 1:
+            if live_pages[j] is None:
+                raise ValueError(f"active slot {j} has no pages")
+            kk, vv = store.gather([live_pages[j]], T)
+            lk[j], lv[j] = kk[0], vv[0]
+    return attention_tick(q, lk, lv, hk, hv, S, active_mask, scale, **kw)
+
+
 # ----------------------------------------------------------------------------
 # key counts and useful FLOPs
 # ----------------------------------------------------------------------------
