@@ -57,7 +57,7 @@ const char* wf_last_error(void);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t wf_abi_version(void);
-#define WF_ABI_VERSION 1
+#define WF_ABI_VERSION 2
 
 /* ------------------------------------------------------------------------ */
 /* Page table: host-only state for one request's attention pages.            */
@@ -117,6 +117,47 @@ wf_status wf_store_paged(const void* k_src, const void* v_src, void* k_pool, voi
                          int32_t num_pages, int32_t P, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* wf_rope_store_paged — a producer's write of one chunk's K and V into its   */
+/* pages, with the rotary position embedding applied to K on the way.        */
+/* [summary] Methodology 3 and [full text] Appendix B.1: K/V are published     */
+/* after the QKV projection and RoPE; [full text] Appendix B.8, Eq. (13): the  */
+/* K/V arrays hold every chunk of the context, live ones included; [full      */
+/* text] Appendix B.3: the anchor keeps its unrotated key and is rotated again */
+/* when the window shifts (call with v_src = v_pool = NULL and the anchor's   */
+/* pages: only K is rewritten).                                               */
+/* Rotation (the pages give no formula; the common rotary form per axis of    */
+/* the latent grid): token t of a grid[0] x grid[1] x grid[2] (frames x rows x */
+/* columns, row-major) chunk has coordinates (frame0 + t/(R*C), (t/C)%R, t%C); */
+/* channel pair (2i, 2i+1) of every head turns by coordinate * frequency:     */
+/* (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a). Pairs are grouped   */
+/* by axis: the first split[0] channels follow the frame, the next split[1]   */
+/* the row, the last split[2] the column; pair i' of a group of d channels has */
+/* frequency theta^(-2i'/d). fp32 arithmetic, bf16 result rounded to nearest  */
+/* even; V is copied bit for bit.                                             */
+/* Placement as wf_store_paged: token t -> slot t % P of page page_ids[t/P],   */
+/* slots past token T-1 of the last page written as zero (K, and V if given). */
+/* k_src (pre-rotation keys), v_src: device bf16 [T][H][D]; pools: device bf16 */
+/* [num_pages][P][H][D]; page_ids: device int32 [ceil(T/P)]. 16-byte aligned. */
+/* Errors: WF_EINVAL for NULL pointers (v_src and v_pool must be both NULL or  */
+/* both set), grid not positive or not holding T tokens, frame0 < 0 or        */
+/* frame0 + grid[0] > 2^24, odd or negative split parts, split sum != D,       */
+/* theta not positive and finite, ceil(T/P) > num_pages; WF_EUNSUPPORTED for  */
+/* D not 64/128 or ceil(T/P)*P >= 2^31; WF_EHIP if the launch fails. With   */
+/* valid sizes and D, T = 0 is a no-op.                                       */
+/* ------------------------------------------------------------------------ */
+typedef struct wf_rope_desc {
+  int32_t grid[3];  /* latent grid of one chunk: frames, rows, columns; product = T */
+  int32_t frame0;   /* latent frame index of the chunk's first frame (>= 0)         */
+  int32_t split[3]; /* channels per axis (frame, row, column): even, sum = D         */
+  float theta;      /* frequency base, e.g. 10000                                   */
+} wf_rope_desc;
+
+wf_status wf_rope_store_paged(const void* k_src, const void* v_src, void* k_pool, void* v_pool,
+                              const int32_t* page_ids, int32_t T, int32_t H, int32_t D,
+                              int32_t num_pages, int32_t P, const wf_rope_desc* rope,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* wf_gather_paged — diagnostic inverse of the store: copy n_chunks chunks    */
 /* from pool pages into contiguous k_dst, v_dst bf16 [n_chunks][T][H][D].     */
 /* page_ids: device int32 [n_chunks][ceil(T/P)]. Same alignment rules.        */
@@ -136,13 +177,15 @@ wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t*
 /* j < s are never enumerated (block skip), so their K/V is never read.        */
 /* Arithmetic: bf16 MFMA products, fp32 accumulation and softmax state, P     */
 /* rounded to bf16 for the P.V product, bf16 output (round to nearest even).  */
+/* With live_pages set, every key of the context is read through pages: the  */
+/* results equal those of the same tick with the live K/V in k and v.         */
 /* Errors: WF_EINVAL for bad sizes, masks, pointers (NULL or not 16-byte      */
 /* aligned), P not a positive multiple of 16, n_hist*ceil(T/P) > num_pages;   */
 /* WF_EUNSUPPORTED for D not 64/128, n_hist + S + 1 > 32, T > 2^24,           */
 /* T*P >= 2^32, num_pages*P >= 2^31, and tables the kernel stages in LDS    */
 /* that would not fit: with P a multiple of 64, more than 1536 64-key tiles   */
-/* in one slot's context (segments * ceil(T/64)); otherwise                   */
-/* n_hist*ceil(T/P) > 4096 page ids;                                          */
+/* in one slot's context (segments * ceil(T/64)); otherwise more than 4096    */
+/* page ids (n_hist*ceil(T/P), plus (S+1)*ceil(T/P) with live_pages);         */
 /* WF_EHIP if the launch fails. T = 0 or active_mask = 0 is a no-op.          */
 /* ------------------------------------------------------------------------ */
 typedef struct wf_tick_desc {
@@ -151,17 +194,22 @@ typedef struct wf_tick_desc {
   int32_t T, H, D;        /* tokens per chunk (>= 0), heads (>= 1), head dim 64|128 */
   float scale;            /* softmax scale (> 0, finite), e.g. 1/sqrt(D)            */
   const void* q;          /* device bf16 [S+1][T][H][D]                             */
-  const void* k;          /* device bf16 [S+1][T][H][D]                             */
-  const void* v;          /* device bf16 [S+1][T][H][D]                             */
+  const void* k;          /* device bf16 [S+1][T][H][D] (unused with live_pages)    */
+  const void* v;          /* device bf16 [S+1][T][H][D] (unused with live_pages)    */
   void* o;                /* device bf16 [S+1][T][H][D]; rows of inactive slots are */
                           /* left untouched                                          */
-  const void* k_pool;     /* device bf16 [num_pages][P][H][D] (NULL iff n_hist = 0) */
-  const void* v_pool;     /* device bf16 [num_pages][P][H][D] (NULL iff n_hist = 0) */
+  const void* k_pool;     /* device bf16 [num_pages][P][H][D]; needed when n_hist > 0 */
+  const void* v_pool;     /* or live_pages is set, ignored otherwise                */
   int32_t num_pages, P;   /* pool size in pages; tokens per page (multiple of 16)   */
   const int32_t* hist_pages; /* device int32 [n_hist][ceil(T/P)], oldest first      */
   int32_t n_hist;         /* clean history chunks, n_hist + S + 1 <= 32            */
   int32_t hist_first[WF_MAX_STAGES]; /* per slot: first visible history chunk,     */
                           /* 0 = all, n_hist = none (per-rank history budgets)      */
+  const int32_t* live_pages; /* device int32 [S+1][ceil(T/P)]: the pages holding    */
+                          /* each live slot's K/V (fully paged context, [full text] */
+                          /* Appendix B.8, Eq. (13); rows of inactive slots are not */
+                          /* read), or NULL: live K/V come from k and v, which may  */
+                          /* then be NULL when this is set                          */
 } wf_tick_desc;
 
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);

@@ -42,11 +42,39 @@ def test_library_exports_every_header_function():
     for n in names:
         assert hasattr(lib, n), f"{n} declared in wf_attn.h but not exported"
     assert sorted(wf.EXPORTED_SYMBOLS) == names
-    assert wf.abi_version() == 1
+    declared = int(re.search(r"#define WF_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert wf.abi_version() == declared
     nm = subprocess.run(["nm", "-D", "--defined-only", build_lib.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
     exported = set(re.findall(r" T (wf_[a-z0-9_]+)$", nm, flags=re.M))
     assert exported == set(names)
+
+
+def test_descriptor_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of wf_tick_desc and wf_rope_desc have the C layout:
+    size and every field offset, as a host compiler lays out the header."""
+    wf = _wfattn()
+    structs = {"wf_tick_desc": wf.WfTickDesc, "wf_rope_desc": wf.WfRopeDesc}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "wf_attn.h"', "int main() {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True,
+                   capture_output=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        cname, field, val = line.split()
+        got[(cname, field)] = int(val)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == __import__("ctypes").sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
 
 
 # ---------------------------------------------------------------------------
@@ -294,6 +322,66 @@ def test_store_gather_validation():
     # zero-size calls are no-ops
     assert lib.wf_store_paged(None, None, None, None, None, 0, 2, 64, 8, 16, None) == 0
     assert lib.wf_gather_paged(None, None, None, 3, None, None, 0, 2, 64, 8, 16, None) == 0
+
+
+def test_tick_validation_live_pages():
+    """A fully paged tick needs the pools but not k and v; the page-id budget of
+    the non-64-multiple page path counts the live slots' pages too."""
+    wf = _wfattn()
+    fake = 1 << 20
+    d = _desc(wf, q=fake, o=fake)
+    d.live_pages = fake
+    with pytest.raises(wf.WfError) as e:  # no pools
+        wf.wf_attn_tick_desc(d, stream=0)
+    assert e.value.status == CODES["EINVAL"]
+    d = _desc(wf, q=fake, o=fake, k_pool=fake, v_pool=fake, num_pages=50)
+    d.live_pages = fake
+    with pytest.raises(wf.WfError) as e:  # a chunk needs 74 pages, the pool has 50
+        wf.wf_attn_tick_desc(d, stream=0)
+    assert e.value.status == CODES["EINVAL"]
+    d = _desc(wf, q=fake, o=fake, k_pool=fake, v_pool=fake, P=16, T=9000, num_pages=40000,
+              hist_pages=fake, n_hist=3)
+    d.live_pages = fake
+    # (3 + 5) * 563 page ids > 4096 (3 * 563 alone would fit)
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_attn_tick_desc(d, stream=0)
+    assert e.value.status == CODES["EUNSUPPORTED"]
+    assert "page table" in wf.last_error()
+    # without live_pages k and v are still required
+    d = _desc(wf, q=fake, o=fake, k_pool=fake, v_pool=fake)
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_attn_tick_desc(d, stream=0)
+    assert e.value.status == CODES["EINVAL"]
+
+
+def test_rope_store_validation():
+    wf = _wfattn()
+    lib = wf.library()
+    fake = 1 << 20
+
+    def call(T=4680, H=12, D=128, num_pages=4096, P=64, grid=(3, 30, 52), frame0=0,
+             split=(44, 42, 42), theta=10000.0, k=fake, v=fake, kp=fake, vp=fake, ids=fake,
+             null_desc=False):
+        r = None if null_desc else wf.make_rope_desc(grid, frame0, split, theta, D)
+        return lib.wf_rope_store_paged(k, v, kp, vp, ids, T, H, D, num_pages, P,
+                                       None if r is None else __import__("ctypes").byref(r), None)
+
+    E, U = CODES["EINVAL"], CODES["EUNSUPPORTED"]
+    assert call(null_desc=True) == E
+    assert call(grid=(3, 30, 51)) == E          # does not hold T tokens
+    assert call(grid=(0, 30, 52)) == E
+    assert call(frame0=-1) == E
+    assert call(frame0=(1 << 24) - 2) == E      # frame coordinates past 2^24
+    assert call(split=(43, 43, 42)) == E        # odd parts
+    assert call(split=(44, 42, 40)) == E        # sum != D
+    assert call(theta=0.0) == E
+    assert call(theta=float("nan")) == E
+    assert call(D=96, split=(32, 32, 32)) == U
+    assert call(k=None) == E
+    assert call(v=None) == E                    # v_src without v_pool or the reverse
+    assert call(kp=fake + 8) == E               # misaligned
+    assert call(num_pages=10) == E              # the chunk needs 74 pages
+    assert call(T=0, grid=(1, 1, 1)) == 0       # empty chunk: no-op
 
 
 @pytest.mark.parametrize("name", ["tiny", "wan13_4step", "wan13_5step", "wan14b_4step"])

@@ -77,6 +77,8 @@ struct AttnParams {
   const uint16_t* k_pool;
   const uint16_t* v_pool;
   const int32_t* hist_pages;
+  const int32_t* live_pages;  // NULL: live K/V from k and v
+  int32_t n_hist;
   int32_t T, H, P, ppc;
   int32_t tps;            // tiles per chunk, ceil(T / 64)
   int32_t t_last;         // keys in a chunk's last tile, T - 64 * (tps - 1)
@@ -84,7 +86,7 @@ struct AttnParams {
   float c;                // scale * log2(e)
   int32_t ntq;            // query tiles per chunk
   int32_t items_per_stage;  // H * ntq
-  int32_t n_page_ids;     // n_hist * ppc entries of hist_pages
+  int32_t n_page_ids;     // page ids staged in LDS (non-fast path): history, then live
   // XCD-aware order: block b runs on XCD b % 8 (round-robin dispatch); its
   // (b / 8)-th item is query tile (b / 8) % ntq of group xcd_groups[x][(b / 8) / ntq],
   // group = rank * H + head. Blocks past an XCD's list exit at once.
@@ -309,7 +311,9 @@ struct TileLoader {
     if (sg != cur_seg) {  // entering a segment: its code, once
       cur_seg = sg;
       const int code = uniform_i32(p.seg[s][sg]);
-      if (code >= 0) {  // live chunk `code` of the tick's q/k/v
+      if (code >= 0 && p.live_pages) {  // live chunk `code` through its pages
+        hist_c = uniform_i32(p.n_hist) + code;
+      } else if (code >= 0) {  // live chunk `code` of the tick's q/k/v
         hist_c = -1;
         const uint64_t e = uint64_t(code) * uint64_t(u.T) * u.row_bytes;
         seg_k = u.k + e;
@@ -445,14 +449,15 @@ attn_tick_kernel(const AttnParams p) {
       const int code = p.seg[s][sg];
       const uint32_t t0 = uint32_t(KT) * uint32_t(mm);
       uint64_t kr, vr;
-      if (code >= 0) {  // live chunk `code`
+      if (code >= 0 && !p.live_pages) {  // live chunk `code`, contiguous
         const uint64_t e = (uint64_t(code) * uint32_t(u.T) + t0) * u.row_bytes;
         kr = reinterpret_cast<uint64_t>(u.k + e);
         vr = reinterpret_cast<uint64_t>(u.v + e);
-      } else {  // history chunk: the tile is rows t0 % P .. of one page
-        const int c = -code - 1;
+      } else {  // history chunk or paged live chunk: rows t0 % P .. of one page
+        const int32_t* ids = code >= 0 ? p.live_pages + code * u.ppc
+                                       : p.hist_pages + (-code - 1) * u.ppc;
         const uint32_t pg = t0 / uint32_t(u.P);
-        const int pid = p.hist_pages[c * u.ppc + int(pg)];
+        const int pid = ids[int(pg)];
         const uint64_t prow = uint64_t(uint32_t(pid)) * uint32_t(u.P) + (t0 - pg * uint32_t(u.P));
         kr = reinterpret_cast<uint64_t>(u.k_pool + prow * u.row_bytes);
         vr = reinterpret_cast<uint64_t>(u.v_pool + prow * u.row_bytes);
@@ -460,8 +465,10 @@ attn_tick_kernel(const AttnParams p) {
       kr |= (mm == u.tps - 1) ? 1u : 0u;  // bases are 16-byte aligned: bit 0 is free
       tile_tab[t] = make_uint4(uint32_t(kr), uint32_t(kr >> 32), uint32_t(vr), uint32_t(vr >> 32));
     }
-  } else {  // page table of the history into LDS
-    for (int i = tid; i < p.n_page_ids; i += NTHREADS) pages_lds[i] = p.hist_pages[i];
+  } else {  // page ids into LDS: history chunks, then (paged) live slots
+    const int nh = p.n_hist * p.ppc;
+    for (int i = tid; i < p.n_page_ids; i += NTHREADS)
+      pages_lds[i] = i < nh ? p.hist_pages[i] : p.live_pages[i - nh];
   }
   __syncthreads();
 
@@ -866,15 +873,18 @@ int32_t validate_tick(const wf_tick_desc* d) {
       return fail(WF_EINVAL, "wf_attn_tick: hist_first[%d] = %d outside [0, %d]", s,
                   d->hist_first[s], d->n_hist);
   if (d->T == 0 || d->active_mask == 0) return WF_OK;
-  if (!d->q || !d->k || !d->v || !d->o)
-    return fail(WF_EINVAL, "wf_attn_tick: q, k, v and o must be non-NULL");
-  if (!aligned16(d->q) || !aligned16(d->k) || !aligned16(d->v) || !aligned16(d->o))
+  const bool live_paged = d->live_pages != nullptr;
+  if (!d->q || !d->o || (!live_paged && (!d->k || !d->v)))
+    return fail(WF_EINVAL, "wf_attn_tick: q, o (and k, v without live_pages) must be non-NULL");
+  if (!aligned16(d->q) || !aligned16(d->o) ||
+      (!live_paged && (!aligned16(d->k) || !aligned16(d->v))))
     return fail(WF_EINVAL, "wf_attn_tick: q, k, v and o must be 16-byte aligned");
   if (int64_t(d->T) > (int64_t(1) << 24))
     return fail(WF_EUNSUPPORTED, "wf_attn_tick: T = %d too large", d->T);
-  if (d->n_hist > 0) {
-    if (!d->k_pool || !d->v_pool || !d->hist_pages)
-      return fail(WF_EINVAL, "wf_attn_tick: n_hist > 0 needs k_pool, v_pool and hist_pages");
+  if (d->n_hist > 0 || live_paged) {
+    if (!d->k_pool || !d->v_pool || (d->n_hist > 0 && !d->hist_pages))
+      return fail(WF_EINVAL,
+                  "wf_attn_tick: n_hist > 0 or live_pages needs k_pool, v_pool (and hist_pages)");
     if (!aligned16(d->k_pool) || !aligned16(d->v_pool))
       return fail(WF_EINVAL, "wf_attn_tick: pools must be 16-byte aligned");
     if (d->P <= 0 || d->P % 16 != 0)
@@ -882,6 +892,9 @@ int32_t validate_tick(const wf_tick_desc* d) {
                   d->P);
     if (d->num_pages <= 0) return fail(WF_EINVAL, "wf_attn_tick: num_pages = %d", d->num_pages);
     const int64_t ppc = (int64_t(d->T) + d->P - 1) / d->P;
+    if (ppc > d->num_pages)
+      return fail(WF_EINVAL, "wf_attn_tick: a chunk needs %lld pages, pool has %d",
+                  static_cast<long long>(ppc), d->num_pages);
     if (int64_t(d->n_hist) * ppc > d->num_pages)
       return fail(WF_EINVAL, "wf_attn_tick: n_hist * ceil(T/P) = %lld exceeds num_pages = %d",
                   static_cast<long long>(int64_t(d->n_hist) * ppc), d->num_pages);
@@ -923,24 +936,38 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     if (d.T == 0 || d.active_mask == 0) return WF_OK;
     StagePlan pl;
     plan_stages(d, pl);
-    const int32_t ppc = d.n_hist > 0 ? int32_t((int64_t(d.T) + d.P - 1) / d.P) : 0;
+    const bool live_paged = d.live_pages != nullptr;
+    const bool paged = d.n_hist > 0 || live_paged;
+    const int32_t ppc = paged ? int32_t((int64_t(d.T) + d.P - 1) / d.P) : 0;
     if (d.n_hist > 0 && check_pages_enabled()) {
       st = check_device_pages(d.hist_pages, int64_t(d.n_hist) * ppc, d.num_pages, stream,
                               "wf_attn_tick");
       if (st != WF_OK) return st;
     }
+    if (live_paged && check_pages_enabled()) {
+      for (int j = 0; j <= d.S; ++j) {
+        if (!((d.active_mask >> j) & 1u)) continue;
+        st = check_device_pages(d.live_pages + int64_t(j) * ppc, ppc, d.num_pages, stream,
+                                "wf_attn_tick (live_pages)");
+        if (st != WF_OK) return st;
+      }
+    }
     AttnParams p;
     std::memset(&p, 0, sizeof(p));
     p.q = static_cast<const uint16_t*>(d.q);
-    p.k = static_cast<const uint16_t*>(d.k);
-    p.v = static_cast<const uint16_t*>(d.v);
-    p.o = static_cast<uint16_t*>(d.o);
     p.k_pool = static_cast<const uint16_t*>(d.k_pool);
     p.v_pool = static_cast<const uint16_t*>(d.v_pool);
+    // with paged live slots k and v are never read (kept non-NULL for the
+    // head-offset arithmetic)
+    p.k = live_paged ? p.k_pool : static_cast<const uint16_t*>(d.k);
+    p.v = live_paged ? p.v_pool : static_cast<const uint16_t*>(d.v);
+    p.o = static_cast<uint16_t*>(d.o);
     p.hist_pages = d.hist_pages;
+    p.live_pages = d.live_pages;
+    p.n_hist = d.n_hist;
     p.T = d.T;
     p.H = d.H;
-    p.P = d.n_hist > 0 ? d.P : 16;
+    p.P = paged ? d.P : 16;
     p.ppc = ppc;
     p.tps = (d.T + KT - 1) / KT;
     p.t_last = d.T - KT * (p.tps - 1);
@@ -948,7 +975,7 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     p.c = float(double(d.scale) * 1.4426950408889634);
     p.ntq = (d.T + QROWS - 1) / QROWS;
     p.items_per_stage = d.H * p.ntq;
-    p.n_page_ids = d.n_hist * ppc;
+    p.n_page_ids = (d.n_hist + (live_paged ? d.S + 1 : 0)) * ppc;
     for (int i = 0; i < pl.n_active; ++i) p.stage_of_rank[i] = pl.order[i];
     for (int s = 0; s <= d.S; ++s) {
       p.nseg[s] = pl.nseg[s];
@@ -957,7 +984,7 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
     plan_xcd_order(pl, d.H, p, blocks);
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
-    const bool fast = d.n_hist == 0 || d.P % KT == 0;
+    const bool fast = !paged || d.P % KT == 0;
     if (fast) {  // the kernel keeps a table of tile sources in LDS
       int max_seg = 0;
       for (int i = 0; i < pl.n_active; ++i) max_seg = std::max(max_seg, pl.nseg[pl.order[i]]);

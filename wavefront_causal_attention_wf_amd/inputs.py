@@ -74,6 +74,19 @@ CONFIGS = {
 }
 
 
+# Latent grid of one chunk (frames, rows, columns): 3 latent frames of a 60 x 104
+# latent patchified 2 x 2, i.e. 30 x 52 tokens per frame, 4680 tokens per chunk.
+WAN_CHUNK_GRID = (3, 30, 52)
+
+
+def chunk_grid(T: int) -> tuple:
+    """Latent grid of a T-token chunk: the Wan chunk grid at T = 4680, else T
+    frames of a single token (a grid only the rotary embedding reads)."""
+    if T == 4680:
+        return WAN_CHUNK_GRID
+    return (T, 1, 1)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (round-to-nearest-even); return the uint16 bits.
 

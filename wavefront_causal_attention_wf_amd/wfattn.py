@@ -48,7 +48,14 @@ class WfTickDesc(ctypes.Structure):
                 ("scale", ctypes.c_float),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp),
                 ("k_pool", _vp), ("v_pool", _vp), ("num_pages", _i32), ("P", _i32),
-                ("hist_pages", _vp), ("n_hist", _i32), ("hist_first", _i32 * MAX_STAGES)]
+                ("hist_pages", _vp), ("n_hist", _i32), ("hist_first", _i32 * MAX_STAGES),
+                ("live_pages", _vp)]
+
+
+class WfRopeDesc(ctypes.Structure):
+    """Mirror of wf_rope_desc."""
+    _fields_ = [("grid", _i32 * 3), ("frame0", _i32), ("split", _i32 * 3),
+                ("theta", ctypes.c_float)]
 
 
 _lib.wf_last_error.restype = ctypes.c_char_p
@@ -64,18 +71,21 @@ _lib.wf_page_table_export.argtypes = [_vp, _i32p, _i32, _i32p]
 _lib.wf_page_table_num_free.argtypes = [_vp, _i32p]
 _lib.wf_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
 _lib.wf_gather_paged.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
+_lib.wf_rope_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                     ctypes.POINTER(WfRopeDesc), _vp]
 _lib.wf_attn_tick.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
 _lib.wf_tick_useful_flops.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_double)]
 for _f in ("wf_page_table_create", "wf_page_table_pages_per_chunk", "wf_page_table_alloc_chunk",
            "wf_page_table_commit", "wf_page_table_export", "wf_page_table_num_free",
-           "wf_store_paged", "wf_gather_paged", "wf_attn_tick", "wf_tick_useful_flops"):
+           "wf_store_paged", "wf_gather_paged", "wf_rope_store_paged", "wf_attn_tick",
+           "wf_tick_useful_flops"):
     getattr(_lib, _f).restype = _i32
 
 EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
                     "wf_page_table_destroy", "wf_page_table_pages_per_chunk",
                     "wf_page_table_alloc_chunk", "wf_page_table_commit", "wf_page_table_export",
                     "wf_page_table_num_free", "wf_store_paged", "wf_gather_paged",
-                    "wf_attn_tick", "wf_tick_useful_flops")
+                    "wf_rope_store_paged", "wf_attn_tick", "wf_tick_useful_flops")
 
 
 def _check(status: int, where: str) -> None:
@@ -212,10 +222,49 @@ def wf_gather_paged(k_pool, v_pool, page_ids, k_dst, v_dst, stream=None) -> None
                                 _stream(stream)), "wf_gather_paged")
 
 
+def default_rope_split(D: int):
+    """Channels per axis (frame, row, column): rows and columns 2*floor(D/6) each."""
+    d_rc = 2 * (D // 6)
+    return (D - 2 * d_rc, d_rc, d_rc)
+
+
+def make_rope_desc(grid: Sequence[int], frame0: int, split: Optional[Sequence[int]] = None,
+                   theta: float = 10000.0, D: int = 128) -> WfRopeDesc:
+    r = WfRopeDesc()
+    for i in range(3):
+        r.grid[i] = int(grid[i])
+    r.frame0 = int(frame0)
+    sp = default_rope_split(D) if split is None else split
+    for i in range(3):
+        r.split[i] = int(sp[i])
+    r.theta = float(theta)
+    return r
+
+
+def wf_rope_store_paged(k_src, v_src, k_pool, v_pool, page_ids, grid: Sequence[int],
+                        frame0: int, split: Optional[Sequence[int]] = None,
+                        theta: float = 10000.0, stream=None) -> None:
+    """Rotate one chunk's keys [T][H][D] (latent grid `grid`, first frame `frame0`)
+    and write them, with V copied, into pool pages; v_src = v_pool = None rewrites
+    K only (the anchor's re-rotation)."""
+    _check_bf16("k_src", k_src)
+    _check_bf16("k_pool", k_pool)
+    if v_src is not None:
+        _check_bf16("v_src", v_src)
+        _check_bf16("v_pool", v_pool)
+    T, H, D = k_src.shape
+    num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    r = make_rope_desc(grid, frame0, split, theta, D)
+    _check(_lib.wf_rope_store_paged(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(page_ids), T, H, D, num_pages, P, ctypes.byref(r),
+                                    _stream(stream)), "wf_rope_store_paged")
+
+
 def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: float,
                    q=None, k=None, v=None, o=None, k_pool=None, v_pool=None,
                    num_pages: int = 0, P: int = 0, hist_pages=None, n_hist: int = 0,
-                   hist_first: Optional[Sequence[int]] = None) -> WfTickDesc:
+                   hist_first: Optional[Sequence[int]] = None,
+                   live_pages=None) -> WfTickDesc:
     d = WfTickDesc()
     d.S, d.active_mask, d.T, d.H, d.D, d.scale = S, active_mask, T, H, D, scale
     d.q, d.k, d.v, d.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
@@ -225,26 +274,31 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
     hf = [0] * MAX_STAGES if hist_first is None else list(hist_first) + [0] * (MAX_STAGES - len(hist_first))
     for i in range(MAX_STAGES):
         d.hist_first[i] = int(hf[i])
+    d.live_pages = _ptr(live_pages)
     return d
 
 
 def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None, v_pool=None,
                  hist_pages=None, hist_first: Optional[Sequence[int]] = None,
-                 stream=None) -> None:
+                 stream=None, live_pages=None) -> None:
     """One tick: q, k, v, o [S+1][T][H][D]; pools [num_pages][P][H][D];
-    hist_pages int32 [n_hist][ceil(T/P)] on the device."""
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+    hist_pages int32 [n_hist][ceil(T/P)] on the device; live_pages (optional)
+    int32 [S+1][ceil(T/P)] on the device: live K/V read from those pages (k and
+    v may then be None)."""
+    for n, t in (("q", q), ("o", o)) + ((("k", k), ("v", v)) if live_pages is None else ()):
         _check_bf16(n, t)
     _, T, H, D = q.shape
     n_hist, num_pages, P = 0, 0, 0
     if hist_pages is not None and hist_pages.numel() > 0:
         n_hist = hist_pages.shape[0]
+    pooled = n_hist > 0 or live_pages is not None
+    if pooled:
         num_pages, P = k_pool.shape[0], k_pool.shape[1]
         _check_bf16("k_pool", k_pool)
         _check_bf16("v_pool", v_pool)
     d = make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
-                       k_pool if n_hist else None, v_pool if n_hist else None, num_pages, P,
-                       hist_pages if n_hist else None, n_hist, hist_first)
+                       k_pool if pooled else None, v_pool if pooled else None, num_pages, P,
+                       hist_pages if n_hist else None, n_hist, hist_first, live_pages)
     _check(_lib.wf_attn_tick(ctypes.byref(d), _stream(stream)), "wf_attn_tick")
 
 
