@@ -5,15 +5,18 @@ One step = one steady-state tick of the streaming rollout at the Wan-1.3B-like
 4-step shape (S = 4: five 4680-token chunks incl. the store, 12 heads x 128,
 bf16, 3 clean history chunks in 64-token pages of a 4096-page pool):
   page-table alloc of the store chunk's pages (host) -> page ids to the device
-  -> wf_store_paged (store K/V into its pages) -> history table to the device
-  -> wf_attn_tick (all five query chunks, one launch) -> commit (promote the
-  store chunk, evict the oldest history chunk, host).
+  -> history table to the device -> wf_attn_tick (all five query chunks and
+  the store chunk's page write, one launch) -> commit (promote the store
+  chunk, evict the oldest history chunk, host).
 Inputs are resident in HBM before the timed region (seeded device RNG).
 
 Prints one JSON line. `value` = useful TFLOP/s of the whole step (mask-true
 query-key pairs x 4*D flops x H); `roofline` = the attention kernel alone,
 timed with HIP events on its launch stream; `cpu_baseline` = the fp64 CPU
-oracle on a bounded sample of the same tick.
+oracle on a bounded sample of the same tick. Also reported: the same tick with
+a separate store launch, the store and rotary-store kernels' bandwidth, and the
+fully paged flow (every live chunk rotated into pages, attention reading the
+whole context through pages).
 """
 from __future__ import annotations
 
@@ -95,22 +98,25 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4, help="distinct live-input sets cycled")
     ap.add_argument("--kernel-hash", action="store_true",
                     help="print the attention kernel's source hash (recorded with its counters)")
-    ap.add_argument("--mode", default="tick", choices=["tick", "attn", "store", "copy"],
+    ap.add_argument("--mode", default="tick",
+                    choices=["tick", "attn", "store", "rope", "paged", "copy"],
                     help="tick: the full hot path (default, prints the JSON line); attn / "
-                         "store: only that kernel, --steps launches (for profilers); copy: "
-                         "a plain 1 GiB device copy (calibrates HBM byte counters)")
+                         "store / rope: only that kernel, --steps launches (for profilers); "
+                         "paged: --steps ticks of the fully paged flow; copy: a plain 1 GiB "
+                         "device copy (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
 class Rollout:
     """Device state of a steady-state rollout: pools, page table, live inputs."""
 
-    def __init__(self, cfg, rotate: int, dev):
+    def __init__(self, cfg, rotate: int, dev, fused: bool = True):
         import torch
 
         from wavefront_causal_attention_wf_amd import inputs, wfattn
 
         self.torch, self.wf, self.cfg, self.dev = torch, wfattn, cfg, dev
+        self.fused = fused
         S, T, H, D, P = cfg.S, cfg.T, cfg.H, cfg.D, cfg.P
         self.order = inputs.initial_free_order(cfg)
         self.pt = wfattn.PageTable(cfg.num_pages, P, T, cfg.n_hist,
@@ -152,7 +158,8 @@ class Rollout:
         ids = self.pt.alloc_chunk()
         self.ids_host[slot].numpy()[:] = ids
         self.ids_dev[slot].copy_(self.ids_host[slot], non_blocking=True)
-        wf.wf_store_paged(k[S], v[S], self.k_pool, self.v_pool, self.ids_dev[slot])
+        if not self.fused:
+            wf.wf_store_paged(k[S], v[S], self.k_pool, self.v_pool, self.ids_dev[slot])
         hist = self.pt.export()
         self.hist_host[slot].numpy()[:] = hist.reshape(-1)
         self.hist_dev[slot].view(-1).copy_(self.hist_host[slot], non_blocking=True)
@@ -162,13 +169,37 @@ class Rollout:
         if attn_events is not None:
             attn_events[0].record()
         wf.wf_attn_tick(q, k, v, self.o, S, self.mask, self.scale, self.k_pool, self.v_pool,
-                        self.hist_dev[slot])
+                        self.hist_dev[slot],
+                        store_pages=self.ids_dev[slot] if self.fused else None)
         if attn_events is not None:
             attn_events[1].record()
         self.pt.commit()
 
 
-def store_bandwidth(cfg, dev, launches: int = 24, rotation: int = 8) -> dict:
+def separate_store_step(cfg, dev, steps: int = 10, warmup: int = 3) -> dict:
+    """The same tick with the store chunk written by its own wf_store_paged launch
+    before the attention launch (two launches per tick)."""
+    import torch
+
+    ro = Rollout(cfg, 2, dev, fused=False)
+    for _ in range(warmup):
+        ro.step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        ro.step(ev[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    attn = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    return {"flow": "wf_store_paged + wf_attn_tick (two launches)", "ms_per_step": round(ms, 4),
+            "attn_kernel_ms_mean": round(attn, 4)}
+
+
+def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = 8) -> dict:
     """wf_store_paged and wf_gather_paged alone, HIP events on their stream.
 
     cold: rotating over `rotation` distinct source chunks and page sets (working
@@ -233,6 +264,154 @@ def store_bandwidth(cfg, dev, launches: int = 24, rotation: int = 8) -> dict:
                        "frac_hbm_peak": round(rate(gbytes, gather_cold) / PEAK_HBM_GBS, 4)}}
 
 
+def rope_store_bandwidth(cfg, dev, launches: int = 96, rotation: int = 8) -> dict:
+    """wf_rope_store_paged alone (HIP events on its stream), inputs rotated over
+    `rotation` chunks and page sets like the store measurement: reads K and V of
+    one chunk, rotates K, writes the chunk's whole pages of K and V."""
+    import torch
+
+    from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+    T, H, D, P = cfg.T, cfg.H, cfg.D, cfg.P
+    ppc = cfg.ppc
+    grid = inputs.chunk_grid(T)
+    pool_pages = max(cfg.num_pages, rotation * ppc)
+    kp = torch.zeros((pool_pages, P, H, D), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    srcs = [inputs.draw_live_torch(cfg, 3100 + i, dev, T=T)[0] for i in range(rotation)]
+    ksrc = [x[0].clone() for x in srcs]
+    vsrc = [x[1].clone() for x in srcs]
+    del srcs
+    ids = [torch.arange(i * ppc, (i + 1) * ppc, dtype=torch.int32, device=dev)
+           for i in range(rotation)]
+
+    def launch(i):
+        wfattn.wf_rope_store_paged(ksrc[i % rotation], vsrc[i % rotation], kp, vp,
+                                   ids[i % rotation], grid, 3 * (100 + i))
+
+    for i in range(rotation):
+        launch(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(launches):
+        launch(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / launches
+    nbytes = 2 * (T * H * D * 2) + 2 * (ppc * P * H * D * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "wf_rope_store_paged", "us_mean": round(ms * 1e3, 2), "bytes": nbytes,
+            "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "rotation": rotation, "grid": list(grid)}
+
+
+class FullyPagedRollout:
+    """Steady ticks of the fully paged flow: every live chunk's K/V is rotated and
+    written into pages by wf_rope_store_paged (denoising slots into fixed pages,
+    the store chunk into freshly allocated FIFO pages), then wf_attn_tick reads
+    the whole context through pages, then the store chunk is promoted."""
+
+    def __init__(self, cfg, dev, rotate: int = 2):
+        import torch
+
+        from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+        self.torch, self.wf, self.cfg, self.dev = torch, wfattn, cfg, dev
+        S, T, H, D, P = cfg.S, cfg.T, cfg.H, cfg.D, cfg.P
+        self.ppc = ppc = cfg.ppc
+        self.grid = inputs.chunk_grid(T)
+        n_fifo = cfg.num_pages
+        self.pt = wfattn.PageTable(n_fifo, P, T, cfg.n_hist,
+                                   initial_free_order=inputs.initial_free_order(cfg))
+        self.k_pool = torch.zeros((n_fifo + S * ppc, P, H, D), dtype=torch.bfloat16, device=dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.slot_ids = [torch.arange(n_fifo + j * ppc, n_fifo + (j + 1) * ppc, dtype=torch.int32,
+                                      device=dev) for j in range(S)]
+        self.chunk = 0   # video chunk index of the next store chunk
+        for c in range(cfg.n_hist):
+            hk, hv, _ = inputs.draw_live_torch(cfg, 2000 + c, dev)
+            ids = torch.from_numpy(self.pt.alloc_chunk()).to(dev)
+            wfattn.wf_rope_store_paged(hk[0], hv[0], self.k_pool, self.v_pool, ids, self.grid,
+                                       3 * self.chunk)
+            self.pt.commit()
+            self.chunk += 1
+        self.live = [inputs.draw_live_torch(cfg, inputs.rollout_seed(i), dev) for i in range(rotate)]
+        self.o = torch.empty_like(self.live[0][0])
+        self.live_dev = torch.empty((S + 1, ppc), dtype=torch.int32, device=dev)
+        # ring of pinned host slots for the per-tick page-id uploads
+        self.nslot = 8
+        self.ids_host = torch.empty((self.nslot, ppc), dtype=torch.int32, pin_memory=True)
+        self.hist_host = torch.empty((self.nslot, cfg.n_hist, ppc), dtype=torch.int32,
+                                     pin_memory=True)
+        self.slot_ev = [None] * self.nslot
+        self.hist_dev = torch.empty((cfg.n_hist, ppc), dtype=torch.int32, device=dev)
+        for j in range(S):
+            self.live_dev[j].copy_(self.slot_ids[j])
+        self.scale = 1.0 / float(np.sqrt(D))
+        self.mask = (1 << (S + 1)) - 1
+        self.i = 0
+        torch.cuda.synchronize()
+
+    def step(self, attn_events=None):
+        torch, wf, cfg = self.torch, self.wf, self.cfg
+        S, F = cfg.S, self.grid[0]
+        q, k, v = self.live[self.i % len(self.live)]
+        slot = self.i % self.nslot
+        self.i += 1
+        if self.slot_ev[slot] is not None:   # that slot's uploads have been consumed
+            self.slot_ev[slot].synchronize()
+        self.ids_host[slot].numpy()[:] = self.pt.alloc_chunk()
+        self.live_dev[S].copy_(self.ids_host[slot], non_blocking=True)
+        c_store = self.chunk
+        for j in range(S + 1):     # slot j holds video chunk c_store + S - j
+            wf.wf_rope_store_paged(k[j], v[j], self.k_pool, self.v_pool, self.live_dev[j],
+                                   self.grid, F * (c_store + S - j))
+        self.hist_host[slot].numpy()[:] = self.pt.export()
+        self.hist_dev.copy_(self.hist_host[slot], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.slot_ev[slot] = ev
+        if attn_events is not None:
+            attn_events[0].record()
+        wf.wf_attn_tick(q, None, None, self.o, S, self.mask, self.scale, self.k_pool,
+                        self.v_pool, self.hist_dev, live_pages=self.live_dev)
+        if attn_events is not None:
+            attn_events[1].record()
+        self.pt.commit()
+        self.chunk += 1
+
+
+def fully_paged(cfg, dev, steps: int = 10, warmup: int = 3) -> dict:
+    import torch
+
+    from wavefront_causal_attention_wf_amd import wfattn
+
+    ro = FullyPagedRollout(cfg, dev)
+    flops = wfattn.wf_tick_useful_flops(cfg.S, ro.mask, cfg.T, cfg.H, cfg.D, cfg.n_hist, P=cfg.P,
+                                        num_pages=cfg.num_pages)
+    for _ in range(warmup):
+        ro.step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        ro.step(ev[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    attn = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    return {"flow": f"{cfg.S + 1} x wf_rope_store_paged (every live chunk) + wf_attn_tick with "
+                    "live_pages (whole context through pages) + commit",
+            "ms_per_tick": round(ms, 4), "ticks_per_s": round(1e3 / ms, 2),
+            "useful_tflop_per_s": round(flops / (ms * 1e-3) / 1e12, 2),
+            "attn_kernel_ms_mean": round(attn, 4),
+            "attn_tflop_per_s": round(flops / (attn * 1e-3) / 1e12, 2),
+            "attn_frac_bf16_peak": round(flops / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def profile_mode(args, cfg, dev) -> None:
     """Launch-only loops for profilers (no JSON line)."""
     import torch
@@ -252,14 +431,25 @@ def profile_mode(args, cfg, dev) -> None:
         r = store_bandwidth(cfg, dev, launches=args.steps)
         log(f"store: {r}")
         return
+    if args.mode == "rope":
+        r = rope_store_bandwidth(cfg, dev, launches=args.steps)
+        log(f"rope store: {r}")
+        return
+    if args.mode == "paged":
+        r = fully_paged(cfg, dev, steps=args.steps)
+        log(f"fully paged: {r}")
+        return
     ro = Rollout(cfg, 1, dev)
     q, k, v = ro.live[0]
     hist = torch.from_numpy(ro.pt.export().copy()).to(dev)
+    # the launch the tick times: attention plus the store chunk's page write
+    store_ids = torch.from_numpy(ro.pt.alloc_chunk()).to(dev)
     mask = (1 << (cfg.S + 1)) - 1
     for _ in range(args.steps):
-        wfattn.wf_attn_tick(q, k, v, ro.o, cfg.S, mask, ro.scale, ro.k_pool, ro.v_pool, hist)
+        wfattn.wf_attn_tick(q, k, v, ro.o, cfg.S, mask, ro.scale, ro.k_pool, ro.v_pool, hist,
+                            store_pages=store_ids)
     torch.cuda.synchronize()
-    log(f"attn: {args.steps} launches")
+    log(f"attn: {args.steps} launches (with the fused store)")
 
 
 def cpu_baseline(cfg, budget_s: float) -> dict:
@@ -379,6 +569,12 @@ def main():
     }
     out["store"] = store_bandwidth(cfg, dev)
     log(f"store: {out['store']}")
+    out["separate_store_step"] = separate_store_step(cfg, dev)
+    log(f"separate store: {out['separate_store_step']}")
+    out["rope_store"] = rope_store_bandwidth(cfg, dev)
+    log(f"rope store: {out['rope_store']}")
+    out["fully_paged"] = fully_paged(cfg, dev)
+    log(f"fully paged: {out['fully_paged']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_s)

@@ -57,7 +57,7 @@ const char* wf_last_error(void);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t wf_abi_version(void);
-#define WF_ABI_VERSION 2
+#define WF_ABI_VERSION 3
 
 /* ------------------------------------------------------------------------ */
 /* Page table: host-only state for one request's attention pages.            */
@@ -210,6 +210,11 @@ typedef struct wf_tick_desc {
                           /* Appendix B.8, Eq. (13); rows of inactive slots are not */
                           /* read), or NULL: live K/V come from k and v, which may  */
                           /* then be NULL when this is set                          */
+  const int32_t* store_pages; /* device int32 [ceil(T/P)], or NULL. Set: the same    */
+                          /* launch also writes live slot S's K/V into these pages, */
+                          /* exactly as wf_store_paged (one launch per tick instead */
+                          /* of two). Needs slot S active, the pools, P, num_pages; */
+                          /* excludes live_pages                                    */
 } wf_tick_desc;
 
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);

@@ -347,6 +347,18 @@ def test_tick_validation_live_pages():
         wf.wf_attn_tick_desc(d, stream=0)
     assert e.value.status == CODES["EUNSUPPORTED"]
     assert "page table" in wf.last_error()
+    # the fused store excludes paged live slots and needs the store slot active
+    d = _desc(wf, q=fake, k=fake, v=fake, o=fake, k_pool=fake, v_pool=fake)
+    d.live_pages = fake
+    d.store_pages = fake
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_attn_tick_desc(d, stream=0)
+    assert e.value.status == CODES["EINVAL"]
+    d = _desc(wf, q=fake, k=fake, v=fake, o=fake, k_pool=fake, v_pool=fake, active_mask=0x0F)
+    d.store_pages = fake
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_attn_tick_desc(d, stream=0)
+    assert e.value.status == CODES["EINVAL"]
     # without live_pages k and v are still required
     d = _desc(wf, q=fake, o=fake, k_pool=fake, v_pool=fake)
     with pytest.raises(wf.WfError) as e:

@@ -45,12 +45,17 @@ class MirroredPages:
         self.v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=DEV)
         self.live_ids = None
 
-    def store_chunk(self, k_chunk: torch.Tensor, v_chunk: torch.Tensor) -> np.ndarray:
+    def store_chunk(self, k_chunk: torch.Tensor, v_chunk: torch.Tensor,
+                    write: bool = True) -> np.ndarray:
+        """Allocate the store chunk's pages (C table and oracle model) and record
+        its K/V in the oracle store; write them to the device pools unless the
+        tick's attention launch does it (write=False, store_pages)."""
         ids = self.pt.alloc_chunk()
         ids_m = self.model.alloc_chunk()
         assert ids.tolist() == ids_m
-        wfattn.wf_store_paged(k_chunk, v_chunk, self.k_pool, self.v_pool,
-                              torch.from_numpy(ids).to(DEV))
+        if write:
+            wfattn.wf_store_paged(k_chunk, v_chunk, self.k_pool, self.v_pool,
+                                  torch.from_numpy(ids).to(DEV))
         self.store.write_chunk(ids_m, bits(k_chunk), bits(v_chunk))
         self.live_ids = ids_m
         return ids
@@ -82,10 +87,12 @@ class MirroredPages:
         return torch.from_numpy(np.ascontiguousarray(h)).to(DEV)
 
 
-def run_tick(cfg, pages: MirroredPages, q, k, v, mask: int) -> torch.Tensor:
+def run_tick(cfg, pages: MirroredPages, q, k, v, mask: int, store_ids=None) -> torch.Tensor:
+    """One tick; with store_ids the same launch writes the store chunk's pages."""
     o = torch.full_like(q, float("nan"))
     wfattn.wf_attn_tick(q, k, v, o, cfg.S, mask, 1.0 / np.sqrt(cfg.D), pages.k_pool,
-                        pages.v_pool, pages.hist_device())
+                        pages.v_pool, pages.hist_device(),
+                        store_pages=None if store_ids is None else torch.from_numpy(store_ids).to(DEV))
     torch.cuda.synchronize()
     return o
 
@@ -129,7 +136,9 @@ def test_streaming_rollout_120_ticks():
     the stored chunk's pool pages equal the oracle store bit for bit; every
     output is finite; head 0 matches the oracle on sampled rows. On a spread of
     ticks (fill, first eviction, recycled pages, last) every head matches on
-    sampled rows, and on ticks 0-3 and the last, head 0 matches on every row."""
+    sampled rows, and on ticks 0-3 and the last, head 0 matches on every row.
+    Odd ticks write the store chunk with wf_store_paged before the attention
+    launch, even ticks let the attention launch write it (store_pages)."""
     cfg = inputs.CONFIGS["rollout120"]
     S = cfg.S
     pages = MirroredPages(cfg, cfg.window)
@@ -139,11 +148,15 @@ def test_streaming_rollout_120_ticks():
         mask = oracle.active_mask_for_tick(t, S)
         q, k, v = inputs.draw_live_torch(cfg, inputs.rollout_seed(t), DEV)
         store_on = bool((mask >> S) & 1)
+        fused = store_on and t % 2 == 0
         if store_on:
-            ids = pages.store_chunk(k[S], v[S])
-            pages.check_pages(ids)
+            ids = pages.store_chunk(k[S], v[S], write=not fused)
+            if not fused:
+                pages.check_pages(ids)
         pages.check_tables()
-        o = run_tick(cfg, pages, q, k, v, mask)
+        o = run_tick(cfg, pages, q, k, v, mask, store_ids=ids if fused else None)
+        if fused:
+            pages.check_pages(ids)
         for s in range(S + 1):
             if (mask >> s) & 1:
                 assert torch.isfinite(o[s].float()).all(), f"tick {t} stage {s}"

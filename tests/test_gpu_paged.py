@@ -84,3 +84,33 @@ def test_check_pages_mode_rejects_bad_ids(monkeypatch):
     good = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
     wfattn.wf_store_paged(k, k, kp, vp, good)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("S,T,H,D,P,n_hist", [(2, 100, 2, 64, 16, 1), (4, 4680, 12, 128, 64, 3),
+                                              (3, 70, 3, 128, 64, 0)])
+def test_store_fused_into_attention_launch(S, T, H, D, P, n_hist):
+    """wf_attn_tick with store_pages: the pages equal the oracle store bit for bit
+    (zero tails, other pages untouched) and the outputs equal those of the
+    separate wf_store_paged + wf_attn_tick sequence bit for bit."""
+    from _gpu_common import setup_tick, run_tick
+    say(f"fused store S={S} T={T} H={H} D={D} P={P} n_hist={n_hist}")
+    ppc = -(-T // P)
+    num_pages = (n_hist + 2) * ppc + 5
+    order = np.random.default_rng(T).permutation(num_pages).astype(np.int32)
+    t = setup_tick(S, T, H, D, P, n_hist, num_pages, seed=T + S, order=order)
+    ids = order[n_hist * ppc:(n_hist + 1) * ppc]
+    before = _bits(t.k_pool), _bits(t.v_pool)
+    o_sep = run_tick(t).clone()
+    o = torch.full_like(t.q, float("nan"))
+    wfattn.wf_attn_tick(t.q, t.k, t.v, o, S, t.active_mask, t.scale, t.k_pool, t.v_pool,
+                        t.hist_pages, store_pages=torch.from_numpy(ids).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_sep.view(torch.int16))
+    t.store.write_chunk(ids, t.k_bits[S], t.v_bits[S])
+    kb, vb = _bits(t.k_pool), _bits(t.v_pool)
+    for pid in range(num_pages):
+        if pid in ids:
+            assert np.array_equal(kb[pid], t.store.pages[int(pid)][0]), pid
+            assert np.array_equal(vb[pid], t.store.pages[int(pid)][1]), pid
+        else:  # history pages and free pages are not touched
+            assert np.array_equal(kb[pid], before[0][pid]) and np.array_equal(vb[pid], before[1][pid]), pid

@@ -78,6 +78,10 @@ struct AttnParams {
   const uint16_t* v_pool;
   const int32_t* hist_pages;
   const int32_t* live_pages;  // NULL: live K/V from k and v
+  const int32_t* store_pages; // non-NULL: the launch also writes the store chunk's pages
+  int32_t n_store_blocks;     // leading blocks that do that copy (a multiple of 8)
+  int32_t store_row16;        // 16-byte units per token row (H * D * 2 / 16)
+  int32_t store_slot;         // S
   int32_t n_hist;
   int32_t T, H, P, ppc;
   int32_t tps;            // tiles per chunk, ceil(T / 64)
@@ -389,6 +393,41 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// The store chunk's pages written by the attention launch itself: block i of
+// the leading n_store_blocks copies page i (K and V) of live slot S exactly as
+// wf_store_paged does (bit copy, zeros past the chunk's last token). Its K/V
+// are read by attention from the live buffers, not from these pages, so the
+// copy and the attention blocks do not depend on each other.
+__device__ __forceinline__ void store_page_block(const AttnParams& p, int S) {
+  const int i = blockIdx.x;
+  if (i >= p.ppc) return;
+  const int64_t row16 = p.store_row16;
+  const int64_t page16 = int64_t(p.P) * row16;
+  const int64_t tok0 = int64_t(i) * p.P;
+  const int64_t valid16 = (p.T - tok0 < p.P ? p.T - tok0 : p.P) * row16;
+  const int64_t pid = p.store_pages[i];
+  const int64_t src0 = (int64_t(S) * p.T + tok0) * row16;
+#pragma unroll
+  for (int tensor = 0; tensor < 2; ++tensor) {
+    const uint4* src = reinterpret_cast<const uint4*>(tensor ? p.v : p.k) + src0;
+    uint4* dst = reinterpret_cast<uint4*>(const_cast<uint16_t*>(tensor ? p.v_pool : p.k_pool)) +
+                 pid * page16;
+    for (int64_t base = threadIdx.x; base < page16; base += 4 * NTHREADS) {
+      uint4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t e = base + u * NTHREADS;
+        x[u] = e < valid16 ? src[e] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t e = base + u * NTHREADS;
+        if (e < page16) store_stream16(dst + e, x[u]);
+      }
+    }
+  }
+}
+
 template <int D, bool kFast>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
@@ -417,8 +456,13 @@ attn_tick_kernel(const AttnParams p) {
   const int r = lane & 31;
   const int g = lane >> 5;
 
+  // ---- the store chunk's page copy (leading blocks, optional) --------------
+  if (int(blockIdx.x) < p.n_store_blocks) {
+    store_page_block(p, p.store_slot);
+    return;
+  }
   // ---- work item: heaviest stage first, then head, then query tile --------
-  const int b = blockIdx.x;
+  const int b = blockIdx.x - p.n_store_blocks;
   int rank, h, qt;
   if (p.use_xcd) {
     const int x = b & (kNumXcd - 1);
@@ -881,7 +925,14 @@ int32_t validate_tick(const wf_tick_desc* d) {
     return fail(WF_EINVAL, "wf_attn_tick: q, k, v and o must be 16-byte aligned");
   if (int64_t(d->T) > (int64_t(1) << 24))
     return fail(WF_EUNSUPPORTED, "wf_attn_tick: T = %d too large", d->T);
-  if (d->n_hist > 0 || live_paged) {
+  const bool store_fused = d->store_pages != nullptr;
+  if (store_fused) {
+    if (live_paged)
+      return fail(WF_EINVAL, "wf_attn_tick: store_pages and live_pages exclude each other");
+    if (!((d->active_mask >> d->S) & 1u))
+      return fail(WF_EINVAL, "wf_attn_tick: store_pages needs the store slot S active");
+  }
+  if (d->n_hist > 0 || live_paged || store_fused) {
     if (!d->k_pool || !d->v_pool || (d->n_hist > 0 && !d->hist_pages))
       return fail(WF_EINVAL,
                   "wf_attn_tick: n_hist > 0 or live_pages needs k_pool, v_pool (and hist_pages)");
@@ -937,11 +988,17 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     StagePlan pl;
     plan_stages(d, pl);
     const bool live_paged = d.live_pages != nullptr;
-    const bool paged = d.n_hist > 0 || live_paged;
+    const bool store_fused = d.store_pages != nullptr;
+    const bool paged = d.n_hist > 0 || live_paged || store_fused;
     const int32_t ppc = paged ? int32_t((int64_t(d.T) + d.P - 1) / d.P) : 0;
     if (d.n_hist > 0 && check_pages_enabled()) {
       st = check_device_pages(d.hist_pages, int64_t(d.n_hist) * ppc, d.num_pages, stream,
                               "wf_attn_tick");
+      if (st != WF_OK) return st;
+    }
+    if (store_fused && check_pages_enabled()) {
+      st = check_device_pages(d.store_pages, ppc, d.num_pages, stream,
+                              "wf_attn_tick (store_pages)");
       if (st != WF_OK) return st;
     }
     if (live_paged && check_pages_enabled()) {
@@ -964,6 +1021,10 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     p.o = static_cast<uint16_t*>(d.o);
     p.hist_pages = d.hist_pages;
     p.live_pages = d.live_pages;
+    p.store_pages = d.store_pages;
+    p.store_slot = d.S;
+    p.store_row16 = int32_t(int64_t(d.H) * d.D * 2 / 16);
+    p.n_store_blocks = store_fused ? (ppc + kNumXcd - 1) / kNumXcd * kNumXcd : 0;
     p.n_hist = d.n_hist;
     p.T = d.T;
     p.H = d.H;
@@ -983,6 +1044,7 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     }
     int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
     plan_xcd_order(pl, d.H, p, blocks);
+    blocks += p.n_store_blocks;  // a multiple of 8: the XCD of every attention block is kept
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
     const bool fast = !paged || d.P % KT == 0;
     if (fast) {  // the kernel keeps a table of tile sources in LDS

@@ -9,7 +9,8 @@
 // source rows [p*P, p*P + P) of a [T][H][D] chunk are one contiguous block of
 // P*H*D bf16, and so is the destination page. Each page is therefore a plain
 // block copy; the kernel is bound by HBM bandwidth. Work is split into 16-byte
-// lanes, four independent loads in flight per thread before the stores.
+// lanes, four independent loads in flight per thread before the stores; the
+// page writes are nontemporal (streamed past the caches).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(kCopyThreads) void store_paged_kernel(
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const int64_t i = base + u * kCopyThreads;
-    if (i < page16) d[i] = val[u];
+    if (i < page16) store_stream16(d + i, val[u]);
   }
 }
 
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_paged_kernel(
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const int64_t i = base + u * kCopyThreads;
-    if (i < valid16) d[i] = val[u];
+    if (i < valid16) store_stream16(d + i, val[u]);
   }
 }
 

@@ -20,10 +20,11 @@
 // result rounded to nearest even.
 //
 // Layout and cost: one thread owns one 16-byte unit (four channel pairs) of one
-// token and walks all H heads of it, so each angle's sine and cosine are
-// computed once per token and reused for every head. A wave covers 4 (D = 128)
-// or 8 (D = 64) tokens, 256 contiguous bytes per (token, head) row. HBM-bound:
-// reads K and V once, writes whole pages (zeros past the chunk's last token).
+// token for four heads, so each angle's sine and cosine serve four heads and
+// four 16-byte loads are in flight per thread. A wave covers 4 (D = 128) or 8
+// (D = 64) tokens, 256 contiguous bytes per (token, head) row. HBM-bound: reads
+// K and V once, writes whole pages (zeros past the chunk's last token) with
+// nontemporal stores.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -35,6 +36,7 @@ namespace wf {
 namespace {
 
 constexpr int kRopeThreads = 256;
+constexpr int kRopeHeads = 4;  // heads per thread: four 16-byte loads in flight
 constexpr int kMaxPairs = 64;  // D <= 128
 
 struct RopeParams {
@@ -68,7 +70,8 @@ __device__ __forceinline__ uint32_t rotate_word(uint32_t w, float c, float s) {
   return pack_bf16(x0 * c - x1 * s, x0 * s + x1 * c);
 }
 
-// blockIdx.z == 0: K (rotated), 1: V (copied). Tokens [T, ppc*P) of the last
+// blockIdx.z == 0: K (rotated), 1: V (copied); blockIdx.y: heads
+// [kRopeHeads * y, kRopeHeads * y + kRopeHeads). Tokens [T, ppc*P) of the last
 // page are written as zero.
 template <int D>
 __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(const RopeParams p) {
@@ -78,55 +81,47 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(const RopePara
   const int t = blockIdx.x * TPB + threadIdx.x / U;
   if (t >= p.tokens) return;  // past the last page
   const int H = p.H;
+  const int h0 = blockIdx.y * kRopeHeads;
+  const int nh = H - h0 < kRopeHeads ? H - h0 : kRopeHeads;
   const int32_t page = t / p.P;
   const int32_t slot = t - page * p.P;
   const int64_t pid = p.page_ids[page];
   const bool is_v = blockIdx.z != 0;
-  uint4* dst = (is_v ? p.v_pool : p.k_pool) + ((pid * p.P + slot) * H) * U + u;
+  uint4* dst = (is_v ? p.v_pool : p.k_pool) + ((pid * p.P + slot) * H + h0) * U + u;
+  uint4 x[kRopeHeads];
   if (t >= p.T) {  // tail slot of the last page
-    for (int h = 0; h < H; ++h) dst[int64_t(h) * U] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kRopeHeads; ++i)
+      if (i < nh) store_stream16(dst + int64_t(i) * U, make_uint4(0u, 0u, 0u, 0u));
     return;
   }
-  const uint4* src = (is_v ? p.v_src : p.k_src) + (int64_t(t) * H) * U + u;
-  if (is_v) {
-    int h = 0;
-    for (; h + 4 <= H; h += 4) {
-      uint4 x[4];
+  const uint4* src = (is_v ? p.v_src : p.k_src) + (int64_t(t) * H + h0) * U + u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = src[int64_t(h + i) * U];
+  for (int i = 0; i < kRopeHeads; ++i)  // every load in flight before any store
+    if (i < nh) x[i] = src[int64_t(i) * U];
+  if (!is_v) {
+    // the four pairs of this unit: 4u .. 4u+3
+    const int rc = p.rows * p.cols;
+    const int f = t / rc;
+    const int rem = t - f * rc;
+    const int row = rem / p.cols;
+    const float cf = float(p.frame0 + f), cr = float(row), cc = float(rem - row * p.cols);
+    float cs[4], sn[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[int64_t(h + i) * U] = x[i];
+    for (int j = 0; j < 4; ++j) {
+      const int pr = 4 * u + j;
+      const int a = p.axis[pr];
+      const float ang = (a == 0 ? cf : (a == 1 ? cr : cc)) * p.inv_freq[pr];
+      sincosf(ang, &sn[j], &cs[j]);
     }
-    for (; h < H; ++h) dst[int64_t(h) * U] = src[int64_t(h) * U];
-    return;
-  }
-  // the four pairs of this unit: 4u .. 4u+3
-  const int rc = p.rows * p.cols;
-  const int f = t / rc;
-  const int rem = t - f * rc;
-  const int row = rem / p.cols;
-  const float cf = float(p.frame0 + f), cr = float(row), cc = float(rem - row * p.cols);
-  float cs[4], sn[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pr = 4 * u + j;
-    const int a = p.axis[pr];
-    const float ang = (a == 0 ? cf : (a == 1 ? cr : cc)) * p.inv_freq[pr];
-    sincosf(ang, &sn[j], &cs[j]);
+    for (int i = 0; i < kRopeHeads; ++i)
+      x[i] = make_uint4(rotate_word(x[i].x, cs[0], sn[0]), rotate_word(x[i].y, cs[1], sn[1]),
+                        rotate_word(x[i].z, cs[2], sn[2]), rotate_word(x[i].w, cs[3], sn[3]));
   }
-  auto rot = [&](uint4 x) __attribute__((always_inline)) {
-    return make_uint4(rotate_word(x.x, cs[0], sn[0]), rotate_word(x.y, cs[1], sn[1]),
-                      rotate_word(x.z, cs[2], sn[2]), rotate_word(x.w, cs[3], sn[3]));
-  };
-  int h = 0;
-  for (; h + 4 <= H; h += 4) {
-    uint4 x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = src[int64_t(h + i) * U];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[int64_t(h + i) * U] = rot(x[i]);
-  }
-  for (; h < H; ++h) dst[int64_t(h) * U] = rot(src[int64_t(h) * U]);
+  for (int i = 0; i < kRopeHeads; ++i)
+    if (i < nh) store_stream16(dst + int64_t(i) * U, x[i]);
 }
 
 }  // namespace
@@ -195,7 +190,8 @@ extern "C" wf_status wf_rope_store_paged(const void* k_src, const void* v_src, v
         p.inv_freq[pr] = float(std::pow(double(rope->theta), -2.0 * i / rope->split[a]));
       }
     const int tpb = kRopeThreads / (D / 8);
-    dim3 grid(unsigned((p.tokens + tpb - 1) / tpb), 1, v_src ? 2 : 1);
+    dim3 grid(unsigned((p.tokens + tpb - 1) / tpb), unsigned((H + kRopeHeads - 1) / kRopeHeads),
+              v_src ? 2 : 1);
     if (D == 128) rope_store_kernel<128><<<grid, kRopeThreads, 0, stream>>>(p);
     else rope_store_kernel<64><<<grid, kRopeThreads, 0, stream>>>(p);
     return check_launch(where);

@@ -49,7 +49,7 @@ class WfTickDesc(ctypes.Structure):
                 ("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp),
                 ("k_pool", _vp), ("v_pool", _vp), ("num_pages", _i32), ("P", _i32),
                 ("hist_pages", _vp), ("n_hist", _i32), ("hist_first", _i32 * MAX_STAGES),
-                ("live_pages", _vp)]
+                ("live_pages", _vp), ("store_pages", _vp)]
 
 
 class WfRopeDesc(ctypes.Structure):
@@ -264,7 +264,7 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
                    q=None, k=None, v=None, o=None, k_pool=None, v_pool=None,
                    num_pages: int = 0, P: int = 0, hist_pages=None, n_hist: int = 0,
                    hist_first: Optional[Sequence[int]] = None,
-                   live_pages=None) -> WfTickDesc:
+                   live_pages=None, store_pages=None) -> WfTickDesc:
     d = WfTickDesc()
     d.S, d.active_mask, d.T, d.H, d.D, d.scale = S, active_mask, T, H, D, scale
     d.q, d.k, d.v, d.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
@@ -275,30 +275,33 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
     for i in range(MAX_STAGES):
         d.hist_first[i] = int(hf[i])
     d.live_pages = _ptr(live_pages)
+    d.store_pages = _ptr(store_pages)
     return d
 
 
 def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None, v_pool=None,
                  hist_pages=None, hist_first: Optional[Sequence[int]] = None,
-                 stream=None, live_pages=None) -> None:
+                 stream=None, live_pages=None, store_pages=None) -> None:
     """One tick: q, k, v, o [S+1][T][H][D]; pools [num_pages][P][H][D];
     hist_pages int32 [n_hist][ceil(T/P)] on the device; live_pages (optional)
     int32 [S+1][ceil(T/P)] on the device: live K/V read from those pages (k and
-    v may then be None)."""
+    v may then be None); store_pages (optional) int32 [ceil(T/P)] on the device:
+    the same launch writes the store chunk's K/V into those pages."""
     for n, t in (("q", q), ("o", o)) + ((("k", k), ("v", v)) if live_pages is None else ()):
         _check_bf16(n, t)
     _, T, H, D = q.shape
     n_hist, num_pages, P = 0, 0, 0
     if hist_pages is not None and hist_pages.numel() > 0:
         n_hist = hist_pages.shape[0]
-    pooled = n_hist > 0 or live_pages is not None
+    pooled = n_hist > 0 or live_pages is not None or store_pages is not None
     if pooled:
         num_pages, P = k_pool.shape[0], k_pool.shape[1]
         _check_bf16("k_pool", k_pool)
         _check_bf16("v_pool", v_pool)
     d = make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
                        k_pool if pooled else None, v_pool if pooled else None, num_pages, P,
-                       hist_pages if n_hist else None, n_hist, hist_first, live_pages)
+                       hist_pages if n_hist else None, n_hist, hist_first, live_pages,
+                       store_pages)
     _check(_lib.wf_attn_tick(ctypes.byref(d), _stream(stream)), "wf_attn_tick")
 
 
