@@ -68,6 +68,9 @@ constexpr int kXcdTable = 512;      // max (stage, head) groups in the XCD table
 // pages are not a multiple of 64 tokens; otherwise a table of tile sources.
 constexpr int kMaxPageIds = 4096;
 constexpr int kMaxTiles = 1536;  // 64-key tiles per (stage, head): 24 KB of sources
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no
+// swizzle, stride 0): plain byte-addressed loads.
+constexpr int kBufferFlags = 0x00020000;
 
 struct AttnParams {
   const uint16_t* q;
@@ -362,19 +365,30 @@ struct TileLoader {
                                        int wave) const {
     lds_void* kdst = opaque_lds(kbuf + (wave * RW + RPI * i) * D);
     lds_void* vdst = opaque_lds(vbuf + (wave * RW + RPI * i) * D);
-    const char* ks;
-    const char* vs;
     if (!kFast && per_lane) {
       const uint64_t o = uint64_t(prow[i]) * u.row_bytes;
       const uint32_t rb = uint32_t(row[i]) * u.row_bytes;
-      ks = kb + o + (koff[i] - rb);
-      vs = vb + o + (voff[i] - rb);
+      __builtin_amdgcn_global_load_lds(kb + o + (koff[i] - rb), kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + o + (voff[i] - rb), vdst, 16, 0, 0);
     } else {
-      ks = kb + (ragged ? koff_r[i] : koff[i]);
-      vs = vb + (ragged ? voff_r[i] : voff[i]);
+      // Uniform tile base as a buffer resource, per-lane byte offset: a buffer
+      // load into LDS counts only on vmcnt, whereas the compiler treats a
+      // global load into LDS as possibly also pending on lgkmcnt, which turns
+      // every LDS operand wait while tile loads are in flight into a wait for
+      // all of them. (Offsets stay below 64 rows, far inside the record range.)
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kb), 0, 0x7fffffff, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vb), 0, 0x7fffffff, kBufferFlags);
+      // last tile of a chunk: rows past its end re-read its last row (a mask
+      // blend rather than a select, which the compiler would turn into an
+      // indexed load of the offset arrays from scratch)
+      const uint32_t rmask = 0u - uint32_t(ragged);
+      const uint32_t ko = koff[i] + ((koff_r[i] - koff[i]) & rmask);
+      const uint32_t vo = voff[i] + ((voff_r[i] - voff[i]) & rmask);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kdst, 16, int(ko), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vdst, 16, int(vo), 0, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(ks, kdst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vs, vdst, 16, 0, 0);
   }
 };
 
@@ -738,7 +752,7 @@ attn_tick_kernel(const AttnParams p) {
       // wait is for reads issued at least one step earlier
       if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
       if (pv0 % DB == 0 && kk + 1 < 4) vload(kk + 1, va[(kk + 1) & 1]);
-      if (kn != nullptr && t < NI) ld.emit(t, u, kn, vn, wave);
+      if (t < NI) ld.emit(t, u, kn, vn, wave);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
