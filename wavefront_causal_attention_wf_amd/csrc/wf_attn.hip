@@ -21,23 +21,28 @@
 //    softmax needs only one cross-lane exchange (lane l <-> l+32) per tile.
 //    K rows are fed to the MFMA in a bit-2/bit-3-swapped order so that the score
 //    registers already are the P operand of the P.V product (no shuffles).
+//  * Ping-pong: the waves of a SIMD run the same sequence one barrier slot
+//    apart, one in its MFMA slot (P.V of tile j interleaved with Q.K^T of tile
+//    j+1) while the other runs its softmax, so MFMA and VALU work overlap.
 //  * K and V tiles [64 keys][D] stream from global memory straight into LDS
-//    (16-byte direct loads, no register staging) into three buffers: the loads
-//    of tile i+2 are issued between the Q.K^T MFMAs of tile i, and a tile ends
-//    with one barrier that waits only for tile i+1. With pages of a multiple of
-//    64 tokens a tile is one contiguous span of a page or a live chunk: its
-//    base is a scalar (the page id comes from a scalar load of the page table)
-//    and each lane adds a fixed offset. Rows are XOR-swizzled so that the MFMA
-//    operand reads are free of LDS bank conflicts; V^T operands are fetched
-//    with the gfx950 transposing LDS read (ds_read_b64_tr_b16), so V needs no
-//    transpose on its way in.
+//    (16-byte buffer loads into LDS, no register staging) through four
+//    buffers; each wave issues its share of a tile two slots before the tile is
+//    needed, at the start of its softmax slot, and every slot ends with a
+//    barrier that waits only for the loads it must. A tile is one contiguous
+//    span of a page or a live chunk (pages of a multiple of 64 tokens): its
+//    source is a table entry in LDS plus a fixed per-lane offset. Rows are
+//    XOR-swizzled so that the MFMA operand reads are free of LDS bank
+//    conflicts; V^T operands are fetched with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16), so V needs no transpose on its way in.
 //  * Online softmax in the exp2 domain (log2 e folded into the scale), fp32
 //    state; the running max is only raised when a tile exceeds it by more than
 //    8 (in log2 units), so the O rescale is rare (exact: numerator and
-//    denominator share the same reference).
+//    denominator share the same reference), and the tile's max is only
+//    computed when the sum of its exponentials says it might.
 //  * Work order: (stage, head) groups, heaviest stage first, dealt to the 8
 //    XCDs so that each XCD streams about the same number of keys and the query
-//    tiles of a group share that XCD's L2.
+//    tiles of a group share that XCD's L2. Optionally the launch also writes
+//    the store chunk's pages (leading blocks).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -62,6 +67,7 @@ constexpr int NWAVES = WF_NWAVES;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int QROWS = 32 * NWAVES;  // query rows per workgroup
 constexpr float kLazyTau = 8.0f;    // raise the running max only beyond this (log2 units)
+constexpr float kLazyBound = 256.0f;  // 2^kLazyTau
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kXcdTable = 512;      // max (stage, head) groups in the XCD table
 // History page table held in LDS (ids of all history pages of one tick) when
@@ -160,25 +166,6 @@ __device__ __forceinline__ lds_void* opaque_lds(const uint16_t* p) {
   return reinterpret_cast<lds_void*>(uintptr_t(a));
 }
 
-// Tile loads straight from global memory into LDS (16 bytes per lane).
-//
-// The stage's key sequence is walked segment by segment (a segment = one chunk
-// of T keys: a history chunk through its pages, or a live chunk), each cut into
-// tps = ceil(T / 64) tiles of 64 keys; only the last tile of a segment is
-// partial (its rows past the chunk re-read the chunk's last key and are masked
-// in the softmax). Wave w fills rows [RW*w, RW*w + RW) of the K and V tiles; one
-// wave instruction writes 1 KB = RPI whole rows, lane l landing at chunk l % DC
-// of row l / DC, so each lane fetches the logical chunk that the row swizzle
-// maps to that position.
-//
-// kFast (page size a multiple of 64, and every live chunk): a tile is 64
-// consecutive rows of one page or chunk, so its source is one uniform base
-// (scalar registers; the page id comes from a scalar load of the page table)
-// plus a fixed per-lane offset, and a tile costs no vector address math.
-// Otherwise history tiles resolve each lane's page through the page table in
-// LDS. prepare() resolves the next tile and advances the cursor; emit(i) issues
-// the two loads of row group i, so the caller can spread them between MFMAs.
-// Past the last tile the cursor reads tile 0 again (finite, masked).
 // Loop-invariant scalars of a launch, read from the kernel arguments once and
 // kept in scalar registers (readfirstlane makes them values the compiler will
 // not re-load from the argument buffer inside the loop: scalar-memory loads
@@ -236,13 +223,13 @@ __device__ __forceinline__ Uniforms load_uniforms(const AttnParams& p, int h) {
 //
 // kFast (page size a multiple of 64, and every live chunk): a tile is 64
 // consecutive rows of one page or chunk, so its source is one uniform base
-// (scalar registers; the page id is one broadcast read of the page table in
-// LDS) plus a fixed per-lane offset, and a tile costs no vector address math.
-// Otherwise history tiles resolve each lane's page through the page table.
-// The segment's code is read (a scalar load) only when the cursor enters a new
-// segment. prepare() resolves the next tile and advances the cursor; emit(i)
-// issues the two loads of row group i, so the caller can spread them between
-// MFMAs. Past the last tile the cursor reads tile 0 again (finite, masked).
+// (from a table of tile sources built in LDS per workgroup) plus a fixed
+// per-lane offset, and a tile costs no vector address math. Otherwise history
+// tiles resolve each lane's page through the page table in LDS, and the
+// segment's code is read (a scalar load) only when the cursor enters a new
+// segment. prepare*() resolves the next tile and advances the cursor; emit(i)
+// issues the two loads of row group i. Past the last tile the cursor reads
+// tile 0 again (finite, masked).
 template <int D, bool kFast>
 struct TileLoader {
   static constexpr int DC = D / 8;        // 16-byte chunks per row
@@ -450,9 +437,8 @@ attn_tick_kernel(const AttnParams p) {
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   using Loader = TileLoader<D, kFast>;
   constexpr int NI = Loader::NI;
-  // Three K and three V tile buffers as six distinct LDS objects; the loop is
-  // unrolled by three so that every access names its buffer statically. Tile
-  // it+2 is loaded while tile it is computed.
+  // Four K and four V tile buffers as eight distinct LDS objects; the loop is
+  // unrolled by four so that every access names its buffer statically.
   __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t k_lds1[KT * D];
   __shared__ __attribute__((aligned(16))) uint16_t k_lds2[KT * D];
@@ -575,7 +561,7 @@ attn_tick_kernel(const AttnParams p) {
   for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds1, v_lds1, wave);
   resolve();
   const bool grp_a = wave < NWAVES / 2;
-  if (!grp_a) {  // B: tile 2 as well (A issues it in its first MFMA slot)
+  if (!grp_a) {  // B: tile 2 as well (A issues it in its first softmax slot)
 #pragma unroll
     for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds2, v_lds2, wave);
     resolve();
@@ -585,7 +571,7 @@ attn_tick_kernel(const AttnParams p) {
   else tile_barrier<4 * NI>();
 
   // Keys of tile j that are real: 64, the chunk's remainder on a segment's last
-  // tile, 0 past the end (the loop runs in groups of three tiles).
+  // tile, 0 past the end (the loop runs in groups of four tiles).
   auto valid_keys = [&](int j) __attribute__((always_inline)) {
     if (j >= ntiles) return 0;
     const int m = j - (j / u.tps) * u.tps;
@@ -595,13 +581,9 @@ attn_tick_kernel(const AttnParams p) {
   f32x16 sacc[2];
   bf16x8 pb[4];
 
-  // S^T = K Q^T for one tile: two 32-key blocks, K operands two k-steps ahead.
-  // With (kn, vn), this wave's loads of the next tile to fetch are issued one
-  // row group per k-step between the MFMAs (scheduling fences keep the
-  // interleave). Each LDS address is one offset added to the buffer: the
-  // compiler tags LDS accesses with the buffer they touch only through a short
-  // chain of address steps.
-  auto qk = [&](const uint16_t* kb, uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
+  // S^T = K Q^T for one tile (the first one, before the slot pairs start): two
+  // 32-key blocks, K operands two k-steps ahead.
+  auto qk = [&](const uint16_t* kb) __attribute__((always_inline)) {
     auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -621,10 +603,8 @@ attn_tick_kernel(const AttnParams p) {
         sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
                                                             0, 0, 0);
       if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
-      if (kn != nullptr && kk < NI) ld.emit(kk, u, kn, vn, wave);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kn != nullptr) resolve();
   };
 
   // Online softmax of the scores of tile j (exp2 domain): P as bf16 into pb.
@@ -640,96 +620,81 @@ attn_tick_kernel(const AttnParams p) {
           if (key >= valid) sacc[blk][x] = -INFINITY;
         }
     }
-    float mx = sacc[0][0];
+    // P = 2^(c s - m_run) (bf16 for the P.V product) and this lane's fp32 sum
+    float lsum;
+    auto exps = [&]() __attribute__((always_inline)) {
+      lsum = 0.f;
 #pragma unroll
-    for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
-    mx = xlane32_max(mx) * u.c;
-    const bool raise = mx > m_run + kLazyTau;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float m_new = raise ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int x = 0; x < 16; ++x) {
+          const float ev = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], u.c, -m_run));
+          lsum += ev;
+          pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(ev);
+        }
+    };
+    exps();
+    // The running reference is raised only when the tile's max exceeds it by
+    // more than kLazyTau (log2 units). No P can then exceed 2^kLazyTau, and as
+    // P >= 0 a sum at or below 2^kLazyTau on both lanes of every query rules
+    // that out without computing the max (the first tile, against -inf, always
+    // takes the check).
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= kLazyBound)) != 0) {
+      float mx = sacc[0][0];
 #pragma unroll
-      for (int i = 0; i < DB; ++i)
+      for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
 #pragma unroll
-        for (int x = 0; x < 16; ++x) oacc[i][x] *= alpha;
-    }
-    float lsum = 0.f;
+      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
+      mx = xlane32_max(mx) * u.c;
+      const bool raise = mx > m_run + kLazyTau;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+        for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], u.c, -m_run));
-        lsum += e;
-        pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(e);
+          for (int x = 0; x < 16; ++x) oacc[i][x] *= alpha;
+        exps();
       }
+    }
     l_run += lsum;
   };
 
-  // O^T += V^T P^T for one tile: four 16-key steps, V^T operands (two
-  // transposed LDS reads per 32-row block) one step ahead.
-  auto pv = [&](const uint16_t* vb) __attribute__((always_inline)) {
-    auto vload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+  // V^T operands of 16-key step kk of a V tile: two transposed LDS reads per
+  // 32-row block of O^T.
+  auto vload = [&](const uint16_t* vb, int kk, bf16x8* dst) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int e0 = (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + e0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + (e0 + 4 * D)));
-        dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
-    bf16x8 va[2][DB];
-    vload(0, va[0]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) vload(kk + 1, va[(kk + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0,
-                                                           0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int db = 0; db < DB; ++db) {
+      const int e0 = (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vb + e0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vb + (e0 + 4 * D)));
+      dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-
   // G(j): O^T += V^T P^T of tile j and S^T = K Q^T of tile j+1, interleaved
   // MFMA by MFMA so that consecutive MFMAs never share an accumulator (the
-  // score blocks recur every fourth MFMA, the output blocks every eighth).
-  // Operands: K two k-steps ahead, V one 16-key step ahead; with (kn, vn) this
-  // wave's loads of the next tile to fetch go out one row group per k-step.
-  auto gphase = [&](const uint16_t* vb, const uint16_t* kb, uint16_t* kn, uint16_t* vn)
-      __attribute__((always_inline)) {
+  // score blocks recur every fourth MFMA, the output blocks every eighth). Each
+  // k-step runs its P.V MFMAs first, then its Q.K^T MFMAs. K operands are read
+  // two k-steps ahead, V operands one 16-key step (two k-steps) ahead.
+  auto gphase = [&](const uint16_t* vb, const uint16_t* kb) __attribute__((always_inline)) {
     auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
         dst[blk] = *reinterpret_cast<const bf16x8*>(
             kb + ((krow0 + 32 * blk) * D + ((2 * kk + g) ^ kx) * 8));
     };
-    auto vload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int e0 = (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + e0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + (e0 + 4 * D)));
-        dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    };
     constexpr int PV_PER_STEP = 4 * DB / KS;  // P.V MFMAs per Q.K^T k-step
     sacc[0] = f32x16{};  // the previous scores were consumed by the last softmax
     sacc[1] = f32x16{};
     bf16x8 ka[3][2];
     bf16x8 va[2][DB];
+    vload(vb, 0, va[0]);
     kload(0, ka[0]);
     kload(1, ka[1]);
-    vload(0, va[0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
@@ -737,22 +702,19 @@ attn_tick_kernel(const AttnParams p) {
       const int pv0 = PV_PER_STEP * t;
       const int kk = pv0 / DB;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int e = 0; e < PV_PER_STEP; ++e) {
+        const int db = (pv0 + e) % DB;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0, 0,
+                                                           0);
+      }
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
         sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], sacc[blk], 0,
                                                             0, 0);
-        const int q = pv0 + blk * PV_PER_STEP / 2;
-#pragma unroll
-        for (int e = 0; e < PV_PER_STEP / 2; ++e) {
-          const int db = (q + e) % DB;
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0,
-                                                             0, 0);
-        }
-      }
       // operands of later steps go out after this step's MFMAs, so that each
       // wait is for reads issued at least one step earlier
       if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
-      if (pv0 % DB == 0 && kk + 1 < 4) vload(kk + 1, va[(kk + 1) & 1]);
-      if (t < NI) ld.emit(t, u, kn, vn, wave);
+      if (pv0 % DB == 0 && kk + 1 < 4) vload(vb, kk + 1, va[(kk + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -767,53 +729,68 @@ attn_tick_kernel(const AttnParams p) {
   //   slot 1: A: S(0)          B: Q.K^T(0)
   //   slot 2: A: G(0)          B: S(0)
   //   slot 3: A: S(1)          B: G(0)      ...
-  // Tile t lives in buffer t % 4 from its first use (slot 2t) to its last
-  // (slot 2t+3). Each wave issues its loads inside its MFMA slot: A those of
-  // tile j+2 in G(j) (slot 2j+2, needed from slot 2j+4), B those of tile j+3
-  // in G(j) (slot 2j+3, needed from slot 2j+6); B loads tiles 0-2 up front.
-  // A's loads of a slot pair land by its end; B's by the end of the next pair.
+  // Tile t lives in buffer t % 4; all its rows must have landed by the barrier
+  // that ends slot 2t-1, and it is last read in slot 2t+3. Each wave issues its
+  // loads at the start of its softmax slot, off the MFMA slot: A those of tile
+  // j+2 in S(j) (slot 2j+1), B those of tile j+3 in S(j) (slot 2j+2); A loads
+  // tiles 0-1 and B tiles 0-2 up front. A buffer is refilled (slot 2t-3 or
+  // 2t-4 for tile t) only after the barrier that ends the last slot reading
+  // its previous tile t-4 (slot 2t-5). So at each barrier a wave may leave the
+  // loads of its last softmax slot in flight (A: 2*NI, B after its softmax
+  // slot: 4*NI, the two newest tiles), and every older load has landed.
   auto end_qk_slot = [&]() __attribute__((always_inline)) {
     tile_barrier<2 * NI>();
   };
   auto end_s_slot = [&]() __attribute__((always_inline)) {
-    if (grp_a) tile_barrier<0>();
-    else tile_barrier<2 * NI>();
+    if (grp_a) tile_barrier<2 * NI>();
+    else tile_barrier<4 * NI>();
   };
-
-  if (!grp_a) tile_barrier<4 * NI>();  // B sits out slot 0
-  if (wave_active) qk(k_lds0, nullptr, nullptr);
-  end_qk_slot();  // B: tile 1 has landed (tile 2 may be in flight)
-  if (wave_active) softmax(0);
-  end_s_slot();
-
-  // G(j) then S(j+1); (vb, kb): V of tile j and K of tile j+1; (kn, vn): where
-  // this wave's loads go (A: tile j+2, B: tile j+3).
-  auto slot_pair = [&](int j, const uint16_t* vb, const uint16_t* kb, uint16_t* ka_, uint16_t* va_,
-                       uint16_t* kb_, uint16_t* vb_) __attribute__((always_inline)) {
-    uint16_t* kn = grp_a ? ka_ : kb_;
-    uint16_t* vn = grp_a ? va_ : vb_;
-    if (wave_active) {
-      // the MFMA phase wins issue arbitration over the other wave's softmax
-      __builtin_amdgcn_s_setprio(1);
-      gphase(vb, kb, kn, vn);
-      __builtin_amdgcn_s_setprio(0);
-    } else {
+  // The softmax slot of tile js: this wave's loads of its next tile go out
+  // first (into kn, vn), then the softmax, then the first V^T operands of the
+  // next MFMA slot (tile vnext).
+  auto s_slot = [&](int js, uint16_t* kn, uint16_t* vn, const uint16_t* vnext)
+      __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
-    }
+    for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
+    resolve();  // the tile this wave loads next
     __builtin_amdgcn_sched_barrier(0);
-    end_qk_slot();
-    if (wave_active) softmax(j + 1);
-    resolve();  // the next tile this wave loads, off the MFMA slot
+    if (wave_active) {
+      softmax(js);
+      // (a fence, so that these reads are not hoisted into the softmax, whose
+      // registers they would compete with)
+    }
     __builtin_amdgcn_sched_barrier(0);
     end_s_slot();
   };
 
+  if (!grp_a) tile_barrier<4 * NI>();  // B sits out slot 0
+  if (wave_active) qk(k_lds0);
+  end_qk_slot();  // B: tile 1 has landed (tile 2 may be in flight)
+  // S(0): A loads tile 2, B tile 3; G(0) reads V of tile 0
+  s_slot(0, grp_a ? k_lds2 : k_lds3, grp_a ? v_lds2 : v_lds3, v_lds0);
+
+  // G(j) then S(j+1); (vb, kb): V of tile j and K of tile j+1, vnext: V of
+  // tile j+1; (ka_, va_) / (kb_, vb_): where A's / B's loads of S(j+1) go
+  // (A: tile j+3, B: tile j+4).
+  auto slot_pair = [&](int j, const uint16_t* vb, const uint16_t* kb, const uint16_t* vnext,
+                       uint16_t* ka_, uint16_t* va_, uint16_t* kb_, uint16_t* vb_)
+      __attribute__((always_inline)) {
+    if (wave_active) {
+      // the MFMA phase wins issue arbitration over the other wave's softmax
+      __builtin_amdgcn_s_setprio(1);
+      gphase(vb, kb);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    end_qk_slot();
+    s_slot(j + 1, grp_a ? ka_ : kb_, grp_a ? va_ : vb_, vnext);
+  };
+
   for (int j = 0; j < ntiles; j += 4) {
-    slot_pair(j, v_lds0, k_lds1, k_lds2, v_lds2, k_lds3, v_lds3);
-    slot_pair(j + 1, v_lds1, k_lds2, k_lds3, v_lds3, k_lds0, v_lds0);
-    slot_pair(j + 2, v_lds2, k_lds3, k_lds0, v_lds0, k_lds1, v_lds1);
-    slot_pair(j + 3, v_lds3, k_lds0, k_lds1, v_lds1, k_lds2, v_lds2);
+    slot_pair(j, v_lds0, k_lds1, v_lds1, k_lds3, v_lds3, k_lds0, v_lds0);
+    slot_pair(j + 1, v_lds1, k_lds2, v_lds2, k_lds0, v_lds0, k_lds1, v_lds1);
+    slot_pair(j + 2, v_lds2, k_lds3, v_lds3, k_lds1, v_lds1, k_lds2, v_lds2);
+    slot_pair(j + 3, v_lds3, k_lds0, v_lds0, k_lds2, v_lds2, k_lds3, v_lds3);
   }
   if (grp_a) tile_barrier<0>();  // A's share of B's last slot
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
