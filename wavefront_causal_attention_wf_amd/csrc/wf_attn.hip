@@ -623,15 +623,16 @@ attn_tick_kernel(const AttnParams p) {
     // P = 2^(c s - m_run) (bf16 for the P.V product) and this lane's fp32 sum
     float lsum;
     auto exps = [&]() __attribute__((always_inline)) {
-      lsum = 0.f;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const float ev = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], u.c, -m_run));
-          lsum += ev;
+          part[x & 3] += ev;
           pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(ev);
         }
+      lsum = (part[0] + part[1]) + (part[2] + part[3]);
     };
     exps();
     // The running reference is raised only when the tile's max exceeds it by
@@ -754,11 +755,7 @@ attn_tick_kernel(const AttnParams p) {
     for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
     resolve();  // the tile this wave loads next
     __builtin_amdgcn_sched_barrier(0);
-    if (wave_active) {
-      softmax(js);
-      // (a fence, so that these reads are not hoisted into the softmax, whose
-      // registers they would compete with)
-    }
+    if (wave_active) softmax(js);
     __builtin_amdgcn_sched_barrier(0);
     end_s_slot();
   };
