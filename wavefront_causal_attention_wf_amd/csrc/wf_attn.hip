@@ -679,8 +679,9 @@ attn_tick_kernel(const AttnParams p) {
   // G(j): O^T += V^T P^T of tile j and S^T = K Q^T of tile j+1, interleaved
   // MFMA by MFMA so that consecutive MFMAs never share an accumulator (the
   // score blocks recur every fourth MFMA, the output blocks every eighth). Each
-  // k-step runs its P.V MFMAs first, then its Q.K^T MFMAs. K operands are read
-  // two k-steps ahead, V operands one 16-key step (two k-steps) ahead.
+  // k-step first issues the operand reads of a later step (K two k-steps
+  // ahead, V one 16-key step = two k-steps ahead), then runs its P.V MFMAs,
+  // then its Q.K^T MFMAs.
   auto gphase = [&](const uint16_t* vb, const uint16_t* kb) __attribute__((always_inline)) {
     auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
 #pragma unroll
@@ -702,6 +703,9 @@ attn_tick_kernel(const AttnParams p) {
       // P.V MFMAs number PV_PER_STEP*t .. : 16-key step kk, output blocks db
       const int pv0 = PV_PER_STEP * t;
       const int kk = pv0 / DB;
+      // operands of later steps go out before this step's MFMAs
+      if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
+      if (pv0 % DB == 0 && kk + 1 < 4) vload(vb, kk + 1, va[(kk + 1) & 1]);
 #pragma unroll
       for (int e = 0; e < PV_PER_STEP; ++e) {
         const int db = (pv0 + e) % DB;
@@ -712,10 +716,6 @@ attn_tick_kernel(const AttnParams p) {
       for (int blk = 0; blk < 2; ++blk)
         sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], sacc[blk], 0,
                                                             0, 0);
-      // operands of later steps go out after this step's MFMAs, so that each
-      // wait is for reads issued at least one step earlier
-      if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
-      if (pv0 % DB == 0 && kk + 1 < 4) vload(vb, kk + 1, va[(kk + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
