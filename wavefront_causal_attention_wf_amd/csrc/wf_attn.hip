@@ -210,6 +210,8 @@ __device__ __forceinline__ Uniforms load_uniforms(const AttnParams& p, int h) {
   return u;
 }
 
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 // Tile loads straight from global memory into LDS (16 bytes per lane).
 //
 // The stage's key sequence is walked segment by segment (a segment = one chunk
@@ -437,16 +439,18 @@ attn_tick_kernel(const AttnParams p) {
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   using Loader = TileLoader<D, kFast>;
   constexpr int NI = Loader::NI;
-  // Four K and four V tile buffers as eight distinct LDS objects; the loop is
-  // unrolled by four so that every access names its buffer statically.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds2[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds3[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds2[KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds3[KT * D];
+  // Four K and four V tile buffers (one array each, 256-byte aligned); the loop
+  // is unrolled by four so that every access names its buffer statically.
+  __shared__ __attribute__((aligned(256))) uint16_t k_tiles[4 * KT * D];
+  __shared__ __attribute__((aligned(256))) uint16_t v_tiles[4 * KT * D];
+  uint16_t* const k_lds0 = k_tiles;
+  uint16_t* const k_lds1 = k_tiles + KT * D;
+  uint16_t* const k_lds2 = k_tiles + 2 * KT * D;
+  uint16_t* const k_lds3 = k_tiles + 3 * KT * D;
+  uint16_t* const v_lds0 = v_tiles;
+  uint16_t* const v_lds1 = v_tiles + KT * D;
+  uint16_t* const v_lds2 = v_tiles + 2 * KT * D;
+  uint16_t* const v_lds3 = v_tiles + 3 * KT * D;
   __shared__ int32_t pages_lds[kFast ? 1 : kMaxPageIds];
   __shared__ uint4 tile_tab[kFast ? kMaxTiles : 1];
 
@@ -545,6 +549,20 @@ attn_tick_kernel(const AttnParams p) {
   const int vx = vswz<D>(vrow);
   const int vcx = 2 * ((lane >> 4) & 1) + ((a16 >> 1) & 1);
   const int vsub = 4 * (a16 & 1);
+  // The same reads as LDS byte addresses. Rows are 2*D bytes and the swizzles
+  // act on the 16-byte chunk index only (address bits 4..7 within a row), so
+  // the address of K step kk is this lane's base XOR (kk << 5), and that of V
+  // output block db is the base XOR (db << 6); buffer, 32-row block, 16-key
+  // step and row half are constant offsets. One base per tensor then serves
+  // every operand read (addresses formed from it inside each MFMA slot rather
+  // than dozens of precomputed address registers).
+  constexpr uint32_t TILE_BYTES = KT * D * 2;
+  // (byte offsets into the tile arrays; reads are formed from the arrays
+  // themselves so that the compiler knows which LDS objects they touch)
+  const uint32_t k_lane = uint32_t(krow0 * D * 2 + ((g ^ kx) << 4));
+  const uint32_t v_lane = uint32_t(vrow * D * 2 + ((vcx ^ vx) << 4) + vsub * 2);
+  const char* const k_bytes = reinterpret_cast<const char*>(k_tiles);
+  const char* const v_bytes = reinterpret_cast<const char*>(v_tiles);
 
   Loader ld;
   ld.init(u, wave, lane);
@@ -583,12 +601,14 @@ attn_tick_kernel(const AttnParams p) {
 
   // S^T = K Q^T for one tile (the first one, before the slot pairs start): two
   // 32-key blocks, K operands two k-steps ahead.
-  auto qk = [&](const uint16_t* kb) __attribute__((always_inline)) {
+  auto qk = [&](int kbuf) __attribute__((always_inline)) {
+    uint32_t kl = k_lane;
+    asm volatile("" : "+v"(kl));
     auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+      const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
-        dst[blk] = *reinterpret_cast<const bf16x8*>(
-            kb + ((krow0 + 32 * blk) * D + ((2 * kk + g) ^ kx) * 8));
+        dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
     };
     sacc[0] = f32x16{};
     sacc[1] = f32x16{};
@@ -663,38 +683,42 @@ attn_tick_kernel(const AttnParams p) {
     l_run += lsum;
   };
 
-  // V^T operands of 16-key step kk of a V tile: two transposed LDS reads per
-  // 32-row block of O^T.
-  auto vload = [&](const uint16_t* vb, int kk, bf16x8* dst) __attribute__((always_inline)) {
+  // V^T operands of 16-key step kk of V tile buffer vbuf: two transposed LDS
+  // reads per 32-row block of O^T (vl: this lane's V base).
+  auto vload = [&](uint32_t vl, int vbuf, int kk, bf16x8* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int e0 = (16 * kk + vrow) * D + ((4 * db + vcx) ^ vx) * 8 + vsub;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vb + e0));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vb + (e0 + 4 * D)));
+      const uint32_t a = (vl ^ uint32_t(db << 6)) + vbuf * TILE_BYTES + kk * (16 * D * 2);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_bytes + a));
+      const i16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_bytes + (a + 4 * D * 2)));
       dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
+
   // G(j): O^T += V^T P^T of tile j and S^T = K Q^T of tile j+1, interleaved
   // MFMA by MFMA so that consecutive MFMAs never share an accumulator (the
   // score blocks recur every fourth MFMA, the output blocks every eighth). Each
   // k-step first issues the operand reads of a later step (K two k-steps
   // ahead, V one 16-key step = two k-steps ahead), then runs its P.V MFMAs,
   // then its Q.K^T MFMAs.
-  auto gphase = [&](const uint16_t* vb, const uint16_t* kb) __attribute__((always_inline)) {
+  auto gphase = [&](int vbuf, int kbuf) __attribute__((always_inline)) {
+    // the lane bases, opaque here so that the read addresses are formed from
+    // them inside the slot instead of being kept in registers across the loop
+    uint32_t kl = k_lane, vl = v_lane;
+    asm volatile("" : "+v"(kl), "+v"(vl));
     auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+      const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
-        dst[blk] = *reinterpret_cast<const bf16x8*>(
-            kb + ((krow0 + 32 * blk) * D + ((2 * kk + g) ^ kx) * 8));
+        dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
     };
     constexpr int PV_PER_STEP = 4 * DB / KS;  // P.V MFMAs per Q.K^T k-step
     sacc[0] = f32x16{};  // the previous scores were consumed by the last softmax
     sacc[1] = f32x16{};
     bf16x8 ka[3][2];
     bf16x8 va[2][DB];
-    vload(vb, 0, va[0]);
+    vload(vl, vbuf, 0, va[0]);
     kload(0, ka[0]);
     kload(1, ka[1]);
     __builtin_amdgcn_sched_barrier(0);
@@ -705,7 +729,7 @@ attn_tick_kernel(const AttnParams p) {
       const int kk = pv0 / DB;
       // operands of later steps go out before this step's MFMAs
       if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
-      if (pv0 % DB == 0 && kk + 1 < 4) vload(vb, kk + 1, va[(kk + 1) & 1]);
+      if (pv0 % DB == 0 && kk + 1 < 4) vload(vl, vbuf, kk + 1, va[(kk + 1) & 1]);
 #pragma unroll
       for (int e = 0; e < PV_PER_STEP; ++e) {
         const int db = (pv0 + e) % DB;
@@ -749,8 +773,7 @@ attn_tick_kernel(const AttnParams p) {
   // The softmax slot of tile js: this wave's loads of its next tile go out
   // first (into kn, vn), then the softmax, then the first V^T operands of the
   // next MFMA slot (tile vnext).
-  auto s_slot = [&](int js, uint16_t* kn, uint16_t* vn, const uint16_t* vnext)
-      __attribute__((always_inline)) {
+  auto s_slot = [&](int js, uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
     resolve();  // the tile this wave loads next
@@ -761,33 +784,32 @@ attn_tick_kernel(const AttnParams p) {
   };
 
   if (!grp_a) tile_barrier<4 * NI>();  // B sits out slot 0
-  if (wave_active) qk(k_lds0);
+  if (wave_active) qk(0);
   end_qk_slot();  // B: tile 1 has landed (tile 2 may be in flight)
   // S(0): A loads tile 2, B tile 3; G(0) reads V of tile 0
-  s_slot(0, grp_a ? k_lds2 : k_lds3, grp_a ? v_lds2 : v_lds3, v_lds0);
+  s_slot(0, grp_a ? k_lds2 : k_lds3, grp_a ? v_lds2 : v_lds3);
 
-  // G(j) then S(j+1); (vb, kb): V of tile j and K of tile j+1, vnext: V of
-  // tile j+1; (ka_, va_) / (kb_, vb_): where A's / B's loads of S(j+1) go
-  // (A: tile j+3, B: tile j+4).
-  auto slot_pair = [&](int j, const uint16_t* vb, const uint16_t* kb, const uint16_t* vnext,
-                       uint16_t* ka_, uint16_t* va_, uint16_t* kb_, uint16_t* vb_)
-      __attribute__((always_inline)) {
+  // G(j) then S(j+1); buffers vbuf, kbuf: V of tile j and K of tile j+1 (tile
+  // t is in buffer t % 4); (ka_, va_) / (kb_, vb_): where A's / B's loads of
+  // S(j+1) go (A: tile j+3, B: tile j+4).
+  auto slot_pair = [&](int j, int vbuf, int kbuf, uint16_t* ka_, uint16_t* va_, uint16_t* kb_,
+                       uint16_t* vb_) __attribute__((always_inline)) {
     if (wave_active) {
       // the MFMA phase wins issue arbitration over the other wave's softmax
       __builtin_amdgcn_s_setprio(1);
-      gphase(vb, kb);
+      gphase(vbuf, kbuf);
       __builtin_amdgcn_s_setprio(0);
     }
     __builtin_amdgcn_sched_barrier(0);
     end_qk_slot();
-    s_slot(j + 1, grp_a ? ka_ : kb_, grp_a ? va_ : vb_, vnext);
+    s_slot(j + 1, grp_a ? ka_ : kb_, grp_a ? va_ : vb_);
   };
 
   for (int j = 0; j < ntiles; j += 4) {
-    slot_pair(j, v_lds0, k_lds1, v_lds1, k_lds3, v_lds3, k_lds0, v_lds0);
-    slot_pair(j + 1, v_lds1, k_lds2, v_lds2, k_lds0, v_lds0, k_lds1, v_lds1);
-    slot_pair(j + 2, v_lds2, k_lds3, v_lds3, k_lds1, v_lds1, k_lds2, v_lds2);
-    slot_pair(j + 3, v_lds3, k_lds0, v_lds0, k_lds2, v_lds2, k_lds3, v_lds3);
+    slot_pair(j, 0, 1, k_lds3, v_lds3, k_lds0, v_lds0);
+    slot_pair(j + 1, 1, 2, k_lds0, v_lds0, k_lds1, v_lds1);
+    slot_pair(j + 2, 2, 3, k_lds1, v_lds1, k_lds2, v_lds2);
+    slot_pair(j + 3, 3, 0, k_lds2, v_lds2, k_lds3, v_lds3);
   }
   if (grp_a) tile_barrier<0>();  // A's share of B's last slot
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
