@@ -748,27 +748,27 @@ attn_tick_kernel(const AttnParams p) {
   // Ping-pong: waves 0..3 (group A) and 4..7 (group B) share the four SIMDs
   // one to one and run the same sequence one slot apart, so that while one
   // wave of a SIMD runs MFMAs (G(j): P.V of tile j, then Q.K^T of tile j+1,
-  // interleaved) the other runs the VALU softmax S of its current tile; a
-  // block-wide barrier ends every slot:
-  //   slot 0: A: Q.K^T(0)      B: -
-  //   slot 1: A: S(0)          B: Q.K^T(0)
+  // interleaved) the other runs the VALU softmax S of its current tile:
+  //   slot 0: A: Q.K^T(0)      B: Q.K^T(0) (early; no data dependence)
+  //   slot 1: A: S(0)          B:   "
   //   slot 2: A: G(0)          B: S(0)
   //   slot 3: A: S(1)          B: G(0)      ...
+  // A block-wide barrier ends every odd slot (A's softmax slots, B's MFMA
+  // slots); within the two slots between barriers each SIMD's waves run one
+  // softmax and one MFMA phase each, in opposite order, so they still overlap.
   // Tile t lives in buffer t % 4; all its rows must have landed by the barrier
-  // that ends slot 2t-1, and it is last read in slot 2t+3. Each wave issues its
-  // loads at the start of its softmax slot, off the MFMA slot: A those of tile
-  // j+2 in S(j) (slot 2j+1), B those of tile j+3 in S(j) (slot 2j+2); A loads
-  // tiles 0-1 and B tiles 0-2 up front. A buffer is refilled (slot 2t-3 or
-  // 2t-4 for tile t) only after the barrier that ends the last slot reading
-  // its previous tile t-4 (slot 2t-5). So at each barrier a wave may leave the
-  // loads of its last softmax slot in flight (A: 2*NI, B after its softmax
-  // slot: 4*NI, the two newest tiles), and every older load has landed.
+  // that ends slot 2t-1, and it is last read in slot 2t+3. Each wave issues
+  // its loads at the start of its softmax slot: A those of tile j+2 in S(j)
+  // (slot 2j+1), B those of tile j+3 in S(j) (slot 2j+2); A loads tiles 0-1
+  // and B tiles 0-2 up front. A buffer is refilled (slot 2t-3 or 2t-4 for tile
+  // t) only after the barrier that ends the last slot reading its previous
+  // tile t-4 (slot 2t-5). So at each barrier a wave may leave the loads of its
+  // newest tile in flight (2*NI) and every older load has landed.
   auto end_qk_slot = [&]() __attribute__((always_inline)) {
-    tile_barrier<2 * NI>();
+    if (!grp_a) tile_barrier<2 * NI>();
   };
   auto end_s_slot = [&]() __attribute__((always_inline)) {
     if (grp_a) tile_barrier<2 * NI>();
-    else tile_barrier<4 * NI>();
   };
   // The softmax slot of tile js: this wave's loads of its next tile go out
   // first (into kn, vn), then the softmax, then the first V^T operands of the
@@ -783,9 +783,8 @@ attn_tick_kernel(const AttnParams p) {
     end_s_slot();
   };
 
-  if (!grp_a) tile_barrier<4 * NI>();  // B sits out slot 0
   if (wave_active) qk(0);
-  end_qk_slot();  // B: tile 1 has landed (tile 2 may be in flight)
+  end_qk_slot();  // B (end of slot 1): tile 1 has landed (tile 2 may be in flight)
   // S(0): A loads tile 2, B tile 3; G(0) reads V of tile 0
   s_slot(0, grp_a ? k_lds2 : k_lds3, grp_a ? v_lds2 : v_lds3);
 
@@ -811,7 +810,6 @@ attn_tick_kernel(const AttnParams p) {
     slot_pair(j + 2, 2, 3, k_lds1, v_lds1, k_lds2, v_lds2);
     slot_pair(j + 3, 3, 0, k_lds2, v_lds2, k_lds3, v_lds3);
   }
-  if (grp_a) tile_barrier<0>();  // A's share of B's last slot
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
 
   // ---- epilogue: O = O^T / l, bf16 ----------------------------------------
