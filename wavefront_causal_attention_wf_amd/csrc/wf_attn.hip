@@ -696,6 +696,10 @@ attn_tick_kernel(const AttnParams p) {
     }
   };
 
+  // V^T operands of the next MFMA slot's first 16-key step, read at the end of
+  // the softmax slot before it (that tile landed a slot earlier), so the MFMA
+  // slot starts on them while its first K operands are still in flight.
+  bf16x8 vpre[DB];
   // G(j): O^T += V^T P^T of tile j and S^T = K Q^T of tile j+1, interleaved
   // MFMA by MFMA so that consecutive MFMAs never share an accumulator (the
   // score blocks recur every fourth MFMA, the output blocks every eighth). Each
@@ -718,7 +722,8 @@ attn_tick_kernel(const AttnParams p) {
     sacc[1] = f32x16{};
     bf16x8 ka[3][2];
     bf16x8 va[2][DB];
-    vload(vl, vbuf, 0, va[0]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
     kload(0, ka[0]);
     kload(1, ka[1]);
     __builtin_amdgcn_sched_barrier(0);
@@ -772,13 +777,19 @@ attn_tick_kernel(const AttnParams p) {
   };
   // The softmax slot of tile js: this wave's loads of its next tile go out
   // first (into kn, vn), then the softmax, then the first V^T operands of the
-  // next MFMA slot (tile vnext).
-  auto s_slot = [&](int js, uint16_t* kn, uint16_t* vn) __attribute__((always_inline)) {
+  // next MFMA slot (from tile buffer vnext).
+  auto s_slot = [&](int js, uint16_t* kn, uint16_t* vn, int vnext) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
     resolve();  // the tile this wave loads next
     __builtin_amdgcn_sched_barrier(0);
-    if (wave_active) softmax(js);
+    if (wave_active) {
+      softmax(js);
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t vl = v_lane;
+      asm volatile("" : "+v"(vl));
+      vload(vl, vnext, 0, vpre);
+    }
     __builtin_amdgcn_sched_barrier(0);
     end_s_slot();
   };
@@ -786,7 +797,7 @@ attn_tick_kernel(const AttnParams p) {
   if (wave_active) qk(0);
   end_qk_slot();  // B (end of slot 1): tile 1 has landed (tile 2 may be in flight)
   // S(0): A loads tile 2, B tile 3; G(0) reads V of tile 0
-  s_slot(0, grp_a ? k_lds2 : k_lds3, grp_a ? v_lds2 : v_lds3);
+  s_slot(0, grp_a ? k_lds2 : k_lds3, grp_a ? v_lds2 : v_lds3, 0);
 
   // G(j) then S(j+1); buffers vbuf, kbuf: V of tile j and K of tile j+1 (tile
   // t is in buffer t % 4); (ka_, va_) / (kb_, vb_): where A's / B's loads of
@@ -801,7 +812,7 @@ attn_tick_kernel(const AttnParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     end_qk_slot();
-    s_slot(j + 1, grp_a ? ka_ : kb_, grp_a ? va_ : vb_);
+    s_slot(j + 1, grp_a ? ka_ : kb_, grp_a ? va_ : vb_, (vbuf + 1) & 3);
   };
 
   for (int j = 0; j < ntiles; j += 4) {
