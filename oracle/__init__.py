@@ -14,13 +14,18 @@ from the Wave Forcing pages:
     math.fsum (tiny shapes only);
   * rope: rotary position embedding of a chunk's keys over its latent grid,
     the anchor's re-rotation after a window shift, and correctly rounded
-    float64 -> bf16 conversion of the rotated keys.
+    float64 -> bf16 conversion of the rotated keys;
+  * fp8: the 8-bit tier's e4m3 encoding and decoding, per-group float32
+    scales (queries per row, keys per 64-token tile and head), an 8-bit page
+    store and the tick over the dequantised values.
 
 Parity status: every function is pinned by the `-m "not gpu"` tests in
-tests/test_oracle_pins.py, tests/test_page_model.py and tests/test_rope_oracle.py
+tests/test_oracle_pins.py, tests/test_page_model.py, tests/test_rope_oracle.py and
+tests/test_fp8_oracle.py
 (brute force, a library attention routine for the dense special case, mask
 invariances, closed forms, rotation invariants, hand-derived tables under
-tests/golden/ and a library bf16 conversion). No function is "parity unpinned".
+tests/golden/, a library bf16 conversion, a library e4m3 conversion and an
+exact reduction of the 8-bit tick to the bf16 one). No function is "parity unpinned".
 """
 from .wave_attention import (  # noqa: F401
     decode_bf16,
@@ -47,4 +52,13 @@ from .rope import (  # noqa: F401
     rope,
     anchor_frame0,
     round_to_bf16_bits,
+)
+from .fp8 import (  # noqa: F401
+    e4m3_decode,
+    e4m3_encode,
+    quantize_groups,
+    quantize_k_tiles,
+    quantize_q_rows,
+    Fp8PageStore,
+    attention_tick_fp8,
 )

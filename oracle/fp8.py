@@ -1,0 +1,189 @@
+"""8-bit (e4m3) keys and queries for the FP8 attention tier.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py). numpy, with the
+quantisation decisions taken in float32 exactly as stated below.
+
+The pages name K/V quantisation as a way to shrink K/V payloads and an 8-bit
+attention backend (SageAttention) for local computation ([full text] §4.3,
+§5 "Compute configurations"), and measure FP8 K/V collectives at about half
+the bf16 time (Appendix C.5, Table 8; C.6). They give neither the 8-bit
+format nor the quantisation granularity. Readings (listed in the design doc):
+  * format: e4m3 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    no infinities; largest finite value 448; exponent field 0 holds the
+    subnormals m * 2^-9);
+  * what is 8-bit: Q and K, the operands of Q.K^T (the SageAttention-like
+    tier); P and V stay 16-bit, since e4m3 P would carry ~6 % per-element error;
+  * scales: one float32 scale per (64-token tile, head) for K and per (query
+    row, head) for Q: amax = max |x| over the group (float32, exact for bf16
+    inputs), scale = amax / 448, inv = 448 / amax (both float32 divisions;
+    inv = scale = 0 for an all-zero group), code = e4m3 of float32(x * inv)
+    rounded to nearest, ties to even; the value a code stands for is
+    decode(code) * scale;
+  * scores are the products of the dequantised Q and K; everything after the
+    scores is the bf16 tier's plain masked softmax attention.
+"""
+from __future__ import annotations
+
+from typing import Tuple
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 e4m3 codes -> float64 values (0x7F / 0xFF are NaN)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float values (|x| <= 464) -> e4m3 codes, rounded to nearest, ties to even
+    (each value is taken exactly as given; callers pass float32 results)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > 464.0) or np.any(np.isnan(x)):
+        raise ValueError("value outside the e4m3 range")
+    sign = np.signbit(x)
+    a = np.abs(x)
+    # quantum of the binade holding a (subnormal quantum 2^-9 below 2^-6)
+    _, ex = np.frexp(a)                     # a = f * 2^ex, 0.5 <= f < 1
+    ex = np.maximum(ex, -5)                 # 2^-6 and below: fixed quantum
+    q = np.ldexp(1.0, ex - 4)               # 3 mantissa bits -> 4 significant bits
+    r = np.round(a / q) * q                 # ties to even
+    r = np.minimum(r, E4M3_MAX)             # 464 / q would be 448 + half a quantum
+    # code from the rounded value
+    codes = np.zeros(a.shape, dtype=np.int64)
+    nz = r > 0
+    _, e2 = np.frexp(r[nz])
+    ee = e2 - 1 + 7                         # biased exponent of r = 1.m * 2^(e2-1)
+    sub = ee <= 0
+    mant = np.where(sub, np.round(r[nz] / 2.0 ** -9),
+                    np.round((r[nz] / np.exp2(e2 - 1.0) - 1.0) * 8.0))
+    codes[nz] = np.where(sub, mant, (ee << 3) | mant.astype(np.int64))
+    codes = codes | np.where(sign, 0x80, 0)  # negative values keep their sign, zero too
+    return codes.astype(np.uint8)
+
+
+def quantize_groups(x: np.ndarray, axes) -> Tuple[np.ndarray, np.ndarray]:
+    """Quantise x (values; bf16 bit patterns must be decoded first) with one
+    scale per group, reducing over `axes` (the other axes index the groups).
+    Returns (codes uint8 like x, scales float32 with the reduced axes kept as 1)."""
+    xf = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(xf), axis=axes, keepdims=True).astype(np.float32)
+    safe = np.where(amax > 0, amax, np.float32(1))
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
+    inv = np.where(amax > 0, np.float32(E4M3_MAX) / safe, np.float32(0)).astype(np.float32)
+    y = (xf * inv).astype(np.float32)       # float32 product, rounded once
+    return e4m3_encode(y), scale
+
+
+def dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    return e4m3_decode(codes) * scale.astype(np.float64)
+
+
+def quantize_k_tiles(k_bits_or_vals: np.ndarray, tile: int = 64) -> Tuple[np.ndarray, np.ndarray]:
+    """Keys [T][H][D] of one chunk -> (codes [T][H][D], scales [ceil(T/tile)][H]):
+    one scale per (64-token tile, head); tokens past T do not exist (a short
+    last tile takes its amax over its own tokens)."""
+    from .wave_attention import as_f64
+
+    k = as_f64(k_bits_or_vals).astype(np.float32)
+    T, H, D = k.shape
+    nt = -(-T // tile)
+    codes = np.zeros((T, H, D), np.uint8)
+    scales = np.zeros((nt, H), np.float32)
+    for t in range(nt):
+        blk = k[t * tile:(t + 1) * tile]                      # [n][H][D]
+        c, s = quantize_groups(blk, axes=(0, 2))              # scale per head
+        codes[t * tile:(t + 1) * tile] = c
+        scales[t] = s[0, :, 0]
+    return codes, scales
+
+
+def quantize_q_rows(q_bits_or_vals: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Queries [..., D] -> (codes, scales [...]): one scale per (row, head)."""
+    from .wave_attention import as_f64
+
+    q = as_f64(q_bits_or_vals).astype(np.float32)
+    c, s = quantize_groups(q, axes=-1)
+    return c, s[..., 0]
+
+
+class Fp8PageStore:
+    """Page id -> (K codes uint8 [P][H][D], K scales float32 [P/64][H], V bf16
+    bits uint16 [P][H][D]): the history pages of the 8-bit tier. A chunk's keys
+    are quantised per (64-token tile, head) of the chunk (quantize_k_tiles), so
+    P must be a multiple of 64 and every scale covers 64 tokens of one page;
+    unused slots of the last page hold zero codes, and a scale slot past the
+    chunk's last tile holds 0."""
+
+    def __init__(self, P: int, H: int, D: int, tile: int = 64):
+        if P % tile:
+            raise ValueError("page size must be a multiple of the scale tile")
+        self.P, self.H, self.D, self.tile = P, H, D, tile
+        self.pages = {}
+
+    def write_chunk(self, ids, k_bits, v_bits) -> None:
+        T = k_bits.shape[0]
+        P, tile = self.P, self.tile
+        if len(ids) != -(-T // P):
+            raise ValueError("wrong number of page ids for the chunk")
+        codes, scales = quantize_k_tiles(k_bits, tile)
+        for n, pid in enumerate(ids):
+            kc = np.zeros((P, self.H, self.D), np.uint8)
+            ks = np.zeros((P // tile, self.H), np.float32)
+            vb = np.zeros((P, self.H, self.D), np.uint16)
+            t0, t1 = n * P, min(T, (n + 1) * P)
+            kc[:t1 - t0] = codes[t0:t1]
+            vb[:t1 - t0] = v_bits[t0:t1]
+            nt = -(-(t1 - t0) // tile)
+            ks[:nt] = scales[t0 // tile:t0 // tile + nt]
+            self.pages[int(pid)] = (kc, ks, vb)
+
+    def drop(self, ids) -> None:
+        for pid in ids:
+            self.pages.pop(int(pid), None)
+
+    def gather(self, page_lists, T: int):
+        """Dequantised K (float64) and V bits (uint16), [n][T][H][D], read token by
+        token through the per-chunk page lists."""
+        n = len(page_lists)
+        K = np.zeros((n, T, self.H, self.D), np.float64)
+        V = np.zeros((n, T, self.H, self.D), np.uint16)
+        for c, ids in enumerate(page_lists):
+            for t in range(T):
+                kc, ks, vb = self.pages[int(ids[t // self.P])]
+                slot = t % self.P
+                K[c, t] = e4m3_decode(kc[slot]) * ks[slot // self.tile][:, None].astype(np.float64)
+                V[c, t] = vb[slot]
+        return K, V
+
+
+def attention_tick_fp8(q_bits, store: "Fp8PageStore", hist_pages, live_pages, S: int,
+                       active_mask: int, scale: float, **kw):
+    """One tick of the 8-bit tier, every key read through the 8-bit pages
+    (the fully paged context of the bf16 tier): each query row is quantised
+    with its own scale (quantize_q_rows), keys and values are the pages'
+    dequantised values, and the attention itself is the plain masked softmax
+    of attention_tick over those values."""
+    from .wave_attention import attention_tick
+
+    T, H, D = q_bits.shape[1], q_bits.shape[2], q_bits.shape[3]
+    qc, qs = quantize_q_rows(q_bits)
+    qv = e4m3_decode(qc) * qs[..., None].astype(np.float64)
+    hk, hv = store.gather(hist_pages, T)
+    lk = np.zeros((S + 1, T, H, D), np.float64)
+    lv = np.zeros((S + 1, T, H, D), np.uint16)
+    for j in range(S + 1):
+        if (active_mask >> j) & 1:
+            if live_pages[j] is None:
+                raise ValueError(f"active slot {j} has no pages")
+            kk, vv = store.gather([live_pages[j]], T)
+            lk[j], lv[j] = kk[0], vv[0]
+    from .wave_attention import as_f64
+    return attention_tick(qv, lk, as_f64(lv), hk, as_f64(hv), S, active_mask, scale, **kw)

@@ -1,0 +1,194 @@
+"""Pins of the 8-bit tier's oracle (oracle/fp8.py) to things other than itself:
+the e4m3 format's definition (closed-form code values), a library conversion
+(torch.float8_e4m3fn), the half-quantum error bound, group structure planted in
+the inputs, and an exact reduction to the bf16 oracle when every group's values
+are representable."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+
+
+def test_decode_matches_library_and_closed_forms():
+    c = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = fp8.e4m3_decode(c)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    # from the format: exponent field e (bias 7), mantissa m (3 bits)
+    assert fp8.e4m3_decode(np.array([0x38]))[0] == 1.0         # e = 7, m = 0
+    assert fp8.e4m3_decode(np.array([0x7E]))[0] == 448.0       # e = 15, m = 6: 1.75 * 2^8
+    assert fp8.e4m3_decode(np.array([0x01]))[0] == 2.0 ** -9   # smallest subnormal
+    assert fp8.e4m3_decode(np.array([0x08]))[0] == 2.0 ** -6   # smallest normal
+    assert fp8.e4m3_decode(np.array([0xB9]))[0] == -1.125      # sign, e = 7, m = 1
+    assert np.isnan(fp8.e4m3_decode(np.array([0x7F, 0xFF]))).all()
+
+
+def test_encode_matches_library_including_ties_and_subnormals():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(100000) * np.exp2(rng.integers(-14, 9, 100000))).astype(np.float32)
+    x = np.clip(x, -463.0, 463.0)
+    # exact midpoints between neighbouring codes (5 significant bits: float32-exact)
+    finite = np.array([c for c in range(0x7E)], np.uint8)
+    v = fp8.e4m3_decode(finite)
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, -mids, np.float32([0.0, -0.0, 448.0, 463.9, -463.9])])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(fp8.e4m3_encode(x), want)
+    # ties go to the even mantissa
+    codes = fp8.e4m3_encode(mids)
+    assert np.all(codes % 2 == 0)
+
+
+def test_encode_decode_round_trip():
+    c = np.array([i for i in range(256) if (i & 0x7F) != 0x7F], np.uint8)
+    assert np.array_equal(fp8.e4m3_encode(fp8.e4m3_decode(c)), c)
+    with pytest.raises(ValueError):
+        fp8.e4m3_encode(np.array([465.0]))
+
+
+def test_group_quantisation_bound_and_amax_code():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((40, 128)) * np.exp2(rng.integers(-6, 6, (40, 1)))).astype(np.float32)
+    x[7] = 0.0                                         # an all-zero group
+    codes, scale = fp8.quantize_groups(x, axes=-1)
+    amax = np.abs(x).max(axis=1)
+    assert scale[7, 0] == 0 and not codes[7].any()
+    nz = amax > 0
+    # scale = amax / 448 in float32; the amax element takes the largest code
+    assert np.array_equal(scale[nz, 0], (amax[nz] / np.float32(448)).astype(np.float32))
+    top = np.abs(x).argmax(axis=1)
+    assert np.all((codes[nz, top[nz]] & 0x7F) == 0x7E)
+    # every value within half a quantum: 2^-4 relative (normals) or 2^-10 * scale
+    deq = fp8.dequantize(codes, scale)
+    err = np.abs(deq - x.astype(np.float64))
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale.astype(np.float64)) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    # library route: float32 group scale, float32 product, torch's e4m3 conversion
+    t = torch.from_numpy(x)
+    am = t.abs().amax(dim=1, keepdim=True)
+    inv = torch.where(am > 0, torch.tensor(448.0) / torch.where(am > 0, am, torch.ones_like(am)),
+                      torch.zeros_like(am))
+    lib = (t * inv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, lib)
+
+
+def _planted_k(T, H, D, tile, rng):
+    """Keys whose only large entry per (tile, head) is planted: |k| <= 1 elsewhere,
+    one entry of magnitude A[tile, head] > 2."""
+    k = rng.uniform(-1, 1, (T, H, D)).astype(np.float32)
+    nt = -(-T // tile)
+    A = np.exp2(rng.uniform(1.5, 6, (nt, H))).astype(np.float32)
+    where = []
+    for t in range(nt):
+        n = min(tile, T - t * tile)
+        for h in range(H):
+            tok, d = t * tile + rng.integers(n), rng.integers(D)
+            k[tok, h, d] = -A[t, h] if (t + h) % 2 else A[t, h]
+            where.append((t, h, tok, d))
+    return k, A, where
+
+
+def test_k_tiles_group_per_tile_and_head():
+    rng = np.random.default_rng(7)
+    T, H, D = 150, 3, 64                     # ragged last tile of 22 tokens
+    k, A, where = _planted_k(T, H, D, 64, rng)
+    codes, scales = fp8.quantize_k_tiles(k)
+    assert scales.shape == (3, H)
+    assert np.array_equal(scales, (A / np.float32(448)).astype(np.float32))
+    top = np.zeros(codes.shape, bool)
+    for t, h, tok, d in where:
+        top[tok, h, d] = True
+    # exactly the planted entries take the largest magnitude code
+    assert np.array_equal((codes & 0x7F) == 0x7E, top)
+    # scaling one tile by 2^3 scales its scales only; codes do not move
+    k2 = k.copy()
+    k2[64:128] *= 8
+    c2, s2 = fp8.quantize_k_tiles(k2)
+    assert np.array_equal(c2, codes)
+    assert np.array_equal(s2[1], scales[1] * 8) and np.array_equal(s2[[0, 2]], scales[[0, 2]])
+
+
+def test_q_rows_group_per_row():
+    rng = np.random.default_rng(8)
+    q = rng.uniform(-1, 1, (2, 5, 3, 64)).astype(np.float32)
+    q[1, 2, 1, 9] = 40.0
+    codes, scales = fp8.quantize_q_rows(q)
+    assert scales.shape == (2, 5, 3)
+    assert scales[1, 2, 1] == np.float32(40.0) / np.float32(448)
+    assert codes[1, 2, 1, 9] == 0x7E
+    # the other rows are untouched by the planted value
+    c0, s0 = fp8.quantize_q_rows(q[0])
+    assert np.array_equal(c0, codes[0]) and np.array_equal(s0, scales[0])
+
+
+def test_fp8_tick_reduces_to_bf16_tick_when_exact():
+    """Inputs that the 8-bit tier represents exactly (each quantisation group's
+    values are e4m3 values times 2^e with one entry at 448 * 2^e, so scale = 2^e)
+    give exactly the bf16 oracle's result; a dropped or misplaced scale would not."""
+    rng = np.random.default_rng(11)
+    S, T, H, D, P, n_hist = 2, 100, 2, 64, 64, 1
+    finite = fp8.e4m3_decode(np.arange(0x7E, dtype=np.uint8))
+
+    def exact_values(shape, group_of):
+        x = rng.choice(finite, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        e = {}
+        out = np.empty(shape)
+        for idx in np.ndindex(*shape[:-1]):
+            g = group_of(idx)
+            if g not in e:
+                e[g] = int(rng.integers(-9, -3))
+            out[idx] = x[idx] * 2.0 ** e[g]
+        # one entry per group at the top code
+        seen = set()
+        for idx in np.ndindex(*shape[:-1]):
+            g = group_of(idx)
+            if g not in seen:
+                seen.add(g)
+                out[idx + (int(rng.integers(shape[-1])),)] = 448.0 * 2.0 ** e[g]
+        return out
+
+    q = exact_values((S + 1, T, H, D), lambda i: i)                       # per row, head
+    kl = exact_values((S + 1, T, H, D), lambda i: (i[0], i[1] // 64, i[2]))  # per tile, head
+    kh = exact_values((n_hist, T, H, D), lambda i: (i[0], i[1] // 64, i[2]))
+    v = rng.standard_normal((S + 1, T, H, D))
+    vh = rng.standard_normal((n_hist, T, H, D))
+    to_bits = lambda a: (np.ascontiguousarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vb, vhb = to_bits(v), to_bits(vh)
+    # the representable values are bf16-exact
+    assert np.array_equal(oracle.decode_bf16(to_bits(q)), q)
+    store = fp8.Fp8PageStore(P, H, D)
+    ppc = -(-T // P)
+    hist = [list(range(c * ppc, (c + 1) * ppc)) for c in range(n_hist)]
+    live = [list(range((n_hist + j) * ppc, (n_hist + j + 1) * ppc)) for j in range(S + 1)]
+    for c in range(n_hist):
+        store.write_chunk(hist[c], to_bits(kh[c]), vhb[c])
+    for j in range(S + 1):
+        store.write_chunk(live[j], to_bits(kl[j]), vb[j])
+    mask = (1 << (S + 1)) - 1
+    got = fp8.attention_tick_fp8(to_bits(q), store, hist, live, S, mask, 0.125)
+    want = oracle.attention_tick(q, kl, oracle.decode_bf16(vb), kh, oracle.decode_bf16(vhb), S,
+                                 mask, 0.125)
+    for s in want:
+        assert np.array_equal(got[s], want[s])
+
+
+def test_page_store_matches_contiguous_quantisation():
+    rng = np.random.default_rng(12)
+    T, H, D, P = 300, 2, 64, 128               # 3 pages, 2 scale slots each, ragged
+    k = (rng.standard_normal((T, H, D)) * 3).astype(np.float32)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    vb = rng.integers(0, 2 ** 15, (T, H, D)).astype(np.uint16)
+    store = fp8.Fp8PageStore(P, H, D)
+    ids = [5, 1, 3]
+    store.write_chunk(ids, kb, vb)
+    codes, scales = fp8.quantize_k_tiles(kb)
+    K, V = store.gather([ids], T)
+    want = fp8.e4m3_decode(codes) * np.repeat(scales, 64, axis=0)[:T, :, None]
+    assert np.array_equal(K[0], want) and np.array_equal(V[0], vb)
+    kc, ks, _ = store.pages[3]
+    assert not kc[T - 2 * P:].any() and ks[1].tolist() == [0.0, 0.0]  # past the chunk
+    with pytest.raises(ValueError):
+        fp8.Fp8PageStore(96, H, D)
