@@ -33,6 +33,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+# 8-bit tier: Q.K^T (half the useful flops) on fp8 MFMA, P.V on bf16 MFMA, so
+# the time floor is F/2 / 5000 + F/2 / 2500 and the blended peak 3333 TFLOP/s.
+PEAK_FP8_TIER_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # HBM traffic of the attention kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
@@ -99,9 +103,10 @@ def parse():
     ap.add_argument("--kernel-hash", action="store_true",
                     help="print the attention kernel's source hash (recorded with its counters)")
     ap.add_argument("--mode", default="tick",
-                    choices=["tick", "attn", "store", "rope", "paged", "copy"],
+                    choices=["tick", "attn", "store", "rope", "paged", "copy", "fp8", "store8"],
                     help="tick: the full hot path (default, prints the JSON line); attn / "
-                         "store / rope: only that kernel, --steps launches (for profilers); "
+                         "store / rope / fp8 (8-bit tier attention) / store8 (8-bit tier "
+                         "producer write): only that kernel, --steps launches (for profilers); "
                          "paged: --steps ticks of the fully paged flow; copy: a plain 1 GiB "
                          "device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -412,6 +417,124 @@ def fully_paged(cfg, dev, steps: int = 10, warmup: int = 3) -> dict:
             "attn_frac_bf16_peak": round(flops / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+class Fp8Tick:
+    """The 8-bit tier at the same shape, fully paged: history and live chunks in
+    e4m3 key pages (+ scales) and bf16 value pages written by wf_store_paged_fp8,
+    the tick's attention reading every key through them."""
+
+    def __init__(self, cfg, dev):
+        import torch
+
+        from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+        self.torch, self.wf, self.cfg = torch, wfattn, cfg
+        S, T, H, D, P = cfg.S, cfg.T, cfg.H, cfg.D, cfg.P
+        self.ppc = ppc = cfg.ppc
+        n = (cfg.n_hist + S + 1) * ppc
+        order = torch.from_numpy(inputs.initial_free_order(cfg)[:n].copy()).to(dev)
+        self.hist = order[:cfg.n_hist * ppc].view(cfg.n_hist, ppc)
+        self.live = order[cfg.n_hist * ppc:].view(S + 1, ppc)
+        self.k_pool = torch.zeros((cfg.num_pages, P, H, D), dtype=torch.uint8, device=dev)
+        self.k_scale = torch.zeros((cfg.num_pages, P // 64, H), dtype=torch.float32, device=dev)
+        self.v_pool = torch.zeros((cfg.num_pages, P, H, D), dtype=torch.bfloat16, device=dev)
+        for c in range(cfg.n_hist):
+            hk, hv, _ = inputs.draw_live_torch(cfg, 2000 + c, dev)
+            wfattn.wf_store_paged_fp8(hk[0], hv[0], self.k_pool, self.k_scale, self.v_pool,
+                                      self.hist[c])
+            del hk, hv
+        self.q, self.k, self.v = inputs.draw_live_torch(cfg, inputs.rollout_seed(0), dev)
+        self.store_live()
+        self.o = torch.empty_like(self.q)
+        self.scale = 1.0 / float(np.sqrt(D))
+        self.mask = (1 << (S + 1)) - 1
+        torch.cuda.synchronize()
+
+    def store_live(self):
+        for j in range(self.cfg.S + 1):
+            self.wf.wf_store_paged_fp8(self.k[j], self.v[j], self.k_pool, self.k_scale,
+                                       self.v_pool, self.live[j])
+
+    def attn(self):
+        self.wf.wf_attn_tick(self.q, None, None, self.o, self.cfg.S, self.mask, self.scale,
+                             self.k_pool, self.v_pool, self.hist, live_pages=self.live,
+                             k_scale=self.k_scale)
+
+
+def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3) -> dict:
+    """8-bit tier: attention launches alone, and the tick with every live chunk's
+    producer write (five wf_store_paged_fp8 + the attention)."""
+    import torch
+
+    from wavefront_causal_attention_wf_amd import wfattn
+
+    ft = Fp8Tick(cfg, dev)
+    flops = wfattn.wf_tick_useful_flops(cfg.S, ft.mask, cfg.T, cfg.H, cfg.D, cfg.n_hist, P=cfg.P,
+                                        num_pages=cfg.num_pages)
+    for _ in range(warmup):
+        ft.attn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(launches):
+        ft.attn()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / launches
+    a.record()
+    for _ in range(launches):
+        ft.store_live()
+        ft.attn()
+    b.record()
+    torch.cuda.synchronize()
+    ms_tick = a.elapsed_time(b) / launches
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"tier": "e4m3 Q and K (per-row / per-(64-token tile, head) fp32 scales), Q.K^T on "
+                    "fp8 MFMA, bf16 P.V; every key through pages",
+            "attn_kernel_ms_mean": round(ms, 4), "useful_tflop_per_s": round(tf, 2),
+            "frac_blended_peak": round(tf / PEAK_FP8_TIER_TFLOPS, 4),
+            "blended_peak_tflop_per_s": round(PEAK_FP8_TIER_TFLOPS, 1),
+            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "tick_with_producer_writes_ms": round(ms_tick, 4),
+            "tick_flow": f"{cfg.S + 1} x wf_store_paged_fp8 (every live chunk) + wf_attn_tick"}
+
+
+def store_fp8_bandwidth(cfg, dev, launches: int = 96, rotation: int = 8) -> dict:
+    """wf_store_paged_fp8 of one chunk (K quantised, V copied), rotating over
+    `rotation` source chunks and page sets so that they do not sit in the
+    last-level cache."""
+    import torch
+
+    from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+    T, H, D, P, ppc = cfg.T, cfg.H, cfg.D, cfg.P, cfg.ppc
+    srcs = [inputs.draw_live_torch(cfg, 3000 + i, dev, T=T)[:2] for i in range(rotation)]
+    k_pool = torch.zeros((rotation * ppc, P, H, D), dtype=torch.uint8, device=dev)
+    k_scale = torch.zeros((rotation * ppc, P // 64, H), dtype=torch.float32, device=dev)
+    v_pool = torch.zeros((rotation * ppc, P, H, D), dtype=torch.bfloat16, device=dev)
+    ids = [torch.arange(i * ppc, (i + 1) * ppc, dtype=torch.int32, device=dev)
+           for i in range(rotation)]
+
+    def launch(i):
+        k, v = srcs[i % rotation]
+        wfattn.wf_store_paged_fp8(k[0], v[0], k_pool, k_scale, v_pool, ids[(i * 3) % rotation])
+
+    for i in range(rotation):
+        launch(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(launches):
+        launch(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / launches
+    nbytes = 2 * (T * H * D * 2) + ppc * P * H * D * 3 + ppc * (P // 64) * H * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "wf_store_paged_fp8", "us_mean": round(ms * 1e3, 2), "bytes": nbytes,
+            "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "rotation": rotation}
+
+
 def profile_mode(args, cfg, dev) -> None:
     """Launch-only loops for profilers (no JSON line)."""
     import torch
@@ -438,6 +561,17 @@ def profile_mode(args, cfg, dev) -> None:
     if args.mode == "paged":
         r = fully_paged(cfg, dev, steps=args.steps)
         log(f"fully paged: {r}")
+        return
+    if args.mode == "fp8":
+        ft = Fp8Tick(cfg, dev)
+        for _ in range(args.steps):
+            ft.attn()
+        torch.cuda.synchronize()
+        log(f"fp8 attn: {args.steps} launches")
+        return
+    if args.mode == "store8":
+        r = store_fp8_bandwidth(cfg, dev, launches=args.steps)
+        log(f"fp8 store: {r}")
         return
     ro = Rollout(cfg, 1, dev)
     q, k, v = ro.live[0]
@@ -575,6 +709,10 @@ def main():
     log(f"rope store: {out['rope_store']}")
     out["fully_paged"] = fully_paged(cfg, dev)
     log(f"fully paged: {out['fully_paged']}")
+    out["fp8_tier"] = fp8_tier(cfg, dev)
+    log(f"fp8 tier: {out['fp8_tier']}")
+    out["store_fp8"] = store_fp8_bandwidth(cfg, dev)
+    log(f"fp8 store: {out['store_fp8']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_s)

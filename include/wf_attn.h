@@ -57,7 +57,7 @@ const char* wf_last_error(void);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t wf_abi_version(void);
-#define WF_ABI_VERSION 3
+#define WF_ABI_VERSION 4
 
 /* ------------------------------------------------------------------------ */
 /* Page table: host-only state for one request's attention pages.            */
@@ -158,6 +158,34 @@ wf_status wf_rope_store_paged(const void* k_src, const void* v_src, void* k_pool
                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* wf_store_paged_fp8 — a producer's write of one chunk into the pages of the */
+/* 8-bit tier: K as e4m3 codes with fp32 scales, V copied as bf16.            */
+/* [full text] §4.3 (K/V quantisation shrinks K/V payloads; an 8-bit attention */
+/* backend for local computation), Appendix C.5 Table 8 and C.6 (FP8 K/V).    */
+/* The pages fix neither the format nor the scale granularity; here: e4m3     */
+/* (1 sign, 4 exponent bits of bias 7, 3 mantissa bits, largest finite 448),  */
+/* one scale per (64-token tile of a page, head): amax = max |k| over the     */
+/* tile's tokens of that head, scale = amax / 448, code = e4m3 of the fp32    */
+/* product k * (448 / amax) rounded to nearest even (both quotients fp32,    */
+/* correctly rounded; an all-zero tile has scale 0 and zero codes). A key    */
+/* stands for decode(code) * scale. Token t -> slot t % P of page             */
+/* page_ids[t / P]; slots past token T-1 hold zero codes and zero V, and a    */
+/* tile holding none of the chunk's tokens has scale 0.                       */
+/* k_src, v_src: device bf16 [T][H][D]; k_pool: device uint8                  */
+/* [num_pages][P][H][D]; k_scale: device fp32 [num_pages][P/64][H]; v_pool:    */
+/* device bf16 [num_pages][P][H][D]; page_ids: device int32 [ceil(T/P)].     */
+/* Precondition (not checked): a tile's amax is 0 or at least 2^-120 (its    */
+/* reciprocal must be finite in fp32).                                        */
+/* Errors: WF_EINVAL for bad sizes, P not a multiple of 64, NULL pointers,    */
+/* tensors not 16-byte aligned (k_scale: 4-byte), ceil(T/P) > num_pages;      */
+/* WF_EUNSUPPORTED for D not 64/128 or H > 65535; WF_EHIP if the launch fails. */
+/* T = 0 is a no-op.                                                         */
+/* ------------------------------------------------------------------------ */
+wf_status wf_store_paged_fp8(const void* k_src, const void* v_src, void* k_pool, float* k_scale,
+                             void* v_pool, const int32_t* page_ids, int32_t T, int32_t H,
+                             int32_t D, int32_t num_pages, int32_t P, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* wf_gather_paged — diagnostic inverse of the store: copy n_chunks chunks    */
 /* from pool pages into contiguous k_dst, v_dst bf16 [n_chunks][T][H][D].     */
 /* page_ids: device int32 [n_chunks][ceil(T/P)]. Same alignment rules.        */
@@ -179,9 +207,21 @@ wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t*
 /* rounded to bf16 for the P.V product, bf16 output (round to nearest even).  */
 /* With live_pages set, every key of the context is read through pages: the  */
 /* results equal those of the same tick with the live K/V in k and v.         */
+/* 8-bit tier (k_format = WF_K_E4M3): k_pool holds e4m3 codes with scales in  */
+/* k_scale, as written by wf_store_paged_fp8; every key is read through pages */
+/* (live_pages required). Each query row (one head) is quantised in the       */
+/* kernel the same way with its own scale (amax over its D channels), Q.K^T   */
+/* runs on the e4m3 MFMA with fp32 accumulation, and the scores are the       */
+/* product of the codes' dot product, the query scale and the key tile's      */
+/* scale; the softmax and P.V are those of the bf16 tier. Needs D = 128, P a  */
+/* multiple of 64, no store_pages; a query row's amax must be 0 or at least   */
+/* 2^-120 (not checked).                                                     */
 /* Errors: WF_EINVAL for bad sizes, masks, pointers (NULL or not 16-byte      */
 /* aligned), P not a positive multiple of 16, n_hist*ceil(T/P) > num_pages;   */
-/* WF_EUNSUPPORTED for D not 64/128, n_hist + S + 1 > 32, T > 2^24,           */
+/* k_format not WF_K_BF16/WF_K_E4M3, or WF_K_E4M3 without live_pages or      */
+/* k_scale, with store_pages, or with P not a multiple of 64;                 */
+/* WF_EUNSUPPORTED for D not 64/128 (WF_K_E4M3: not 128), n_hist + S + 1 > 32, */
+/* T > 2^24,                                                                  */
 /* T*P >= 2^32, num_pages*P >= 2^31, and tables the kernel stages in LDS    */
 /* that would not fit: with P a multiple of 64, more than 1536 64-key tiles   */
 /* in one slot's context (segments * ceil(T/64)); otherwise more than 4096    */
@@ -215,7 +255,14 @@ typedef struct wf_tick_desc {
                           /* exactly as wf_store_paged (one launch per tick instead */
                           /* of two). Needs slot S active, the pools, P, num_pages; */
                           /* excludes live_pages                                    */
+  int32_t k_format;       /* WF_K_BF16 (0): k_pool bf16; WF_K_E4M3 (1): k_pool uint8 */
+                          /* e4m3 codes [num_pages][P][H][D] with k_scale           */
+  const float* k_scale;   /* device fp32 [num_pages][P/64][H] with WF_K_E4M3, else  */
+                          /* ignored                                                */
 } wf_tick_desc;
+
+#define WF_K_BF16 0
+#define WF_K_E4M3 1
 
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);
 

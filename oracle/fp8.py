@@ -174,8 +174,15 @@ def attention_tick_fp8(q_bits, store: "Fp8PageStore", hist_pages, live_pages, S:
     from .wave_attention import attention_tick
 
     T, H, D = q_bits.shape[1], q_bits.shape[2], q_bits.shape[3]
-    qc, qs = quantize_q_rows(q_bits)
-    qv = e4m3_decode(qc) * qs[..., None].astype(np.float64)
+    rows = kw.get("rows")
+    if rows is None:
+        qc, qs = quantize_q_rows(q_bits)
+        qv = e4m3_decode(qc) * qs[..., None].astype(np.float64)
+    else:  # each row is quantised on its own: only the requested rows are needed
+        rows = np.asarray(rows)
+        qc, qs = quantize_q_rows(q_bits[:, rows])
+        qv = np.zeros(q_bits.shape, np.float64)
+        qv[:, rows] = e4m3_decode(qc) * qs[..., None].astype(np.float64)
     hk, hv = store.gather(hist_pages, T)
     lk = np.zeros((S + 1, T, H, D), np.float64)
     lv = np.zeros((S + 1, T, H, D), np.uint16)

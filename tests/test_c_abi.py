@@ -409,3 +409,59 @@ def test_useful_flops_matches_oracle(name):
     if name == "wan13_4step":
         assert abs(wf.wf_tick_useful_flops(c.S, full, c.T, c.H, c.D, c.n_hist, P=c.P,
                                            num_pages=c.num_pages) - 4.037e12) < 1e9
+
+
+def test_tick_validation_fp8_keys():
+    """The 8-bit tier: k_format must be known; e4m3 keys need D = 128, P a
+    multiple of 64, live_pages, k_scale (4-byte aligned) and no fused store."""
+    wf = _wfattn()
+    fake = 1 << 20
+
+    def desc(**kw):
+        base = dict(q=fake, o=fake, k_pool=fake, v_pool=fake)
+        live = kw.pop("live", True)
+        fmt = kw.pop("k_format", wf.K_E4M3)
+        scale = kw.pop("k_scale", fake)
+        store = kw.pop("store", False)
+        d = _desc(wf, **{**base, **kw})
+        if live:
+            d.live_pages = fake
+        if store:
+            d.store_pages = fake
+        d.k_format = fmt
+        d.k_scale = scale
+        return d
+
+    for d, code in ((desc(k_format=2), "EINVAL"),
+                    (desc(D=64), "EUNSUPPORTED"),
+                    (desc(P=16), "EINVAL"),
+                    (desc(live=False, k=fake, v=fake), "EINVAL"),
+                    (desc(store=True, k=fake, v=fake), "EINVAL"),
+                    (desc(k_scale=None), "EINVAL"),
+                    (desc(k_scale=fake + 2), "EINVAL")):
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_attn_tick_desc(d, stream=0)
+        assert e.value.status == CODES[code], wf.last_error()
+    wf.wf_attn_tick_desc(desc(T=0), stream=0)  # empty tick: no-op
+
+
+def test_store_fp8_validation():
+    wf = _wfattn()
+    lib = wf.library()
+    fake = 1 << 20
+
+    def call(T=4680, H=12, D=128, num_pages=4096, P=64, k=fake, v=fake, kp=fake, ks=fake,
+             vp=fake, ids=fake):
+        return lib.wf_store_paged_fp8(k, v, kp, ks, vp, ids, T, H, D, num_pages, P, None)
+
+    E, U = CODES["EINVAL"], CODES["EUNSUPPORTED"]
+    assert call(P=96) == E                      # scale tiles of 64 tokens must tile a page
+    assert call(P=0) == E
+    assert call(T=-1) == E
+    assert call(D=96) == U
+    assert call(ks=None) == E
+    assert call(ids=None) == E
+    assert call(ks=fake + 2) == E               # scales not 4-byte aligned
+    assert call(kp=fake + 8) == E               # codes not 16-byte aligned
+    assert call(num_pages=10) == E              # the chunk needs 74 pages
+    assert call(T=0, k=None, v=None, kp=None, ks=None, vp=None, ids=None) == 0

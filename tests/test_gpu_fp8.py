@@ -1,0 +1,186 @@
+"""GPU: the 8-bit tier — e4m3 key pages with per-(64-token tile, head) scales
+written by wf_store_paged_fp8, and the tick whose Q.K^T runs on the e4m3 MFMA
+([full text] §4.3: K/V quantisation and an 8-bit attention backend;
+Appendix C.5 Table 8 and C.6: FP8 K/V).
+
+* The producer's pages (codes, scales, V) must equal the oracle's 8-bit page
+  store bit for bit: both take every decision (amax, the two fp32 quotients,
+  the fp32 product, rounding to nearest even) in the same precision.
+* The tick must match the oracle's attention over the dequantised values
+  within the bf16 tier's tolerance: the only extra rounding on the device is
+  the fp32 accumulation of exact e4m3 products and two fp32 scale products.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as ofp8
+from _gpu_common import DEV, compare, say
+from test_gpu_fullsize import sample_rows
+from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+pytestmark = pytest.mark.gpu
+
+bits = inputs.bf16_tensor_bits
+
+
+class Fp8Pages:
+    """Device pools of the 8-bit tier (codes poisoned with NaN codes 0xFF, scales
+    and V with NaN) and the oracle's 8-bit page store, written side by side."""
+
+    def __init__(self, num_pages, P, H, D):
+        self.P, self.H, self.D = P, H, D
+        self.k_pool = torch.full((num_pages, P, H, D), 0xFF, dtype=torch.uint8, device=DEV)
+        self.k_scale = torch.full((num_pages, P // 64, H), float("nan"), dtype=torch.float32,
+                                  device=DEV)
+        self.v_pool = torch.full((num_pages, P, H, D), float("nan"), dtype=torch.bfloat16,
+                                 device=DEV)
+        self.store = ofp8.Fp8PageStore(P, H, D)
+
+    def write(self, ids, k_chunk: torch.Tensor, v_chunk: torch.Tensor, k_bits=None, v_bits=None):
+        wfattn.wf_store_paged_fp8(k_chunk, v_chunk, self.k_pool, self.k_scale, self.v_pool,
+                                  torch.from_numpy(np.asarray(ids, np.int32)).to(DEV))
+        self.store.write_chunk(list(ids), bits(k_chunk) if k_bits is None else k_bits,
+                               bits(v_chunk) if v_bits is None else v_bits)
+
+    def check(self, ids):
+        """Device pages of `ids` == the oracle's pages, bit for bit."""
+        torch.cuda.synchronize()
+        idx = torch.as_tensor(np.asarray(ids), dtype=torch.long, device=DEV)
+        kc = self.k_pool.index_select(0, idx).cpu().numpy()
+        ks = self.k_scale.index_select(0, idx).cpu().numpy()
+        vb = bits(self.v_pool.index_select(0, idx))
+        for n, pid in enumerate(ids):
+            wk, ws, wv = self.store.pages[int(pid)]
+            bad = kc[n] != wk
+            if bad.any():
+                signed_zero = np.all(((kc[n][bad] | wk[bad]) & 0x7F) == 0)
+                raise AssertionError(f"page {pid}: {int(bad.sum())} codes differ "
+                                     f"(only signed zeros: {bool(signed_zero)}); first "
+                                     f"{kc[n][bad][:4]} vs {wk[bad][:4]}")
+            assert np.array_equal(ks[n].view(np.uint32), ws.view(np.uint32)), f"page {pid} scales"
+            assert np.array_equal(vb[n], wv), f"page {pid} V"
+
+
+@pytest.mark.parametrize("T,H,D,P", [
+    (200, 2, 128, 64),      # ragged last page
+    (150, 3, 64, 128),      # two scale tiles per page, the last page's second one empty
+    (64, 1, 128, 64),       # one full page
+    (4680, 12, 128, 64),    # the Wan-1.3B-like chunk
+])
+def test_store_fp8_matches_oracle_bits(T, H, D, P):
+    say(f"store fp8 T={T} H={H} D={D} P={P}")
+    ppc = -(-T // P)
+    num_pages = ppc + 5
+    cfg = inputs.TickConfig("s", S=0, T=T, H=H, D=D, P=P, n_hist=0, num_pages=num_pages,
+                            std=0.5, bf16_inputs=True, page_order="permutation")
+    k, v, _ = inputs.draw_live_torch(cfg, 77 + T, DEV)
+    k[0, 3] = 0.0                                   # a zero row inside a tile
+    pg = Fp8Pages(num_pages, P, H, D)
+    ids = np.random.default_rng(T).permutation(num_pages)[:ppc].astype(np.int32)
+    pg.write(ids, k[0], v[0])
+    pg.check(ids)
+    # pages outside the chunk are untouched
+    others = sorted(set(range(num_pages)) - set(ids.tolist()))
+    torch.cuda.synchronize()
+    idx = torch.as_tensor(others, dtype=torch.long, device=DEV)
+    assert bool((pg.k_pool.index_select(0, idx) == 0xFF).all())
+    assert bool(torch.isnan(pg.k_scale.index_select(0, idx)).all())
+
+
+def _fp8_tick(S, T, H, P, n_hist, mask, seed, q_gain=1.0):
+    D = 128
+    cfg = inputs.TickConfig("f8", S=S, T=T, H=H, D=D, P=P, n_hist=n_hist, num_pages=1,
+                            std=0.5, bf16_inputs=True, page_order="identity", seed=seed)
+    x = inputs.draw_tick(cfg)
+    q_bits = x.q_bits
+    if q_gain != 1.0:
+        q_bits = inputs.f32_to_bf16_bits(oracle.decode_bf16(q_bits).astype(np.float32)
+                                         * np.float32(q_gain))
+    ppc = -(-T // P)
+    num_pages = (n_hist + S + 2) * ppc + 3
+    order = np.random.default_rng(seed + 5).permutation(num_pages).astype(np.int32)
+    pg = Fp8Pages(num_pages, P, H, D)
+    hist = order[:n_hist * ppc].reshape(n_hist, ppc) if n_hist else np.zeros((0, ppc), np.int32)
+    for c in range(n_hist):
+        pg.write(hist[c], inputs.to_device_bf16(x.hist_k_bits[c], DEV),
+                 inputs.to_device_bf16(x.hist_v_bits[c], DEV), x.hist_k_bits[c], x.hist_v_bits[c])
+    nan_ids = order[-ppc:]                    # never written: inactive slots point here
+    live = np.empty((S + 1, ppc), np.int32)
+    live_lists = []
+    for j in range(S + 1):
+        if (mask >> j) & 1:
+            ids = order[(n_hist + j) * ppc:(n_hist + j + 1) * ppc]
+            pg.write(ids, inputs.to_device_bf16(x.k_bits[j], DEV),
+                     inputs.to_device_bf16(x.v_bits[j], DEV), x.k_bits[j], x.v_bits[j])
+            live[j] = ids
+            live_lists.append(ids.tolist())
+        else:
+            live[j] = nan_ids
+            live_lists.append(None)
+    q = inputs.to_device_bf16(q_bits, DEV)
+    o = torch.full_like(q, float("nan"))
+    scale = 1.0 / np.sqrt(D)
+    wfattn.wf_attn_tick(q, None, None, o, S, mask, scale, pg.k_pool, pg.v_pool,
+                        torch.from_numpy(np.ascontiguousarray(hist)).to(DEV) if n_hist else None,
+                        live_pages=torch.from_numpy(live).to(DEV), k_scale=pg.k_scale)
+    torch.cuda.synchronize()
+    return pg, q_bits, hist, live_lists, o, scale
+
+
+@pytest.mark.parametrize("S,T,H,P,n_hist,mask,q_gain", [
+    (4, 200, 2, 64, 2, 0b11111, 1.0),
+    (3, 130, 2, 128, 1, 0b1011, 1.0),     # slot 2 inactive, two scale tiles per page
+    (2, 64, 2, 64, 0, 0b111, 1.0),        # no history, one tile per chunk
+    (4, 70, 3, 64, 3, 0b10110, 1.0),      # stages 0 and 3 inactive, ragged tiles
+    (2, 300, 2, 64, 1, 0b111, 4.0),       # peaked softmax: the running max is raised
+])
+def test_fp8_tick_matches_oracle(S, T, H, P, n_hist, mask, q_gain):
+    say(f"fp8 tick S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b} q_gain={q_gain}")
+    pg, q_bits, hist, live_lists, o, scale = _fp8_tick(S, T, H, P, n_hist, mask,
+                                                       seed=S * 31 + T, q_gain=q_gain)
+    for ids in list(hist) + [l for l in live_lists if l is not None]:
+        pg.check(list(ids))
+    want = ofp8.attention_tick_fp8(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
+    worst = compare(o, want, label="fp8 tick")
+    # rows of inactive slots are left untouched
+    for s in range(S + 1):
+        if not (mask >> s) & 1:
+            assert torch.isnan(o[s].float()).all()
+    say(f"  worst rel-L2 {worst:.2e}")
+
+
+def test_fp8_tick_full_size_sampled_rows():
+    """The Wan-1.3B-like 4-step tick in the 8-bit tier, as the bench times it:
+    three history chunks and five live chunks in 8-bit pages, sampled rows of
+    every stage and head against the oracle."""
+    cfg = inputs.CONFIGS["wan13_4step"]
+    say(f"[full-size fp8] S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist}")
+    ppc = cfg.ppc
+    pg = Fp8Pages(cfg.num_pages, cfg.P, cfg.H, cfg.D)
+    order = inputs.initial_free_order(cfg)
+    hist = order[:cfg.n_hist * ppc].reshape(cfg.n_hist, ppc)
+    for c in range(cfg.n_hist):
+        hk, hv, _ = inputs.draw_live_torch(cfg, 2000 + c, DEV)
+        pg.write(hist[c], hk[0], hv[0])
+        del hk, hv
+    q, k, v = inputs.draw_live_torch(cfg, inputs.rollout_seed(0), DEV)
+    live = order[cfg.n_hist * ppc:(cfg.n_hist + cfg.S + 1) * ppc].reshape(cfg.S + 1, ppc)
+    for j in range(cfg.S + 1):
+        pg.write(live[j], k[j], v[j])
+    pg.check(list(hist[0]) + list(live[cfg.S]))
+    mask = (1 << (cfg.S + 1)) - 1
+    o = torch.full_like(q, float("nan"))
+    scale = 1.0 / np.sqrt(cfg.D)
+    wfattn.wf_attn_tick(q, None, None, o, cfg.S, mask, scale, pg.k_pool, pg.v_pool,
+                        torch.from_numpy(np.ascontiguousarray(hist)).to(DEV),
+                        live_pages=torch.from_numpy(np.ascontiguousarray(live)).to(DEV),
+                        k_scale=pg.k_scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    rows = sample_rows(cfg.T, seed=8)
+    want = ofp8.attention_tick_fp8(bits(q), pg.store, hist.tolist(), live.tolist(), cfg.S, mask,
+                                   scale, rows=rows)
+    worst = compare(o, want, rows=rows, label="fp8 full size")
+    say(f"[full-size fp8] worst rel-L2 {worst:.2e} over {len(rows)} rows x {cfg.H} heads")

@@ -20,7 +20,7 @@ LIB_NAME = "libwfattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["wf_attn.hip", "wf_paged.hip", "wf_rope.hip", "wf_page_table.cpp", "wf_error.cpp"]
+SOURCES = ["wf_attn.hip", "wf_paged.hip", "wf_rope.hip", "wf_fp8.hip", "wf_page_table.cpp", "wf_error.cpp"]
 
 # Packed-FP32 VALU forms are kept out of the generated code (the device pass
 # honours the flag; the host pass only warns that it does not know it).

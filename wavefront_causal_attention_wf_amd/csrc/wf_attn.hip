@@ -43,6 +43,12 @@
 //    XCDs so that each XCD streams about the same number of keys and the query
 //    tiles of a group share that XCD's L2. Optionally the launch also writes
 //    the store chunk's pages (leading blocks).
+//  * 8-bit tier (full text §4.3: K/V quantisation, an 8-bit attention
+//    backend): keys come from e4m3 pages with one fp32 scale per (64-key tile,
+//    head), each query row is quantised to e4m3 in the kernel with its own
+//    scale, and Q.K^T runs on v_mfma_f32_32x32x64_f8f6f4 (half the MFMA time and
+//    half the K bytes in LDS of the bf16 product); the two scales fold into the
+//    softmax's per-tile multiplier, and P.V stays bf16.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -58,6 +64,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KT = 64;              // keys per tile
 #ifndef WF_NWAVES
@@ -92,6 +100,8 @@ struct AttnParams {
   int32_t store_row16;        // 16-byte units per token row (H * D * 2 / 16)
   int32_t store_slot;         // S
   int32_t n_hist;
+  const float* k_scale;   // 8-bit tier: [num_pages][P / 64][H] key tile scales
+  int32_t spp;            // 64-token scale tiles per page (P / 64)
   int32_t T, H, P, ppc;
   int32_t tps;            // tiles per chunk, ceil(T / 64)
   int32_t t_last;         // keys in a chunk's last tile, T - 64 * (tps - 1)
@@ -135,6 +145,13 @@ __device__ __forceinline__ int kswz(int row) {
   if constexpr (D == 128) return (row & 3) | ((row >> 1) & 4) | ((row << 1) & 8);
   return (row & 3) ^ ((row >> 2) & 1) ^ ((row >> 1) & 4);
 }
+// 8-bit keys (D = 128: rows of 128 bytes, 8 chunks; two rows per 256 bytes):
+// a read touches rows {0..3, 8..11} (+4, ...) at one logical chunk; bits 0, 1
+// and 3 of the row (bit 0 mixed with bit 2) pick the chunk, so any such 8 rows
+// land in distinct chunks, and rows 0..15 of one parity too.
+__device__ __forceinline__ int kswz8(int row) {
+  return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 1) & 4);
+}
 template <int D>
 __device__ __forceinline__ int vswz(int row) {
   const int q = row & 3;
@@ -176,7 +193,7 @@ struct Uniforms {
   const char* k_pool;
   const char* v_pool;
   int32_t T, H, P, ppc, tps, t_last;
-  uint32_t p_magic, row_bytes;
+  uint32_t p_magic, row_bytes, krow_bytes;  // token row bytes of V (and bf16 K), of K
   float c;  // softmax scale * log2(e)
 };
 
@@ -190,7 +207,7 @@ __device__ __forceinline__ const char* uniform_ptr(const void* ptr) {
   return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
 }
 
-template <int D>
+template <int D, int KB>
 __device__ __forceinline__ Uniforms load_uniforms(const AttnParams& p, int h) {
   Uniforms u;
   u.T = uniform_i32(p.T);
@@ -201,11 +218,12 @@ __device__ __forceinline__ Uniforms load_uniforms(const AttnParams& p, int h) {
   u.t_last = uniform_i32(p.t_last);
   u.p_magic = uint32_t(uniform_i32(int32_t(p.p_magic)));
   u.row_bytes = uint32_t(u.H) * D * 2;
+  u.krow_bytes = uint32_t(u.H) * D * KB;
   u.c = __builtin_bit_cast(float, uniform_i32(__builtin_bit_cast(int32_t, p.c)));
   // head h's column block of every tensor
   u.k = uniform_ptr(p.k + int64_t(h) * D);
   u.v = uniform_ptr(p.v + int64_t(h) * D);
-  u.k_pool = uniform_ptr(p.k_pool + int64_t(h) * D);
+  u.k_pool = uniform_ptr(reinterpret_cast<const char*>(p.k_pool) + int64_t(h) * D * KB);
   u.v_pool = uniform_ptr(p.v_pool + int64_t(h) * D);
   return u;
 }
@@ -230,17 +248,24 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // tiles resolve each lane's page through the page table in LDS, and the
 // segment's code is read (a scalar load) only when the cursor enters a new
 // segment. prepare*() resolves the next tile and advances the cursor; emit(i)
-// issues the two loads of row group i. Past the last tile the cursor reads
-// tile 0 again (finite, masked).
-template <int D, bool kFast>
+// issues the loads of row group i. Past the last tile the cursor reads tile 0
+// again (finite, masked). KB = bytes per key element: 2 (bf16), or 1 (e4m3
+// keys of the 8-bit tier, whose rows are half as long, so a wave needs half
+// as many K instructions per tile; kFast only).
+template <int D, bool kFast, int KB>
 struct TileLoader {
-  static constexpr int DC = D / 8;        // 16-byte chunks per row
-  static constexpr int RPI = 64 / DC;     // rows per wave instruction
+  static_assert(KB == 2 || kFast, "8-bit keys need whole-tile sources");
+  static constexpr int DC = D / 8;        // 16-byte chunks per V row
+  static constexpr int RPI = 64 / DC;     // V rows per wave instruction
   static constexpr int RW = KT / NWAVES;  // tile rows loaded by each wave
-  static constexpr int NI = RW / RPI;     // instructions per wave per tensor
+  static constexpr int NI = RW / RPI;     // V instructions per wave per tile
+  static constexpr int DCK = D * KB / 16; // 16-byte chunks per K row
+  static constexpr int RPIK = 64 / DCK;   // K rows per wave instruction
+  static constexpr int NIK = RW / RPIK;   // K instructions per wave per tile (<= NI)
+  static constexpr int LPT = NI + NIK;    // loads per wave per tile
 
   // per lane (bytes): row offset + swizzled column, full and last-tile rows
-  uint32_t koff[NI], voff[NI], koff_r[NI], voff_r[NI];
+  uint32_t koff[NIK], voff[NI], koff_r[NIK], voff_r[NI];
   int32_t row[NI];
   // cursor: next tile to resolve
   int seg, m;
@@ -263,12 +288,18 @@ struct TileLoader {
     for (int i = 0; i < NI; ++i) {
       row[i] = wave * RW + RPI * i + lane / DC;
       const int rr = row[i] < u.t_last ? row[i] : u.t_last - 1;
-      const uint32_t kc = uint32_t(pc ^ kswz<D>(row[i])) * 16;
       const uint32_t vc = uint32_t(pc ^ vswz<D>(row[i])) * 16;
-      koff[i] = uint32_t(row[i]) * u.row_bytes + kc;
       voff[i] = uint32_t(row[i]) * u.row_bytes + vc;
-      koff_r[i] = uint32_t(rr) * u.row_bytes + kc;
       voff_r[i] = uint32_t(rr) * u.row_bytes + vc;
+    }
+    const int pck = lane % DCK;
+#pragma unroll
+    for (int i = 0; i < NIK; ++i) {
+      const int kr = wave * RW + RPIK * i + lane / DCK;
+      const int rr = kr < u.t_last ? kr : u.t_last - 1;
+      const uint32_t kc = uint32_t(pck ^ (KB == 2 ? kswz<D>(kr) : kswz8(kr))) * 16;
+      koff[i] = uint32_t(kr) * u.krow_bytes + kc;
+      koff_r[i] = uint32_t(rr) * u.krow_bytes + kc;
     }
     seg = 0;
     m = 0;
@@ -352,7 +383,8 @@ struct TileLoader {
 
   __device__ __forceinline__ void emit(int i, const Uniforms& u, uint16_t* kbuf, uint16_t* vbuf,
                                        int wave) const {
-    lds_void* kdst = opaque_lds(kbuf + (wave * RW + RPI * i) * D);
+    // (K buffer offset in 16-bit elements: rows of D * KB bytes)
+    lds_void* kdst = opaque_lds(kbuf + (wave * RW + RPIK * (i < NIK ? i : 0)) * D * KB / 2);
     lds_void* vdst = opaque_lds(vbuf + (wave * RW + RPI * i) * D);
     if (!kFast && per_lane) {
       const uint64_t o = uint64_t(prow[i]) * u.row_bytes;
@@ -373,9 +405,11 @@ struct TileLoader {
       // blend rather than a select, which the compiler would turn into an
       // indexed load of the offset arrays from scratch)
       const uint32_t rmask = 0u - uint32_t(ragged);
-      const uint32_t ko = koff[i] + ((koff_r[i] - koff[i]) & rmask);
+      if (i < NIK) {
+        const uint32_t ko = koff[i] + ((koff_r[i] - koff[i]) & rmask);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kdst, 16, int(ko), 0, 0, 0);
+      }
       const uint32_t vo = voff[i] + ((voff_r[i] - voff[i]) & rmask);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kdst, 16, int(ko), 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vdst, 16, int(vo), 0, 0, 0);
     }
   }
@@ -431,28 +465,35 @@ __device__ __forceinline__ void store_page_block(const AttnParams& p, int S) {
   }
 }
 
-template <int D, bool kFast>
+template <int D, bool kFast, bool kF8>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 attn_tick_kernel(const AttnParams p) {
+  static_assert(!kF8 || (D == 128 && kFast), "8-bit keys: D = 128, whole-tile sources");
   constexpr int KS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  using Loader = TileLoader<D, kFast>;
+  constexpr int KB = kF8 ? 1 : 2;  // bytes per key element
+  using Loader = TileLoader<D, kFast, KB>;
   constexpr int NI = Loader::NI;
+  constexpr int LPT = Loader::LPT;
+  constexpr int KTILE = KT * D * KB / 2;  // one K tile in 16-bit elements
   // Four K and four V tile buffers (one array each, 256-byte aligned); the loop
   // is unrolled by four so that every access names its buffer statically.
-  __shared__ __attribute__((aligned(256))) uint16_t k_tiles[4 * KT * D];
+  __shared__ __attribute__((aligned(256))) uint16_t k_tiles[4 * KTILE];
   __shared__ __attribute__((aligned(256))) uint16_t v_tiles[4 * KT * D];
   uint16_t* const k_lds0 = k_tiles;
-  uint16_t* const k_lds1 = k_tiles + KT * D;
-  uint16_t* const k_lds2 = k_tiles + 2 * KT * D;
-  uint16_t* const k_lds3 = k_tiles + 3 * KT * D;
+  uint16_t* const k_lds1 = k_tiles + KTILE;
+  uint16_t* const k_lds2 = k_tiles + 2 * KTILE;
+  uint16_t* const k_lds3 = k_tiles + 3 * KTILE;
   uint16_t* const v_lds0 = v_tiles;
   uint16_t* const v_lds1 = v_tiles + KT * D;
   uint16_t* const v_lds2 = v_tiles + 2 * KT * D;
   uint16_t* const v_lds3 = v_tiles + 3 * KT * D;
   __shared__ int32_t pages_lds[kFast ? 1 : kMaxPageIds];
   __shared__ uint4 tile_tab[kFast ? kMaxTiles : 1];
+  // 8-bit tier: each tile's key scale for this head (0 replaced by 1: an
+  // all-zero tile has zero codes, so any finite multiplier gives its scores)
+  __shared__ float tile_scale[kF8 ? kMaxTiles : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -488,7 +529,7 @@ attn_tick_kernel(const AttnParams p) {
   const int T = p.T;
   const int ntiles = nseg * p.tps;
 
-  const Uniforms u = load_uniforms<D>(p, h);
+  const Uniforms u = load_uniforms<D, KB>(p, h);
   if constexpr (kFast) {
     // sources of every tile of this (stage, head), one thread per tile
     for (int t = tid; t < ntiles; t += NTHREADS) {
@@ -506,9 +547,15 @@ attn_tick_kernel(const AttnParams p) {
                                        : p.hist_pages + (-code - 1) * u.ppc;
         const uint32_t pg = t0 / uint32_t(u.P);
         const int pid = ids[int(pg)];
-        const uint64_t prow = uint64_t(uint32_t(pid)) * uint32_t(u.P) + (t0 - pg * uint32_t(u.P));
-        kr = reinterpret_cast<uint64_t>(u.k_pool + prow * u.row_bytes);
+        const uint32_t off = t0 - pg * uint32_t(u.P);
+        const uint64_t prow = uint64_t(uint32_t(pid)) * uint32_t(u.P) + off;
+        kr = reinterpret_cast<uint64_t>(u.k_pool + prow * u.krow_bytes);
         vr = reinterpret_cast<uint64_t>(u.v_pool + prow * u.row_bytes);
+        if constexpr (kF8) {
+          const float ks =
+              p.k_scale[(int64_t(pid) * p.spp + int(off / uint32_t(KT))) * u.H + h];
+          tile_scale[t] = ks > 0.f ? ks : 1.f;
+        }
       }
       kr |= (mm == u.tps - 1) ? 1u : 0u;  // bases are 16-byte aligned: bit 0 is free
       tile_tab[t] = make_uint4(uint32_t(kr), uint32_t(kr >> 32), uint32_t(vr), uint32_t(vr >> 32));
@@ -525,8 +572,48 @@ attn_tick_kernel(const AttnParams p) {
   const int qrow = q0w + r;
 
   // ---- Q^T operand: lane holds query qrow, head dims 16*ks + 8*g .. +7 -----
-  bf16x8 qf[KS];
-  {
+  // (8-bit tier: head dims 64*dh + 32*g .. +31 of MFMA dh, as e4m3 codes)
+  bf16x8 qf[kF8 ? 1 : KS];
+  i32x8 qf8[2];
+  float cq = u.c;  // multiplier of this lane's raw scores (8-bit: times its query scale)
+  if constexpr (kF8) {
+    const uint4* qp = reinterpret_cast<const uint4*>(p.q + ((int64_t(s) * T + qrow) * p.H + h) * D);
+    uint4 raw[2][4];
+    float am = 0.f;
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        raw[dh][c] = (qrow < T) ? qp[8 * dh + 4 * g + c] : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t w[4] = {raw[dh][c].x, raw[dh][c].y, raw[dh][c].z, raw[dh][c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          am = fmaxf(am, fmaxf(fabsf(__uint_as_float(w[i] << 16)),
+                               fabsf(__uint_as_float(w[i] & 0xffff0000u))));
+      }
+    // the row's amax (lanes l and l + 32 hold the two halves of one row), its
+    // scale amax / 448 and the codes of q * (448 / amax), as the keys' producer
+    am = xlane32_max(am);
+    const float inv = am > 0.f ? 448.0f / am : 0.f;
+    const float qscale = am / 448.0f;
+    cq = qscale > 0.f ? u.c * qscale : u.c;  // zero row: zero codes, any multiplier
+#pragma unroll
+    for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t w[4] = {raw[dh][c].x, raw[dh][c].y, raw[dh][c].z, raw[dh][c].w};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t a = w[2 * half], b = w[2 * half + 1];
+          int r4 = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(a << 16) * inv,
+                                                   __uint_as_float(a & 0xffff0000u) * inv, 0,
+                                                   false);
+          r4 = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(b << 16) * inv,
+                                               __uint_as_float(b & 0xffff0000u) * inv, r4, true);
+          qf8[dh][2 * c + half] = r4;
+        }
+      }
+  } else {
     const uint4* qp = reinterpret_cast<const uint4*>(p.q + ((int64_t(s) * T + qrow) * p.H + h) * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -556,10 +643,15 @@ attn_tick_kernel(const AttnParams p) {
   // step and row half are constant offsets. One base per tensor then serves
   // every operand read (addresses formed from it inside each MFMA slot rather
   // than dozens of precomputed address registers).
-  constexpr uint32_t TILE_BYTES = KT * D * 2;
+  constexpr uint32_t TILE_BYTES = KT * D * 2;      // one V (and bf16 K) tile
+  constexpr uint32_t KTILE_BYTES = KT * D * KB;   // one K tile
+  // 8-bit keys: rows of D bytes, 16-byte chunk 4*dh + 2*g + piece of MFMA dh
+  // (the two pieces of one 32-byte operand), swizzled by kswz8; as for bf16 the
+  // address of (dh, piece) is the base XOR ((4*dh + piece) << 4).
   // (byte offsets into the tile arrays; reads are formed from the arrays
   // themselves so that the compiler knows which LDS objects they touch)
-  const uint32_t k_lane = uint32_t(krow0 * D * 2 + ((g ^ kx) << 4));
+  const uint32_t k_lane = kF8 ? uint32_t(krow0 * D + (((2 * g) ^ kswz8(krow0)) << 4))
+                              : uint32_t(krow0 * D * 2 + ((g ^ kx) << 4));
   const uint32_t v_lane = uint32_t(vrow * D * 2 + ((vcx ^ vx) << 4) + vsub * 2);
   const char* const k_bytes = reinterpret_cast<const char*>(k_tiles);
   const char* const v_bytes = reinterpret_cast<const char*>(v_tiles);
@@ -585,8 +677,8 @@ attn_tick_kernel(const AttnParams p) {
     resolve();
   }
   // tile 0 has landed (A: tile 1 may still be in flight; B: tiles 1 and 2)
-  if (grp_a) tile_barrier<2 * NI>();
-  else tile_barrier<4 * NI>();
+  if (grp_a) tile_barrier<LPT>();
+  else tile_barrier<2 * LPT>();
 
   // Keys of tile j that are real: 64, the chunk's remainder on a segment's last
   // tile, 0 past the end (the loop runs in groups of four tiles).
@@ -598,38 +690,67 @@ attn_tick_kernel(const AttnParams p) {
 
   f32x16 sacc[2];
   bf16x8 pb[4];
+  float ks_next = 1.f;  // 8-bit tier: key scale of the tile whose scores are in sacc
+
+  // 8-bit K operand op = 2*dh + blk of K tile buffer kbuf: rows of 32-key block
+  // blk, head dims 64*dh + 32*g .. +31 (two 16-byte reads).
+  auto kload8 = [&](uint32_t kl, int kbuf, int op) __attribute__((always_inline)) {
+    const uint32_t a = (kl ^ uint32_t((4 * (op >> 1)) << 4)) + kbuf * KTILE_BYTES +
+                       (op & 1) * (32 * D);
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(k_bytes + a);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(k_bytes + (a ^ 16u));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto mfma8 = [&](const i32x8& a, const i32x8& b, const f32x16& c)
+                   __attribute__((always_inline)) {
+    // formats 0, 0: both operands e4m3; unit block scales
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  };
 
   // S^T = K Q^T for one tile (the first one, before the slot pairs start): two
   // 32-key blocks, K operands two k-steps ahead.
   auto qk = [&](int kbuf) __attribute__((always_inline)) {
     uint32_t kl = k_lane;
     asm volatile("" : "+v"(kl));
-    auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
-      const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
+    if constexpr (kF8) {
+      ks_next = tile_scale[0];
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+      i32x8 ka[4];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
-    };
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
-    bf16x8 ka[3][2];
-    kload(0, ka[0]);
-    kload(1, ka[1]);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int op = 0; op < 4; ++op) ka[op] = kload8(kl, kbuf, op);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+      for (int op = 0; op < 4; ++op) sacc[op & 1] = mfma8(ka[op], qf8[op >> 1], sacc[op & 1]);
+    } else {
+      auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+        const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
-                                                            0, 0, 0);
-      if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
+        for (int blk = 0; blk < 2; ++blk)
+          dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
+      };
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+      bf16x8 ka[3][2];
+      kload(0, ka[0]);
+      kload(1, ka[1]);
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
+                                                              0, 0, 0);
+        if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
   // Online softmax of the scores of tile j (exp2 domain): P as bf16 into pb.
   // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
-  auto softmax = [&](int j) __attribute__((always_inline)) {
+  // ce: the scores' multiplier (softmax scale * log2 e, times the query and
+  // key scales in the 8-bit tier).
+  auto softmax = [&](int j, float ce) __attribute__((always_inline)) {
     const int valid = valid_keys(j);
     if (valid < KT) {
 #pragma unroll
@@ -648,7 +769,7 @@ attn_tick_kernel(const AttnParams p) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const float ev = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], u.c, -m_run));
+          const float ev = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], ce, -m_run));
           part[x & 3] += ev;
           pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(ev);
         }
@@ -666,7 +787,7 @@ attn_tick_kernel(const AttnParams p) {
       for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
 #pragma unroll
       for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
-      mx = xlane32_max(mx) * u.c;
+      mx = xlane32_max(mx) * ce;
       const bool raise = mx > m_run + kLazyTau;
       if (__builtin_amdgcn_ballot_w64(raise) != 0) {
         const float m_new = raise ? mx : m_run;
@@ -706,46 +827,73 @@ attn_tick_kernel(const AttnParams p) {
   // k-step first issues the operand reads of a later step (K two k-steps
   // ahead, V one 16-key step = two k-steps ahead), then runs its P.V MFMAs,
   // then its Q.K^T MFMAs.
-  auto gphase = [&](int vbuf, int kbuf) __attribute__((always_inline)) {
+  auto gphase = [&](int vbuf, int kbuf, int jn) __attribute__((always_inline)) {
     // the lane bases, opaque here so that the read addresses are formed from
     // them inside the slot instead of being kept in registers across the loop
     uint32_t kl = k_lane, vl = v_lane;
     asm volatile("" : "+v"(kl), "+v"(vl));
-    auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
-      const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
+    if constexpr (kF8) {
+      // four 16-key P.V steps (four MFMAs each), each followed by one of the
+      // four 8-bit Q.K^T MFMAs (blocks alternate, so no two in a row share an
+      // accumulator); K operands two steps ahead, V one
+      ks_next = tile_scale[jn < ntiles ? jn : 0];
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+      i32x8 ka[3];
+      bf16x8 va[2][DB];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
-    };
-    constexpr int PV_PER_STEP = 4 * DB / KS;  // P.V MFMAs per Q.K^T k-step
-    sacc[0] = f32x16{};  // the previous scores were consumed by the last softmax
-    sacc[1] = f32x16{};
-    bf16x8 ka[3][2];
-    bf16x8 va[2][DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
-    kload(0, ka[0]);
-    kload(1, ka[1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      // P.V MFMAs number PV_PER_STEP*t .. : 16-key step kk, output blocks db
-      const int pv0 = PV_PER_STEP * t;
-      const int kk = pv0 / DB;
-      // operands of later steps go out before this step's MFMAs
-      if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
-      if (pv0 % DB == 0 && kk + 1 < 4) vload(vl, vbuf, kk + 1, va[(kk + 1) & 1]);
-#pragma unroll
-      for (int e = 0; e < PV_PER_STEP; ++e) {
-        const int db = (pv0 + e) % DB;
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0, 0,
-                                                           0);
-      }
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], sacc[blk], 0,
-                                                            0, 0);
+      for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
+      ka[0] = kload8(kl, kbuf, 0);
+      ka[1] = kload8(kl, kbuf, 1);
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t + 2 < 4) ka[(t + 2) % 3] = kload8(kl, kbuf, t + 2);
+        if (t + 1 < 4) vload(vl, vbuf, t + 1, va[(t + 1) & 1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t & 1][db], pb[t], oacc[db], 0, 0,
+                                                             0);
+        sacc[t & 1] = mfma8(ka[t % 3], qf8[t >> 1], sacc[t & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+        const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+          dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
+      };
+      constexpr int PV_PER_STEP = 4 * DB / KS;  // P.V MFMAs per Q.K^T k-step
+      sacc[0] = f32x16{};  // the previous scores were consumed by the last softmax
+      sacc[1] = f32x16{};
+      bf16x8 ka[3][2];
+      bf16x8 va[2][DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
+      kload(0, ka[0]);
+      kload(1, ka[1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        // P.V MFMAs number PV_PER_STEP*t .. : 16-key step kk, output blocks db
+        const int pv0 = PV_PER_STEP * t;
+        const int kk = pv0 / DB;
+        // operands of later steps go out before this step's MFMAs
+        if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
+        if (pv0 % DB == 0 && kk + 1 < 4) vload(vl, vbuf, kk + 1, va[(kk + 1) & 1]);
+#pragma unroll
+        for (int e = 0; e < PV_PER_STEP; ++e) {
+          const int db = (pv0 + e) % DB;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0, 0,
+                                                             0);
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], sacc[blk], 0,
+                                                              0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -768,12 +916,12 @@ attn_tick_kernel(const AttnParams p) {
   // and B tiles 0-2 up front. A buffer is refilled (slot 2t-3 or 2t-4 for tile
   // t) only after the barrier that ends the last slot reading its previous
   // tile t-4 (slot 2t-5). So at each barrier a wave may leave the loads of its
-  // newest tile in flight (2*NI) and every older load has landed.
+  // newest tile in flight (LPT) and every older load has landed.
   auto end_qk_slot = [&]() __attribute__((always_inline)) {
-    if (!grp_a) tile_barrier<2 * NI>();
+    if (!grp_a) tile_barrier<LPT>();
   };
   auto end_s_slot = [&]() __attribute__((always_inline)) {
-    if (grp_a) tile_barrier<2 * NI>();
+    if (grp_a) tile_barrier<LPT>();
   };
   // The softmax slot of tile js: this wave's loads of its next tile go out
   // first (into kn, vn), then the softmax, then the first V^T operands of the
@@ -784,7 +932,7 @@ attn_tick_kernel(const AttnParams p) {
     resolve();  // the tile this wave loads next
     __builtin_amdgcn_sched_barrier(0);
     if (wave_active) {
-      softmax(js);
+      softmax(js, kF8 ? cq * ks_next : cq);
       __builtin_amdgcn_sched_barrier(0);
       uint32_t vl = v_lane;
       asm volatile("" : "+v"(vl));
@@ -807,7 +955,7 @@ attn_tick_kernel(const AttnParams p) {
     if (wave_active) {
       // the MFMA phase wins issue arbitration over the other wave's softmax
       __builtin_amdgcn_s_setprio(1);
-      gphase(vbuf, kbuf);
+      gphase(vbuf, kbuf, j + 1);
       __builtin_amdgcn_s_setprio(0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -907,9 +1055,9 @@ void plan_xcd_order(const StagePlan& pl, int H, AttnParams& p, int64_t& blocks) 
 
 // kFast: every tile is one uniform span of a page or live chunk (page size a
 // multiple of 64, or no history); otherwise history tiles resolve per lane.
-template <int D, bool kFast>
+template <int D, bool kFast, bool kF8 = false>
 int32_t launch_attn(const AttnParams& p, unsigned blocks, hipStream_t stream) {
-  attn_tick_kernel<D, kFast><<<dim3(blocks), NTHREADS, 0, stream>>>(p);
+  attn_tick_kernel<D, kFast, kF8><<<dim3(blocks), NTHREADS, 0, stream>>>(p);
   return WF_OK;
 }
 
@@ -935,8 +1083,24 @@ int32_t validate_tick(const wf_tick_desc* d) {
     if (d->hist_first[s] < 0 || d->hist_first[s] > d->n_hist)
       return fail(WF_EINVAL, "wf_attn_tick: hist_first[%d] = %d outside [0, %d]", s,
                   d->hist_first[s], d->n_hist);
+  if (d->k_format != WF_K_BF16 && d->k_format != WF_K_E4M3)
+    return fail(WF_EINVAL, "wf_attn_tick: k_format = %d (WF_K_BF16 or WF_K_E4M3)", d->k_format);
+  if (d->k_format == WF_K_E4M3) {
+    if (d->D != 128)
+      return fail(WF_EUNSUPPORTED, "wf_attn_tick: 8-bit keys need D = 128 (D = %d)", d->D);
+    if (d->P <= 0 || d->P % KT != 0)
+      return fail(WF_EINVAL, "wf_attn_tick: 8-bit keys need P a multiple of 64 (P = %d)", d->P);
+  }
   if (d->T == 0 || d->active_mask == 0) return WF_OK;
   const bool live_paged = d->live_pages != nullptr;
+  if (d->k_format == WF_K_E4M3) {
+    if (!live_paged)
+      return fail(WF_EINVAL, "wf_attn_tick: 8-bit keys are read through pages: set live_pages");
+    if (d->store_pages)
+      return fail(WF_EINVAL, "wf_attn_tick: store_pages writes bf16 pages: not with 8-bit keys");
+    if (!d->k_scale || (reinterpret_cast<uintptr_t>(d->k_scale) & 3u))
+      return fail(WF_EINVAL, "wf_attn_tick: 8-bit keys need k_scale (4-byte aligned)");
+  }
   if (!d->q || !d->o || (!live_paged && (!d->k || !d->v)))
     return fail(WF_EINVAL, "wf_attn_tick: q, o (and k, v without live_pages) must be non-NULL");
   if (!aligned16(d->q) || !aligned16(d->o) ||
@@ -1045,6 +1209,9 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     p.store_row16 = int32_t(int64_t(d.H) * d.D * 2 / 16);
     p.n_store_blocks = store_fused ? (ppc + kNumXcd - 1) / kNumXcd * kNumXcd : 0;
     p.n_hist = d.n_hist;
+    const bool f8 = d.k_format == WF_K_E4M3;
+    p.k_scale = f8 ? d.k_scale : nullptr;
+    p.spp = f8 ? d.P / KT : 0;
     p.T = d.T;
     p.H = d.H;
     p.P = paged ? d.P : 16;
@@ -1076,7 +1243,9 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
       return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %d", p.n_page_ids,
                   kMaxPageIds);
     }
-    if (d.D == 128)
+    if (f8)  // (validated: D = 128, P a multiple of 64, so fast)
+      st = launch_attn<128, true, true>(p, unsigned(blocks), stream);
+    else if (d.D == 128)
       st = fast ? launch_attn<128, true>(p, unsigned(blocks), stream)
                 : launch_attn<128, false>(p, unsigned(blocks), stream);
     else

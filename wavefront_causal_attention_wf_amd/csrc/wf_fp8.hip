@@ -1,0 +1,148 @@
+// wf_store_paged_fp8: a producer's write of one chunk into the pages of the
+// 8-bit tier — keys as e4m3 codes with one fp32 scale per (64-token tile,
+// head), values copied as bf16.
+//
+// "Wave Forcing: Towards Speed-of-Light Streaming Video Generation", full text
+// §4.3 (K/V quantisation shrinks the K/V payload; an 8-bit attention backend
+// for local computation), Appendix C.5 Table 8 and C.6 (FP8 K/V): the pages
+// name the technique but not the format or the scale granularity. Here: e4m3
+// (largest finite value 448), scale = amax / 448 over the tile's keys of one
+// head, code = e4m3(x * (448 / amax)) rounded to nearest even, both divisions
+// and the product in fp32 (correctly rounded). A tile is 64 consecutive tokens
+// of one page (pages hold a multiple of 64 tokens), so the attention kernel's
+// 64-key tiles each carry one scale per head.
+//
+// Layout: K codes [num_pages][P][H][D] bytes, scales [num_pages][P/64][H]
+// fp32, V [num_pages][P][H][D] bf16; token t of the chunk goes to slot t % P of
+// page page_ids[t / P]. Slots past the chunk's last token hold zero codes (and
+// zero V), and a tile with no token of the chunk has scale 0.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "wf_internal.h"
+
+namespace wf {
+namespace {
+
+constexpr int kQThreads = 256;
+constexpr int kScaleTile = 64;
+constexpr float kE4m3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Four bf16 values (two words) times inv -> four e4m3 codes, first value in
+// the lowest byte.
+__device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, float inv) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w0) * inv, bf16_hi(w0) * inv, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w1) * inv, bf16_hi(w1) * inv, r, true);
+  return uint32_t(r);
+}
+
+// Block (x = 64-token tile in page order, y = head): the tile's keys of head
+// h -> codes and scale, and its values of head h copied. One thread owns UPT
+// 16-byte units (8 channels of one token), all loaded before any store.
+template <int D>
+__global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
+    const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint8_t* __restrict__ k_pool,
+    float* __restrict__ k_scale, uint4* __restrict__ v_pool, const int32_t* __restrict__ page_ids,
+    int32_t T, int32_t H, int32_t P) {
+  constexpr int UPR = D / 8;                             // 16-byte units per head row
+  constexpr int UPT = kScaleTile * UPR / kQThreads;      // units per thread
+  static_assert(UPT * kQThreads == kScaleTile * UPR, "tile must split evenly");
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y;
+  const int spp = P / kScaleTile;
+  const int pg = tile / spp;
+  const int sub = tile - pg * spp;
+  const int64_t pid = page_ids[pg];
+  const int tok0 = tile * kScaleTile;
+
+  uint4 kx[UPT], vx[UPT];
+  int64_t dst_row[UPT];
+  float am = 0.f;
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int e = threadIdx.x + u * kQThreads;
+    const int tok = e / UPR;
+    const int c = e - tok * UPR;
+    const int t = tok0 + tok;
+    const int64_t src = (int64_t(t) * H + h) * UPR + c;
+    kx[u] = t < T ? k_src[src] : make_uint4(0u, 0u, 0u, 0u);
+    vx[u] = t < T ? v_src[src] : make_uint4(0u, 0u, 0u, 0u);
+    dst_row[u] = ((pid * P + sub * kScaleTile + tok) * H + h) * UPR + c;  // in 16-byte units
+  }
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const uint32_t w[4] = {kx[u].x, kx[u].y, kx[u].z, kx[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) am = fmaxf(am, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  }
+  // block max: within each wave, then across the four waves
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  __shared__ float wave_max[kQThreads / 64];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = am;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kQThreads / 64; ++i) am = fmaxf(am, wave_max[i]);
+  const float inv = am > 0.f ? kE4m3Max / am : 0.f;
+  if (threadIdx.x == 0) k_scale[(pid * spp + sub) * H + h] = am / kE4m3Max;
+
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const v2u codes = {e4m3x4(kx[u].x, kx[u].y, inv), e4m3x4(kx[u].z, kx[u].w, inv)};
+    // unit (16 bytes of bf16) -> 8 bytes of codes at half the offset
+    __builtin_nontemporal_store(codes, reinterpret_cast<v2u*>(k_pool + dst_row[u] * 8));
+    store_stream16(v_pool + dst_row[u], vx[u]);
+  }
+}
+
+}  // namespace
+}  // namespace wf
+
+extern "C" wf_status wf_store_paged_fp8(const void* k_src, const void* v_src, void* k_pool,
+                                        float* k_scale, void* v_pool, const int32_t* page_ids,
+                                        int32_t T, int32_t H, int32_t D, int32_t num_pages,
+                                        int32_t P, hipStream_t stream) {
+  using namespace wf;
+  try {
+    const char* where = "wf_store_paged_fp8";
+    if (T < 0 || H <= 0 || num_pages <= 0 || P <= 0)
+      return fail(WF_EINVAL, "%s: bad sizes T=%d H=%d num_pages=%d P=%d", where, T, H, num_pages,
+                  P);
+    if (D != 64 && D != 128)
+      return fail(WF_EUNSUPPORTED, "%s: head dim D = %d (supported: 64, 128)", where, D);
+    if (P % kScaleTile != 0)
+      return fail(WF_EINVAL, "%s: page size P = %d must be a multiple of 64", where, P);
+    if (T == 0) return WF_OK;
+    if (!k_src || !v_src || !k_pool || !k_scale || !v_pool || !page_ids)
+      return fail(WF_EINVAL, "%s: NULL pointer", where);
+    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+      return fail(WF_EINVAL, "%s: tensors must be 16-byte aligned (scales 4-byte)", where);
+    const int64_t ppc = (int64_t(T) + P - 1) / P;
+    if (ppc > num_pages)
+      return fail(WF_EINVAL, "%s: chunk needs %lld pages, pool has %d", where,
+                  static_cast<long long>(ppc), num_pages);
+    if (H > 65535) return fail(WF_EUNSUPPORTED, "%s: H = %d exceeds 65535", where, H);
+    if (check_pages_enabled()) {
+      const int32_t st = check_device_pages(page_ids, ppc, num_pages, stream, where);
+      if (st != WF_OK) return st;
+    }
+    const dim3 grid(unsigned(ppc * (P / kScaleTile)), unsigned(H));
+    if (D == 128)
+      store_fp8_kernel<128><<<grid, kQThreads, 0, stream>>>(
+          static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
+          static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), page_ids, T, H, P);
+    else
+      store_fp8_kernel<64><<<grid, kQThreads, 0, stream>>>(
+          static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
+          static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), page_ids, T, H, P);
+    return check_launch(where);
+  } catch (...) {
+    return fail(WF_EINVAL, "wf_store_paged_fp8: internal error");
+  }
+}

@@ -49,7 +49,12 @@ class WfTickDesc(ctypes.Structure):
                 ("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp),
                 ("k_pool", _vp), ("v_pool", _vp), ("num_pages", _i32), ("P", _i32),
                 ("hist_pages", _vp), ("n_hist", _i32), ("hist_first", _i32 * MAX_STAGES),
-                ("live_pages", _vp), ("store_pages", _vp)]
+                ("live_pages", _vp), ("store_pages", _vp),
+                ("k_format", _i32), ("k_scale", _vp)]
+
+
+K_BF16 = 0
+K_E4M3 = 1
 
 
 class WfRopeDesc(ctypes.Structure):
@@ -73,19 +78,22 @@ _lib.wf_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
 _lib.wf_gather_paged.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
 _lib.wf_rope_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      ctypes.POINTER(WfRopeDesc), _vp]
+_lib.wf_store_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _vp]
 _lib.wf_attn_tick.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
 _lib.wf_tick_useful_flops.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_double)]
 for _f in ("wf_page_table_create", "wf_page_table_pages_per_chunk", "wf_page_table_alloc_chunk",
            "wf_page_table_commit", "wf_page_table_export", "wf_page_table_num_free",
-           "wf_store_paged", "wf_gather_paged", "wf_rope_store_paged", "wf_attn_tick",
-           "wf_tick_useful_flops"):
+           "wf_store_paged", "wf_gather_paged", "wf_rope_store_paged", "wf_store_paged_fp8",
+           "wf_attn_tick", "wf_tick_useful_flops"):
     getattr(_lib, _f).restype = _i32
 
 EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
                     "wf_page_table_destroy", "wf_page_table_pages_per_chunk",
                     "wf_page_table_alloc_chunk", "wf_page_table_commit", "wf_page_table_export",
                     "wf_page_table_num_free", "wf_store_paged", "wf_gather_paged",
-                    "wf_rope_store_paged", "wf_attn_tick", "wf_tick_useful_flops")
+                    "wf_rope_store_paged", "wf_store_paged_fp8", "wf_attn_tick",
+                    "wf_tick_useful_flops")
 
 
 def _check(status: int, where: str) -> None:
@@ -222,6 +230,24 @@ def wf_gather_paged(k_pool, v_pool, page_ids, k_dst, v_dst, stream=None) -> None
                                 _stream(stream)), "wf_gather_paged")
 
 
+def wf_store_paged_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=None) -> None:
+    """One chunk's K/V [T][H][D] (bf16) into the 8-bit tier's pages: K as e4m3
+    codes in k_pool (uint8 [num_pages][P][H][D]) with fp32 scales in k_scale
+    ([num_pages][P/64][H]), V copied into v_pool (bf16 [num_pages][P][H][D])."""
+    import torch
+    for n, t in (("k_src", k_src), ("v_src", v_src), ("v_pool", v_pool)):
+        _check_bf16(n, t)
+    if k_pool.dtype != torch.uint8 or not k_pool.is_contiguous():
+        raise TypeError("k_pool must be a contiguous uint8 tensor of e4m3 codes")
+    if k_scale.dtype != torch.float32 or not k_scale.is_contiguous():
+        raise TypeError("k_scale must be a contiguous float32 tensor")
+    T, H, D = k_src.shape
+    num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    _check(_lib.wf_store_paged_fp8(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(k_scale),
+                                   _ptr(v_pool), _ptr(page_ids), T, H, D, num_pages, P,
+                                   _stream(stream)), "wf_store_paged_fp8")
+
+
 def default_rope_split(D: int):
     """Channels per axis (frame, row, column): rows and columns 2*floor(D/6) each."""
     d_rc = 2 * (D // 6)
@@ -264,7 +290,7 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
                    q=None, k=None, v=None, o=None, k_pool=None, v_pool=None,
                    num_pages: int = 0, P: int = 0, hist_pages=None, n_hist: int = 0,
                    hist_first: Optional[Sequence[int]] = None,
-                   live_pages=None, store_pages=None) -> WfTickDesc:
+                   live_pages=None, store_pages=None, k_scale=None) -> WfTickDesc:
     d = WfTickDesc()
     d.S, d.active_mask, d.T, d.H, d.D, d.scale = S, active_mask, T, H, D, scale
     d.q, d.k, d.v, d.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
@@ -276,17 +302,21 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
         d.hist_first[i] = int(hf[i])
     d.live_pages = _ptr(live_pages)
     d.store_pages = _ptr(store_pages)
+    d.k_format = K_BF16 if k_scale is None else K_E4M3
+    d.k_scale = _ptr(k_scale)
     return d
 
 
 def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None, v_pool=None,
                  hist_pages=None, hist_first: Optional[Sequence[int]] = None,
-                 stream=None, live_pages=None, store_pages=None) -> None:
+                 stream=None, live_pages=None, store_pages=None, k_scale=None) -> None:
     """One tick: q, k, v, o [S+1][T][H][D]; pools [num_pages][P][H][D];
     hist_pages int32 [n_hist][ceil(T/P)] on the device; live_pages (optional)
     int32 [S+1][ceil(T/P)] on the device: live K/V read from those pages (k and
     v may then be None); store_pages (optional) int32 [ceil(T/P)] on the device:
-    the same launch writes the store chunk's K/V into those pages."""
+    the same launch writes the store chunk's K/V into those pages. k_scale
+    (optional, float32 [num_pages][P/64][H]): the 8-bit tier — k_pool holds
+    e4m3 codes (uint8) as written by wf_store_paged_fp8, live_pages required."""
     for n, t in (("q", q), ("o", o)) + ((("k", k), ("v", v)) if live_pages is None else ()):
         _check_bf16(n, t)
     _, T, H, D = q.shape
@@ -296,12 +326,15 @@ def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None
     pooled = n_hist > 0 or live_pages is not None or store_pages is not None
     if pooled:
         num_pages, P = k_pool.shape[0], k_pool.shape[1]
-        _check_bf16("k_pool", k_pool)
+        if k_scale is None:
+            _check_bf16("k_pool", k_pool)
+        elif str(k_pool.dtype) != "torch.uint8" or not k_pool.is_contiguous():
+            raise TypeError("with k_scale, k_pool must be a contiguous uint8 tensor of e4m3 codes")
         _check_bf16("v_pool", v_pool)
     d = make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
                        k_pool if pooled else None, v_pool if pooled else None, num_pages, P,
                        hist_pages if n_hist else None, n_hist, hist_first, live_pages,
-                       store_pages)
+                       store_pages, k_scale)
     _check(_lib.wf_attn_tick(ctypes.byref(d), _stream(stream)), "wf_attn_tick")
 
 
