@@ -77,7 +77,11 @@ constexpr int QROWS = 32 * NWAVES;  // query rows per workgroup
 constexpr float kLazyTau = 8.0f;    // raise the running max only beyond this (log2 units)
 constexpr float kLazyBound = 256.0f;  // 2^kLazyTau
 constexpr int kNumXcd = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kXcdTable = 512;      // max (stage, head) groups in the XCD table
+constexpr int kXcdTable = 256;      // max (stage, head) groups in the XCD group table
+// Packed work order (below): per XCD at most kPackSegs runs of query tiles and
+// kPackItems workgroups, each named by a 4-bit run index.
+constexpr int kPackSegs = 16;
+constexpr int kPackItems = 192;
 // History page table held in LDS (ids of all history pages of one tick) when
 // pages are not a multiple of 64 tokens; otherwise a table of tile sources.
 constexpr int kMaxPageIds = 4096;
@@ -110,13 +114,19 @@ struct AttnParams {
   int32_t ntq;            // query tiles per chunk
   int32_t items_per_stage;  // H * ntq
   int32_t n_page_ids;     // page ids staged in LDS (non-fast path): history, then live
-  // XCD-aware order: block b runs on XCD b % 8 (round-robin dispatch); its
-  // (b / 8)-th item is query tile (b / 8) % ntq of group xcd_groups[x][(b / 8) / ntq],
-  // group = rank * H + head. Blocks past an XCD's list exit at once.
+  // XCD-aware order: block b runs on XCD x = b % 8 (round-robin dispatch) as
+  // that XCD's item k = b / 8. use_xcd = 1: item k is query tile k % ntq of
+  // group xcd_groups[x][k / ntq] (group = rank * H + head). use_xcd = 2
+  // (packed): item k belongs to run r = the 4-bit code k of pack_code[x], and
+  // is the run's query tile pack_qt0[x][r] + (number of earlier items of run r);
+  // its group is pack_grp[x][r]. Blocks past an XCD's list exit at once.
   int32_t use_xcd;
   int32_t xcd_stride;
   int16_t xcd_n[kNumXcd];
   int16_t xcd_groups[kXcdTable];
+  int16_t pack_grp[kNumXcd][kPackSegs];
+  int16_t pack_qt0[kNumXcd][kPackSegs];
+  uint32_t pack_code[kNumXcd][kPackItems / 8];  // eight 4-bit run indices per word
   // (32-bit entries: the kernel reads them with scalar loads, which are
   // dword-granular; a narrower type would turn them into vector loads)
   int32_t stage_of_rank[WF_MAX_STAGES];  // work order, heaviest stage first
@@ -124,6 +134,9 @@ struct AttnParams {
   // per stage: segment code >= 0 is live slot j, < 0 is history chunk (-code - 1)
   int32_t seg[WF_MAX_STAGES][WF_MAX_SEGMENTS];
 };
+
+// passed by value as the kernel argument: keep it within 4 KB
+static_assert(sizeof(AttnParams) <= 4096, "kernel argument too large");
 
 __device__ __forceinline__ int swap_bits23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -509,7 +522,25 @@ attn_tick_kernel(const AttnParams p) {
   // ---- work item: heaviest stage first, then head, then query tile --------
   const int b = blockIdx.x - p.n_store_blocks;
   int rank, h, qt;
-  if (p.use_xcd) {
+  if (p.use_xcd == 2) {
+    const int x = b & (kNumXcd - 1);
+    const int k = b / kNumXcd;
+    if (k >= p.xcd_n[x]) return;  // whole block: this XCD's list is shorter
+    const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
+    // earlier items of the same run: zero nibbles of (codes XOR run * 0x11111111)
+    int before = 0;
+    const uint32_t rep8 = uint32_t(run) * 0x11111111u;
+    for (int w = 0; w <= (k >> 3); ++w) {
+      uint32_t y = p.pack_code[x][w] ^ rep8;
+      if (w == (k >> 3)) y |= ~((1u << (4 * (k & 7))) - 1u);  // only items before k
+      const uint32_t z = ~(((y & 0x77777777u) + 0x77777777u) | y | 0x77777777u);
+      before += __builtin_popcount(z);
+    }
+    const int grp = p.pack_grp[x][run];
+    qt = p.pack_qt0[x][run] + before;
+    rank = grp / p.H;
+    h = grp - rank * p.H;
+  } else if (p.use_xcd) {
     const int x = b & (kNumXcd - 1);
     const int k = b / kNumXcd;
     const int gi = k / p.ntq;
@@ -1053,6 +1084,167 @@ void plan_xcd_order(const StagePlan& pl, int H, AttnParams& p, int64_t& blocks) 
   blocks = int64_t(kNumXcd) * stride * p.ntq;
 }
 
+// Compute units per XCD of the current device (the packing below fills that
+// many bins per XCD); 0 if the runtime cannot say.
+int cus_per_xcd() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    v = n / kNumXcd;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Packed work order. One workgroup fills a CU, so each XCD runs its list of
+// workgroups like a machine shop with C machines taking jobs in list order;
+// the groups' workgroups differ in length (a stage's keys), and dealing whole
+// groups heaviest first leaves XCDs uneven and CUs idle at the end (an 8 %
+// loss on the 4-step tick in a list-scheduling model). Here:
+//  1. groups, heaviest first, are dealt to the least-loaded XCD, a group being
+//     split between XCDs when it would overshoot the even share (so a group's
+//     query tiles stay on one or two XCDs and share their L2);
+//  2. each XCD's workgroups are packed into C bins (longest first into the
+//     emptiest bin, then moves and swaps out of the fullest bin while they
+//     lower it);
+//  3. the list order is what makes CUs that free up pick their bin's next
+//     workgroup: all first workgroups of the bins, then the rest in the order
+//     their predecessors are modelled to finish.
+// Workgroup length is modelled as its key tiles plus a fixed start-up cost.
+// Falls back (returns false) when the tables would not hold the plan.
+bool plan_packed_order(const StagePlan& pl, int H, int tps, AttnParams& p, int64_t& blocks) {
+  const int C = cus_per_xcd();
+  if (C <= 0 || C > 64) return false;
+  const int ntq = p.ntq;
+  if (ntq > 32767) return false;
+  const int G = pl.n_active * H;
+  if (G > 32767) return false;
+  constexpr int kStartup = 2;  // start-up cost of a workgroup, in key tiles
+  auto weight = [&](int g) { return int(pl.nseg[pl.order[g / H]]) * tps + kStartup; };
+  int64_t total = 0;
+  for (int g = 0; g < G; ++g) total += int64_t(weight(g)) * ntq;
+  const double target = double(total) / kNumXcd;
+  struct Run { int grp, qt0, n; };
+  Run runs[kNumXcd][kPackSegs];
+  int nrun[kNumXcd] = {0};
+  int64_t load[kNumXcd] = {0};
+  for (int g = 0; g < G; ++g) {  // groups are in rank order: heaviest first
+    const int w = weight(g);
+    int rem = ntq, qt = 0;
+    while (rem > 0) {
+      int x = 0;
+      for (int i = 1; i < kNumXcd; ++i)
+        if (load[i] < load[x]) x = i;
+      const double room = target - double(load[x]);
+      int n = room <= 0 ? rem : std::min(rem, std::max(1, int(std::ceil(room / w))));
+      if (nrun[x] == kPackSegs) return false;
+      runs[x][nrun[x]++] = Run{g, qt, n};
+      load[x] += int64_t(n) * w;
+      rem -= n;
+      qt += n;
+    }
+  }
+  for (int x = 0; x < kNumXcd; ++x) {
+    int n_items = 0;
+    for (int r = 0; r < nrun[x]; ++r) n_items += runs[x][r].n;
+    if (n_items > kPackItems) return false;
+  }
+  for (int x = 0; x < kNumXcd; ++x) {
+    // items of this XCD: run index and length, longest first (runs already are)
+    int item_run[kPackItems], item_w[kPackItems];
+    int n = 0;
+    for (int r = 0; r < nrun[x]; ++r)
+      for (int i = 0; i < runs[x][r].n; ++i) {
+        item_run[n] = r;
+        item_w[n] = weight(runs[x][r].grp);
+        ++n;
+      }
+    // bins: item indices; longest first into the emptiest bin
+    std::vector<std::vector<int>> bin(C);
+    std::vector<int64_t> bl(C, 0);
+    for (int i = 0; i < n; ++i) {
+      int b = 0;
+      for (int j = 1; j < C; ++j)
+        if (bl[j] < bl[b]) b = j;
+      bin[b].push_back(i);
+      bl[b] += item_w[i];
+    }
+    // moves and swaps out of the fullest bin while they lower it
+    for (int iter = 0; iter < 4096; ++iter) {
+      int hi = 0;
+      for (int j = 1; j < C; ++j)
+        if (bl[j] > bl[hi]) hi = j;
+      bool done = false;
+      for (int lo = 0; lo < C && !done; ++lo) {
+        if (lo == hi) continue;
+        for (size_t ai = 0; ai < bin[hi].size() && !done; ++ai) {
+          const int a = bin[hi][ai];
+          if (bl[lo] + item_w[a] < bl[hi]) {  // move a
+            bin[hi].erase(bin[hi].begin() + ai);
+            bin[lo].push_back(a);
+            bl[hi] -= item_w[a];
+            bl[lo] += item_w[a];
+            done = true;
+            break;
+          }
+          for (size_t bi = 0; bi < bin[lo].size(); ++bi) {
+            const int c = bin[lo][bi];
+            const int d = item_w[a] - item_w[c];
+            if (d > 0 && bl[lo] + d < bl[hi]) {  // swap a and c
+              bin[hi][ai] = c;
+              bin[lo][bi] = a;
+              bl[hi] -= d;
+              bl[lo] += d;
+              done = true;
+              break;
+            }
+          }
+        }
+      }
+      if (!done) break;
+    }
+    for (int j = 0; j < C; ++j)  // longest first within a bin
+      std::sort(bin[j].begin(), bin[j].end(), [&](int a, int b) { return item_w[a] > item_w[b]; });
+    // list order: the bins' first items, then by modelled finish time
+    int order[kPackItems];
+    int no = 0;
+    std::vector<size_t> next(C, 1);
+    std::vector<int64_t> t(C, 0);
+    for (int j = 0; j < C; ++j)
+      if (!bin[j].empty()) {
+        order[no++] = bin[j][0];
+        t[j] = item_w[bin[j][0]];
+      }
+    for (;;) {
+      int best = -1;
+      for (int j = 0; j < C; ++j)
+        if (next[j] < bin[j].size() && (best < 0 || t[j] < t[best])) best = j;
+      if (best < 0) break;
+      const int it = bin[best][next[best]++];
+      order[no++] = it;
+      t[best] += item_w[it];
+    }
+    p.xcd_n[x] = int16_t(no);
+    for (int r = 0; r < kPackSegs; ++r) {
+      p.pack_grp[x][r] = int16_t(r < nrun[x] ? runs[x][r].grp : 0);
+      p.pack_qt0[x][r] = int16_t(r < nrun[x] ? runs[x][r].qt0 : 0);
+    }
+    for (int w = 0; w < kPackItems / 8; ++w) p.pack_code[x][w] = 0;
+    for (int k = 0; k < no; ++k)
+      p.pack_code[x][k >> 3] |= uint32_t(item_run[order[k]]) << (4 * (k & 7));
+  }
+  int stride = 0;
+  for (int x = 0; x < kNumXcd; ++x) stride = std::max(stride, int(p.xcd_n[x]));
+  p.use_xcd = 2;
+  blocks = int64_t(kNumXcd) * stride;
+  return true;
+}
+
 // kFast: every tile is one uniform span of a page or live chunk (page size a
 // multiple of 64, or no history); otherwise history tiles resolve per lane.
 template <int D, bool kFast, bool kF8 = false>
@@ -1229,7 +1421,7 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
       for (int i = 0; i < pl.nseg[s]; ++i) p.seg[s][i] = pl.seg[s][i];
     }
     int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
-    plan_xcd_order(pl, d.H, p, blocks);
+    if (!plan_packed_order(pl, d.H, p.tps, p, blocks)) plan_xcd_order(pl, d.H, p, blocks);
     blocks += p.n_store_blocks;  // a multiple of 8: the XCD of every attention block is kept
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
     const bool fast = !paged || d.P % KT == 0;
