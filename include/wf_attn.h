@@ -266,6 +266,22 @@ typedef struct wf_tick_desc {
 
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);
 
+/* Diagnostic, host only: the work order wf_attn_tick would launch for this
+ * descriptor. Attention block b (counted after the blocks that write the
+ * store's pages) computes query tile out[3b+2] (256 rows) of slot out[3b] and
+ * head out[3b+1], or exits at once when all three are -1; block b runs on XCD
+ * b % 8. cus_per_xcd: compute units per XCD to plan for (<= 0: the current
+ * device's). *n_blocks receives the block count; out (host int32, capacity
+ * elements, may be NULL to query the count) must hold 3 * n_blocks.
+ * The plan ([summary] Methodology 3: stage s reads N_s keys, so workgroups
+ * differ in length): (slot, head) groups, heaviest first, are dealt to the
+ * least-loaded XCD (split between XCDs to even the loads), then each XCD's
+ * workgroups are packed onto its CUs and listed in the order a freed CU
+ * should take them. Errors as wf_attn_tick's validation; WF_EINVAL for a
+ * short out or a NULL n_blocks. */
+wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_per_xcd, int32_t* out,
+                             int64_t capacity, int64_t* n_blocks);
+
 /* Useful FLOPs of one call with this descriptor: 4*D*H per visible
  * (query, key) pair (Q.K^T plus P.V), exponentials not counted. Host only. */
 wf_status wf_tick_useful_flops(const wf_tick_desc* desc, double* out);

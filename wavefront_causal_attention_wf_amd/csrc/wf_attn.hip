@@ -1117,8 +1117,8 @@ int cus_per_xcd() {
 //     their predecessors are modelled to finish.
 // Workgroup length is modelled as its key tiles plus a fixed start-up cost.
 // Falls back (returns false) when the tables would not hold the plan.
-bool plan_packed_order(const StagePlan& pl, int H, int tps, AttnParams& p, int64_t& blocks) {
-  const int C = cus_per_xcd();
+bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, AttnParams& p,
+                       int64_t& blocks) {
   if (C <= 0 || C > 64) return false;
   const int ntq = p.ntq;
   if (ntq > 32767) return false;
@@ -1333,8 +1333,79 @@ int32_t validate_tick(const wf_tick_desc* d) {
   return WF_OK;
 }
 
+// The work item of attention block b (counted after the store blocks), as the
+// kernel decodes it from the plan: false if the block exits at once.
+bool decode_block(const AttnParams& p, int b, int& rank, int& h, int& qt) {
+  if (p.use_xcd == 2) {
+    const int x = b & (kNumXcd - 1);
+    const int k = b / kNumXcd;
+    if (k >= p.xcd_n[x]) return false;
+    const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
+    int before = 0;
+    for (int i = 0; i < k; ++i) before += ((p.pack_code[x][i >> 3] >> (4 * (i & 7))) & 15) == run;
+    const int grp = p.pack_grp[x][run];
+    qt = p.pack_qt0[x][run] + before;
+    rank = grp / p.H;
+    h = grp - rank * p.H;
+  } else if (p.use_xcd) {
+    const int x = b & (kNumXcd - 1);
+    const int k = b / kNumXcd;
+    const int gi = k / p.ntq;
+    if (gi >= p.xcd_n[x]) return false;
+    const int grp = p.xcd_groups[x * p.xcd_stride + gi];
+    qt = k - gi * p.ntq;
+    rank = grp / p.H;
+    h = grp - rank * p.H;
+  } else {
+    rank = b / p.items_per_stage;
+    const int rem = b - rank * p.items_per_stage;
+    h = rem / p.ntq;
+    qt = rem - h * p.ntq;
+  }
+  return true;
+}
+
 }  // namespace
 }  // namespace wf
+
+extern "C" wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_per_xcd_hint,
+                                        int32_t* out, int64_t capacity, int64_t* n_blocks) {
+  using namespace wf;
+  try {
+    if (!n_blocks) return fail(WF_EINVAL, "wf_tick_work_order: n_blocks is NULL");
+    int32_t st = validate_tick(desc);
+    if (st != WF_OK) return st;
+    const wf_tick_desc& d = *desc;
+    *n_blocks = 0;
+    if (d.T == 0 || d.active_mask == 0) return WF_OK;
+    StagePlan pl;
+    plan_stages(d, pl);
+    AttnParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.H = d.H;
+    p.tps = (d.T + KT - 1) / KT;
+    p.ntq = (d.T + QROWS - 1) / QROWS;
+    p.items_per_stage = d.H * p.ntq;
+    int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
+    const int C = cus_per_xcd_hint > 0 ? cus_per_xcd_hint : cus_per_xcd();
+    if (!plan_packed_order(pl, d.H, p.tps, C, p, blocks)) plan_xcd_order(pl, d.H, p, blocks);
+    *n_blocks = blocks;
+    if (!out) return WF_OK;
+    if (capacity < 3 * blocks)
+      return fail(WF_EINVAL, "wf_tick_work_order: capacity %lld < 3 * %lld blocks",
+                  static_cast<long long>(capacity), static_cast<long long>(blocks));
+    for (int64_t b = 0; b < blocks; ++b) {
+      int rank = 0, h = 0, qt = 0;
+      const bool live = decode_block(p, int(b), rank, h, qt);
+      out[3 * b] = live ? pl.order[rank] : -1;
+      out[3 * b + 1] = live ? h : -1;
+      out[3 * b + 2] = live ? qt : -1;
+    }
+    return WF_OK;
+  } catch (...) {
+    return fail(WF_EINVAL, "wf_tick_work_order: internal error");
+  }
+}
 
 extern "C" wf_status wf_tick_useful_flops(const wf_tick_desc* desc, double* out) {
   using namespace wf;
@@ -1421,7 +1492,8 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
       for (int i = 0; i < pl.nseg[s]; ++i) p.seg[s][i] = pl.seg[s][i];
     }
     int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
-    if (!plan_packed_order(pl, d.H, p.tps, p, blocks)) plan_xcd_order(pl, d.H, p, blocks);
+    if (!plan_packed_order(pl, d.H, p.tps, cus_per_xcd(), p, blocks))
+      plan_xcd_order(pl, d.H, p, blocks);
     blocks += p.n_store_blocks;  // a multiple of 8: the XCD of every attention block is kept
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
     const bool fast = !paged || d.P % KT == 0;

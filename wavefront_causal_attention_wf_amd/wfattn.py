@@ -82,10 +82,12 @@ _lib.wf_store_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i
                                     _vp]
 _lib.wf_attn_tick.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
 _lib.wf_tick_useful_flops.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_double)]
+_lib.wf_tick_work_order.argtypes = [ctypes.POINTER(WfTickDesc), _i32, _i32p, ctypes.c_int64,
+                                    ctypes.POINTER(ctypes.c_int64)]
 for _f in ("wf_page_table_create", "wf_page_table_pages_per_chunk", "wf_page_table_alloc_chunk",
            "wf_page_table_commit", "wf_page_table_export", "wf_page_table_num_free",
            "wf_store_paged", "wf_gather_paged", "wf_rope_store_paged", "wf_store_paged_fp8",
-           "wf_attn_tick", "wf_tick_useful_flops"):
+           "wf_attn_tick", "wf_tick_useful_flops", "wf_tick_work_order"):
     getattr(_lib, _f).restype = _i32
 
 EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
@@ -93,7 +95,7 @@ EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
                     "wf_page_table_alloc_chunk", "wf_page_table_commit", "wf_page_table_export",
                     "wf_page_table_num_free", "wf_store_paged", "wf_gather_paged",
                     "wf_rope_store_paged", "wf_store_paged_fp8", "wf_attn_tick",
-                    "wf_tick_useful_flops")
+                    "wf_tick_useful_flops", "wf_tick_work_order")
 
 
 def _check(status: int, where: str) -> None:
@@ -361,3 +363,15 @@ def tick_useful_flops_desc(desc: WfTickDesc) -> float:
     _check(_lib.wf_tick_useful_flops(ctypes.byref(desc), ctypes.byref(out)),
            "wf_tick_useful_flops")
     return out.value
+
+
+def tick_work_order(desc: WfTickDesc, cus_per_xcd: int = 0) -> np.ndarray:
+    """Host-only plan of wf_attn_tick: int32 [n_blocks][3] = (slot, head, query
+    tile) per attention block in launch order, -1 rows for blocks that exit."""
+    n = ctypes.c_int64()
+    _check(_lib.wf_tick_work_order(ctypes.byref(desc), cus_per_xcd, None, 0, ctypes.byref(n)),
+           "wf_tick_work_order")
+    out = np.empty(3 * n.value, np.int32)
+    _check(_lib.wf_tick_work_order(ctypes.byref(desc), cus_per_xcd, out.ctypes.data_as(_i32p),
+                                   out.size, ctypes.byref(n)), "wf_tick_work_order")
+    return out.reshape(n.value, 3)
