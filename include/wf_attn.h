@@ -267,20 +267,22 @@ typedef struct wf_tick_desc {
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);
 
 /* Diagnostic, host only: the work order wf_attn_tick would launch for this
- * descriptor. Attention block b (counted after the blocks that write the
- * store's pages) computes query tile out[3b+2] (256 rows) of slot out[3b] and
- * head out[3b+1], or exits at once when all three are -1; block b runs on XCD
- * b % 8. cus_per_xcd: compute units per XCD to plan for (<= 0: the current
- * device's). *n_blocks receives the block count; out (host int32, capacity
- * elements, may be NULL to query the count) must hold 3 * n_blocks.
- * The plan ([summary] Methodology 3: stage s reads N_s keys, so workgroups
+ * descriptor. Row i = out[4i .. 4i+3] = (block, slot, head, query tile): the
+ * attention block (counted after the blocks that write the store's pages)
+ * that computes query tile (256 rows) of that slot and head, rows of one block
+ * in the order it runs them; block b runs on XCD b % 8. cus_per_xcd: compute
+ * units per XCD to plan for (<= 0: the current device's). *n_items receives
+ * the row count; out (host int32, capacity elements, may be NULL to query the
+ * count) must hold 4 * n_items.
+ * The plan ([summary] Methodology 3: stage s reads N_s keys, so work items
  * differ in length): (slot, head) groups, heaviest first, are dealt to the
- * least-loaded XCD (split between XCDs to even the loads), then each XCD's
- * workgroups are packed onto its CUs and listed in the order a freed CU
- * should take them. Errors as wf_attn_tick's validation; WF_EINVAL for a
- * short out or a NULL n_blocks. */
+ * least-loaded XCD (split between two XCDs to even the loads), and each XCD's
+ * items are packed onto its CUs, one block per CU running its list, longest
+ * first. Ticks whose plan does not fit the kernel's tables run one item per
+ * block instead, whole groups per XCD. Errors as wf_attn_tick's validation;
+ * WF_EINVAL for a short out or a NULL n_items. */
 wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_per_xcd, int32_t* out,
-                             int64_t capacity, int64_t* n_blocks);
+                             int64_t capacity, int64_t* n_items);
 
 /* Useful FLOPs of one call with this descriptor: 4*D*H per visible
  * (query, key) pair (Q.K^T plus P.V), exponentials not counted. Host only. */

@@ -44,35 +44,35 @@ CASES = [
 @pytest.mark.parametrize("cus", [32, 0])
 def test_every_tile_once(name, S, mask, T, H, n_hist, hf, cus):
     order = wf.tick_work_order(desc(S, mask, T, H, n_hist, hf), cus)
-    live = order[order[:, 0] >= 0]
-    assert np.all(order[order[:, 0] < 0] == -1)
     ntq = -(-T // 256)
     want = {(s, h, q) for s in range(S + 1) if (mask >> s) & 1 for h in range(H)
             for q in range(ntq)}
-    got = [tuple(int(v) for v in r) for r in live]
+    got = [tuple(int(v) for v in r[1:]) for r in order]
     assert len(got) == len(set(got)), "a tile is computed twice"
     assert set(got) == want
-    assert len(order) % 8 == 0 or len(order) == len(want)
+    assert np.all(np.diff(order[:, 0]) >= 0)  # rows grouped by block, launch order
 
 
 def makespan(order, S, mask, n_hist, hf, T, cus):
-    """List scheduling per XCD (block b on XCD b % 8), workgroup length = key tiles."""
+    """Modelled CU efficiency (block b on XCD b % 8, item length = key tiles):
+    one block per CU running its list (packed order), or one item per block
+    taken by the XCD's next free CU in launch order."""
     tps = -(-T // 64)
-    worst, total = 0, 0
-    for x in range(8):
-        items = order[x::8]
-        t = [0] * cus
-        heapq.heapify(t)
-        for s, h, q in items:
-            if s < 0:
-                continue
-            w = keys_of(S, mask, n_hist, hf, s) * tps
-            total += w
-            heapq.heappush(t, heapq.heappop(t) + w)
-        worst = max(worst, max(t))
+    w = lambda s: keys_of(S, mask, n_hist, hf, s) * tps
+    total = sum(w(s) for _, s, _, _ in order)
+    blocks = order[:, 0]
+    worst = 0
+    if len(np.unique(blocks)) < len(blocks):       # lists per block
+        for blk in np.unique(blocks):
+            worst = max(worst, sum(w(s) for _, s, _, _ in order[blocks == blk]))
+    else:
+        for x in range(8):
+            t = [0] * cus
+            heapq.heapify(t)
+            for _, s, _, _ in order[blocks % 8 == x]:
+                heapq.heappush(t, heapq.heappop(t) + w(s))
+            worst = max(worst, max(t))
     return total / (8 * cus * worst)
-
-
 # lowest modelled efficiency accepted: the fill tick's workgroups are 1-3 key
 # chunks long and an XCD has 5.3 chunks of work per CU, so 6 is the best
 # makespan (89 %)
@@ -90,7 +90,7 @@ def test_packed_order_keeps_cus_busy(name, S, mask, T, H, n_hist, hf):
     assert eff >= eff_groups
     # XCD loads within 2 % of each other
     tps = -(-T // 64)
-    loads = [sum(keys_of(S, mask, n_hist, hf, s) * tps for s, h, q in packed[x::8] if s >= 0)
+    loads = [sum(keys_of(S, mask, n_hist, hf, s) * tps for _, s, _, _ in packed[packed[:, 0] % 8 == x])
              for x in range(8)]
     assert max(loads) <= 1.02 * min(loads), loads
 
@@ -102,5 +102,5 @@ def test_work_order_errors():
     st = wf.library().wf_tick_work_order(__import__("ctypes").byref(d), 32,
                                          out.ctypes.data_as(wf._i32p), out.size,
                                          __import__("ctypes").byref(n))
-    assert st == -1 and n.value > 2  # capacity too small, count still reported
+    assert st == -1  # capacity too small
     assert wf.library().wf_tick_work_order(__import__("ctypes").byref(d), 32, None, 0, None) == -1

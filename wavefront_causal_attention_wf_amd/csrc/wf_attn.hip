@@ -82,6 +82,7 @@ constexpr int kXcdTable = 256;      // max (stage, head) groups in the XCD group
 // kPackItems workgroups, each named by a 4-bit run index.
 constexpr int kPackSegs = 16;
 constexpr int kPackItems = 192;
+constexpr int kPackBins = 40;  // CUs per XCD the packed order can fill
 // History page table held in LDS (ids of all history pages of one tick) when
 // pages are not a multiple of 64 tokens; otherwise a table of tile sources.
 constexpr int kMaxPageIds = 4096;
@@ -114,18 +115,21 @@ struct AttnParams {
   int32_t ntq;            // query tiles per chunk
   int32_t items_per_stage;  // H * ntq
   int32_t n_page_ids;     // page ids staged in LDS (non-fast path): history, then live
-  // XCD-aware order: block b runs on XCD x = b % 8 (round-robin dispatch) as
-  // that XCD's item k = b / 8. use_xcd = 1: item k is query tile k % ntq of
-  // group xcd_groups[x][k / ntq] (group = rank * H + head). use_xcd = 2
-  // (packed): item k belongs to run r = the 4-bit code k of pack_code[x], and
-  // is the run's query tile pack_qt0[x][r] + (number of earlier items of run r);
-  // its group is pack_grp[x][r]. Blocks past an XCD's list exit at once.
+  // Work order; block b runs on XCD x = b % 8 (round-robin dispatch).
+  // use_xcd = 1: block b is that XCD's item k = b / 8, query tile k % ntq of
+  // group xcd_groups[x][k / ntq] (group = rank * H + head); blocks past an
+  // XCD's list exit at once. use_xcd = 2 (packed, one block per CU): block b
+  // runs items pack_bin[x][c] .. pack_bin[x][c + 1] - 1 of XCD x's list, c =
+  // b / 8; item i belongs to run r = the 4-bit code i of pack_code[x] and is
+  // the run's query tile pack_qt0[x][r] + (number of earlier items of run r in
+  // the list); its group is pack_grp[x][r].
   int32_t use_xcd;
   int32_t xcd_stride;
   int16_t xcd_n[kNumXcd];
   int16_t xcd_groups[kXcdTable];
   int16_t pack_grp[kNumXcd][kPackSegs];
   int16_t pack_qt0[kNumXcd][kPackSegs];
+  int16_t pack_bin[kNumXcd][kPackBins + 1];
   uint32_t pack_code[kNumXcd][kPackItems / 8];  // eight 4-bit run indices per word
   // (32-bit entries: the kernel reads them with scalar loads, which are
   // dword-granular; a narrower type would turn them into vector loads)
@@ -508,514 +512,528 @@ attn_tick_kernel(const AttnParams p) {
   // all-zero tile has zero codes, so any finite multiplier gives its scores)
   __shared__ float tile_scale[kF8 ? kMaxTiles : 1];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 31;
-  const int g = lane >> 5;
-
   // ---- the store chunk's page copy (leading blocks, optional) --------------
   if (int(blockIdx.x) < p.n_store_blocks) {
     store_page_block(p, p.store_slot);
     return;
   }
-  // ---- work item: heaviest stage first, then head, then query tile --------
+  // ---- work items: one per block, or (packed order) a CU's list -----------
   const int b = blockIdx.x - p.n_store_blocks;
-  int rank, h, qt;
+  int item = 0, item_end = 1;
   if (p.use_xcd == 2) {
-    const int x = b & (kNumXcd - 1);
-    const int k = b / kNumXcd;
-    if (k >= p.xcd_n[x]) return;  // whole block: this XCD's list is shorter
-    const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
-    // earlier items of the same run: zero nibbles of (codes XOR run * 0x11111111)
-    int before = 0;
-    const uint32_t rep8 = uint32_t(run) * 0x11111111u;
-    for (int w = 0; w <= (k >> 3); ++w) {
-      uint32_t y = p.pack_code[x][w] ^ rep8;
-      if (w == (k >> 3)) y |= ~((1u << (4 * (k & 7))) - 1u);  // only items before k
-      const uint32_t z = ~(((y & 0x77777777u) + 0x77777777u) | y | 0x77777777u);
-      before += __builtin_popcount(z);
-    }
-    const int grp = p.pack_grp[x][run];
-    qt = p.pack_qt0[x][run] + before;
-    rank = grp / p.H;
-    h = grp - rank * p.H;
-  } else if (p.use_xcd) {
-    const int x = b & (kNumXcd - 1);
-    const int k = b / kNumXcd;
-    const int gi = k / p.ntq;
-    if (gi >= p.xcd_n[x]) return;  // whole block: this XCD's list is shorter
-    const int grp = p.xcd_groups[x * p.xcd_stride + gi];
-    qt = k - gi * p.ntq;
-    rank = grp / p.H;
-    h = grp - rank * p.H;
-  } else {
-    rank = b / p.items_per_stage;
-    const int rem = b - rank * p.items_per_stage;
-    h = rem / p.ntq;
-    qt = rem - h * p.ntq;
+    const int c = b / kNumXcd;
+    item = p.pack_bin[b & (kNumXcd - 1)][c];
+    item_end = p.pack_bin[b & (kNumXcd - 1)][c + 1];
+    if (item >= item_end) return;  // an empty bin
   }
-  const int s = p.stage_of_rank[rank];
-  const int nseg = p.nseg[s];
-  const int T = p.T;
-  const int ntiles = nseg * p.tps;
-
-  const Uniforms u = load_uniforms<D, KB>(p, h);
-  if constexpr (kFast) {
-    // sources of every tile of this (stage, head), one thread per tile
-    for (int t = tid; t < ntiles; t += NTHREADS) {
-      const int sg = t / u.tps;
-      const int mm = t - sg * u.tps;
-      const int code = p.seg[s][sg];
-      const uint32_t t0 = uint32_t(KT) * uint32_t(mm);
-      uint64_t kr, vr;
-      if (code >= 0 && !p.live_pages) {  // live chunk `code`, contiguous
-        const uint64_t e = (uint64_t(code) * uint32_t(u.T) + t0) * u.row_bytes;
-        kr = reinterpret_cast<uint64_t>(u.k + e);
-        vr = reinterpret_cast<uint64_t>(u.v + e);
-      } else {  // history chunk or paged live chunk: rows t0 % P .. of one page
-        const int32_t* ids = code >= 0 ? p.live_pages + code * u.ppc
-                                       : p.hist_pages + (-code - 1) * u.ppc;
-        const uint32_t pg = t0 / uint32_t(u.P);
-        const int pid = ids[int(pg)];
-        const uint32_t off = t0 - pg * uint32_t(u.P);
-        const uint64_t prow = uint64_t(uint32_t(pid)) * uint32_t(u.P) + off;
-        kr = reinterpret_cast<uint64_t>(u.k_pool + prow * u.krow_bytes);
-        vr = reinterpret_cast<uint64_t>(u.v_pool + prow * u.row_bytes);
-        if constexpr (kF8) {
-          const float ks =
-              p.k_scale[(int64_t(pid) * p.spp + int(off / uint32_t(KT))) * u.H + h];
-          tile_scale[t] = ks > 0.f ? ks : 1.f;
-        }
+  for (;;) {
+    // Thread coordinates, opaque per item so that nothing derived from them
+    // (per-lane offsets and bases, a few dozen registers) is hoisted out of
+    // the item loop and kept live, or spilled, across it.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31;
+    const int g = lane >> 5;
+    int rank, h, qt;
+    if (p.use_xcd == 2) {
+      const int x = b & (kNumXcd - 1);
+      const int k = item;
+      const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
+      // earlier items of the same run: zero nibbles of (codes XOR run * 0x11111111)
+      int before = 0;
+      const uint32_t rep8 = uint32_t(run) * 0x11111111u;
+      for (int w = 0; w <= (k >> 3); ++w) {
+        uint32_t y = p.pack_code[x][w] ^ rep8;
+        if (w == (k >> 3)) y |= ~((1u << (4 * (k & 7))) - 1u);  // only items before k
+        const uint32_t z = ~(((y & 0x77777777u) + 0x77777777u) | y | 0x77777777u);
+        before += __builtin_popcount(z);
       }
-      kr |= (mm == u.tps - 1) ? 1u : 0u;  // bases are 16-byte aligned: bit 0 is free
-      tile_tab[t] = make_uint4(uint32_t(kr), uint32_t(kr >> 32), uint32_t(vr), uint32_t(vr >> 32));
-    }
-  } else {  // page ids into LDS: history chunks, then (paged) live slots
-    const int nh = p.n_hist * p.ppc;
-    for (int i = tid; i < p.n_page_ids; i += NTHREADS)
-      pages_lds[i] = i < nh ? p.hist_pages[i] : p.live_pages[i - nh];
-  }
-  __syncthreads();
-
-  const int q0w = qt * QROWS + wave * 32;  // first query row of this wave
-  const bool wave_active = q0w < T;
-  const int qrow = q0w + r;
-
-  // ---- Q^T operand: lane holds query qrow, head dims 16*ks + 8*g .. +7 -----
-  // (8-bit tier: head dims 64*dh + 32*g .. +31 of MFMA dh, as e4m3 codes)
-  bf16x8 qf[kF8 ? 1 : KS];
-  i32x8 qf8[2];
-  float cq = u.c;  // multiplier of this lane's raw scores (8-bit: times its query scale)
-  if constexpr (kF8) {
-    const uint4* qp = reinterpret_cast<const uint4*>(p.q + ((int64_t(s) * T + qrow) * p.H + h) * D);
-    uint4 raw[2][4];
-    float am = 0.f;
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        raw[dh][c] = (qrow < T) ? qp[8 * dh + 4 * g + c] : make_uint4(0u, 0u, 0u, 0u);
-        const uint32_t w[4] = {raw[dh][c].x, raw[dh][c].y, raw[dh][c].z, raw[dh][c].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          am = fmaxf(am, fmaxf(fabsf(__uint_as_float(w[i] << 16)),
-                               fabsf(__uint_as_float(w[i] & 0xffff0000u))));
-      }
-    // the row's amax (lanes l and l + 32 hold the two halves of one row), its
-    // scale amax / 448 and the codes of q * (448 / amax), as the keys' producer
-    am = xlane32_max(am);
-    const float inv = am > 0.f ? 448.0f / am : 0.f;
-    const float qscale = am / 448.0f;
-    cq = qscale > 0.f ? u.c * qscale : u.c;  // zero row: zero codes, any multiplier
-#pragma unroll
-    for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t w[4] = {raw[dh][c].x, raw[dh][c].y, raw[dh][c].z, raw[dh][c].w};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const uint32_t a = w[2 * half], b = w[2 * half + 1];
-          int r4 = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(a << 16) * inv,
-                                                   __uint_as_float(a & 0xffff0000u) * inv, 0,
-                                                   false);
-          r4 = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(b << 16) * inv,
-                                               __uint_as_float(b & 0xffff0000u) * inv, r4, true);
-          qf8[dh][2 * c + half] = r4;
-        }
-      }
-  } else {
-    const uint4* qp = reinterpret_cast<const uint4*>(p.q + ((int64_t(s) * T + qrow) * p.H + h) * D);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 u = (qrow < T) ? qp[2 * ks + g] : make_uint4(0u, 0u, 0u, 0u);
-      qf[ks] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-
-  // per-lane LDS read offsets (elements)
-  const int krow0 = swap_bits23(r);   // K row feeding MFMA row r of block 0 (+32: block 1)
-  const int kx = kswz<D>(krow0);      // same swizzle for row + 32
-  const int a16 = lane & 15;          // lane within its 16-lane group (transposed V reads)
-  const int vrow = 8 * g + (a16 >> 2);
-  const int vx = vswz<D>(vrow);
-  const int vcx = 2 * ((lane >> 4) & 1) + ((a16 >> 1) & 1);
-  const int vsub = 4 * (a16 & 1);
-  // The same reads as LDS byte addresses. Rows are 2*D bytes and the swizzles
-  // act on the 16-byte chunk index only (address bits 4..7 within a row), so
-  // the address of K step kk is this lane's base XOR (kk << 5), and that of V
-  // output block db is the base XOR (db << 6); buffer, 32-row block, 16-key
-  // step and row half are constant offsets. One base per tensor then serves
-  // every operand read (addresses formed from it inside each MFMA slot rather
-  // than dozens of precomputed address registers).
-  constexpr uint32_t TILE_BYTES = KT * D * 2;      // one V (and bf16 K) tile
-  constexpr uint32_t KTILE_BYTES = KT * D * KB;   // one K tile
-  // 8-bit keys: rows of D bytes, 16-byte chunk 4*dh + 2*g + piece of MFMA dh
-  // (the two pieces of one 32-byte operand), swizzled by kswz8; as for bf16 the
-  // address of (dh, piece) is the base XOR ((4*dh + piece) << 4).
-  // (byte offsets into the tile arrays; reads are formed from the arrays
-  // themselves so that the compiler knows which LDS objects they touch)
-  const uint32_t k_lane = kF8 ? uint32_t(krow0 * D + (((2 * g) ^ kswz8(krow0)) << 4))
-                              : uint32_t(krow0 * D * 2 + ((g ^ kx) << 4));
-  const uint32_t v_lane = uint32_t(vrow * D * 2 + ((vcx ^ vx) << 4) + vsub * 2);
-  const char* const k_bytes = reinterpret_cast<const char*>(k_tiles);
-  const char* const v_bytes = reinterpret_cast<const char*>(v_tiles);
-
-  Loader ld;
-  ld.init(u, wave, lane);
-  auto resolve = [&]() __attribute__((always_inline)) {
-    if constexpr (kFast) ld.prepare_table(tile_tab, ntiles);
-    else ld.prepare(p, u, pages_lds, s, nseg);
-  };
-  if constexpr (kFast) ld.start_table(tile_tab);
-  resolve();
-#pragma unroll
-  for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds0, v_lds0, wave);
-  resolve();
-#pragma unroll
-  for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds1, v_lds1, wave);
-  resolve();
-  const bool grp_a = wave < NWAVES / 2;
-  if (!grp_a) {  // B: tile 2 as well (A issues it in its first softmax slot)
-#pragma unroll
-    for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds2, v_lds2, wave);
-    resolve();
-  }
-  // tile 0 has landed (A: tile 1 may still be in flight; B: tiles 1 and 2)
-  if (grp_a) tile_barrier<LPT>();
-  else tile_barrier<2 * LPT>();
-
-  // Keys of tile j that are real: 64, the chunk's remainder on a segment's last
-  // tile, 0 past the end (the loop runs in groups of four tiles).
-  auto valid_keys = [&](int j) __attribute__((always_inline)) {
-    if (j >= ntiles) return 0;
-    const int m = j - (j / u.tps) * u.tps;
-    return m == u.tps - 1 ? u.t_last : KT;
-  };
-
-  f32x16 sacc[2];
-  bf16x8 pb[4];
-  float ks_next = 1.f;  // 8-bit tier: key scale of the tile whose scores are in sacc
-
-  // 8-bit K operand op = 2*dh + blk of K tile buffer kbuf: rows of 32-key block
-  // blk, head dims 64*dh + 32*g .. +31 (two 16-byte reads).
-  auto kload8 = [&](uint32_t kl, int kbuf, int op) __attribute__((always_inline)) {
-    const uint32_t a = (kl ^ uint32_t((4 * (op >> 1)) << 4)) + kbuf * KTILE_BYTES +
-                       (op & 1) * (32 * D);
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(k_bytes + a);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(k_bytes + (a ^ 16u));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  auto mfma8 = [&](const i32x8& a, const i32x8& b, const f32x16& c)
-                   __attribute__((always_inline)) {
-    // formats 0, 0: both operands e4m3; unit block scales
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-  };
-
-  // S^T = K Q^T for one tile (the first one, before the slot pairs start): two
-  // 32-key blocks, K operands two k-steps ahead.
-  auto qk = [&](int kbuf) __attribute__((always_inline)) {
-    uint32_t kl = k_lane;
-    asm volatile("" : "+v"(kl));
-    if constexpr (kF8) {
-      ks_next = tile_scale[0];
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
-      i32x8 ka[4];
-#pragma unroll
-      for (int op = 0; op < 4; ++op) ka[op] = kload8(kl, kbuf, op);
-#pragma unroll
-      for (int op = 0; op < 4; ++op) sacc[op & 1] = mfma8(ka[op], qf8[op >> 1], sacc[op & 1]);
+      const int grp = p.pack_grp[x][run];
+      qt = p.pack_qt0[x][run] + before;
+      rank = grp / p.H;
+      h = grp - rank * p.H;
+    } else if (p.use_xcd) {
+      const int x = b & (kNumXcd - 1);
+      const int k = b / kNumXcd;
+      const int gi = k / p.ntq;
+      if (gi >= p.xcd_n[x]) return;  // whole block: this XCD's list is shorter
+      const int grp = p.xcd_groups[x * p.xcd_stride + gi];
+      qt = k - gi * p.ntq;
+      rank = grp / p.H;
+      h = grp - rank * p.H;
     } else {
-      auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
-        const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
+      rank = b / p.items_per_stage;
+      const int rem = b - rank * p.items_per_stage;
+      h = rem / p.ntq;
+      qt = rem - h * p.ntq;
+    }
+    const int s = p.stage_of_rank[rank];
+    const int nseg = p.nseg[s];
+    const int T = p.T;
+    const int ntiles = nseg * p.tps;
+
+    const Uniforms u = load_uniforms<D, KB>(p, h);
+    if constexpr (kFast) {
+      // sources of every tile of this (stage, head), one thread per tile
+      for (int t = tid; t < ntiles; t += NTHREADS) {
+        const int sg = t / u.tps;
+        const int mm = t - sg * u.tps;
+        const int code = p.seg[s][sg];
+        const uint32_t t0 = uint32_t(KT) * uint32_t(mm);
+        uint64_t kr, vr;
+        if (code >= 0 && !p.live_pages) {  // live chunk `code`, contiguous
+          const uint64_t e = (uint64_t(code) * uint32_t(u.T) + t0) * u.row_bytes;
+          kr = reinterpret_cast<uint64_t>(u.k + e);
+          vr = reinterpret_cast<uint64_t>(u.v + e);
+        } else {  // history chunk or paged live chunk: rows t0 % P .. of one page
+          const int32_t* ids = code >= 0 ? p.live_pages + code * u.ppc
+                                         : p.hist_pages + (-code - 1) * u.ppc;
+          const uint32_t pg = t0 / uint32_t(u.P);
+          const int pid = ids[int(pg)];
+          const uint32_t off = t0 - pg * uint32_t(u.P);
+          const uint64_t prow = uint64_t(uint32_t(pid)) * uint32_t(u.P) + off;
+          kr = reinterpret_cast<uint64_t>(u.k_pool + prow * u.krow_bytes);
+          vr = reinterpret_cast<uint64_t>(u.v_pool + prow * u.row_bytes);
+          if constexpr (kF8) {
+            const float ks =
+                p.k_scale[(int64_t(pid) * p.spp + int(off / uint32_t(KT))) * u.H + h];
+            tile_scale[t] = ks > 0.f ? ks : 1.f;
+          }
+        }
+        kr |= (mm == u.tps - 1) ? 1u : 0u;  // bases are 16-byte aligned: bit 0 is free
+        tile_tab[t] = make_uint4(uint32_t(kr), uint32_t(kr >> 32), uint32_t(vr), uint32_t(vr >> 32));
+      }
+    } else {  // page ids into LDS: history chunks, then (paged) live slots
+      const int nh = p.n_hist * p.ppc;
+      for (int i = tid; i < p.n_page_ids; i += NTHREADS)
+        pages_lds[i] = i < nh ? p.hist_pages[i] : p.live_pages[i - nh];
+    }
+    __syncthreads();
+
+    const int q0w = qt * QROWS + wave * 32;  // first query row of this wave
+    const bool wave_active = q0w < T;
+    const int qrow = q0w + r;
+
+    // ---- Q^T operand: lane holds query qrow, head dims 16*ks + 8*g .. +7 -----
+    // (8-bit tier: head dims 64*dh + 32*g .. +31 of MFMA dh, as e4m3 codes)
+    bf16x8 qf[kF8 ? 1 : KS];
+    i32x8 qf8[2];
+    float cq = u.c;  // multiplier of this lane's raw scores (8-bit: times its query scale)
+    if constexpr (kF8) {
+      const uint4* qp = reinterpret_cast<const uint4*>(p.q + ((int64_t(s) * T + qrow) * p.H + h) * D);
+      uint4 raw[2][4];
+      float am = 0.f;
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-          dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
-      };
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
-      bf16x8 ka[3][2];
-      kload(0, ka[0]);
-      kload(1, ka[1]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
+        for (int c = 0; c < 4; ++c) {
+          raw[dh][c] = (qrow < T) ? qp[8 * dh + 4 * g + c] : make_uint4(0u, 0u, 0u, 0u);
+          const uint32_t w[4] = {raw[dh][c].x, raw[dh][c].y, raw[dh][c].z, raw[dh][c].w};
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
-                                                              0, 0, 0);
-        if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < 4; ++i)
+            am = fmaxf(am, fmaxf(fabsf(__uint_as_float(w[i] << 16)),
+                                 fabsf(__uint_as_float(w[i] & 0xffff0000u))));
+        }
+      // the row's amax (lanes l and l + 32 hold the two halves of one row), its
+      // scale amax / 448 and the codes of q * (448 / amax), as the keys' producer
+      am = xlane32_max(am);
+      const float inv = am > 0.f ? 448.0f / am : 0.f;
+      const float qscale = am / 448.0f;
+      cq = qscale > 0.f ? u.c * qscale : u.c;  // zero row: zero codes, any multiplier
+#pragma unroll
+      for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t w[4] = {raw[dh][c].x, raw[dh][c].y, raw[dh][c].z, raw[dh][c].w};
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const uint32_t a = w[2 * half], b = w[2 * half + 1];
+            int r4 = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(a << 16) * inv,
+                                                     __uint_as_float(a & 0xffff0000u) * inv, 0,
+                                                     false);
+            r4 = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(b << 16) * inv,
+                                                 __uint_as_float(b & 0xffff0000u) * inv, r4, true);
+            qf8[dh][2 * c + half] = r4;
+          }
+        }
+    } else {
+      const uint4* qp = reinterpret_cast<const uint4*>(p.q + ((int64_t(s) * T + qrow) * p.H + h) * D);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 u = (qrow < T) ? qp[2 * ks + g] : make_uint4(0u, 0u, 0u, 0u);
+        qf[ks] = __builtin_bit_cast(bf16x8, u);
       }
     }
-  };
 
-  // Online softmax of the scores of tile j (exp2 domain): P as bf16 into pb.
-  // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
-  // ce: the scores' multiplier (softmax scale * log2 e, times the query and
-  // key scales in the 8-bit tier).
-  auto softmax = [&](int j, float ce) __attribute__((always_inline)) {
-    const int valid = valid_keys(j);
-    if (valid < KT) {
+    f32x16 oacc[DB];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int key = 32 * blk + 16 * (x >> 3) + 8 * g + (x & 7);
-          if (key >= valid) sacc[blk][x] = -INFINITY;
-        }
-    }
-    // P = 2^(c s - m_run) (bf16 for the P.V product) and this lane's fp32 sum
-    float lsum;
-    auto exps = [&]() __attribute__((always_inline)) {
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const float ev = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], ce, -m_run));
-          part[x & 3] += ev;
-          pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(ev);
-        }
-      lsum = (part[0] + part[1]) + (part[2] + part[3]);
+    for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    // per-lane LDS read offsets (elements)
+    const int krow0 = swap_bits23(r);   // K row feeding MFMA row r of block 0 (+32: block 1)
+    const int kx = kswz<D>(krow0);      // same swizzle for row + 32
+    const int a16 = lane & 15;          // lane within its 16-lane group (transposed V reads)
+    const int vrow = 8 * g + (a16 >> 2);
+    const int vx = vswz<D>(vrow);
+    const int vcx = 2 * ((lane >> 4) & 1) + ((a16 >> 1) & 1);
+    const int vsub = 4 * (a16 & 1);
+    // The same reads as LDS byte addresses. Rows are 2*D bytes and the swizzles
+    // act on the 16-byte chunk index only (address bits 4..7 within a row), so
+    // the address of K step kk is this lane's base XOR (kk << 5), and that of V
+    // output block db is the base XOR (db << 6); buffer, 32-row block, 16-key
+    // step and row half are constant offsets. One base per tensor then serves
+    // every operand read (addresses formed from it inside each MFMA slot rather
+    // than dozens of precomputed address registers).
+    constexpr uint32_t TILE_BYTES = KT * D * 2;      // one V (and bf16 K) tile
+    constexpr uint32_t KTILE_BYTES = KT * D * KB;   // one K tile
+    // 8-bit keys: rows of D bytes, 16-byte chunk 4*dh + 2*g + piece of MFMA dh
+    // (the two pieces of one 32-byte operand), swizzled by kswz8; as for bf16 the
+    // address of (dh, piece) is the base XOR ((4*dh + piece) << 4).
+    // (byte offsets into the tile arrays; reads are formed from the arrays
+    // themselves so that the compiler knows which LDS objects they touch)
+    const uint32_t k_lane = kF8 ? uint32_t(krow0 * D + (((2 * g) ^ kswz8(krow0)) << 4))
+                                : uint32_t(krow0 * D * 2 + ((g ^ kx) << 4));
+    const uint32_t v_lane = uint32_t(vrow * D * 2 + ((vcx ^ vx) << 4) + vsub * 2);
+    const char* const k_bytes = reinterpret_cast<const char*>(k_tiles);
+    const char* const v_bytes = reinterpret_cast<const char*>(v_tiles);
+
+    Loader ld;
+    ld.init(u, wave, lane);
+    auto resolve = [&]() __attribute__((always_inline)) {
+      if constexpr (kFast) ld.prepare_table(tile_tab, ntiles);
+      else ld.prepare(p, u, pages_lds, s, nseg);
     };
-    exps();
-    // The running reference is raised only when the tile's max exceeds it by
-    // more than kLazyTau (log2 units). No P can then exceed 2^kLazyTau, and as
-    // P >= 0 a sum at or below 2^kLazyTau on both lanes of every query rules
-    // that out without computing the max (the first tile, against -inf, always
-    // takes the check).
-    if (__builtin_amdgcn_ballot_w64(!(lsum <= kLazyBound)) != 0) {
-      float mx = sacc[0][0];
+    if constexpr (kFast) ld.start_table(tile_tab);
+    resolve();
 #pragma unroll
-      for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
+    for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds0, v_lds0, wave);
+    resolve();
 #pragma unroll
-      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
-      mx = xlane32_max(mx) * ce;
-      const bool raise = mx > m_run + kLazyTau;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = raise ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+    for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds1, v_lds1, wave);
+    resolve();
+    const bool grp_a = wave < NWAVES / 2;
+    if (!grp_a) {  // B: tile 2 as well (A issues it in its first softmax slot)
 #pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) oacc[i][x] *= alpha;
-        exps();
-      }
+      for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds2, v_lds2, wave);
+      resolve();
     }
-    l_run += lsum;
-  };
-
-  // V^T operands of 16-key step kk of V tile buffer vbuf: two transposed LDS
-  // reads per 32-row block of O^T (vl: this lane's V base).
-  auto vload = [&](uint32_t vl, int vbuf, int kk, bf16x8* dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint32_t a = (vl ^ uint32_t(db << 6)) + vbuf * TILE_BYTES + kk * (16 * D * 2);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_bytes + a));
-      const i16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_bytes + (a + 4 * D * 2)));
-      dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  };
-
-  // V^T operands of the next MFMA slot's first 16-key step, read at the end of
-  // the softmax slot before it (that tile landed a slot earlier), so the MFMA
-  // slot starts on them while its first K operands are still in flight.
-  bf16x8 vpre[DB];
-  // G(j): O^T += V^T P^T of tile j and S^T = K Q^T of tile j+1, interleaved
-  // MFMA by MFMA so that consecutive MFMAs never share an accumulator (the
-  // score blocks recur every fourth MFMA, the output blocks every eighth). Each
-  // k-step first issues the operand reads of a later step (K two k-steps
-  // ahead, V one 16-key step = two k-steps ahead), then runs its P.V MFMAs,
-  // then its Q.K^T MFMAs.
-  auto gphase = [&](int vbuf, int kbuf, int jn) __attribute__((always_inline)) {
-    // the lane bases, opaque here so that the read addresses are formed from
-    // them inside the slot instead of being kept in registers across the loop
-    uint32_t kl = k_lane, vl = v_lane;
-    asm volatile("" : "+v"(kl), "+v"(vl));
-    if constexpr (kF8) {
-      // four 16-key P.V steps (four MFMAs each), each followed by one of the
-      // four 8-bit Q.K^T MFMAs (blocks alternate, so no two in a row share an
-      // accumulator); K operands two steps ahead, V one
-      ks_next = tile_scale[jn < ntiles ? jn : 0];
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
-      i32x8 ka[3];
-      bf16x8 va[2][DB];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
-      ka[0] = kload8(kl, kbuf, 0);
-      ka[1] = kload8(kl, kbuf, 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t + 2 < 4) ka[(t + 2) % 3] = kload8(kl, kbuf, t + 2);
-        if (t + 1 < 4) vload(vl, vbuf, t + 1, va[(t + 1) & 1]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t & 1][db], pb[t], oacc[db], 0, 0,
-                                                             0);
-        sacc[t & 1] = mfma8(ka[t % 3], qf8[t >> 1], sacc[t & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
-        const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-          dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
-      };
-      constexpr int PV_PER_STEP = 4 * DB / KS;  // P.V MFMAs per Q.K^T k-step
-      sacc[0] = f32x16{};  // the previous scores were consumed by the last softmax
-      sacc[1] = f32x16{};
-      bf16x8 ka[3][2];
-      bf16x8 va[2][DB];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
-      kload(0, ka[0]);
-      kload(1, ka[1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        // P.V MFMAs number PV_PER_STEP*t .. : 16-key step kk, output blocks db
-        const int pv0 = PV_PER_STEP * t;
-        const int kk = pv0 / DB;
-        // operands of later steps go out before this step's MFMAs
-        if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
-        if (pv0 % DB == 0 && kk + 1 < 4) vload(vl, vbuf, kk + 1, va[(kk + 1) & 1]);
-#pragma unroll
-        for (int e = 0; e < PV_PER_STEP; ++e) {
-          const int db = (pv0 + e) % DB;
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0, 0,
-                                                             0);
-        }
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-          sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], sacc[blk], 0,
-                                                              0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-
-  // Ping-pong: waves 0..3 (group A) and 4..7 (group B) share the four SIMDs
-  // one to one and run the same sequence one slot apart, so that while one
-  // wave of a SIMD runs MFMAs (G(j): P.V of tile j, then Q.K^T of tile j+1,
-  // interleaved) the other runs the VALU softmax S of its current tile:
-  //   slot 0: A: Q.K^T(0)      B: Q.K^T(0) (early; no data dependence)
-  //   slot 1: A: S(0)          B:   "
-  //   slot 2: A: G(0)          B: S(0)
-  //   slot 3: A: S(1)          B: G(0)      ...
-  // A block-wide barrier ends every odd slot (A's softmax slots, B's MFMA
-  // slots); within the two slots between barriers each SIMD's waves run one
-  // softmax and one MFMA phase each, in opposite order, so they still overlap.
-  // Tile t lives in buffer t % 4; all its rows must have landed by the barrier
-  // that ends slot 2t-1, and it is last read in slot 2t+3. Each wave issues
-  // its loads at the start of its softmax slot: A those of tile j+2 in S(j)
-  // (slot 2j+1), B those of tile j+3 in S(j) (slot 2j+2); A loads tiles 0-1
-  // and B tiles 0-2 up front. A buffer is refilled (slot 2t-3 or 2t-4 for tile
-  // t) only after the barrier that ends the last slot reading its previous
-  // tile t-4 (slot 2t-5). So at each barrier a wave may leave the loads of its
-  // newest tile in flight (LPT) and every older load has landed.
-  auto end_qk_slot = [&]() __attribute__((always_inline)) {
-    if (!grp_a) tile_barrier<LPT>();
-  };
-  auto end_s_slot = [&]() __attribute__((always_inline)) {
+    // tile 0 has landed (A: tile 1 may still be in flight; B: tiles 1 and 2)
     if (grp_a) tile_barrier<LPT>();
-  };
-  // The softmax slot of tile js: this wave's loads of its next tile go out
-  // first (into kn, vn), then the softmax, then the first V^T operands of the
-  // next MFMA slot (from tile buffer vnext).
-  auto s_slot = [&](int js, uint16_t* kn, uint16_t* vn, int vnext) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
-    resolve();  // the tile this wave loads next
-    __builtin_amdgcn_sched_barrier(0);
-    if (wave_active) {
-      softmax(js, kF8 ? cq * ks_next : cq);
-      __builtin_amdgcn_sched_barrier(0);
-      uint32_t vl = v_lane;
-      asm volatile("" : "+v"(vl));
-      vload(vl, vnext, 0, vpre);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    end_s_slot();
-  };
+    else tile_barrier<2 * LPT>();
 
-  if (wave_active) qk(0);
-  end_qk_slot();  // B (end of slot 1): tile 1 has landed (tile 2 may be in flight)
-  // S(0): A loads tile 2, B tile 3; G(0) reads V of tile 0
-  s_slot(0, grp_a ? k_lds2 : k_lds3, grp_a ? v_lds2 : v_lds3, 0);
+    // Keys of tile j that are real: 64, the chunk's remainder on a segment's last
+    // tile, 0 past the end (the loop runs in groups of four tiles).
+    auto valid_keys = [&](int j) __attribute__((always_inline)) {
+      if (j >= ntiles) return 0;
+      const int m = j - (j / u.tps) * u.tps;
+      return m == u.tps - 1 ? u.t_last : KT;
+    };
 
-  // G(j) then S(j+1); buffers vbuf, kbuf: V of tile j and K of tile j+1 (tile
-  // t is in buffer t % 4); (ka_, va_) / (kb_, vb_): where A's / B's loads of
-  // S(j+1) go (A: tile j+3, B: tile j+4).
-  auto slot_pair = [&](int j, int vbuf, int kbuf, uint16_t* ka_, uint16_t* va_, uint16_t* kb_,
-                       uint16_t* vb_) __attribute__((always_inline)) {
-    if (wave_active) {
-      // the MFMA phase wins issue arbitration over the other wave's softmax
-      __builtin_amdgcn_s_setprio(1);
-      gphase(vbuf, kbuf, j + 1);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    end_qk_slot();
-    s_slot(j + 1, grp_a ? ka_ : kb_, grp_a ? va_ : vb_, (vbuf + 1) & 3);
-  };
+    f32x16 sacc[2];
+    bf16x8 pb[4];
+    float ks_next = 1.f;  // 8-bit tier: key scale of the tile whose scores are in sacc
 
-  for (int j = 0; j < ntiles; j += 4) {
-    slot_pair(j, 0, 1, k_lds3, v_lds3, k_lds0, v_lds0);
-    slot_pair(j + 1, 1, 2, k_lds0, v_lds0, k_lds1, v_lds1);
-    slot_pair(j + 2, 2, 3, k_lds1, v_lds1, k_lds2, v_lds2);
-    slot_pair(j + 3, 3, 0, k_lds2, v_lds2, k_lds3, v_lds3);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
+    // 8-bit K operand op = 2*dh + blk of K tile buffer kbuf: rows of 32-key block
+    // blk, head dims 64*dh + 32*g .. +31 (two 16-byte reads).
+    auto kload8 = [&](uint32_t kl, int kbuf, int op) __attribute__((always_inline)) {
+      const uint32_t a = (kl ^ uint32_t((4 * (op >> 1)) << 4)) + kbuf * KTILE_BYTES +
+                         (op & 1) * (32 * D);
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(k_bytes + a);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(k_bytes + (a ^ 16u));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto mfma8 = [&](const i32x8& a, const i32x8& b, const f32x16& c)
+                     __attribute__((always_inline)) {
+      // formats 0, 0: both operands e4m3; unit block scales
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    };
 
-  // ---- epilogue: O = O^T / l, bf16 ----------------------------------------
-  if (wave_active && qrow < T) {
-    const float inv = 1.0f / xlane32_sum(l_run);
-    uint16_t* op = p.o + ((int64_t(s) * T + qrow) * p.H + h) * D;
+    // S^T = K Q^T for one tile (the first one, before the slot pairs start): two
+    // 32-key blocks, K operands two k-steps ahead.
+    auto qk = [&](int kbuf) __attribute__((always_inline)) {
+      uint32_t kl = k_lane;
+      asm volatile("" : "+v"(kl));
+      if constexpr (kF8) {
+        ks_next = tile_scale[0];
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+        i32x8 ka[4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int op = 0; op < 4; ++op) ka[op] = kload8(kl, kbuf, op);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * db + 8 * i + 4 * g;
-        bf16x4 v4;
+        for (int op = 0; op < 4; ++op) sacc[op & 1] = mfma8(ka[op], qf8[op >> 1], sacc[op & 1]);
+      } else {
+        auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+          const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(oacc[db][4 * i + j] * inv);
-        *reinterpret_cast<uint2*>(op + d) = __builtin_bit_cast(uint2, v4);
+          for (int blk = 0; blk < 2; ++blk)
+            dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
+        };
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+        bf16x8 ka[3][2];
+        kload(0, ka[0]);
+        kload(1, ka[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+            sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3][blk], qf[kk], sacc[blk],
+                                                                0, 0, 0);
+          if (kk + 2 < KS) kload(kk + 2, ka[(kk + 2) % 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+    };
+
+    // Online softmax of the scores of tile j (exp2 domain): P as bf16 into pb.
+    // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
+    // ce: the scores' multiplier (softmax scale * log2 e, times the query and
+    // key scales in the 8-bit tier).
+    auto softmax = [&](int j, float ce) __attribute__((always_inline)) {
+      const int valid = valid_keys(j);
+      if (valid < KT) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int key = 32 * blk + 16 * (x >> 3) + 8 * g + (x & 7);
+            if (key >= valid) sacc[blk][x] = -INFINITY;
+          }
+      }
+      // P = 2^(c s - m_run) (bf16 for the P.V product) and this lane's fp32 sum
+      float lsum;
+      auto exps = [&]() __attribute__((always_inline)) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const float ev = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], ce, -m_run));
+            part[x & 3] += ev;
+            pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(ev);
+          }
+        lsum = (part[0] + part[1]) + (part[2] + part[3]);
+      };
+      exps();
+      // The running reference is raised only when the tile's max exceeds it by
+      // more than kLazyTau (log2 units). No P can then exceed 2^kLazyTau, and as
+      // P >= 0 a sum at or below 2^kLazyTau on both lanes of every query rules
+      // that out without computing the max (the first tile, against -inf, always
+      // takes the check).
+      if (__builtin_amdgcn_ballot_w64(!(lsum <= kLazyBound)) != 0) {
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
+#pragma unroll
+        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
+        mx = xlane32_max(mx) * ce;
+        const bool raise = mx > m_run + kLazyTau;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+          const float m_new = raise ? mx : m_run;
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) oacc[i][x] *= alpha;
+          exps();
+        }
+      }
+      l_run += lsum;
+    };
+
+    // V^T operands of 16-key step kk of V tile buffer vbuf: two transposed LDS
+    // reads per 32-row block of O^T (vl: this lane's V base).
+    auto vload = [&](uint32_t vl, int vbuf, int kk, bf16x8* dst) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint32_t a = (vl ^ uint32_t(db << 6)) + vbuf * TILE_BYTES + kk * (16 * D * 2);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_bytes + a));
+        const i16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_bytes + (a + 4 * D * 2)));
+        dst[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+
+    // V^T operands of the next MFMA slot's first 16-key step, read at the end of
+    // the softmax slot before it (that tile landed a slot earlier), so the MFMA
+    // slot starts on them while its first K operands are still in flight.
+    bf16x8 vpre[DB];
+    // G(j): O^T += V^T P^T of tile j and S^T = K Q^T of tile j+1, interleaved
+    // MFMA by MFMA so that consecutive MFMAs never share an accumulator (the
+    // score blocks recur every fourth MFMA, the output blocks every eighth). Each
+    // k-step first issues the operand reads of a later step (K two k-steps
+    // ahead, V one 16-key step = two k-steps ahead), then runs its P.V MFMAs,
+    // then its Q.K^T MFMAs.
+    auto gphase = [&](int vbuf, int kbuf, int jn) __attribute__((always_inline)) {
+      // the lane bases, opaque here so that the read addresses are formed from
+      // them inside the slot instead of being kept in registers across the loop
+      uint32_t kl = k_lane, vl = v_lane;
+      asm volatile("" : "+v"(kl), "+v"(vl));
+      if constexpr (kF8) {
+        // four 16-key P.V steps (four MFMAs each), each followed by one of the
+        // four 8-bit Q.K^T MFMAs (blocks alternate, so no two in a row share an
+        // accumulator); K operands two steps ahead, V one
+        ks_next = tile_scale[jn < ntiles ? jn : 0];
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+        i32x8 ka[3];
+        bf16x8 va[2][DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
+        ka[0] = kload8(kl, kbuf, 0);
+        ka[1] = kload8(kl, kbuf, 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t + 2 < 4) ka[(t + 2) % 3] = kload8(kl, kbuf, t + 2);
+          if (t + 1 < 4) vload(vl, vbuf, t + 1, va[(t + 1) & 1]);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t & 1][db], pb[t], oacc[db], 0, 0,
+                                                               0);
+          sacc[t & 1] = mfma8(ka[t % 3], qf8[t >> 1], sacc[t & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        auto kload = [&](int kk, bf16x8* dst) __attribute__((always_inline)) {
+          const uint32_t a = (kl ^ uint32_t(kk << 5)) + kbuf * TILE_BYTES;
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+            dst[blk] = *reinterpret_cast<const bf16x8*>(k_bytes + (a + blk * (32 * D * 2)));
+        };
+        constexpr int PV_PER_STEP = 4 * DB / KS;  // P.V MFMAs per Q.K^T k-step
+        sacc[0] = f32x16{};  // the previous scores were consumed by the last softmax
+        sacc[1] = f32x16{};
+        bf16x8 ka[3][2];
+        bf16x8 va[2][DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
+        kload(0, ka[0]);
+        kload(1, ka[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          // P.V MFMAs number PV_PER_STEP*t .. : 16-key step kk, output blocks db
+          const int pv0 = PV_PER_STEP * t;
+          const int kk = pv0 / DB;
+          // operands of later steps go out before this step's MFMAs
+          if (t + 2 < KS) kload(t + 2, ka[(t + 2) % 3]);
+          if (pv0 % DB == 0 && kk + 1 < 4) vload(vl, vbuf, kk + 1, va[(kk + 1) & 1]);
+#pragma unroll
+          for (int e = 0; e < PV_PER_STEP; ++e) {
+            const int db = (pv0 + e) % DB;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk & 1][db], pb[kk], oacc[db], 0, 0,
+                                                               0);
+          }
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+            sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3][blk], qf[t], sacc[blk], 0,
+                                                                0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+
+    // Ping-pong: waves 0..3 (group A) and 4..7 (group B) share the four SIMDs
+    // one to one and run the same sequence one slot apart, so that while one
+    // wave of a SIMD runs MFMAs (G(j): P.V of tile j, then Q.K^T of tile j+1,
+    // interleaved) the other runs the VALU softmax S of its current tile:
+    //   slot 0: A: Q.K^T(0)      B: Q.K^T(0) (early; no data dependence)
+    //   slot 1: A: S(0)          B:   "
+    //   slot 2: A: G(0)          B: S(0)
+    //   slot 3: A: S(1)          B: G(0)      ...
+    // A block-wide barrier ends every odd slot (A's softmax slots, B's MFMA
+    // slots); within the two slots between barriers each SIMD's waves run one
+    // softmax and one MFMA phase each, in opposite order, so they still overlap.
+    // Tile t lives in buffer t % 4; all its rows must have landed by the barrier
+    // that ends slot 2t-1, and it is last read in slot 2t+3. Each wave issues
+    // its loads at the start of its softmax slot: A those of tile j+2 in S(j)
+    // (slot 2j+1), B those of tile j+3 in S(j) (slot 2j+2); A loads tiles 0-1
+    // and B tiles 0-2 up front. A buffer is refilled (slot 2t-3 or 2t-4 for tile
+    // t) only after the barrier that ends the last slot reading its previous
+    // tile t-4 (slot 2t-5). So at each barrier a wave may leave the loads of its
+    // newest tile in flight (LPT) and every older load has landed.
+    auto end_qk_slot = [&]() __attribute__((always_inline)) {
+      if (!grp_a) tile_barrier<LPT>();
+    };
+    auto end_s_slot = [&]() __attribute__((always_inline)) {
+      if (grp_a) tile_barrier<LPT>();
+    };
+    // The softmax slot of tile js: this wave's loads of its next tile go out
+    // first (into kn, vn), then the softmax, then the first V^T operands of the
+    // next MFMA slot (from tile buffer vnext).
+    auto s_slot = [&](int js, uint16_t* kn, uint16_t* vn, int vnext) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
+      resolve();  // the tile this wave loads next
+      __builtin_amdgcn_sched_barrier(0);
+      if (wave_active) {
+        softmax(js, kF8 ? cq * ks_next : cq);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t vl = v_lane;
+        asm volatile("" : "+v"(vl));
+        vload(vl, vnext, 0, vpre);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      end_s_slot();
+    };
+
+    if (wave_active) qk(0);
+    end_qk_slot();  // B (end of slot 1): tile 1 has landed (tile 2 may be in flight)
+    // S(0): A loads tile 2, B tile 3; G(0) reads V of tile 0
+    s_slot(0, grp_a ? k_lds2 : k_lds3, grp_a ? v_lds2 : v_lds3, 0);
+
+    // G(j) then S(j+1); buffers vbuf, kbuf: V of tile j and K of tile j+1 (tile
+    // t is in buffer t % 4); (ka_, va_) / (kb_, vb_): where A's / B's loads of
+    // S(j+1) go (A: tile j+3, B: tile j+4).
+    auto slot_pair = [&](int j, int vbuf, int kbuf, uint16_t* ka_, uint16_t* va_, uint16_t* kb_,
+                         uint16_t* vb_) __attribute__((always_inline)) {
+      if (wave_active) {
+        // the MFMA phase wins issue arbitration over the other wave's softmax
+        __builtin_amdgcn_s_setprio(1);
+        gphase(vbuf, kbuf, j + 1);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      end_qk_slot();
+      s_slot(j + 1, grp_a ? ka_ : kb_, grp_a ? va_ : vb_, (vbuf + 1) & 3);
+    };
+
+    for (int j = 0; j < ntiles; j += 4) {
+      slot_pair(j, 0, 1, k_lds3, v_lds3, k_lds0, v_lds0);
+      slot_pair(j + 1, 1, 2, k_lds0, v_lds0, k_lds1, v_lds1);
+      slot_pair(j + 2, 2, 3, k_lds1, v_lds1, k_lds2, v_lds2);
+      slot_pair(j + 3, 3, 0, k_lds2, v_lds2, k_lds3, v_lds3);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
+
+    // ---- epilogue: O = O^T / l, bf16 ----------------------------------------
+    if (wave_active && qrow < T) {
+      const float inv = 1.0f / xlane32_sum(l_run);
+      uint16_t* op = p.o + ((int64_t(s) * T + qrow) * p.H + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 32 * db + 8 * i + 4 * g;
+          bf16x4 v4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(oacc[db][4 * i + j] * inv);
+          *reinterpret_cast<uint2*>(op + d) = __builtin_bit_cast(uint2, v4);
+        }
+    }
+    if (++item >= item_end) break;
+    // the next item rewrites the tile-source table and the tile buffers
+    __syncthreads();
   }
 }
 
@@ -1101,25 +1119,25 @@ int cus_per_xcd() {
   return v;
 }
 
-// Packed work order. One workgroup fills a CU, so each XCD runs its list of
-// workgroups like a machine shop with C machines taking jobs in list order;
-// the groups' workgroups differ in length (a stage's keys), and dealing whole
-// groups heaviest first leaves XCDs uneven and CUs idle at the end (an 8 %
-// loss on the 4-step tick in a list-scheduling model). Here:
+// Packed work order. One workgroup fills a CU, and work items differ in
+// length (a stage's keys). Launching one block per item and letting the
+// hardware hand them out leaves CUs idle: the dispatcher deals blocks to the
+// XCDs strictly in turn, so a CU that frees up waits until the turn reaches
+// its XCD (measured: 23 us between a CU's blocks on average), and dealing
+// whole groups heaviest first leaves XCDs uneven and CUs idle at the end (7 %
+// of the 4-step tick). Here every CU gets one block that runs a list of items
+// planned on the host:
 //  1. groups, heaviest first, are dealt to the least-loaded XCD, a group being
 //     split between XCDs when it would overshoot the even share (so a group's
 //     query tiles stay on one or two XCDs and share their L2);
-//  2. each XCD's workgroups are packed into C bins (longest first into the
-//     emptiest bin, then moves and swaps out of the fullest bin while they
-//     lower it);
-//  3. the list order is what makes CUs that free up pick their bin's next
-//     workgroup: all first workgroups of the bins, then the rest in the order
-//     their predecessors are modelled to finish.
-// Workgroup length is modelled as its key tiles plus a fixed start-up cost.
+//  2. each XCD's items are packed into C bins, one per CU (longest first into
+//     the emptiest bin, then moves and swaps out of the fullest bin while
+//     they lower it); a block runs its bin, longest item first.
+// An item's length is modelled as its key tiles plus a fixed start-up cost.
 // Falls back (returns false) when the tables would not hold the plan.
 bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, AttnParams& p,
                        int64_t& blocks) {
-  if (C <= 0 || C > 64) return false;
+  if (C <= 0 || C > kPackBins) return false;
   const int ntq = p.ntq;
   if (ntq > 32767) return false;
   const int G = pl.n_active * H;
@@ -1208,27 +1226,15 @@ bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, AttnParams& p
       }
       if (!done) break;
     }
-    for (int j = 0; j < C; ++j)  // longest first within a bin
-      std::sort(bin[j].begin(), bin[j].end(), [&](int a, int b) { return item_w[a] > item_w[b]; });
-    // list order: the bins' first items, then by modelled finish time
+    // the XCD's list: bin by bin, longest first within a bin
     int order[kPackItems];
     int no = 0;
-    std::vector<size_t> next(C, 1);
-    std::vector<int64_t> t(C, 0);
-    for (int j = 0; j < C; ++j)
-      if (!bin[j].empty()) {
-        order[no++] = bin[j][0];
-        t[j] = item_w[bin[j][0]];
-      }
-    for (;;) {
-      int best = -1;
-      for (int j = 0; j < C; ++j)
-        if (next[j] < bin[j].size() && (best < 0 || t[j] < t[best])) best = j;
-      if (best < 0) break;
-      const int it = bin[best][next[best]++];
-      order[no++] = it;
-      t[best] += item_w[it];
+    for (int j = 0; j < C; ++j) {
+      std::sort(bin[j].begin(), bin[j].end(), [&](int a, int b) { return item_w[a] > item_w[b]; });
+      p.pack_bin[x][j] = int16_t(no);
+      for (int it : bin[j]) order[no++] = it;
     }
+    p.pack_bin[x][C] = int16_t(no);
     p.xcd_n[x] = int16_t(no);
     for (int r = 0; r < kPackSegs; ++r) {
       p.pack_grp[x][r] = int16_t(r < nrun[x] ? runs[x][r].grp : 0);
@@ -1238,10 +1244,8 @@ bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, AttnParams& p
     for (int k = 0; k < no; ++k)
       p.pack_code[x][k >> 3] |= uint32_t(item_run[order[k]]) << (4 * (k & 7));
   }
-  int stride = 0;
-  for (int x = 0; x < kNumXcd; ++x) stride = std::max(stride, int(p.xcd_n[x]));
   p.use_xcd = 2;
-  blocks = int64_t(kNumXcd) * stride;
+  blocks = int64_t(kNumXcd) * C;  // one block per CU
   return true;
 }
 
@@ -1333,50 +1337,46 @@ int32_t validate_tick(const wf_tick_desc* d) {
   return WF_OK;
 }
 
-// The work item of attention block b (counted after the store blocks), as the
-// kernel decodes it from the plan: false if the block exits at once.
-bool decode_block(const AttnParams& p, int b, int& rank, int& h, int& qt) {
+// The work items of attention block b (counted after the store blocks), as
+// the kernel decodes them from the plan, appended to `items` as (rank, head,
+// query tile).
+void decode_block(const AttnParams& p, int b, std::vector<int>& items) {
   if (p.use_xcd == 2) {
     const int x = b & (kNumXcd - 1);
-    const int k = b / kNumXcd;
-    if (k >= p.xcd_n[x]) return false;
-    const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
-    int before = 0;
-    for (int i = 0; i < k; ++i) before += ((p.pack_code[x][i >> 3] >> (4 * (i & 7))) & 15) == run;
-    const int grp = p.pack_grp[x][run];
-    qt = p.pack_qt0[x][run] + before;
-    rank = grp / p.H;
-    h = grp - rank * p.H;
+    const int c = b / kNumXcd;
+    for (int k = p.pack_bin[x][c]; k < p.pack_bin[x][c + 1]; ++k) {
+      const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
+      int before = 0;
+      for (int i = 0; i < k; ++i) before += ((p.pack_code[x][i >> 3] >> (4 * (i & 7))) & 15) == run;
+      const int grp = p.pack_grp[x][run];
+      items.insert(items.end(), {grp / p.H, grp % p.H, p.pack_qt0[x][run] + before});
+    }
   } else if (p.use_xcd) {
     const int x = b & (kNumXcd - 1);
     const int k = b / kNumXcd;
     const int gi = k / p.ntq;
-    if (gi >= p.xcd_n[x]) return false;
+    if (gi >= p.xcd_n[x]) return;
     const int grp = p.xcd_groups[x * p.xcd_stride + gi];
-    qt = k - gi * p.ntq;
-    rank = grp / p.H;
-    h = grp - rank * p.H;
+    items.insert(items.end(), {grp / p.H, grp % p.H, k - gi * p.ntq});
   } else {
-    rank = b / p.items_per_stage;
+    const int rank = b / p.items_per_stage;
     const int rem = b - rank * p.items_per_stage;
-    h = rem / p.ntq;
-    qt = rem - h * p.ntq;
+    items.insert(items.end(), {rank, rem / p.ntq, rem % p.ntq});
   }
-  return true;
 }
 
 }  // namespace
 }  // namespace wf
 
 extern "C" wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_per_xcd_hint,
-                                        int32_t* out, int64_t capacity, int64_t* n_blocks) {
+                                        int32_t* out, int64_t capacity, int64_t* n_items) {
   using namespace wf;
   try {
-    if (!n_blocks) return fail(WF_EINVAL, "wf_tick_work_order: n_blocks is NULL");
+    if (!n_items) return fail(WF_EINVAL, "wf_tick_work_order: n_items is NULL");
     int32_t st = validate_tick(desc);
     if (st != WF_OK) return st;
     const wf_tick_desc& d = *desc;
-    *n_blocks = 0;
+    *n_items = 0;
     if (d.T == 0 || d.active_mask == 0) return WF_OK;
     StagePlan pl;
     plan_stages(d, pl);
@@ -1389,18 +1389,19 @@ extern "C" wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_pe
     int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
     const int C = cus_per_xcd_hint > 0 ? cus_per_xcd_hint : cus_per_xcd();
     if (!plan_packed_order(pl, d.H, p.tps, C, p, blocks)) plan_xcd_order(pl, d.H, p, blocks);
-    *n_blocks = blocks;
-    if (!out) return WF_OK;
-    if (capacity < 3 * blocks)
-      return fail(WF_EINVAL, "wf_tick_work_order: capacity %lld < 3 * %lld blocks",
-                  static_cast<long long>(capacity), static_cast<long long>(blocks));
+    std::vector<int> rows;
     for (int64_t b = 0; b < blocks; ++b) {
-      int rank = 0, h = 0, qt = 0;
-      const bool live = decode_block(p, int(b), rank, h, qt);
-      out[3 * b] = live ? pl.order[rank] : -1;
-      out[3 * b + 1] = live ? h : -1;
-      out[3 * b + 2] = live ? qt : -1;
+      std::vector<int> items;
+      decode_block(p, int(b), items);
+      for (size_t i = 0; i < items.size(); i += 3)
+        rows.insert(rows.end(), {int(b), pl.order[items[i]], items[i + 1], items[i + 2]});
     }
+    *n_items = int64_t(rows.size() / 4);
+    if (!out) return WF_OK;
+    if (capacity < int64_t(rows.size()))
+      return fail(WF_EINVAL, "wf_tick_work_order: capacity %lld < 4 * %lld items",
+                  static_cast<long long>(capacity), static_cast<long long>(rows.size() / 4));
+    std::copy(rows.begin(), rows.end(), out);
     return WF_OK;
   } catch (...) {
     return fail(WF_EINVAL, "wf_tick_work_order: internal error");
