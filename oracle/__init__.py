@@ -16,8 +16,9 @@ from the Wave Forcing pages:
     the anchor's re-rotation after a window shift, and correctly rounded
     float64 -> bf16 conversion of the rotated keys;
   * fp8: the 8-bit tier's e4m3 encoding and decoding, per-group float32
-    scales (queries per row, keys per 64-token tile and head), an 8-bit page
-    store and the tick over the dequantised values.
+    scales (queries per row, keys per 64-token tile and head), power-of-two
+    scales for 8-bit values, 8-bit page stores, the tick over the dequantised
+    values and the bound on what rounding P to e4m3 can change.
 
 Parity status: every function is pinned by the `-m "not gpu"` tests in
 tests/test_oracle_pins.py, tests/test_page_model.py, tests/test_rope_oracle.py and
@@ -61,4 +62,9 @@ from .fp8 import (  # noqa: F401
     quantize_q_rows,
     Fp8PageStore,
     attention_tick_fp8,
+    pow2_exponent,
+    quantize_v_tiles,
+    Fp8KvPageStore,
+    attention_tick_fp8kv,
+    p_error_bound,
 )

@@ -194,3 +194,134 @@ def attention_tick_fp8(q_bits, store: "Fp8PageStore", hist_pages, live_pages, S:
             lk[j], lv[j] = kk[0], vv[0]
     from .wave_attention import as_f64
     return attention_tick(qv, lk, as_f64(lv), hk, as_f64(hv), S, active_mask, scale, **kw)
+
+
+# ----------------------------------------------------------------------------
+# 8-bit values (the tier where V is e4m3 too)
+# ----------------------------------------------------------------------------
+# Reading: V is quantised per (64-token tile, head) with a
+# power-of-two scale 2^e, e the smallest integer with amax <= 448 * 2^e (so the
+# scale is an 8-bit exponent and the codes are e4m3 of v * 2^-e, a product
+# that is exact in float32), e = 0 for an all-zero tile. P is rounded to e4m3
+# (P <= 2^8 under the bf16 tier's lazy reference) for the P.V product; that
+# rounding depends on the kernel's running reference, so the tick is checked
+# against the exact attention of the dequantised values within the bound
+# p_error_bound() gives.
+
+
+def pow2_exponent(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e (amax > 0), else 0.
+    amax = f * 2^E with 0.5 <= f < 1 and 448 = 0.875 * 2^9, so e = E - 9 when
+    f <= 0.875 and E - 8 otherwise."""
+    amax = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(amax)
+    e = np.where(f <= 0.875, E - 9, E - 8)
+    return np.where(amax > 0, e, 0).astype(np.int64)
+
+
+def quantize_v_tiles(v_bits_or_vals: np.ndarray, tile: int = 64) -> Tuple[np.ndarray, np.ndarray]:
+    """Values [T][H][D] of one chunk -> (codes [T][H][D], exponents [ceil(T/tile)][H]):
+    codes = e4m3 of v * 2^-e per (64-token tile, head)."""
+    from .wave_attention import as_f64
+
+    v = as_f64(v_bits_or_vals).astype(np.float32)
+    T, H, D = v.shape
+    nt = -(-T // tile)
+    codes = np.zeros((T, H, D), np.uint8)
+    exps = np.zeros((nt, H), np.int64)
+    for t in range(nt):
+        blk = v[t * tile:(t + 1) * tile]
+        amax = np.abs(blk).max(axis=(0, 2)).astype(np.float32)       # [H]
+        e = pow2_exponent(amax)
+        exps[t] = e
+        y = blk.astype(np.float64) * np.exp2(-e)[None, :, None]        # exact (power of two)
+        codes[t * tile:(t + 1) * tile] = e4m3_encode(y)
+    return codes, exps
+
+
+class Fp8KvPageStore(Fp8PageStore):
+    """The 8-bit page store with V in e4m3 as well: page id -> (K codes, K scales,
+    V codes uint8 [P][H][D], V exponents int [P/64][H])."""
+
+    def write_chunk(self, ids, k_bits, v_bits) -> None:
+        T = k_bits.shape[0]
+        P, tile = self.P, self.tile
+        if len(ids) != -(-T // P):
+            raise ValueError("wrong number of page ids for the chunk")
+        kc_all, ks_all = quantize_k_tiles(k_bits, tile)
+        vc_all, ve_all = quantize_v_tiles(v_bits, tile)
+        for n, pid in enumerate(ids):
+            kc = np.zeros((P, self.H, self.D), np.uint8)
+            ks = np.zeros((P // tile, self.H), np.float32)
+            vc = np.zeros((P, self.H, self.D), np.uint8)
+            ve = np.zeros((P // tile, self.H), np.int64)
+            t0, t1 = n * P, min(T, (n + 1) * P)
+            kc[:t1 - t0] = kc_all[t0:t1]
+            vc[:t1 - t0] = vc_all[t0:t1]
+            nt = -(-(t1 - t0) // tile)
+            ks[:nt] = ks_all[t0 // tile:t0 // tile + nt]
+            ve[:nt] = ve_all[t0 // tile:t0 // tile + nt]
+            self.pages[int(pid)] = (kc, ks, vc, ve)
+
+    def gather(self, page_lists, T: int):
+        """Dequantised K and V (float64), [n][T][H][D]."""
+        n = len(page_lists)
+        K = np.zeros((n, T, self.H, self.D), np.float64)
+        V = np.zeros((n, T, self.H, self.D), np.float64)
+        for c, ids in enumerate(page_lists):
+            for t in range(T):
+                kc, ks, vc, ve = self.pages[int(ids[t // self.P])]
+                slot = t % self.P
+                K[c, t] = e4m3_decode(kc[slot]) * ks[slot // self.tile][:, None].astype(np.float64)
+                V[c, t] = e4m3_decode(vc[slot]) * np.exp2(ve[slot // self.tile])[:, None]
+        return K, V
+
+
+def attention_tick_fp8kv(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: int,
+                         active_mask: int, scale: float, **kw):
+    """The tick of the 8-bit K/V tier over the dequantised Q, K and V (exact
+    softmax, float64): what the device approximates up to its e4m3 rounding of
+    P, bounded by p_error_bound()."""
+    return attention_tick_fp8(q_bits, store, hist_pages, live_pages, S, active_mask, scale, **kw)
+
+
+def p_error_bound(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: int,
+                  active_mask: int, scale: float, stages=None, heads=None, rows=None):
+    """Per (stage, row, head) bound on |O_device - O_exact| from rounding P to
+    e4m3 alone: with P relative to the row's max (max P = 1), the device's P is
+    that times 2^a for some a in [0, 8] (its running reference lies at most 8
+    below the max, never above), and e4m3 rounds it within 2^-4 of itself or
+    2^-10 absolutely (subnormals), so each P moves by at most
+    max(2^-4 P, 2^-10); the output, a P-weighted mean with the exact sum of P as
+    divisor, moves by at most sum(max(2^-4 P, 2^-10) |v|) / sum(P).
+    Returns {stage: [rows][heads]}."""
+    from .wave_attention import _active, _hf, token_mask, _key_matrix
+
+    T, H, D = q_bits.shape[1], q_bits.shape[2], q_bits.shape[3]
+    qc, qs = quantize_q_rows(q_bits)
+    qv = e4m3_decode(qc) * qs[..., None].astype(np.float64)
+    hk, hv = store.gather(hist_pages, T)
+    lk = np.zeros((S + 1, T, H, D))
+    lv = np.zeros((S + 1, T, H, D))
+    for j in range(S + 1):
+        if (active_mask >> j) & 1:
+            kk, vv = store.gather([live_pages[j]], T)
+            lk[j], lv[j] = kk[0], vv[0]
+    act = _active(active_mask, S)
+    stages = act if stages is None else [s for s in stages if s in act]
+    heads = list(range(H)) if heads is None else list(heads)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    n_hist = hk.shape[0]
+    out = {}
+    for s in stages:
+        m = token_mask(s, S, active_mask, n_hist, T, 0)
+        out[s] = np.zeros((len(rows), len(heads)))
+        for hi, h in enumerate(heads):
+            K = _key_matrix(lk, hk, h, S)[m]
+            Vabs = np.abs(_key_matrix(lv, hv, h, S)[m])                    # [keys][D]
+            sc = (qv[s, rows, h, :] @ K.T) * scale
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            w = np.maximum(2.0 ** -4 * p, 2.0 ** -10)
+            # bound for the worst channel of each row
+            out[s][:, hi] = ((w @ Vabs) / p.sum(axis=1, keepdims=True)).max(axis=1)
+    return out

@@ -192,3 +192,77 @@ def test_page_store_matches_contiguous_quantisation():
     assert not kc[T - 2 * P:].any() and ks[1].tolist() == [0.0, 0.0]  # past the chunk
     with pytest.raises(ValueError):
         fp8.Fp8PageStore(96, H, D)
+
+
+def test_pow2_exponent_closed_forms_and_property():
+    e = fp8.pow2_exponent(np.array([448.0, 449.0, 1.0, 0.875 * 2.0 ** -3, 0.0, 3.5, 2.0 ** -100]))
+    assert e.tolist() == [0, 1, -8, -12, 0, -7, -108]
+    rng = np.random.default_rng(21)
+    amax = np.exp2(rng.uniform(-20, 20, 5000))
+    e = fp8.pow2_exponent(amax)
+    assert np.all(amax <= 448.0 * np.exp2(e)) and np.all(amax > 448.0 * np.exp2(e - 1))
+
+
+def test_v_tiles_pow2_scale_and_library_codes():
+    rng = np.random.default_rng(22)
+    T, H, D = 150, 3, 64
+    v = (rng.standard_normal((T, H, D)) * np.exp2(rng.integers(-3, 4, (1, H, 1)))).astype(np.float32)
+    v[64:128, 1] = 0.0                                      # an all-zero (tile, head)
+    codes, exps = fp8.quantize_v_tiles(v)
+    assert exps.shape == (3, H) and exps[1, 1] == 0 and not codes[64:128, 1].any()
+    for t in range(3):
+        blk = v[t * 64:(t + 1) * 64]
+        for h in range(H):
+            amax = np.abs(blk[:, h]).max()
+            if amax == 0:
+                continue
+            e = int(exps[t, h])
+            assert amax <= 448 * 2.0 ** e < 2 * amax
+            lib = torch.from_numpy((blk[:, h] * np.float32(2.0 ** -e)).astype(np.float32)) \
+                .to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(codes[t * 64:(t + 1) * 64, h], lib)
+
+
+def test_kv_page_store_matches_contiguous():
+    rng = np.random.default_rng(23)
+    T, H, D, P = 200, 2, 64, 128
+    kb = (rng.standard_normal((T, H, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vb = (rng.standard_normal((T, H, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    store = fp8.Fp8KvPageStore(P, H, D)
+    store.write_chunk([3, 0], kb, vb)
+    K, V = store.gather([[3, 0]], T)
+    kc, ks = fp8.quantize_k_tiles(kb)
+    vc, ve = fp8.quantize_v_tiles(vb)
+    assert np.array_equal(K[0], fp8.e4m3_decode(kc) * np.repeat(ks, 64, axis=0)[:T, :, None])
+    assert np.array_equal(V[0], fp8.e4m3_decode(vc) * np.exp2(np.repeat(ve, 64, axis=0)[:T, :, None]))
+
+
+def test_p_error_bound_holds_for_rounded_p():
+    """Round P to e4m3 at references 0..8 below the row max (as the device may)
+    and check the output moves by no more than the bound."""
+    rng = np.random.default_rng(24)
+    S, T, H, D, P = 1, 96, 1, 64, 64
+    qb = (rng.standard_normal((S + 1, T, H, D)).astype(np.float32) * 2).view(np.uint32) >> 16
+    kb = (rng.standard_normal((T, H, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    vb = (rng.standard_normal((T, H, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    store = fp8.Fp8KvPageStore(P, H, D)
+    ids = [[0, 1], [2, 3]]
+    store.write_chunk(ids[0], kb, vb)
+    store.write_chunk(ids[1], kb[::-1].copy(), vb[::-1].copy())
+    qb = qb.astype(np.uint16)
+    bound = fp8.p_error_bound(qb, store, [], ids, S, 0b11, 0.125)
+    # the exact outputs and their e4m3-P versions, computed here from the definition
+    qc, qs = fp8.quantize_q_rows(qb)
+    qv = fp8.e4m3_decode(qc) * qs[..., None]
+    K0, V0 = store.gather([ids[0]], T)
+    K1, V1 = store.gather([ids[1]], T)
+    for s, keys in ((0, (0, 1)), (1, (1,))):
+        Kc = np.concatenate([[K1, K0][0][0] if k == 1 else K0[0] for k in keys])[:, 0]
+        Vc = np.concatenate([V1[0] if k == 1 else V0[0] for k in keys])[:, 0]
+        sc = qv[s, :, 0] @ Kc.T * 0.125
+        p = np.exp(sc - sc.max(axis=1, keepdims=True))
+        exact = p @ Vc / p.sum(axis=1, keepdims=True)
+        for a in range(9):
+            pq = fp8.e4m3_decode(fp8.e4m3_encode(p * 2.0 ** a)) / 2.0 ** a
+            approx = pq @ Vc / p.sum(axis=1, keepdims=True)
+            assert np.all(np.abs(approx - exact).max(axis=1) <= bound[s][:, 0] * (1 + 1e-9))
