@@ -185,7 +185,7 @@ def attention_tick_fp8(q_bits, store: "Fp8PageStore", hist_pages, live_pages, S:
         qv[:, rows] = e4m3_decode(qc) * qs[..., None].astype(np.float64)
     hk, hv = store.gather(hist_pages, T)
     lk = np.zeros((S + 1, T, H, D), np.float64)
-    lv = np.zeros((S + 1, T, H, D), np.uint16)
+    lv = np.zeros((S + 1, T, H, D), hv.dtype)   # bf16 bits, or dequantised values
     for j in range(S + 1):
         if (active_mask >> j) & 1:
             if live_pages[j] is None:
@@ -298,7 +298,8 @@ def p_error_bound(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: in
     from .wave_attention import _active, _hf, token_mask, _key_matrix
 
     T, H, D = q_bits.shape[1], q_bits.shape[2], q_bits.shape[3]
-    qc, qs = quantize_q_rows(q_bits)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    qc, qs = quantize_q_rows(q_bits[:, rows])     # each row is quantised on its own
     qv = e4m3_decode(qc) * qs[..., None].astype(np.float64)
     hk, hv = store.gather(hist_pages, T)
     lk = np.zeros((S + 1, T, H, D))
@@ -310,7 +311,6 @@ def p_error_bound(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: in
     act = _active(active_mask, S)
     stages = act if stages is None else [s for s in stages if s in act]
     heads = list(range(H)) if heads is None else list(heads)
-    rows = np.arange(T) if rows is None else np.asarray(rows)
     n_hist = hk.shape[0]
     out = {}
     for s in stages:
@@ -319,7 +319,7 @@ def p_error_bound(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: in
         for hi, h in enumerate(heads):
             K = _key_matrix(lk, hk, h, S)[m]
             Vabs = np.abs(_key_matrix(lv, hv, h, S)[m])                    # [keys][D]
-            sc = (qv[s, rows, h, :] @ K.T) * scale
+            sc = (qv[s, :, h, :] @ K.T) * scale
             p = np.exp(sc - sc.max(axis=1, keepdims=True))
             w = np.maximum(2.0 ** -4 * p, 2.0 ** -10)
             # bound for the worst channel of each row

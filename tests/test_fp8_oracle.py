@@ -266,3 +266,40 @@ def test_p_error_bound_holds_for_rounded_p():
             pq = fp8.e4m3_decode(fp8.e4m3_encode(p * 2.0 ** a)) / 2.0 ** a
             approx = pq @ Vc / p.sum(axis=1, keepdims=True)
             assert np.all(np.abs(approx - exact).max(axis=1) <= bound[s][:, 0] * (1 + 1e-9))
+
+
+def test_fp8kv_tick_reduces_to_bf16_tick_when_exact():
+    """Keys and values the 8-bit K/V store represents exactly (e4m3 values times
+    2^e with one entry at 448 * 2^e per (tile, head)) and zero queries (P = 1,
+    exact in e4m3): the 8-bit K/V tick equals the bf16 oracle's tick."""
+    rng = np.random.default_rng(31)
+    S, T, H, D, P, n_hist = 2, 100, 2, 64, 64, 1
+    finite = fp8.e4m3_decode(np.arange(0x7E, dtype=np.uint8))
+
+    def exact(shape):
+        x = rng.choice(finite, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        for c in range(shape[0]):
+            for t0 in range(0, shape[1], 64):
+                for h in range(shape[2]):
+                    e = int(rng.integers(-9, -3))
+                    x[c, t0:t0 + 64, h] *= 2.0 ** e
+                    x[c, t0, h, int(rng.integers(shape[3]))] = 448.0 * 2.0 ** e
+        return x
+
+    to_bits = lambda a: (np.ascontiguousarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kl, vl = exact((S + 1, T, H, D)), exact((S + 1, T, H, D))
+    kh, vh = exact((n_hist, T, H, D)), exact((n_hist, T, H, D))
+    q = np.zeros((S + 1, T, H, D))
+    store = fp8.Fp8KvPageStore(P, H, D)
+    ppc = -(-T // P)
+    hist = [list(range(c * ppc, (c + 1) * ppc)) for c in range(n_hist)]
+    live = [list(range((n_hist + j) * ppc, (n_hist + j + 1) * ppc)) for j in range(S + 1)]
+    for c in range(n_hist):
+        store.write_chunk(hist[c], to_bits(kh[c]), to_bits(vh[c]))
+    for j in range(S + 1):
+        store.write_chunk(live[j], to_bits(kl[j]), to_bits(vl[j]))
+    mask = (1 << (S + 1)) - 1
+    got = fp8.attention_tick_fp8kv(to_bits(q), store, hist, live, S, mask, 0.125)
+    want = oracle.attention_tick(q, kl, vl, kh, vh, S, mask, 0.125)
+    for s in want:
+        assert np.array_equal(got[s], want[s])
