@@ -103,7 +103,8 @@ def parse():
     ap.add_argument("--kernel-hash", action="store_true",
                     help="print the attention kernel's source hash (recorded with its counters)")
     ap.add_argument("--mode", default="tick",
-                    choices=["tick", "attn", "store", "rope", "paged", "copy", "fp8", "store8"],
+                    choices=["tick", "attn", "store", "rope", "paged", "copy", "fp8", "fp8kv",
+                             "store8"],
                     help="tick: the full hot path (default, prints the JSON line); attn / "
                          "store / rope / fp8 (8-bit tier attention) / store8 (8-bit tier "
                          "producer write): only that kernel, --steps launches (for profilers); "
@@ -420,9 +421,10 @@ def fully_paged(cfg, dev, steps: int = 10, warmup: int = 3) -> dict:
 class Fp8Tick:
     """The 8-bit tier at the same shape, fully paged: history and live chunks in
     e4m3 key pages (+ scales) and bf16 value pages written by wf_store_paged_fp8,
-    the tick's attention reading every key through them."""
+    the tick's attention reading every key through them; with v8, e4m3 value
+    pages (transposed tiles + exponents) as well."""
 
-    def __init__(self, cfg, dev):
+    def __init__(self, cfg, dev, v8: bool = False):
         import torch
 
         from wavefront_causal_attention_wf_amd import inputs, wfattn
@@ -436,11 +438,17 @@ class Fp8Tick:
         self.live = order[cfg.n_hist * ppc:].view(S + 1, ppc)
         self.k_pool = torch.zeros((cfg.num_pages, P, H, D), dtype=torch.uint8, device=dev)
         self.k_scale = torch.zeros((cfg.num_pages, P // 64, H), dtype=torch.float32, device=dev)
-        self.v_pool = torch.zeros((cfg.num_pages, P, H, D), dtype=torch.bfloat16, device=dev)
+        if v8:
+            self.v_pool = torch.zeros((cfg.num_pages, P // 64, H, D, 64), dtype=torch.uint8,
+                                      device=dev)
+            self.v_exp = torch.zeros((cfg.num_pages, P // 64, H), dtype=torch.uint8, device=dev)
+        else:
+            self.v_pool = torch.zeros((cfg.num_pages, P, H, D), dtype=torch.bfloat16, device=dev)
+            self.v_exp = None
         for c in range(cfg.n_hist):
             hk, hv, _ = inputs.draw_live_torch(cfg, 2000 + c, dev)
             wfattn.wf_store_paged_fp8(hk[0], hv[0], self.k_pool, self.k_scale, self.v_pool,
-                                      self.hist[c])
+                                      self.hist[c], v_exp=self.v_exp)
             del hk, hv
         self.q, self.k, self.v = inputs.draw_live_torch(cfg, inputs.rollout_seed(0), dev)
         self.store_live()
@@ -452,22 +460,23 @@ class Fp8Tick:
     def store_live(self):
         for j in range(self.cfg.S + 1):
             self.wf.wf_store_paged_fp8(self.k[j], self.v[j], self.k_pool, self.k_scale,
-                                       self.v_pool, self.live[j])
+                                       self.v_pool, self.live[j], v_exp=self.v_exp)
 
     def attn(self):
         self.wf.wf_attn_tick(self.q, None, None, self.o, self.cfg.S, self.mask, self.scale,
                              self.k_pool, self.v_pool, self.hist, live_pages=self.live,
-                             k_scale=self.k_scale)
+                             k_scale=self.k_scale, v_exp=self.v_exp)
 
 
-def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3) -> dict:
+def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3, v8: bool = False) -> dict:
     """8-bit tier: attention launches alone, and the tick with every live chunk's
-    producer write (five wf_store_paged_fp8 + the attention)."""
+    producer write (five wf_store_paged_fp8 + the attention). v8: values in
+    e4m3 too (P.V on the fp8 MFMA: all useful flops at the fp8 peak)."""
     import torch
 
     from wavefront_causal_attention_wf_amd import wfattn
 
-    ft = Fp8Tick(cfg, dev)
+    ft = Fp8Tick(cfg, dev, v8)
     flops = wfattn.wf_tick_useful_flops(cfg.S, ft.mask, cfg.T, cfg.H, cfg.D, cfg.n_hist, P=cfg.P,
                                         num_pages=cfg.num_pages)
     for _ in range(warmup):
@@ -488,6 +497,15 @@ def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3) -> dict:
     torch.cuda.synchronize()
     ms_tick = a.elapsed_time(b) / launches
     tf = flops / (ms * 1e-3) / 1e12
+    if v8:
+        return {"tier": "e4m3 Q, K and V (per-row / per-(64-token tile, head) fp32 scales for Q "
+                        "and K, power-of-two per-(tile, head) scales for V), e4m3 P; Q.K^T and "
+                        "P.V on fp8 MFMA; every key and value through pages",
+                "attn_kernel_ms_mean": round(ms, 4), "useful_tflop_per_s": round(tf, 2),
+                "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                "tick_with_producer_writes_ms": round(ms_tick, 4),
+                "tick_flow": f"{cfg.S + 1} x wf_store_paged_fp8 with v_exp + wf_attn_tick"}
     return {"tier": "e4m3 Q and K (per-row / per-(64-token tile, head) fp32 scales), Q.K^T on "
                     "fp8 MFMA, bf16 P.V; every key through pages",
             "attn_kernel_ms_mean": round(ms, 4), "useful_tflop_per_s": round(tf, 2),
@@ -562,8 +580,8 @@ def profile_mode(args, cfg, dev) -> None:
         r = fully_paged(cfg, dev, steps=args.steps)
         log(f"fully paged: {r}")
         return
-    if args.mode == "fp8":
-        ft = Fp8Tick(cfg, dev)
+    if args.mode in ("fp8", "fp8kv"):
+        ft = Fp8Tick(cfg, dev, v8=args.mode == "fp8kv")
         for _ in range(args.steps):
             ft.attn()
         torch.cuda.synchronize()
@@ -711,6 +729,8 @@ def main():
     log(f"fully paged: {out['fully_paged']}")
     out["fp8_tier"] = fp8_tier(cfg, dev)
     log(f"fp8 tier: {out['fp8_tier']}")
+    out["fp8kv_tier"] = fp8_tier(cfg, dev, v8=True)
+    log(f"fp8 K/V tier: {out['fp8kv_tier']}")
     out["store_fp8"] = store_fp8_bandwidth(cfg, dev)
     log(f"fp8 store: {out['store_fp8']}")
     if not args.no_cpu_baseline:

@@ -57,7 +57,7 @@ const char* wf_last_error(void);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t wf_abi_version(void);
-#define WF_ABI_VERSION 4
+#define WF_ABI_VERSION 5
 
 /* ------------------------------------------------------------------------ */
 /* Page table: host-only state for one request's attention pages.            */
@@ -172,18 +172,30 @@ wf_status wf_rope_store_paged(const void* k_src, const void* v_src, void* k_pool
 /* page_ids[t / P]; slots past token T-1 hold zero codes and zero V, and a    */
 /* tile holding none of the chunk's tokens has scale 0.                       */
 /* k_src, v_src: device bf16 [T][H][D]; k_pool: device uint8                  */
-/* [num_pages][P][H][D]; k_scale: device fp32 [num_pages][P/64][H]; v_pool:    */
-/* device bf16 [num_pages][P][H][D]; page_ids: device int32 [ceil(T/P)].     */
-/* Precondition (not checked): a tile's amax is 0 or at least 2^-120 (its    */
-/* reciprocal must be finite in fp32).                                        */
+/* [num_pages][P][H][D]; k_scale: device fp32 [num_pages][P/64][H]; page_ids: */
+/* device int32 [ceil(T/P)].                                                  */
+/* v_exp NULL: v_pool is device bf16 [num_pages][P][H][D] and V is copied.    */
+/* v_exp set (8-bit values): V is quantised per (64-token tile, head) with a  */
+/* power-of-two scale 2^e, e the smallest integer with amax <= 448 * 2^e (0   */
+/* for an all-zero tile), code = e4m3 of v * 2^-e (exact product, rounded to  */
+/* nearest even); v_exp: device uint8 [num_pages][P/64][H] receives e + 127;  */
+/* v_pool: device uint8 [num_pages][P/64][H][D][64] is written in the layout  */
+/* the attention's P.V operand reads: row d of tile (page, sub-tile, head)    */
+/* holds channel d of the tile's 64 tokens, byte 32*g + j being token         */
+/* 32*(j/16) + 16*((j/8)%2) + 8*g + j%8 (g = 0, 1; j = 0..31); tokens past    */
+/* the chunk hold zero codes.                                                 */
+/* Preconditions (not checked): a key tile's amax is 0 or at least 2^-120, a  */
+/* value tile's 0 or at least 2^-100 (the scales' reciprocals must be finite  */
+/* in fp32).                                                                  */
 /* Errors: WF_EINVAL for bad sizes, P not a multiple of 64, NULL pointers,    */
 /* tensors not 16-byte aligned (k_scale: 4-byte), ceil(T/P) > num_pages;      */
 /* WF_EUNSUPPORTED for D not 64/128 or H > 65535; WF_EHIP if the launch fails. */
 /* T = 0 is a no-op.                                                         */
 /* ------------------------------------------------------------------------ */
 wf_status wf_store_paged_fp8(const void* k_src, const void* v_src, void* k_pool, float* k_scale,
-                             void* v_pool, const int32_t* page_ids, int32_t T, int32_t H,
-                             int32_t D, int32_t num_pages, int32_t P, hipStream_t stream);
+                             void* v_pool, uint8_t* v_exp, const int32_t* page_ids, int32_t T,
+                             int32_t H, int32_t D, int32_t num_pages, int32_t P,
+                             hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* wf_gather_paged — diagnostic inverse of the store: copy n_chunks chunks    */
@@ -216,8 +228,15 @@ wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t*
 /* scale; the softmax and P.V are those of the bf16 tier. Needs D = 128, P a  */
 /* multiple of 64, no store_pages; a query row's amax must be 0 or at least   */
 /* 2^-120 (not checked).                                                     */
+/* 8-bit values as well (v_format = WF_V_E4M3, with WF_K_E4M3): v_pool holds  */
+/* the transposed e4m3 tiles and v_exp their exponents, as written by          */
+/* wf_store_paged_fp8 with v_exp; P is rounded to e4m3 (P <= 2^8 under the    */
+/* running reference) and P.V runs on the e4m3 MFMA with the tile's          */
+/* power-of-two scale applied by the MFMA; the softmax's sum uses the          */
+/* unrounded P.                                                               */
 /* Errors: WF_EINVAL for bad sizes, masks, pointers (NULL or not 16-byte      */
 /* aligned), P not a positive multiple of 16, n_hist*ceil(T/P) > num_pages;   */
+/* v_format not WF_V_BF16/WF_V_E4M3, WF_V_E4M3 without WF_K_E4M3 or v_exp;  */
 /* k_format not WF_K_BF16/WF_K_E4M3, or WF_K_E4M3 without live_pages or      */
 /* k_scale, with store_pages, or with P not a multiple of 64;                 */
 /* WF_EUNSUPPORTED for D not 64/128 (WF_K_E4M3: not 128), n_hist + S + 1 > 32, */
@@ -259,10 +278,16 @@ typedef struct wf_tick_desc {
                           /* e4m3 codes [num_pages][P][H][D] with k_scale           */
   const float* k_scale;   /* device fp32 [num_pages][P/64][H] with WF_K_E4M3, else  */
                           /* ignored                                                */
+  int32_t v_format;       /* WF_V_BF16 (0), or WF_V_E4M3 (1, needs WF_K_E4M3):      */
+                          /* v_pool uint8 transposed tiles [num_pages][P/64][H][D]  */
+                          /* [64] with v_exp                                        */
+  const uint8_t* v_exp;   /* device uint8 [num_pages][P/64][H] with WF_V_E4M3       */
 } wf_tick_desc;
 
 #define WF_K_BF16 0
 #define WF_K_E4M3 1
+#define WF_V_BF16 0
+#define WF_V_E4M3 1
 
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);
 

@@ -452,7 +452,7 @@ def test_store_fp8_validation():
 
     def call(T=4680, H=12, D=128, num_pages=4096, P=64, k=fake, v=fake, kp=fake, ks=fake,
              vp=fake, ids=fake):
-        return lib.wf_store_paged_fp8(k, v, kp, ks, vp, ids, T, H, D, num_pages, P, None)
+        return lib.wf_store_paged_fp8(k, v, kp, ks, vp, None, ids, T, H, D, num_pages, P, None)
 
     E, U = CODES["EINVAL"], CODES["EUNSUPPORTED"]
     assert call(P=96) == E                      # scale tiles of 64 tokens must tile a page

@@ -184,3 +184,188 @@ def test_fp8_tick_full_size_sampled_rows():
                                    scale, rows=rows)
     worst = compare(o, want, rows=rows, label="fp8 full size")
     say(f"[full-size fp8] worst rel-L2 {worst:.2e} over {len(rows)} rows x {cfg.H} heads")
+
+
+# ---------------------------------------------------------------------------
+# 8-bit values too (v_format = E4M3)
+# ---------------------------------------------------------------------------
+def v8_token_of_column():
+    """Token (0..63) stored at byte 32*g + j of a transposed 8-bit V row."""
+    return np.array([32 * (j // 16) + 16 * ((j // 8) % 2) + 8 * g + j % 8
+                     for g in range(2) for j in range(32)])
+
+
+class Fp8KvPages:
+    """Device pools of the 8-bit K/V tier, poisoned, and the oracle's store."""
+
+    def __init__(self, num_pages, P, H, D):
+        self.P, self.H, self.D = P, H, D
+        self.k_pool = torch.full((num_pages, P, H, D), 0xFF, dtype=torch.uint8, device=DEV)
+        self.k_scale = torch.full((num_pages, P // 64, H), float("nan"), dtype=torch.float32,
+                                  device=DEV)
+        self.v_pool = torch.full((num_pages, P // 64, H, D, 64), 0xFF, dtype=torch.uint8,
+                                 device=DEV)
+        self.v_exp = torch.full((num_pages, P // 64, H), 0xFF, dtype=torch.uint8, device=DEV)
+        self.store = ofp8.Fp8KvPageStore(P, H, D)
+
+    def write(self, ids, k_chunk, v_chunk, k_bits=None, v_bits=None):
+        wfattn.wf_store_paged_fp8(k_chunk, v_chunk, self.k_pool, self.k_scale, self.v_pool,
+                                  torch.from_numpy(np.asarray(ids, np.int32)).to(DEV),
+                                  v_exp=self.v_exp)
+        self.store.write_chunk(list(ids), bits(k_chunk) if k_bits is None else k_bits,
+                               bits(v_chunk) if v_bits is None else v_bits)
+
+    def check(self, ids):
+        torch.cuda.synchronize()
+        idx = torch.as_tensor(np.asarray(ids), dtype=torch.long, device=DEV)
+        kc = self.k_pool.index_select(0, idx).cpu().numpy()
+        ks = self.k_scale.index_select(0, idx).cpu().numpy()
+        vt = self.v_pool.index_select(0, idx).cpu().numpy()      # [n][P/64][H][D][64]
+        ve = self.v_exp.index_select(0, idx).cpu().numpy()
+        tok = v8_token_of_column()
+        for n, pid in enumerate(ids):
+            wk, ws, wv, we = self.store.pages[int(pid)]
+            assert np.array_equal(kc[n], wk), f"page {pid} key codes"
+            assert np.array_equal(ks[n].view(np.uint32), ws.view(np.uint32)), f"page {pid} scales"
+            # logical value codes [P][H][D] from the transposed tiles
+            logical = np.zeros_like(wv)
+            for sub in range(self.P // 64):
+                rows = vt[n, sub]                                  # [H][D][64]
+                logical[sub * 64 + tok] = rows.transpose(2, 0, 1)
+            bad = logical != wv
+            assert not bad.any(), f"page {pid}: {int(bad.sum())} value codes differ"
+            assert np.array_equal(ve[n].astype(np.int64), we + 127), f"page {pid} exponents"
+
+
+def _fp8kv_tick(S, T, H, P, n_hist, mask, seed, q_zero=False):
+    D = 128
+    cfg = inputs.TickConfig("f8kv", S=S, T=T, H=H, D=D, P=P, n_hist=n_hist, num_pages=1,
+                            std=0.5, bf16_inputs=True, page_order="identity", seed=seed)
+    x = inputs.draw_tick(cfg)
+    q_bits = np.zeros_like(x.q_bits) if q_zero else x.q_bits
+    ppc = -(-T // P)
+    num_pages = (n_hist + S + 2) * ppc + 3
+    order = np.random.default_rng(seed + 9).permutation(num_pages).astype(np.int32)
+    pg = Fp8KvPages(num_pages, P, H, D)
+    hist = order[:n_hist * ppc].reshape(n_hist, ppc) if n_hist else np.zeros((0, ppc), np.int32)
+    for c in range(n_hist):
+        pg.write(hist[c], inputs.to_device_bf16(x.hist_k_bits[c], DEV),
+                 inputs.to_device_bf16(x.hist_v_bits[c], DEV), x.hist_k_bits[c], x.hist_v_bits[c])
+    nan_ids = order[-ppc:]
+    live = np.empty((S + 1, ppc), np.int32)
+    live_lists = []
+    for j in range(S + 1):
+        if (mask >> j) & 1:
+            ids = order[(n_hist + j) * ppc:(n_hist + j + 1) * ppc]
+            pg.write(ids, inputs.to_device_bf16(x.k_bits[j], DEV),
+                     inputs.to_device_bf16(x.v_bits[j], DEV), x.k_bits[j], x.v_bits[j])
+            live[j] = ids
+            live_lists.append(ids.tolist())
+        else:
+            live[j] = nan_ids
+            live_lists.append(None)
+    q = inputs.to_device_bf16(q_bits, DEV)
+    o = torch.full_like(q, float("nan"))
+    scale = 1.0 / np.sqrt(D)
+    wfattn.wf_attn_tick(q, None, None, o, S, mask, scale, pg.k_pool, pg.v_pool,
+                        torch.from_numpy(np.ascontiguousarray(hist)).to(DEV) if n_hist else None,
+                        live_pages=torch.from_numpy(live).to(DEV), k_scale=pg.k_scale,
+                        v_exp=pg.v_exp)
+    torch.cuda.synchronize()
+    return pg, q_bits, hist, live_lists, o, scale
+
+
+def compare_within_p_bound(o, want, bound, rows=None, label=""):
+    """|device - exact| <= the e4m3-P bound + the bf16 output rounding and fp32
+    slack (2^-8 |exact| + 2e-3), element by element."""
+    if rows is not None:
+        o = o.index_select(1, torch.as_tensor(np.asarray(rows), dtype=torch.long, device=o.device))
+    g = o.float().cpu().numpy().astype(np.float64)
+    worst_ratio = 0.0
+    for s, w in want.items():
+        d = np.abs(g[s] - w)
+        lim = bound[s][:, :, None] + 2.0 ** -8 * np.abs(w) + 2e-3
+        assert np.isfinite(g[s]).all(), f"{label} stage {s}: non-finite outputs"
+        assert np.all(d <= lim), f"{label} stage {s}: max excess {float((d - lim).max()):.3e}"
+        worst_ratio = max(worst_ratio, float((d / lim).max()))
+    return worst_ratio
+
+
+@pytest.mark.parametrize("T,H,P", [(200, 2, 64), (150, 3, 128), (4680, 12, 64)])
+def test_store_fp8kv_matches_oracle_bits(T, H, P):
+    say(f"store fp8 K/V T={T} H={H} P={P}")
+    ppc = -(-T // P)
+    num_pages = ppc + 3
+    cfg = inputs.TickConfig("s", S=0, T=T, H=H, D=128, P=P, n_hist=0, num_pages=num_pages,
+                            std=0.5, bf16_inputs=True, page_order="permutation")
+    k, v, _ = inputs.draw_live_torch(cfg, 99 + T, DEV)
+    v[0, 5] = 0.0
+    pg = Fp8KvPages(num_pages, P, H, 128)
+    ids = np.random.default_rng(T + 1).permutation(num_pages)[:ppc].astype(np.int32)
+    pg.write(ids, k[0], v[0])
+    pg.check(ids)
+
+
+@pytest.mark.parametrize("S,T,H,P,n_hist,mask", [
+    (4, 200, 2, 64, 2, 0b11111),
+    (3, 130, 2, 128, 1, 0b1011),
+])
+def test_fp8kv_tick_exact_p(S, T, H, P, n_hist, mask):
+    """Zero queries make every score 0 and every P exactly 1 (an e4m3 value), so
+    the output is the mean of the dequantised values: the bf16 tier's bounds."""
+    say(f"fp8 K/V tick, P = 1: S={S} T={T} H={H} P={P}")
+    pg, q_bits, hist, live_lists, o, scale = _fp8kv_tick(S, T, H, P, n_hist, mask, seed=T,
+                                                         q_zero=True)
+    want = ofp8.attention_tick_fp8kv(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
+    compare(o, want, label="fp8 K/V, P = 1")
+
+
+@pytest.mark.parametrize("S,T,H,P,n_hist,mask", [
+    (4, 200, 2, 64, 2, 0b11111),
+    (3, 130, 2, 128, 1, 0b1011),
+    (4, 70, 3, 64, 3, 0b10110),
+])
+def test_fp8kv_tick_within_p_bound(S, T, H, P, n_hist, mask):
+    say(f"fp8 K/V tick S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b}")
+    pg, q_bits, hist, live_lists, o, scale = _fp8kv_tick(S, T, H, P, n_hist, mask, seed=T + 7)
+    for ids in list(hist) + [l for l in live_lists if l is not None]:
+        pg.check(list(ids))
+    want = ofp8.attention_tick_fp8kv(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
+    bound = ofp8.p_error_bound(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
+    r = compare_within_p_bound(o, want, bound, label="fp8 K/V")
+    say(f"  worst |error| / allowance {r:.3f}")
+
+
+def test_fp8kv_tick_full_size_sampled_rows():
+    cfg = inputs.CONFIGS["wan13_4step"]
+    say(f"[full-size fp8 K/V] S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist}")
+    ppc = cfg.ppc
+    pg = Fp8KvPages(cfg.num_pages, cfg.P, cfg.H, cfg.D)
+    order = inputs.initial_free_order(cfg)
+    hist = order[:cfg.n_hist * ppc].reshape(cfg.n_hist, ppc)
+    for c in range(cfg.n_hist):
+        hk, hv, _ = inputs.draw_live_torch(cfg, 2000 + c, DEV)
+        pg.write(hist[c], hk[0], hv[0])
+        del hk, hv
+    q, k, v = inputs.draw_live_torch(cfg, inputs.rollout_seed(0), DEV)
+    live = order[cfg.n_hist * ppc:(cfg.n_hist + cfg.S + 1) * ppc].reshape(cfg.S + 1, ppc)
+    for j in range(cfg.S + 1):
+        pg.write(live[j], k[j], v[j])
+    pg.check(list(hist[0][:4]) + list(live[cfg.S][-4:]))
+    mask = (1 << (cfg.S + 1)) - 1
+    o = torch.full_like(q, float("nan"))
+    scale = 1.0 / np.sqrt(cfg.D)
+    wfattn.wf_attn_tick(q, None, None, o, cfg.S, mask, scale, pg.k_pool, pg.v_pool,
+                        torch.from_numpy(np.ascontiguousarray(hist)).to(DEV),
+                        live_pages=torch.from_numpy(np.ascontiguousarray(live)).to(DEV),
+                        k_scale=pg.k_scale, v_exp=pg.v_exp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    rows = sample_rows(cfg.T, seed=9, n_random=8)
+    qb = bits(q)
+    want = ofp8.attention_tick_fp8kv(qb, pg.store, hist.tolist(), live.tolist(), cfg.S, mask,
+                                     scale, rows=rows)
+    bound = ofp8.p_error_bound(qb, pg.store, hist.tolist(), live.tolist(), cfg.S, mask, scale,
+                               rows=rows)
+    r = compare_within_p_bound(o, want, bound, rows=rows, label="fp8 K/V full size")
+    say(f"[full-size fp8 K/V] worst |error| / allowance {r:.3f} over {len(rows)} rows")

@@ -106,6 +106,7 @@ struct AttnParams {
   int32_t store_slot;         // S
   int32_t n_hist;
   const float* k_scale;   // 8-bit tier: [num_pages][P / 64][H] key tile scales
+  const uint8_t* v_exp;   // 8-bit values: [num_pages][P / 64][H] tile exponents + 127
   int32_t spp;            // 64-token scale tiles per page (P / 64)
   int32_t T, H, P, ppc;
   int32_t tps;            // tiles per chunk, ceil(T / 64)
@@ -169,6 +170,10 @@ __device__ __forceinline__ int kswz(int row) {
 __device__ __forceinline__ int kswz8(int row) {
   return ((row ^ (row >> 2)) & 1) | (row & 2) | ((row >> 1) & 4);
 }
+// 8-bit values (transposed tile, rows of 64 bytes = four 16-byte chunks): a
+// read touches one chunk of 16 consecutive rows; rows r and r + 4k land in
+// distinct chunks when the chunk is XORed with bits 2-3 of the row.
+__device__ __forceinline__ int v8swz(int drow) { return (drow >> 2) & 3; }
 template <int D>
 __device__ __forceinline__ int vswz(int row) {
   const int q = row & 3;
@@ -268,14 +273,18 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // issues the loads of row group i. Past the last tile the cursor reads tile 0
 // again (finite, masked). KB = bytes per key element: 2 (bf16), or 1 (e4m3
 // keys of the 8-bit tier, whose rows are half as long, so a wave needs half
-// as many K instructions per tile; kFast only).
-template <int D, bool kFast, int KB>
+// as many K instructions per tile; kFast only). VB = bytes per value
+// element: 2, or 1 (8-bit values: a V tile is D rows of 64 token bytes, one
+// contiguous 64*D-byte block of its page, which each wave loads 16 rows of
+// with one instruction).
+template <int D, bool kFast, int KB, int VB = 2>
 struct TileLoader {
   static_assert(KB == 2 || kFast, "8-bit keys need whole-tile sources");
+  static_assert(VB == 2 || (KB == 1 && D == 128 && NWAVES == 8), "8-bit values: D = 128");
   static constexpr int DC = D / 8;        // 16-byte chunks per V row
   static constexpr int RPI = 64 / DC;     // V rows per wave instruction
   static constexpr int RW = KT / NWAVES;  // tile rows loaded by each wave
-  static constexpr int NI = RW / RPI;     // V instructions per wave per tile
+  static constexpr int NI = VB == 2 ? RW / RPI : 1;  // V instructions per wave per tile
   static constexpr int DCK = D * KB / 16; // 16-byte chunks per K row
   static constexpr int RPIK = 64 / DCK;   // K rows per wave instruction
   static constexpr int NIK = RW / RPIK;   // K instructions per wave per tile (<= NI)
@@ -308,6 +317,11 @@ struct TileLoader {
       const uint32_t vc = uint32_t(pc ^ vswz<D>(row[i])) * 16;
       voff[i] = uint32_t(row[i]) * u.row_bytes + vc;
       voff_r[i] = uint32_t(rr) * u.row_bytes + vc;
+      if constexpr (VB == 1) {  // channel row of the transposed tile, its 16-byte chunk
+        const int drow = wave * (D / NWAVES) + lane / 4;
+        voff[i] = uint32_t(drow * 64 + (((lane & 3) ^ v8swz(drow)) << 4));
+        voff_r[i] = voff[i];  // tokens past the chunk are zero codes
+      }
     }
     const int pck = lane % DCK;
 #pragma unroll
@@ -402,7 +416,7 @@ struct TileLoader {
                                        int wave) const {
     // (K buffer offset in 16-bit elements: rows of D * KB bytes)
     lds_void* kdst = opaque_lds(kbuf + (wave * RW + RPIK * (i < NIK ? i : 0)) * D * KB / 2);
-    lds_void* vdst = opaque_lds(vbuf + (wave * RW + RPI * i) * D);
+    lds_void* vdst = opaque_lds(vbuf + (VB == 2 ? (wave * RW + RPI * i) * D : wave * (D / NWAVES) * 32));
     if (!kFast && per_lane) {
       const uint64_t o = uint64_t(prow[i]) * u.row_bytes;
       const uint32_t rb = uint32_t(row[i]) * u.row_bytes;
@@ -482,35 +496,40 @@ __device__ __forceinline__ void store_page_block(const AttnParams& p, int S) {
   }
 }
 
-template <int D, bool kFast, bool kF8>
+template <int D, bool kFast, bool kF8, bool kV8 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS),
                           amdgpu_waves_per_eu(2, 2))) void
 attn_tick_kernel(const AttnParams p) {
   static_assert(!kF8 || (D == 128 && kFast), "8-bit keys: D = 128, whole-tile sources");
+  static_assert(!kV8 || kF8, "8-bit values come with 8-bit keys");
   constexpr int KS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int KB = kF8 ? 1 : 2;  // bytes per key element
-  using Loader = TileLoader<D, kFast, KB>;
+  constexpr int VB = kV8 ? 1 : 2;  // bytes per value element
+  using Loader = TileLoader<D, kFast, KB, VB>;
   constexpr int NI = Loader::NI;
   constexpr int LPT = Loader::LPT;
   constexpr int KTILE = KT * D * KB / 2;  // one K tile in 16-bit elements
+  constexpr int VTILE = KT * D * VB / 2;  // one V tile in 16-bit elements
   // Four K and four V tile buffers (one array each, 256-byte aligned); the loop
   // is unrolled by four so that every access names its buffer statically.
   __shared__ __attribute__((aligned(256))) uint16_t k_tiles[4 * KTILE];
-  __shared__ __attribute__((aligned(256))) uint16_t v_tiles[4 * KT * D];
+  __shared__ __attribute__((aligned(256))) uint16_t v_tiles[4 * VTILE];
   uint16_t* const k_lds0 = k_tiles;
   uint16_t* const k_lds1 = k_tiles + KTILE;
   uint16_t* const k_lds2 = k_tiles + 2 * KTILE;
   uint16_t* const k_lds3 = k_tiles + 3 * KTILE;
   uint16_t* const v_lds0 = v_tiles;
-  uint16_t* const v_lds1 = v_tiles + KT * D;
-  uint16_t* const v_lds2 = v_tiles + 2 * KT * D;
-  uint16_t* const v_lds3 = v_tiles + 3 * KT * D;
+  uint16_t* const v_lds1 = v_tiles + VTILE;
+  uint16_t* const v_lds2 = v_tiles + 2 * VTILE;
+  uint16_t* const v_lds3 = v_tiles + 3 * VTILE;
   __shared__ int32_t pages_lds[kFast ? 1 : kMaxPageIds];
   __shared__ uint4 tile_tab[kFast ? kMaxTiles : 1];
   // 8-bit tier: each tile's key scale for this head (0 replaced by 1: an
   // all-zero tile has zero codes, so any finite multiplier gives its scores)
   __shared__ float tile_scale[kF8 ? kMaxTiles : 1];
+  // 8-bit values: each tile's value exponent for this head (E8M0: e + 127)
+  __shared__ int32_t tile_vexp[kV8 ? kMaxTiles : 1];
 
   // ---- the store chunk's page copy (leading blocks, optional) --------------
   if (int(blockIdx.x) < p.n_store_blocks) {
@@ -596,6 +615,11 @@ attn_tick_kernel(const AttnParams p) {
           const uint64_t prow = uint64_t(uint32_t(pid)) * uint32_t(u.P) + off;
           kr = reinterpret_cast<uint64_t>(u.k_pool + prow * u.krow_bytes);
           vr = reinterpret_cast<uint64_t>(u.v_pool + prow * u.row_bytes);
+          if constexpr (kV8) {  // the tile's transposed block of D x 64 bytes
+            const int64_t vt = (int64_t(pid) * p.spp + int(off / uint32_t(KT))) * u.H + h;
+            vr = reinterpret_cast<uint64_t>(reinterpret_cast<const char*>(p.v_pool) + vt * (D * KT));
+            tile_vexp[t] = p.v_exp[vt];
+          }
           if constexpr (kF8) {
             const float ks =
                 p.k_scale[(int64_t(pid) * p.spp + int(off / uint32_t(KT))) * u.H + h];
@@ -697,7 +721,10 @@ attn_tick_kernel(const AttnParams p) {
     // themselves so that the compiler knows which LDS objects they touch)
     const uint32_t k_lane = kF8 ? uint32_t(krow0 * D + (((2 * g) ^ kswz8(krow0)) << 4))
                                 : uint32_t(krow0 * D * 2 + ((g ^ kx) << 4));
-    const uint32_t v_lane = uint32_t(vrow * D * 2 + ((vcx ^ vx) << 4) + vsub * 2);
+    // (8-bit values: row r of the transposed tile, logical chunks 2g, 2g + 1,
+    // swizzled with v8swz; the second chunk is the base XOR 16)
+    const uint32_t v_lane = kV8 ? uint32_t(r * 64 + (((2 * g) ^ v8swz(r)) << 4))
+                                : uint32_t(vrow * D * 2 + ((vcx ^ vx) << 4) + vsub * 2);
     const char* const k_bytes = reinterpret_cast<const char*>(k_tiles);
     const char* const v_bytes = reinterpret_cast<const char*>(v_tiles);
 
@@ -735,6 +762,7 @@ attn_tick_kernel(const AttnParams p) {
 
     f32x16 sacc[2];
     bf16x8 pb[4];
+    i32x8 pb8;  // 8-bit values: P of the tile as e4m3 codes (byte j = score register j)
     float ks_next = 1.f;  // 8-bit tier: key scale of the tile whose scores are in sacc
 
     // 8-bit K operand op = 2*dh + blk of K tile buffer kbuf: rows of 32-key block
@@ -744,6 +772,15 @@ attn_tick_kernel(const AttnParams p) {
                          (op & 1) * (32 * D);
       const i32x4 lo = *reinterpret_cast<const i32x4*>(k_bytes + a);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(k_bytes + (a ^ 16u));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // 8-bit V^T operand of 32-channel block db of V tile buffer vbuf: row
+    // 32*db + r of the transposed tile, bytes 32*g .. +31 (two 16-byte reads;
+    // vl: this lane's base)
+    auto vload8 = [&](uint32_t vl, int vbuf, int db) __attribute__((always_inline)) {
+      const uint32_t a = vl + vbuf * uint32_t(KT * D * VB) + db * (32 * 64);
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(v_bytes + a);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(v_bytes + (a ^ 16u));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto mfma8 = [&](const i32x8& a, const i32x8& b, const f32x16& c)
@@ -813,10 +850,21 @@ attn_tick_kernel(const AttnParams p) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const float ev = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x], ce, -m_run));
-            part[x & 3] += ev;
-            pb[2 * blk + (x >> 3)][x & 7] = static_cast<__bf16>(ev);
+          for (int x = 0; x < 16; x += 4) {
+            float ev[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ev[i] = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x + i], ce, -m_run));
+              part[i] += ev[i];
+            }
+            if constexpr (kV8) {  // e4m3 P (at most 2^kLazyTau, inside the range)
+              int w = __builtin_amdgcn_cvt_pk_fp8_f32(ev[0], ev[1], 0, false);
+              pb8[4 * blk + x / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(ev[2], ev[3], w, true);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                pb[2 * blk + (x >> 3)][(x & 7) + i] = static_cast<__bf16>(ev[i]);
+            }
           }
         lsum = (part[0] + part[1]) + (part[2] + part[3]);
       };
@@ -877,7 +925,29 @@ attn_tick_kernel(const AttnParams p) {
       // them inside the slot instead of being kept in registers across the loop
       uint32_t kl = k_lane, vl = v_lane;
       asm volatile("" : "+v"(kl), "+v"(vl));
-      if constexpr (kF8) {
+      if constexpr (kV8) {
+        // four e4m3 P.V MFMAs (one per 32-channel block of O^T, the tile's
+        // power-of-two V scale applied by the MFMA) alternating with the four
+        // 8-bit Q.K^T ones; K operands two steps ahead, V one
+        ks_next = tile_scale[jn < ntiles ? jn : 0];
+        const int ve = tile_vexp[jn - 1 < ntiles ? jn - 1 : 0];
+        sacc[0] = f32x16{};
+        sacc[1] = f32x16{};
+        i32x8 ka[3], va[2];
+        ka[0] = kload8(kl, kbuf, 0);
+        ka[1] = kload8(kl, kbuf, 1);
+        va[0] = vload8(vl, vbuf, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t + 2 < 4) ka[(t + 2) % 3] = kload8(kl, kbuf, t + 2);
+          if (t + 1 < 4) va[(t + 1) & 1] = vload8(vl, vbuf, t + 1);
+          oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[t & 1], pb8, oacc[t], 0, 0,
+                                                                     0, ve, 0, 127);
+          sacc[t & 1] = mfma8(ka[t % 3], qf8[t >> 1], sacc[t & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else if constexpr (kF8) {
         // four 16-key P.V steps (four MFMAs each), each followed by one of the
         // four 8-bit Q.K^T MFMAs (blocks alternate, so no two in a row share an
         // accumulator); K operands two steps ahead, V one
@@ -979,9 +1049,11 @@ attn_tick_kernel(const AttnParams p) {
       if (wave_active) {
         softmax(js, kF8 ? cq * ks_next : cq);
         __builtin_amdgcn_sched_barrier(0);
-        uint32_t vl = v_lane;
-        asm volatile("" : "+v"(vl));
-        vload(vl, vnext, 0, vpre);
+        if constexpr (!kV8) {
+          uint32_t vl = v_lane;
+          asm volatile("" : "+v"(vl));
+          vload(vl, vnext, 0, vpre);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       end_s_slot();
@@ -1251,9 +1323,9 @@ bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, AttnParams& p
 
 // kFast: every tile is one uniform span of a page or live chunk (page size a
 // multiple of 64, or no history); otherwise history tiles resolve per lane.
-template <int D, bool kFast, bool kF8 = false>
+template <int D, bool kFast, bool kF8 = false, bool kV8 = false>
 int32_t launch_attn(const AttnParams& p, unsigned blocks, hipStream_t stream) {
-  attn_tick_kernel<D, kFast, kF8><<<dim3(blocks), NTHREADS, 0, stream>>>(p);
+  attn_tick_kernel<D, kFast, kF8, kV8><<<dim3(blocks), NTHREADS, 0, stream>>>(p);
   return WF_OK;
 }
 
@@ -1281,6 +1353,10 @@ int32_t validate_tick(const wf_tick_desc* d) {
                   d->hist_first[s], d->n_hist);
   if (d->k_format != WF_K_BF16 && d->k_format != WF_K_E4M3)
     return fail(WF_EINVAL, "wf_attn_tick: k_format = %d (WF_K_BF16 or WF_K_E4M3)", d->k_format);
+  if (d->v_format != WF_V_BF16 && d->v_format != WF_V_E4M3)
+    return fail(WF_EINVAL, "wf_attn_tick: v_format = %d (WF_V_BF16 or WF_V_E4M3)", d->v_format);
+  if (d->v_format == WF_V_E4M3 && d->k_format != WF_K_E4M3)
+    return fail(WF_EINVAL, "wf_attn_tick: 8-bit values need 8-bit keys (k_format = WF_K_E4M3)");
   if (d->k_format == WF_K_E4M3) {
     if (d->D != 128)
       return fail(WF_EUNSUPPORTED, "wf_attn_tick: 8-bit keys need D = 128 (D = %d)", d->D);
@@ -1296,6 +1372,8 @@ int32_t validate_tick(const wf_tick_desc* d) {
       return fail(WF_EINVAL, "wf_attn_tick: store_pages writes bf16 pages: not with 8-bit keys");
     if (!d->k_scale || (reinterpret_cast<uintptr_t>(d->k_scale) & 3u))
       return fail(WF_EINVAL, "wf_attn_tick: 8-bit keys need k_scale (4-byte aligned)");
+    if (d->v_format == WF_V_E4M3 && !d->v_exp)
+      return fail(WF_EINVAL, "wf_attn_tick: 8-bit values need v_exp");
   }
   if (!d->q || !d->o || (!live_paged && (!d->k || !d->v)))
     return fail(WF_EINVAL, "wf_attn_tick: q, o (and k, v without live_pages) must be non-NULL");
@@ -1475,6 +1553,8 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
     p.n_hist = d.n_hist;
     const bool f8 = d.k_format == WF_K_E4M3;
     p.k_scale = f8 ? d.k_scale : nullptr;
+    const bool v8 = f8 && d.v_format == WF_V_E4M3;
+    p.v_exp = v8 ? d.v_exp : nullptr;
     p.spp = f8 ? d.P / KT : 0;
     p.T = d.T;
     p.H = d.H;
@@ -1508,7 +1588,9 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
       return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %d", p.n_page_ids,
                   kMaxPageIds);
     }
-    if (f8)  // (validated: D = 128, P a multiple of 64, so fast)
+    if (v8)  // (validated: D = 128, P a multiple of 64, so fast)
+      st = launch_attn<128, true, true, true>(p, unsigned(blocks), stream);
+    else if (f8)
       st = launch_attn<128, true, true>(p, unsigned(blocks), stream);
     else if (d.D == 128)
       st = fast ? launch_attn<128, true>(p, unsigned(blocks), stream)

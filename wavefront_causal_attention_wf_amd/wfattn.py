@@ -50,11 +50,13 @@ class WfTickDesc(ctypes.Structure):
                 ("k_pool", _vp), ("v_pool", _vp), ("num_pages", _i32), ("P", _i32),
                 ("hist_pages", _vp), ("n_hist", _i32), ("hist_first", _i32 * MAX_STAGES),
                 ("live_pages", _vp), ("store_pages", _vp),
-                ("k_format", _i32), ("k_scale", _vp)]
+                ("k_format", _i32), ("k_scale", _vp), ("v_format", _i32), ("v_exp", _vp)]
 
 
 K_BF16 = 0
 K_E4M3 = 1
+V_BF16 = 0
+V_E4M3 = 1
 
 
 class WfRopeDesc(ctypes.Structure):
@@ -78,8 +80,8 @@ _lib.wf_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
 _lib.wf_gather_paged.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
 _lib.wf_rope_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      ctypes.POINTER(WfRopeDesc), _vp]
-_lib.wf_store_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                    _vp]
+_lib.wf_store_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                    _i32, _vp]
 _lib.wf_attn_tick.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
 _lib.wf_tick_useful_flops.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_double)]
 _lib.wf_tick_work_order.argtypes = [ctypes.POINTER(WfTickDesc), _i32, _i32p, ctypes.c_int64,
@@ -232,13 +234,20 @@ def wf_gather_paged(k_pool, v_pool, page_ids, k_dst, v_dst, stream=None) -> None
                                 _stream(stream)), "wf_gather_paged")
 
 
-def wf_store_paged_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=None) -> None:
+def wf_store_paged_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=None,
+                       v_exp=None) -> None:
     """One chunk's K/V [T][H][D] (bf16) into the 8-bit tier's pages: K as e4m3
     codes in k_pool (uint8 [num_pages][P][H][D]) with fp32 scales in k_scale
-    ([num_pages][P/64][H]), V copied into v_pool (bf16 [num_pages][P][H][D])."""
+    ([num_pages][P/64][H]); V copied into v_pool (bf16 [num_pages][P][H][D]),
+    or with v_exp (uint8 [num_pages][P/64][H]) quantised into v_pool (uint8
+    [num_pages][P/64][H][D][64], transposed tiles)."""
     import torch
-    for n, t in (("k_src", k_src), ("v_src", v_src), ("v_pool", v_pool)):
+    for n, t in (("k_src", k_src), ("v_src", v_src)):
         _check_bf16(n, t)
+    if v_exp is None:
+        _check_bf16("v_pool", v_pool)
+    elif v_pool.dtype != torch.uint8 or v_exp.dtype != torch.uint8:
+        raise TypeError("with v_exp, v_pool and v_exp must be uint8 tensors")
     if k_pool.dtype != torch.uint8 or not k_pool.is_contiguous():
         raise TypeError("k_pool must be a contiguous uint8 tensor of e4m3 codes")
     if k_scale.dtype != torch.float32 or not k_scale.is_contiguous():
@@ -246,8 +255,8 @@ def wf_store_paged_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=N
     T, H, D = k_src.shape
     num_pages, P = k_pool.shape[0], k_pool.shape[1]
     _check(_lib.wf_store_paged_fp8(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(k_scale),
-                                   _ptr(v_pool), _ptr(page_ids), T, H, D, num_pages, P,
-                                   _stream(stream)), "wf_store_paged_fp8")
+                                   _ptr(v_pool), _ptr(v_exp), _ptr(page_ids), T, H, D, num_pages,
+                                   P, _stream(stream)), "wf_store_paged_fp8")
 
 
 def default_rope_split(D: int):
@@ -292,7 +301,8 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
                    q=None, k=None, v=None, o=None, k_pool=None, v_pool=None,
                    num_pages: int = 0, P: int = 0, hist_pages=None, n_hist: int = 0,
                    hist_first: Optional[Sequence[int]] = None,
-                   live_pages=None, store_pages=None, k_scale=None) -> WfTickDesc:
+                   live_pages=None, store_pages=None, k_scale=None,
+                   v_exp=None) -> WfTickDesc:
     d = WfTickDesc()
     d.S, d.active_mask, d.T, d.H, d.D, d.scale = S, active_mask, T, H, D, scale
     d.q, d.k, d.v, d.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
@@ -306,19 +316,24 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
     d.store_pages = _ptr(store_pages)
     d.k_format = K_BF16 if k_scale is None else K_E4M3
     d.k_scale = _ptr(k_scale)
+    d.v_format = V_BF16 if v_exp is None else V_E4M3
+    d.v_exp = _ptr(v_exp)
     return d
 
 
 def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None, v_pool=None,
                  hist_pages=None, hist_first: Optional[Sequence[int]] = None,
-                 stream=None, live_pages=None, store_pages=None, k_scale=None) -> None:
+                 stream=None, live_pages=None, store_pages=None, k_scale=None,
+                 v_exp=None) -> None:
     """One tick: q, k, v, o [S+1][T][H][D]; pools [num_pages][P][H][D];
     hist_pages int32 [n_hist][ceil(T/P)] on the device; live_pages (optional)
     int32 [S+1][ceil(T/P)] on the device: live K/V read from those pages (k and
     v may then be None); store_pages (optional) int32 [ceil(T/P)] on the device:
     the same launch writes the store chunk's K/V into those pages. k_scale
     (optional, float32 [num_pages][P/64][H]): the 8-bit tier — k_pool holds
-    e4m3 codes (uint8) as written by wf_store_paged_fp8, live_pages required."""
+    e4m3 codes (uint8) as written by wf_store_paged_fp8, live_pages required.
+    v_exp (optional, uint8 [num_pages][P/64][H], with k_scale): 8-bit values —
+    v_pool holds the transposed e4m3 tiles written by wf_store_paged_fp8."""
     for n, t in (("q", q), ("o", o)) + ((("k", k), ("v", v)) if live_pages is None else ()):
         _check_bf16(n, t)
     _, T, H, D = q.shape
@@ -332,11 +347,14 @@ def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None
             _check_bf16("k_pool", k_pool)
         elif str(k_pool.dtype) != "torch.uint8" or not k_pool.is_contiguous():
             raise TypeError("with k_scale, k_pool must be a contiguous uint8 tensor of e4m3 codes")
-        _check_bf16("v_pool", v_pool)
+        if v_exp is None:
+            _check_bf16("v_pool", v_pool)
+        elif str(v_pool.dtype) != "torch.uint8" or not v_pool.is_contiguous():
+            raise TypeError("with v_exp, v_pool must be a contiguous uint8 tensor of e4m3 codes")
     d = make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
                        k_pool if pooled else None, v_pool if pooled else None, num_pages, P,
                        hist_pages if n_hist else None, n_hist, hist_first, live_pages,
-                       store_pages, k_scale)
+                       store_pages, k_scale, v_exp)
     _check(_lib.wf_attn_tick(ctypes.byref(d), _stream(stream)), "wf_attn_tick")
 
 
