@@ -412,8 +412,9 @@ def test_useful_flops_matches_oracle(name):
 
 
 def test_tick_validation_fp8_keys():
-    """The 8-bit tier: k_format must be known; e4m3 keys need D = 128, P a
-    multiple of 64, live_pages, k_scale (4-byte aligned) and no fused store."""
+    """The 8-bit tier: k_format and v_format must be known; e4m3 keys need D =
+    128, P a multiple of 64, live_pages, k_scale (4-byte aligned) and no fused
+    store; e4m3 values need e4m3 keys and v_exp."""
     wf = _wfattn()
     fake = 1 << 20
 
@@ -432,6 +433,18 @@ def test_tick_validation_fp8_keys():
         d.k_scale = scale
         return d
 
+    def desc_v(v_format, k_format=None, v_exp=fake):
+        d = desc() if k_format is None else desc(k_format=k_format)
+        d.v_format = v_format
+        d.v_exp = v_exp
+        return d
+
+    for d, code in ((desc_v(2), "EINVAL"),                        # unknown value format
+                    (desc_v(1, k_format=0), "EINVAL"),            # 8-bit values need 8-bit keys
+                    (desc_v(1, v_exp=None), "EINVAL")):           # 8-bit values need v_exp
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_attn_tick_desc(d, stream=0)
+        assert e.value.status == CODES[code], wf.last_error()
     for d, code in ((desc(k_format=2), "EINVAL"),
                     (desc(D=64), "EUNSUPPORTED"),
                     (desc(P=16), "EINVAL"),
