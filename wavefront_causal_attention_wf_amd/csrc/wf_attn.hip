@@ -742,7 +742,7 @@ attn_tick_kernel(const AttnParams p) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds1, v_lds1, wave);
     resolve();
-    const bool grp_a = wave < NWAVES / 2;
+    const bool grp_a = wave < NWAVES / 2 && !kV8;
     if (!grp_a) {  // B: tile 2 as well (A issues it in its first softmax slot)
 #pragma unroll
       for (int i = 0; i < NI; ++i) ld.emit(i, u, k_lds2, v_lds2, wave);
@@ -832,7 +832,7 @@ attn_tick_kernel(const AttnParams p) {
     // Register x of block blk holds key 32*blk + 16*(x>>3) + 8*g + (x&7).
     // ce: the scores' multiplier (softmax scale * log2 e, times the query and
     // key scales in the 8-bit tier).
-    auto softmax = [&](int j, float ce) __attribute__((always_inline)) {
+    auto softmax = [&](int j, float ce, f32x16* sc) __attribute__((always_inline)) {
       const int valid = valid_keys(j);
       if (valid < KT) {
 #pragma unroll
@@ -840,7 +840,7 @@ attn_tick_kernel(const AttnParams p) {
 #pragma unroll
           for (int x = 0; x < 16; ++x) {
             const int key = 32 * blk + 16 * (x >> 3) + 8 * g + (x & 7);
-            if (key >= valid) sacc[blk][x] = -INFINITY;
+            if (key >= valid) sc[blk][x] = -INFINITY;
           }
       }
       // P = 2^(c s - m_run) (bf16 for the P.V product) and this lane's fp32 sum
@@ -854,7 +854,7 @@ attn_tick_kernel(const AttnParams p) {
             float ev[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              ev[i] = __builtin_amdgcn_exp2f(fmaf(sacc[blk][x + i], ce, -m_run));
+              ev[i] = __builtin_amdgcn_exp2f(fmaf(sc[blk][x + i], ce, -m_run));
               part[i] += ev[i];
             }
             if constexpr (kV8) {  // e4m3 P (at most 2^kLazyTau, inside the range)
@@ -875,11 +875,11 @@ attn_tick_kernel(const AttnParams p) {
       // that out without computing the max (the first tile, against -inf, always
       // takes the check).
       if (__builtin_amdgcn_ballot_w64(!(lsum <= kLazyBound)) != 0) {
-        float mx = sacc[0][0];
+        float mx = sc[0][0];
 #pragma unroll
-        for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sacc[0][x]);
+        for (int x = 1; x < 16; ++x) mx = fmaxf(mx, sc[0][x]);
 #pragma unroll
-        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[1][x]);
+        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sc[1][x]);
         mx = xlane32_max(mx) * ce;
         const bool raise = mx > m_run + kLazyTau;
         if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -1047,7 +1047,7 @@ attn_tick_kernel(const AttnParams p) {
       resolve();  // the tile this wave loads next
       __builtin_amdgcn_sched_barrier(0);
       if (wave_active) {
-        softmax(js, kF8 ? cq * ks_next : cq);
+        softmax(js, kF8 ? cq * ks_next : cq, sacc);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (!kV8) {
           uint32_t vl = v_lane;
@@ -1059,6 +1059,63 @@ attn_tick_kernel(const AttnParams p) {
       end_s_slot();
     };
 
+    if constexpr (kV8) {
+      // 8-bit K/V: the softmax, not the MFMA, bounds this tier, so instead of
+      // the ping-pong every wave runs both phases, both waves of a SIMD in step:
+      // tile j's iteration issues tile j+3's loads, the 8-bit Q.K^T of tile
+      // j+1 (into the other score registers), the softmax of tile j while
+      // those MFMAs run, then P.V of tile j; the two waves of a SIMD share its
+      // VALU (which issues faster for two waves than for one) and overlap each
+      // other's MFMAs. Tile t is in buffer t % 4; the barrier opening iteration
+      // j waits for this wave's loads of tile j+1 (those of tile j+2 may still
+      // be in flight) and for every wave to have finished iteration j-1, whose
+      // reads were the last of buffer (j+3) % 4.
+      f32x16 s0[2], s1[2];
+      auto step = [&](int j, int kbuf, int vbuf, uint16_t* kn, uint16_t* vn, f32x16* sc,
+                      f32x16* sn) __attribute__((always_inline)) {
+        tile_barrier<LPT>();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
+        resolve();
+        __builtin_amdgcn_sched_barrier(0);
+        if (wave_active) {
+          uint32_t kl = k_lane, vl = v_lane;
+          asm volatile("" : "+v"(kl), "+v"(vl));
+          const int jj = j < ntiles ? j : 0;
+          const float ks = tile_scale[jj];
+          const int ve = tile_vexp[jj];
+          i32x8 ka[4], va[4];
+#pragma unroll
+          for (int op = 0; op < 4; ++op) ka[op] = kload8(kl, kbuf, op);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) va[db] = vload8(vl, vbuf, db);
+          sn[0] = f32x16{};
+          sn[1] = f32x16{};
+#pragma unroll
+          for (int op = 0; op < 4; ++op) sn[op & 1] = mfma8(ka[op], qf8[op >> 1], sn[op & 1]);
+          softmax(j, cq * ks, sc);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db], pb8, oacc[db], 0,
+                                                                       0, 0, ve, 0, 127);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if (wave_active) {  // Q.K^T of tile 0 (tile 0 has landed)
+        uint32_t kl = k_lane;
+        asm volatile("" : "+v"(kl));
+        s0[0] = f32x16{};
+        s0[1] = f32x16{};
+#pragma unroll
+        for (int op = 0; op < 4; ++op) s0[op & 1] = mfma8(kload8(kl, 0, op), qf8[op >> 1], s0[op & 1]);
+      }
+      for (int j = 0; j < ntiles; j += 4) {
+        step(j, 1, 0, k_lds3, v_lds3, s0, s1);
+        step(j + 1, 2, 1, k_lds0, v_lds0, s1, s0);
+        step(j + 2, 3, 2, k_lds1, v_lds1, s0, s1);
+        step(j + 3, 0, 3, k_lds2, v_lds2, s1, s0);
+      }
+    } else {
     if (wave_active) qk(0);
     end_qk_slot();  // B (end of slot 1): tile 1 has landed (tile 2 may be in flight)
     // S(0): A loads tile 2, B tile 3; G(0) reads V of tile 0
@@ -1085,6 +1142,7 @@ attn_tick_kernel(const AttnParams p) {
       slot_pair(j + 1, 1, 2, k_lds0, v_lds0, k_lds1, v_lds1);
       slot_pair(j + 2, 2, 3, k_lds1, v_lds1, k_lds2, v_lds2);
       slot_pair(j + 3, 3, 0, k_lds2, v_lds2, k_lds3, v_lds3);
+    }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
 
