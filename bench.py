@@ -693,7 +693,7 @@ def main():
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
     achieved = flops / (attn_ms.mean() * 1e-3) / 1e12
     out = {
-        "metric": "wave-attn TFLOP/s (useful) + ticks/s, % bf16 MFMA peak, 1xMI355X",
+        "metric": "wave-attn TFLOP/s (useful) + ticks/s, % bf16 MFMA peak, 1\u00d7MI355X",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
