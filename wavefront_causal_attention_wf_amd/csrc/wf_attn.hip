@@ -925,29 +925,7 @@ attn_tick_kernel(const AttnParams p) {
       // them inside the slot instead of being kept in registers across the loop
       uint32_t kl = k_lane, vl = v_lane;
       asm volatile("" : "+v"(kl), "+v"(vl));
-      if constexpr (kV8) {
-        // four e4m3 P.V MFMAs (one per 32-channel block of O^T, the tile's
-        // power-of-two V scale applied by the MFMA) alternating with the four
-        // 8-bit Q.K^T ones; K operands two steps ahead, V one
-        ks_next = tile_scale[jn < ntiles ? jn : 0];
-        const int ve = tile_vexp[jn - 1 < ntiles ? jn - 1 : 0];
-        sacc[0] = f32x16{};
-        sacc[1] = f32x16{};
-        i32x8 ka[3], va[2];
-        ka[0] = kload8(kl, kbuf, 0);
-        ka[1] = kload8(kl, kbuf, 1);
-        va[0] = vload8(vl, vbuf, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (t + 2 < 4) ka[(t + 2) % 3] = kload8(kl, kbuf, t + 2);
-          if (t + 1 < 4) va[(t + 1) & 1] = vload8(vl, vbuf, t + 1);
-          oacc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[t & 1], pb8, oacc[t], 0, 0,
-                                                                     0, ve, 0, 127);
-          sacc[t & 1] = mfma8(ka[t % 3], qf8[t >> 1], sacc[t & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else if constexpr (kF8) {
+      if constexpr (kF8) {
         // four 16-key P.V steps (four MFMAs each), each followed by one of the
         // four 8-bit Q.K^T MFMAs (blocks alternate, so no two in a row share an
         // accumulator); K operands two steps ahead, V one
@@ -1049,11 +1027,9 @@ attn_tick_kernel(const AttnParams p) {
       if (wave_active) {
         softmax(js, kF8 ? cq * ks_next : cq, sacc);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!kV8) {
-          uint32_t vl = v_lane;
-          asm volatile("" : "+v"(vl));
-          vload(vl, vnext, 0, vpre);
-        }
+        uint32_t vl = v_lane;
+        asm volatile("" : "+v"(vl));
+        vload(vl, vnext, 0, vpre);
       }
       __builtin_amdgcn_sched_barrier(0);
       end_s_slot();
