@@ -647,8 +647,8 @@ def main():
         print(attn_kernel_hash())
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the sharding design is described in DESIGN.md)"}))
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1 "
+                                   "(the tick is not sharded across GPUs)"}))
         sys.exit(2)
     import torch
 

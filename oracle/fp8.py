@@ -7,7 +7,7 @@ The pages name K/V quantisation as a way to shrink K/V payloads and an 8-bit
 attention backend (SageAttention) for local computation ([full text] §4.3,
 §5 "Compute configurations"), and measure FP8 K/V collectives at about half
 the bf16 time (Appendix C.5, Table 8; C.6). They give neither the 8-bit
-format nor the quantisation granularity. Readings (listed in the design doc):
+format nor the quantisation granularity. Readings taken here:
   * format: e4m3 (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
     no infinities; largest finite value 448; exponent field 0 holds the
     subnormals m * 2^-9);
@@ -199,7 +199,7 @@ def attention_tick_fp8(q_bits, store: "Fp8PageStore", hist_pages, live_pages, S:
 # ----------------------------------------------------------------------------
 # 8-bit values (the tier where V is e4m3 too)
 # ----------------------------------------------------------------------------
-# Reading (DESIGN.md): V is quantised per (64-token tile, head) with a
+# Reading: V is quantised per (64-token tile, head) with a
 # power-of-two scale 2^e, e the smallest integer with amax <= 448 * 2^e (so the
 # scale is an 8-bit exponent and the codes are e4m3 of v * 2^-e, a product
 # that is exact in float32), e = 0 for an all-zero tile. P is rounded to e4m3

@@ -10,7 +10,7 @@ What the pages fix ([full text] §4.2, Appendix B.3 and B.8, Eq. (13)):
     second broadcast), and the bounded window drops the oldest chunk; the
     first clean chunk may be kept as a persistent anchor.
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
   * a page holds P consecutive tokens of one chunk, all heads: [P][H][D]; a
     chunk owns ceil(T/P) whole pages and the slots past token T-1 of its last
     page are zero, so page contents are fully determined;

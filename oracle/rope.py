@@ -16,7 +16,7 @@ What the pages fix:
     that RoPE can be applied again when the bounded window shifts; every other
     page keeps the rotated keys it was written with ([full text] Appendix B.3).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * rotary form: channel pair (2i, 2i+1) of a head vector is turned by the
     angle a = coordinate * frequency: (x0, x1) -> (x0 cos a - x1 sin a,
     x0 sin a + x1 cos a);

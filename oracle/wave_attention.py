@@ -9,7 +9,7 @@ Generation":
   [summary]   the structured summary page (picx.dev), section "Methodology";
   [full text] the full-text page (paperpeel.com), with section / equation.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * the store chunk is stage S of the tick and is an active chunk like the
     others; the wave mask 1[j >= s] therefore gives every denoising stage the
     live store, and the store sees only itself among live chunks;
