@@ -72,7 +72,8 @@ __device__ __forceinline__ int v8_column(int t) {
 // head h -> codes and scale, and (bf16 values) its values of head h copied;
 // z = 1 (8-bit values only): its values of head h -> codes in the transposed
 // tile and the exponent. One thread owns UPT 16-byte units (8 channels of one
-// token), all loaded before any store.
+// token), all loaded before any store; bf16 values are copied before the
+// block's amax reduction.
 template <int D>
 __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
     const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint8_t* __restrict__ k_pool,
@@ -110,6 +111,11 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
     const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) am = fmaxf(am, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  }
+  // bf16 values need no scale: their copy drains while the block reduces
+  if (!v8) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) store_stream16(v_pool + dst_row[u], vx[u]);
   }
   // block max: within each wave, then across the four waves
 #pragma unroll
@@ -150,7 +156,6 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
     const v2u codes = {e4m3x4(x[u].x, x[u].y, inv), e4m3x4(x[u].z, x[u].w, inv)};
     // unit (16 bytes of bf16) -> 8 bytes of codes at half the offset
     __builtin_nontemporal_store(codes, reinterpret_cast<v2u*>(k_pool + dst_row[u] * 8));
-    if (!v8) store_stream16(v_pool + dst_row[u], vx[u]);
   }
 }
 
