@@ -151,11 +151,17 @@ def test_fp8_tick_matches_oracle(S, T, H, P, n_hist, mask, q_gain):
     say(f"  worst rel-L2 {worst:.2e}")
 
 
-def test_fp8_tick_full_size_sampled_rows():
-    """The Wan-1.3B-like 4-step tick in the 8-bit tier, as the bench times it:
+# wan13_4step runs the packed per-CU work order; wan14b_4step (H = 40) has too
+# many items for it and runs whole (stage, head) groups dealt to XCDs
+FULL_SIZE = ["wan13_4step", "wan14b_4step"]
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_fp8_tick_full_size_sampled_rows(name):
+    """Full-size 4-step ticks in the 8-bit tier, as the bench times them:
     three history chunks and five live chunks in 8-bit pages, sampled rows of
     every stage and head against the oracle."""
-    cfg = inputs.CONFIGS["wan13_4step"]
+    cfg = inputs.CONFIGS[name]
     say(f"[full-size fp8] S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist}")
     ppc = cfg.ppc
     pg = Fp8Pages(cfg.num_pages, cfg.P, cfg.H, cfg.D)
@@ -336,8 +342,9 @@ def test_fp8kv_tick_within_p_bound(S, T, H, P, n_hist, mask):
     say(f"  worst |error| / allowance {r:.3f}")
 
 
-def test_fp8kv_tick_full_size_sampled_rows():
-    cfg = inputs.CONFIGS["wan13_4step"]
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_fp8kv_tick_full_size_sampled_rows(name):
+    cfg = inputs.CONFIGS[name]
     say(f"[full-size fp8 K/V] S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist}")
     ppc = cfg.ppc
     pg = Fp8KvPages(cfg.num_pages, cfg.P, cfg.H, cfg.D)
