@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(const RopePara
   const int64_t pid = p.page_ids[page];
   const bool is_v = blockIdx.z != 0;
   uint4* dst = (is_v ? p.v_pool : p.k_pool) + ((pid * p.P + slot) * H + h0) * U + u;
-  uint4 x[kRopeHeads];
+  uint4 x[kRopeHeads] = {};  // (heads past H stay zero: rotated, never stored)
   if (t >= p.T) {  // tail slot of the last page
 #pragma unroll
     for (int i = 0; i < kRopeHeads; ++i)
