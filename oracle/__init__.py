@@ -18,7 +18,9 @@ from the Wave Forcing pages:
   * fp8: the 8-bit tier's e4m3 encoding and decoding, per-group float32
     scales (queries per row, keys per 64-token tile and head), power-of-two
     scales for 8-bit values, 8-bit page stores, the tick over the dequantised
-    values and the bound on what rounding P to e4m3 can change.
+    values, the worst-case bound on what rounding P to e4m3 can change, and
+    the rel-L2 criterion of the 8-bit K/V tick derived from that rounding's
+    statistics.
 
 Parity status: every function is pinned by the `-m "not gpu"` tests in
 tests/test_oracle_pins.py, tests/test_page_model.py, tests/test_rope_oracle.py and
@@ -67,4 +69,7 @@ from .fp8 import (  # noqa: F401
     Fp8KvPageStore,
     attention_tick_fp8kv,
     p_error_bound,
+    p_rounding_rms,
+    p_rounding_terms,
+    kv8_l2_allowance,
 )

@@ -16,7 +16,8 @@ format nor the quantisation granularity. Readings taken here:
   * scales: one float32 scale per (64-token tile, head) for K and per (query
     row, head) for Q: amax = max |x| over the group (float32, exact for bf16
     inputs), scale = amax / 448, inv = 448 / amax (both float32 divisions;
-    inv = scale = 0 for an all-zero group), code = e4m3 of float32(x * inv)
+    inv = scale = 0 for an all-zero group, and for a group with amax below
+    2^-100, TINY_AMAX), code = e4m3 of float32(x * inv)
     rounded to nearest, ties to even; the value a code stands for is
     decode(code) * scale;
   * scores are the products of the dequantised Q and K; everything after the
@@ -29,6 +30,15 @@ from typing import Tuple
 import numpy as np
 
 E4M3_MAX = 448.0
+# Groups of queries or keys whose amax lies below 2^-100 are stored as zero
+# (scale 0, zero codes). Below about 2^-119, 448 / amax would exceed the largest
+# float32, and between the two the scale amax / 448 would fall among float32's
+# subnormals; the values such a group carries are below 2^-100 in any case.
+TINY_AMAX = 2.0 ** -100
+# The exponent of a power-of-two value scale is an E8M0 byte (e + 127), so
+# e >= -127; tiles with amax below 448 * 2^-128 take e = -127 and are still
+# scaled exactly (their codes are e4m3 of v * 2^127, below 448).
+E8M0_MIN = -127
 
 
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
@@ -72,12 +82,15 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
 def quantize_groups(x: np.ndarray, axes) -> Tuple[np.ndarray, np.ndarray]:
     """Quantise x (values; bf16 bit patterns must be decoded first) with one
     scale per group, reducing over `axes` (the other axes index the groups).
-    Returns (codes uint8 like x, scales float32 with the reduced axes kept as 1)."""
+    Returns (codes uint8 like x, scales float32 with the reduced axes kept as 1).
+    A group whose amax is below TINY_AMAX is stored as all-zero (scale 0, zero
+    codes), as a group of zeros is."""
     xf = np.asarray(x, dtype=np.float32)
     amax = np.max(np.abs(xf), axis=axes, keepdims=True).astype(np.float32)
-    safe = np.where(amax > 0, amax, np.float32(1))
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
-    inv = np.where(amax > 0, np.float32(E4M3_MAX) / safe, np.float32(0)).astype(np.float32)
+    big = amax >= np.float32(TINY_AMAX)
+    safe = np.where(big, amax, np.float32(1))
+    scale = np.where(big, amax / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
+    inv = np.where(big, np.float32(E4M3_MAX) / safe, np.float32(0)).astype(np.float32)
     y = (xf * inv).astype(np.float32)       # float32 product, rounded once
     return e4m3_encode(y), scale
 
@@ -203,19 +216,21 @@ def attention_tick_fp8(q_bits, store: "Fp8PageStore", hist_pages, live_pages, S:
 # power-of-two scale 2^e, e the smallest integer with amax <= 448 * 2^e (so the
 # scale is an 8-bit exponent and the codes are e4m3 of v * 2^-e, a product
 # that is exact in float32), e = 0 for an all-zero tile. P is rounded to e4m3
-# (P <= 2^8 under the bf16 tier's lazy reference) for the P.V product; that
-# rounding depends on the kernel's running reference, so the tick is checked
-# against the exact attention of the dequantised values within the bound
-# p_error_bound() gives.
+# (the device keeps every P at most 448) for the P.V product; that rounding
+# depends on the device's running reference, so the tick is checked against the
+# exact attention of the dequantised values: element by element within the
+# worst-case bound p_error_bound() gives, and per (stage, head) in the rel-L2
+# sense within kv8_l2_allowance() of the RMS term p_rounding_rms() gives.
 
 
 def pow2_exponent(amax: np.ndarray) -> np.ndarray:
-    """Smallest integer e with amax <= 448 * 2^e (amax > 0), else 0.
+    """Smallest integer e >= -127 with amax <= 448 * 2^e (amax > 0), else 0.
     amax = f * 2^E with 0.5 <= f < 1 and 448 = 0.875 * 2^9, so e = E - 9 when
-    f <= 0.875 and E - 8 otherwise."""
+    f <= 0.875 and E - 8 otherwise; -127 is the smallest exponent the E8M0
+    scale byte holds."""
     amax = np.asarray(amax, dtype=np.float64)
     f, E = np.frexp(amax)
-    e = np.where(f <= 0.875, E - 9, E - 8)
+    e = np.maximum(np.where(f <= 0.875, E - 9, E - 8), E8M0_MIN)
     return np.where(amax > 0, e, 0).astype(np.int64)
 
 
@@ -285,17 +300,12 @@ def attention_tick_fp8kv(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages
     return attention_tick_fp8(q_bits, store, hist_pages, live_pages, S, active_mask, scale, **kw)
 
 
-def p_error_bound(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: int,
-                  active_mask: int, scale: float, stages=None, heads=None, rows=None):
-    """Per (stage, row, head) bound on |O_device - O_exact| from rounding P to
-    e4m3 alone: with P relative to the row's max (max P = 1), the device's P is
-    that times 2^a for some a in [0, 8] (its running reference lies at most 8
-    below the max, never above), and e4m3 rounds it within 2^-4 of itself or
-    2^-10 absolutely (subnormals), so each P moves by at most
-    max(2^-4 P, 2^-10); the output, a P-weighted mean with the exact sum of P as
-    divisor, moves by at most sum(max(2^-4 P, 2^-10) |v|) / sum(P).
-    Returns {stage: [rows][heads]}."""
-    from .wave_attention import _active, _hf, token_mask, _key_matrix
+def _p_rounding_inputs(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: int,
+                       active_mask: int, scale: float, stages, heads, rows):
+    """For each requested (stage, head): the exact softmax weights P of the
+    dequantised tick relative to each row's max (max P = 1) over the stage's
+    visible keys, and those keys' dequantised values. Yields (s, hi, P, V)."""
+    from .wave_attention import _active, token_mask, _key_matrix
 
     T, H, D = q_bits.shape[1], q_bits.shape[2], q_bits.shape[3]
     rows = np.arange(T) if rows is None else np.asarray(rows)
@@ -312,16 +322,91 @@ def p_error_bound(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: in
     stages = act if stages is None else [s for s in stages if s in act]
     heads = list(range(H)) if heads is None else list(heads)
     n_hist = hk.shape[0]
-    out = {}
     for s in stages:
         m = token_mask(s, S, active_mask, n_hist, T, 0)
-        out[s] = np.zeros((len(rows), len(heads)))
         for hi, h in enumerate(heads):
             K = _key_matrix(lk, hk, h, S)[m]
-            Vabs = np.abs(_key_matrix(lv, hv, h, S)[m])                    # [keys][D]
+            V = _key_matrix(lv, hv, h, S)[m]                               # [keys][D]
             sc = (qv[s, :, h, :] @ K.T) * scale
-            p = np.exp(sc - sc.max(axis=1, keepdims=True))
-            w = np.maximum(2.0 ** -4 * p, 2.0 ** -10)
-            # bound for the worst channel of each row
-            out[s][:, hi] = ((w @ Vabs) / p.sum(axis=1, keepdims=True)).max(axis=1)
-    return out
+            yield s, hi, np.exp(sc - sc.max(axis=1, keepdims=True)), V
+
+
+def _p_rounding_weights(p: np.ndarray) -> np.ndarray:
+    """Largest change of each P (relative to its row's max) when the device
+    rounds it to e4m3 at a reference at or below the row max: the device holds
+    P * 2^a with a >= 0 (its reference is a below the max) and every such value
+    at most 448, inside e4m3's range; a normal e4m3 value (at least 2^-6) is
+    within half a quantum, 2^-4 of itself, of the value it rounds, a subnormal
+    one within 2^-10 absolutely, i.e. 2^-10 * 2^-a <= 2^-10 relative to the max."""
+    return np.maximum(2.0 ** -4 * p, 2.0 ** -10)
+
+
+def p_error_bound(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: int,
+                  active_mask: int, scale: float, stages=None, heads=None, rows=None):
+    """Per (stage, row, head) worst-case bound on |O_device - O_exact| from
+    rounding P to e4m3 alone, for any reference the device may take at or below
+    the row max with every P at most 448 (_p_rounding_weights): each P moves by
+    at most w(P) = max(2^-4 P, 2^-10), so the output, a P-weighted mean with the
+    exact sum of P as divisor, moves by at most sum(w(P) |v|) / sum(P) in every
+    channel. Returns {stage: [rows][heads]} (the worst channel of each row).
+
+    The bound assumes every rounding errs the same way; for near-uniform rows
+    over thousands of keys it exceeds the outputs themselves, so on its own it
+    cannot tell a wrong output from a right one there (p_rounding_rms can)."""
+    return p_rounding_terms(q_bits, store, hist_pages, live_pages, S, active_mask, scale,
+                            stages, heads, rows)[0]
+
+
+# Rel-L2 criterion of the 8-bit K/V tick (per stage and head). The device
+# output differs from the exact attention of the dequantised values by
+#   E = sum_k d_k v_k / sum_k P_k   (d_k: the e4m3 rounding error of P_k)
+# plus bf16 output rounding. Over the many (row, channel) elements of one
+# (stage, head) the roundings of different P act as independent errors of
+# mean near zero, so the squared norm of E concentrates near
+#   sum_rows sum_d sum_k var(d_k) v_kd^2 / (sum_k P_k)^2 .
+# Rounding to nearest gives |d_k| <= w(P_k) (_p_rounding_weights), hence
+# var(d_k) <= w(P_k)^2: R^2 = sum_rows sum_d sum_k w(P_k)^2 v_kd^2 / L^2 bounds
+# that expectation (for a uniformly placed value within its quantum, var =
+# quantum^2 / 12 <= w^2 / 3, so R is at least 1.7x the expected norm), and the
+# criterion allows twice R. What is not independent — the small bias of
+# rounding values spread over a binade (at most ~(quantum / value)^2 / 12 <=
+# 2^-8 / 12 relative) and the bf16 rounding of the output (at most 2^-9
+# relative) — is a fraction of the output itself: 2^-8 of its norm covers both.
+# When one key dominates a row, E is that key's rounding error alone, at most
+# w(P) |v|, which the same 2 R covers with room to spare.
+KV8_RMS_FACTOR = 2.0
+KV8_REL_SLACK = 2.0 ** -8
+
+
+def p_rounding_rms(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: int,
+                   active_mask: int, scale: float, stages=None, heads=None, rows=None):
+    """R per (stage, head) over the given rows (see the criterion above):
+    sqrt(sum over rows and channels of sum_k w(P_k)^2 v_kd^2 / (sum_k P_k)^2).
+    Returns {stage: [heads]}."""
+    return p_rounding_terms(q_bits, store, hist_pages, live_pages, S, active_mask, scale,
+                            stages, heads, rows)[1]
+
+
+def p_rounding_terms(q_bits, store: "Fp8KvPageStore", hist_pages, live_pages, S: int,
+                     active_mask: int, scale: float, stages=None, heads=None, rows=None):
+    """(p_error_bound(...), p_rounding_rms(...)) from one pass over the tick."""
+    T, H = q_bits.shape[1], q_bits.shape[2]
+    n_rows = T if rows is None else len(rows)
+    n_heads = H if heads is None else len(list(heads))
+    bound, rms = {}, {}
+    for s, hi, p, V in _p_rounding_inputs(q_bits, store, hist_pages, live_pages, S, active_mask,
+                                         scale, stages, heads, rows):
+        if s not in bound:
+            bound[s] = np.zeros((n_rows, n_heads))
+            rms[s] = np.zeros(n_heads)
+        w = _p_rounding_weights(p)
+        L = p.sum(axis=1, keepdims=True)
+        bound[s][:, hi] = ((w @ np.abs(V)) / L).max(axis=1)
+        rms[s][hi] = np.sqrt(float((((w * w) @ (V * V)) / (L * L)).sum()))
+    return bound, rms
+
+
+def kv8_l2_allowance(rms: float, exact_norm: float) -> float:
+    """The largest ||O_device - O_exact|| (Frobenius norm over one stage and head)
+    the 8-bit K/V tick may show: KV8_RMS_FACTOR * R + KV8_REL_SLACK * ||O_exact||."""
+    return KV8_RMS_FACTOR * rms + KV8_REL_SLACK * exact_norm

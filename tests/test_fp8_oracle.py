@@ -195,8 +195,11 @@ def test_page_store_matches_contiguous_quantisation():
 
 
 def test_pow2_exponent_closed_forms_and_property():
-    e = fp8.pow2_exponent(np.array([448.0, 449.0, 1.0, 0.875 * 2.0 ** -3, 0.0, 3.5, 2.0 ** -100]))
-    assert e.tolist() == [0, 1, -8, -12, 0, -7, -108]
+    e = fp8.pow2_exponent(np.array([448.0, 449.0, 1.0, 0.875 * 2.0 ** -3, 0.0, 3.5, 2.0 ** -100,
+                                    448.0 * 2.0 ** -127, 449.0 * 2.0 ** -128, 2.0 ** -140, 1e-45]))
+    # (the E8M0 scale byte holds e >= -127: smaller tiles clamp there and their
+    # values times 2^127 still lie below 448)
+    assert e.tolist() == [0, 1, -8, -12, 0, -7, -108, -127, -127, -127, -127]
     rng = np.random.default_rng(21)
     amax = np.exp2(rng.uniform(-20, 20, 5000))
     e = fp8.pow2_exponent(amax)
@@ -303,3 +306,137 @@ def test_fp8kv_tick_reduces_to_bf16_tick_when_exact():
     want = oracle.attention_tick(q, kl, vl, kh, vh, S, mask, 0.125)
     for s in want:
         assert np.array_equal(got[s], want[s])
+
+
+# ---------------------------------------------------------------------------
+# The rel-L2 criterion of the 8-bit K/V tick at the 4-step tick's statistics
+# (4680-token chunks, three history chunks, N(0, 0.5^2) bf16 inputs, one head,
+# sampled query rows): a model of the device that rounds P to e4m3 at any
+# reference 0..8 below the row max passes it, and the mistakes the tick could
+# make — no output, a wrong value exponent, the transposed value tile read in a
+# wrong token order — fail it.
+# ---------------------------------------------------------------------------
+FS_T, FS_NH, FS_S, FS_D = 4680, 3, 4, 128
+
+
+@pytest.fixture(scope="module")
+def full_size_kv8():
+    from wavefront_causal_attention_wf_amd import inputs
+
+    rng = np.random.default_rng(41)
+
+    def draw(shape):
+        return inputs.f32_to_bf16_bits((rng.standard_normal(shape) * 0.5).astype(np.float32))
+
+    T, H, D, P = FS_T, 1, FS_D, 64
+    ppc = -(-T // P)
+    store = fp8.Fp8KvPageStore(P, H, D)
+    hist = [list(range(c * ppc, (c + 1) * ppc)) for c in range(FS_NH)]
+    live = [list(range((FS_NH + j) * ppc, (FS_NH + j + 1) * ppc)) for j in range(FS_S + 1)]
+    for ids in hist + live:
+        store.write_chunk(ids, draw((T, H, D)), draw((T, H, D)))
+    q = draw((FS_S + 1, T, H, D))
+    rows = np.concatenate([np.arange(0, 16), rng.choice(T, 16, replace=False), [T - 1]])
+    return store, q, hist, live, rows
+
+
+def _stage_keys(store, hist, live, s):
+    """Dequantised K and V of head 0 along stage s's visible keys (Eq. (5) order)."""
+    segs = [hist[c] for c in range(FS_NH)] + [live[FS_S]]
+    if s < FS_S:
+        segs += [live[j] for j in range(s, FS_S)]
+    K, V = store.gather(segs, FS_T)
+    return K[:, :, 0].reshape(-1, FS_D), V[:, :, 0].reshape(-1, FS_D)
+
+
+def _device_model(qv, K, V, refs, perm=None, v_gain=None):
+    """Outputs of one stage and head as the device forms them: P of the
+    dequantised scores relative to the row max, rounded to e4m3 at reference
+    refs[row] below the max, P.V over the (possibly mis-ordered or mis-scaled)
+    values divided by the unrounded sum, rounded to bf16. Also the exact outputs."""
+    from wavefront_causal_attention_wf_amd import inputs
+
+    sc = qv @ K.T / np.sqrt(FS_D)
+    p = np.exp(sc - sc.max(axis=1, keepdims=True))
+    L = p.sum(axis=1, keepdims=True)
+    exact = p @ V / L
+    a = np.asarray(refs, np.float64)[:, None]
+    pq = fp8.e4m3_decode(fp8.e4m3_encode(p * 2.0 ** a)) / 2.0 ** a
+    Vd = V if v_gain is None else V * v_gain
+    if perm is not None:      # token t of each 64-token tile read from perm(t)
+        n = V.shape[0]
+        idx = np.arange(n)
+        src = (idx // 64) * 64 + perm(idx % 64)
+        Vd = Vd[np.where(src < n, src, idx)]
+    dev = oracle.decode_bf16(inputs.f32_to_bf16_bits((pq @ Vd / L).astype(np.float32)))
+    return dev, exact
+
+
+@pytest.mark.parametrize("s", [0, FS_S])
+def test_kv8_rel_l2_criterion_at_full_size(full_size_kv8, s):
+    store, q, hist, live, rows = full_size_kv8
+    rms = fp8.p_rounding_rms(q, store, hist, live, FS_S, (1 << (FS_S + 1)) - 1,
+                             1.0 / np.sqrt(FS_D), stages=[s], rows=rows)[s][0]
+    rng = np.random.default_rng(42 + s)
+    n = len(rows)
+    K, V = _stage_keys(store, hist, live, s)
+    qc, qs = fp8.quantize_q_rows(q[s, rows])
+    qv = (fp8.e4m3_decode(qc) * qs[..., None])[:, 0]
+    # the device model passes at every reference 0..8 below the max, and with
+    # references drawn per row
+    ratios = []
+    for refs in [np.full(n, a) for a in range(9)] + [rng.uniform(0, 8, n) for _ in range(4)]:
+        dev, exact = _device_model(qv, K, V, refs)
+        allow = fp8.kv8_l2_allowance(rms, np.linalg.norm(exact))
+        err = np.linalg.norm(dev - exact)
+        ratios.append(err / allow)
+        assert err <= allow, (refs[:3], err, allow)
+    # R itself is not loose by more than the derivation says (and not tight)
+    assert 0.15 < max(ratios) < 0.6, ratios
+    refs = rng.uniform(0, 8, n)
+    dev, exact = _device_model(qv, K, V, refs)
+    allow = fp8.kv8_l2_allowance(rms, np.linalg.norm(exact))
+    # the element-wise worst-case bound alone would accept an all-zero output
+    bound = fp8.p_error_bound(q, store, hist, live, FS_S, (1 << (FS_S + 1)) - 1,
+                              1.0 / np.sqrt(FS_D), stages=[s], rows=rows)[s][:, 0]
+    assert np.all(np.abs(exact).max(axis=1) < bound)
+    # mistakes fail the criterion: no output, every value exponent one too high
+    # or too low, the transposed value tile read in a wrong token order
+    mistakes = {
+        "zero": np.zeros_like(exact),
+        "exp+1": _device_model(qv, K, V, refs, v_gain=2.0)[0],
+        "exp-1": _device_model(qv, K, V, refs, v_gain=0.5)[0],
+        "halves": _device_model(qv, K, V, refs, perm=lambda t: t ^ 32)[0],
+        "groups": _device_model(qv, K, V, refs, perm=lambda t: t ^ 8)[0],
+        "reversed": _device_model(qv, K, V, refs, perm=lambda t: 63 - t)[0],
+    }
+    print("error / allowance, device model:", np.round(ratios, 3))
+    for name, wrong in mistakes.items():
+        err = np.linalg.norm(wrong - exact)
+        print(f"{name}: error / allowance {err / allow:.2f}")
+        assert err > 1.5 * allow, (name, err, allow)
+
+
+def test_tiny_groups_are_stored_as_zero():
+    """A key tile or query row whose amax is below 2^-100 is stored as zero (scale
+    0): 448 / amax would otherwise overflow float32 (NaN and infinite codes) or
+    leave a subnormal scale. At 2^-100 and above, the usual rule holds and the
+    amax element takes the largest code."""
+    x = np.zeros((4, 64), np.float32)
+    x[0, 3] = 2.0 ** -101            # tiny
+    x[1, 5] = np.float32(1e-38)      # tiny (bf16 and float32 still normal)
+    x[2, 7] = 2.0 ** -100            # at the threshold
+    x[2, 8] = -2.0 ** -102
+    x[3, 1] = 1.5
+    codes, scale = fp8.quantize_groups(x, axes=-1)
+    assert scale[0, 0] == 0 and scale[1, 0] == 0 and not codes[:2].any()
+    assert scale[2, 0] == np.float32(2.0 ** -100) / np.float32(448)
+    assert codes[2, 7] == 0x7E and codes[2, 8] == 0x80 | 0x6E     # -448 / 4 = -112
+    assert np.all(np.isfinite(fp8.dequantize(codes, scale)))
+    v = np.zeros((64, 1, 8), np.float32)
+    v[3, 0, 2] = np.float32(3e-39)                                  # subnormal in float32
+    v[9, 0, 5] = np.float32(-1e-38)
+    vc, ve = fp8.quantize_v_tiles(v)
+    assert ve[0, 0] == -127
+    back = fp8.e4m3_decode(vc) * 2.0 ** -127
+    assert np.all(np.abs(back - v) <= 2.0 ** -4 * np.abs(v) + 2.0 ** -136)
