@@ -9,6 +9,7 @@ import subprocess
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from oracle.page_model import PageModelError
@@ -478,3 +479,121 @@ def test_store_fp8_validation():
     assert call(kp=fake + 8) == E               # codes not 16-byte aligned
     assert call(num_pages=10) == E              # the chunk needs 74 pages
     assert call(T=0, k=None, v=None, kp=None, ks=None, vp=None, ids=None) == 0
+
+
+# ---------------------------------------------------------------------------
+# The Python binding refuses, before any library call, arguments whose element
+# type, layout or shape do not match what the call reads and writes (the
+# library trusts sizes and device page ids). CPU tensors suffice: every check
+# here runs before the check that tensors live on the GPU, which is tested last.
+# ---------------------------------------------------------------------------
+def _bf(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _ids(*shape, dtype=None):
+    return torch.zeros(shape, dtype=dtype or torch.int32)
+
+
+def test_binding_rejects_bad_store_and_gather_arguments():
+    wf = _wfattn()
+    T, H, D, P, N = 100, 2, 64, 16, 20
+    ppc = -(-T // P)
+    k, kp = _bf(T, H, D), _bf(N, P, H, D)
+    cases = [
+        (TypeError, lambda: wf.wf_store_paged(k, k, kp, kp, _ids(ppc, dtype=torch.int64))),
+        (ValueError, lambda: wf.wf_store_paged(k, k, kp, kp, _ids(ppc + 1))),
+        (ValueError, lambda: wf.wf_store_paged(k, k, kp, kp, _ids(ppc, 1))),
+        (ValueError, lambda: wf.wf_store_paged(k, k, kp, kp, _ids(2 * ppc)[::2])),
+        (ValueError, lambda: wf.wf_store_paged(k, k, _bf(N, P, H, 2 * D), _bf(N, P, H, 2 * D),
+                                               _ids(ppc))),                       # pool's D
+        (ValueError, lambda: wf.wf_store_paged(k, k, _bf(N, P, H + 1, D), _bf(N, P, H + 1, D),
+                                               _ids(ppc))),                       # pool's H
+        (ValueError, lambda: wf.wf_store_paged(k, _bf(T + 1, H, D), kp, kp, _ids(ppc))),
+        (ValueError, lambda: wf.wf_store_paged(k, k, kp, _bf(N + 1, P, H, D), _ids(ppc))),
+        (TypeError, lambda: wf.wf_store_paged(k.float(), k, kp, kp, _ids(ppc))),
+        (ValueError, lambda: wf.wf_store_paged(k, k, kp, kp, _ids(ppc))),         # on the CPU
+        (ValueError, lambda: wf.wf_gather_paged(kp, kp, _ids(ppc), _bf(1, T, H, D),
+                                                _bf(1, T, H, D))),               # ids not [n][ppc]
+        (TypeError, lambda: wf.wf_gather_paged(kp, kp, _ids(1, ppc, dtype=torch.int64),
+                                               _bf(1, T, H, D), _bf(1, T, H, D))),
+        (ValueError, lambda: wf.wf_gather_paged(kp, kp, _ids(1, ppc), _bf(1, T, H, D),
+                                                _bf(2, T, H, D))),
+        (ValueError, lambda: wf.wf_rope_store_paged(k, k, kp, None, _ids(ppc), (T, 1, 1), 0)),
+        (TypeError, lambda: wf.wf_rope_store_paged(k, None, kp, None,
+                                                   _ids(ppc, dtype=torch.int64), (T, 1, 1), 0)),
+        (ValueError, lambda: wf.wf_rope_store_paged(k, None, _bf(N, P, H, D + 2), None,
+                                                    _ids(ppc), (T, 1, 1), 0)),
+    ]
+    for exc, call in cases:
+        with pytest.raises(exc):
+            call()
+
+
+def test_binding_rejects_bad_fp8_store_arguments():
+    wf = _wfattn()
+    T, H, D, P, N = 100, 2, 128, 64, 6
+    ppc = -(-T // P)
+    k = _bf(T, H, D)
+    kc = torch.zeros((N, P, H, D), dtype=torch.uint8)
+    ks = torch.zeros((N, P // 64, H), dtype=torch.float32)
+    vb = _bf(N, P, H, D)
+    v8 = torch.zeros((N, P // 64, H, D, 64), dtype=torch.uint8)
+    ve = torch.zeros((N, P // 64, H), dtype=torch.uint8)
+    cases = [
+        (TypeError, lambda: wf.wf_store_paged_fp8(k, k, vb, ks, vb, _ids(ppc))),   # K not uint8
+        (TypeError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks.double(), vb, _ids(ppc))),
+        (ValueError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks[:, :, :1].contiguous(), vb,
+                                                   _ids(ppc))),
+        (TypeError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks, v8, _ids(ppc))),   # 8-bit V, no v_exp
+        (TypeError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks, vb, _ids(ppc), v_exp=ve)),
+        (ValueError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks, v8[:, :, :, :64].contiguous(),
+                                                   _ids(ppc), v_exp=ve)),          # V layout
+        (ValueError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks, v8, _ids(ppc),
+                                                   v_exp=ve[:, :, :1].contiguous())),
+        (TypeError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks, vb, _ids(ppc, dtype=torch.int64))),
+        (ValueError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks, vb, _ids(ppc + 1))),
+        (ValueError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks, vb, _ids(ppc))),  # on the CPU
+        (ValueError, lambda: wf.wf_store_paged_fp8(k, k, kc, ks, v8, _ids(ppc), v_exp=ve)),
+    ]
+    for exc, call in cases:
+        with pytest.raises(exc):
+            call()
+
+
+def test_binding_rejects_bad_tick_arguments():
+    wf = _wfattn()
+    S, T, H, D, P, N, nh = 2, 100, 2, 64, 16, 40, 2
+    ppc = -(-T // P)
+    q = _bf(S + 1, T, H, D)
+    kp = _bf(N, P, H, D)
+    hist = _ids(nh, ppc)
+
+    def tick(**kw):
+        args = dict(q=q, k=q, v=q, o=q, S=S, active_mask=0b111, scale=0.125, k_pool=kp,
+                    v_pool=kp, hist_pages=hist)
+        args.update(kw)
+        wf.wf_attn_tick(**args)
+
+    cases = [
+        (ValueError, dict(S=S + 1)),                                   # q not [S+1][T][H][D]
+        (ValueError, dict(o=_bf(S + 1, T, H, D + 64))),
+        (ValueError, dict(k=_bf(S + 1, T + 1, H, D))),
+        (TypeError, dict(v=q.float())),
+        (TypeError, dict(hist_pages=_ids(nh, ppc, dtype=torch.int64))),   # int64 page ids
+        (ValueError, dict(hist_pages=_ids(nh, ppc + 1))),
+        (ValueError, dict(hist_pages=_ids(nh * ppc))),                  # flat, not [n][ppc]
+        (ValueError, dict(hist_pages=_ids(nh, 2 * ppc)[:, ::2])),       # not contiguous
+        (ValueError, dict(k_pool=_bf(N, P, H, 2 * D), v_pool=_bf(N, P, H, 2 * D))),  # pool's D
+        (ValueError, dict(v_pool=_bf(N, P, H + 1, D))),                 # pool's H
+        (ValueError, dict(k_pool=None)),
+        (TypeError, dict(store_pages=_ids(ppc, dtype=torch.int64))),
+        (ValueError, dict(store_pages=_ids(ppc - 1))),
+        (ValueError, dict(k=None, v=None, live_pages=_ids(S, ppc))),    # not [S+1][ppc]
+        (TypeError, dict(k=None, v=None, live_pages=_ids(S + 1, ppc),
+                         k_scale=torch.zeros((N, 1, H)))),             # 8-bit keys, bf16 pool
+        (ValueError, dict()),                                           # right, but on the CPU
+    ]
+    for exc, kw in cases:
+        with pytest.raises(exc):
+            tick(**kw)

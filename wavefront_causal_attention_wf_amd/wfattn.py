@@ -140,12 +140,55 @@ def _stream(stream) -> Optional[int]:
     return int(stream.cuda_stream)
 
 
+# Argument checks. The library trusts sizes and page ids it is given (device
+# page ids are range-checked only with WF_CHECK_PAGES=1), so the binding
+# refuses, before any call, tensors whose element type, layout or shape do not
+# match what the call reads and writes: dtype and contiguity first, then
+# shapes, then that every tensor is on the GPU.
 def _check_bf16(name, t):
     import torch
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError(f"{name} must hold bf16 bit patterns (bfloat16/int16/uint16), got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _check_typed(name, t, dtype_name: str):
+    if str(t.dtype) != "torch." + dtype_name:
+        raise TypeError(f"{name} must be a {dtype_name} tensor, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_shape(name, t, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_ids(name, t, shape) -> None:
+    """Page ids: a contiguous int32 tensor of exactly `shape`."""
+    if t is None or not hasattr(t, "data_ptr"):
+        raise TypeError(f"{name} must be an int32 tensor on the GPU")
+    _check_typed(name, t, "int32")
+    _check_shape(name, t, shape)
+
+
+def _check_on_gpu(**tensors) -> None:
+    devs = set()
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU, got {t.device}")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"tensors on several devices: {sorted(map(str, devs))}")
+
+
+def _pages_per_chunk(T: int, P: int) -> int:
+    if P <= 0:
+        raise ValueError(f"page size P = {P} must be positive")
+    return -(-T // P)
 
 
 # ---------------------------------------------------------------------------
@@ -216,8 +259,15 @@ def wf_store_paged(k_src, v_src, k_pool, v_pool, page_ids, stream=None) -> None:
     """Scatter one chunk's K/V [T][H][D] into pool pages [num_pages][P][H][D]."""
     for n, t in (("k_src", k_src), ("v_src", v_src), ("k_pool", k_pool), ("v_pool", v_pool)):
         _check_bf16(n, t)
+    if k_src.dim() != 3 or k_pool.dim() != 4:
+        raise ValueError("k_src must be [T][H][D] and k_pool [num_pages][P][H][D]")
     T, H, D = k_src.shape
     num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    _check_shape("v_src", v_src, k_src.shape)
+    _check_shape("k_pool", k_pool, (num_pages, P, H, D))
+    _check_shape("v_pool", v_pool, k_pool.shape)
+    _check_ids("page_ids", page_ids, (_pages_per_chunk(T, P),))
+    _check_on_gpu(k_src=k_src, v_src=v_src, k_pool=k_pool, v_pool=v_pool, page_ids=page_ids)
     _check(_lib.wf_store_paged(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(v_pool),
                                _ptr(page_ids), T, H, D, num_pages, P, _stream(stream)),
            "wf_store_paged")
@@ -227,8 +277,15 @@ def wf_gather_paged(k_pool, v_pool, page_ids, k_dst, v_dst, stream=None) -> None
     """Copy n chunks out of pool pages into contiguous [n][T][H][D]."""
     for n, t in (("k_pool", k_pool), ("v_pool", v_pool), ("k_dst", k_dst), ("v_dst", v_dst)):
         _check_bf16(n, t)
+    if k_dst.dim() != 4 or k_pool.dim() != 4:
+        raise ValueError("k_dst must be [n][T][H][D] and k_pool [num_pages][P][H][D]")
     n_chunks, T, H, D = k_dst.shape
     num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    _check_shape("v_dst", v_dst, k_dst.shape)
+    _check_shape("k_pool", k_pool, (num_pages, P, H, D))
+    _check_shape("v_pool", v_pool, k_pool.shape)
+    _check_ids("page_ids", page_ids, (n_chunks, _pages_per_chunk(T, P)))
+    _check_on_gpu(k_pool=k_pool, v_pool=v_pool, page_ids=page_ids, k_dst=k_dst, v_dst=v_dst)
     _check(_lib.wf_gather_paged(_ptr(k_pool), _ptr(v_pool), _ptr(page_ids), n_chunks,
                                 _ptr(k_dst), _ptr(v_dst), T, H, D, num_pages, P,
                                 _stream(stream)), "wf_gather_paged")
@@ -241,19 +298,30 @@ def wf_store_paged_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=N
     ([num_pages][P/64][H]); V copied into v_pool (bf16 [num_pages][P][H][D]),
     or with v_exp (uint8 [num_pages][P/64][H]) quantised into v_pool (uint8
     [num_pages][P/64][H][D][64], transposed tiles)."""
-    import torch
     for n, t in (("k_src", k_src), ("v_src", v_src)):
         _check_bf16(n, t)
+    _check_typed("k_pool", k_pool, "uint8")
+    _check_typed("k_scale", k_scale, "float32")
     if v_exp is None:
         _check_bf16("v_pool", v_pool)
-    elif v_pool.dtype != torch.uint8 or v_exp.dtype != torch.uint8:
-        raise TypeError("with v_exp, v_pool and v_exp must be uint8 tensors")
-    if k_pool.dtype != torch.uint8 or not k_pool.is_contiguous():
-        raise TypeError("k_pool must be a contiguous uint8 tensor of e4m3 codes")
-    if k_scale.dtype != torch.float32 or not k_scale.is_contiguous():
-        raise TypeError("k_scale must be a contiguous float32 tensor")
+    else:
+        _check_typed("v_pool", v_pool, "uint8")
+        _check_typed("v_exp", v_exp, "uint8")
+    if k_src.dim() != 3 or k_pool.dim() != 4:
+        raise ValueError("k_src must be [T][H][D] and k_pool [num_pages][P][H][D]")
     T, H, D = k_src.shape
     num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    _check_shape("v_src", v_src, k_src.shape)
+    _check_shape("k_pool", k_pool, (num_pages, P, H, D))
+    _check_shape("k_scale", k_scale, (num_pages, P // 64, H))
+    if v_exp is None:
+        _check_shape("v_pool", v_pool, (num_pages, P, H, D))
+    else:
+        _check_shape("v_pool", v_pool, (num_pages, P // 64, H, D, 64))
+        _check_shape("v_exp", v_exp, (num_pages, P // 64, H))
+    _check_ids("page_ids", page_ids, (_pages_per_chunk(T, P),))
+    _check_on_gpu(k_src=k_src, v_src=v_src, k_pool=k_pool, k_scale=k_scale, v_pool=v_pool,
+                  v_exp=v_exp, page_ids=page_ids)
     _check(_lib.wf_store_paged_fp8(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(k_scale),
                                    _ptr(v_pool), _ptr(v_exp), _ptr(page_ids), T, H, D, num_pages,
                                    P, _stream(stream)), "wf_store_paged_fp8")
@@ -286,11 +354,21 @@ def wf_rope_store_paged(k_src, v_src, k_pool, v_pool, page_ids, grid: Sequence[i
     K only (the anchor's re-rotation)."""
     _check_bf16("k_src", k_src)
     _check_bf16("k_pool", k_pool)
+    if (v_src is None) != (v_pool is None):
+        raise ValueError("v_src and v_pool are given together (or both None: K only)")
     if v_src is not None:
         _check_bf16("v_src", v_src)
         _check_bf16("v_pool", v_pool)
+    if k_src.dim() != 3 or k_pool.dim() != 4:
+        raise ValueError("k_src must be [T][H][D] and k_pool [num_pages][P][H][D]")
     T, H, D = k_src.shape
     num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    _check_shape("k_pool", k_pool, (num_pages, P, H, D))
+    if v_src is not None:
+        _check_shape("v_src", v_src, k_src.shape)
+        _check_shape("v_pool", v_pool, k_pool.shape)
+    _check_ids("page_ids", page_ids, (_pages_per_chunk(T, P),))
+    _check_on_gpu(k_src=k_src, v_src=v_src, k_pool=k_pool, v_pool=v_pool, page_ids=page_ids)
     r = make_rope_desc(grid, frame0, split, theta, D)
     _check(_lib.wf_rope_store_paged(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(v_pool),
                                     _ptr(page_ids), T, H, D, num_pages, P, ctypes.byref(r),
@@ -334,23 +412,56 @@ def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None
     e4m3 codes (uint8) as written by wf_store_paged_fp8, live_pages required.
     v_exp (optional, uint8 [num_pages][P/64][H], with k_scale): 8-bit values —
     v_pool holds the transposed e4m3 tiles written by wf_store_paged_fp8."""
-    for n, t in (("q", q), ("o", o)) + ((("k", k), ("v", v)) if live_pages is None else ()):
+    live = (("k", k), ("v", v)) if live_pages is None else ()
+    for n, t in (("q", q), ("o", o)) + live:
         _check_bf16(n, t)
+    if q.dim() != 4 or q.shape[0] != S + 1:
+        raise ValueError(f"q must be [S+1][T][H][D] with S + 1 = {S + 1}, got {tuple(q.shape)}")
     _, T, H, D = q.shape
+    for n, t in (("o", o),) + live:
+        _check_shape(n, t, q.shape)
     n_hist, num_pages, P = 0, 0, 0
     if hist_pages is not None and hist_pages.numel() > 0:
+        if hist_pages.dim() != 2:
+            raise ValueError("hist_pages must be [n_hist][ceil(T/P)]")
         n_hist = hist_pages.shape[0]
     pooled = n_hist > 0 or live_pages is not None or store_pages is not None
     if pooled:
-        num_pages, P = k_pool.shape[0], k_pool.shape[1]
+        if k_pool is None or v_pool is None:
+            raise ValueError("history, live_pages or store_pages need k_pool and v_pool")
         if k_scale is None:
             _check_bf16("k_pool", k_pool)
-        elif str(k_pool.dtype) != "torch.uint8" or not k_pool.is_contiguous():
-            raise TypeError("with k_scale, k_pool must be a contiguous uint8 tensor of e4m3 codes")
+        else:
+            _check_typed("k_pool", k_pool, "uint8")
+            _check_typed("k_scale", k_scale, "float32")
         if v_exp is None:
             _check_bf16("v_pool", v_pool)
-        elif str(v_pool.dtype) != "torch.uint8" or not v_pool.is_contiguous():
-            raise TypeError("with v_exp, v_pool must be a contiguous uint8 tensor of e4m3 codes")
+        else:
+            _check_typed("v_pool", v_pool, "uint8")
+            _check_typed("v_exp", v_exp, "uint8")
+        if k_pool.dim() != 4:
+            raise ValueError("k_pool must be [num_pages][P][H][D]")
+        num_pages, P = k_pool.shape[0], k_pool.shape[1]
+        ppc = _pages_per_chunk(T, P)
+        _check_shape("k_pool", k_pool, (num_pages, P, H, D))
+        if v_exp is None:
+            _check_shape("v_pool", v_pool, (num_pages, P, H, D))
+        else:
+            _check_shape("v_pool", v_pool, (num_pages, P // 64, H, D, 64))
+            _check_shape("v_exp", v_exp, (num_pages, P // 64, H))
+        if k_scale is not None:
+            _check_shape("k_scale", k_scale, (num_pages, P // 64, H))
+        if n_hist:
+            _check_ids("hist_pages", hist_pages, (n_hist, ppc))
+        if live_pages is not None:
+            _check_ids("live_pages", live_pages, (S + 1, ppc))
+        if store_pages is not None:
+            _check_ids("store_pages", store_pages, (ppc,))
+    _check_on_gpu(q=q, o=o, k=k if live_pages is None else None,
+                  v=v if live_pages is None else None,
+                  k_pool=k_pool if pooled else None, v_pool=v_pool if pooled else None,
+                  hist_pages=hist_pages if n_hist else None, live_pages=live_pages,
+                  store_pages=store_pages, k_scale=k_scale, v_exp=v_exp)
     d = make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
                        k_pool if pooled else None, v_pool if pooled else None, num_pages, P,
                        hist_pages if n_hist else None, n_hist, hist_first, live_pages,
