@@ -38,6 +38,11 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 # the time floor is F/2 / 5000 + F/2 / 2500 and the blended peak 3333 TFLOP/s.
 PEAK_FP8_TIER_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# Bandwidth kernels are timed over this many distinct source chunks and page
+# sets, launched in turn: at the 1.3B shape the sources alone take 24 x 28.75 MB
+# = 690 MB, well above the 256 MB last-level cache, so each launch reads its
+# inputs from HBM rather than from the cache the previous launches filled.
+ROTATION = 24
 
 # HBM traffic of the attention kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes (scaled by a plain-copy calibration), recorded with a hash of the
@@ -205,11 +210,11 @@ def separate_store_step(cfg, dev, steps: int = 10, warmup: int = 3) -> dict:
             "attn_kernel_ms_mean": round(attn, 4)}
 
 
-def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = 8) -> dict:
+def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> dict:
     """wf_store_paged and wf_gather_paged alone, HIP events on their stream.
 
-    cold: rotating over `rotation` distinct source chunks and page sets (working
-    set above the 256 MB last-level cache); warm: one chunk and page set
+    cold: rotating over `rotation` distinct source chunks and page sets (the
+    sources alone exceed the 256 MB last-level cache); warm: one chunk and page set
     repeated; copy: a plain device-to-device copy of the store's byte count (the
     achievable ceiling for a read+write stream of that size)."""
     import torch
@@ -247,7 +252,8 @@ def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = 8) -> dict:
     store_cold = timed(lambda i: wfattn.wf_store_paged(ksrc[i % rotation], vsrc[i % rotation],
                                                        kp, vp, ids[i % rotation]))
     store_warm = timed(lambda i: wfattn.wf_store_paged(ksrc[0], vsrc[0], kp, vp, ids[0]))
-    gather_cold = timed(lambda i: wfattn.wf_gather_paged(kp, vp, ids[i % rotation], kd, vd))
+    gather_cold = timed(lambda i: wfattn.wf_gather_paged(kp, vp, ids[i % rotation].view(1, ppc),
+                                                         kd, vd))
     nbytes = 2 * (T * H * D * 2) + 2 * (ppc * P * H * D * 2)   # read K,V + write whole pages
     gbytes = 4 * (T * H * D * 2)   # read the K,V tokens from their pages + write them
     # a copy of nbytes / 2 bytes moves nbytes (read + write)
@@ -270,7 +276,7 @@ def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = 8) -> dict:
                        "frac_hbm_peak": round(rate(gbytes, gather_cold) / PEAK_HBM_GBS, 4)}}
 
 
-def rope_store_bandwidth(cfg, dev, launches: int = 96, rotation: int = 8) -> dict:
+def rope_store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> dict:
     """wf_rope_store_paged alone (HIP events on its stream), inputs rotated over
     `rotation` chunks and page sets like the store measurement: reads K and V of
     one chunk, rotates K, writes the chunk's whole pages of K and V."""
@@ -516,7 +522,7 @@ def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3, v8: bool = False) ->
             "tick_flow": f"{cfg.S + 1} x wf_store_paged_fp8 (every live chunk) + wf_attn_tick"}
 
 
-def store_fp8_bandwidth(cfg, dev, launches: int = 96, rotation: int = 8) -> dict:
+def store_fp8_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> dict:
     """wf_store_paged_fp8 of one chunk (K quantised, V copied), rotating over
     `rotation` source chunks and page sets so that they do not sit in the
     last-level cache."""

@@ -167,8 +167,9 @@ wf_status wf_rope_store_paged(const void* k_src, const void* v_src, void* k_pool
 /* one scale per (64-token tile of a page, head): amax = max |k| over the     */
 /* tile's tokens of that head, scale = amax / 448, code = e4m3 of the fp32    */
 /* product k * (448 / amax) rounded to nearest even (both quotients fp32,    */
-/* correctly rounded; an all-zero tile has scale 0 and zero codes). A key    */
-/* stands for decode(code) * scale. Token t -> slot t % P of page             */
+/* correctly rounded; an all-zero tile, or one with amax below 2^-100, has    */
+/* scale 0 and zero codes). A key stands for decode(code) * scale.           */
+/* Token t -> slot t % P of page                                              */
 /* page_ids[t / P]; slots past token T-1 hold zero codes and zero V, and a    */
 /* tile holding none of the chunk's tokens has scale 0.                       */
 /* k_src, v_src: device bf16 [T][H][D]; k_pool: device uint8                  */
@@ -176,17 +177,15 @@ wf_status wf_rope_store_paged(const void* k_src, const void* v_src, void* k_pool
 /* device int32 [ceil(T/P)].                                                  */
 /* v_exp NULL: v_pool is device bf16 [num_pages][P][H][D] and V is copied.    */
 /* v_exp set (8-bit values): V is quantised per (64-token tile, head) with a  */
-/* power-of-two scale 2^e, e the smallest integer with amax <= 448 * 2^e (0   */
-/* for an all-zero tile), code = e4m3 of v * 2^-e (exact product, rounded to  */
+/* power-of-two scale 2^e, e the smallest integer >= -127 with              */
+/* amax <= 448 * 2^e (0 for an all-zero tile; -127 is the least exponent     */
+/* v_exp holds), code = e4m3 of v * 2^-e (exact product, rounded to           */
 /* nearest even); v_exp: device uint8 [num_pages][P/64][H] receives e + 127;  */
 /* v_pool: device uint8 [num_pages][P/64][H][D][64] is written in the layout  */
 /* the attention's P.V operand reads: row d of tile (page, sub-tile, head)    */
 /* holds channel d of the tile's 64 tokens, byte 32*g + j being token         */
 /* 32*(j/16) + 16*((j/8)%2) + 8*g + j%8 (g = 0, 1; j = 0..31); tokens past    */
 /* the chunk hold zero codes.                                                 */
-/* Preconditions (not checked): a key tile's amax is 0 or at least 2^-120, a  */
-/* value tile's 0 or at least 2^-100 (the scales' reciprocals must be finite  */
-/* in fp32).                                                                  */
 /* Errors: WF_EINVAL for bad sizes, P not a multiple of 64, NULL pointers,    */
 /* tensors not 16-byte aligned (k_scale: 4-byte), ceil(T/P) > num_pages;      */
 /* WF_EUNSUPPORTED for D not 64/128 or H > 65535; WF_EHIP if the launch fails. */
@@ -226,12 +225,13 @@ wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t*
 /* runs on the e4m3 MFMA with fp32 accumulation, and the scores are the       */
 /* product of the codes' dot product, the query scale and the key tile's      */
 /* scale; the softmax and P.V are those of the bf16 tier. Needs D = 128, P a  */
-/* multiple of 64, no store_pages; a query row's amax must be 0 or at least   */
-/* 2^-120 (not checked).                                                     */
+/* multiple of 64, no store_pages; a query row with amax below 2^-100 is     */
+/* taken as zero, as key tiles are.                                           */
 /* 8-bit values as well (v_format = WF_V_E4M3, with WF_K_E4M3): v_pool holds  */
 /* the transposed e4m3 tiles and v_exp their exponents, as written by          */
-/* wf_store_paged_fp8 with v_exp; P is rounded to e4m3 (P <= 2^8 under the    */
-/* running reference) and P.V runs on the e4m3 MFMA with the tile's          */
+/* wf_store_paged_fp8 with v_exp; P is rounded to e4m3 (P <= 2^8: the running */
+/* reference lies at most 8 below the row max in log2 units, never above it) */
+/* and P.V runs on the e4m3 MFMA with the tile's                             */
 /* power-of-two scale applied by the MFMA; the softmax's sum uses the          */
 /* unrounded P.                                                               */
 /* Errors: WF_EINVAL for bad sizes, masks, pointers (NULL or not 16-byte      */

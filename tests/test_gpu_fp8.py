@@ -89,6 +89,33 @@ def test_store_fp8_matches_oracle_bits(T, H, D, P):
     assert bool(torch.isnan(pg.k_scale.index_select(0, idx)).all())
 
 
+@pytest.mark.parametrize("v8", [False, True])
+def test_store_fp8_tiny_tiles(v8):
+    """Tiles whose amax lies far below 1: keys under 2^-100 are stored as zero
+    (scale 0), values take the least exponent -127 when smaller than 448 *
+    2^-128. bf16 inputs around 2^-120 (normal) and 1e-38 (subnormal)."""
+    say(f"store fp8 tiny tiles, 8-bit values {v8}")
+    T, H, D, P = 256, 2, 128, 64
+    cfg = inputs.TickConfig("s", S=0, T=T, H=H, D=D, P=P, n_hist=0, num_pages=8, std=0.5,
+                            bf16_inputs=True, page_order="identity")
+    k, v, _ = inputs.draw_live_torch(cfg, 5, DEV)
+    k, v = k[0].clone(), v[0].clone()
+    k[0:64, 0] *= 2.0 ** -120            # normal bf16, far below 2^-100
+    k[64:128, 1] *= 1e-38                # subnormal bf16
+    k[128:192, 0] *= 2.0 ** -99          # just above the threshold: a normal tile
+    v[0:64, 1] *= 2.0 ** -120
+    v[128:192, 0] *= 1e-38
+    ids = np.array([5, 2, 7, 0], np.int32)
+    pg = Fp8KvPages(8, P, H, D) if v8 else Fp8Pages(8, P, H, D)
+    pg.write(ids, k, v)
+    pg.check(ids)
+    torch.cuda.synchronize()
+    assert float(pg.k_scale[5, 0, 0]) == 0.0 and float(pg.k_scale[2, 0, 1]) == 0.0
+    assert float(pg.k_scale[7, 0, 0]) > 0.0
+    if v8:
+        assert int(pg.v_exp[5, 0, 1]) == 0 and int(pg.v_exp[7, 0, 0]) == 0   # e = -127
+
+
 def _fp8_tick(S, T, H, P, n_hist, mask, seed, q_gain=1.0):
     D = 128
     cfg = inputs.TickConfig("f8", S=S, T=T, H=H, D=D, P=P, n_hist=n_hist, num_pages=1,
@@ -281,20 +308,33 @@ def _fp8kv_tick(S, T, H, P, n_hist, mask, seed, q_zero=False):
     return pg, q_bits, hist, live_lists, o, scale
 
 
-def compare_within_p_bound(o, want, bound, rows=None, label=""):
-    """|device - exact| <= the e4m3-P bound + the bf16 output rounding and fp32
-    slack (2^-8 |exact| + 2e-3), element by element."""
+def compare_kv8(o, want, bound, rms, rows=None, label=""):
+    """The two checks of the 8-bit K/V tick against the exact attention of the
+    dequantised values:
+      * element by element, |device - exact| <= the worst-case e4m3-P bound +
+        the bf16 output rounding and fp32 slack (2^-8 |exact| + 2e-3);
+      * per (stage, head), ||device - exact|| <= kv8_l2_allowance(R, ||exact||),
+        R from the statistics of the e4m3 rounding of P (p_rounding_rms). At the
+        workload's size the first check alone would accept an all-zero output;
+        this one rejects it, a wrong value exponent and a wrong token order.
+    Returns the worst ratios (element, rel-L2) of error to allowance."""
     if rows is not None:
         o = o.index_select(1, torch.as_tensor(np.asarray(rows), dtype=torch.long, device=o.device))
     g = o.float().cpu().numpy().astype(np.float64)
-    worst_ratio = 0.0
+    worst_el, worst_l2 = 0.0, 0.0
     for s, w in want.items():
         d = np.abs(g[s] - w)
         lim = bound[s][:, :, None] + 2.0 ** -8 * np.abs(w) + 2e-3
         assert np.isfinite(g[s]).all(), f"{label} stage {s}: non-finite outputs"
         assert np.all(d <= lim), f"{label} stage {s}: max excess {float((d - lim).max()):.3e}"
-        worst_ratio = max(worst_ratio, float((d / lim).max()))
-    return worst_ratio
+        worst_el = max(worst_el, float((d / lim).max()))
+        for h in range(w.shape[1]):
+            err = float(np.linalg.norm(g[s][:, h] - w[:, h]))
+            allow = ofp8.kv8_l2_allowance(float(rms[s][h]), float(np.linalg.norm(w[:, h])))
+            assert err <= allow, (f"{label} stage {s} head {h}: ||error|| {err:.3e} > "
+                                  f"allowance {allow:.3e} (rel-L2 {err / np.linalg.norm(w[:, h]):.3e})")
+            worst_l2 = max(worst_l2, err / allow)
+    return worst_el, worst_l2
 
 
 @pytest.mark.parametrize("T,H,P", [(200, 2, 64), (150, 3, 128), (4680, 12, 64)])
@@ -337,9 +377,10 @@ def test_fp8kv_tick_within_p_bound(S, T, H, P, n_hist, mask):
     for ids in list(hist) + [l for l in live_lists if l is not None]:
         pg.check(list(ids))
     want = ofp8.attention_tick_fp8kv(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
-    bound = ofp8.p_error_bound(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
-    r = compare_within_p_bound(o, want, bound, label="fp8 K/V")
-    say(f"  worst |error| / allowance {r:.3f}")
+    bound, rms = ofp8.p_rounding_terms(q_bits, pg.store, hist.tolist(), live_lists, S, mask,
+                                       scale)
+    r_el, r_l2 = compare_kv8(o, want, bound, rms, label="fp8 K/V")
+    say(f"  worst error / allowance: element {r_el:.3f}, rel-L2 {r_l2:.3f}")
 
 
 @pytest.mark.parametrize("name", FULL_SIZE)
@@ -372,7 +413,8 @@ def test_fp8kv_tick_full_size_sampled_rows(name):
     qb = bits(q)
     want = ofp8.attention_tick_fp8kv(qb, pg.store, hist.tolist(), live.tolist(), cfg.S, mask,
                                      scale, rows=rows)
-    bound = ofp8.p_error_bound(qb, pg.store, hist.tolist(), live.tolist(), cfg.S, mask, scale,
-                               rows=rows)
-    r = compare_within_p_bound(o, want, bound, rows=rows, label="fp8 K/V full size")
-    say(f"[full-size fp8 K/V] worst |error| / allowance {r:.3f} over {len(rows)} rows")
+    bound, rms = ofp8.p_rounding_terms(qb, pg.store, hist.tolist(), live.tolist(), cfg.S, mask,
+                                       scale, rows=rows)
+    r_el, r_l2 = compare_kv8(o, want, bound, rms, rows=rows, label="fp8 K/V full size")
+    say(f"[full-size fp8 K/V] worst error / allowance: element {r_el:.3f}, rel-L2 {r_l2:.3f} "
+        f"over {len(rows)} rows")

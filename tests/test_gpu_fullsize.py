@@ -6,7 +6,9 @@ q/k/v drawn on the device by the seeded generator, history written through
 wf_store_paged into NaN-poisoned pools); the oracle reads host copies of the
 same generator output and builds its own page store from its own page model.
 Outputs are compared on sampled query rows (every stage and head), chosen to
-cover tile edges and the ragged last query tile.
+cover tile edges and the ragged last query tile, and on every row of every
+stage and head for the bench's 4-step tick and for the rollout's fill ticks
+and its last tick.
 """
 import numpy as np
 import pytest
@@ -127,7 +129,56 @@ def test_full_size_tick_sampled_rows(name):
     say(f"[full-size] {name}: worst rel-L2 {worst:.2e} over {len(rows)} rows x {cfg.H} heads")
 
 
-def test_streaming_rollout_120_ticks():
+def _bench_tick(cfg):
+    pages = MirroredPages(cfg, cfg.n_hist)
+    for c in range(cfg.n_hist):
+        hk, hv, _ = inputs.draw_live_torch(cfg, 2000 + c, DEV)
+        ids = pages.store_chunk(hk[0], hv[0])
+        pages.check_pages(ids)
+        pages.commit()
+        del hk, hv
+    q, k, v = inputs.draw_live_torch(cfg, inputs.rollout_seed(0), DEV)
+    return pages, q, k, v
+
+
+def test_full_size_4step_every_row_every_head():
+    """The bench's 4-step tick with its store write fused into the launch (the
+    timed configuration): every row of every stage and head against the
+    oracle, and the store chunk's pages bit for bit."""
+    cfg = inputs.CONFIGS["wan13_4step"]
+    say(f"[full-size, all rows] S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist}")
+    pages, q, k, v = _bench_tick(cfg)
+    mask = (1 << (cfg.S + 1)) - 1
+    ids = pages.store_chunk(k[cfg.S], v[cfg.S], write=False)
+    o = run_tick(cfg, pages, q, k, v, mask, store_ids=ids)
+    pages.check_pages(ids)
+    pages.store.drop(ids)          # the store chunk's pages are not history yet
+    want = oracle_rows(cfg, pages, q, k, v, mask, None)
+    worst = compare(o, want, label="wan13_4step all rows")
+    say(f"[full-size, all rows] worst rel-L2 {worst:.2e} over {cfg.T} rows x {cfg.H} heads")
+
+
+def test_full_size_4step_peaked_sampled_rows():
+    """The 4-step tick with Q x 16: scores of std 4 over 18,720-37,440 keys,
+    so each row is dominated by a few keys ([full text] Eq. (4): where the
+    mask matters most). Sampled rows of every stage and head."""
+    cfg = inputs.CONFIGS["wan13_4step"]
+    say(f"[full-size, peaked] S={cfg.S} T={cfg.T} H={cfg.H}, Q x 16")
+    pages, q, k, v = _bench_tick(cfg)
+    q = q * 16.0                   # exact in bf16 (a power of two)
+    mask = (1 << (cfg.S + 1)) - 1
+    o = run_tick(cfg, pages, q, k, v, mask)
+    rows = sample_rows(cfg.T, seed=16)
+    want = oracle_rows(cfg, pages, q, k, v, mask, rows)
+    worst = compare(o, want, rows=rows, label="wan13_4step q*16")
+    say(f"[full-size, peaked] worst rel-L2 {worst:.2e} over {len(rows)} rows x {cfg.H} heads")
+
+
+ROLLOUT_KEY_TICKS = (0, 1, 2, 3, 119)
+
+
+@pytest.fixture(scope="module")
+def rollout120():
     """120 ticks of a streaming rollout from an empty history (pipeline fill:
     stages activate one per tick and the store joins at tick S), window 3,
     4096-page permuted pool (pages are recycled about every 55 chunks).
@@ -136,14 +187,15 @@ def test_streaming_rollout_120_ticks():
     the stored chunk's pool pages equal the oracle store bit for bit; every
     output is finite; head 0 matches the oracle on sampled rows. On a spread of
     ticks (fill, first eviction, recycled pages, last) every head matches on
-    sampled rows, and on ticks 0-3 and the last, head 0 matches on every row.
-    Odd ticks write the store chunk with wf_store_paged before the attention
-    launch, even ticks let the attention launch write it (store_pages)."""
+    sampled rows. Odd ticks write the store chunk with wf_store_paged before the
+    attention launch, even ticks let the attention launch write it
+    (store_pages). Returns host copies of the key ticks' inputs, outputs and
+    history pages, which the tests below compare in full."""
     cfg = inputs.CONFIGS["rollout120"]
     S = cfg.S
     pages = MirroredPages(cfg, cfg.window)
     check_at = {0, 1, S - 1, S, S + 1, S + 3, S + 4, 40, 61, 90, cfg.ticks - 1}
-    all_rows_at = {0, 1, 2, 3, cfg.ticks - 1}
+    kept = {}
     for t in range(cfg.ticks):
         mask = oracle.active_mask_for_tick(t, S)
         q, k, v = inputs.draw_live_torch(cfg, inputs.rollout_seed(t), DEV)
@@ -160,13 +212,9 @@ def test_streaming_rollout_120_ticks():
         for s in range(S + 1):
             if (mask >> s) & 1:
                 assert torch.isfinite(o[s].float()).all(), f"tick {t} stage {s}"
-        if t in all_rows_at:
-            want = oracle_rows(cfg, pages, q, k, v, mask, None, heads=[0])
-            worst0 = compare(o, want, heads=[0], label=f"tick {t} head 0 all rows")
-        else:
-            rows0 = sample_rows(cfg.T, seed=10_000 + t, n_random=4)
-            want = oracle_rows(cfg, pages, q, k, v, mask, rows0, heads=[0])
-            worst0 = compare(o, want, heads=[0], rows=rows0, label=f"tick {t} head 0")
+        rows0 = sample_rows(cfg.T, seed=10_000 + t, n_random=4)
+        want = oracle_rows(cfg, pages, q, k, v, mask, rows0, heads=[0])
+        worst0 = compare(o, want, heads=[0], rows=rows0, label=f"tick {t} head 0")
         if t in check_at:
             rows = sample_rows(cfg.T, seed=t, n_random=6)
             want = oracle_rows(cfg, pages, q, k, v, mask, rows)
@@ -174,9 +222,36 @@ def test_streaming_rollout_120_ticks():
             say(f"[rollout] tick {t}: mask {mask:#x}, history "
                 f"{len(pages.model.export())} chunks, worst rel-L2 {worst:.2e} (all heads, "
                 f"sampled rows), {worst0:.2e} (head 0)")
+        if t in ROLLOUT_KEY_TICKS:
+            hist = pages.model.export()
+            kept[t] = dict(q=bits(q), k=bits(k), v=bits(v), o=o.float().cpu().numpy(), mask=mask,
+                           hist=hist, pages={p: pages.store.pages[p] for c in hist for p in c})
         if store_on:
             pages.commit()
+        del q, k, v, o
     # every page still resident matches the oracle store
     resident = [p for c in pages.model.export() for p in c]
     pages.check_pages(resident)
     assert pages.pt.num_free() == cfg.num_pages - cfg.window * cfg.ppc
+    return kept
+
+
+def test_streaming_rollout_120_ticks(rollout120):
+    assert sorted(rollout120) == list(ROLLOUT_KEY_TICKS)
+
+
+@pytest.mark.parametrize("t", ROLLOUT_KEY_TICKS)
+def test_rollout_key_tick_every_row_every_head(rollout120, t):
+    """Ticks 0-3 (pipeline fill: one, two, three, four active stages, no store
+    yet) and the last tick (full width, three history chunks on recycled
+    pages): every row of every active stage and head against the oracle
+    ([full text] Appendix B.6: the same outputs at every tick)."""
+    cfg = inputs.CONFIGS["rollout120"]
+    r = rollout120[t]
+    store = oracle.PageStore(cfg.P, cfg.H, cfg.D)
+    store.pages.update(r["pages"])
+    want = oracle.attention_tick_paged(r["q"], r["k"], r["v"], store, r["hist"], cfg.S,
+                                       r["mask"], 1.0 / np.sqrt(cfg.D))
+    worst = compare(torch.from_numpy(r["o"]), want, label=f"tick {t} all rows")
+    say(f"[rollout] tick {t}: every row of {len(want)} stages x {cfg.H} heads, "
+        f"worst rel-L2 {worst:.2e}")

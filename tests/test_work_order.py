@@ -37,6 +37,7 @@ CASES = [
     ("fill", 4, 0b00111, 4680, 12, 0, None),                 # fill tick, no store yet
     ("budgets", 4, 0b11111, 4680, 12, 3, [0, 1, 1, 2, 3]),   # per-slot history budgets
     ("small", 2, 0b101, 700, 3, 1, None),
+    ("plain", 7, 0xFF, 96, 40, 1, None),                     # 320 groups: plain order
 ]
 
 
@@ -104,3 +105,18 @@ def test_work_order_errors():
                                          __import__("ctypes").byref(n))
     assert st == -1  # capacity too small
     assert wf.library().wf_tick_work_order(__import__("ctypes").byref(d), 32, None, 0, None) == -1
+
+
+def test_plain_order_when_tables_overflow():
+    """8 slots x 40 heads = 320 (stage, head) groups exceed the XCD tables: one
+    item per block, blocks in stage-major order (heaviest stage first), head,
+    then query tile — the order the kernel decodes when no table is used."""
+    S, mask, T, H = 7, 0xFF, 96, 40
+    order = wf.tick_work_order(desc(S, mask, T, H, 1), 32)
+    ntq = -(-T // 256)
+    assert len(order) == (S + 1) * H * ntq
+    assert np.array_equal(order[:, 0], np.arange(len(order)))      # one item per block
+    stages = [s for s in range(S + 1)]
+    stages.sort(key=lambda s: -keys_of(S, mask, 1, None, s))        # heaviest first (stable)
+    want = [(s, h, q) for s in stages for h in range(H) for q in range(ntq)]
+    assert [tuple(int(v) for v in r[1:]) for r in order] == want

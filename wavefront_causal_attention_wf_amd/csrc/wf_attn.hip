@@ -662,10 +662,13 @@ attn_tick_kernel(const AttnParams p) {
         }
       // the row's amax (lanes l and l + 32 hold the two halves of one row), its
       // scale amax / 448 and the codes of q * (448 / amax), as the keys' producer
+      // (a row with amax below 2^-100 is stored as zero, as its producer does
+      // for key tiles: 448 / amax would leave float32's range)
       am = xlane32_max(am);
-      const float inv = am > 0.f ? 448.0f / am : 0.f;
+      const bool big = am >= 0x1p-100f;
+      const float inv = big ? 448.0f / am : 0.f;
       const float qscale = am / 448.0f;
-      cq = qscale > 0.f ? u.c * qscale : u.c;  // zero row: zero codes, any multiplier
+      cq = big ? u.c * qscale : u.c;  // zero row: zero codes, any multiplier
 #pragma unroll
       for (int dh = 0; dh < 2; ++dh)
 #pragma unroll

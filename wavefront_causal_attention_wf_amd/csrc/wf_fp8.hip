@@ -8,7 +8,8 @@
 // name the technique but not the format or the scale granularity. Here: e4m3
 // (largest finite value 448), scale = amax / 448 over the tile's keys of one
 // head, code = e4m3(x * (448 / amax)) rounded to nearest even, both divisions
-// and the product in fp32 (correctly rounded). A tile is 64 consecutive tokens
+// and the product in fp32 (correctly rounded); a tile with amax below 2^-100
+// is stored as zero (scale 0, zero codes). A tile is 64 consecutive tokens
 // of one page (pages hold a multiple of 64 tokens), so the attention kernel's
 // 64-key tiles each carry one scale per head.
 //
@@ -18,8 +19,8 @@
 // zero V), and a tile with no token of the chunk has scale 0.
 //
 // With 8-bit values (v_exp set) V is quantised too, per (64-token tile, head)
-// with a power-of-two scale 2^e (e the smallest integer with amax <= 448 * 2^e,
-// 0 for an all-zero tile; v_exp holds e + 127) and stored the way the
+// with a power-of-two scale 2^e (e the smallest integer >= -127 with
+// amax <= 448 * 2^e, 0 for an all-zero tile; v_exp holds e + 127) and stored the way the
 // attention kernel's P.V operand reads it: the V pool is
 // [num_pages][P/64][H][D][64] bytes, row d of tile (page, sub-tile, head)
 // holding channel d of its 64 tokens in the order of the kernel's score
@@ -37,6 +38,7 @@ namespace {
 constexpr int kQThreads = 256;
 constexpr int kScaleTile = 64;
 constexpr float kE4m3Max = 448.0f;
+constexpr float kTinyAmax = 0x1p-100f;  // smaller key tiles are stored as zero
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -49,8 +51,10 @@ __device__ __forceinline__ uint32_t e4m3x4(uint32_t w0, uint32_t w1, float inv) 
   return uint32_t(r);
 }
 
-// Smallest e with amax <= 448 * 2^e (amax > 0 and finite): amax = f * 2^E with
-// 0.5 <= f < 1 and 448 = 0.875 * 2^9, so e = E - 9 when f <= 0.875, else E - 8.
+// Smallest e >= -127 with amax <= 448 * 2^e (amax > 0 and finite): amax =
+// f * 2^E with 0.5 <= f < 1 and 448 = 0.875 * 2^9, so e = E - 9 when
+// f <= 0.875, else E - 8; -127 is the smallest exponent of the E8M0 scale byte
+// (a smaller tile keeps e = -127: its values times 2^127 stay below 448).
 __device__ __forceinline__ int pow2_exponent(float amax) {
   if (!(amax > 0.f)) return 0;
   uint32_t u = __float_as_uint(amax);
@@ -60,7 +64,8 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
     E = -117 - __clz(u);
     u <<= shift;
   }
-  return ((u & 0x7fffffu) <= 0x600000u) ? E - 9 : E - 8;  // f <= 0.875 <=> mantissa <= 0.75
+  const int e = ((u & 0x7fffffu) <= 0x600000u) ? E - 9 : E - 8;  // f <= 0.875 <=> mantissa <= 0.75
+  return e < -127 ? -127 : e;
 }
 
 // Column of token t (0..63) within a transposed 8-bit V row (see above).
@@ -147,8 +152,11 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
     if (threadIdx.x == 0) v_exp[(pid * spp + sub) * H + h] = uint8_t(e + 127);
     return;
   }
-  const float inv = am > 0.f ? kE4m3Max / am : 0.f;
-  if (threadIdx.x == 0) k_scale[(pid * spp + sub) * H + h] = am / kE4m3Max;
+  // a tile with amax below kTinyAmax is stored as zero (scale 0, zero codes):
+  // 448 / amax would leave float32's range, or amax / 448 its normal range
+  const bool big = am >= kTinyAmax;
+  const float inv = big ? kE4m3Max / am : 0.f;
+  if (threadIdx.x == 0) k_scale[(pid * spp + sub) * H + h] = big ? am / kE4m3Max : 0.f;
 
   typedef unsigned v2u __attribute__((ext_vector_type(2)));
 #pragma unroll
