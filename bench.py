@@ -14,9 +14,10 @@ Prints one JSON line. `value` = useful TFLOP/s of the whole step (mask-true
 query-key pairs x 4*D flops x H); `roofline` = the attention kernel alone,
 timed with HIP events on its launch stream; `cpu_baseline` = the fp64 CPU
 oracle on a bounded sample of the same tick. Also reported: the same tick with
-a separate store launch, the store and rotary-store kernels' bandwidth, and the
+a separate store launch, the store and rotary-store kernels' bandwidth, the
 fully paged flow (every live chunk rotated into pages, attention reading the
-whole context through pages).
+whole context through pages), the 8-bit tiers, the 5-step and 14B-like ticks
+(`configs`) and the 120-tick streaming rollout timed whole (`rollout120`).
 """
 from __future__ import annotations
 
@@ -559,6 +560,152 @@ def store_fp8_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) 
             "rotation": rotation}
 
 
+def other_config(name: str, dev, steps: int = 10, warmup: int = 3) -> dict:
+    """Steady ticks of another full-size configuration, timed like the main one
+    (the attention launch with the store chunk's page write, HIP events)."""
+    import torch
+
+    from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+    cfg = inputs.CONFIGS[name]
+    ro = Rollout(cfg, 2, dev)
+    flops = wfattn.wf_tick_useful_flops(cfg.S, ro.mask, cfg.T, cfg.H, cfg.D, cfg.n_hist, P=cfg.P,
+                                        num_pages=cfg.num_pages)
+    for _ in range(warmup):
+        ro.step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        ro.step(ev[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    attn = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    tf = flops / (attn * 1e-3) / 1e12
+    del ro
+    torch.cuda.empty_cache()
+    return {"workload": f"{name}: S={cfg.S} (width {cfg.S + 1}), T={cfg.T}, H={cfg.H}, "
+                        f"D={cfg.D}, {cfg.n_hist} history chunks in P={cfg.P} pages of a "
+                        f"{cfg.num_pages}-page pool",
+            "useful_tflop_per_tick": round(flops / 1e12, 4), "ms_per_step": round(ms, 4),
+            "ticks_per_s": round(1e3 / ms, 2), "attn_kernel_ms_mean": round(attn, 4),
+            "useful_tflop_per_s": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def active_slots(t: int, S: int) -> int:
+    """Occupied slots at rollout tick t from an empty start ([summary]
+    Methodology 1: stage s holds chunk t - s, the store chunk t - S; a slot is
+    occupied once its chunk exists)."""
+    return (1 << (min(t, S) + 1)) - 1
+
+
+def rollout120(dev, warmup: int = 1) -> dict:
+    """The 120-tick streaming rollout at the 1.3B 4-step shape, timed whole.
+
+    Every tick's live Q/K/V (fresh seeded N(0, 0.5^2) draws) is generated on
+    the device before the timed region (120 x 3 x 71.9 MB = 25.9 GB). From an
+    empty history the stages fill one per tick and the store joins at tick S;
+    each tick with the store: alloc (host page table) -> its page ids to the
+    device -> the history table to the device -> wf_attn_tick (all occupied
+    query chunks plus the store chunk's page write, one launch) -> commit
+    (promotion, eviction of the oldest chunk beyond the 3-chunk window, host).
+    `warmup` whole rollouts run first on a separate page table."""
+    import torch
+
+    from wavefront_causal_attention_wf_amd import inputs, wfattn
+
+    cfg = inputs.CONFIGS["rollout120"]
+    S, T, H, D, P = cfg.S, cfg.T, cfg.H, cfg.D, cfg.P
+    ticks = cfg.ticks
+    live = [inputs.draw_live_torch(cfg, inputs.rollout_seed(t), dev) for t in range(ticks)]
+    k_pool = torch.zeros((cfg.num_pages, P, H, D), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.zeros_like(k_pool)
+    o = torch.empty_like(live[0][0])
+    ppc = cfg.ppc
+    nslot = 8
+    ids_host = torch.empty((nslot, ppc), dtype=torch.int32, pin_memory=True)
+    hist_host = torch.empty((nslot, cfg.window * ppc), dtype=torch.int32, pin_memory=True)
+    ids_dev = torch.empty((nslot, ppc), dtype=torch.int32, device=dev)
+    hist_dev = torch.empty((nslot, cfg.window * ppc), dtype=torch.int32, device=dev)
+    scale = 1.0 / float(np.sqrt(D))
+    flops = []
+    n_hist = 0
+    for t in range(ticks):
+        flops.append(wfattn.wf_tick_useful_flops(S, active_slots(t, S), T, H, D, n_hist, P=P,
+                                                 num_pages=cfg.num_pages))
+        if t >= S:
+            n_hist = min(n_hist + 1, cfg.window)
+    torch.cuda.synchronize()
+
+    def run(events=None):
+        pt = wfattn.PageTable(cfg.num_pages, P, T, cfg.window,
+                              initial_free_order=inputs.initial_free_order(cfg))
+        slot_ev = [None] * nslot
+        for t in range(ticks):
+            slot = t % nslot
+            if slot_ev[slot] is not None:
+                slot_ev[slot].synchronize()
+            if events is not None:
+                events[t].record()
+            q, k, v = live[t]
+            mask = active_slots(t, S)
+            store = None
+            if t >= S:
+                ids_host[slot].numpy()[:] = pt.alloc_chunk()
+                ids_dev[slot].copy_(ids_host[slot], non_blocking=True)
+                store = ids_dev[slot]
+            hist = pt.export()
+            nh = hist.shape[0]
+            hd = None
+            if nh:
+                hist_host[slot].numpy()[:nh * ppc] = hist.reshape(-1)
+                hd = hist_dev[slot][:nh * ppc].view(nh, ppc)
+                hd.copy_(hist_host[slot][:nh * ppc].view(nh, ppc), non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record()
+            slot_ev[slot] = ev
+            wfattn.wf_attn_tick(q, k, v, o, S, mask, scale, k_pool, v_pool, hd,
+                                store_pages=store)
+            if t >= S:
+                pt.commit()
+        if events is not None:
+            events[ticks].record()
+        pt.close()
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(ticks + 1)]
+    wall0 = time.perf_counter()
+    run(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    tick_ms = np.array([events[t].elapsed_time(events[t + 1]) for t in range(ticks)])
+    total_ms = events[0].elapsed_time(events[ticks])
+    flops = np.array(flops)
+
+    def part(lo: int) -> dict:
+        ms = float(tick_ms[lo:].sum())
+        return {"ticks": ticks - lo, "ms": round(ms, 3), "ticks_per_s": round((ticks - lo) * 1e3 / ms, 2),
+                "useful_tflop_per_s": round(float(flops[lo:].sum()) / (ms * 1e-3) / 1e12, 2),
+                "tick_ms_p50": round(float(np.median(tick_ms[lo:])), 4)}
+
+    out = {"workload": f"rollout120: {ticks} consecutive ticks from an empty history, S={S}, "
+                       f"T={T}, H={H}, D={D}, window {cfg.window} chunks, {cfg.num_pages}-page "
+                       f"FIFO pool, fresh Q/K/V per tick (pre-generated on the device)",
+           "ticks_per_s": round(ticks * 1e3 / total_ms, 2), "total_ms": round(total_ms, 3),
+           "wall_ms": round(wall * 1e3, 3),
+           "useful_tflop_per_s": round(float(flops.sum()) / (total_ms * 1e-3) / 1e12, 2),
+           "ticks_3_to_119": part(3),
+           "full_width_ticks_7_to_119": part(S + cfg.window)}
+    del live, k_pool, v_pool, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def profile_mode(args, cfg, dev) -> None:
     """Launch-only loops for profilers (no JSON line)."""
     import torch
@@ -739,6 +886,15 @@ def main():
     log(f"fp8 K/V tier: {out['fp8kv_tier']}")
     out["store_fp8"] = store_fp8_bandwidth(cfg, dev)
     log(f"fp8 store: {out['store_fp8']}")
+    if cfg.name == "wan13_4step":
+        del ro
+        torch.cuda.empty_cache()
+        out["configs"] = {}
+        for name in ("wan13_5step", "wan14b_4step"):
+            out["configs"][name] = other_config(name, dev)
+            log(f"{name}: {out['configs'][name]}")
+        out["rollout120"] = rollout120(dev)
+        log(f"rollout120: {out['rollout120']}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_s)

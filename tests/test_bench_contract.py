@@ -45,3 +45,11 @@ def test_recorded_traffic_follows_the_kernel_hash(tmp_path, monkeypatch):
     assert value is None and "changed" in why
     monkeypatch.setattr(bench, "COUNTERS_FILE", str(tmp_path / "missing.md"))
     assert bench.recorded_traffic("wan13_4step")[0] is None
+
+
+def test_rollout_driver_fill_masks_match_the_oracle():
+    """The bench's rollout driver occupies slots as the tick composition says."""
+    import oracle
+    for S in (2, 4, 5):
+        for t in range(3 * S):
+            assert bench.active_slots(t, S) == oracle.active_mask_for_tick(t, S), (S, t)
