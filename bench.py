@@ -211,8 +211,36 @@ def separate_store_step(cfg, dev, steps: int = 10, warmup: int = 3) -> dict:
             "attn_kernel_ms_mean": round(attn, 4)}
 
 
+def graph_time_ms(fn, rotation: int, launches: int) -> float:
+    """Mean device time per launch of fn(0), fn(1), ... (fn(i) launches one
+    kernel on the current stream): `launches` launches captured once in a HIP
+    graph and replayed, HIP events around the replays, so the host's per-call
+    cost (argument checks, ctypes) does not pace launches of ~10 us."""
+    import torch
+
+    for i in range(rotation):  # warm, and nothing lazy left for the capture
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (reps * launches)
+    del g
+    return ms
+
+
 def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> dict:
-    """wf_store_paged and wf_gather_paged alone, HIP events on their stream.
+    """wf_store_paged and wf_gather_paged alone (graph_time_ms).
 
     cold: rotating over `rotation` distinct source chunks and page sets (the
     sources alone exceed the 256 MB last-level cache); warm: one chunk and page set
@@ -239,16 +267,7 @@ def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> d
     vd = torch.empty_like(kd)
 
     def timed(fn) -> float:
-        for i in range(rotation):  # warm
-            fn(i)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(launches):
-            fn(i)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / launches
+        return graph_time_ms(fn, rotation, launches)
 
     store_cold = timed(lambda i: wfattn.wf_store_paged(ksrc[i % rotation], vsrc[i % rotation],
                                                        kp, vp, ids[i % rotation]))
@@ -278,7 +297,7 @@ def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> d
 
 
 def rope_store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> dict:
-    """wf_rope_store_paged alone (HIP events on its stream), inputs rotated over
+    """wf_rope_store_paged alone (graph_time_ms), inputs rotated over
     `rotation` chunks and page sets like the store measurement: reads K and V of
     one chunk, rotates K, writes the chunk's whole pages of K and V."""
     import torch
@@ -302,16 +321,7 @@ def rope_store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION)
         wfattn.wf_rope_store_paged(ksrc[i % rotation], vsrc[i % rotation], kp, vp,
                                    ids[i % rotation], grid, 3 * (100 + i))
 
-    for i in range(rotation):
-        launch(i)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(launches):
-        launch(i)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / launches
+    ms = graph_time_ms(launch, rotation, launches)
     nbytes = 2 * (T * H * D * 2) + 2 * (ppc * P * H * D * 2)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "wf_rope_store_paged", "us_mean": round(ms * 1e3, 2), "bytes": nbytes,
@@ -543,16 +553,7 @@ def store_fp8_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) 
         k, v = srcs[i % rotation]
         wfattn.wf_store_paged_fp8(k[0], v[0], k_pool, k_scale, v_pool, ids[(i * 3) % rotation])
 
-    for i in range(rotation):
-        launch(i)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(launches):
-        launch(i)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / launches
+    ms = graph_time_ms(launch, rotation, launches)
     nbytes = 2 * (T * H * D * 2) + ppc * P * H * D * 3 + ppc * (P // 64) * H * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "wf_store_paged_fp8", "us_mean": round(ms * 1e3, 2), "bytes": nbytes,

@@ -111,6 +111,9 @@ wf_status wf_page_table_num_free(const wf_page_table* pt, int32_t* out);
 /* k_src, v_src: device bf16 [T][H][D]; k_pool, v_pool: device bf16           */
 /* [num_pages][P][H][D]; page_ids: device int32 [ceil(T/P)], each in          */
 /* [0, num_pages). All pointers 16-byte aligned; H*D*2 a multiple of 16 bytes. */
+/* Errors: WF_EINVAL for bad sizes, NULL or misaligned pointers, ceil(T/P) >   */
+/* num_pages; WF_EUNSUPPORTED when K and V together exceed 2^32 16-byte units */
+/* (64 GiB); WF_EHIP if the launch fails. T = 0 is a no-op.                  */
 /* ------------------------------------------------------------------------ */
 wf_status wf_store_paged(const void* k_src, const void* v_src, void* k_pool, void* v_pool,
                          const int32_t* page_ids, int32_t T, int32_t H, int32_t D,
@@ -199,7 +202,8 @@ wf_status wf_store_paged_fp8(const void* k_src, const void* v_src, void* k_pool,
 /* ------------------------------------------------------------------------ */
 /* wf_gather_paged — diagnostic inverse of the store: copy n_chunks chunks    */
 /* from pool pages into contiguous k_dst, v_dst bf16 [n_chunks][T][H][D].     */
-/* page_ids: device int32 [n_chunks][ceil(T/P)]. Same alignment rules.        */
+/* page_ids: device int32 [n_chunks][ceil(T/P)]. Same alignment rules and     */
+/* errors (the 2^32-unit limit counts the n_chunks chunks of K and of V).      */
 /* ------------------------------------------------------------------------ */
 wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t* page_ids,
                           int32_t n_chunks, void* k_dst, void* v_dst, int32_t T, int32_t H,

@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
     const int c = e - tok * UPR;
     const int t = tok0 + tok;
     const int64_t src = (int64_t(t) * H + h) * UPR + c;
-    x[u] = t < T ? (is_v ? v_src : k_src)[src] : make_uint4(0u, 0u, 0u, 0u);
-    vx[u] = (t < T && !v8) ? v_src[src] : make_uint4(0u, 0u, 0u, 0u);
+    x[u] = t < T ? load_stream16((is_v ? v_src : k_src) + src) : make_uint4(0u, 0u, 0u, 0u);
+    vx[u] = (t < T && !v8) ? load_stream16(v_src + src) : make_uint4(0u, 0u, 0u, 0u);
     dst_row[u] = ((pid * P + sub * kScaleTile + tok) * H + h) * UPR + c;  // in 16-byte units
   }
 #pragma unroll

@@ -23,6 +23,14 @@ __device__ __forceinline__ void store_stream16(uint4* dst, const uint4& v) {
   __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(dst));
 }
 
+// 16-byte load that streams past the caches (nontemporal): for sources a
+// kernel reads exactly once.
+__device__ __forceinline__ uint4 load_stream16(const uint4* src) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Maps a failed HIP call to WF_EHIP with the runtime's text.
 inline int32_t hip_fail(hipError_t e, const char* where) {
   return fail(WF_EHIP, "%s: %s (%d)", where, hipGetErrorString(e), int(e));

@@ -23,8 +23,8 @@
 // token for four heads, so each angle's sine and cosine serve four heads and
 // four 16-byte loads are in flight per thread. A wave covers 4 (D = 128) or 8
 // (D = 64) tokens, 256 contiguous bytes per (token, head) row. HBM-bound: reads
-// K and V once, writes whole pages (zeros past the chunk's last token) with
-// nontemporal stores.
+// K and V once and writes whole pages (zeros past the chunk's last token), both
+// nontemporal.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(const RopePara
   const uint4* src = (is_v ? p.v_src : p.k_src) + (int64_t(t) * H + h0) * U + u;
 #pragma unroll
   for (int i = 0; i < kRopeHeads; ++i)  // every load in flight before any store
-    if (i < nh) x[i] = src[int64_t(i) * U];
+    if (i < nh) x[i] = load_stream16(src + int64_t(i) * U);
   if (!is_v) {
     // the four pairs of this unit: 4u .. 4u+3
     const int rc = p.rows * p.cols;
