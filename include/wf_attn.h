@@ -57,7 +57,7 @@ const char* wf_last_error(void);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t wf_abi_version(void);
-#define WF_ABI_VERSION 5
+#define WF_ABI_VERSION 6
 
 /* ------------------------------------------------------------------------ */
 /* Page table: host-only state for one request's attention pages.            */
@@ -296,18 +296,26 @@ typedef struct wf_tick_desc {
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);
 
 /* Diagnostic, host only: the work order wf_attn_tick would launch for this
- * descriptor. Row i = out[4i .. 4i+3] = (block, slot, head, query tile): the
- * attention block (counted after the blocks that write the store's pages)
- * that computes query tile (256 rows) of that slot and head, rows of one block
- * in the order it runs them; block b runs on XCD b % 8. cus_per_xcd: compute
- * units per XCD to plan for (<= 0: the current device's). *n_items receives
- * the row count; out (host int32, capacity elements, may be NULL to query the
- * count) must hold 4 * n_items.
+ * descriptor. Row i = out[6i .. 6i+5] = (block, item, slot, head, first query
+ * row, rows): attention block `block` (counted after the blocks that write the
+ * store's pages; it runs on XCD block % 8) computes query rows [first, first +
+ * rows) of that slot and head in its item number `item`, items in the order
+ * the block runs them. An ordinary item is one query tile (256 rows) of one
+ * slot; a tail item holds the last query tile's rows of several slots of one
+ * head, one row per slot. cus_per_xcd: compute units per XCD to plan for
+ * (<= 0: the current device's). *n_items receives the row count; out (host
+ * int32, capacity elements, may be NULL to query the count) must hold
+ * 6 * n_items.
  * The plan ([summary] Methodology 3: stage s reads N_s keys, so work items
  * differ in length): (slot, head) groups, heaviest first, are dealt to the
  * least-loaded XCD (split between two XCDs to even the loads), and each XCD's
  * items are packed onto its CUs, one block per CU running its list, longest
- * first. Ticks whose plan does not fit the kernel's tables run one item per
+ * first. When every slot's last query tile holds at most 128 rows and the
+ * slots' contexts nest (equal history budgets), those tiles of one head are
+ * merged into tail items of eight 32-row slices that walk the heaviest such
+ * slot's context with the live chunks in descending order, each slice's wave
+ * stopping after its own slot's chunks (bf16 keys with whole-tile sources
+ * only). Ticks whose plan does not fit the kernel's tables run one item per
  * block instead, whole groups per XCD. Errors as wf_attn_tick's validation;
  * WF_EINVAL for a short out or a NULL n_items. */
 wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_per_xcd, int32_t* out,

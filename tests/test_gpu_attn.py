@@ -53,12 +53,30 @@ def test_peaked_softmax_parity(qscale):
 
 def test_plain_work_order_parity():
     """More (stage, head) groups than the XCD tables hold (8 slots x 40 heads =
-    320 > 256): the launch falls back to one item per block in stage-major
-    order. Every (stage, head) against the oracle."""
-    say("plain work order: S=7 T=96 H=40 D=64 P=16 n_hist=1")
-    t = setup_tick(7, 96, 40, 64, 16, 1, 32, seed=19)
+    320 > 256) and 200-row query tiles: the launch falls back to one item per
+    block in stage-major order. Every (stage, head) against the oracle."""
+    say("plain work order: S=7 T=200 H=40 D=64 P=16 n_hist=1")
+    t = setup_tick(7, 200, 40, 64, 16, 1, 64, seed=19)
     o = run_tick(t)
     worst = compare(o, oracle_tick(t), label="plain order")
+    say(f"  worst rel-L2 {worst:.2e}")
+
+
+@pytest.mark.parametrize("S,T,H,P,n_hist,mask", [
+    (7, 96, 40, 64, 1, 0xFF),      # one query tile: every row in tail items (3 per head)
+    (4, 300, 3, 64, 2, 0b11111),   # 44-row last tiles: 10 slices -> 2 tail items per head
+    (4, 330, 2, 128, 3, 0b00111),  # fill tick, no store: 74-row last tiles of 3 slots
+])
+def test_tail_items_parity(S, T, H, P, n_hist, mask):
+    """Last query tiles of several slots merged into tail items (each walks the
+    heaviest slot's context with the live chunks in descending order; waves of
+    lighter slots stop after their own chunks): every (stage, head) against
+    the oracle, and every row is written (outputs start as NaN)."""
+    say(f"tail items: S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b}")
+    t = setup_tick(S, T, H, 128, P, n_hist, (n_hist + 2) * -(-T // P) + 8, seed=T + S,
+                   active_mask=mask)
+    o = run_tick(t)
+    worst = compare(o, oracle_tick(t), label="tail items")
     say(f"  worst rel-L2 {worst:.2e}")
 
 

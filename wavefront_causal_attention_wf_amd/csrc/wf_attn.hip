@@ -52,9 +52,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
+#include <vector>
 
 #include "wf_internal.h"
 
@@ -126,6 +129,21 @@ struct AttnParams {
   // the list); its group is pack_grp[x][r].
   int32_t use_xcd;
   int32_t xcd_stride;
+  // Tail items (packed order only). The last query tile of every active slot
+  // (rows tail_row0 .. T-1, tail_spr 32-row slices) is not an item of its own:
+  // the slices of all slots of a head, laid out slot by slot in rank order, are
+  // cut into tail_per_head items of NWAVES slices, one slice per wave. An item
+  // walks the context of its first slice's slot with the live chunks in
+  // descending order (history, live store, S-1, S-2, ...), so each other
+  // slice's slot sees the first nseg[s] chunks of that walk, and its wave stops
+  // there. Item k of a packed list names one with group n_active * H + h *
+  // tail_per_head + m.
+  int32_t tail;           // 0: every query tile is an item of its own
+  int32_t tail_row0;
+  int32_t tail_spr;
+  int32_t tail_per_head;
+  int32_t tail_npre;      // leading chunks of every slot's walk: history + live store
+  int32_t n_active;       // active slots
   int16_t xcd_n[kNumXcd];
   int16_t xcd_groups[kXcdTable];
   int16_t pack_grp[kNumXcd][kPackSegs];
@@ -555,7 +573,8 @@ attn_tick_kernel(const AttnParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31;
     const int g = lane >> 5;
-    int rank, h, qt;
+    int rank = 0, h, qt;
+    int tail_m = -1;  // tail item index within its head, or -1
     if (p.use_xcd == 2) {
       const int x = b & (kNumXcd - 1);
       const int k = item;
@@ -571,8 +590,14 @@ attn_tick_kernel(const AttnParams p) {
       }
       const int grp = p.pack_grp[x][run];
       qt = p.pack_qt0[x][run] + before;
-      rank = grp / p.H;
-      h = grp - rank * p.H;
+      const int n_groups = p.n_active * p.H;
+      if (grp >= n_groups) {  // a tail item
+        h = (grp - n_groups) / p.tail_per_head;
+        tail_m = grp - n_groups - h * p.tail_per_head;
+      } else {
+        rank = grp / p.H;
+        h = grp - rank * p.H;
+      }
     } else if (p.use_xcd) {
       const int x = b & (kNumXcd - 1);
       const int k = b / kNumXcd;
@@ -588,18 +613,40 @@ attn_tick_kernel(const AttnParams p) {
       h = rem / p.ntq;
       qt = rem - h * p.ntq;
     }
-    const int s = p.stage_of_rank[rank];
-    const int nseg = p.nseg[s];
     const int T = p.T;
+    // s_blk: the slot whose context the item walks; s: the slot of this wave's
+    // query rows (they differ only in tail items); ntiles_w: the tiles of the
+    // walk this wave uses (a prefix)
+    int s_blk, s, q0w, ntiles_w;
+    bool wave_active;
+    if (tail_m >= 0) {
+      const int g0 = tail_m * NWAVES;
+      s_blk = p.stage_of_rank[g0 / p.tail_spr];
+      const int gw = g0 + wave;
+      const bool has = gw < p.n_active * p.tail_spr;
+      const int rank_w = has ? gw / p.tail_spr : 0;
+      s = p.stage_of_rank[rank_w];
+      q0w = p.tail_row0 + (gw - rank_w * p.tail_spr) * 32;
+      wave_active = has && q0w < T;
+      ntiles_w = p.nseg[s] * p.tps;
+    } else {
+      s_blk = s = p.stage_of_rank[rank];
+      q0w = qt * QROWS + wave * 32;  // first query row of this wave
+      wave_active = q0w < T;
+      ntiles_w = p.nseg[s] * p.tps;
+    }
+    const int nseg = p.nseg[s_blk];
     const int ntiles = nseg * p.tps;
 
     const Uniforms u = load_uniforms<D, KB>(p, h);
     if constexpr (kFast) {
       // sources of every tile of this (stage, head), one thread per tile
       for (int t = tid; t < ntiles; t += NTHREADS) {
-        const int sg = t / u.tps;
-        const int mm = t - sg * u.tps;
-        const int code = p.seg[s][sg];
+        const int sw = t / u.tps;  // chunk index of the walk
+        const int mm = t - sw * u.tps;
+        // tail items walk the live chunks in descending order
+        const int sg = (tail_m >= 0 && sw >= p.tail_npre) ? p.tail_npre + nseg - 1 - sw : sw;
+        const int code = p.seg[s_blk][sg];
         const uint32_t t0 = uint32_t(KT) * uint32_t(mm);
         uint64_t kr, vr;
         if (code >= 0 && !p.live_pages) {  // live chunk `code`, contiguous
@@ -636,8 +683,6 @@ attn_tick_kernel(const AttnParams p) {
     }
     __syncthreads();
 
-    const int q0w = qt * QROWS + wave * 32;  // first query row of this wave
-    const bool wave_active = q0w < T;
     const int qrow = q0w + r;
 
     // ---- Q^T operand: lane holds query qrow, head dims 16*ks + 8*g .. +7 -----
@@ -735,7 +780,7 @@ attn_tick_kernel(const AttnParams p) {
     ld.init(u, wave, lane);
     auto resolve = [&]() __attribute__((always_inline)) {
       if constexpr (kFast) ld.prepare_table(tile_tab, ntiles);
-      else ld.prepare(p, u, pages_lds, s, nseg);
+      else ld.prepare(p, u, pages_lds, s_blk, nseg);
     };
     if constexpr (kFast) ld.start_table(tile_tab);
     resolve();
@@ -1027,7 +1072,7 @@ attn_tick_kernel(const AttnParams p) {
       for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
       resolve();  // the tile this wave loads next
       __builtin_amdgcn_sched_barrier(0);
-      if (wave_active) {
+      if (wave_active && js < ntiles_w) {
         softmax(js, kF8 ? cq * ks_next : cq, sacc);
         __builtin_amdgcn_sched_barrier(0);
         uint32_t vl = v_lane;
@@ -1103,9 +1148,14 @@ attn_tick_kernel(const AttnParams p) {
     // G(j) then S(j+1); buffers vbuf, kbuf: V of tile j and K of tile j+1 (tile
     // t is in buffer t % 4); (ka_, va_) / (kb_, vb_): where A's / B's loads of
     // S(j+1) go (A: tile j+3, B: tile j+4).
+    // A wave runs P.V of tile j (and Q.K^T of tile j+1, whose scores are used
+    // only if j+1 < ntiles_w) for j < ntiles_w, and the softmax of tile j for
+    // j < ntiles_w: tiles past its prefix are loaded for the other waves but
+    // never enter its arithmetic, and the group of four tiles that overhangs
+    // the walk costs no MFMA.
     auto slot_pair = [&](int j, int vbuf, int kbuf, uint16_t* ka_, uint16_t* va_, uint16_t* kb_,
                          uint16_t* vb_) __attribute__((always_inline)) {
-      if (wave_active) {
+      if (wave_active && j < ntiles_w) {
         // the MFMA phase wins issue arbitration over the other wave's softmax
         __builtin_amdgcn_s_setprio(1);
         gphase(vbuf, kbuf, j + 1);
@@ -1250,112 +1300,308 @@ bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, AttnParams& p
   const int ntq = p.ntq;
   if (ntq > 32767) return false;
   const int G = pl.n_active * H;
-  if (G > 32767) return false;
+  const int n_tail = p.tail ? H * p.tail_per_head : 0;
+  if (int64_t(G) + n_tail > 32767) return false;
   constexpr int kStartup = 2;  // start-up cost of a workgroup, in key tiles
-  auto weight = [&](int g) { return int(pl.nseg[pl.order[g / H]]) * tps + kStartup; };
+  // work groups: (stage, head) groups of ntq query tiles (ntq - 1 with tail
+  // items), and the tail items, one each; heaviest first
+  struct Group { int grp, n, w; };
+  std::vector<Group> groups;
+  const int ntq_full = p.tail ? ntq - 1 : ntq;
+  for (int g = 0; g < G && ntq_full > 0; ++g)
+    groups.push_back(Group{g, ntq_full, int(pl.nseg[pl.order[g / H]]) * tps + kStartup});
+  for (int t = 0; t < n_tail; ++t) {
+    const int m = t % p.tail_per_head;
+    const int s_walk = pl.order[(m * NWAVES) / p.tail_spr];
+    groups.push_back(Group{G + t, 1, int(pl.nseg[s_walk]) * tps + kStartup});
+  }
+  std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.w > b.w; });
   int64_t total = 0;
-  for (int g = 0; g < G; ++g) total += int64_t(weight(g)) * ntq;
-  const double target = double(total) / kNumXcd;
-  struct Run { int grp, qt0, n; };
-  Run runs[kNumXcd][kPackSegs];
-  int nrun[kNumXcd] = {0};
-  int64_t load[kNumXcd] = {0};
-  for (int g = 0; g < G; ++g) {  // groups are in rank order: heaviest first
-    const int w = weight(g);
-    int rem = ntq, qt = 0;
-    while (rem > 0) {
-      int x = 0;
-      for (int i = 1; i < kNumXcd; ++i)
-        if (load[i] < load[x]) x = i;
-      const double room = target - double(load[x]);
-      int n = room <= 0 ? rem : std::min(rem, std::max(1, int(std::ceil(room / w))));
-      if (nrun[x] == kPackSegs) return false;
-      runs[x][nrun[x]++] = Run{g, qt, n};
-      load[x] += int64_t(n) * w;
-      rem -= n;
-      qt += n;
-    }
-  }
-  for (int x = 0; x < kNumXcd; ++x) {
-    int n_items = 0;
-    for (int r = 0; r < nrun[x]; ++r) n_items += runs[x][r].n;
-    if (n_items > kPackItems) return false;
-  }
-  for (int x = 0; x < kNumXcd; ++x) {
-    // items of this XCD: run index and length, longest first (runs already are)
-    int item_run[kPackItems], item_w[kPackItems];
-    int n = 0;
-    for (int r = 0; r < nrun[x]; ++r)
-      for (int i = 0; i < runs[x][r].n; ++i) {
-        item_run[n] = r;
-        item_w[n] = weight(runs[x][r].grp);
-        ++n;
+  for (const Group& gr : groups) total += int64_t(gr.w) * gr.n;
+  struct Run { int grp, qt0, n, w; };
+  struct Packed {
+    int16_t grp[kNumXcd][kPackSegs], qt0[kNumXcd][kPackSegs], bin[kNumXcd][kPackBins + 1];
+    uint32_t code[kNumXcd][kPackItems / 8];
+    int16_t n[kNumXcd];
+  };
+  // Deal the groups to XCDs against a per-XCD target, then pack each XCD's
+  // items onto its CUs; returns the busiest CU's load, or -1 if the tables do
+  // not hold the plan.
+  auto plan_with = [&](double target, Packed& out) -> int64_t {
+    Run runs[kNumXcd][kPackSegs];
+    int nrun[kNumXcd] = {0};
+    int64_t load[kNumXcd] = {0};
+    for (const Group& gr : groups) {
+      const int w = gr.w;
+      int rem = gr.n, qt = 0;
+      while (rem > 0) {
+        int x = 0;
+        for (int i = 1; i < kNumXcd; ++i)
+          if (load[i] < load[x]) x = i;
+        const double room = target - double(load[x]);
+        int n = room <= 0 ? rem : std::min(rem, std::max(1, int(std::ceil(room / w))));
+        if (nrun[x] == kPackSegs) return -1;
+        runs[x][nrun[x]++] = Run{gr.grp, qt, n, w};
+        load[x] += int64_t(n) * w;
+        rem -= n;
+        qt += n;
       }
-    // bins: item indices; longest first into the emptiest bin
-    std::vector<std::vector<int>> bin(C);
-    std::vector<int64_t> bl(C, 0);
-    for (int i = 0; i < n; ++i) {
-      int b = 0;
-      for (int j = 1; j < C; ++j)
-        if (bl[j] < bl[b]) b = j;
-      bin[b].push_back(i);
-      bl[b] += item_w[i];
     }
-    // moves and swaps out of the fullest bin while they lower it
-    for (int iter = 0; iter < 4096; ++iter) {
-      int hi = 0;
-      for (int j = 1; j < C; ++j)
-        if (bl[j] > bl[hi]) hi = j;
-      bool done = false;
-      for (int lo = 0; lo < C && !done; ++lo) {
-        if (lo == hi) continue;
-        for (size_t ai = 0; ai < bin[hi].size() && !done; ++ai) {
-          const int a = bin[hi][ai];
-          if (bl[lo] + item_w[a] < bl[hi]) {  // move a
-            bin[hi].erase(bin[hi].begin() + ai);
-            bin[lo].push_back(a);
-            bl[hi] -= item_w[a];
-            bl[lo] += item_w[a];
-            done = true;
-            break;
-          }
-          for (size_t bi = 0; bi < bin[lo].size(); ++bi) {
-            const int c = bin[lo][bi];
-            const int d = item_w[a] - item_w[c];
-            if (d > 0 && bl[lo] + d < bl[hi]) {  // swap a and c
-              bin[hi][ai] = c;
-              bin[lo][bi] = a;
-              bl[hi] -= d;
-              bl[lo] += d;
-              done = true;
-              break;
-            }
-          }
+    for (int x = 0; x < kNumXcd; ++x) {
+      int n_items = 0;
+      for (int r = 0; r < nrun[x]; ++r) n_items += runs[x][r].n;
+      if (n_items > kPackItems) return -1;
+    }
+    int64_t busiest = 0;
+    for (int x = 0; x < kNumXcd; ++x) {
+      // items of this XCD: run index and length, longest first (runs already are)
+      int item_run[kPackItems], item_w[kPackItems];
+      int n = 0;
+      for (int r = 0; r < nrun[x]; ++r)
+        for (int i = 0; i < runs[x][r].n; ++i) {
+          item_run[n] = r;
+          item_w[n] = runs[x][r].w;
+          ++n;
         }
+      // bins: item indices; longest first into the emptiest bin
+      std::vector<std::vector<int>> bin(C);
+      std::vector<int64_t> bl(C, 0);
+      for (int i = 0; i < n; ++i) {
+        int b = 0;
+        for (int j = 1; j < C; ++j)
+          if (bl[j] < bl[b]) b = j;
+        bin[b].push_back(i);
+        bl[b] += item_w[i];
       }
-      if (!done) break;
+      // Local search on the fullest bin: among moving one item out of it and
+      // exchanging one or two of its items for zero, one or two of another bin's,
+      // take the exchange that leaves the pair's larger load smallest, while that
+      // is below the fullest load. (Items come in a few lengths — one per stage —
+      // so single moves and swaps alone stall well above the mean load.)
+      for (int iter = 0; iter < 4096; ++iter) {
+        int hi = 0;
+        for (int j = 1; j < C; ++j)
+          if (bl[j] > bl[hi]) hi = j;
+        // best exchange: sets of up to two positions in bin[hi] and in bin[lo]
+        int64_t best = bl[hi];
+        int b_lo = -1, b_a[2] = {-1, -1}, b_c[2] = {-1, -1};
+        const std::vector<int>& H_ = bin[hi];
+        const int nh = int(H_.size());
+        for (int lo = 0; lo < C; ++lo) {
+          if (lo == hi) continue;
+          const std::vector<int>& L_ = bin[lo];
+          const int nl = int(L_.size());
+          // (a0, a1): positions in hi (a1 = -1: one item); (c0, c1): in lo (-1: none)
+          for (int a0 = 0; a0 < nh; ++a0)
+            for (int a1 = -1; a1 < nh; ++a1) {
+              if (a1 >= 0 && a1 <= a0) continue;
+              const int wa = item_w[H_[a0]] + (a1 >= 0 ? item_w[H_[a1]] : 0);
+              for (int c0 = -1; c0 < nl; ++c0)
+                for (int c1 = -1; c1 < nl; ++c1) {
+                  if (c0 < 0 && c1 >= 0) continue;
+                  if (c1 >= 0 && c1 <= c0) continue;
+                  const int wc = (c0 >= 0 ? item_w[L_[c0]] : 0) + (c1 >= 0 ? item_w[L_[c1]] : 0);
+                  const int d = wa - wc;
+                  if (d <= 0) continue;
+                  const int64_t m = std::max(bl[hi] - d, bl[lo] + d);
+                  if (m < best) {
+                    best = m;
+                    b_lo = lo;
+                    b_a[0] = a0; b_a[1] = a1; b_c[0] = c0; b_c[1] = c1;
+                  }
+                }
+            }
+        }
+        if (b_lo < 0) break;
+        std::vector<int> out_hi, out_lo;
+        std::vector<int> keep_hi, keep_lo;
+        for (int i = 0; i < nh; ++i) (i == b_a[0] || i == b_a[1] ? out_hi : keep_hi).push_back(H_[i]);
+        for (int i = 0; i < int(bin[b_lo].size()); ++i)
+          (i == b_c[0] || i == b_c[1] ? out_lo : keep_lo).push_back(bin[b_lo][i]);
+        for (int it : out_lo) keep_hi.push_back(it);
+        for (int it : out_hi) keep_lo.push_back(it);
+        int64_t l_hi = 0, l_lo = 0;
+        for (int it : keep_hi) l_hi += item_w[it];
+        for (int it : keep_lo) l_lo += item_w[it];
+        bin[hi] = keep_hi;
+        bin[b_lo] = keep_lo;
+        bl[hi] = l_hi;
+        bl[b_lo] = l_lo;
+      }
+      // the XCD's list: bin by bin, longest first within a bin
+      int order[kPackItems];
+      int no = 0;
+      for (int j = 0; j < C; ++j) {
+        std::sort(bin[j].begin(), bin[j].end(), [&](int a, int b) { return item_w[a] > item_w[b]; });
+        out.bin[x][j] = int16_t(no);
+        for (int it : bin[j]) order[no++] = it;
+      }
+      out.bin[x][C] = int16_t(no);
+      out.n[x] = int16_t(no);
+      for (int r = 0; r < kPackSegs; ++r) {
+        out.grp[x][r] = int16_t(r < nrun[x] ? runs[x][r].grp : 0);
+        out.qt0[x][r] = int16_t(r < nrun[x] ? runs[x][r].qt0 : 0);
+      }
+      for (int w = 0; w < kPackItems / 8; ++w) out.code[x][w] = 0;
+      for (int k = 0; k < no; ++k)
+        out.code[x][k >> 3] |= uint32_t(item_run[order[k]]) << (4 * (k & 7));
+      for (int j = 0; j < C; ++j) busiest = std::max(busiest, bl[j]);
     }
-    // the XCD's list: bin by bin, longest first within a bin
-    int order[kPackItems];
-    int no = 0;
-    for (int j = 0; j < C; ++j) {
-      std::sort(bin[j].begin(), bin[j].end(), [&](int a, int b) { return item_w[a] > item_w[b]; });
-      p.pack_bin[x][j] = int16_t(no);
-      for (int it : bin[j]) order[no++] = it;
+    return busiest;
+  };
+  // The dealing overshoots each XCD's target by up to one item, and items
+  // come in a few lengths, so an XCD may end up a fraction of an item above
+  // what its CUs can share evenly: a few targets are tried and the plan with
+  // the least-loaded busiest CU is kept.
+  static const double kTargetScale[] = {1.0, 0.999, 0.998, 0.996, 0.994, 0.992, 0.99, 0.985, 0.98};
+  Packed best{}, cand{};
+  int64_t best_load = -1;
+  for (double f : kTargetScale) {
+    const int64_t l = plan_with(f * double(total) / kNumXcd, cand);
+    if (l >= 0 && (best_load < 0 || l < best_load)) {
+      best_load = l;
+      best = cand;
     }
-    p.pack_bin[x][C] = int16_t(no);
-    p.xcd_n[x] = int16_t(no);
-    for (int r = 0; r < kPackSegs; ++r) {
-      p.pack_grp[x][r] = int16_t(r < nrun[x] ? runs[x][r].grp : 0);
-      p.pack_qt0[x][r] = int16_t(r < nrun[x] ? runs[x][r].qt0 : 0);
-    }
-    for (int w = 0; w < kPackItems / 8; ++w) p.pack_code[x][w] = 0;
-    for (int k = 0; k < no; ++k)
-      p.pack_code[x][k >> 3] |= uint32_t(item_run[order[k]]) << (4 * (k & 7));
   }
+  if (best_load < 0) return false;
+  std::memcpy(p.pack_grp, best.grp, sizeof(best.grp));
+  std::memcpy(p.pack_qt0, best.qt0, sizeof(best.qt0));
+  std::memcpy(p.pack_bin, best.bin, sizeof(best.bin));
+  std::memcpy(p.pack_code, best.code, sizeof(best.code));
+  std::memcpy(p.xcd_n, best.n, sizeof(best.n));
   p.use_xcd = 2;
   blocks = int64_t(kNumXcd) * C;  // one block per CU
   return true;
+}
+
+// Tail items (see AttnParams): used when every active slot's last query tile
+// holds at most half a workgroup's rows, so that two or more slots share an
+// item, and every active slot's context is, as a set, a prefix of the heaviest
+// slot's walk (history and live store as listed, then the live chunks in
+// descending order) — true unless the slots' history budgets differ. Only the
+// bf16 kernel with whole-tile sources runs them.
+void plan_tail(const wf_tick_desc& d, const StagePlan& pl, AttnParams& p) {
+  p.tail = 0;
+  if (pl.n_active < 2) return;
+  const int r = d.T - (p.ntq - 1) * QROWS;
+  const int spr = (r + 31) / 32;
+  if (2 * spr > NWAVES) return;
+  const int s0 = pl.order[0];
+  const int n0 = pl.nseg[s0];
+  int npre = 0;  // history chunks and the live store lead every list
+  while (npre < n0 && (pl.seg[s0][npre] < 0 || pl.seg[s0][npre] == d.S)) ++npre;
+  int walk[WF_MAX_SEGMENTS];
+  for (int i = 0; i < n0; ++i) walk[i] = i < npre ? pl.seg[s0][i] : pl.seg[s0][npre + n0 - 1 - i];
+  auto bit = [](int code) { return uint64_t(1) << (code >= 0 ? 32 + code : -code - 1); };
+  for (int k = 0; k < pl.n_active; ++k) {
+    const int s = pl.order[k];
+    if (pl.nseg[s] > n0) return;
+    uint64_t want = 0, got = 0;
+    for (int i = 0; i < pl.nseg[s]; ++i) {
+      want |= bit(walk[i]);
+      got |= bit(pl.seg[s][i]);
+    }
+    if (want != got) return;
+    int lead = 0;  // its list must lead with the same history and store entries
+    while (lead < pl.nseg[s] && (pl.seg[s][lead] < 0 || pl.seg[s][lead] == d.S)) ++lead;
+    if (lead != std::min(npre, int(pl.nseg[s]))) return;
+  }
+  p.tail = 1;
+  p.tail_row0 = (p.ntq - 1) * QROWS;
+  p.tail_spr = spr;
+  p.tail_per_head = (pl.n_active * spr + NWAVES - 1) / NWAVES;
+  p.tail_npre = npre;
+}
+
+// The launch's work order: tail items and the packed per-CU lists when they
+// fit, else whole (stage, head) groups dealt to XCDs, else the plain order.
+void plan_launch_uncached(const wf_tick_desc& d, const StagePlan& pl, int C, AttnParams& p,
+                          int64_t& blocks) {
+  p.n_active = pl.n_active;
+  const bool paged = d.n_hist > 0 || d.live_pages != nullptr || d.store_pages != nullptr;
+  const bool fast = !paged || d.P % KT == 0;
+  if (fast && d.k_format == WF_K_BF16) plan_tail(d, pl, p);
+  blocks = int64_t(pl.n_active) * p.items_per_stage;
+  if (!plan_packed_order(pl, d.H, p.tps, C, p, blocks)) {
+    p.tail = 0;
+    blocks = int64_t(pl.n_active) * p.items_per_stage;
+    plan_xcd_order(pl, d.H, p, blocks);
+  }
+}
+
+// The work-order members of AttnParams, copied between a cached plan and a
+// launch's parameters.
+void copy_plan(const AttnParams& from, AttnParams& to) {
+  to.use_xcd = from.use_xcd;
+  to.xcd_stride = from.xcd_stride;
+  to.tail = from.tail;
+  to.tail_row0 = from.tail_row0;
+  to.tail_spr = from.tail_spr;
+  to.tail_per_head = from.tail_per_head;
+  to.tail_npre = from.tail_npre;
+  to.n_active = from.n_active;
+  std::memcpy(to.xcd_n, from.xcd_n, sizeof(to.xcd_n));
+  std::memcpy(to.xcd_groups, from.xcd_groups, sizeof(to.xcd_groups));
+  std::memcpy(to.pack_grp, from.pack_grp, sizeof(to.pack_grp));
+  std::memcpy(to.pack_qt0, from.pack_qt0, sizeof(to.pack_qt0));
+  std::memcpy(to.pack_bin, from.pack_bin, sizeof(to.pack_bin));
+  std::memcpy(to.pack_code, from.pack_code, sizeof(to.pack_code));
+}
+
+// Plans depend only on the tick's shape (slots, mask, sizes, history budgets,
+// formats, paging) and the CU count, and a streaming rollout repeats a few
+// shapes tick after tick, so the last kPlanCache plans are kept (the packing
+// search costs tens of milliseconds of host time).
+constexpr int kPlanCache = 8;
+struct PlanKey {
+  int32_t v[16 + WF_MAX_STAGES];
+  bool operator==(const PlanKey& o) const { return std::memcmp(v, o.v, sizeof(v)) == 0; }
+};
+struct PlanEntry {
+  PlanKey key;
+  AttnParams plan;
+  int64_t blocks;
+  uint64_t used;
+};
+
+PlanKey plan_key(const wf_tick_desc& d, int C) {
+  PlanKey k;
+  std::memset(&k, 0, sizeof(k));
+  const int32_t head[] = {d.S, int32_t(d.active_mask), d.T, d.H, d.D, d.n_hist, d.P,
+                          d.k_format, d.v_format, d.live_pages != nullptr, d.store_pages != nullptr,
+                          C};
+  std::memcpy(k.v, head, sizeof(head));
+  for (int s = 0; s <= d.S && s < WF_MAX_STAGES; ++s) k.v[16 + s] = d.hist_first[s];
+  return k;
+}
+
+void plan_launch(const wf_tick_desc& d, const StagePlan& pl, int C, AttnParams& p,
+                 int64_t& blocks) {
+  static std::mutex mu;
+  static PlanEntry cache[kPlanCache];
+  static int n_cached = 0;
+  static uint64_t clock = 0;
+  const PlanKey key = plan_key(d, C);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n_cached; ++i)
+      if (cache[i].key == key) {
+        cache[i].used = ++clock;
+        copy_plan(cache[i].plan, p);
+        blocks = cache[i].blocks;
+        return;
+      }
+  }
+  plan_launch_uncached(d, pl, C, p, blocks);
+  std::lock_guard<std::mutex> lock(mu);
+  int slot = n_cached < kPlanCache ? n_cached++ : 0;
+  if (slot == 0 && n_cached == kPlanCache)  // evict the least recently used
+    for (int i = 1; i < kPlanCache; ++i)
+      if (cache[i].used < cache[slot].used) slot = i;
+  cache[slot].key = key;
+  copy_plan(p, cache[slot].plan);
+  cache[slot].blocks = blocks;
+  cache[slot].used = ++clock;
 }
 
 // kFast: every tile is one uniform span of a page or live chunk (page size a
@@ -1453,18 +1699,43 @@ int32_t validate_tick(const wf_tick_desc* d) {
 }
 
 // The work items of attention block b (counted after the store blocks), as
-// the kernel decodes them from the plan, appended to `items` as (rank, head,
-// query tile).
-void decode_block(const AttnParams& p, int b, std::vector<int>& items) {
+// the kernel decodes them from the plan, appended to `rows` as (item index in
+// the block, rank, head, first query row, rows): one row per item, or for a
+// tail item one per rank among its slices.
+void decode_block(const AttnParams& p, int b, std::vector<std::array<int, 5>>& rows) {
+  auto tile = [&](int k, int rank, int h, int qt) {
+    const int q0 = qt * QROWS;
+    rows.push_back({k, rank, h, q0, std::min(QROWS, p.T - q0)});
+  };
   if (p.use_xcd == 2) {
     const int x = b & (kNumXcd - 1);
     const int c = b / kNumXcd;
+    const int G = p.n_active * p.H;
     for (int k = p.pack_bin[x][c]; k < p.pack_bin[x][c + 1]; ++k) {
       const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
       int before = 0;
       for (int i = 0; i < k; ++i) before += ((p.pack_code[x][i >> 3] >> (4 * (i & 7))) & 15) == run;
       const int grp = p.pack_grp[x][run];
-      items.insert(items.end(), {grp / p.H, grp % p.H, p.pack_qt0[x][run] + before});
+      const int item = k - p.pack_bin[x][c];
+      if (grp < G) {
+        tile(item, grp / p.H, grp % p.H, p.pack_qt0[x][run] + before);
+        continue;
+      }
+      const int h = (grp - G) / p.tail_per_head;
+      const int m = (grp - G) % p.tail_per_head;
+      for (int w = 0; w < NWAVES; ++w) {  // slices, grouped by rank
+        const int gw = m * NWAVES + w;
+        if (gw >= p.n_active * p.tail_spr) break;
+        const int rank = gw / p.tail_spr;
+        const int q0 = p.tail_row0 + (gw - rank * p.tail_spr) * 32;
+        if (q0 >= p.T) continue;
+        const int n = std::min(32, p.T - q0);
+        if (!rows.empty() && rows.back()[0] == item && rows.back()[1] == rank &&
+            rows.back()[2] == h && rows.back()[3] + rows.back()[4] == q0)
+          rows.back()[4] += n;
+        else
+          rows.push_back({item, rank, h, q0, n});
+      }
     }
   } else if (p.use_xcd) {
     const int x = b & (kNumXcd - 1);
@@ -1472,11 +1743,11 @@ void decode_block(const AttnParams& p, int b, std::vector<int>& items) {
     const int gi = k / p.ntq;
     if (gi >= p.xcd_n[x]) return;
     const int grp = p.xcd_groups[x * p.xcd_stride + gi];
-    items.insert(items.end(), {grp / p.H, grp % p.H, k - gi * p.ntq});
+    tile(0, grp / p.H, grp % p.H, k - gi * p.ntq);
   } else {
     const int rank = b / p.items_per_stage;
     const int rem = b - rank * p.items_per_stage;
-    items.insert(items.end(), {rank, rem / p.ntq, rem % p.ntq});
+    tile(0, rank, rem / p.ntq, rem % p.ntq);
   }
 }
 
@@ -1497,26 +1768,26 @@ extern "C" wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_pe
     plan_stages(d, pl);
     AttnParams p;
     std::memset(&p, 0, sizeof(p));
+    p.T = d.T;
     p.H = d.H;
     p.tps = (d.T + KT - 1) / KT;
     p.ntq = (d.T + QROWS - 1) / QROWS;
     p.items_per_stage = d.H * p.ntq;
-    int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
-    const int C = cus_per_xcd_hint > 0 ? cus_per_xcd_hint : cus_per_xcd();
-    if (!plan_packed_order(pl, d.H, p.tps, C, p, blocks)) plan_xcd_order(pl, d.H, p, blocks);
-    std::vector<int> rows;
+    int64_t blocks = 0;
+    plan_launch(d, pl, cus_per_xcd_hint > 0 ? cus_per_xcd_hint : cus_per_xcd(), p, blocks);
+    std::vector<int> out_rows;
     for (int64_t b = 0; b < blocks; ++b) {
-      std::vector<int> items;
+      std::vector<std::array<int, 5>> items;
       decode_block(p, int(b), items);
-      for (size_t i = 0; i < items.size(); i += 3)
-        rows.insert(rows.end(), {int(b), pl.order[items[i]], items[i + 1], items[i + 2]});
+      for (const auto& it : items)
+        out_rows.insert(out_rows.end(), {int(b), it[0], pl.order[it[1]], it[2], it[3], it[4]});
     }
-    *n_items = int64_t(rows.size() / 4);
+    *n_items = int64_t(out_rows.size() / 6);
     if (!out) return WF_OK;
-    if (capacity < int64_t(rows.size()))
-      return fail(WF_EINVAL, "wf_tick_work_order: capacity %lld < 4 * %lld items",
-                  static_cast<long long>(capacity), static_cast<long long>(rows.size() / 4));
-    std::copy(rows.begin(), rows.end(), out);
+    if (capacity < int64_t(out_rows.size()))
+      return fail(WF_EINVAL, "wf_tick_work_order: capacity %lld < 6 * %lld rows",
+                  static_cast<long long>(capacity), static_cast<long long>(out_rows.size() / 6));
+    std::copy(out_rows.begin(), out_rows.end(), out);
     return WF_OK;
   } catch (...) {
     return fail(WF_EINVAL, "wf_tick_work_order: internal error");
@@ -1609,9 +1880,8 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
       p.nseg[s] = pl.nseg[s];
       for (int i = 0; i < pl.nseg[s]; ++i) p.seg[s][i] = pl.seg[s][i];
     }
-    int64_t blocks = int64_t(pl.n_active) * p.items_per_stage;
-    if (!plan_packed_order(pl, d.H, p.tps, cus_per_xcd(), p, blocks))
-      plan_xcd_order(pl, d.H, p, blocks);
+    int64_t blocks = 0;
+    plan_launch(d, pl, cus_per_xcd(), p, blocks);
     blocks += p.n_store_blocks;  // a multiple of 8: the XCD of every attention block is kept
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
     const bool fast = !paged || d.P % KT == 0;

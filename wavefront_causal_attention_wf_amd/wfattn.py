@@ -495,12 +495,13 @@ def tick_useful_flops_desc(desc: WfTickDesc) -> float:
 
 
 def tick_work_order(desc: WfTickDesc, cus_per_xcd: int = 0) -> np.ndarray:
-    """Host-only plan of wf_attn_tick: int32 [n_items][4] = (block, slot, head,
-    query tile) in launch order, a block's items in the order it runs them."""
+    """Host-only plan of wf_attn_tick: int32 [n_rows][6] = (block, item, slot,
+    head, first query row, rows) in launch order, a block's items in the order
+    it runs them (a tail item has one row per slot it serves)."""
     n = ctypes.c_int64()
     _check(_lib.wf_tick_work_order(ctypes.byref(desc), cus_per_xcd, None, 0, ctypes.byref(n)),
            "wf_tick_work_order")
-    out = np.empty(4 * n.value, np.int32)
+    out = np.empty(6 * n.value, np.int32)
     _check(_lib.wf_tick_work_order(ctypes.byref(desc), cus_per_xcd, out.ctypes.data_as(_i32p),
                                    out.size, ctypes.byref(n)), "wf_tick_work_order")
-    return out.reshape(n.value, 4)
+    return out.reshape(n.value, 6)
