@@ -119,6 +119,19 @@ def parse():
     return ap.parse_args()
 
 
+def tick_workspace(cfg, dev, live_paged: bool = False):
+    """The attention launch's workspace (run-time pool) for the configuration's
+    full-width tick, or None where the tick takes none."""
+    import torch
+
+    from wavefront_causal_attention_wf_amd import wfattn
+
+    nb = wfattn.workspace_bytes(cfg.S, (1 << (cfg.S + 1)) - 1, cfg.T, cfg.H, cfg.D,
+                                max(cfg.n_hist, 1), None, cfg.P, cfg.num_pages,
+                                live_paged=live_paged)
+    return torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+
+
 class Rollout:
     """Device state of a steady-state rollout: pools, page table, live inputs."""
 
@@ -157,6 +170,7 @@ class Rollout:
         self.o = torch.empty_like(self.live[0][0])
         self.scale = 1.0 / float(np.sqrt(D))
         self.mask = (1 << (S + 1)) - 1
+        self.ws = tick_workspace(cfg, dev)
         torch.cuda.synchronize()
 
     def step(self, attn_events=None):
@@ -182,7 +196,8 @@ class Rollout:
             attn_events[0].record()
         wf.wf_attn_tick(q, k, v, self.o, S, self.mask, self.scale, self.k_pool, self.v_pool,
                         self.hist_dev[slot],
-                        store_pages=self.ids_dev[slot] if self.fused else None)
+                        store_pages=self.ids_dev[slot] if self.fused else None,
+                        workspace=self.ws)
         if attn_events is not None:
             attn_events[1].record()
         self.pt.commit()
@@ -374,6 +389,7 @@ class FullyPagedRollout:
         self.scale = 1.0 / float(np.sqrt(D))
         self.mask = (1 << (S + 1)) - 1
         self.i = 0
+        self.ws = tick_workspace(cfg, dev, live_paged=True)
         torch.cuda.synchronize()
 
     def step(self, attn_events=None):
@@ -398,7 +414,8 @@ class FullyPagedRollout:
         if attn_events is not None:
             attn_events[0].record()
         wf.wf_attn_tick(q, None, None, self.o, S, self.mask, self.scale, self.k_pool,
-                        self.v_pool, self.hist_dev, live_pages=self.live_dev)
+                        self.v_pool, self.hist_dev, live_pages=self.live_dev,
+                        workspace=self.ws)
         if attn_events is not None:
             attn_events[1].record()
         self.pt.commit()
@@ -625,6 +642,7 @@ def rollout120(dev, warmup: int = 1) -> dict:
     k_pool = torch.zeros((cfg.num_pages, P, H, D), dtype=torch.bfloat16, device=dev)
     v_pool = torch.zeros_like(k_pool)
     o = torch.empty_like(live[0][0])
+    ws = tick_workspace(cfg, dev)
     ppc = cfg.ppc
     nslot = 8
     ids_host = torch.empty((nslot, ppc), dtype=torch.int32, pin_memory=True)
@@ -669,7 +687,7 @@ def rollout120(dev, warmup: int = 1) -> dict:
             ev.record()
             slot_ev[slot] = ev
             wfattn.wf_attn_tick(q, k, v, o, S, mask, scale, k_pool, v_pool, hd,
-                                store_pages=store)
+                                store_pages=store, workspace=ws)
             if t >= S:
                 pt.commit()
         if events is not None:
@@ -702,7 +720,7 @@ def rollout120(dev, warmup: int = 1) -> dict:
            "useful_tflop_per_s": round(float(flops.sum()) / (total_ms * 1e-3) / 1e12, 2),
            "ticks_3_to_119": part(3),
            "full_width_ticks_7_to_119": part(S + cfg.window)}
-    del live, k_pool, v_pool, o
+    del live, k_pool, v_pool, o, ws
     torch.cuda.empty_cache()
     return out
 
@@ -753,7 +771,7 @@ def profile_mode(args, cfg, dev) -> None:
     mask = (1 << (cfg.S + 1)) - 1
     for _ in range(args.steps):
         wfattn.wf_attn_tick(q, k, v, ro.o, cfg.S, mask, ro.scale, ro.k_pool, ro.v_pool, hist,
-                            store_pages=store_ids)
+                            store_pages=store_ids, workspace=ro.ws)
     torch.cuda.synchronize()
     log(f"attn: {args.steps} launches (with the fused store)")
 

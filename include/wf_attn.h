@@ -57,7 +57,7 @@ const char* wf_last_error(void);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t wf_abi_version(void);
-#define WF_ABI_VERSION 6
+#define WF_ABI_VERSION 7
 
 /* ------------------------------------------------------------------------ */
 /* Page table: host-only state for one request's attention pages.            */
@@ -239,7 +239,8 @@ wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t*
 /* power-of-two scale applied by the MFMA; the softmax's sum uses the          */
 /* unrounded P.                                                               */
 /* Errors: WF_EINVAL for bad sizes, masks, pointers (NULL or not 16-byte      */
-/* aligned), P not a positive multiple of 16, n_hist*ceil(T/P) > num_pages;   */
+/* aligned; workspace not 256-byte aligned or workspace_bytes < 0), P not a   */
+/* positive multiple of 16, n_hist*ceil(T/P) > num_pages;                     */
 /* v_format not WF_V_BF16/WF_V_E4M3, WF_V_E4M3 without WF_K_E4M3 or v_exp;  */
 /* k_format not WF_K_BF16/WF_K_E4M3, or WF_K_E4M3 without live_pages or      */
 /* k_scale, with store_pages, or with P not a multiple of 64;                 */
@@ -286,6 +287,19 @@ typedef struct wf_tick_desc {
                           /* v_pool uint8 transposed tiles [num_pages][P/64][H][D]  */
                           /* [64] with v_exp                                        */
   const uint8_t* v_exp;   /* device uint8 [num_pages][P/64][H] with WF_V_E4M3       */
+  void* workspace;        /* device scratch (256-byte aligned), or NULL. Set, with   */
+                          /* the bf16 kernel and whole-tile sources, part of the    */
+                          /* work (query tiles of the heaviest slot, cut into one  */
+                          /* chunk of keys each) is handed out while the launch    */
+                          /* runs to whichever CU is free, and the pieces' partial  */
+                          /* softmax states are merged there; the results are those */
+                          /* of the same arithmetic in another summation order. The */
+                          /* library zeroes the counters it uses before each launch; */
+                          /* launches sharing a workspace must not overlap.          */
+                          /* wf_tick_workspace_bytes gives the size that lets the   */
+                          /* pool reach its full share; a smaller one holds fewer   */
+                          /* pieces. Not read or written by the caller.             */
+  int64_t workspace_bytes; /* bytes at workspace (>= 0)                              */
 } wf_tick_desc;
 
 #define WF_K_BF16 0
@@ -295,12 +309,20 @@ typedef struct wf_tick_desc {
 
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);
 
+/* Workspace size for wf_attn_tick with this descriptor: the bytes that hold the
+ * run-time pool's full share (about 8 % of the tick's work, at most 128 query
+ * tiles, one partial state of 256 rows x (D + 2) fp32 per chunk of keys, plus
+ * 1 KB of counters); 0 when the tick does not use one. Host only; errors as
+ * wf_attn_tick's validation, WF_EINVAL for a NULL bytes. */
+wf_status wf_tick_workspace_bytes(const wf_tick_desc* desc, int64_t* bytes);
+
 /* Diagnostic, host only: the work order wf_attn_tick would launch for this
  * descriptor. Row i = out[6i .. 6i+5] = (block, item, slot, head, first query
  * row, rows): attention block `block` (counted after the blocks that write the
  * store's pages; it runs on XCD block % 8) computes query rows [first, first +
  * rows) of that slot and head in its item number `item`, items in the order
- * the block runs them. An ordinary item is one query tile (256 rows) of one
+ * the block runs them; block -1 lists the run-time pool's items (with a
+ * workspace), which whichever blocks are free compute chunk by chunk. An ordinary item is one query tile (256 rows) of one
  * slot; a tail item holds the last query tile's rows of several slots of one
  * head, one row per slot. cus_per_xcd: compute units per XCD to plan for
  * (<= 0: the current device's). *n_items receives the row count; out (host

@@ -94,14 +94,23 @@ def setup_tick(S, T, H, D, P, n_hist, num_pages, *, seed=0, page_seed=1, qscale=
                 np.asarray(hist), store)
 
 
+def workspace_for(t: Tick) -> Optional[torch.Tensor]:
+    """A workspace of the size wf_tick_workspace_bytes asks for this tick
+    (None where the tick takes none)."""
+    nb = wfattn.workspace_bytes(t.S, t.active_mask, t.T, t.H, t.D, t.n_hist, t.hist_first, t.P,
+                                t.num_pages)
+    return None if nb == 0 else torch.empty(nb, dtype=torch.uint8, device=DEV)
+
+
 def run_tick(t: Tick, q=None, k=None, v=None, o=None, hist_pages=None, k_pool=None,
-             v_pool=None) -> torch.Tensor:
+             v_pool=None, workspace=None) -> torch.Tensor:
     o = t.o if o is None else o
     wfattn.wf_attn_tick(t.q if q is None else q, t.k if k is None else k,
                         t.v if v is None else v, o, t.S, t.active_mask, t.scale,
                         t.k_pool if k_pool is None else k_pool,
                         t.v_pool if v_pool is None else v_pool,
-                        t.hist_pages if hist_pages is None else hist_pages, t.hist_first)
+                        t.hist_pages if hist_pages is None else hist_pages, t.hist_first,
+                        workspace=workspace)
     torch.cuda.synchronize()
     return o
 

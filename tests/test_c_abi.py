@@ -597,3 +597,29 @@ def test_binding_rejects_bad_tick_arguments():
     for exc, kw in cases:
         with pytest.raises(exc):
             tick(**kw)
+
+
+def test_tick_validation_workspace():
+    """A workspace must be 256-byte aligned with workspace_bytes >= 0 (bytes
+    without a pointer are ignored); wf_tick_workspace_bytes validates like the
+    launch and refuses a NULL result pointer."""
+    import ctypes
+    wf = _wfattn()
+    fake = 1 << 20
+
+    def desc(ws, nb):
+        d = _desc(wf, q=fake, k=fake, v=fake, o=fake)
+        d.workspace = ws
+        d.workspace_bytes = nb
+        return d
+
+    for d in (desc(fake + 128, 1 << 20), desc(fake, -1)):
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_attn_tick_desc(d, stream=0)
+        assert e.value.status == CODES["EINVAL"], wf.last_error()
+    assert wf.library().wf_tick_workspace_bytes(ctypes.byref(desc(None, 0)), None) == CODES["EINVAL"]
+    bad = desc(None, 0)
+    bad.H = 0
+    with pytest.raises(wf.WfError):
+        wf.tick_workspace_bytes(bad)
+    assert wf.tick_workspace_bytes(desc(None, 0)) >= 0

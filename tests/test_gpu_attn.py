@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from _gpu_common import DEV, compare, oracle_tick, run_tick, say, setup_tick
-from wavefront_causal_attention_wf_amd import inputs
+from _gpu_common import DEV, compare, oracle_tick, run_tick, say, setup_tick, workspace_for
+from wavefront_causal_attention_wf_amd import inputs, wfattn
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +78,47 @@ def test_tail_items_parity(S, T, H, P, n_hist, mask):
     o = run_tick(t)
     worst = compare(o, oracle_tick(t), label="tail items")
     say(f"  worst rel-L2 {worst:.2e}")
+
+
+@pytest.mark.parametrize("S,T,H,P,n_hist,mask", [
+    (4, 1100, 4, 64, 3, 0b11111),   # 8-chunk walks, 76-row last tiles (tail items too)
+    (4, 1024, 3, 128, 2, 0b01111),  # whole tiles only, no store: 6-chunk walks
+    (2, 600, 2, 64, 1, 0b111),      # 4-chunk walks
+])
+def test_run_time_pool_parity(S, T, H, P, n_hist, mask):
+    """With a workspace, query tiles of the heaviest slot are computed chunk by
+    chunk by whichever CUs are free, each chunk's partial softmax state
+    (unnormalised O, row max, row sum) left in the workspace, and merged by
+    the CU that finishes an item's last chunk: a row's context is a union of
+    chunks ([full text] Eq. (5)), and the softmax over a union of key sets
+    follows exactly from the per-set maxima and sums.
+    Every (stage, head) against the oracle, every row written, and a second
+    launch on the same workspace (its counters cleared by the library) bit for
+    bit equal to the first: the merge sums the chunks in walk order whichever
+    CU does it."""
+    say(f"run-time pool: S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b}")
+    t = setup_tick(S, T, H, 128, P, n_hist, (n_hist + 2) * -(-T // P) + 8, seed=T + 7,
+                   active_mask=mask)
+    ws = workspace_for(t)
+    assert ws is not None
+    d = wfattn.make_tick_desc(t.S, t.active_mask, t.T, t.H, t.D, t.scale, t.q, t.k, t.v, t.o,
+                              t.k_pool, t.v_pool, t.num_pages, t.P, t.hist_pages, t.n_hist,
+                              t.hist_first, workspace=ws)
+    order = wfattn.tick_work_order(d, 0)
+    n_pool = int(np.sum(order[:, 0] == -1))
+    say(f"  pool items: {n_pool}")
+    assert n_pool > 0
+    o = run_tick(t, workspace=ws)
+    worst = compare(o, oracle_tick(t), label="pool")
+    say(f"  worst rel-L2 {worst:.2e}")
+    o2 = run_tick(t, o=torch.full_like(t.o, float("nan")), workspace=ws)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    # without the workspace: the same results up to the summation order
+    o3 = run_tick(t, o=torch.full_like(t.o, float("nan")))
+    act = [s for s in range(S + 1) if (mask >> s) & 1]
+    diff = max((o3[s].float() - o[s].float()).abs().max().item() for s in act)
+    say(f"  max |pool - lists| = {diff:.2e}")
+    assert diff <= 2 ** -6
 
 
 @pytest.mark.parametrize("mask,hist_first", [

@@ -89,12 +89,24 @@ class MirroredPages:
         return torch.from_numpy(np.ascontiguousarray(h)).to(DEV)
 
 
-def run_tick(cfg, pages: MirroredPages, q, k, v, mask: int, store_ids=None) -> torch.Tensor:
-    """One tick; with store_ids the same launch writes the store chunk's pages."""
+def workspace(cfg) -> torch.Tensor:
+    """The workspace the bench passes: wf_tick_workspace_bytes of the
+    configuration's full-width tick (ticks of other shapes use what fits)."""
+    nb = wfattn.workspace_bytes(cfg.S, (1 << (cfg.S + 1)) - 1, cfg.T, cfg.H, cfg.D,
+                                max(cfg.n_hist, 1), None, cfg.P, cfg.num_pages)
+    assert nb > 0, cfg.name
+    return torch.empty(nb, dtype=torch.uint8, device=DEV)
+
+
+def run_tick(cfg, pages: MirroredPages, q, k, v, mask: int, store_ids=None,
+             ws=None) -> torch.Tensor:
+    """One tick; with store_ids the same launch writes the store chunk's pages;
+    with ws part of the work goes through the run-time pool."""
     o = torch.full_like(q, float("nan"))
     wfattn.wf_attn_tick(q, k, v, o, cfg.S, mask, 1.0 / np.sqrt(cfg.D), pages.k_pool,
                         pages.v_pool, pages.hist_device(),
-                        store_pages=None if store_ids is None else torch.from_numpy(store_ids).to(DEV))
+                        store_pages=None if store_ids is None else torch.from_numpy(store_ids).to(DEV),
+                        workspace=ws)
     torch.cuda.synchronize()
     return o
 
@@ -105,13 +117,17 @@ def oracle_rows(cfg, pages: MirroredPages, q, k, v, mask: int, rows, heads=None)
                                        rows=rows, heads=heads)
 
 
-@pytest.mark.parametrize("name", ["wan13_4step", "wan13_5step", "wan14b_4step"])
-def test_full_size_tick_sampled_rows(name):
+@pytest.mark.parametrize("name,pool", [("wan13_4step", True), ("wan13_4step", False),
+                                       ("wan13_5step", True), ("wan13_5step", False),
+                                       ("wan14b_4step", False)])
+def test_full_size_tick_sampled_rows(name, pool):
     """One steady tick exactly as the bench sets it up: n_hist history chunks
     (generator seeds 2000 + c) stored through the page table, live inputs from
-    the rollout seed of tick 0, all S+1 slots active."""
+    the rollout seed of tick 0, all S+1 slots active; with the bench's
+    workspace (run-time pool) and without. (The 14B-like tick's 200 groups
+    are dealt whole to the XCDs, without lists: it takes no workspace.)"""
     cfg = inputs.CONFIGS[name]
-    say(f"[full-size] {name}: S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist}")
+    say(f"[full-size] {name}: S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist} pool={pool}")
     pages = MirroredPages(cfg, cfg.n_hist)
     for c in range(cfg.n_hist):
         hk, hv, _ = inputs.draw_live_torch(cfg, 2000 + c, DEV)
@@ -121,7 +137,7 @@ def test_full_size_tick_sampled_rows(name):
         del hk, hv
     q, k, v = inputs.draw_live_torch(cfg, inputs.rollout_seed(0), DEV)
     mask = (1 << (cfg.S + 1)) - 1
-    o = run_tick(cfg, pages, q, k, v, mask)
+    o = run_tick(cfg, pages, q, k, v, mask, ws=workspace(cfg) if pool else None)
     assert torch.isfinite(o.float()).all()
     rows = sample_rows(cfg.T, seed=len(name))
     want = oracle_rows(cfg, pages, q, k, v, mask, rows)
@@ -142,15 +158,15 @@ def _bench_tick(cfg):
 
 
 def test_full_size_4step_every_row_every_head():
-    """The bench's 4-step tick with its store write fused into the launch (the
-    timed configuration): every row of every stage and head against the
-    oracle, and the store chunk's pages bit for bit."""
+    """The bench's 4-step tick with its store write fused into the launch and
+    the bench's workspace (the timed configuration): every row of every stage
+    and head against the oracle, and the store chunk's pages bit for bit."""
     cfg = inputs.CONFIGS["wan13_4step"]
     say(f"[full-size, all rows] S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist}")
     pages, q, k, v = _bench_tick(cfg)
     mask = (1 << (cfg.S + 1)) - 1
     ids = pages.store_chunk(k[cfg.S], v[cfg.S], write=False)
-    o = run_tick(cfg, pages, q, k, v, mask, store_ids=ids)
+    o = run_tick(cfg, pages, q, k, v, mask, store_ids=ids, ws=workspace(cfg))
     pages.check_pages(ids)
     pages.store.drop(ids)          # the store chunk's pages are not history yet
     want = oracle_rows(cfg, pages, q, k, v, mask, None)
@@ -167,7 +183,7 @@ def test_full_size_4step_peaked_sampled_rows():
     pages, q, k, v = _bench_tick(cfg)
     q = q * 16.0                   # exact in bf16 (a power of two)
     mask = (1 << (cfg.S + 1)) - 1
-    o = run_tick(cfg, pages, q, k, v, mask)
+    o = run_tick(cfg, pages, q, k, v, mask, ws=workspace(cfg))
     rows = sample_rows(cfg.T, seed=16)
     want = oracle_rows(cfg, pages, q, k, v, mask, rows)
     worst = compare(o, want, rows=rows, label="wan13_4step q*16")
@@ -189,13 +205,14 @@ def rollout120():
     ticks (fill, first eviction, recycled pages, last) every head matches on
     sampled rows. Odd ticks write the store chunk with wf_store_paged before the
     attention launch, even ticks let the attention launch write it
-    (store_pages). Returns host copies of the key ticks' inputs, outputs and
+    (store_pages); every tick passes the bench's workspace (run-time pool). Returns host copies of the key ticks' inputs, outputs and
     history pages, which the tests below compare in full."""
     cfg = inputs.CONFIGS["rollout120"]
     S = cfg.S
     pages = MirroredPages(cfg, cfg.window)
     check_at = {0, 1, S - 1, S, S + 1, S + 3, S + 4, 40, 61, 90, cfg.ticks - 1}
     kept = {}
+    ws = workspace(cfg)
     for t in range(cfg.ticks):
         mask = oracle.active_mask_for_tick(t, S)
         q, k, v = inputs.draw_live_torch(cfg, inputs.rollout_seed(t), DEV)
@@ -206,7 +223,7 @@ def rollout120():
             if not fused:
                 pages.check_pages(ids)
         pages.check_tables()
-        o = run_tick(cfg, pages, q, k, v, mask, store_ids=ids if fused else None)
+        o = run_tick(cfg, pages, q, k, v, mask, store_ids=ids if fused else None, ws=ws)
         if fused:
             pages.check_pages(ids)
         for s in range(S + 1):

@@ -72,7 +72,8 @@ def test_paged_live_equals_contiguous_and_oracle(S, T, H, D, P, n_hist, mask):
 def test_fully_paged_rollout_with_anchor():
     """12 ticks from an empty history, S = 4, T = 4680 (3 x 30 x 52 latent grid),
     12 heads x 128, window 3 with the anchor pinned; pre-rotation K and V drawn
-    per tick, Q taken as already rotated. Chunk c covers latent frames 3c..3c+2."""
+    per tick, Q taken as already rotated. Chunk c covers latent frames 3c..3c+2.
+    Every launch passes a workspace (run-time pool), as the bench does."""
     cfg = inputs.CONFIGS["wan13_4step"]
     S, T, H, D, P = cfg.S, cfg.T, cfg.H, cfg.D, cfg.P
     grid = inputs.chunk_grid(T)
@@ -93,6 +94,11 @@ def test_fully_paged_rollout_with_anchor():
     anchor = None             # (ids, K before rotation: device + host bits, V bits)
     scale = 1.0 / np.sqrt(D)
     live_dev = torch.empty((S + 1, ppc), dtype=torch.int32, device=DEV)
+    # the bench's workspace: part of each tick through the run-time pool
+    nb = wfattn.workspace_bytes(S, (1 << (S + 1)) - 1, T, H, D, window, None, P, n_pool,
+                                live_paged=True)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
     for k in range(ticks):
         mask = oracle.active_mask_for_tick(k, S)
         q, kk, vv = inputs.draw_live_torch(cfg, inputs.rollout_seed(k), DEV)
@@ -122,7 +128,7 @@ def test_fully_paged_rollout_with_anchor():
         o = torch.full_like(q, float("nan"))
         wfattn.wf_attn_tick(q, None, None, o, S, mask, scale, k_pool, v_pool,
                             torch.from_numpy(np.ascontiguousarray(hist)).to(DEV),
-                            live_pages=live_dev)
+                            live_pages=live_dev, workspace=ws)
         torch.cuda.synchronize()
         rows = np.array(sorted({0, 63, 64, 2339, T - 9, T - 8, T - 1}
                                | set(np.random.default_rng(k).choice(T, 6, replace=False))))

@@ -42,12 +42,22 @@ CASES = [
 ]
 
 
+def with_workspace(d, nbytes=None):
+    """The descriptor with a (never dereferenced) workspace of nbytes, by
+    default the size wf_tick_workspace_bytes asks for."""
+    d.workspace = FAKE
+    d.workspace_bytes = wf.tick_workspace_bytes(d) if nbytes is None else nbytes
+    return d
+
+
 @pytest.mark.parametrize("name,S,mask,T,H,n_hist,hf", CASES)
-@pytest.mark.parametrize("cus", [32, 0])
-def test_every_row_once(name, S, mask, T, H, n_hist, hf, cus):
+@pytest.mark.parametrize("cus,ws", [(32, False), (0, False), (32, True)])
+def test_every_row_once(name, S, mask, T, H, n_hist, hf, cus, ws):
     """Every query row of every active (slot, head) is computed by exactly one
-    item, in rows of whole query tiles or (tail items) 32-row slices."""
-    order = wf.tick_work_order(desc(S, mask, T, H, n_hist, hf), cus)
+    item, in rows of whole query tiles or (tail items) 32-row slices; with a
+    workspace, some of them by the run-time pool (block -1, listed last)."""
+    d = desc(S, mask, T, H, n_hist, hf)
+    order = wf.tick_work_order(with_workspace(d) if ws else d, cus)
     assert order.shape[1] == 6
     cover = {(s, h): np.zeros(T, np.int32) for s in range(S + 1) if (mask >> s) & 1
              for h in range(H)}
@@ -57,7 +67,9 @@ def test_every_row_once(name, S, mask, T, H, n_hist, hf, cus):
         cover[(int(s), int(h))][q0:q0 + n] += 1
     for key, c in cover.items():
         assert np.all(c == 1), (key, int(c.min()), int(c.max()))
-    assert np.all(np.diff(order[:, 0]) >= 0)  # rows grouped by block, launch order
+    listed = order[order[:, 0] >= 0]
+    assert np.all(np.diff(listed[:, 0]) >= 0)  # rows grouped by block, launch order
+    assert np.all(order[len(listed):, 0] == -1)
 
 
 def items_of(order):
@@ -171,3 +183,62 @@ def test_plain_order_when_tables_overflow():
     stages.sort(key=lambda s: -keys_of(S, mask, 1, None, s))        # heaviest first (stable)
     want = [(s, h, 256 * q) for s in stages for h in range(H) for q in range(ntq)]
     assert [(int(r[2]), int(r[3]), int(r[4])) for r in order] == want
+
+
+STATE_BYTES = 256 * (128 + 2) * 4   # one piece's partial state, D = 128
+
+
+@pytest.mark.parametrize("name,S,mask,T,H,n_hist,hf", CASES[:2] + CASES[3:6])
+def test_run_time_pool(name, S, mask, T, H, n_hist, hf):
+    """The pool holds whole query tiles of the heaviest slot (the one with the
+    most keys), at most 128, about 8 % of the tick's key tiles, spread over
+    heads; the workspace holds 1 KB of counters and one partial state per
+    chunk of that slot's walk for each item."""
+    d = with_workspace(desc(S, mask, T, H, n_hist, hf))
+    order = wf.tick_work_order(d, 32)
+    pool = order[order[:, 0] == -1]
+    keys = {s: keys_of(S, mask, n_hist, hf, s) for s in range(S + 1) if (mask >> s) & 1}
+    heavy = max(keys, key=lambda s: keys[s])
+    assert 0 < len(pool) <= 128
+    assert np.array_equal(pool[:, 1], np.arange(len(pool)))
+    assert np.all(pool[:, 2] == heavy)
+    assert np.all(pool[:, 4] % 256 == 0)
+    assert d.workspace_bytes == 1024 + len(pool) * keys[heavy] * STATE_BYTES
+    # share of the work: pool tiles x walk length over all tiles' walks
+    tps = -(-T // 64)
+    all_w = sum(-(-T // 32) * 32 / 256 * keys[s] for s in keys) * H   # in query-tile walks
+    share = len(pool) * keys[heavy] / all_w
+    assert len(pool) == 128 or 0.06 <= share <= 0.10, share
+    heads = np.bincount(pool[:, 3], minlength=H)
+    assert heads.max() - heads.min() <= 1          # one tile per head in turn
+
+
+def test_pool_follows_workspace_size():
+    """A smaller workspace holds fewer pool items; one below a single item's
+    states, or none at all, gives no pool (and the same lists as without)."""
+    S, mask, T, H, n_hist = 4, 0b11111, 4680, 12, 3
+    full = wf.tick_workspace_bytes(desc(S, mask, T, H, n_hist))
+    per_item = 8 * STATE_BYTES
+    n_full = (full - 1024) // per_item
+    assert full == 1024 + n_full * per_item and n_full > 5
+    for n in (5, 1):
+        order = wf.tick_work_order(with_workspace(desc(S, mask, T, H, n_hist), 1024 + n * per_item + 100), 32)
+        assert int(np.sum(order[:, 0] == -1)) == n
+    plain = wf.tick_work_order(desc(S, mask, T, H, n_hist), 32)
+    for nbytes in (0, 1024 + per_item - 1):
+        order = wf.tick_work_order(with_workspace(desc(S, mask, T, H, n_hist), nbytes), 32)
+        assert np.array_equal(order, plain)
+
+
+@pytest.mark.parametrize("kw", [dict(P=48), dict(k8=True)])
+def test_no_pool_where_it_does_not_apply(kw):
+    """8-bit keys and pages that are not whole 64-key tiles take no workspace."""
+    S, mask, T, H, n_hist = 4, 0b11111, 4680, 12, 3
+    d = desc(S, mask, T, H, n_hist)
+    if "P" in kw:
+        d.P = kw["P"]
+    if kw.get("k8"):
+        d.k_format = wf.K_E4M3
+        d.k_scale = FAKE
+        d.live_pages = FAKE
+    assert wf.tick_workspace_bytes(d) == 0

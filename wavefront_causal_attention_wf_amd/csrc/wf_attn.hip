@@ -86,6 +86,15 @@ constexpr int kXcdTable = 256;      // max (stage, head) groups in the XCD group
 constexpr int kPackSegs = 16;
 constexpr int kPackItems = 192;
 constexpr int kPackBins = 40;  // CUs per XCD the packed order can fill
+// Run-time pool (see AttnParams): at most kMaxPool items; the workspace holds
+// kWsHeader bytes of counters, then one partial softmax state per piece.
+constexpr int kMaxPool = 128;
+constexpr int kWsHeader = 1024;
+static_assert((1 + kMaxPool) * 4 <= kWsHeader, "pool counters exceed the workspace header");
+constexpr double kPoolShare = 0.08;  // share of a tick's work the pool takes
+// A piece's partial state: [QROWS][D] unnormalised output, then the QROWS row
+// maxima and the QROWS row sums (fp32).
+constexpr int64_t state_bytes(int D) { return int64_t(QROWS) * (D + 2) * 4; }
 // History page table held in LDS (ids of all history pages of one tick) when
 // pages are not a multiple of 64 tokens; otherwise a table of tile sources.
 constexpr int kMaxPageIds = 4096;
@@ -93,6 +102,10 @@ constexpr int kMaxTiles = 1536;  // 64-key tiles per (stage, head): 24 KB of sou
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no
 // swizzle, stride 0): plain byte-addressed loads.
 constexpr int kBufferFlags = 0x00020000;
+// Cache-policy operand of a buffer access with device scope (the SC1 bit): the
+// access is coherent across the XCDs' separate L2 caches without writing back
+// or invalidating them, as the device-scope atomic loads and stores are.
+constexpr int kDeviceScope = 16;
 
 struct AttnParams {
   const uint16_t* q;
@@ -144,6 +157,20 @@ struct AttnParams {
   int32_t tail_per_head;
   int32_t tail_npre;      // leading chunks of every slot's walk: history + live store
   int32_t n_active;       // active slots
+  // Run-time pool (packed order with a workspace). pool_items query tiles of
+  // the heaviest slot (rank 0), item i being tile pool_qt0 - i / H of head
+  // i % H (the last full tiles of each head in turn), are not on any list: each is cut into its pool_nseg chunks of keys, piece k
+  // being chunk k % pool_nseg of item k / pool_nseg. A block that has run its
+  // list takes pieces from a counter in the workspace until none are left, so
+  // CUs that run faster (whole XCDs differ by several per cent) take more. A
+  // piece leaves its partial softmax state — the unnormalised O, the running
+  // reference m and the row sum l of every row — in the workspace, and the
+  // block that completes an item's last piece merges the item's states.
+  uint32_t* ws;           // [0]: next piece, [1 + i]: pieces done of item i
+  int32_t pool_pieces;
+  int32_t pool_nseg;
+  int32_t pool_items;
+  int32_t pool_qt0;
   int16_t xcd_n[kNumXcd];
   int16_t xcd_groups[kXcdTable];
   int16_t pack_grp[kNumXcd][kPackSegs];
@@ -561,9 +588,19 @@ attn_tick_kernel(const AttnParams p) {
     const int c = b / kNumXcd;
     item = p.pack_bin[b & (kNumXcd - 1)][c];
     item_end = p.pack_bin[b & (kNumXcd - 1)][c + 1];
-    if (item >= item_end) return;  // an empty bin
   }
+  // pieces of the run-time pool follow the list (an empty list goes straight to them)
+  __shared__ int32_t pool_slot[2];  // [0]: the piece taken; [1]: 1 = this block merges its item
+  bool in_pool = item >= item_end;
+  if (in_pool && p.pool_pieces == 0) return;
   for (;;) {
+    int piece = 0;
+    if (in_pool) {
+      if (threadIdx.x == 0) pool_slot[0] = int(atomicAdd(p.ws, 1u));
+      __syncthreads();
+      piece = pool_slot[0];
+      if (piece >= p.pool_pieces) break;  // (uniform: every thread read the same value)
+    }
     // Thread coordinates, opaque per item so that nothing derived from them
     // (per-lane offsets and bases, a few dozen registers) is hoisted out of
     // the item loop and kept live, or spilled, across it.
@@ -575,7 +612,13 @@ attn_tick_kernel(const AttnParams p) {
     const int g = lane >> 5;
     int rank = 0, h, qt;
     int tail_m = -1;  // tail item index within its head, or -1
-    if (p.use_xcd == 2) {
+    int seg0 = 0;     // pieces: the chunk of the walk this piece covers
+    if (in_pool) {
+      const int pi = piece / p.pool_nseg;
+      h = pi % p.H;
+      qt = p.pool_qt0 - pi / p.H;
+      seg0 = piece - pi * p.pool_nseg;
+    } else if (p.use_xcd == 2) {
       const int x = b & (kNumXcd - 1);
       const int k = item;
       const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
@@ -635,8 +678,9 @@ attn_tick_kernel(const AttnParams p) {
       wave_active = q0w < T;
       ntiles_w = p.nseg[s] * p.tps;
     }
-    const int nseg = p.nseg[s_blk];
+    const int nseg = in_pool ? 1 : p.nseg[s_blk];  // chunks of this item's walk
     const int ntiles = nseg * p.tps;
+    if (in_pool) ntiles_w = ntiles;
 
     const Uniforms u = load_uniforms<D, KB>(p, h);
     if constexpr (kFast) {
@@ -644,8 +688,8 @@ attn_tick_kernel(const AttnParams p) {
       for (int t = tid; t < ntiles; t += NTHREADS) {
         const int sw = t / u.tps;  // chunk index of the walk
         const int mm = t - sw * u.tps;
-        // tail items walk the live chunks in descending order
-        const int sg = (tail_m >= 0 && sw >= p.tail_npre) ? p.tail_npre + nseg - 1 - sw : sw;
+        // tail items walk the live chunks in descending order; a piece walks one chunk
+        const int sg = (tail_m >= 0 && sw >= p.tail_npre) ? p.tail_npre + nseg - 1 - sw : seg0 + sw;
         const int code = p.seg[s_blk][sg];
         const uint32_t t0 = uint32_t(KT) * uint32_t(mm);
         uint64_t kr, vr;
@@ -1176,9 +1220,10 @@ attn_tick_kernel(const AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no tile load outlives the loop
 
     // ---- epilogue: O = O^T / l, bf16 ----------------------------------------
-    if (wave_active && qrow < T) {
-      const float inv = 1.0f / xlane32_sum(l_run);
-      uint16_t* op = p.o + ((int64_t(s) * T + qrow) * p.H + h) * D;
+    // (a piece: its partial state to the workspace, and the merge of its
+    // item's states by the block that completes the item)
+    uint16_t* const op = p.o + ((int64_t(s) * T + qrow) * p.H + h) * D;
+    auto store_row = [&](const float* acc, float inv) __attribute__((always_inline)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1186,14 +1231,115 @@ attn_tick_kernel(const AttnParams p) {
           const int d = 32 * db + 8 * i + 4 * g;
           bf16x4 v4;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(oacc[db][4 * i + j] * inv);
+          for (int j = 0; j < 4; ++j) v4[j] = static_cast<__bf16>(acc[16 * db + 4 * i + j] * inv);
           *reinterpret_cast<uint2*>(op + d) = __builtin_bit_cast(uint2, v4);
         }
+    };
+    if (!in_pool) {
+      if (wave_active && qrow < T) {
+        float acc[16 * DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) acc[16 * db + x] = oacc[db][x];
+        store_row(acc, 1.0f / xlane32_sum(l_run));
+      }
+    } else {
+      // Piece state, fp32: the unnormalised O as each lane holds it (16-byte
+      // unit (wave, db, i, lane), so that every store and load of a wave is
+      // 1 KB contiguous; the merging block's lanes hold the same rows and
+      // columns), then m [QROWS] and l [QROWS] by row. Pieces of one item run
+      // on any XCD, so the states are written and read with device-scope
+      // accesses; a fence would write back and invalidate this XCD's whole
+      // L2, the other CUs' cached tiles too.
+      typedef unsigned v4u __attribute__((ext_vector_type(4)));
+      constexpr int kStateBytes = QROWS * (D + 2) * 4;
+      char* const states = reinterpret_cast<char*>(p.ws) + kWsHeader;
+      const int pi = piece / p.pool_nseg;
+      const int row = wave * 32 + r;  // row of the query tile
+      if (wave_active) {
+        const float lsum = xlane32_sum(l_run);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            states + int64_t(piece) * kStateBytes, 0, kStateBytes, kBufferFlags);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const v4u val = {__float_as_uint(oacc[db][4 * i]), __float_as_uint(oacc[db][4 * i + 1]),
+                             __float_as_uint(oacc[db][4 * i + 2]), __float_as_uint(oacc[db][4 * i + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(val, rs, (((wave * DB + db) * 4 + i) * 64 + lane) * 16,
+                                                   0, kDeviceScope);
+          }
+        if (g == 0) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), rs, (QROWS * D + row) * 4, 0,
+                                                kDeviceScope);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lsum), rs,
+                                                (QROWS * D + QROWS + row) * 4, 0, kDeviceScope);
+        }
+      }
+      // every store of the state has completed (device-visible) before the
+      // count that lets another CU read it
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      __syncthreads();
+      if (threadIdx.x == 0)
+        pool_slot[1] = atomicAdd(p.ws + 1 + pi, 1u) == uint32_t(p.pool_nseg - 1);
+      __syncthreads();
+      if (pool_slot[1] && wave_active && qrow < T) {  // every piece of item pi has left its state
+        // merge in walk order (the same sums whichever block merges): the
+        // states' maxima and sums first, then each state's O, weighted
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            states + int64_t(pi) * p.pool_nseg * kStateBytes, 0, p.pool_nseg * kStateBytes,
+            kBufferFlags);
+        const int nk = p.pool_nseg;
+        float m_all = -INFINITY;
+        for (int k0 = 0; k0 < nk; k0 += 8) {  // eight loads in flight (repeats past the last are harmless)
+          float mk[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            mk[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rs, min(k0 + j, nk - 1) * kStateBytes + (QROWS * D + row) * 4, 0, kDeviceScope));
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m_all = fmaxf(m_all, mk[j]);
+        }
+        float acc[16 * DB];
+#pragma unroll
+        for (int x = 0; x < 16 * DB; ++x) acc[x] = 0.f;
+        float l_all = 0.f;
+        for (int k = 0; k < nk; ++k) {
+          const int base = k * kStateBytes;
+          v4u o[4 * DB];
+#pragma unroll
+          for (int x = 0; x < 4 * DB; ++x)
+            o[x] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + ((wave * 4 * DB + x) * 64 + lane) * 16,
+                                                         0, kDeviceScope);
+          const float mk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rs, base + (QROWS * D + row) * 4, 0, kDeviceScope));
+          const float lk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rs, base + (QROWS * D + QROWS + row) * 4, 0, kDeviceScope));
+          const float w = __builtin_amdgcn_exp2f(mk - m_all);
+          l_all += w * lk;
+#pragma unroll
+          for (int x = 0; x < 4 * DB; ++x)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * x + j] += w * __uint_as_float(o[x][j]);
+        }
+        store_row(acc, 1.0f / l_all);
+      }
     }
-    if (++item >= item_end) break;
-    // the next item rewrites the tile-source table and the tile buffers
+    if (!in_pool && ++item < item_end) {
+      __syncthreads();  // the next item rewrites the tile-source table and the tile buffers
+      continue;
+    }
+    if (p.pool_pieces == 0) break;
+    in_pool = true;
     __syncthreads();
   }
+}
+
+// Zeroes the run-time pool's counters ahead of the attention launch (a kernel
+// rather than a memset, so that the pair can be captured in a graph).
+__global__ void clear_pool_kernel(uint32_t* ws, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ws[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -1294,7 +1440,7 @@ int cus_per_xcd() {
 //     they lower it); a block runs its bin, longest item first.
 // An item's length is modelled as its key tiles plus a fixed start-up cost.
 // Falls back (returns false) when the tables would not hold the plan.
-bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, AttnParams& p,
+bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, int pool_max, AttnParams& p,
                        int64_t& blocks) {
   if (C <= 0 || C > kPackBins) return false;
   const int ntq = p.ntq;
@@ -1314,6 +1460,21 @@ bool plan_packed_order(const StagePlan& pl, int H, int tps, int C, AttnParams& p
     const int m = t % p.tail_per_head;
     const int s_walk = pl.order[(m * NWAVES) / p.tail_spr];
     groups.push_back(Group{G + t, 1, int(pl.nseg[s_walk]) * tps + kStartup});
+  }
+  // the run-time pool: full query tiles of the heaviest slot, the last ones of
+  // its heads in turn, about kPoolShare of the tick's work
+  p.pool_items = p.pool_pieces = p.pool_nseg = 0;
+  if (pool_max > 0 && ntq_full > 0 && pl.nseg[pl.order[0]] >= 2) {
+    int64_t all = 0;
+    for (const Group& gr : groups) all += int64_t(gr.w) * gr.n;
+    const int w0 = groups[0].w;  // a query tile of rank 0 (groups 0 .. H-1 are rank 0's)
+    int want = int(std::lround(kPoolShare * double(all) / w0));
+    want = std::min({want, pool_max, kMaxPool, H * ntq_full});
+    for (int i = 0; i < want; ++i) --groups[i % H].n;  // tile ntq_full - 1 - i / H of head i % H
+    p.pool_qt0 = ntq_full - 1;
+    p.pool_items = want;
+    p.pool_nseg = pl.nseg[pl.order[0]];
+    p.pool_pieces = want * p.pool_nseg;
   }
   std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.w > b.w; });
   int64_t total = 0;
@@ -1515,15 +1676,34 @@ void plan_tail(const wf_tick_desc& d, const StagePlan& pl, AttnParams& p) {
 
 // The launch's work order: tail items and the packed per-CU lists when they
 // fit, else whole (stage, head) groups dealt to XCDs, else the plain order.
-void plan_launch_uncached(const wf_tick_desc& d, const StagePlan& pl, int C, AttnParams& p,
-                          int64_t& blocks) {
+// Pool items a workspace of `bytes` holds for this tick (each item takes one
+// partial state per chunk of the heaviest slot's walk); 0 where the pool does
+// not apply (8-bit keys, per-lane page lookups, or no workspace).
+int pool_capacity(const wf_tick_desc& d, const StagePlan& pl, int64_t bytes) {
+  const bool paged = d.n_hist > 0 || d.live_pages != nullptr || d.store_pages != nullptr;
+  const bool fast = !paged || d.P % KT == 0;
+  if (!fast || d.k_format != WF_K_BF16 || pl.n_active == 0 || bytes <= kWsHeader) return 0;
+  const int64_t per_item = pl.nseg[pl.order[0]] * state_bytes(d.D);
+  return int(std::min<int64_t>(kMaxPool, (bytes - kWsHeader) / per_item));
+}
+
+void plan_launch_uncached(const wf_tick_desc& d, const StagePlan& pl, int C, int pool_max,
+                          AttnParams& p, int64_t& blocks) {
   p.n_active = pl.n_active;
+  p.pool_items = p.pool_pieces = p.pool_nseg = 0;
   const bool paged = d.n_hist > 0 || d.live_pages != nullptr || d.store_pages != nullptr;
   const bool fast = !paged || d.P % KT == 0;
   if (fast && d.k_format == WF_K_BF16) plan_tail(d, pl, p);
   blocks = int64_t(pl.n_active) * p.items_per_stage;
-  if (!plan_packed_order(pl, d.H, p.tps, C, p, blocks)) {
+  // a pool leaves groups with fewer tiles, which can split into more runs
+  // than the tables hold: retry with one pool item fewer (the pool takes at
+  // most pool_max and at most its share) before giving up packing
+  bool packed = plan_packed_order(pl, d.H, p.tps, C, pool_max, p, blocks);
+  for (int cap = p.pool_items - 1; !packed && cap >= 0; --cap)
+    packed = plan_packed_order(pl, d.H, p.tps, C, cap, p, blocks);
+  if (!packed) {
     p.tail = 0;
+    p.pool_items = p.pool_pieces = p.pool_nseg = 0;
     blocks = int64_t(pl.n_active) * p.items_per_stage;
     plan_xcd_order(pl, d.H, p, blocks);
   }
@@ -1540,6 +1720,10 @@ void copy_plan(const AttnParams& from, AttnParams& to) {
   to.tail_per_head = from.tail_per_head;
   to.tail_npre = from.tail_npre;
   to.n_active = from.n_active;
+  to.pool_pieces = from.pool_pieces;
+  to.pool_nseg = from.pool_nseg;
+  to.pool_items = from.pool_items;
+  to.pool_qt0 = from.pool_qt0;
   std::memcpy(to.xcd_n, from.xcd_n, sizeof(to.xcd_n));
   std::memcpy(to.xcd_groups, from.xcd_groups, sizeof(to.xcd_groups));
   std::memcpy(to.pack_grp, from.pack_grp, sizeof(to.pack_grp));
@@ -1564,24 +1748,24 @@ struct PlanEntry {
   uint64_t used;
 };
 
-PlanKey plan_key(const wf_tick_desc& d, int C) {
+PlanKey plan_key(const wf_tick_desc& d, int C, int pool_max) {
   PlanKey k;
   std::memset(&k, 0, sizeof(k));
   const int32_t head[] = {d.S, int32_t(d.active_mask), d.T, d.H, d.D, d.n_hist, d.P,
                           d.k_format, d.v_format, d.live_pages != nullptr, d.store_pages != nullptr,
-                          C};
+                          C, pool_max};
   std::memcpy(k.v, head, sizeof(head));
   for (int s = 0; s <= d.S && s < WF_MAX_STAGES; ++s) k.v[16 + s] = d.hist_first[s];
   return k;
 }
 
-void plan_launch(const wf_tick_desc& d, const StagePlan& pl, int C, AttnParams& p,
+void plan_launch(const wf_tick_desc& d, const StagePlan& pl, int C, int pool_max, AttnParams& p,
                  int64_t& blocks) {
   static std::mutex mu;
   static PlanEntry cache[kPlanCache];
   static int n_cached = 0;
   static uint64_t clock = 0;
-  const PlanKey key = plan_key(d, C);
+  const PlanKey key = plan_key(d, C, pool_max);
   {
     std::lock_guard<std::mutex> lock(mu);
     for (int i = 0; i < n_cached; ++i)
@@ -1592,7 +1776,7 @@ void plan_launch(const wf_tick_desc& d, const StagePlan& pl, int C, AttnParams& 
         return;
       }
   }
-  plan_launch_uncached(d, pl, C, p, blocks);
+  plan_launch_uncached(d, pl, C, pool_max, p, blocks);
   std::lock_guard<std::mutex> lock(mu);
   int slot = n_cached < kPlanCache ? n_cached++ : 0;
   if (slot == 0 && n_cached == kPlanCache)  // evict the least recently used
@@ -1602,6 +1786,20 @@ void plan_launch(const wf_tick_desc& d, const StagePlan& pl, int C, AttnParams& 
   copy_plan(p, cache[slot].plan);
   cache[slot].blocks = blocks;
   cache[slot].used = ++clock;
+}
+
+// The launch's work order for a descriptor, planned on the host alone (the
+// diagnostic and the workspace size).
+void plan_host_only(const wf_tick_desc& d, const StagePlan& pl, int C, int pool_max, AttnParams& p,
+                    int64_t& blocks) {
+  std::memset(&p, 0, sizeof(p));
+  p.T = d.T;
+  p.H = d.H;
+  p.tps = (d.T + KT - 1) / KT;
+  p.ntq = (d.T + QROWS - 1) / QROWS;
+  p.items_per_stage = d.H * p.ntq;
+  blocks = 0;
+  plan_launch(d, pl, C, pool_max, p, blocks);
 }
 
 // kFast: every tile is one uniform span of a page or live chunk (page size a
@@ -1767,20 +1965,19 @@ extern "C" wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_pe
     StagePlan pl;
     plan_stages(d, pl);
     AttnParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.T = d.T;
-    p.H = d.H;
-    p.tps = (d.T + KT - 1) / KT;
-    p.ntq = (d.T + QROWS - 1) / QROWS;
-    p.items_per_stage = d.H * p.ntq;
     int64_t blocks = 0;
-    plan_launch(d, pl, cus_per_xcd_hint > 0 ? cus_per_xcd_hint : cus_per_xcd(), p, blocks);
+    plan_host_only(d, pl, cus_per_xcd_hint > 0 ? cus_per_xcd_hint : cus_per_xcd(),
+                   pool_capacity(d, pl, d.workspace ? d.workspace_bytes : 0), p, blocks);
     std::vector<int> out_rows;
     for (int64_t b = 0; b < blocks; ++b) {
       std::vector<std::array<int, 5>> items;
       decode_block(p, int(b), items);
       for (const auto& it : items)
         out_rows.insert(out_rows.end(), {int(b), it[0], pl.order[it[1]], it[2], it[3], it[4]});
+    }
+    for (int i = 0; i < p.pool_items; ++i) {  // run-time pool: block -1
+      const int q0 = (p.pool_qt0 - i / d.H) * QROWS;
+      out_rows.insert(out_rows.end(), {-1, i, pl.order[0], i % d.H, q0, std::min(QROWS, d.T - q0)});
     }
     *n_items = int64_t(out_rows.size() / 6);
     if (!out) return WF_OK;
@@ -1811,9 +2008,10 @@ extern "C" wf_status wf_tick_useful_flops(const wf_tick_desc* desc, double* out)
   }
 }
 
-extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) {
-  using namespace wf;
-  try {
+namespace wf {
+namespace {
+int32_t attn_tick_impl(const wf_tick_desc* desc, void* ws, int64_t ws_bytes, hipStream_t stream) {
+  {
     int32_t st = validate_tick(desc);
     if (st != WF_OK) return st;
     const wf_tick_desc& d = *desc;
@@ -1881,7 +2079,13 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
       for (int i = 0; i < pl.nseg[s]; ++i) p.seg[s][i] = pl.seg[s][i];
     }
     int64_t blocks = 0;
-    plan_launch(d, pl, cus_per_xcd(), p, blocks);
+    plan_launch(d, pl, cus_per_xcd(), pool_capacity(d, pl, ws ? ws_bytes : 0), p, blocks);
+    p.ws = static_cast<uint32_t*>(ws);
+    if (p.pool_pieces > 0) {  // counters of the run-time pool start at zero
+      clear_pool_kernel<<<1, 64, 0, stream>>>(p.ws, 1 + p.pool_items);
+      st = check_launch("wf_attn_tick (pool counters)");
+      if (st != WF_OK) return st;
+    }
     blocks += p.n_store_blocks;  // a multiple of 8: the XCD of every attention block is kept
     if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
     const bool fast = !paged || d.P % KT == 0;
@@ -1907,7 +2111,48 @@ extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) 
                 : launch_attn<64, false>(p, unsigned(blocks), stream);
     if (st != WF_OK) return st;
     return check_launch("wf_attn_tick");
+  }
+}
+
+}  // namespace
+}  // namespace wf
+
+extern "C" wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream) {
+  using namespace wf;
+  try {
+    if (desc && desc->workspace && (reinterpret_cast<uintptr_t>(desc->workspace) & 255u))
+      return fail(WF_EINVAL, "wf_attn_tick: workspace must be 256-byte aligned");
+    if (desc && desc->workspace_bytes < 0)
+      return fail(WF_EINVAL, "wf_attn_tick: workspace_bytes = %lld",
+                  static_cast<long long>(desc->workspace_bytes));
+    return attn_tick_impl(desc, desc ? desc->workspace : nullptr,
+                          desc ? desc->workspace_bytes : 0, stream);
   } catch (...) {
     return fail(WF_EINVAL, "wf_attn_tick: internal error");
+  }
+}
+
+extern "C" wf_status wf_tick_workspace_bytes(const wf_tick_desc* desc, int64_t* bytes) {
+  using namespace wf;
+  try {
+    if (!bytes) return fail(WF_EINVAL, "wf_tick_workspace_bytes: bytes is NULL");
+    int32_t st = validate_tick(desc);
+    if (st != WF_OK) return st;
+    *bytes = 0;
+    if (desc->T == 0 || desc->active_mask == 0) return WF_OK;
+    StagePlan pl;
+    plan_stages(*desc, pl);
+    if (pool_capacity(*desc, pl, int64_t(1) << 60) == 0) return WF_OK;
+    // the items the planner gives the pool when space is no limit (the CU
+    // count of the current device, else MI355X's 32 per XCD)
+    AttnParams p;
+    int64_t blocks = 0;
+    const int C = cus_per_xcd();
+    plan_host_only(*desc, pl, C > 0 ? C : 32, kMaxPool, p, blocks);
+    if (p.pool_items > 0)
+      *bytes = kWsHeader + int64_t(p.pool_items) * p.pool_nseg * state_bytes(desc->D);
+    return WF_OK;
+  } catch (...) {
+    return fail(WF_EINVAL, "wf_tick_workspace_bytes: internal error");
   }
 }

@@ -50,7 +50,8 @@ class WfTickDesc(ctypes.Structure):
                 ("k_pool", _vp), ("v_pool", _vp), ("num_pages", _i32), ("P", _i32),
                 ("hist_pages", _vp), ("n_hist", _i32), ("hist_first", _i32 * MAX_STAGES),
                 ("live_pages", _vp), ("store_pages", _vp),
-                ("k_format", _i32), ("k_scale", _vp), ("v_format", _i32), ("v_exp", _vp)]
+                ("k_format", _i32), ("k_scale", _vp), ("v_format", _i32), ("v_exp", _vp),
+                ("workspace", _vp), ("workspace_bytes", ctypes.c_int64)]
 
 
 K_BF16 = 0
@@ -86,10 +87,12 @@ _lib.wf_attn_tick.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
 _lib.wf_tick_useful_flops.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_double)]
 _lib.wf_tick_work_order.argtypes = [ctypes.POINTER(WfTickDesc), _i32, _i32p, ctypes.c_int64,
                                     ctypes.POINTER(ctypes.c_int64)]
+_lib.wf_tick_workspace_bytes.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_int64)]
 for _f in ("wf_page_table_create", "wf_page_table_pages_per_chunk", "wf_page_table_alloc_chunk",
            "wf_page_table_commit", "wf_page_table_export", "wf_page_table_num_free",
            "wf_store_paged", "wf_gather_paged", "wf_rope_store_paged", "wf_store_paged_fp8",
-           "wf_attn_tick", "wf_tick_useful_flops", "wf_tick_work_order"):
+           "wf_attn_tick", "wf_tick_useful_flops", "wf_tick_work_order",
+           "wf_tick_workspace_bytes"):
     getattr(_lib, _f).restype = _i32
 
 EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
@@ -97,7 +100,7 @@ EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
                     "wf_page_table_alloc_chunk", "wf_page_table_commit", "wf_page_table_export",
                     "wf_page_table_num_free", "wf_store_paged", "wf_gather_paged",
                     "wf_rope_store_paged", "wf_store_paged_fp8", "wf_attn_tick",
-                    "wf_tick_useful_flops", "wf_tick_work_order")
+                    "wf_tick_useful_flops", "wf_tick_work_order", "wf_tick_workspace_bytes")
 
 
 def _check(status: int, where: str) -> None:
@@ -380,7 +383,7 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
                    num_pages: int = 0, P: int = 0, hist_pages=None, n_hist: int = 0,
                    hist_first: Optional[Sequence[int]] = None,
                    live_pages=None, store_pages=None, k_scale=None,
-                   v_exp=None) -> WfTickDesc:
+                   v_exp=None, workspace=None) -> WfTickDesc:
     d = WfTickDesc()
     d.S, d.active_mask, d.T, d.H, d.D, d.scale = S, active_mask, T, H, D, scale
     d.q, d.k, d.v, d.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
@@ -396,13 +399,15 @@ def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: floa
     d.k_scale = _ptr(k_scale)
     d.v_format = V_BF16 if v_exp is None else V_E4M3
     d.v_exp = _ptr(v_exp)
+    d.workspace = _ptr(workspace)
+    d.workspace_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     return d
 
 
 def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None, v_pool=None,
                  hist_pages=None, hist_first: Optional[Sequence[int]] = None,
                  stream=None, live_pages=None, store_pages=None, k_scale=None,
-                 v_exp=None) -> None:
+                 v_exp=None, workspace=None) -> None:
     """One tick: q, k, v, o [S+1][T][H][D]; pools [num_pages][P][H][D];
     hist_pages int32 [n_hist][ceil(T/P)] on the device; live_pages (optional)
     int32 [S+1][ceil(T/P)] on the device: live K/V read from those pages (k and
@@ -411,7 +416,10 @@ def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None
     (optional, float32 [num_pages][P/64][H]): the 8-bit tier — k_pool holds
     e4m3 codes (uint8) as written by wf_store_paged_fp8, live_pages required.
     v_exp (optional, uint8 [num_pages][P/64][H], with k_scale): 8-bit values —
-    v_pool holds the transposed e4m3 tiles written by wf_store_paged_fp8."""
+    v_pool holds the transposed e4m3 tiles written by wf_store_paged_fp8.
+    workspace (optional, contiguous device tensor of workspace_bytes(...)
+    bytes, 256-byte aligned): part of the work is handed out at run time to
+    free CUs (launches sharing a workspace must not overlap)."""
     live = (("k", k), ("v", v)) if live_pages is None else ()
     for n, t in (("q", q), ("o", o)) + live:
         _check_bf16(n, t)
@@ -457,15 +465,17 @@ def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None
             _check_ids("live_pages", live_pages, (S + 1, ppc))
         if store_pages is not None:
             _check_ids("store_pages", store_pages, (ppc,))
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     _check_on_gpu(q=q, o=o, k=k if live_pages is None else None,
                   v=v if live_pages is None else None,
                   k_pool=k_pool if pooled else None, v_pool=v_pool if pooled else None,
                   hist_pages=hist_pages if n_hist else None, live_pages=live_pages,
-                  store_pages=store_pages, k_scale=k_scale, v_exp=v_exp)
+                  store_pages=store_pages, k_scale=k_scale, v_exp=v_exp, workspace=workspace)
     d = make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
                        k_pool if pooled else None, v_pool if pooled else None, num_pages, P,
                        hist_pages if n_hist else None, n_hist, hist_first, live_pages,
-                       store_pages, k_scale, v_exp)
+                       store_pages, k_scale, v_exp, workspace)
     _check(_lib.wf_attn_tick(ctypes.byref(d), _stream(stream)), "wf_attn_tick")
 
 
@@ -505,3 +515,24 @@ def tick_work_order(desc: WfTickDesc, cus_per_xcd: int = 0) -> np.ndarray:
     _check(_lib.wf_tick_work_order(ctypes.byref(desc), cus_per_xcd, out.ctypes.data_as(_i32p),
                                    out.size, ctypes.byref(n)), "wf_tick_work_order")
     return out.reshape(n.value, 6)
+
+
+def tick_workspace_bytes(desc: WfTickDesc) -> int:
+    """wf_tick_workspace_bytes: workspace size for the full run-time pool (0: none)."""
+    out = ctypes.c_int64()
+    _check(_lib.wf_tick_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)),
+           "wf_tick_workspace_bytes")
+    return out.value
+
+
+def workspace_bytes(S: int, active_mask: int, T: int, H: int, D: int, n_hist: int = 0,
+                    hist_first: Optional[Sequence[int]] = None, P: int = 64,
+                    num_pages: int = 0, live_paged: bool = False) -> int:
+    """Workspace bytes wf_attn_tick would use for a bf16 tick of this shape."""
+    fake = 16
+    d = make_tick_desc(S, active_mask, T, H, D, 1.0, fake, fake, fake, fake,
+                       fake if (n_hist or live_paged) else None, fake if (n_hist or live_paged) else None,
+                       max(num_pages, (n_hist + S + 1) * -(-T // P)) if (n_hist or live_paged) else 0,
+                       P if (n_hist or live_paged) else 0, fake if n_hist else None, n_hist,
+                       hist_first, fake if live_paged else None)
+    return tick_workspace_bytes(d)
