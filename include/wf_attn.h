@@ -309,6 +309,22 @@ typedef struct wf_tick_desc {
 
 wf_status wf_attn_tick(const wf_tick_desc* desc, hipStream_t stream);
 
+/* Allocation-free variant of wf_attn_tick, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the run-time pool's workspace is an array of
+ * WF_NOALLOC_SCRATCH_BYTES in the library's code object, one per GPU, held
+ * until the process ends; the call allocates nothing. desc->workspace must be
+ * NULL and desc->workspace_bytes (0 .. WF_NOALLOC_SCRATCH_BYTES) is the part of
+ * the array the pool may use: the smaller of wf_tick_workspace_bytes and the
+ * maximum gives the same launch as wf_attn_tick with a workspace of that size
+ * (0: no pool). Beyond the maximum, or with a workspace pointer: WF_EINVAL.
+ * Every call on a GPU uses that GPU's one array, which keeps the last call's
+ * contents (the counters are cleared at each call): calls that overlap on one
+ * GPU (on different streams, or from several host threads) race. Otherwise as
+ * wf_attn_tick. */
+#define WF_NOALLOC_SCRATCH_BYTES (64ll << 20)
+wf_status wf_attn_tick_noalloc(const wf_tick_desc* desc, hipStream_t stream);
+
 /* Workspace size for wf_attn_tick with this descriptor: the bytes that hold the
  * run-time pool's full share (about 8 % of the tick's work, at most 128 query
  * tiles, one partial state of 256 rows x (D + 2) fp32 per chunk of keys, plus

@@ -623,3 +623,19 @@ def test_tick_validation_workspace():
     with pytest.raises(wf.WfError):
         wf.tick_workspace_bytes(bad)
     assert wf.tick_workspace_bytes(desc(None, 0)) >= 0
+
+
+def test_noalloc_validation():
+    """wf_attn_tick_noalloc refuses a workspace pointer and workspace_bytes
+    outside [0, WF_NOALLOC_SCRATCH_BYTES] before touching the device."""
+    import ctypes
+    wf = _wfattn()
+    fake = 1 << 20
+    declared = re.search(r"#define WF_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", open(HEADER).read())
+    assert int(declared.group(1)) << int(declared.group(2)) == wf.NOALLOC_SCRATCH_BYTES
+    for ws, nb in ((fake, 1 << 20), (None, wf.NOALLOC_SCRATCH_BYTES + 1), (None, -1)):
+        d = _desc(wf, q=fake, k=fake, v=fake, o=fake)
+        d.workspace = ws
+        d.workspace_bytes = nb
+        assert wf.library().wf_attn_tick_noalloc(ctypes.byref(d), None) == CODES["EINVAL"]
+        assert "wf_attn_tick_noalloc" in wf.last_error()

@@ -1,0 +1,50 @@
+"""wf_attn_tick_noalloc (the run-time pool in the library's own per-GPU array,
+no allocation by the call) against wf_attn_tick with a caller workspace of the
+same size: two calls in a row, the second with a smaller tick (the array keeps
+the first call's states and counters), each bit for bit equal to the other
+entry point's launch and within the parity bar of the oracle on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from _gpu_common import compare, oracle_tick, run_tick, say, setup_tick
+from wavefront_causal_attention_wf_amd import wfattn
+
+pytestmark = pytest.mark.gpu
+
+# (S, T, H, P, n_hist): the 4-step steady tick's shape, then a smaller tick
+CALLS = [(4, 4680, 12, 64, 3), (2, 600, 2, 64, 1)]
+
+
+def sample_rows(T: int, seed: int) -> np.ndarray:
+    fixed = [0, 31, 32, 255, 256, T // 2, T - 73, T - 33, T - 1]
+    rnd = np.random.default_rng(seed).choice(T, 8, replace=False)
+    return np.array(sorted({r for r in fixed + list(rnd) if 0 <= r < T}))
+
+
+def test_noalloc_two_calls_second_smaller():
+    for i, (S, T, H, P, n_hist) in enumerate(CALLS):
+        say(f"no-alloc call {i}: S={S} T={T} H={H} P={P} n_hist={n_hist}")
+        t = setup_tick(S, T, H, 128, P, n_hist, (n_hist + 2) * -(-T // P) + 8, seed=40 + i)
+        full = wfattn.workspace_bytes(S, t.active_mask, T, H, 128, n_hist, None, P, t.num_pages)
+        nb = min(full, wfattn.NOALLOC_SCRATCH_BYTES)
+        assert nb > 0
+        ws = torch.empty(nb, dtype=torch.uint8, device=t.q.device)
+        d = wfattn.make_tick_desc(S, t.active_mask, T, H, 128, t.scale, t.q, t.k, t.v, t.o,
+                                  t.k_pool, t.v_pool, t.num_pages, P, t.hist_pages, n_hist,
+                                  None, workspace=ws)
+        n_pool = int(np.sum(wfattn.tick_work_order(d, 0)[:, 0] == -1))
+        say(f"  scratch bytes {nb} (full pool {full}), pool items {n_pool}")
+        assert n_pool > 0
+        o_na = torch.full_like(t.q, float("nan"))
+        wfattn.wf_attn_tick_noalloc(t.q, t.k, t.v, o_na, S, t.active_mask, t.scale, t.k_pool,
+                                    t.v_pool, t.hist_pages, scratch_bytes=nb)
+        torch.cuda.synchronize()
+        o_ws = run_tick(t, o=torch.full_like(t.q, float("nan")), workspace=ws)
+        assert torch.equal(o_na.view(torch.int16), o_ws.view(torch.int16)), f"call {i}"
+        rows = sample_rows(T, seed=i)
+        worst = compare(o_na, oracle_tick(t, rows=rows), rows=rows, label=f"no-alloc call {i}")
+        say(f"  bit-identical to wf_attn_tick with a workspace; worst rel-L2 vs oracle {worst:.2e}")
+        del t, ws, o_na, o_ws
+        torch.cuda.empty_cache()

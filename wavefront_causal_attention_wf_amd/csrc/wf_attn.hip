@@ -61,6 +61,11 @@
 
 #include "wf_internal.h"
 
+// Workspace of wf_attn_tick_noalloc: one array per GPU in the code object,
+// held until the process ends. Host code takes its device address from
+// hipGetSymbolAddress (once per device), never from the name.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[WF_NOALLOC_SCRATCH_BYTES];
+
 namespace wf {
 namespace {
 
@@ -2010,6 +2015,35 @@ extern "C" wf_status wf_tick_useful_flops(const wf_tick_desc* desc, double* out)
 
 namespace wf {
 namespace {
+// Device address of the allocation-free entry point's workspace on the
+// current device, looked up with that device current on its first call there.
+void* scratch_address(int32_t& st) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    st = hip_fail(e, "wf_attn_tick_noalloc (hipGetDevice)");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= 64) {
+    st = fail(WF_EUNSUPPORTED, "wf_attn_tick_noalloc: device %d beyond 64", dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      st = hip_fail(e, "wf_attn_tick_noalloc (hipGetSymbolAddress)");
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  st = WF_OK;
+  return addr[dev];
+}
+
 int32_t attn_tick_impl(const wf_tick_desc* desc, void* ws, int64_t ws_bytes, hipStream_t stream) {
   {
     int32_t st = validate_tick(desc);
@@ -2154,5 +2188,27 @@ extern "C" wf_status wf_tick_workspace_bytes(const wf_tick_desc* desc, int64_t* 
     return WF_OK;
   } catch (...) {
     return fail(WF_EINVAL, "wf_tick_workspace_bytes: internal error");
+  }
+}
+
+extern "C" wf_status wf_attn_tick_noalloc(const wf_tick_desc* desc, hipStream_t stream) {
+  using namespace wf;
+  try {
+    if (!desc) return fail(WF_EINVAL, "wf_attn_tick_noalloc: desc is NULL");
+    if (desc->workspace)
+      return fail(WF_EINVAL, "wf_attn_tick_noalloc: workspace must be NULL (the library's own is used)");
+    if (desc->workspace_bytes < 0 || desc->workspace_bytes > WF_NOALLOC_SCRATCH_BYTES)
+      return fail(WF_EINVAL, "wf_attn_tick_noalloc: workspace_bytes = %lld outside [0, %lld]",
+                  static_cast<long long>(desc->workspace_bytes),
+                  static_cast<long long>(WF_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    if (desc->workspace_bytes > 0) {
+      int32_t st = WF_OK;
+      ws = scratch_address(st);
+      if (!ws) return st;
+    }
+    return attn_tick_impl(desc, ws, desc->workspace_bytes, stream);
+  } catch (...) {
+    return fail(WF_EINVAL, "wf_attn_tick_noalloc: internal error");
   }
 }

@@ -58,6 +58,7 @@ K_BF16 = 0
 K_E4M3 = 1
 V_BF16 = 0
 V_E4M3 = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20   # WF_NOALLOC_SCRATCH_BYTES
 
 
 class WfRopeDesc(ctypes.Structure):
@@ -84,6 +85,7 @@ _lib.wf_rope_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, 
 _lib.wf_store_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _vp]
 _lib.wf_attn_tick.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
+_lib.wf_attn_tick_noalloc.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
 _lib.wf_tick_useful_flops.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_double)]
 _lib.wf_tick_work_order.argtypes = [ctypes.POINTER(WfTickDesc), _i32, _i32p, ctypes.c_int64,
                                     ctypes.POINTER(ctypes.c_int64)]
@@ -92,7 +94,7 @@ for _f in ("wf_page_table_create", "wf_page_table_pages_per_chunk", "wf_page_tab
            "wf_page_table_commit", "wf_page_table_export", "wf_page_table_num_free",
            "wf_store_paged", "wf_gather_paged", "wf_rope_store_paged", "wf_store_paged_fp8",
            "wf_attn_tick", "wf_tick_useful_flops", "wf_tick_work_order",
-           "wf_tick_workspace_bytes"):
+           "wf_tick_workspace_bytes", "wf_attn_tick_noalloc"):
     getattr(_lib, _f).restype = _i32
 
 EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
@@ -100,7 +102,8 @@ EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
                     "wf_page_table_alloc_chunk", "wf_page_table_commit", "wf_page_table_export",
                     "wf_page_table_num_free", "wf_store_paged", "wf_gather_paged",
                     "wf_rope_store_paged", "wf_store_paged_fp8", "wf_attn_tick",
-                    "wf_tick_useful_flops", "wf_tick_work_order", "wf_tick_workspace_bytes")
+                    "wf_tick_useful_flops", "wf_tick_work_order", "wf_tick_workspace_bytes",
+                    "wf_attn_tick_noalloc")
 
 
 def _check(status: int, where: str) -> None:
@@ -408,7 +411,29 @@ def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None
                  hist_pages=None, hist_first: Optional[Sequence[int]] = None,
                  stream=None, live_pages=None, store_pages=None, k_scale=None,
                  v_exp=None, workspace=None) -> None:
-    """One tick: q, k, v, o [S+1][T][H][D]; pools [num_pages][P][H][D];
+    """wf_attn_tick; arguments as tick_desc."""
+    d = tick_desc(q, k, v, o, S, active_mask, scale, k_pool, v_pool, hist_pages, hist_first,
+                  live_pages, store_pages, k_scale, v_exp, workspace)
+    _check(_lib.wf_attn_tick(ctypes.byref(d), _stream(stream)), "wf_attn_tick")
+
+
+def wf_attn_tick_noalloc(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None,
+                         v_pool=None, hist_pages=None, hist_first: Optional[Sequence[int]] = None,
+                         stream=None, live_pages=None, store_pages=None, k_scale=None,
+                         v_exp=None, scratch_bytes: int = 0) -> None:
+    """wf_attn_tick_noalloc: as wf_attn_tick, the run-time pool in the
+    library's own per-GPU array, of which it may use scratch_bytes (at most
+    WF_NOALLOC_SCRATCH_BYTES)."""
+    d = tick_desc(q, k, v, o, S, active_mask, scale, k_pool, v_pool, hist_pages, hist_first,
+                  live_pages, store_pages, k_scale, v_exp, None)
+    d.workspace_bytes = int(scratch_bytes)
+    _check(_lib.wf_attn_tick_noalloc(ctypes.byref(d), _stream(stream)), "wf_attn_tick_noalloc")
+
+
+def tick_desc(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None, v_pool=None,
+              hist_pages=None, hist_first: Optional[Sequence[int]] = None, live_pages=None,
+              store_pages=None, k_scale=None, v_exp=None, workspace=None) -> WfTickDesc:
+    """Checked descriptor of one tick: q, k, v, o [S+1][T][H][D]; pools [num_pages][P][H][D];
     hist_pages int32 [n_hist][ceil(T/P)] on the device; live_pages (optional)
     int32 [S+1][ceil(T/P)] on the device: live K/V read from those pages (k and
     v may then be None); store_pages (optional) int32 [ceil(T/P)] on the device:
@@ -472,11 +497,10 @@ def wf_attn_tick(q, k, v, o, S: int, active_mask: int, scale: float, k_pool=None
                   k_pool=k_pool if pooled else None, v_pool=v_pool if pooled else None,
                   hist_pages=hist_pages if n_hist else None, live_pages=live_pages,
                   store_pages=store_pages, k_scale=k_scale, v_exp=v_exp, workspace=workspace)
-    d = make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
-                       k_pool if pooled else None, v_pool if pooled else None, num_pages, P,
-                       hist_pages if n_hist else None, n_hist, hist_first, live_pages,
-                       store_pages, k_scale, v_exp, workspace)
-    _check(_lib.wf_attn_tick(ctypes.byref(d), _stream(stream)), "wf_attn_tick")
+    return make_tick_desc(S, active_mask, T, H, D, scale, q, k, v, o,
+                          k_pool if pooled else None, v_pool if pooled else None, num_pages, P,
+                          hist_pages if n_hist else None, n_hist, hist_first, live_pages,
+                          store_pages, k_scale, v_exp, workspace)
 
 
 def wf_attn_tick_desc(desc: WfTickDesc, stream=None) -> None:
