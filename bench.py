@@ -492,9 +492,9 @@ class Fp8Tick:
         torch.cuda.synchronize()
 
     def store_live(self):
-        for j in range(self.cfg.S + 1):
-            self.wf.wf_store_paged_fp8(self.k[j], self.v[j], self.k_pool, self.k_scale,
-                                       self.v_pool, self.live[j], v_exp=self.v_exp)
+        # every live chunk's producer write, one launch
+        self.wf.wf_store_paged_fp8_chunks(self.k, self.v, self.k_pool, self.k_scale, self.v_pool,
+                                          self.live, v_exp=self.v_exp)
 
     def attn(self):
         self.wf.wf_attn_tick(self.q, None, None, self.o, self.cfg.S, self.mask, self.scale,
@@ -504,7 +504,7 @@ class Fp8Tick:
 
 def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3, v8: bool = False) -> dict:
     """8-bit tier: attention launches alone, and the tick with every live chunk's
-    producer write (five wf_store_paged_fp8 + the attention). v8: values in
+    producer write (one wf_store_paged_fp8_chunks launch + the attention). v8: values in
     e4m3 too (P.V on the fp8 MFMA: all useful flops at the fp8 peak)."""
     import torch
 
@@ -539,7 +539,8 @@ def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3, v8: bool = False) ->
                 "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
                 "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                 "tick_with_producer_writes_ms": round(ms_tick, 4),
-                "tick_flow": f"{cfg.S + 1} x wf_store_paged_fp8 with v_exp + wf_attn_tick"}
+                "tick_flow": f"wf_store_paged_fp8_chunks with v_exp ({cfg.S + 1} live chunks, "
+                             "one launch) + wf_attn_tick"}
     return {"tier": "e4m3 Q and K (per-row / per-(64-token tile, head) fp32 scales), Q.K^T on "
                     "fp8 MFMA, bf16 P.V; every key through pages",
             "attn_kernel_ms_mean": round(ms, 4), "useful_tflop_per_s": round(tf, 2),
@@ -547,35 +548,63 @@ def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3, v8: bool = False) ->
             "blended_peak_tflop_per_s": round(PEAK_FP8_TIER_TFLOPS, 1),
             "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "tick_with_producer_writes_ms": round(ms_tick, 4),
-            "tick_flow": f"{cfg.S + 1} x wf_store_paged_fp8 (every live chunk) + wf_attn_tick"}
+            "tick_flow": f"wf_store_paged_fp8_chunks ({cfg.S + 1} live chunks, one launch) + "
+                         "wf_attn_tick"}
 
 
 def store_fp8_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> dict:
-    """wf_store_paged_fp8 of one chunk (K quantised, V copied), rotating over
-    `rotation` source chunks and page sets so that they do not sit in the
-    last-level cache."""
+    """The 8-bit tier's producer writes, rotating over `rotation` source ticks
+    and page sets so that they do not sit in the last-level cache:
+    wf_store_paged_fp8 of one chunk (K quantised, V copied), and
+    wf_store_paged_fp8_chunks of a tick's S+1 live chunks in one launch, with V
+    copied and with V quantised (v_exp) — the tick's producer write."""
     import torch
 
     from wavefront_causal_attention_wf_amd import inputs, wfattn
 
-    T, H, D, P, ppc = cfg.T, cfg.H, cfg.D, cfg.P, cfg.ppc
-    srcs = [inputs.draw_live_torch(cfg, 3000 + i, dev, T=T)[:2] for i in range(rotation)]
-    k_pool = torch.zeros((rotation * ppc, P, H, D), dtype=torch.uint8, device=dev)
-    k_scale = torch.zeros((rotation * ppc, P // 64, H), dtype=torch.float32, device=dev)
-    v_pool = torch.zeros((rotation * ppc, P, H, D), dtype=torch.bfloat16, device=dev)
-    ids = [torch.arange(i * ppc, (i + 1) * ppc, dtype=torch.int32, device=dev)
+    S, T, H, D, P, ppc = cfg.S, cfg.T, cfg.H, cfg.D, cfg.P, cfg.ppc
+    n = S + 1
+    srcs = [inputs.draw_live_torch(cfg, 3000 + i, dev, T=T)[1:3] for i in range(rotation)]
+    pages = rotation * n * ppc
+    k_pool = torch.zeros((pages, P, H, D), dtype=torch.uint8, device=dev)
+    k_scale = torch.zeros((pages, P // 64, H), dtype=torch.float32, device=dev)
+    v_pool = torch.zeros((pages, P, H, D), dtype=torch.bfloat16, device=dev)
+    v8_pool = torch.zeros((pages, P // 64, H, D, 64), dtype=torch.uint8, device=dev)
+    v_exp = torch.zeros((pages, P // 64, H), dtype=torch.uint8, device=dev)
+    ids = [torch.arange(i * n * ppc, (i + 1) * n * ppc, dtype=torch.int32, device=dev).view(n, ppc)
            for i in range(rotation)]
 
-    def launch(i):
+    def one(i):
         k, v = srcs[i % rotation]
-        wfattn.wf_store_paged_fp8(k[0], v[0], k_pool, k_scale, v_pool, ids[(i * 3) % rotation])
+        wfattn.wf_store_paged_fp8(k[0], v[0], k_pool, k_scale, v_pool, ids[(i * 3) % rotation][0])
 
-    ms = graph_time_ms(launch, rotation, launches)
-    nbytes = 2 * (T * H * D * 2) + ppc * P * H * D * 3 + ppc * (P // 64) * H * 4
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"kernel": "wf_store_paged_fp8", "us_mean": round(ms * 1e3, 2), "bytes": nbytes,
-            "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "rotation": rotation}
+    def tick(i):
+        k, v = srcs[i % rotation]
+        wfattn.wf_store_paged_fp8_chunks(k, v, k_pool, k_scale, v_pool, ids[(i * 3) % rotation])
+
+    def tick_v8(i):
+        k, v = srcs[i % rotation]
+        wfattn.wf_store_paged_fp8_chunks(k, v, k_pool, k_scale, v8_pool, ids[(i * 3) % rotation],
+                                         v_exp=v_exp)
+
+    def rate(ms, nbytes):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"us_mean": round(ms * 1e3, 2), "bytes": nbytes, "gb_per_s": round(gbs, 1),
+                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+    # per chunk: K and V read (bf16), codes + bf16 V written, one scale per (tile, head)
+    chunk = 2 * (T * H * D * 2) + ppc * P * H * D * 3 + ppc * (P // 64) * H * 4
+    # 8-bit values: codes for V too, one exponent byte per (tile, head)
+    chunk8 = 2 * (T * H * D * 2) + ppc * P * H * D * 2 + ppc * (P // 64) * H * 5
+    out = {"kernel": "wf_store_paged_fp8", **rate(graph_time_ms(one, rotation, launches), chunk),
+           "rotation": rotation}
+    out["tick_chunks"] = {"kernel": f"wf_store_paged_fp8_chunks ({n} chunks, one launch)",
+                          **rate(graph_time_ms(tick, rotation, launches // 4), n * chunk)}
+    out["tick_chunks_v8"] = {"kernel": f"wf_store_paged_fp8_chunks with v_exp ({n} chunks)",
+                             **rate(graph_time_ms(tick_v8, rotation, launches // 4), n * chunk8)}
+    del srcs, k_pool, k_scale, v_pool, v8_pool, v_exp
+    torch.cuda.empty_cache()
+    return out
 
 
 def other_config(name: str, dev, steps: int = 10, warmup: int = 3) -> dict:

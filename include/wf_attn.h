@@ -199,6 +199,19 @@ wf_status wf_store_paged_fp8(const void* k_src, const void* v_src, void* k_pool,
                              int32_t H, int32_t D, int32_t num_pages, int32_t P,
                              hipStream_t stream);
 
+/* wf_store_paged_fp8_chunks — n_chunks producer writes in one launch (a tick's
+ * live chunks, each into its own pages), each chunk exactly as
+ * wf_store_paged_fp8 writes it: k_src, v_src device bf16 [n_chunks][T][H][D],
+ * page_ids device int32 [n_chunks][ceil(T/P)]; pools, scales and v_exp as
+ * there. The chunks' pages must be distinct. One launch instead of n keeps the
+ * memory system busy across the chunks instead of ramping up and down for
+ * each. Errors as wf_store_paged_fp8, plus WF_EINVAL for n_chunks < 0;
+ * n_chunks = 0 is a no-op. */
+wf_status wf_store_paged_fp8_chunks(const void* k_src, const void* v_src, int32_t n_chunks,
+                                    void* k_pool, float* k_scale, void* v_pool, uint8_t* v_exp,
+                                    const int32_t* page_ids, int32_t T, int32_t H, int32_t D,
+                                    int32_t num_pages, int32_t P, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* wf_gather_paged — diagnostic inverse of the store: copy n_chunks chunks    */
 /* from pool pages into contiguous k_dst, v_dst bf16 [n_chunks][T][H][D].     */

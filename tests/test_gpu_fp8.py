@@ -418,3 +418,45 @@ def test_fp8kv_tick_full_size_sampled_rows(name):
     r_el, r_l2 = compare_kv8(o, want, bound, rms, rows=rows, label="fp8 K/V full size")
     say(f"[full-size fp8 K/V] worst error / allowance: element {r_el:.3f}, rel-L2 {r_l2:.3f} "
         f"over {len(rows)} rows")
+
+
+@pytest.mark.parametrize("n,T,H,D,P", [
+    (3, 200, 2, 128, 64),      # ragged last page
+    (2, 150, 3, 64, 128),      # two scale tiles per page, the last one empty
+    (5, 4680, 12, 128, 64),    # a 4-step tick's live chunks
+])
+@pytest.mark.parametrize("v8", [False, True])
+def test_store_fp8_chunks_equals_one_call_per_chunk(n, T, H, D, P, v8):
+    """wf_store_paged_fp8_chunks (n chunks, one launch) leaves every pool byte
+    as n wf_store_paged_fp8 calls do (pools poisoned alike beforehand), so its
+    pages are the oracle's as well."""
+    if v8 and D != 128:
+        pytest.skip("8-bit values: D = 128")
+    say(f"store fp8 chunks n={n} T={T} H={H} D={D} P={P} v8={v8}")
+    ppc = -(-T // P)
+    num_pages = n * ppc + 7
+    cfg = inputs.TickConfig("s", S=n - 1, T=T, H=H, D=D, P=P, n_hist=0, num_pages=num_pages,
+                            std=0.5, bf16_inputs=True, page_order="permutation")
+    _, k, v = inputs.draw_live_torch(cfg, 91 + T, DEV)
+    ids = torch.from_numpy(np.random.default_rng(T).permutation(num_pages)[:n * ppc]
+                           .astype(np.int32).reshape(n, ppc)).to(DEV)
+
+    def pools():
+        kp = torch.full((num_pages, P, H, D), 0xFF, dtype=torch.uint8, device=DEV)
+        ks = torch.full((num_pages, P // 64, H), float("nan"), dtype=torch.float32, device=DEV)
+        if v8:
+            vp = torch.full((num_pages, P // 64, H, D, 64), 0xFF, dtype=torch.uint8, device=DEV)
+            ve = torch.full((num_pages, P // 64, H), 0xFF, dtype=torch.uint8, device=DEV)
+        else:
+            vp = torch.full((num_pages, P, H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+            ve = None
+        return kp, ks, vp, ve
+
+    a, b = pools(), pools()
+    wfattn.wf_store_paged_fp8_chunks(k, v, a[0], a[1], a[2], ids, v_exp=a[3])
+    for c in range(n):
+        wfattn.wf_store_paged_fp8(k[c], v[c], b[0], b[1], b[2], ids[c], v_exp=b[3])
+    torch.cuda.synchronize()
+    for x, y, name in zip(a, b, ("k_pool", "k_scale", "v_pool", "v_exp")):
+        if x is not None:
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), name

@@ -28,6 +28,7 @@
 // 32*(j / 16) + 16*((j / 8) % 2) + 8*g + j % 8 of the tile.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "wf_internal.h"
@@ -73,31 +74,34 @@ __device__ __forceinline__ int v8_column(int t) {
   return 32 * ((t >> 3) & 1) + 16 * ((t >> 5) & 1) + 8 * ((t >> 4) & 1) + (t & 7);
 }
 
-// Block (x = 64-token tile in page order, y = head, z = 0): the tile's keys of
-// head h -> codes and scale, and (bf16 values) its values of head h copied;
-// z = 1 (8-bit values only): its values of head h -> codes in the transposed
-// tile and the exponent. One thread owns UPT 16-byte units (8 channels of one
-// token), all loaded before any store; bf16 values are copied before the
-// block's amax reduction.
+// 8-bit values. Block (x = chunk * tiles + 64-token tile in page order, y =
+// head, z = 0): the tile's keys of head h -> codes and scale; z = 1: its
+// values of head h -> codes in the transposed tile and the exponent. One thread owns UPT 16-byte units
+// (8 channels of one token), all loaded before any store; bf16 values are
+// copied before the block's amax reduction. Chunk c reads its sources at
+// c * T * H * D and its page ids at c * ppc.
 template <int D>
-__global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
+__global__ __launch_bounds__(kQThreads) void store_fp8_v8_kernel(
     const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint8_t* __restrict__ k_pool,
     float* __restrict__ k_scale, uint4* __restrict__ v_pool, uint8_t* __restrict__ v_exp,
-    const int32_t* __restrict__ page_ids, int32_t T, int32_t H, int32_t P) {
+    const int32_t* __restrict__ page_ids, int32_t T, int32_t H, int32_t P, int32_t tiles,
+    int32_t ppc) {
   constexpr int UPR = D / 8;                             // 16-byte units per head row
   constexpr int UPT = kScaleTile * UPR / kQThreads;      // units per thread
   static_assert(UPT * kQThreads == kScaleTile * UPR, "tile must split evenly");
-  const int tile = blockIdx.x;
+  const int chunk = int(blockIdx.x) / tiles;
+  const int tile = int(blockIdx.x) - chunk * tiles;
   const int h = blockIdx.y;
-  const bool v8 = v_exp != nullptr;
-  const bool is_v = blockIdx.z != 0;                     // (only with 8-bit values)
+  const bool is_v = blockIdx.z != 0;
   const int spp = P / kScaleTile;
   const int pg = tile / spp;
   const int sub = tile - pg * spp;
-  const int64_t pid = page_ids[pg];
+  const int64_t pid = page_ids[int64_t(chunk) * ppc + pg];
   const int tok0 = tile * kScaleTile;
+  k_src += int64_t(chunk) * T * H * UPR;
+  v_src += int64_t(chunk) * T * H * UPR;
 
-  uint4 x[UPT], vx[UPT];
+  uint4 x[UPT];
   int64_t dst_row[UPT];
   float am = 0.f;
 #pragma unroll
@@ -108,7 +112,6 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
     const int t = tok0 + tok;
     const int64_t src = (int64_t(t) * H + h) * UPR + c;
     x[u] = t < T ? load_stream16((is_v ? v_src : k_src) + src) : make_uint4(0u, 0u, 0u, 0u);
-    vx[u] = (t < T && !v8) ? load_stream16(v_src + src) : make_uint4(0u, 0u, 0u, 0u);
     dst_row[u] = ((pid * P + sub * kScaleTile + tok) * H + h) * UPR + c;  // in 16-byte units
   }
 #pragma unroll
@@ -116,11 +119,6 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
     const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) am = fmaxf(am, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
-  }
-  // bf16 values need no scale: their copy drains while the block reduces
-  if (!v8) {
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) store_stream16(v_pool + dst_row[u], vx[u]);
   }
   // block max: within each wave, then across the four waves
 #pragma unroll
@@ -131,7 +129,7 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
 #pragma unroll
   for (int i = 0; i < kQThreads / 64; ++i) am = fmaxf(am, wave_max[i]);
 
-  if (is_v) {  // 8-bit values: power-of-two scale, transposed tile
+  if (is_v) {  // values: power-of-two scale, transposed tile
     __shared__ __attribute__((aligned(16))) uint8_t tile_t[D * kScaleTile];
     const int e = pow2_exponent(am);
     const float mul = __uint_as_float(uint32_t(127 - e) << 23);  // 2^-e (exact)
@@ -167,6 +165,173 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_kernel(
   }
 }
 
+
+// bf16 values (v_exp NULL): a persistent grid. Each block walks units (chunk,
+// tile, head) a grid-stride apart, the next unit's loads in flight while the
+// current one is reduced and written; the grid is sized so that every block
+// gets the same number of units and a CU at most two blocks (measured on a
+// 4-step tick's five live chunks in one launch: 62 -> 68 % of HBM peak
+// against one block per unit).
+template <int D>
+__global__ __launch_bounds__(kQThreads) void store_fp8_stream_kernel(
+    const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint8_t* __restrict__ k_pool,
+    float* __restrict__ k_scale, uint4* __restrict__ v_pool, const int32_t* __restrict__ page_ids,
+    int32_t T, int32_t H, int32_t P, int32_t tiles, int32_t ppc, int32_t n_units) {
+  constexpr int UPR = D / 8;                             // 16-byte units per head row
+  constexpr int UPT = kScaleTile * UPR / kQThreads;      // units per thread
+  static_assert(UPT * kQThreads == kScaleTile * UPR, "tile must split evenly");
+  const int spp = P / kScaleTile;
+  __shared__ float wave_max[2][kQThreads / 64];  // by unit parity: no write waits on a read
+  struct Buf { uint4 x[UPT], vx[UPT]; };
+  auto load = [&](Buf& b, int unit) __attribute__((always_inline)) {
+    const int h = unit % H;
+    const int ct = unit / H;
+    const int chunk = ct / tiles;
+    const int tok0 = (ct - chunk * tiles) * kScaleTile;
+    const uint4* ks = k_src + int64_t(chunk) * T * H * UPR;
+    const uint4* vs = v_src + int64_t(chunk) * T * H * UPR;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int e = threadIdx.x + u * kQThreads;
+      const int tok = e / UPR;
+      const int t = tok0 + tok;
+      const int64_t src = (int64_t(t) * H + h) * UPR + (e - tok * UPR);
+      b.x[u] = t < T ? load_stream16(ks + src) : make_uint4(0u, 0u, 0u, 0u);
+      b.vx[u] = t < T ? load_stream16(vs + src) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto process = [&](const Buf& b, int unit, int par) __attribute__((always_inline)) {
+    const int h = unit % H;
+    const int ct = unit / H;
+    const int chunk = ct / tiles;
+    const int tile = ct - chunk * tiles;
+    const int pg = tile / spp;
+    const int sub = tile - pg * spp;
+    const int64_t pid = page_ids[int64_t(chunk) * ppc + pg];
+    float am = 0.f;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const uint32_t w[4] = {b.x[u].x, b.x[u].y, b.x[u].z, b.x[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am = fmaxf(am, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+    }
+    // the value copy drains while the block reduces
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int e = threadIdx.x + u * kQThreads;
+      const int tok = e / UPR;
+      store_stream16(v_pool + ((pid * P + sub * kScaleTile + tok) * H + h) * UPR + (e - tok * UPR),
+                     b.vx[u]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    if ((threadIdx.x & 63) == 0) wave_max[par][threadIdx.x >> 6] = am;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kQThreads / 64; ++i) am = fmaxf(am, wave_max[par][i]);
+    // a tile with amax below kTinyAmax is stored as zero (scale 0, zero codes)
+    const bool big = am >= kTinyAmax;
+    const float inv = big ? kE4m3Max / am : 0.f;
+    if (threadIdx.x == 0) k_scale[(pid * spp + sub) * H + h] = big ? am / kE4m3Max : 0.f;
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int e = threadIdx.x + u * kQThreads;
+      const int tok = e / UPR;
+      const int64_t row = ((pid * P + sub * kScaleTile + tok) * H + h) * UPR + (e - tok * UPR);
+      const v2u codes = {e4m3x4(b.x[u].x, b.x[u].y, inv), e4m3x4(b.x[u].z, b.x[u].w, inv)};
+      // unit (16 bytes of bf16) -> 8 bytes of codes at half the offset
+      __builtin_nontemporal_store(codes, reinterpret_cast<v2u*>(k_pool + row * 8));
+    }
+  };
+  const int stride = gridDim.x;
+  int unit = blockIdx.x;
+  if (unit >= n_units) return;  // (the grid never exceeds the units)
+  Buf a, b;
+  load(a, unit);
+  for (;;) {  // two units per pass, so that the buffers keep their names
+    const int u1 = unit + stride;
+    if (u1 < n_units) load(b, u1);
+    process(a, unit, 0);
+    if (u1 >= n_units) break;
+    const int u2 = u1 + stride;
+    if (u2 < n_units) load(a, u2);
+    process(b, u1, 1);
+    if (u2 >= n_units) break;
+    unit = u2;
+  }
+}
+}  // namespace
+}  // namespace wf
+
+namespace wf {
+namespace {
+
+int32_t store_fp8(const char* where, const void* k_src, const void* v_src, int32_t n_chunks,
+                  void* k_pool, float* k_scale, void* v_pool, uint8_t* v_exp,
+                  const int32_t* page_ids, int32_t T, int32_t H, int32_t D, int32_t num_pages,
+                  int32_t P, hipStream_t stream) {
+  if (T < 0 || H <= 0 || num_pages <= 0 || P <= 0 || n_chunks < 0)
+    return fail(WF_EINVAL, "%s: bad sizes T=%d H=%d num_pages=%d P=%d n_chunks=%d", where, T, H,
+                num_pages, P, n_chunks);
+  if (D != 64 && D != 128)
+    return fail(WF_EUNSUPPORTED, "%s: head dim D = %d (supported: 64, 128)", where, D);
+  if (P % kScaleTile != 0)
+    return fail(WF_EINVAL, "%s: page size P = %d must be a multiple of 64", where, P);
+  if (T == 0 || n_chunks == 0) return WF_OK;
+  if (!k_src || !v_src || !k_pool || !k_scale || !v_pool || !page_ids)
+    return fail(WF_EINVAL, "%s: NULL pointer", where);
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+    return fail(WF_EINVAL, "%s: tensors must be 16-byte aligned (scales 4-byte)", where);
+  const int64_t ppc = (int64_t(T) + P - 1) / P;
+  if (ppc > num_pages)
+    return fail(WF_EINVAL, "%s: chunk needs %lld pages, pool has %d", where,
+                static_cast<long long>(ppc), num_pages);
+  if (H > 65535) return fail(WF_EUNSUPPORTED, "%s: H = %d exceeds 65535", where, H);
+  const int64_t tiles = ppc * (P / kScaleTile);
+  if (int64_t(n_chunks) * tiles > 0x7fffffff)
+    return fail(WF_EUNSUPPORTED, "%s: %d chunks of %lld tiles exceed the grid", where, n_chunks,
+                static_cast<long long>(tiles));
+  if (check_pages_enabled()) {
+    const int32_t st = check_device_pages(page_ids, int64_t(n_chunks) * ppc, num_pages, stream, where);
+    if (st != WF_OK) return st;
+  }
+  if (!v_exp) {
+    // every block the same number of units, at most two blocks per CU
+    const int64_t n_units = int64_t(n_chunks) * tiles * H;
+    if (n_units > 0x7fffffff)
+      return fail(WF_EUNSUPPORTED, "%s: %lld (tile, head) units exceed 2^31", where,
+                  static_cast<long long>(n_units));
+    const int64_t slots = 2 * int64_t(std::max(device_cu_count(), 1));
+    const int64_t per_block = (n_units + slots - 1) / slots;
+    const unsigned blocks = unsigned((n_units + per_block - 1) / per_block);
+    if (D == 128)
+      store_fp8_stream_kernel<128><<<blocks, kQThreads, 0, stream>>>(
+          static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
+          static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), page_ids, T, H, P,
+          int32_t(tiles), int32_t(ppc), int32_t(n_units));
+    else
+      store_fp8_stream_kernel<64><<<blocks, kQThreads, 0, stream>>>(
+          static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
+          static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), page_ids, T, H, P,
+          int32_t(tiles), int32_t(ppc), int32_t(n_units));
+    return check_launch(where);
+  }
+  const dim3 grid(unsigned(int64_t(n_chunks) * tiles), unsigned(H), 2);
+  if (D == 128)
+    store_fp8_v8_kernel<128><<<grid, kQThreads, 0, stream>>>(
+        static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
+        static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), v_exp, page_ids, T,
+        H, P, int32_t(tiles), int32_t(ppc));
+  else
+    store_fp8_v8_kernel<64><<<grid, kQThreads, 0, stream>>>(
+        static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
+        static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), v_exp, page_ids, T,
+        H, P, int32_t(tiles), int32_t(ppc));
+  return check_launch(where);
+}
+
 }  // namespace
 }  // namespace wf
 
@@ -174,44 +339,24 @@ extern "C" wf_status wf_store_paged_fp8(const void* k_src, const void* v_src, vo
                                         float* k_scale, void* v_pool, uint8_t* v_exp,
                                         const int32_t* page_ids, int32_t T, int32_t H, int32_t D,
                                         int32_t num_pages, int32_t P, hipStream_t stream) {
-  using namespace wf;
   try {
-    const char* where = "wf_store_paged_fp8";
-    if (T < 0 || H <= 0 || num_pages <= 0 || P <= 0)
-      return fail(WF_EINVAL, "%s: bad sizes T=%d H=%d num_pages=%d P=%d", where, T, H, num_pages,
-                  P);
-    if (D != 64 && D != 128)
-      return fail(WF_EUNSUPPORTED, "%s: head dim D = %d (supported: 64, 128)", where, D);
-    if (P % kScaleTile != 0)
-      return fail(WF_EINVAL, "%s: page size P = %d must be a multiple of 64", where, P);
-    if (T == 0) return WF_OK;
-    if (!k_src || !v_src || !k_pool || !k_scale || !v_pool || !page_ids)
-      return fail(WF_EINVAL, "%s: NULL pointer", where);
-    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_pool) || !aligned16(v_pool) ||
-        (reinterpret_cast<uintptr_t>(k_scale) & 3u))
-      return fail(WF_EINVAL, "%s: tensors must be 16-byte aligned (scales 4-byte)", where);
-    const int64_t ppc = (int64_t(T) + P - 1) / P;
-    if (ppc > num_pages)
-      return fail(WF_EINVAL, "%s: chunk needs %lld pages, pool has %d", where,
-                  static_cast<long long>(ppc), num_pages);
-    if (H > 65535) return fail(WF_EUNSUPPORTED, "%s: H = %d exceeds 65535", where, H);
-    if (check_pages_enabled()) {
-      const int32_t st = check_device_pages(page_ids, ppc, num_pages, stream, where);
-      if (st != WF_OK) return st;
-    }
-    const dim3 grid(unsigned(ppc * (P / kScaleTile)), unsigned(H), v_exp ? 2 : 1);
-    if (D == 128)
-      store_fp8_kernel<128><<<grid, kQThreads, 0, stream>>>(
-          static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
-          static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), v_exp, page_ids, T,
-          H, P);
-    else
-      store_fp8_kernel<64><<<grid, kQThreads, 0, stream>>>(
-          static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
-          static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), v_exp, page_ids, T,
-          H, P);
-    return check_launch(where);
+    return wf::store_fp8("wf_store_paged_fp8", k_src, v_src, 1, k_pool, k_scale, v_pool, v_exp,
+                         page_ids, T, H, D, num_pages, P, stream);
   } catch (...) {
-    return fail(WF_EINVAL, "wf_store_paged_fp8: internal error");
+    return wf::fail(WF_EINVAL, "wf_store_paged_fp8: internal error");
+  }
+}
+
+extern "C" wf_status wf_store_paged_fp8_chunks(const void* k_src, const void* v_src,
+                                               int32_t n_chunks, void* k_pool, float* k_scale,
+                                               void* v_pool, uint8_t* v_exp,
+                                               const int32_t* page_ids, int32_t T, int32_t H,
+                                               int32_t D, int32_t num_pages, int32_t P,
+                                               hipStream_t stream) {
+  try {
+    return wf::store_fp8("wf_store_paged_fp8_chunks", k_src, v_src, n_chunks, k_pool, k_scale,
+                         v_pool, v_exp, page_ids, T, H, D, num_pages, P, stream);
+  } catch (...) {
+    return wf::fail(WF_EINVAL, "wf_store_paged_fp8_chunks: internal error");
   }
 }

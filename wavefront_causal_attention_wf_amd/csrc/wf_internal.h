@@ -43,6 +43,19 @@ inline int32_t check_launch(const char* where) {
   return WF_OK;
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+inline int device_cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 inline bool check_pages_enabled() {
   const char* v = std::getenv("WF_CHECK_PAGES");
   return v && v[0] == '1';

@@ -84,6 +84,8 @@ _lib.wf_rope_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, 
                                      ctypes.POINTER(WfRopeDesc), _vp]
 _lib.wf_store_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _vp]
+_lib.wf_store_paged_fp8_chunks.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                            _i32, _i32, _i32, _vp]
 _lib.wf_attn_tick.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
 _lib.wf_attn_tick_noalloc.argtypes = [ctypes.POINTER(WfTickDesc), _vp]
 _lib.wf_tick_useful_flops.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POINTER(ctypes.c_double)]
@@ -93,6 +95,7 @@ _lib.wf_tick_workspace_bytes.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POIN
 for _f in ("wf_page_table_create", "wf_page_table_pages_per_chunk", "wf_page_table_alloc_chunk",
            "wf_page_table_commit", "wf_page_table_export", "wf_page_table_num_free",
            "wf_store_paged", "wf_gather_paged", "wf_rope_store_paged", "wf_store_paged_fp8",
+           "wf_store_paged_fp8_chunks",
            "wf_attn_tick", "wf_tick_useful_flops", "wf_tick_work_order",
            "wf_tick_workspace_bytes", "wf_attn_tick_noalloc"):
     getattr(_lib, _f).restype = _i32
@@ -101,7 +104,8 @@ EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
                     "wf_page_table_destroy", "wf_page_table_pages_per_chunk",
                     "wf_page_table_alloc_chunk", "wf_page_table_commit", "wf_page_table_export",
                     "wf_page_table_num_free", "wf_store_paged", "wf_gather_paged",
-                    "wf_rope_store_paged", "wf_store_paged_fp8", "wf_attn_tick",
+                    "wf_rope_store_paged", "wf_store_paged_fp8", "wf_store_paged_fp8_chunks",
+                    "wf_attn_tick",
                     "wf_tick_useful_flops", "wf_tick_work_order", "wf_tick_workspace_bytes",
                     "wf_attn_tick_noalloc")
 
@@ -304,6 +308,17 @@ def wf_store_paged_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=N
     ([num_pages][P/64][H]); V copied into v_pool (bf16 [num_pages][P][H][D]),
     or with v_exp (uint8 [num_pages][P/64][H]) quantised into v_pool (uint8
     [num_pages][P/64][H][D][64], transposed tiles)."""
+    _store_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream, v_exp, chunks=False)
+
+
+def wf_store_paged_fp8_chunks(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=None,
+                              v_exp=None) -> None:
+    """n chunks [n][T][H][D] in one launch, page_ids int32 [n][ceil(T/P)]; each
+    chunk as wf_store_paged_fp8 writes it."""
+    _store_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream, v_exp, chunks=True)
+
+
+def _store_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream, v_exp, chunks):
     for n, t in (("k_src", k_src), ("v_src", v_src)):
         _check_bf16(n, t)
     _check_typed("k_pool", k_pool, "uint8")
@@ -313,9 +328,11 @@ def wf_store_paged_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=N
     else:
         _check_typed("v_pool", v_pool, "uint8")
         _check_typed("v_exp", v_exp, "uint8")
-    if k_src.dim() != 3 or k_pool.dim() != 4:
-        raise ValueError("k_src must be [T][H][D] and k_pool [num_pages][P][H][D]")
-    T, H, D = k_src.shape
+    if k_src.dim() != (4 if chunks else 3) or k_pool.dim() != 4:
+        raise ValueError(f"k_src must be {'[n][T][H][D]' if chunks else '[T][H][D]'} and k_pool "
+                         "[num_pages][P][H][D]")
+    n_chunks = k_src.shape[0] if chunks else 1
+    T, H, D = k_src.shape[-3:]
     num_pages, P = k_pool.shape[0], k_pool.shape[1]
     _check_shape("v_src", v_src, k_src.shape)
     _check_shape("k_pool", k_pool, (num_pages, P, H, D))
@@ -325,12 +342,19 @@ def wf_store_paged_fp8(k_src, v_src, k_pool, k_scale, v_pool, page_ids, stream=N
     else:
         _check_shape("v_pool", v_pool, (num_pages, P // 64, H, D, 64))
         _check_shape("v_exp", v_exp, (num_pages, P // 64, H))
-    _check_ids("page_ids", page_ids, (_pages_per_chunk(T, P),))
+    ppc = _pages_per_chunk(T, P)
+    _check_ids("page_ids", page_ids, (n_chunks, ppc) if chunks else (ppc,))
     _check_on_gpu(k_src=k_src, v_src=v_src, k_pool=k_pool, k_scale=k_scale, v_pool=v_pool,
                   v_exp=v_exp, page_ids=page_ids)
-    _check(_lib.wf_store_paged_fp8(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(k_scale),
-                                   _ptr(v_pool), _ptr(v_exp), _ptr(page_ids), T, H, D, num_pages,
-                                   P, _stream(stream)), "wf_store_paged_fp8")
+    if chunks:
+        _check(_lib.wf_store_paged_fp8_chunks(_ptr(k_src), _ptr(v_src), n_chunks, _ptr(k_pool),
+                                              _ptr(k_scale), _ptr(v_pool), _ptr(v_exp),
+                                              _ptr(page_ids), T, H, D, num_pages, P,
+                                              _stream(stream)), "wf_store_paged_fp8_chunks")
+    else:
+        _check(_lib.wf_store_paged_fp8(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(k_scale),
+                                       _ptr(v_pool), _ptr(v_exp), _ptr(page_ids), T, H, D,
+                                       num_pages, P, _stream(stream)), "wf_store_paged_fp8")
 
 
 def default_rope_split(D: int):
