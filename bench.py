@@ -313,35 +313,47 @@ def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> d
 
 def rope_store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> dict:
     """wf_rope_store_paged alone (graph_time_ms), inputs rotated over
-    `rotation` chunks and page sets like the store measurement: reads K and V of
-    one chunk, rotates K, writes the chunk's whole pages of K and V."""
+    `rotation` ticks and page sets like the store measurement: reads K and V of
+    one chunk, rotates K, writes the chunk's whole pages of K and V; and
+    wf_rope_store_paged_chunks of a tick's S+1 live chunks in one launch (the
+    fully paged tick's producer write)."""
     import torch
 
     from wavefront_causal_attention_wf_amd import inputs, wfattn
 
-    T, H, D, P = cfg.T, cfg.H, cfg.D, cfg.P
+    S, T, H, D, P = cfg.S, cfg.T, cfg.H, cfg.D, cfg.P
+    n = S + 1
     ppc = cfg.ppc
     grid = inputs.chunk_grid(T)
-    pool_pages = max(cfg.num_pages, rotation * ppc)
+    pool_pages = max(cfg.num_pages, rotation * n * ppc)
     kp = torch.zeros((pool_pages, P, H, D), dtype=torch.bfloat16, device=dev)
     vp = torch.zeros_like(kp)
-    srcs = [inputs.draw_live_torch(cfg, 3100 + i, dev, T=T)[0] for i in range(rotation)]
-    ksrc = [x[0].clone() for x in srcs]
-    vsrc = [x[1].clone() for x in srcs]
-    del srcs
-    ids = [torch.arange(i * ppc, (i + 1) * ppc, dtype=torch.int32, device=dev)
+    srcs = [inputs.draw_live_torch(cfg, 3100 + i, dev, T=T)[1:3] for i in range(rotation)]
+    ids = [torch.arange(i * n * ppc, (i + 1) * n * ppc, dtype=torch.int32, device=dev).view(n, ppc)
            for i in range(rotation)]
 
     def launch(i):
-        wfattn.wf_rope_store_paged(ksrc[i % rotation], vsrc[i % rotation], kp, vp,
-                                   ids[i % rotation], grid, 3 * (100 + i))
+        k, v = srcs[i % rotation]
+        wfattn.wf_rope_store_paged(k[0], v[0], kp, vp, ids[i % rotation][0], grid, 3 * (100 + i))
 
-    ms = graph_time_ms(launch, rotation, launches)
+    def tick(i):
+        k, v = srcs[i % rotation]
+        wfattn.wf_rope_store_paged_chunks(k, v, kp, vp, ids[i % rotation], grid,
+                                          grid[0] * (100 + i + S), -grid[0])
+
+    def rate(ms, nbytes):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"us_mean": round(ms * 1e3, 2), "bytes": nbytes, "gb_per_s": round(gbs, 1),
+                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
     nbytes = 2 * (T * H * D * 2) + 2 * (ppc * P * H * D * 2)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"kernel": "wf_rope_store_paged", "us_mean": round(ms * 1e3, 2), "bytes": nbytes,
-            "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "rotation": rotation, "grid": list(grid)}
+    out = {"kernel": "wf_rope_store_paged", **rate(graph_time_ms(launch, rotation, launches), nbytes),
+           "rotation": rotation, "grid": list(grid)}
+    out["tick_chunks"] = {"kernel": f"wf_rope_store_paged_chunks ({n} chunks, one launch)",
+                          **rate(graph_time_ms(tick, rotation, launches // 4), n * nbytes)}
+    del srcs, kp, vp
+    torch.cuda.empty_cache()
+    return out
 
 
 class FullyPagedRollout:
@@ -403,9 +415,9 @@ class FullyPagedRollout:
         self.ids_host[slot].numpy()[:] = self.pt.alloc_chunk()
         self.live_dev[S].copy_(self.ids_host[slot], non_blocking=True)
         c_store = self.chunk
-        for j in range(S + 1):     # slot j holds video chunk c_store + S - j
-            wf.wf_rope_store_paged(k[j], v[j], self.k_pool, self.v_pool, self.live_dev[j],
-                                   self.grid, F * (c_store + S - j))
+        # slot j holds video chunk c_store + S - j: every live chunk in one launch
+        wf.wf_rope_store_paged_chunks(k, v, self.k_pool, self.v_pool, self.live_dev, self.grid,
+                                      F * (c_store + S), -F)
         self.hist_host[slot].numpy()[:] = self.pt.export()
         self.hist_dev.copy_(self.hist_host[slot], non_blocking=True)
         ev = torch.cuda.Event()
@@ -443,7 +455,8 @@ def fully_paged(cfg, dev, steps: int = 10, warmup: int = 3) -> dict:
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
     attn = float(np.mean([x.elapsed_time(y) for x, y in ev]))
-    return {"flow": f"{cfg.S + 1} x wf_rope_store_paged (every live chunk) + wf_attn_tick with "
+    return {"flow": f"wf_rope_store_paged_chunks ({cfg.S + 1} live chunks, one launch) + "
+                    "wf_attn_tick with "
                     "live_pages (whole context through pages) + commit",
             "ms_per_tick": round(ms, 4), "ticks_per_s": round(1e3 / ms, 2),
             "useful_tflop_per_s": round(flops / (ms * 1e-3) / 1e12, 2),

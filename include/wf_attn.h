@@ -160,6 +160,20 @@ wf_status wf_rope_store_paged(const void* k_src, const void* v_src, void* k_pool
                               int32_t num_pages, int32_t P, const wf_rope_desc* rope,
                               hipStream_t stream);
 
+/* wf_rope_store_paged_chunks — n_chunks producer writes in one launch (a tick's
+ * live chunks), chunk c exactly as wf_rope_store_paged writes it with its
+ * first frame at rope->frame0 + c * frame_step: k_src (and v_src, or both
+ * NULL with v_pool) device bf16 [n_chunks][T][H][D], page_ids device int32
+ * [n_chunks][ceil(T/P)], the chunks' pages distinct. In the wave, slot j holds
+ * video chunk c_store + S - j, so slots 0..S in order have frame_step = -F
+ * ([summary] Methodology 1). Errors as wf_rope_store_paged, each chunk's first
+ * frame checked; WF_EINVAL for n_chunks < 0; n_chunks = 0 is a no-op. */
+wf_status wf_rope_store_paged_chunks(const void* k_src, const void* v_src, int32_t n_chunks,
+                                     void* k_pool, void* v_pool, const int32_t* page_ids,
+                                     int32_t T, int32_t H, int32_t D, int32_t num_pages,
+                                     int32_t P, const wf_rope_desc* rope, int32_t frame_step,
+                                     hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* wf_store_paged_fp8 — a producer's write of one chunk into the pages of the */
 /* 8-bit tier: K as e4m3 codes with fp32 scales, V copied as bf16.            */

@@ -119,3 +119,37 @@ def test_rope_k_only_rewrite_keeps_v():
     torch.cuda.synchronize()
     assert np.array_equal(_bits(vp), v_before)
     check_k_pages(_bits(kp), ids, k, grid, new_f0, oracle.default_split(D))
+
+
+@pytest.mark.parametrize("n,T,grid,H,D,P,frame0,step", [
+    (3, 100, (4, 5, 5), 2, 128, 48, 40, -4),      # ragged pages, frames descending
+    (2, 64, (1, 8, 8), 3, 64, 16, 0, 1),          # heads not a multiple of four
+    (5, 4680, (3, 30, 52), 12, 128, 64, 12, -3),  # a 4-step tick's live chunks
+])
+def test_rope_store_chunks_equals_one_call_per_chunk(n, T, grid, H, D, P, frame0, step):
+    """wf_rope_store_paged_chunks (n chunks, one launch, chunk c at first frame
+    frame0 + c * step) leaves every pool byte as n wf_rope_store_paged calls
+    do, so its pages are the oracle's as well; the first chunk's keys are also
+    checked against the oracle directly."""
+    say(f"rope store chunks n={n} T={T} grid={grid} H={H} D={D} P={P} frame0={frame0} step={step}")
+    rng = np.random.default_rng(T + n)
+    ppc = -(-T // P)
+    num_pages = n * ppc + 5
+    k_bits = _draw(rng, (n, T, H, D))
+    v_bits = _draw(rng, (n, T, H, D))
+    k = inputs.to_device_bf16(k_bits, DEV)
+    v = inputs.to_device_bf16(v_bits, DEV)
+    ids = rng.permutation(num_pages)[:n * ppc].astype(np.int32).reshape(n, ppc)
+    ids_dev = torch.from_numpy(ids).to(DEV)
+    pools = [torch.full((num_pages, P, H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+             for _ in range(4)]
+    wfattn.wf_rope_store_paged_chunks(k, v, pools[0], pools[1], ids_dev, grid, frame0, step)
+    for c in range(n):
+        wfattn.wf_rope_store_paged(k[c], v[c], pools[2], pools[3], ids_dev[c], grid,
+                                   frame0 + c * step)
+    torch.cuda.synchronize()
+    assert torch.equal(pools[0].view(torch.int16), pools[2].view(torch.int16)), "K pages"
+    assert torch.equal(pools[1].view(torch.int16), pools[3].view(torch.int16)), "V pages"
+    split = wfattn.default_rope_split(D)
+    same = check_k_pages(_bits(pools[0]), ids[0], k_bits[0], grid, frame0, tuple(split))
+    say(f"  equal to per-chunk calls; chunk 0 keys correctly rounded: {same:.4f}")

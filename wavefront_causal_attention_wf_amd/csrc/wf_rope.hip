@@ -48,7 +48,10 @@ struct RopeParams {
   int32_t T, H, P;
   int32_t tokens;         // ceil(T / P) * P: every slot of the chunk's pages
   int32_t rows, cols;     // R and C of the latent grid
-  int32_t frame0;
+  int32_t frame0;         // first frame of chunk 0
+  int32_t frame_step;     // chunk c starts at frame0 + c * frame_step
+  int32_t tblocks;        // token blocks per chunk
+  int32_t ppc;            // pages per chunk
   float inv_freq[kMaxPairs];  // per channel pair
   int32_t axis[kMaxPairs];    // 0 frame, 1 row, 2 column
 };
@@ -70,22 +73,23 @@ __device__ __forceinline__ uint32_t rotate_word(uint32_t w, float c, float s) {
   return pack_bf16(x0 * c - x1 * s, x0 * s + x1 * c);
 }
 
-// blockIdx.z == 0: K (rotated), 1: V (copied); blockIdx.y: heads
-// [kRopeHeads * y, kRopeHeads * y + kRopeHeads). Tokens [T, ppc*P) of the last
-// page are written as zero.
+// blockIdx.x: chunk c = x / tblocks, token block x % tblocks; blockIdx.z == 0:
+// K (rotated), 1: V (copied); blockIdx.y: heads [kRopeHeads * y, kRopeHeads *
+// y + kRopeHeads). Tokens [T, ppc*P) of the last page are written as zero.
 template <int D>
 __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(const RopeParams p) {
   constexpr int U = D / 8;                 // 16-byte units per (token, head) row
   constexpr int TPB = kRopeThreads / U;    // tokens per block
   const int u = threadIdx.x % U;
-  const int t = blockIdx.x * TPB + threadIdx.x / U;
+  const int chunk = int(blockIdx.x) / p.tblocks;
+  const int t = (int(blockIdx.x) - chunk * p.tblocks) * TPB + threadIdx.x / U;
   if (t >= p.tokens) return;  // past the last page
   const int H = p.H;
   const int h0 = blockIdx.y * kRopeHeads;
   const int nh = H - h0 < kRopeHeads ? H - h0 : kRopeHeads;
   const int32_t page = t / p.P;
   const int32_t slot = t - page * p.P;
-  const int64_t pid = p.page_ids[page];
+  const int64_t pid = p.page_ids[int64_t(chunk) * p.ppc + page];
   const bool is_v = blockIdx.z != 0;
   uint4* dst = (is_v ? p.v_pool : p.k_pool) + ((pid * p.P + slot) * H + h0) * U + u;
   uint4 x[kRopeHeads] = {};  // (heads past H stay zero: rotated, never stored)
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(const RopePara
       if (i < nh) store_stream16(dst + int64_t(i) * U, make_uint4(0u, 0u, 0u, 0u));
     return;
   }
-  const uint4* src = (is_v ? p.v_src : p.k_src) + (int64_t(t) * H + h0) * U + u;
+  const uint4* src = (is_v ? p.v_src : p.k_src) + ((int64_t(chunk) * p.T + t) * H + h0) * U + u;
 #pragma unroll
   for (int i = 0; i < kRopeHeads; ++i)  // every load in flight before any store
     if (i < nh) x[i] = load_stream16(src + int64_t(i) * U);
@@ -105,7 +109,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(const RopePara
     const int f = t / rc;
     const int rem = t - f * rc;
     const int row = rem / p.cols;
-    const float cf = float(p.frame0 + f), cr = float(row), cc = float(rem - row * p.cols);
+    const float cf = float(p.frame0 + chunk * p.frame_step + f), cr = float(row),
+                cc = float(rem - row * p.cols);
     float cs[4], sn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -127,75 +132,110 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(const RopePara
 }  // namespace
 }  // namespace wf
 
+namespace wf {
+namespace {
+
+int32_t rope_store(const char* where, const void* k_src, const void* v_src, int32_t n_chunks,
+                   void* k_pool, void* v_pool, const int32_t* page_ids, int32_t T, int32_t H,
+                   int32_t D, int32_t num_pages, int32_t P, const wf_rope_desc* rope,
+                   int32_t frame_step, hipStream_t stream) {
+  if (!rope) return fail(WF_EINVAL, "%s: NULL rope descriptor", where);
+  if (T < 0 || H <= 0 || num_pages <= 0 || P <= 0 || n_chunks < 0)
+    return fail(WF_EINVAL, "%s: bad sizes T=%d H=%d num_pages=%d P=%d n_chunks=%d", where, T, H,
+                num_pages, P, n_chunks);
+  if (D != 64 && D != 128) return fail(WF_EUNSUPPORTED, "%s: D=%d (64 or 128)", where, D);
+  if (T == 0 || n_chunks == 0) return WF_OK;
+  const int64_t cells = int64_t(rope->grid[0]) * rope->grid[1] * rope->grid[2];
+  if (rope->grid[0] <= 0 || rope->grid[1] <= 0 || rope->grid[2] <= 0 || cells != T)
+    return fail(WF_EINVAL, "%s: grid %d x %d x %d does not hold T=%d tokens", where,
+                rope->grid[0], rope->grid[1], rope->grid[2], T);
+  for (int64_t c : {int64_t(0), int64_t(n_chunks) - 1}) {  // first frames are monotone in c
+    const int64_t f0 = int64_t(rope->frame0) + c * frame_step;
+    if (f0 < 0 || f0 + rope->grid[0] > (int64_t(1) << 24))
+      return fail(WF_EINVAL, "%s: chunk %lld starts at frame %lld, outside [0, 2^24 - frames]",
+                  where, static_cast<long long>(c), static_cast<long long>(f0));
+  }
+  for (int a = 0; a < 3; ++a)
+    if (rope->split[a] < 0 || rope->split[a] % 2)
+      return fail(WF_EINVAL, "%s: split[%d]=%d must be even and >= 0", where, a, rope->split[a]);
+  if (int64_t(rope->split[0]) + rope->split[1] + rope->split[2] != D)
+    return fail(WF_EINVAL, "%s: split %d+%d+%d != D=%d", where, rope->split[0], rope->split[1],
+                rope->split[2], D);
+  if (!(rope->theta > 0.0f) || !std::isfinite(rope->theta))
+    return fail(WF_EINVAL, "%s: theta must be positive and finite", where);
+  if (!k_src || !k_pool || !page_ids) return fail(WF_EINVAL, "%s: NULL pointer", where);
+  if ((v_src == nullptr) != (v_pool == nullptr))
+    return fail(WF_EINVAL, "%s: v_src and v_pool must both be given or both be NULL", where);
+  if (!aligned16(k_src) || !aligned16(k_pool) || (v_src && (!aligned16(v_src) || !aligned16(v_pool))))
+    return fail(WF_EINVAL, "%s: tensors must be 16-byte aligned", where);
+  const int64_t ppc = (int64_t(T) + P - 1) / P;
+  if (ppc > num_pages)
+    return fail(WF_EINVAL, "%s: chunk needs %lld pages, pool has %d", where,
+                static_cast<long long>(ppc), num_pages);
+  if (ppc * P >= (int64_t(1) << 31))
+    return fail(WF_EUNSUPPORTED, "%s: ceil(T/P)*P must stay below 2^31", where);
+  const int tpb = kRopeThreads / (D / 8);
+  const int64_t tblocks = (ppc * P + tpb - 1) / tpb;
+  if (int64_t(n_chunks) * tblocks > 0x7fffffff)
+    return fail(WF_EUNSUPPORTED, "%s: %d chunks exceed the grid", where, n_chunks);
+  if (check_pages_enabled()) {
+    int32_t st = check_device_pages(page_ids, int64_t(n_chunks) * ppc, num_pages, stream, where);
+    if (st != WF_OK) return st;
+  }
+  RopeParams p{};
+  p.k_src = static_cast<const uint4*>(k_src);
+  p.v_src = static_cast<const uint4*>(v_src);
+  p.k_pool = static_cast<uint4*>(k_pool);
+  p.v_pool = static_cast<uint4*>(v_pool);
+  p.page_ids = page_ids;
+  p.T = T;
+  p.H = H;
+  p.P = P;
+  p.rows = rope->grid[1];
+  p.cols = rope->grid[2];
+  p.frame0 = rope->frame0;
+  p.frame_step = frame_step;
+  p.tblocks = int32_t(tblocks);
+  p.ppc = int32_t(ppc);
+  p.tokens = int32_t(ppc * P);
+  int pr = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int i = 0; i < rope->split[a] / 2; ++i, ++pr) {
+      p.axis[pr] = a;
+      p.inv_freq[pr] = float(std::pow(double(rope->theta), -2.0 * i / rope->split[a]));
+    }
+  dim3 grid(unsigned(int64_t(n_chunks) * tblocks), unsigned((H + kRopeHeads - 1) / kRopeHeads),
+            v_src ? 2 : 1);
+  if (D == 128) rope_store_kernel<128><<<grid, kRopeThreads, 0, stream>>>(p);
+  else rope_store_kernel<64><<<grid, kRopeThreads, 0, stream>>>(p);
+  return check_launch(where);
+}
+
+}  // namespace
+}  // namespace wf
+
 extern "C" wf_status wf_rope_store_paged(const void* k_src, const void* v_src, void* k_pool,
                                          void* v_pool, const int32_t* page_ids, int32_t T,
                                          int32_t H, int32_t D, int32_t num_pages, int32_t P,
                                          const wf_rope_desc* rope, hipStream_t stream) {
-  using namespace wf;
   try {
-    const char* where = "wf_rope_store_paged";
-    if (!rope) return fail(WF_EINVAL, "%s: NULL rope descriptor", where);
-    if (T < 0 || H <= 0 || num_pages <= 0 || P <= 0)
-      return fail(WF_EINVAL, "%s: bad sizes T=%d H=%d num_pages=%d P=%d", where, T, H, num_pages,
-                  P);
-    if (D != 64 && D != 128) return fail(WF_EUNSUPPORTED, "%s: D=%d (64 or 128)", where, D);
-    if (T == 0) return WF_OK;
-    const int64_t cells = int64_t(rope->grid[0]) * rope->grid[1] * rope->grid[2];
-    if (rope->grid[0] <= 0 || rope->grid[1] <= 0 || rope->grid[2] <= 0 || cells != T)
-      return fail(WF_EINVAL, "%s: grid %d x %d x %d does not hold T=%d tokens", where,
-                  rope->grid[0], rope->grid[1], rope->grid[2], T);
-    if (rope->frame0 < 0 || int64_t(rope->frame0) + rope->grid[0] > (int64_t(1) << 24))
-      return fail(WF_EINVAL, "%s: frame0=%d outside [0, 2^24 - frames]", where, rope->frame0);
-    for (int a = 0; a < 3; ++a)
-      if (rope->split[a] < 0 || rope->split[a] % 2)
-        return fail(WF_EINVAL, "%s: split[%d]=%d must be even and >= 0", where, a,
-                    rope->split[a]);
-    if (int64_t(rope->split[0]) + rope->split[1] + rope->split[2] != D)
-      return fail(WF_EINVAL, "%s: split %d+%d+%d != D=%d", where, rope->split[0], rope->split[1],
-                  rope->split[2], D);
-    if (!(rope->theta > 0.0f) || !std::isfinite(rope->theta))
-      return fail(WF_EINVAL, "%s: theta must be positive and finite", where);
-    if (!k_src || !k_pool || !page_ids) return fail(WF_EINVAL, "%s: NULL pointer", where);
-    if ((v_src == nullptr) != (v_pool == nullptr))
-      return fail(WF_EINVAL, "%s: v_src and v_pool must both be given or both be NULL", where);
-    if (!aligned16(k_src) || !aligned16(k_pool) || (v_src && (!aligned16(v_src) || !aligned16(v_pool))))
-      return fail(WF_EINVAL, "%s: tensors must be 16-byte aligned", where);
-    const int64_t ppc = (int64_t(T) + P - 1) / P;
-    if (ppc > num_pages)
-      return fail(WF_EINVAL, "%s: chunk needs %lld pages, pool has %d", where,
-                  static_cast<long long>(ppc), num_pages);
-    if (ppc * P >= (int64_t(1) << 31))
-      return fail(WF_EUNSUPPORTED, "%s: ceil(T/P)*P must stay below 2^31", where);
-    if (check_pages_enabled()) {
-      int32_t st = check_device_pages(page_ids, ppc, num_pages, stream, where);
-      if (st != WF_OK) return st;
-    }
-    RopeParams p{};
-    p.k_src = static_cast<const uint4*>(k_src);
-    p.v_src = static_cast<const uint4*>(v_src);
-    p.k_pool = static_cast<uint4*>(k_pool);
-    p.v_pool = static_cast<uint4*>(v_pool);
-    p.page_ids = page_ids;
-    p.T = T;
-    p.H = H;
-    p.P = P;
-    p.rows = rope->grid[1];
-    p.cols = rope->grid[2];
-    p.frame0 = rope->frame0;
-    p.tokens = int32_t(ppc * P);
-    int pr = 0;
-    for (int a = 0; a < 3; ++a)
-      for (int i = 0; i < rope->split[a] / 2; ++i, ++pr) {
-        p.axis[pr] = a;
-        p.inv_freq[pr] = float(std::pow(double(rope->theta), -2.0 * i / rope->split[a]));
-      }
-    const int tpb = kRopeThreads / (D / 8);
-    dim3 grid(unsigned((p.tokens + tpb - 1) / tpb), unsigned((H + kRopeHeads - 1) / kRopeHeads),
-              v_src ? 2 : 1);
-    if (D == 128) rope_store_kernel<128><<<grid, kRopeThreads, 0, stream>>>(p);
-    else rope_store_kernel<64><<<grid, kRopeThreads, 0, stream>>>(p);
-    return check_launch(where);
+    return wf::rope_store("wf_rope_store_paged", k_src, v_src, 1, k_pool, v_pool, page_ids, T, H,
+                          D, num_pages, P, rope, 0, stream);
   } catch (...) {
-    return fail(WF_EINVAL, "wf_rope_store_paged: internal error");
+    return wf::fail(WF_EINVAL, "wf_rope_store_paged: internal error");
+  }
+}
+
+extern "C" wf_status wf_rope_store_paged_chunks(const void* k_src, const void* v_src,
+                                                int32_t n_chunks, void* k_pool, void* v_pool,
+                                                const int32_t* page_ids, int32_t T, int32_t H,
+                                                int32_t D, int32_t num_pages, int32_t P,
+                                                const wf_rope_desc* rope, int32_t frame_step,
+                                                hipStream_t stream) {
+  try {
+    return wf::rope_store("wf_rope_store_paged_chunks", k_src, v_src, n_chunks, k_pool, v_pool,
+                          page_ids, T, H, D, num_pages, P, rope, frame_step, stream);
+  } catch (...) {
+    return wf::fail(WF_EINVAL, "wf_rope_store_paged_chunks: internal error");
   }
 }

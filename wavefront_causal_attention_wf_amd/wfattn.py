@@ -82,6 +82,8 @@ _lib.wf_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
 _lib.wf_gather_paged.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]
 _lib.wf_rope_store_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      ctypes.POINTER(WfRopeDesc), _vp]
+_lib.wf_rope_store_paged_chunks.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                            _i32, ctypes.POINTER(WfRopeDesc), _i32, _vp]
 _lib.wf_store_paged_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _vp]
 _lib.wf_store_paged_fp8_chunks.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
@@ -95,7 +97,7 @@ _lib.wf_tick_workspace_bytes.argtypes = [ctypes.POINTER(WfTickDesc), ctypes.POIN
 for _f in ("wf_page_table_create", "wf_page_table_pages_per_chunk", "wf_page_table_alloc_chunk",
            "wf_page_table_commit", "wf_page_table_export", "wf_page_table_num_free",
            "wf_store_paged", "wf_gather_paged", "wf_rope_store_paged", "wf_store_paged_fp8",
-           "wf_store_paged_fp8_chunks",
+           "wf_store_paged_fp8_chunks", "wf_rope_store_paged_chunks",
            "wf_attn_tick", "wf_tick_useful_flops", "wf_tick_work_order",
            "wf_tick_workspace_bytes", "wf_attn_tick_noalloc"):
     getattr(_lib, _f).restype = _i32
@@ -104,8 +106,8 @@ EXPORTED_SYMBOLS = ("wf_last_error", "wf_abi_version", "wf_page_table_create",
                     "wf_page_table_destroy", "wf_page_table_pages_per_chunk",
                     "wf_page_table_alloc_chunk", "wf_page_table_commit", "wf_page_table_export",
                     "wf_page_table_num_free", "wf_store_paged", "wf_gather_paged",
-                    "wf_rope_store_paged", "wf_store_paged_fp8", "wf_store_paged_fp8_chunks",
-                    "wf_attn_tick",
+                    "wf_rope_store_paged", "wf_rope_store_paged_chunks", "wf_store_paged_fp8",
+                    "wf_store_paged_fp8_chunks", "wf_attn_tick",
                     "wf_tick_useful_flops", "wf_tick_work_order", "wf_tick_workspace_bytes",
                     "wf_attn_tick_noalloc")
 
@@ -403,6 +405,37 @@ def wf_rope_store_paged(k_src, v_src, k_pool, v_pool, page_ids, grid: Sequence[i
     _check(_lib.wf_rope_store_paged(_ptr(k_src), _ptr(v_src), _ptr(k_pool), _ptr(v_pool),
                                     _ptr(page_ids), T, H, D, num_pages, P, ctypes.byref(r),
                                     _stream(stream)), "wf_rope_store_paged")
+
+
+def wf_rope_store_paged_chunks(k_src, v_src, k_pool, v_pool, page_ids, grid: Sequence[int],
+                               frame0: int, frame_step: int,
+                               split: Optional[Sequence[int]] = None, theta: float = 10000.0,
+                               stream=None) -> None:
+    """n chunks [n][T][H][D] in one launch, page_ids int32 [n][ceil(T/P)];
+    chunk c as wf_rope_store_paged writes it at first frame frame0 + c *
+    frame_step."""
+    _check_bf16("k_src", k_src)
+    _check_bf16("k_pool", k_pool)
+    if (v_src is None) != (v_pool is None):
+        raise ValueError("v_src and v_pool are given together (or both None: K only)")
+    if v_src is not None:
+        _check_bf16("v_src", v_src)
+        _check_bf16("v_pool", v_pool)
+    if k_src.dim() != 4 or k_pool.dim() != 4:
+        raise ValueError("k_src must be [n][T][H][D] and k_pool [num_pages][P][H][D]")
+    n, T, H, D = k_src.shape
+    num_pages, P = k_pool.shape[0], k_pool.shape[1]
+    _check_shape("k_pool", k_pool, (num_pages, P, H, D))
+    if v_src is not None:
+        _check_shape("v_src", v_src, k_src.shape)
+        _check_shape("v_pool", v_pool, k_pool.shape)
+    _check_ids("page_ids", page_ids, (n, _pages_per_chunk(T, P)))
+    _check_on_gpu(k_src=k_src, v_src=v_src, k_pool=k_pool, v_pool=v_pool, page_ids=page_ids)
+    r = make_rope_desc(grid, frame0, split, theta, D)
+    _check(_lib.wf_rope_store_paged_chunks(_ptr(k_src), _ptr(v_src), n, _ptr(k_pool),
+                                           _ptr(v_pool), _ptr(page_ids), T, H, D, num_pages, P,
+                                           ctypes.byref(r), int(frame_step), _stream(stream)),
+           "wf_rope_store_paged_chunks")
 
 
 def make_tick_desc(S: int, active_mask: int, T: int, H: int, D: int, scale: float,
