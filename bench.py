@@ -609,10 +609,11 @@ def store_fp8_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) 
     chunk = 2 * (T * H * D * 2) + ppc * P * H * D * 3 + ppc * (P // 64) * H * 4
     # 8-bit values: codes for V too, one exponent byte per (tile, head)
     chunk8 = 2 * (T * H * D * 2) + ppc * P * H * D * 2 + ppc * (P // 64) * H * 5
-    out = {"kernel": "wf_store_paged_fp8", **rate(graph_time_ms(one, rotation, launches), chunk),
-           "rotation": rotation}
-    out["tick_chunks"] = {"kernel": f"wf_store_paged_fp8_chunks ({n} chunks, one launch)",
-                          **rate(graph_time_ms(tick, rotation, launches // 4), n * chunk)}
+    # headline: the tick's producer write (its live chunks, one launch)
+    out = {"kernel": f"wf_store_paged_fp8_chunks ({n} live chunks of a tick, one launch)",
+           **rate(graph_time_ms(tick, rotation, launches // 4), n * chunk), "rotation": rotation}
+    out["one_chunk"] = {"kernel": "wf_store_paged_fp8 (one chunk per launch)",
+                        **rate(graph_time_ms(one, rotation, launches), chunk)}
     out["tick_chunks_v8"] = {"kernel": f"wf_store_paged_fp8_chunks with v_exp ({n} chunks)",
                              **rate(graph_time_ms(tick_v8, rotation, launches // 4), n * chunk8)}
     del srcs, k_pool, k_scale, v_pool, v8_pool, v_exp
