@@ -80,12 +80,15 @@ def test_tail_items_parity(S, T, H, P, n_hist, mask):
     say(f"  worst rel-L2 {worst:.2e}")
 
 
-@pytest.mark.parametrize("S,T,H,P,n_hist,mask", [
-    (4, 1100, 4, 64, 3, 0b11111),   # 8-chunk walks, 76-row last tiles (tail items too)
-    (4, 1024, 3, 128, 2, 0b01111),  # whole tiles only, no store: 6-chunk walks
-    (2, 600, 2, 64, 1, 0b111),      # 4-chunk walks
+@pytest.mark.parametrize("S,T,H,D,P,n_hist,mask,hist_first", [
+    (4, 1100, 4, 128, 64, 3, 0b11111, None),   # 8-chunk walks, 76-row last tiles (tail items too)
+    (4, 1024, 3, 128, 128, 2, 0b01111, None),  # whole tiles only, no store: 6-chunk walks
+    (2, 600, 2, 128, 64, 1, 0b111, None),      # 4-chunk walks
+    (4, 1100, 4, 64, 64, 3, 0b11111, None),    # D = 64
+    (4, 1024, 3, 128, 64, 3, 0b11100, None),   # drain tick: slots 2, 3 and the store
+    (4, 1024, 3, 128, 64, 3, 0b11111, [0, 1, 1, 2, 3]),  # per-slot history budgets
 ])
-def test_run_time_pool_parity(S, T, H, P, n_hist, mask):
+def test_run_time_pool_parity(S, T, H, D, P, n_hist, mask, hist_first):
     """With a workspace, query tiles of the heaviest slot are computed chunk by
     chunk by whichever CUs are free, each chunk's partial softmax state
     (unnormalised O, row max, row sum) left in the workspace, and merged by
@@ -96,9 +99,10 @@ def test_run_time_pool_parity(S, T, H, P, n_hist, mask):
     launch on the same workspace (its counters cleared by the library) bit for
     bit equal to the first: the merge sums the chunks in walk order whichever
     CU does it."""
-    say(f"run-time pool: S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b}")
-    t = setup_tick(S, T, H, 128, P, n_hist, (n_hist + 2) * -(-T // P) + 8, seed=T + 7,
-                   active_mask=mask)
+    say(f"run-time pool: S={S} T={T} H={H} D={D} P={P} n_hist={n_hist} mask={mask:b} "
+        f"hist_first={hist_first}")
+    t = setup_tick(S, T, H, D, P, n_hist, (n_hist + 2) * -(-T // P) + 8, seed=T + 7 + D,
+                   active_mask=mask, hist_first=hist_first)
     ws = workspace_for(t)
     assert ws is not None
     d = wfattn.make_tick_desc(t.S, t.active_mask, t.T, t.H, t.D, t.scale, t.q, t.k, t.v, t.o,
