@@ -87,6 +87,7 @@ def test_tail_items_parity(S, T, H, P, n_hist, mask):
     (4, 1100, 4, 64, 64, 3, 0b11111, None),    # D = 64
     (4, 1024, 3, 128, 64, 3, 0b11100, None),   # drain tick: slots 2, 3 and the store
     (4, 1024, 3, 128, 64, 3, 0b11111, [0, 1, 1, 2, 3]),  # per-slot history budgets
+    (4, 1460, 3, 128, 64, 2, 0b11111, None),   # 180-row last tiles in the pool (no tail items)
 ])
 def test_run_time_pool_parity(S, T, H, D, P, n_hist, mask, hist_first):
     """With a workspace, query tiles of the heaviest slot are computed chunk by

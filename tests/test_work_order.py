@@ -242,3 +242,15 @@ def test_no_pool_where_it_does_not_apply(kw):
         d.k_scale = FAKE
         d.live_pages = FAKE
     assert wf.tick_workspace_bytes(d) == 0
+
+
+def test_pool_takes_ragged_last_tiles_without_tail_items():
+    """Last query tiles of more than half a workgroup (180 rows at T = 1460)
+    are not tail items; the pool then starts with them (rows past T are never
+    a piece's output)."""
+    d = with_workspace(desc(4, 0b11111, 1460, 3, 2))
+    pool = wf.tick_work_order(d, 32)
+    pool = pool[pool[:, 0] == -1]
+    assert len(pool) >= 3
+    assert np.all(pool[:3, 4] == 1280) and np.all(pool[:3, 5] == 180)
+    assert sorted(pool[:3, 3].tolist()) == [0, 1, 2]
