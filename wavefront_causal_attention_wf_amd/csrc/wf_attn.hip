@@ -164,8 +164,9 @@ struct AttnParams {
   int32_t n_active;       // active slots
   // Run-time pool (packed order with a workspace). pool_items query tiles of
   // the heaviest slot (rank 0), item i being tile pool_qt0 - i / H of head
-  // i % H (the last full tiles of each head in turn), are not on any list: each is cut into its pool_nseg chunks of keys, piece k
-  // being chunk k % pool_nseg of item k / pool_nseg. A block that has run its
+  // i % H (the last full tiles of each head in turn), are not on any list:
+  // each is cut into its pool_nseg chunks of keys, piece k being chunk k %
+  // pool_nseg of item k / pool_nseg. A block that has run its
   // list takes pieces from a counter in the workspace until none are left, so
   // CUs that run faster (whole XCDs differ by several per cent) take more. A
   // piece leaves its partial softmax state — the unnormalised O, the running
@@ -1258,7 +1259,7 @@ attn_tick_kernel(const AttnParams p) {
       // accesses; a fence would write back and invalidate this XCD's whole
       // L2, the other CUs' cached tiles too.
       typedef unsigned v4u __attribute__((ext_vector_type(4)));
-      constexpr int kStateBytes = QROWS * (D + 2) * 4;
+      constexpr int kStateBytes = int(state_bytes(D));
       char* const states = reinterpret_cast<char*>(p.ws) + kWsHeader;
       const int pi = piece / p.pool_nseg;
       const int row = wave * 32 + r;  // row of the query tile
@@ -1291,7 +1292,7 @@ attn_tick_kernel(const AttnParams p) {
       __syncthreads();
       if (pool_slot[1] && wave_active && qrow < T) {  // every piece of item pi has left its state
         // merge in walk order (the same sums whichever block merges): the
-        // states' maxima and sums first, then each state's O, weighted
+        // states' maxima first, then each state's O and row sum, weighted
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             states + int64_t(pi) * p.pool_nseg * kStateBytes, 0, p.pool_nseg * kStateBytes,
             kBufferFlags);
