@@ -420,18 +420,18 @@ def test_fp8kv_tick_full_size_sampled_rows(name):
         f"over {len(rows)} rows")
 
 
-@pytest.mark.parametrize("n,T,H,D,P", [
-    (3, 200, 2, 128, 64),      # ragged last page
-    (2, 150, 3, 64, 128),      # two scale tiles per page, the last one empty
-    (5, 4680, 12, 128, 64),    # a 4-step tick's live chunks
+@pytest.mark.parametrize("n,T,H,D,P,v8", [
+    (3, 200, 2, 128, 64, False),    # ragged last page
+    (2, 150, 3, 64, 128, False),    # two scale tiles per page, the last one empty
+    (5, 4680, 12, 128, 64, False),  # a 4-step tick's live chunks
+    (3, 200, 2, 128, 64, True),     # 8-bit values (D = 128, as the attention reads them)
+    (2, 150, 3, 128, 128, True),
+    (5, 4680, 12, 128, 64, True),
 ])
-@pytest.mark.parametrize("v8", [False, True])
 def test_store_fp8_chunks_equals_one_call_per_chunk(n, T, H, D, P, v8):
     """wf_store_paged_fp8_chunks (n chunks, one launch) leaves every pool byte
     as n wf_store_paged_fp8 calls do (pools poisoned alike beforehand), so its
     pages are the oracle's as well."""
-    if v8 and D != 128:
-        pytest.skip("8-bit values: D = 128")
     say(f"store fp8 chunks n={n} T={T} H={H} D={D} P={P} v8={v8}")
     ppc = -(-T // P)
     num_pages = n * ppc + 7
