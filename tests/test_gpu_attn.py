@@ -126,6 +126,33 @@ def test_run_time_pool_parity(S, T, H, D, P, n_hist, mask, hist_first):
     assert diff <= 2 ** -6
 
 
+@pytest.mark.parametrize("S,T,H,n_hist,pool", [
+    (5, 1460, 40, 2, False),   # 240 (stage, head) groups: two launches of 20 heads
+    (5, 1460, 40, 2, True),    # the same with the run-time pool in each launch
+    (7, 1460, 40, 1, True),    # 320 groups: three launches (14, 14, 12 heads)
+])
+def test_head_split_parity(S, T, H, n_hist, pool):
+    """A tick with more (stage, head) groups than one packed plan holds runs as
+    launches over head ranges, each planned as a tick of its heads and offset
+    to its first head: every (stage, head) against the oracle, every row
+    written, and more than one launch in the work order (its blocks numbered
+    on across the launches, more than one per CU)."""
+    say(f"head split: S={S} T={T} H={H} n_hist={n_hist} pool={pool}")
+    t = setup_tick(S, T, H, 128, 64, n_hist, (n_hist + 2) * -(-T // 64) + 8, seed=T + H + S)
+    ws = workspace_for(t) if pool else None
+    d = wfattn.make_tick_desc(t.S, t.active_mask, t.T, t.H, t.D, t.scale, t.q, t.k, t.v, t.o,
+                              t.k_pool, t.v_pool, t.num_pages, t.P, t.hist_pages, t.n_hist,
+                              t.hist_first, workspace=ws)
+    order = wfattn.tick_work_order(d, 0)
+    n_blocks = len(set(order[order[:, 0] >= 0, 0].tolist()))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"  blocks {n_blocks} on {cus} CUs, pool items {int(np.sum(order[:, 0] == -1))}")
+    assert n_blocks > cus
+    o = run_tick(t, workspace=ws)
+    worst = compare(o, oracle_tick(t), label="head split")
+    say(f"  worst rel-L2 {worst:.2e}")
+
+
 @pytest.mark.parametrize("mask,hist_first", [
     (0b00011, None),                 # fill tick: only stages 0, 1
     (0b11100, None),                 # drain tick: stages 2, 3 and the store

@@ -119,13 +119,13 @@ def oracle_rows(cfg, pages: MirroredPages, q, k, v, mask: int, rows, heads=None)
 
 @pytest.mark.parametrize("name,pool", [("wan13_4step", True), ("wan13_4step", False),
                                        ("wan13_5step", True), ("wan13_5step", False),
-                                       ("wan14b_4step", False)])
+                                       ("wan14b_4step", True), ("wan14b_4step", False)])
 def test_full_size_tick_sampled_rows(name, pool):
     """One steady tick exactly as the bench sets it up: n_hist history chunks
     (generator seeds 2000 + c) stored through the page table, live inputs from
     the rollout seed of tick 0, all S+1 slots active; with the bench's
     workspace (run-time pool) and without. (The 14B-like tick's 200 groups
-    are dealt whole to the XCDs, without lists: it takes no workspace.)"""
+    run as launches over head ranges.)"""
     cfg = inputs.CONFIGS[name]
     say(f"[full-size] {name}: S={cfg.S} T={cfg.T} H={cfg.H} n_hist={cfg.n_hist} pool={pool}")
     pages = MirroredPages(cfg, cfg.n_hist)

@@ -87,7 +87,8 @@ def test_check_pages_mode_rejects_bad_ids(monkeypatch):
 
 
 @pytest.mark.parametrize("S,T,H,D,P,n_hist", [(2, 100, 2, 64, 16, 1), (4, 4680, 12, 128, 64, 3),
-                                              (3, 70, 3, 128, 64, 0)])
+                                              (3, 70, 3, 128, 64, 0),
+                                              (5, 1460, 40, 128, 64, 2)])  # two head launches
 def test_store_fused_into_attention_launch(S, T, H, D, P, n_hist):
     """wf_attn_tick with store_pages: the pages equal the oracle store bit for bit
     (zero tails, other pages untouched) and the outputs equal those of the

@@ -33,7 +33,7 @@ def keys_of(S, mask, n_hist, hist_first, s):
 CASES = [
     ("wan13_4step", 4, 0b11111, 4680, 12, 3, None),
     ("wan13_5step", 5, 0b111111, 4680, 12, 6, None),
-    ("wan14b_4step", 4, 0b11111, 4680, 40, 3, None),        # too large to pack: whole groups
+    ("wan14b_4step", 4, 0b11111, 4680, 40, 3, None),        # 200 groups: launches of fewer heads
     ("fill", 4, 0b00111, 4680, 12, 0, None),                 # fill tick, no store yet
     ("budgets", 4, 0b11111, 4680, 12, 3, [0, 1, 1, 2, 3]),   # per-slot history budgets
     ("small", 2, 0b101, 700, 3, 1, None),
@@ -183,6 +183,37 @@ def test_plain_order_when_tables_overflow():
     stages.sort(key=lambda s: -keys_of(S, mask, 1, None, s))        # heaviest first (stable)
     want = [(s, h, 256 * q) for s in stages for h in range(H) for q in range(ntq)]
     assert [(int(r[2]), int(r[3]), int(r[4])) for r in order] == want
+
+
+@pytest.mark.parametrize("ws", [False, True])
+def test_head_split_launches(ws):
+    """200 (stage, head) groups of the 14B-like tick are more than one packed
+    plan holds, and one item per block would leave 15 items per CU to the
+    dispatcher: the tick runs as launches over head ranges of ceil(H / n)
+    heads, each a packed plan of one block per CU (blocks numbered on across
+    the launches), each launch's items of its own heads only."""
+    S, mask, T, H, n_hist = 4, 0b11111, 4680, 40, 3
+    d = desc(S, mask, T, H, n_hist)
+    order = wf.tick_work_order(with_workspace(d) if ws else d, 32)
+    listed = order[order[:, 0] >= 0]
+    n_blocks = int(listed[:, 0].max()) + 1
+    assert n_blocks % 256 == 0 and n_blocks // 256 >= 2
+    n = n_blocks // 256
+    hp = -(-H // n)
+    ranges = []
+    for launch in range(n):
+        rows = listed[(listed[:, 0] >= 256 * launch) & (listed[:, 0] < 256 * (launch + 1))]
+        heads = sorted(set(rows[:, 3].tolist()))
+        assert heads == list(range(heads[0], heads[0] + len(heads)))
+        ranges.append((heads[0], len(heads)))
+        eff, _ = makespan(rows, S, mask, n_hist, None, T, 32)
+        assert eff >= 0.95, (launch, eff)
+    assert ranges == [(i * hp, min(hp, H - i * hp)) for i in range(n)]
+    pool = order[order[:, 0] == -1]
+    assert (len(pool) > 0) == ws
+    assert np.all(np.diff(pool[:, 1]) == 1)
+    # pool items follow the launches: heads of each launch's range in turn
+    assert np.all(np.diff(pool[:, 3] // hp) >= 0)
 
 
 STATE_BYTES = 256 * (128 + 2) * 4   # one piece's partial state, D = 128

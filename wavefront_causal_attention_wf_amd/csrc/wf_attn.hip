@@ -97,6 +97,8 @@ constexpr int kMaxPool = 128;
 constexpr int kWsHeader = 1024;
 static_assert((1 + kMaxPool) * 4 <= kWsHeader, "pool counters exceed the workspace header");
 constexpr double kPoolShare = 0.08;  // share of a tick's work the pool takes
+constexpr int kMaxHeadParts = 8;     // launches a tick's heads may be split into
+constexpr int kMinSplitItems = 4;    // items per CU below which a tick is not split
 // A piece's partial state: [QROWS][D] unnormalised output, then the QROWS row
 // maxima and the QROWS row sums (fp32).
 constexpr int64_t state_bytes(int D) { return int64_t(QROWS) * (D + 2) * 4; }
@@ -135,7 +137,10 @@ struct AttnParams {
   uint32_t p_magic;       // floor(2^32 / P) + 1: t / P == umulhi(t, p_magic) for t*P < 2^32
   float c;                // scale * log2(e)
   int32_t ntq;            // query tiles per chunk
-  int32_t items_per_stage;  // H * ntq
+  // A tick with too many heads for one packed plan runs as several launches,
+  // each over heads [h0, h0 + hp); the plan counts heads of its launch.
+  int32_t hp, h0;
+  int32_t items_per_stage;  // hp * ntq
   int32_t n_page_ids;     // page ids staged in LDS (non-fast path): history, then live
   // Work order; block b runs on XCD x = b % 8 (round-robin dispatch).
   // use_xcd = 1: block b is that XCD's item k = b / 8, query tile k % ntq of
@@ -621,8 +626,8 @@ attn_tick_kernel(const AttnParams p) {
     int seg0 = 0;     // pieces: the chunk of the walk this piece covers
     if (in_pool) {
       const int pi = piece / p.pool_nseg;
-      h = pi % p.H;
-      qt = p.pool_qt0 - pi / p.H;
+      h = pi % p.hp;
+      qt = p.pool_qt0 - pi / p.hp;
       seg0 = piece - pi * p.pool_nseg;
     } else if (p.use_xcd == 2) {
       const int x = b & (kNumXcd - 1);
@@ -639,13 +644,13 @@ attn_tick_kernel(const AttnParams p) {
       }
       const int grp = p.pack_grp[x][run];
       qt = p.pack_qt0[x][run] + before;
-      const int n_groups = p.n_active * p.H;
+      const int n_groups = p.n_active * p.hp;
       if (grp >= n_groups) {  // a tail item
         h = (grp - n_groups) / p.tail_per_head;
         tail_m = grp - n_groups - h * p.tail_per_head;
       } else {
-        rank = grp / p.H;
-        h = grp - rank * p.H;
+        rank = grp / p.hp;
+        h = grp - rank * p.hp;
       }
     } else if (p.use_xcd) {
       const int x = b & (kNumXcd - 1);
@@ -654,14 +659,15 @@ attn_tick_kernel(const AttnParams p) {
       if (gi >= p.xcd_n[x]) return;  // whole block: this XCD's list is shorter
       const int grp = p.xcd_groups[x * p.xcd_stride + gi];
       qt = k - gi * p.ntq;
-      rank = grp / p.H;
-      h = grp - rank * p.H;
+      rank = grp / p.hp;
+      h = grp - rank * p.hp;
     } else {
       rank = b / p.items_per_stage;
       const int rem = b - rank * p.items_per_stage;
       h = rem / p.ntq;
       qt = rem - h * p.ntq;
     }
+    h += p.h0;  // the plan counts this launch's heads
     const int T = p.T;
     // s_blk: the slot whose context the item walks; s: the slot of this wave's
     // query rows (they differ only in tail items); ntiles_w: the tiles of the
@@ -1742,7 +1748,7 @@ void copy_plan(const AttnParams& from, AttnParams& to) {
 // formats, paging) and the CU count, and a streaming rollout repeats a few
 // shapes tick after tick, so the last kPlanCache plans are kept (the packing
 // search costs tens of milliseconds of host time).
-constexpr int kPlanCache = 8;
+constexpr int kPlanCache = 16;
 struct PlanKey {
   int32_t v[16 + WF_MAX_STAGES];
   bool operator==(const PlanKey& o) const { return std::memcmp(v, o.v, sizeof(v)) == 0; }
@@ -1794,19 +1800,56 @@ void plan_launch(const wf_tick_desc& d, const StagePlan& pl, int C, int pool_max
   cache[slot].used = ++clock;
 }
 
-// The launch's work order for a descriptor, planned on the host alone (the
-// diagnostic and the workspace size).
-void plan_host_only(const wf_tick_desc& d, const StagePlan& pl, int C, int pool_max, AttnParams& p,
-                    int64_t& blocks) {
+// The work order of the launch over heads [h0, h0 + hp) of a descriptor:
+// planned as a tick of hp heads (the plan counts the launch's heads), into the
+// plan members of p (p.H, the tensors' head count, is not touched).
+void plan_part(const wf_tick_desc& d, const StagePlan& pl, int C, int64_t ws_bytes, int h0, int hp,
+               AttnParams& p, int64_t& blocks) {
+  wf_tick_desc dp = d;
+  dp.H = hp;
+  p.hp = hp;
+  p.h0 = h0;
+  p.items_per_stage = hp * p.ntq;
+  blocks = 0;
+  plan_launch(dp, pl, C, pool_capacity(dp, pl, ws_bytes), p, blocks);
+}
+
+// Heads per launch. One launch covers every head unless its plan cannot be
+// packed (one block per CU running a list) while a split into n launches of
+// ceil(H / n) heads can: more (stage, head) groups than the tables hold would
+// otherwise run one block per item, which leaves CUs waiting for the
+// dispatcher between blocks and idle at the end. A tick of a few items per CU
+// loses little that way and stays one launch. Returns (h0, hp) per launch.
+std::vector<std::array<int, 2>> head_parts(const wf_tick_desc& d, const StagePlan& pl, int C,
+                                           int64_t ws_bytes, AttnParams& scratch) {
+  int64_t blocks = 0;
+  plan_part(d, pl, C, ws_bytes, 0, d.H, scratch, blocks);
+  if (scratch.use_xcd == 2 || C <= 0 || blocks < int64_t(kMinSplitItems) * kNumXcd * C)
+    return {{0, d.H}};
+  for (int n = 2; n <= kMaxHeadParts && n <= d.H; ++n) {
+    const int hp = (d.H + n - 1) / n;
+    const int last = d.H - (n - 1) * hp;
+    if (last <= 0) continue;
+    plan_part(d, pl, C, ws_bytes, 0, hp, scratch, blocks);
+    if (scratch.use_xcd != 2) continue;
+    plan_part(d, pl, C, ws_bytes, 0, last, scratch, blocks);
+    if (scratch.use_xcd != 2) continue;
+    std::vector<std::array<int, 2>> parts;
+    for (int i = 0; i < n; ++i) parts.push_back({i * hp, i + 1 < n ? hp : last});
+    return parts;
+  }
+  return {{0, d.H}};
+}
+
+// Base members of a launch's parameters that the host-only planners need.
+void plan_base(const wf_tick_desc& d, AttnParams& p) {
   std::memset(&p, 0, sizeof(p));
   p.T = d.T;
   p.H = d.H;
   p.tps = (d.T + KT - 1) / KT;
   p.ntq = (d.T + QROWS - 1) / QROWS;
-  p.items_per_stage = d.H * p.ntq;
-  blocks = 0;
-  plan_launch(d, pl, C, pool_max, p, blocks);
 }
+
 
 // kFast: every tile is one uniform span of a page or live chunk (page size a
 // multiple of 64, or no history); otherwise history tiles resolve per lane.
@@ -1914,7 +1957,7 @@ void decode_block(const AttnParams& p, int b, std::vector<std::array<int, 5>>& r
   if (p.use_xcd == 2) {
     const int x = b & (kNumXcd - 1);
     const int c = b / kNumXcd;
-    const int G = p.n_active * p.H;
+    const int G = p.n_active * p.hp;
     for (int k = p.pack_bin[x][c]; k < p.pack_bin[x][c + 1]; ++k) {
       const int run = (p.pack_code[x][k >> 3] >> (4 * (k & 7))) & 15;
       int before = 0;
@@ -1922,7 +1965,7 @@ void decode_block(const AttnParams& p, int b, std::vector<std::array<int, 5>>& r
       const int grp = p.pack_grp[x][run];
       const int item = k - p.pack_bin[x][c];
       if (grp < G) {
-        tile(item, grp / p.H, grp % p.H, p.pack_qt0[x][run] + before);
+        tile(item, grp / p.hp, grp % p.hp, p.pack_qt0[x][run] + before);
         continue;
       }
       const int h = (grp - G) / p.tail_per_head;
@@ -1947,7 +1990,7 @@ void decode_block(const AttnParams& p, int b, std::vector<std::array<int, 5>>& r
     const int gi = k / p.ntq;
     if (gi >= p.xcd_n[x]) return;
     const int grp = p.xcd_groups[x * p.xcd_stride + gi];
-    tile(0, grp / p.H, grp % p.H, k - gi * p.ntq);
+    tile(0, grp / p.hp, grp % p.hp, k - gi * p.ntq);
   } else {
     const int rank = b / p.items_per_stage;
     const int rem = b - rank * p.items_per_stage;
@@ -1970,21 +2013,35 @@ extern "C" wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_pe
     if (d.T == 0 || d.active_mask == 0) return WF_OK;
     StagePlan pl;
     plan_stages(d, pl);
+    const int C = cus_per_xcd_hint > 0 ? cus_per_xcd_hint : cus_per_xcd();
+    const int64_t ws_bytes = d.workspace ? d.workspace_bytes : 0;
     AttnParams p;
-    int64_t blocks = 0;
-    plan_host_only(d, pl, cus_per_xcd_hint > 0 ? cus_per_xcd_hint : cus_per_xcd(),
-                   pool_capacity(d, pl, d.workspace ? d.workspace_bytes : 0), p, blocks);
-    std::vector<int> out_rows;
-    for (int64_t b = 0; b < blocks; ++b) {
-      std::vector<std::array<int, 5>> items;
-      decode_block(p, int(b), items);
-      for (const auto& it : items)
-        out_rows.insert(out_rows.end(), {int(b), it[0], pl.order[it[1]], it[2], it[3], it[4]});
+    plan_base(d, p);
+    AttnParams scratch = p;
+    const auto parts = head_parts(d, pl, C, ws_bytes, scratch);
+    // launches in order, their blocks numbered on; then every launch's pool items
+    std::vector<int> out_rows, pool_rows;
+    int64_t block0 = 0;
+    int pool0 = 0;
+    for (const auto& part : parts) {
+      int64_t blocks = 0;
+      plan_part(d, pl, C, ws_bytes, part[0], part[1], p, blocks);
+      for (int64_t b = 0; b < blocks; ++b) {
+        std::vector<std::array<int, 5>> items;
+        decode_block(p, int(b), items);
+        for (const auto& it : items)
+          out_rows.insert(out_rows.end(), {int(block0 + b), it[0], pl.order[it[1]], part[0] + it[2],
+                                           it[3], it[4]});
+      }
+      for (int i = 0; i < p.pool_items; ++i) {  // run-time pool: block -1
+        const int q0 = (p.pool_qt0 - i / part[1]) * QROWS;
+        pool_rows.insert(pool_rows.end(), {-1, pool0 + i, pl.order[0], part[0] + i % part[1], q0,
+                                           std::min(QROWS, d.T - q0)});
+      }
+      block0 += blocks;
+      pool0 += p.pool_items;
     }
-    for (int i = 0; i < p.pool_items; ++i) {  // run-time pool: block -1
-      const int q0 = (p.pool_qt0 - i / d.H) * QROWS;
-      out_rows.insert(out_rows.end(), {-1, i, pl.order[0], i % d.H, q0, std::min(QROWS, d.T - q0)});
-    }
+    out_rows.insert(out_rows.end(), pool_rows.begin(), pool_rows.end());
     *n_items = int64_t(out_rows.size() / 6);
     if (!out) return WF_OK;
     if (capacity < int64_t(out_rows.size()))
@@ -2106,23 +2163,12 @@ int32_t attn_tick_impl(const wf_tick_desc* desc, void* ws, int64_t ws_bytes, hip
     p.p_magic = uint32_t((uint64_t(1) << 32) / uint64_t(p.P) + 1);
     p.c = float(double(d.scale) * 1.4426950408889634);
     p.ntq = (d.T + QROWS - 1) / QROWS;
-    p.items_per_stage = d.H * p.ntq;
     p.n_page_ids = (d.n_hist + (live_paged ? d.S + 1 : 0)) * ppc;
     for (int i = 0; i < pl.n_active; ++i) p.stage_of_rank[i] = pl.order[i];
     for (int s = 0; s <= d.S; ++s) {
       p.nseg[s] = pl.nseg[s];
       for (int i = 0; i < pl.nseg[s]; ++i) p.seg[s][i] = pl.seg[s][i];
     }
-    int64_t blocks = 0;
-    plan_launch(d, pl, cus_per_xcd(), pool_capacity(d, pl, ws ? ws_bytes : 0), p, blocks);
-    p.ws = static_cast<uint32_t*>(ws);
-    if (p.pool_pieces > 0) {  // counters of the run-time pool start at zero
-      clear_pool_kernel<<<1, 64, 0, stream>>>(p.ws, 1 + p.pool_items);
-      st = check_launch("wf_attn_tick (pool counters)");
-      if (st != WF_OK) return st;
-    }
-    blocks += p.n_store_blocks;  // a multiple of 8: the XCD of every attention block is kept
-    if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
     const bool fast = !paged || d.P % KT == 0;
     if (fast) {  // the kernel keeps a table of tile sources in LDS
       int max_seg = 0;
@@ -2134,18 +2180,38 @@ int32_t attn_tick_impl(const wf_tick_desc* desc, void* ws, int64_t ws_bytes, hip
       return fail(WF_EUNSUPPORTED, "wf_attn_tick: page table of %d ids exceeds %d", p.n_page_ids,
                   kMaxPageIds);
     }
-    if (v8)  // (validated: D = 128, P a multiple of 64, so fast)
-      st = launch_attn<128, true, true, true>(p, unsigned(blocks), stream);
-    else if (f8)
-      st = launch_attn<128, true, true>(p, unsigned(blocks), stream);
-    else if (d.D == 128)
-      st = fast ? launch_attn<128, true>(p, unsigned(blocks), stream)
-                : launch_attn<128, false>(p, unsigned(blocks), stream);
-    else
-      st = fast ? launch_attn<64, true>(p, unsigned(blocks), stream)
-                : launch_attn<64, false>(p, unsigned(blocks), stream);
-    if (st != WF_OK) return st;
-    return check_launch("wf_attn_tick");
+    const int C = cus_per_xcd();
+    const int64_t pool_bytes = ws ? ws_bytes : 0;
+    p.ws = static_cast<uint32_t*>(ws);
+    const int n_store_blocks = p.n_store_blocks;
+    AttnParams scratch = p;
+    const auto parts = head_parts(d, pl, C, pool_bytes, scratch);
+    for (size_t i = 0; i < parts.size(); ++i) {  // launches in stream order, one per head range
+      int64_t blocks = 0;
+      plan_part(d, pl, C, pool_bytes, parts[i][0], parts[i][1], p, blocks);
+      p.n_store_blocks = i == 0 ? n_store_blocks : 0;  // the first launch writes the store pages
+      if (p.pool_pieces > 0) {  // counters of the run-time pool start at zero
+        clear_pool_kernel<<<1, 64, 0, stream>>>(p.ws, 1 + p.pool_items);
+        st = check_launch("wf_attn_tick (pool counters)");
+        if (st != WF_OK) return st;
+      }
+      blocks += p.n_store_blocks;  // a multiple of 8: the XCD of every attention block is kept
+      if (blocks > 0x7fffffff) return fail(WF_EUNSUPPORTED, "wf_attn_tick: grid too large");
+      if (v8)  // (validated: D = 128, P a multiple of 64, so fast)
+        st = launch_attn<128, true, true, true>(p, unsigned(blocks), stream);
+      else if (f8)
+        st = launch_attn<128, true, true>(p, unsigned(blocks), stream);
+      else if (d.D == 128)
+        st = fast ? launch_attn<128, true>(p, unsigned(blocks), stream)
+                  : launch_attn<128, false>(p, unsigned(blocks), stream);
+      else
+        st = fast ? launch_attn<64, true>(p, unsigned(blocks), stream)
+                  : launch_attn<64, false>(p, unsigned(blocks), stream);
+      if (st != WF_OK) return st;
+      st = check_launch("wf_attn_tick");
+      if (st != WF_OK) return st;
+    }
+    return WF_OK;
   }
 }
 
@@ -2180,12 +2246,18 @@ extern "C" wf_status wf_tick_workspace_bytes(const wf_tick_desc* desc, int64_t* 
     if (pool_capacity(*desc, pl, int64_t(1) << 60) == 0) return WF_OK;
     // the items the planner gives the pool when space is no limit (the CU
     // count of the current device, else MI355X's 32 per XCD)
+    const int C = cus_per_xcd() > 0 ? cus_per_xcd() : 32;
+    const int64_t unlimited = int64_t(1) << 60;
     AttnParams p;
-    int64_t blocks = 0;
-    const int C = cus_per_xcd();
-    plan_host_only(*desc, pl, C > 0 ? C : 32, kMaxPool, p, blocks);
-    if (p.pool_items > 0)
-      *bytes = kWsHeader + int64_t(p.pool_items) * p.pool_nseg * state_bytes(desc->D);
+    plan_base(*desc, p);
+    AttnParams scratch = p;
+    for (const auto& part : head_parts(*desc, pl, C, unlimited, scratch)) {
+      int64_t blocks = 0;
+      plan_part(*desc, pl, C, unlimited, part[0], part[1], p, blocks);
+      if (p.pool_items > 0)
+        *bytes = std::max<int64_t>(
+            *bytes, kWsHeader + int64_t(p.pool_items) * p.pool_nseg * state_bytes(desc->D));
+    }
     return WF_OK;
   } catch (...) {
     return fail(WF_EINVAL, "wf_tick_workspace_bytes: internal error");
