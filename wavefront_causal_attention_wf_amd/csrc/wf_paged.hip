@@ -16,10 +16,19 @@
 // grid-stride apart, so a block's loads are contiguous while a thread's lie far
 // apart. That spreads each wave's requests over the memory channels better than
 // giving a block a contiguous range of one page (5.2 -> 5.6 TB/s for the store).
-// Every load is issued before any store; sources are read once, so loads and
-// stores are both nontemporal.
+// Sources are read once, so loads and stores are both nontemporal.
+//
+// The store runs as many blocks as the GPU keeps resident at once (8 of 256
+// threads per CU, so every SIMD holds 8 waves) and each thread works through
+// batches of up to kCopyUnroll units a grid-stride apart, the next batch's
+// loads issued before the current batch's stores. For the 4680-token chunk
+// that is one batch of 3-4 units per thread: 10.4 -> 10.1 us against one block
+// per 4 units per thread (1776 blocks, 6.9 waves per SIMD). More blocks than
+// stay resident measured slower, and so did issuing all of a thread's loads
+// before any wait (13 us: in-flight requests spread over distant addresses).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "wf_internal.h"
@@ -30,34 +39,61 @@ namespace {
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 
+constexpr int kStoreBlocksPerCu = 8;  // 32 waves per CU: 8 per SIMD at <= 64 VGPRs
+
 // Units [0, 2 * total): K's pages (z = 0), then V's (z = 1); unit e of a
 // tensor is unit e % page16 of its page e / page16. Units at or past the
-// chunk's last token (valid16) are written as zero.
-__global__ __launch_bounds__(kCopyThreads) void store_paged_kernel(
-    const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint4* __restrict__ k_pool,
-    uint4* __restrict__ v_pool, const int32_t* __restrict__ page_ids, uint32_t valid16,
-    uint32_t page16, uint32_t total) {
-  const uint32_t stride = gridDim.x * kCopyThreads;
-  const uint32_t first = blockIdx.x * kCopyThreads + threadIdx.x;
+// chunk's last token (valid16) are written as zero. Batch j of a thread holds
+// its units first + (j * kCopyUnroll + u) * stride.
+struct CopyBatch {
   uint4 val[kCopyUnroll];
-  uint64_t dst[kCopyUnroll];  // unit offset in its pool (bit 63: V)
+  uint64_t dst[kCopyUnroll];  // unit offset in its pool (bit 63: V); ~0: none
+};
+
+__device__ __forceinline__ void store_batch_load(CopyBatch& b, uint32_t base, uint32_t stride,
+                                                 const uint4* __restrict__ k_src,
+                                                 const uint4* __restrict__ v_src,
+                                                 const int32_t* __restrict__ page_ids,
+                                                 uint32_t valid16, uint32_t page16, uint32_t total) {
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
-    const uint32_t e2 = first + u * stride;
+    const uint32_t e2 = base + u * stride;
     const bool z = e2 >= total;
     const uint32_t e = z ? e2 - total : e2;
     const bool in = e2 < 2 * total;
-    val[u] = (in && e < valid16) ? load_stream16((z ? v_src : k_src) + e) : make_uint4(0u, 0u, 0u, 0u);
+    b.val[u] = (in && e < valid16) ? load_stream16((z ? v_src : k_src) + e)
+                                   : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t pg = e / page16;
-    dst[u] = in ? (uint64_t(uint32_t(page_ids[pg])) * page16 + (e - pg * page16)) |
-                      (uint64_t(z) << 63)
-                : ~uint64_t(0);
+    b.dst[u] = in ? (uint64_t(uint32_t(page_ids[pg])) * page16 + (e - pg * page16)) |
+                        (uint64_t(z) << 63)
+                  : ~uint64_t(0);
   }
+}
+
+__global__ __launch_bounds__(kCopyThreads) __attribute__((amdgpu_waves_per_eu(kStoreBlocksPerCu)))
+void store_paged_kernel(const uint4* __restrict__ k_src, const uint4* __restrict__ v_src,
+                        uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                        const int32_t* __restrict__ page_ids, uint32_t valid16, uint32_t page16,
+                        uint32_t total) {
+  const uint32_t stride = gridDim.x * kCopyThreads;
+  const uint32_t step = kCopyUnroll * stride;
+  uint32_t base = blockIdx.x * kCopyThreads + threadIdx.x;
+  CopyBatch cur;
+  store_batch_load(cur, base, stride, k_src, v_src, page_ids, valid16, page16, total);
+  while (true) {
+    const bool more = base + step < 2 * total;  // (no wrap: checked on the host)
+    CopyBatch nxt;
+    if (more)
+      store_batch_load(nxt, base + step, stride, k_src, v_src, page_ids, valid16, page16, total);
 #pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    if (dst[u] == ~uint64_t(0)) continue;
-    const bool z = dst[u] >> 63;
-    store_stream16((z ? v_pool : k_pool) + (dst[u] & ~(uint64_t(1) << 63)), val[u]);
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      if (cur.dst[u] == ~uint64_t(0)) continue;
+      const bool z = cur.dst[u] >> 63;
+      store_stream16((z ? v_pool : k_pool) + (cur.dst[u] & ~(uint64_t(1) << 63)), cur.val[u]);
+    }
+    if (!more) break;
+    cur = nxt;
+    base += step;
   }
 }
 
@@ -131,12 +167,19 @@ extern "C" wf_status wf_store_paged(const void* k_src, const void* v_src, void* 
     const int64_t row16 = int64_t(H) * D * 2 / 16;
     const int64_t page16 = int64_t(P) * row16;
     const int64_t total = int64_t(ppc) * page16;  // units per tensor (whole pages)
-    if (2 * total + int64_t(kCopyThreads) * kCopyUnroll >= (int64_t(1) << 32) ||
+    // every resident slot filled (a thread may hold fewer than kCopyUnroll
+    // units), unless the chunk has fewer units than threads
+    const int64_t per_block = kCopyThreads * kCopyUnroll;
+    const int cus = device_cu_count();
+    int64_t blocks = (2 * total + kCopyThreads - 1) / kCopyThreads;
+    blocks = std::min<int64_t>(blocks, cus > 0 ? int64_t(kStoreBlocksPerCu) * cus
+                                               : (2 * total + per_block - 1) / per_block);
+    // a thread's last batch start plus one step stays below 2^32
+    if (2 * total + 2 * blocks * per_block >= (int64_t(1) << 32) ||
         int64_t(num_pages) * page16 >= (int64_t(1) << 62))
       return fail(WF_EUNSUPPORTED, "wf_store_paged: chunk of %lld bytes too large",
                   static_cast<long long>(total * 16));
-    const int64_t per_block = kCopyThreads * kCopyUnroll;
-    const dim3 grid(unsigned((2 * total + per_block - 1) / per_block));
+    const dim3 grid(static_cast<unsigned>(blocks));
     store_paged_kernel<<<grid, kCopyThreads, 0, stream>>>(
         static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
         static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), page_ids,
