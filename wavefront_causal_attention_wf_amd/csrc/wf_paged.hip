@@ -98,18 +98,18 @@ void store_paged_kernel(const uint4* __restrict__ k_src, const uint4* __restrict
 }
 
 // Inverse: unit e of chunk c (tokens [0, T) only) comes from page
-// page_ids[c * ppc + e / page16]. Units [0, 2 * total): K's chunks, then V's;
-// the grid and batches as in the store.
-__device__ __forceinline__ void gather_batch_load(uint4 (&val)[kCopyUnroll], uint32_t base,
-                                                  uint32_t stride,
-                                                  const uint4* __restrict__ k_pool,
-                                                  const uint4* __restrict__ v_pool,
-                                                  const int32_t* __restrict__ page_ids,
-                                                  uint32_t valid16, uint32_t page16, uint32_t ppc,
-                                                  uint32_t total) {
+// page_ids[c * ppc + e / page16]. Units [0, 2 * n * valid16): K's chunks, then
+// V's.
+__global__ __launch_bounds__(kCopyThreads) void gather_paged_kernel(
+    const uint4* __restrict__ k_pool, const uint4* __restrict__ v_pool,
+    const int32_t* __restrict__ page_ids, uint4* __restrict__ k_dst, uint4* __restrict__ v_dst,
+    uint32_t valid16, uint32_t page16, uint32_t ppc, uint32_t total) {
+  const uint32_t stride = gridDim.x * kCopyThreads;
+  const uint32_t first = blockIdx.x * kCopyThreads + threadIdx.x;
+  uint4 val[kCopyUnroll];
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
-    const uint32_t e2 = base + u * stride;
+    const uint32_t e2 = first + u * stride;
     if (e2 >= 2 * total) continue;
     const bool z = e2 >= total;
     const uint32_t ec = z ? e2 - total : e2;     // unit within the n chunks
@@ -119,39 +119,16 @@ __device__ __forceinline__ void gather_batch_load(uint4 (&val)[kCopyUnroll], uin
     const uint64_t src = uint64_t(uint32_t(page_ids[c * ppc + pg])) * page16 + (e - pg * page16);
     val[u] = load_stream16((z ? v_pool : k_pool) + src);
   }
-}
-
-__global__ __launch_bounds__(kCopyThreads) __attribute__((amdgpu_waves_per_eu(kStoreBlocksPerCu)))
-void gather_paged_kernel(const uint4* __restrict__ k_pool, const uint4* __restrict__ v_pool,
-                         const int32_t* __restrict__ page_ids, uint4* __restrict__ k_dst,
-                         uint4* __restrict__ v_dst, uint32_t valid16, uint32_t page16, uint32_t ppc,
-                         uint32_t total) {
-  const uint32_t stride = gridDim.x * kCopyThreads;
-  const uint32_t step = kCopyUnroll * stride;
-  uint32_t base = blockIdx.x * kCopyThreads + threadIdx.x;
-  uint4 cur[kCopyUnroll];
-  gather_batch_load(cur, base, stride, k_pool, v_pool, page_ids, valid16, page16, ppc, total);
-  while (true) {
-    const bool more = base + step < 2 * total;  // (no wrap: checked on the host)
-    uint4 nxt[kCopyUnroll];
-    if (more)
-      gather_batch_load(nxt, base + step, stride, k_pool, v_pool, page_ids, valid16, page16, ppc,
-                        total);
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const uint32_t e2 = base + u * stride;
-      if (e2 >= 2 * total) continue;
-      const bool z = e2 >= total;
-      store_stream16((z ? v_dst : k_dst) + (z ? e2 - total : e2), cur[u]);
-    }
-    if (!more) break;
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) cur[u] = nxt[u];
-    base += step;
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const uint32_t e2 = first + u * stride;
+    if (e2 >= 2 * total) continue;
+    const bool z = e2 >= total;
+    store_stream16((z ? v_dst : k_dst) + (z ? e2 - total : e2), val[u]);
   }
 }
 
-// Blocks for a copy of n_units 16-byte units: every resident slot filled (a
+// Blocks for the store's n_units 16-byte units: every resident slot filled (a
 // thread may hold fewer than kCopyUnroll units), unless there are fewer units
 // than threads.
 int64_t copy_blocks(int64_t n_units) {
@@ -238,12 +215,12 @@ extern "C" wf_status wf_gather_paged(const void* k_pool, const void* v_pool,
     const int64_t page16 = int64_t(P) * row16;
     const int64_t valid16 = int64_t(T) * row16;
     const int64_t total = int64_t(n_chunks) * valid16;  // units per tensor
-    const int64_t blocks = copy_blocks(2 * total);
-    if (2 * total + 2 * blocks * kCopyThreads * kCopyUnroll >= (int64_t(1) << 32) ||
+    if (2 * total + int64_t(kCopyThreads) * kCopyUnroll >= (int64_t(1) << 32) ||
         int64_t(num_pages) * page16 >= (int64_t(1) << 62))
       return fail(WF_EUNSUPPORTED, "wf_gather_paged: %lld bytes per tensor too large",
                   static_cast<long long>(total * 16));
-    const dim3 grid(static_cast<unsigned>(blocks));
+    const int64_t per_block = kCopyThreads * kCopyUnroll;
+    const dim3 grid(unsigned((2 * total + per_block - 1) / per_block));
     gather_paged_kernel<<<grid, kCopyThreads, 0, stream>>>(
         static_cast<const uint4*>(k_pool), static_cast<const uint4*>(v_pool), page_ids,
         static_cast<uint4*>(k_dst), static_cast<uint4*>(v_dst), uint32_t(valid16),
