@@ -237,7 +237,9 @@ wf_status wf_gather_paged(const void* k_pool, const void* v_pool, const int32_t*
                           int32_t D, int32_t num_pages, int32_t P, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
-/* wf_attn_tick — all S+1 query chunks of one tick in a single launch.        */
+/* wf_attn_tick — all S+1 query chunks of one tick in a single launch (a     */
+/* tick with more (stage, head) groups than one launch's work plan packs runs */
+/* as a few launches over head ranges, in stream order on the same stream).   */
 /* For each active stage s and head h:                                        */
 /*   O_s = softmax(scale * Q_s K_ctx(s)^T) V_ctx(s), where ctx(s) is, in the  */
 /*   Eq. (5) order: history chunks c = hist_first[s] .. n_hist-1 (read through */
