@@ -950,7 +950,8 @@ attn_tick_kernel(const AttnParams p) {
       // P = 2^(c s - m_run) (bf16 for the P.V product) and this lane's fp32 sum
       float lsum;
       auto exps = [&]() __attribute__((always_inline)) {
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        // -0 + x is x exactly, so the first additions fold away
+        float part[4] = {-0.f, -0.f, -0.f, -0.f};
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -962,7 +963,9 @@ attn_tick_kernel(const AttnParams p) {
               part[i] += ev[i];
             }
             if constexpr (kV8) {  // e4m3 P (at most 2^kLazyTau, inside the range)
-              int w = __builtin_amdgcn_cvt_pk_fp8_f32(ev[0], ev[1], 0, false);
+              // (the first conversion's high half, taken from ev[0]'s register
+              // rather than a zeroed one, is replaced by the second)
+              int w = __builtin_amdgcn_cvt_pk_fp8_f32(ev[0], ev[1], __float_as_int(ev[0]), false);
               pb8[4 * blk + x / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(ev[2], ev[3], w, true);
             } else {
 #pragma unroll
