@@ -870,21 +870,31 @@ attn_tick_kernel(const AttnParams p) {
     float ks_next = 1.f;  // 8-bit tier: key scale of the tile whose scores are in sacc
 
     // 8-bit K operand op = 2*dh + blk of K tile buffer kbuf: rows of 32-key block
-    // blk, head dims 64*dh + 32*g .. +31 (two 16-byte reads).
-    auto kload8 = [&](uint32_t kl, int kbuf, int op) __attribute__((always_inline)) {
-      const uint32_t a = (kl ^ uint32_t((4 * (op >> 1)) << 4)) + kbuf * KTILE_BYTES +
-                         (op & 1) * (32 * D);
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(k_bytes + a);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(k_bytes + (a ^ 16u));
+    // blk, head dims 64*dh + 32*g .. +31 (two 16-byte reads). The swizzled
+    // chunk (dh, piece) sits at the lane base XOR ((4*dh + piece) << 4) plus
+    // the buffer's and block's offsets, multiples of 32 that leave the XORed
+    // bits alone: kb holds the four XORed bases (formed once per tile) and
+    // every read is a base plus an immediate offset.
+    struct KBase8 {
+      uint32_t b[2][2];  // [dh][piece]
+    };
+    auto kbase8 = [&](uint32_t kl) __attribute__((always_inline)) {
+      return KBase8{{{kl, kl ^ 16u}, {kl ^ 64u, kl ^ 80u}}};
+    };
+    auto kload8 = [&](const KBase8& kb, int kbuf, int op) __attribute__((always_inline)) {
+      const uint32_t c = kbuf * KTILE_BYTES + (op & 1) * (32 * D);
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(k_bytes + (kb.b[op >> 1][0] + c));
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(k_bytes + (kb.b[op >> 1][1] + c));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     // 8-bit V^T operand of 32-channel block db of V tile buffer vbuf: row
     // 32*db + r of the transposed tile, bytes 32*g .. +31 (two 16-byte reads;
-    // vl: this lane's base)
-    auto vload8 = [&](uint32_t vl, int vbuf, int db) __attribute__((always_inline)) {
-      const uint32_t a = vl + vbuf * uint32_t(KT * D * VB) + db * (32 * 64);
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(v_bytes + a);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(v_bytes + (a ^ 16u));
+    // vl: this lane's base, vl16 = vl ^ 16 the second chunk's, the offsets
+    // again multiples of 32)
+    auto vload8 = [&](uint32_t vl, uint32_t vl16, int vbuf, int db) __attribute__((always_inline)) {
+      const uint32_t c = vbuf * uint32_t(KT * D * VB) + db * (32 * 64);
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(v_bytes + (vl + c));
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(v_bytes + (vl16 + c));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto mfma8 = [&](const i32x8& a, const i32x8& b, const f32x16& c)
@@ -903,8 +913,9 @@ attn_tick_kernel(const AttnParams p) {
         sacc[0] = f32x16{};
         sacc[1] = f32x16{};
         i32x8 ka[4];
+        const KBase8 kb = kbase8(kl);
 #pragma unroll
-        for (int op = 0; op < 4; ++op) ka[op] = kload8(kl, kbuf, op);
+        for (int op = 0; op < 4; ++op) ka[op] = kload8(kb, kbuf, op);
 #pragma unroll
         for (int op = 0; op < 4; ++op) sacc[op & 1] = mfma8(ka[op], qf8[op >> 1], sacc[op & 1]);
       } else {
@@ -1043,12 +1054,13 @@ attn_tick_kernel(const AttnParams p) {
         bf16x8 va[2][DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) va[0][db] = vpre[db];
-        ka[0] = kload8(kl, kbuf, 0);
-        ka[1] = kload8(kl, kbuf, 1);
+        const KBase8 kb = kbase8(kl);
+        ka[0] = kload8(kb, kbuf, 0);
+        ka[1] = kload8(kb, kbuf, 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          if (t + 2 < 4) ka[(t + 2) % 3] = kload8(kl, kbuf, t + 2);
+          if (t + 2 < 4) ka[(t + 2) % 3] = kload8(kb, kbuf, t + 2);
           if (t + 1 < 4) vload(vl, vbuf, t + 1, va[(t + 1) & 1]);
 #pragma unroll
           for (int db = 0; db < DB; ++db)
@@ -1168,10 +1180,12 @@ attn_tick_kernel(const AttnParams p) {
           const float ks = tile_scale[jj];
           const int ve = tile_vexp[jj];
           i32x8 ka[4], va[4];
+          const KBase8 kb = kbase8(kl);
+          const uint32_t vl16 = vl ^ 16u;
 #pragma unroll
-          for (int op = 0; op < 4; ++op) ka[op] = kload8(kl, kbuf, op);
+          for (int op = 0; op < 4; ++op) ka[op] = kload8(kb, kbuf, op);
 #pragma unroll
-          for (int db = 0; db < DB; ++db) va[db] = vload8(vl, vbuf, db);
+          for (int db = 0; db < DB; ++db) va[db] = vload8(vl, vl16, vbuf, db);
           sn[0] = f32x16{};
           sn[1] = f32x16{};
 #pragma unroll
@@ -1189,8 +1203,9 @@ attn_tick_kernel(const AttnParams p) {
         asm volatile("" : "+v"(kl));
         s0[0] = f32x16{};
         s0[1] = f32x16{};
+        const KBase8 kb = kbase8(kl);
 #pragma unroll
-        for (int op = 0; op < 4; ++op) s0[op & 1] = mfma8(kload8(kl, 0, op), qf8[op >> 1], s0[op & 1]);
+        for (int op = 0; op < 4; ++op) s0[op & 1] = mfma8(kload8(kb, 0, op), qf8[op >> 1], s0[op & 1]);
       }
       for (int j = 0; j < ntiles; j += 4) {
         step(j, 1, 0, k_lds3, v_lds3, s0, s1);
