@@ -48,3 +48,32 @@ def test_noalloc_two_calls_second_smaller():
         say(f"  bit-identical to wf_attn_tick with a workspace; worst rel-L2 vs oracle {worst:.2e}")
         del t, ws, o_na, o_ws
         torch.cuda.empty_cache()
+
+
+def test_noalloc_head_split_tick():
+    """A tick that runs as two launches over head ranges (240 (stage, head)
+    groups), each with its own pool in the same array: bit for bit equal to
+    wf_attn_tick with a caller workspace of the same size, and within the
+    parity bar of the oracle on sampled rows."""
+    S, T, H, P, n_hist = 5, 1460, 40, 64, 2
+    say(f"no-alloc head split: S={S} T={T} H={H} P={P} n_hist={n_hist}")
+    t = setup_tick(S, T, H, 128, P, n_hist, (n_hist + 2) * -(-T // P) + 8, seed=47)
+    full = wfattn.workspace_bytes(S, t.active_mask, T, H, 128, n_hist, None, P, t.num_pages)
+    nb = min(full, wfattn.NOALLOC_SCRATCH_BYTES)
+    ws = torch.empty(nb, dtype=torch.uint8, device=t.q.device)
+    d = wfattn.make_tick_desc(S, t.active_mask, T, H, 128, t.scale, t.q, t.k, t.v, t.o,
+                              t.k_pool, t.v_pool, t.num_pages, P, t.hist_pages, n_hist,
+                              None, workspace=ws)
+    order = wfattn.tick_work_order(d, 0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert len(set(order[order[:, 0] >= 0, 0].tolist())) > cus   # more than one launch
+    assert int(np.sum(order[:, 0] == -1)) > 0
+    o_na = torch.full_like(t.q, float("nan"))
+    wfattn.wf_attn_tick_noalloc(t.q, t.k, t.v, o_na, S, t.active_mask, t.scale, t.k_pool,
+                                t.v_pool, t.hist_pages, scratch_bytes=nb)
+    torch.cuda.synchronize()
+    o_ws = run_tick(t, o=torch.full_like(t.q, float("nan")), workspace=ws)
+    assert torch.equal(o_na.view(torch.int16), o_ws.view(torch.int16))
+    rows = sample_rows(T, seed=5)
+    worst = compare(o_na, oracle_tick(t, rows=rows), rows=rows, label="no-alloc head split")
+    say(f"  bit-identical to wf_attn_tick with a workspace; worst rel-L2 vs oracle {worst:.2e}")
