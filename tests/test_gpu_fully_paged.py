@@ -69,6 +69,29 @@ def test_paged_live_equals_contiguous_and_oracle(S, T, H, D, P, n_hist, mask):
     say(f"  bit-identical to the contiguous launch; worst rel-L2 vs oracle {worst:.2e}")
 
 
+def test_paged_live_head_split_equals_contiguous():
+    """240 (stage, head) groups: both launches run as launches over head ranges;
+    reading the live chunks through pages gives the bits of reading them from
+    k and v (whose parity against the oracle the attention tests check)."""
+    S, T, H, D, P, n_hist = 5, 1460, 40, 128, 64, 2
+    mask = (1 << (S + 1)) - 1
+    say(f"fully paged, head split: S={S} T={T} H={H} n_hist={n_hist}")
+    ppc = -(-T // P)
+    num_pages = (n_hist + S + 2) * ppc + 3
+    order = np.random.default_rng(T + H).permutation(num_pages).astype(np.int32)
+    t = setup_tick(S, T, H, D, P, n_hist, num_pages, seed=S * 100 + T + H, order=order)
+    live = np.stack([order[(n_hist + j) * ppc:(n_hist + j + 1) * ppc] for j in range(S + 1)])
+    for j in range(S + 1):
+        wfattn.wf_store_paged(t.k[j], t.v[j], t.k_pool, t.v_pool, torch.from_numpy(live[j]).to(DEV))
+    o_contig = run_tick(t).clone()
+    o_paged = torch.full_like(t.q, float("nan"))
+    wfattn.wf_attn_tick(t.q, None, None, o_paged, S, mask, t.scale, t.k_pool, t.v_pool,
+                        t.hist_pages, t.hist_first, live_pages=torch.from_numpy(live).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o_paged.view(torch.int16), o_contig.view(torch.int16))
+    say("  bit-identical to the contiguous launch")
+
+
 def test_fully_paged_rollout_with_anchor():
     """12 ticks from an empty history, S = 4, T = 4680 (3 x 30 x 52 latent grid),
     12 heads x 128, window 3 with the anchor pinned; pre-rotation K and V drawn
