@@ -74,98 +74,6 @@ __device__ __forceinline__ int v8_column(int t) {
   return 32 * ((t >> 3) & 1) + 16 * ((t >> 5) & 1) + 8 * ((t >> 4) & 1) + (t & 7);
 }
 
-// 8-bit values. Block (x = chunk * tiles + 64-token tile in page order, y =
-// head, z = 0): the tile's keys of head h -> codes and scale; z = 1: its
-// values of head h -> codes in the transposed tile and the exponent. One thread owns UPT 16-byte units
-// (8 channels of one token), all loaded before any store; bf16 values are
-// copied before the block's amax reduction. Chunk c reads its sources at
-// c * T * H * D and its page ids at c * ppc.
-template <int D>
-__global__ __launch_bounds__(kQThreads) void store_fp8_v8_kernel(
-    const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint8_t* __restrict__ k_pool,
-    float* __restrict__ k_scale, uint4* __restrict__ v_pool, uint8_t* __restrict__ v_exp,
-    const int32_t* __restrict__ page_ids, int32_t T, int32_t H, int32_t P, int32_t tiles,
-    int32_t ppc) {
-  constexpr int UPR = D / 8;                             // 16-byte units per head row
-  constexpr int UPT = kScaleTile * UPR / kQThreads;      // units per thread
-  static_assert(UPT * kQThreads == kScaleTile * UPR, "tile must split evenly");
-  const int chunk = int(blockIdx.x) / tiles;
-  const int tile = int(blockIdx.x) - chunk * tiles;
-  const int h = blockIdx.y;
-  const bool is_v = blockIdx.z != 0;
-  const int spp = P / kScaleTile;
-  const int pg = tile / spp;
-  const int sub = tile - pg * spp;
-  const int64_t pid = page_ids[int64_t(chunk) * ppc + pg];
-  const int tok0 = tile * kScaleTile;
-  k_src += int64_t(chunk) * T * H * UPR;
-  v_src += int64_t(chunk) * T * H * UPR;
-
-  uint4 x[UPT];
-  int64_t dst_row[UPT];
-  float am = 0.f;
-#pragma unroll
-  for (int u = 0; u < UPT; ++u) {
-    const int e = threadIdx.x + u * kQThreads;
-    const int tok = e / UPR;
-    const int c = e - tok * UPR;
-    const int t = tok0 + tok;
-    const int64_t src = (int64_t(t) * H + h) * UPR + c;
-    x[u] = t < T ? load_stream16((is_v ? v_src : k_src) + src) : make_uint4(0u, 0u, 0u, 0u);
-    dst_row[u] = ((pid * P + sub * kScaleTile + tok) * H + h) * UPR + c;  // in 16-byte units
-  }
-#pragma unroll
-  for (int u = 0; u < UPT; ++u) {
-    const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) am = fmaxf(am, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
-  }
-  // block max: within each wave, then across the four waves
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-  __shared__ float wave_max[kQThreads / 64];
-  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = am;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kQThreads / 64; ++i) am = fmaxf(am, wave_max[i]);
-
-  if (is_v) {  // values: power-of-two scale, transposed tile
-    __shared__ __attribute__((aligned(16))) uint8_t tile_t[D * kScaleTile];
-    const int e = pow2_exponent(am);
-    const float mul = __uint_as_float(uint32_t(127 - e) << 23);  // 2^-e (exact)
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = threadIdx.x + u * kQThreads;
-      const int col = v8_column(unit / UPR);
-      const int d0 = (unit % UPR) * 8;
-      const uint32_t codes[2] = {e4m3x4(x[u].x, x[u].y, mul), e4m3x4(x[u].z, x[u].w, mul)};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        tile_t[(d0 + i) * kScaleTile + col] = uint8_t(codes[i >> 2] >> (8 * (i & 3)));
-    }
-    __syncthreads();
-    const int64_t tile16 = ((pid * spp + sub) * H + h) * int64_t(D * kScaleTile / 16);
-    for (int i = threadIdx.x; i < D * kScaleTile / 16; i += kQThreads)
-      store_stream16(v_pool + tile16 + i, reinterpret_cast<const uint4*>(tile_t)[i]);
-    if (threadIdx.x == 0) v_exp[(pid * spp + sub) * H + h] = uint8_t(e + 127);
-    return;
-  }
-  // a tile with amax below kTinyAmax is stored as zero (scale 0, zero codes):
-  // 448 / amax would leave float32's range, or amax / 448 its normal range
-  const bool big = am >= kTinyAmax;
-  const float inv = big ? kE4m3Max / am : 0.f;
-  if (threadIdx.x == 0) k_scale[(pid * spp + sub) * H + h] = big ? am / kE4m3Max : 0.f;
-
-  typedef unsigned v2u __attribute__((ext_vector_type(2)));
-#pragma unroll
-  for (int u = 0; u < UPT; ++u) {
-    const v2u codes = {e4m3x4(x[u].x, x[u].y, inv), e4m3x4(x[u].z, x[u].w, inv)};
-    // unit (16 bytes of bf16) -> 8 bytes of codes at half the offset
-    __builtin_nontemporal_store(codes, reinterpret_cast<v2u*>(k_pool + dst_row[u] * 8));
-  }
-}
-
-
 // bf16 values (v_exp NULL): a persistent grid. Each block walks units (chunk,
 // tile, head) a grid-stride apart, the next unit's loads in flight while the
 // current one is reduced and written; the grid is sized so that every block
@@ -261,6 +169,113 @@ __global__ __launch_bounds__(kQThreads) void store_fp8_stream_kernel(
     unit = u2;
   }
 }
+
+// 8-bit values (v_exp set): block b handles unit b = (chunk, 64-token tile,
+// head), head fastest, keys and values both: one reduction pass gives both
+// maxima; the key codes and scale go out as in store_fp8_stream_kernel, the
+// values as a power-of-two scale and codes written through a transposed LDS
+// tile. One thread owns UPT 16-byte units (8 channels of one token) of each
+// tensor, all loaded before any store. (One unit per block, keys and values
+// together, measured 56.0 -> 41.7 us for a 4-step tick's five live chunks,
+// against one block per unit and tensor; a persistent grid with the next
+// unit's loads in flight needs twice the registers and was slower.)
+template <int D>
+__global__ __launch_bounds__(kQThreads) void store_fp8_v8_kernel(
+    const uint4* __restrict__ k_src, const uint4* __restrict__ v_src, uint8_t* __restrict__ k_pool,
+    float* __restrict__ k_scale, uint4* __restrict__ v_pool, uint8_t* __restrict__ v_exp,
+    const int32_t* __restrict__ page_ids, int32_t T, int32_t H, int32_t P, int32_t tiles,
+    int32_t ppc) {
+  constexpr int UPR = D / 8;                             // 16-byte units per head row
+  constexpr int UPT = kScaleTile * UPR / kQThreads;      // units per thread
+  static_assert(UPT * kQThreads == kScaleTile * UPR, "tile must split evenly");
+  const int spp = P / kScaleTile;
+  const int unit = blockIdx.x;
+  const int h = unit % H;
+  const int ct = unit / H;
+  const int chunk = ct / tiles;
+  const int tile = ct - chunk * tiles;
+  const int pg = tile / spp;
+  const int sub = tile - pg * spp;
+  const int tok0 = tile * kScaleTile;
+  const uint4* ks = k_src + int64_t(chunk) * T * H * UPR;
+  const uint4* vs = v_src + int64_t(chunk) * T * H * UPR;
+  uint4 x[UPT], vx[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int e = threadIdx.x + u * kQThreads;
+    const int tok = e / UPR;
+    const int t = tok0 + tok;
+    const int64_t src = (int64_t(t) * H + h) * UPR + (e - tok * UPR);
+    x[u] = t < T ? load_stream16(ks + src) : make_uint4(0u, 0u, 0u, 0u);
+    vx[u] = t < T ? load_stream16(vs + src) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const int64_t pid = page_ids[int64_t(chunk) * ppc + pg];
+  float am = 0.f, vm = 0.f;
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const uint32_t w[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+    const uint32_t wv[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      am = fmaxf(am, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+      vm = fmaxf(vm, fmaxf(fabsf(bf16_lo(wv[i])), fabsf(bf16_hi(wv[i]))));
+    }
+  }
+  // block maxima: within each wave, then across the four waves
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    am = fmaxf(am, __shfl_xor(am, off));
+    vm = fmaxf(vm, __shfl_xor(vm, off));
+  }
+  __shared__ float wave_max[2][kQThreads / 64];  // [K, V][wave]
+  __shared__ __attribute__((aligned(16))) uint8_t tile_t[D * kScaleTile];
+  if ((threadIdx.x & 63) == 0) {
+    wave_max[0][threadIdx.x >> 6] = am;
+    wave_max[1][threadIdx.x >> 6] = vm;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kQThreads / 64; ++i) {
+    am = fmaxf(am, wave_max[0][i]);
+    vm = fmaxf(vm, wave_max[1][i]);
+  }
+  // values: power-of-two scale, codes into the transposed tile
+  const int ev = pow2_exponent(vm);
+  const float mul = __uint_as_float(uint32_t(127 - ev) << 23);  // 2^-e (exact)
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int e = threadIdx.x + u * kQThreads;
+    const int col = v8_column(e / UPR);
+    const int d0 = (e % UPR) * 8;
+    const uint32_t codes[2] = {e4m3x4(vx[u].x, vx[u].y, mul), e4m3x4(vx[u].z, vx[u].w, mul)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      tile_t[(d0 + i) * kScaleTile + col] = uint8_t(codes[i >> 2] >> (8 * (i & 3)));
+  }
+  // keys: a tile with amax below kTinyAmax is stored as zero (scale 0, zero
+  // codes): 448 / amax would leave float32's range, or amax / 448 its normal range
+  const bool big = am >= kTinyAmax;
+  const float inv = big ? kE4m3Max / am : 0.f;
+  if (threadIdx.x == 0) {
+    k_scale[(pid * spp + sub) * H + h] = big ? am / kE4m3Max : 0.f;
+    v_exp[(pid * spp + sub) * H + h] = uint8_t(ev + 127);
+  }
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int e = threadIdx.x + u * kQThreads;
+    const int tok = e / UPR;
+    const int64_t row = ((pid * P + sub * kScaleTile + tok) * H + h) * UPR + (e - tok * UPR);
+    const v2u codes = {e4m3x4(x[u].x, x[u].y, inv), e4m3x4(x[u].z, x[u].w, inv)};
+    // unit (16 bytes of bf16) -> 8 bytes of codes at half the offset
+    __builtin_nontemporal_store(codes, reinterpret_cast<v2u*>(k_pool + row * 8));
+  }
+  __syncthreads();
+  const int64_t tile16 = ((pid * spp + sub) * H + h) * int64_t(D * kScaleTile / 16);
+#pragma unroll
+  for (int i = threadIdx.x; i < D * kScaleTile / 16; i += kQThreads)
+    store_stream16(v_pool + tile16 + i, reinterpret_cast<const uint4*>(tile_t)[i]);
+}
 }  // namespace
 }  // namespace wf
 
@@ -318,14 +333,18 @@ int32_t store_fp8(const char* where, const void* k_src, const void* v_src, int32
           int32_t(tiles), int32_t(ppc), int32_t(n_units));
     return check_launch(where);
   }
-  const dim3 grid(unsigned(int64_t(n_chunks) * tiles), unsigned(H), 2);
+  // 8-bit values: one block per (chunk, tile, head)
+  const int64_t n_units = int64_t(n_chunks) * tiles * H;
+  if (n_units > 0x7fffffff)
+    return fail(WF_EUNSUPPORTED, "%s: %lld (tile, head) units exceed 2^31", where,
+                static_cast<long long>(n_units));
   if (D == 128)
-    store_fp8_v8_kernel<128><<<grid, kQThreads, 0, stream>>>(
+    store_fp8_v8_kernel<128><<<unsigned(n_units), kQThreads, 0, stream>>>(
         static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
         static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), v_exp, page_ids, T,
         H, P, int32_t(tiles), int32_t(ppc));
   else
-    store_fp8_v8_kernel<64><<<grid, kQThreads, 0, stream>>>(
+    store_fp8_v8_kernel<64><<<unsigned(n_units), kQThreads, 0, stream>>>(
         static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src),
         static_cast<uint8_t*>(k_pool), k_scale, static_cast<uint4*>(v_pool), v_exp, page_ids, T,
         H, P, int32_t(tiles), int32_t(ppc));
