@@ -232,3 +232,34 @@ def test_constant_values_give_constant_output():
     kp, vp = t.k_pool.clone(), torch.full_like(t.v_pool, c)
     o = run_tick(t, v=v, v_pool=vp, k_pool=kp)
     assert torch.allclose(o.float(), torch.full_like(o.float(), c), atol=2e-3)
+
+
+def _random_ticks(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        S = int(rng.integers(0, 8))
+        mask = int(rng.integers(1, 1 << (S + 1)))
+        T = int(rng.choice([33, 96, 300, 700]))
+        H = int(rng.choice([1, 2, 3]))
+        D = int(rng.choice([64, 128]))
+        P = int(rng.choice([16, 64, 128]))
+        n_hist = int(rng.integers(0, 4))
+        hf = None
+        if n_hist and rng.random() < 0.4:
+            hf = [int(rng.integers(0, n_hist + 1)) for _ in range(S + 1)]
+        out.append((S, mask, T, H, D, P, n_hist, hf))
+    return out
+
+
+@pytest.mark.parametrize("S,mask,T,H,D,P,n_hist,hf", _random_ticks(8, 31))
+def test_random_ticks_parity(S, mask, T, H, D, P, n_hist, hf):
+    """Seeded random tick shapes (masks, history budgets, page sizes, head
+    dims), each with the workspace the library asks for: every active (stage,
+    head) against the oracle, every row written."""
+    say(f"random tick: S={S} mask={mask:b} T={T} H={H} D={D} P={P} n_hist={n_hist} hf={hf}")
+    t = setup_tick(S, T, H, D, P, n_hist, (n_hist + 2) * -(-T // P) + 8, seed=S + T + H + D,
+                   active_mask=mask, hist_first=hf)
+    o = run_tick(t, workspace=workspace_for(t))
+    worst = compare(o, oracle_tick(t), label="random tick")
+    say(f"  worst rel-L2 {worst:.2e}")

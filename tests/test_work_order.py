@@ -285,3 +285,62 @@ def test_pool_takes_ragged_last_tiles_without_tail_items():
     assert len(pool) >= 3
     assert np.all(pool[:3, 4] == 1280) and np.all(pool[:3, 5] == 180)
     assert sorted(pool[:3, 3].tolist()) == [0, 1, 2]
+
+
+def _random_shapes(n, seed, large=False):
+    """Seeded tick shapes across the planner's regimes: packed lists, tail
+    items, head splits, plain order, fill/drain masks, history budgets."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        S = int(rng.integers(3 if large else 0, 8))
+        mask = int(rng.integers(1, 1 << (S + 1)))
+        if large and rng.random() < 0.6:
+            mask = (1 << (S + 1)) - 1
+        T = int(rng.choice([1460, 2048, 4680] if large else
+                           [1, 64, 96, 200, 256, 300, 700, 1024, 1460, 2048, 4680]))
+        H = int(rng.choice([12, 24, 40] if large else [1, 2, 3, 12, 24, 40]))
+        n_hist = int(rng.integers(0, 4))
+        if n_hist + S + 1 > 32:
+            n_hist = 0
+        hf = None
+        if n_hist and rng.random() < 0.3:
+            hf = [int(rng.integers(0, n_hist + 1)) for _ in range(S + 1)]
+        out.append((S, mask, T, H, n_hist, hf))
+    return out
+
+
+@pytest.mark.parametrize("S,mask,T,H,n_hist,hf",
+                         _random_shapes(40, 2026) + _random_shapes(40, 7, large=True))
+def test_random_shapes_every_row_once(S, mask, T, H, n_hist, hf):
+    """Every row of every active (slot, head) exactly once, with and without a
+    workspace; launches over head ranges cover disjoint, contiguous ranges."""
+    for ws in (False, True):
+        d = desc(S, mask, T, H, n_hist, hf)
+        if ws:
+            d = with_workspace(d)
+            if d.workspace_bytes == 0:
+                continue
+        order = wf.tick_work_order(d, 32)
+        cover = {(s, h): np.zeros(T, np.int32) for s in range(S + 1) if (mask >> s) & 1
+                 for h in range(H)}
+        for blk, item, s, h, q0, n in order:
+            assert (int(s), int(h)) in cover, (s, h)
+            assert 0 <= q0 and n > 0 and q0 + n <= T
+            cover[(int(s), int(h))][q0:q0 + n] += 1
+        for key, c in cover.items():
+            assert np.all(c == 1), (key, ws, int(c.min()), int(c.max()))
+        listed = order[order[:, 0] >= 0]
+        assert np.all(np.diff(listed[:, 0]) >= 0)
+        assert np.all(order[len(listed):, 0] == -1)
+        n_blocks = int(listed[:, 0].max()) + 1 if len(listed) else 0
+        if n_blocks > 256 and n_blocks % 256 == 0 and len(set(listed[:, 0].tolist())) == n_blocks:
+            # packed launches of one block per CU: each covers a contiguous head range
+            ranges = []
+            for launch in range(n_blocks // 256):
+                rows = listed[(listed[:, 0] >= 256 * launch) & (listed[:, 0] < 256 * (launch + 1))]
+                heads = sorted(set(rows[:, 3].tolist()))
+                assert heads == list(range(heads[0], heads[0] + len(heads)))
+                ranges.append(heads)
+            flat = [h for r in ranges for h in r]
+            assert flat == sorted(flat) and len(flat) == len(set(flat))
