@@ -1839,19 +1839,19 @@ void plan_part(const wf_tick_desc& d, const StagePlan& pl, int C, int64_t ws_byt
 // dispatcher between blocks and idle at the end. A tick of a few items per CU
 // loses little that way and stays one launch. Returns (h0, hp) per launch.
 std::vector<std::array<int, 2>> head_parts(const wf_tick_desc& d, const StagePlan& pl, int C,
-                                           int64_t ws_bytes, AttnParams& scratch) {
+                                           int64_t ws_bytes, AttnParams& trial) {
   int64_t blocks = 0;
-  plan_part(d, pl, C, ws_bytes, 0, d.H, scratch, blocks);
-  if (scratch.use_xcd == 2 || C <= 0 || blocks < int64_t(kMinSplitItems) * kNumXcd * C)
+  plan_part(d, pl, C, ws_bytes, 0, d.H, trial, blocks);
+  if (trial.use_xcd == 2 || C <= 0 || blocks < int64_t(kMinSplitItems) * kNumXcd * C)
     return {{0, d.H}};
   for (int n = 2; n <= kMaxHeadParts && n <= d.H; ++n) {
     const int hp = (d.H + n - 1) / n;
     const int last = d.H - (n - 1) * hp;
     if (last <= 0) continue;
-    plan_part(d, pl, C, ws_bytes, 0, hp, scratch, blocks);
-    if (scratch.use_xcd != 2) continue;
-    plan_part(d, pl, C, ws_bytes, 0, last, scratch, blocks);
-    if (scratch.use_xcd != 2) continue;
+    plan_part(d, pl, C, ws_bytes, 0, hp, trial, blocks);
+    if (trial.use_xcd != 2) continue;
+    plan_part(d, pl, C, ws_bytes, 0, last, trial, blocks);
+    if (trial.use_xcd != 2) continue;
     std::vector<std::array<int, 2>> parts;
     for (int i = 0; i < n; ++i) parts.push_back({i * hp, i + 1 < n ? hp : last});
     return parts;
@@ -2035,8 +2035,8 @@ extern "C" wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_pe
     const int64_t ws_bytes = d.workspace ? d.workspace_bytes : 0;
     AttnParams p;
     plan_base(d, p);
-    AttnParams scratch = p;
-    const auto parts = head_parts(d, pl, C, ws_bytes, scratch);
+    AttnParams trial = p;
+    const auto parts = head_parts(d, pl, C, ws_bytes, trial);
     // launches in order, their blocks numbered on; then every launch's pool items
     std::vector<int> out_rows, pool_rows;
     int64_t block0 = 0;
@@ -2202,8 +2202,8 @@ int32_t attn_tick_impl(const wf_tick_desc* desc, void* ws, int64_t ws_bytes, hip
     const int64_t pool_bytes = ws ? ws_bytes : 0;
     p.ws = static_cast<uint32_t*>(ws);
     const int n_store_blocks = p.n_store_blocks;
-    AttnParams scratch = p;
-    const auto parts = head_parts(d, pl, C, pool_bytes, scratch);
+    AttnParams trial = p;
+    const auto parts = head_parts(d, pl, C, pool_bytes, trial);
     for (size_t i = 0; i < parts.size(); ++i) {  // launches in stream order, one per head range
       int64_t blocks = 0;
       plan_part(d, pl, C, pool_bytes, parts[i][0], parts[i][1], p, blocks);
@@ -2268,8 +2268,8 @@ extern "C" wf_status wf_tick_workspace_bytes(const wf_tick_desc* desc, int64_t* 
     const int64_t unlimited = int64_t(1) << 60;
     AttnParams p;
     plan_base(*desc, p);
-    AttnParams scratch = p;
-    for (const auto& part : head_parts(*desc, pl, C, unlimited, scratch)) {
+    AttnParams trial = p;
+    for (const auto& part : head_parts(*desc, pl, C, unlimited, trial)) {
       int64_t blocks = 0;
       plan_part(*desc, pl, C, unlimited, part[0], part[1], p, blocks);
       if (p.pool_items > 0)
