@@ -95,6 +95,68 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+PEAK_CLOCK_MHZ = 2400.0     # the clock the MFMA peaks are quoted at
+
+
+def power_window(step, seconds: float = 1.5) -> dict:
+    """Socket power and GFX clocks while `step` (one tick) runs back to back
+    for `seconds`: the amdsmi GPU metrics table (the first GPU it lists, the
+    only one on a one-GPU machine), read every 0.1 s after the first 0.4 s.
+    Reading it changes nothing on the GPU. Returns the medians over the
+    samples (per XCD for the clocks), or an error note where the library or
+    the metrics are not available."""
+    import threading
+
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # no amdsmi, no driver access: report, do not fail the bench
+        return {"error": f"amdsmi unavailable: {str(e)[:160]}"}
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        time.sleep(0.4)
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            except Exception:
+                break
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 100 <= c <= 5000]
+            pw = m.get("current_socket_power")
+            if isinstance(pw, (int, float)) and clks:
+                samples.append((float(pw), clks))
+            time.sleep(0.1)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    ticks = 0
+    while time.perf_counter() - t0 < seconds:
+        step()
+        ticks += 1
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return {"error": "no power or clock samples from the GPU metrics table"}
+    n_xcd = min(len(c) for _, c in samples)
+    per_xcd = [float(np.median([c[i] for _, c in samples])) for i in range(n_xcd)]
+    return {"source": "amdsmi GPU metrics, sampled while the tick ran back to back",
+            "ticks": ticks, "samples": len(samples),
+            "socket_power_w": float(np.median([p for p, _ in samples])),
+            "gfx_clk_mhz_per_xcd": per_xcd,
+            "gfx_clk_mhz_mean": round(float(np.mean(per_xcd)), 1)}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -903,6 +965,11 @@ def main():
             log(f"{name}: {extra['configs'][name]}")
         extra["rollout120"] = rollout120(dev)
         log(f"rollout120: {extra['rollout120']}")
+    # the power and clocks the chip holds under this tick (the MFMA peaks are
+    # quoted at 2.4 GHz; under sustained MFMA load the board's power limit sets
+    # the clock)
+    power = power_window(ro.step)
+    log(f"power: {power}")
     mask = (1 << (cfg.S + 1)) - 1
     flops = wfattn.wf_tick_useful_flops(cfg.S, mask, cfg.T, cfg.H, cfg.D, cfg.n_hist, P=cfg.P,
                                         num_pages=cfg.num_pages)
@@ -960,6 +1027,11 @@ def main():
                      "kernel": "wf_attn_tick",
                      "kernel_ms_mean": round(float(attn_ms.mean()), 4)},
     }
+    if "gfx_clk_mhz_mean" in power:  # the fraction of the peak at the clock held
+        held = PEAK_BF16_TFLOPS * power["gfx_clk_mhz_mean"] / PEAK_CLOCK_MHZ
+        power["bf16_peak_at_held_clock_tflops"] = round(held, 1)
+        power["frac_of_peak_at_held_clock"] = round(achieved / held, 4)
+    out["power"] = power
     out.update(extra)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
