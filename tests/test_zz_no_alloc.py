@@ -77,3 +77,48 @@ def test_noalloc_head_split_tick():
     rows = sample_rows(T, seed=5)
     worst = compare(o_na, oracle_tick(t, rows=rows), rows=rows, label="no-alloc head split")
     say(f"  bit-identical to wf_attn_tick with a workspace; worst rel-L2 vs oracle {worst:.2e}")
+
+
+def test_noalloc_replays_in_a_graph():
+    """The allocation-free call captured in a HIP graph and replayed, with the
+    program's own eager work (poisoned outputs, a tick of another shape through
+    the same array) and synchronisations between replays: every replay equal
+    bit for bit to the eager call, which equals wf_attn_tick with a caller
+    workspace of the same size."""
+    S, T, H, P, n_hist = 4, 1100, 4, 64, 3
+    say(f"no-alloc graph: S={S} T={T} H={H} P={P} n_hist={n_hist}")
+    t = setup_tick(S, T, H, 128, P, n_hist, (n_hist + 2) * -(-T // P) + 8, seed=48)
+    full = wfattn.workspace_bytes(S, t.active_mask, T, H, 128, n_hist, None, P, t.num_pages)
+    nb = min(full, wfattn.NOALLOC_SCRATCH_BYTES)
+    assert nb > 0
+    o = torch.full_like(t.q, float("nan"))
+
+    def launch():
+        wfattn.wf_attn_tick_noalloc(t.q, t.k, t.v, o, S, t.active_mask, t.scale, t.k_pool,
+                                    t.v_pool, t.hist_pages, scratch_bytes=nb)
+
+    launch()  # eager: takes the array's address and plans the launch before the capture
+    torch.cuda.synchronize()
+    o_ref = o.clone()
+    ws = torch.empty(nb, dtype=torch.uint8, device=t.q.device)
+    o_ws = run_tick(t, o=torch.full_like(t.q, float("nan")), workspace=ws)
+    assert torch.equal(o_ref.view(torch.int16), o_ws.view(torch.int16))
+    other = setup_tick(2, 600, 2, 128, 64, 1, 3 * 10 + 8, seed=49)
+    o_other = torch.full_like(other.q, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    torch.cuda.synchronize()
+    for r in range(4):
+        o.fill_(float("nan"))
+        # another tick through the same array between replays (its counters and
+        # states are left there; the replay must clear what it needs)
+        wfattn.wf_attn_tick_noalloc(other.q, other.k, other.v, o_other, other.S,
+                                    other.active_mask, other.scale, other.k_pool, other.v_pool,
+                                    other.hist_pages, scratch_bytes=wfattn.NOALLOC_SCRATCH_BYTES)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), f"replay {r}"
+    say("  4 replays bit-identical to the eager call")
+    del g
