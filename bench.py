@@ -351,6 +351,13 @@ def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> d
     store_warm = timed(lambda i: wfattn.wf_store_paged(ksrc[0], vsrc[0], kp, vp, ids[0]))
     gather_cold = timed(lambda i: wfattn.wf_gather_paged(kp, vp, ids[i % rotation].view(1, ppc),
                                                          kd, vd))
+    # a tick's S+1 chunks out of their pages in one launch (page sets rotated)
+    n = cfg.S + 1
+    ids_n = [torch.stack([ids[(i * n + c) % rotation] for c in range(n)]) for i in range(rotation)]
+    kd_n = torch.empty((n, T, H, D), dtype=torch.bfloat16, device=dev)
+    vd_n = torch.empty_like(kd_n)
+    gather_n = graph_time_ms(lambda i: wfattn.wf_gather_paged(kp, vp, ids_n[i % rotation], kd_n, vd_n),
+                             rotation, launches // 4)
     nbytes = 2 * (T * H * D * 2) + 2 * (ppc * P * H * D * 2)   # read K,V + write whole pages
     gbytes = 4 * (T * H * D * 2)   # read the K,V tokens from their pages + write them
     # a copy of nbytes / 2 bytes moves nbytes (read + write)
@@ -370,7 +377,12 @@ def store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> d
             "copy_same_bytes_gb_per_s": rate(nbytes, copy_cold),
             "gather": {"kernel": "wf_gather_paged", "us_mean": round(gather_cold * 1e3, 2),
                        "bytes": gbytes, "gb_per_s": rate(gbytes, gather_cold),
-                       "frac_hbm_peak": round(rate(gbytes, gather_cold) / PEAK_HBM_GBS, 4)}}
+                       "frac_hbm_peak": round(rate(gbytes, gather_cold) / PEAK_HBM_GBS, 4),
+                       "tick_chunks": {
+                           "kernel": f"wf_gather_paged ({n} chunks, one launch)",
+                           "us_mean": round(gather_n * 1e3, 2), "bytes": n * gbytes,
+                           "gb_per_s": rate(n * gbytes, gather_n),
+                           "frac_hbm_peak": round(rate(n * gbytes, gather_n) / PEAK_HBM_GBS, 4)}}}
 
 
 def rope_store_bandwidth(cfg, dev, launches: int = 96, rotation: int = ROTATION) -> dict:
