@@ -98,17 +98,21 @@ def log(msg: str) -> None:
 PEAK_CLOCK_MHZ = 2400.0     # the clock the MFMA peaks are quoted at
 
 
-def power_window(step, seconds: float = 1.5) -> dict:
+def power_window(step, seconds: float = 1.5, sync=None) -> dict:
     """Socket power and GFX clocks while `step` (one tick) runs back to back
     for `seconds`: the amdsmi GPU metrics table (the first GPU it lists, the
     only one on a one-GPU machine), read every 0.1 s after the first 0.4 s.
     Reading it changes nothing on the GPU. Returns the medians over the
-    samples (per XCD for the clocks), or an error note where the library or
-    the metrics are not available."""
+    samples (per XCD for the clocks; entries outside 100-5000 MHz, which the
+    table uses for absent XCDs, are dropped), or an error note where the
+    library or the metrics are not available. `sync` waits for the device
+    (torch.cuda.synchronize unless given)."""
     import threading
 
-    import torch
+    if sync is None:
+        import torch
 
+        sync = torch.cuda.synchronize
     try:
         import amdsmi
 
@@ -139,7 +143,7 @@ def power_window(step, seconds: float = 1.5) -> dict:
     while time.perf_counter() - t0 < seconds:
         step()
         ticks += 1
-    torch.cuda.synchronize()
+    sync()
     stop.set()
     th.join()
     try:

@@ -53,3 +53,44 @@ def test_rollout_driver_fill_masks_match_the_oracle():
     for S in (2, 4, 5):
         for t in range(3 * S):
             assert bench.active_slots(t, S) == oracle.active_mask_for_tick(t, S), (S, t)
+
+
+def test_power_window_medians_and_fallbacks(monkeypatch):
+    """Power and clock summary from a stand-in metrics library: medians over
+    the samples, per XCD, invalid clock entries dropped; a missing library or
+    an empty table gives an error note instead of failing the bench."""
+    import types
+
+    readings = iter([(1390, [1700, 1800, 65535]), (1380, [1720, 1760, 65535]),
+                     (1400, [1710, 1790, 65535])] + [(1395, [1705, 1795, 65535])] * 100)
+    fake = types.SimpleNamespace(
+        amdsmi_init=lambda: None,
+        amdsmi_get_processor_handles=lambda: ["gpu0"],
+        amdsmi_get_gpu_metrics_info=lambda h: dict(zip(("current_socket_power", "current_gfxclks"),
+                                                       next(readings))),
+        amdsmi_shut_down=lambda: None)
+    monkeypatch.setitem(sys.modules, "amdsmi", fake)
+    import time
+    ticks = []
+
+    def step():
+        ticks.append(1)
+        time.sleep(0.001)
+    r = bench.power_window(step, seconds=0.8, sync=lambda: None)
+    assert r["samples"] >= 2 and r["ticks"] == len(ticks) > 0
+    assert len(r["gfx_clk_mhz_per_xcd"]) == 2           # the 65535 placeholder dropped
+    assert 1380 <= r["socket_power_w"] <= 1400
+    assert 1700 <= r["gfx_clk_mhz_per_xcd"][0] <= 1720 and 1760 <= r["gfx_clk_mhz_per_xcd"][1] <= 1800
+    assert r["gfx_clk_mhz_mean"] == pytest.approx(sum(r["gfx_clk_mhz_per_xcd"]) / 2, abs=0.1)
+
+    def broken_init():
+        raise RuntimeError("driver not loaded")
+    monkeypatch.setitem(sys.modules, "amdsmi", types.SimpleNamespace(amdsmi_init=broken_init))
+    assert "error" in bench.power_window(lambda: None, seconds=0.1, sync=lambda: None)
+
+    empty = types.SimpleNamespace(
+        amdsmi_init=lambda: None, amdsmi_get_processor_handles=lambda: ["gpu0"],
+        amdsmi_get_gpu_metrics_info=lambda h: {"current_socket_power": "N/A"},
+        amdsmi_shut_down=lambda: None)
+    monkeypatch.setitem(sys.modules, "amdsmi", empty)
+    assert "error" in bench.power_window(lambda: None, seconds=0.6, sync=lambda: None)
