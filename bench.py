@@ -960,27 +960,37 @@ def main():
     # load rather than while it is still rising from idle (ticks right after an
     # idle GPU run up to 25 % slower for the first ~25 ticks).
     extra = {}
-    extra["store"] = store_bandwidth(cfg, dev)
-    log(f"store: {extra['store']}")
-    extra["separate_store_step"] = separate_store_step(cfg, dev)
-    log(f"separate store: {extra['separate_store_step']}")
-    extra["rope_store"] = rope_store_bandwidth(cfg, dev)
-    log(f"rope store: {extra['rope_store']}")
-    extra["fully_paged"] = fully_paged(cfg, dev)
-    log(f"fully paged: {extra['fully_paged']}")
-    extra["fp8_tier"] = fp8_tier(cfg, dev)
-    log(f"fp8 tier: {extra['fp8_tier']}")
-    extra["fp8kv_tier"] = fp8_tier(cfg, dev, v8=True)
-    log(f"fp8 K/V tier: {extra['fp8kv_tier']}")
-    extra["store_fp8"] = store_fp8_bandwidth(cfg, dev)
-    log(f"fp8 store: {extra['store_fp8']}")
+
+    def section(key, fn, *args):
+        """A secondary measurement; a Python-level failure there is recorded
+        in its place rather than costing the run its main line."""
+        try:
+            extra[key] = fn(*args)
+        except Exception as e:  # noqa: BLE001 - reported in the JSON line
+            extra[key] = {"error": f"{type(e).__name__}: {str(e)[:300]}"}
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        log(f"{key}: {extra[key]}")
+
+    section("store", store_bandwidth, cfg, dev)
+    section("separate_store_step", separate_store_step, cfg, dev)
+    section("rope_store", rope_store_bandwidth, cfg, dev)
+    section("fully_paged", fully_paged, cfg, dev)
+    section("fp8_tier", fp8_tier, cfg, dev)
+    section("fp8kv_tier", lambda c, d: fp8_tier(c, d, v8=True), cfg, dev)
+    section("store_fp8", store_fp8_bandwidth, cfg, dev)
     if cfg.name == "wan13_4step":
-        extra["configs"] = {}
+        configs = {}
         for name in ("wan13_5step", "wan14b_4step"):
-            extra["configs"][name] = other_config(name, dev)
-            log(f"{name}: {extra['configs'][name]}")
-        extra["rollout120"] = rollout120(dev)
-        log(f"rollout120: {extra['rollout120']}")
+            try:
+                configs[name] = other_config(name, dev)
+            except Exception as e:  # noqa: BLE001
+                configs[name] = {"error": f"{type(e).__name__}: {str(e)[:300]}"}
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+            log(f"{name}: {configs[name]}")
+        extra["configs"] = configs
+        section("rollout120", rollout120, dev)
     # the power and clocks the chip holds under this tick (the MFMA peaks are
     # quoted at 2.4 GHz; under sustained MFMA load the board's power limit sets
     # the clock)
