@@ -314,14 +314,18 @@ def _random_shapes(n, seed, large=False):
                          _random_shapes(40, 2026) + _random_shapes(40, 7, large=True))
 def test_random_shapes_every_row_once(S, mask, T, H, n_hist, hf):
     """Every row of every active (slot, head) exactly once, with and without a
-    workspace; launches over head ranges cover disjoint, contiguous ranges."""
-    for ws in (False, True):
+    workspace (also one a third of the size asked for, which holds fewer pool
+    items), and for parts with 24 or 38 CUs per XCD; launches over head ranges
+    cover disjoint, contiguous ranges."""
+    for cus, ws in ((32, False), (32, True), (32, "third"), (24, True), (38, False)):
         d = desc(S, mask, T, H, n_hist, hf)
         if ws:
             d = with_workspace(d)
             if d.workspace_bytes == 0:
                 continue
-        order = wf.tick_work_order(d, 32)
+            if ws == "third":
+                d.workspace_bytes = 1024 + (d.workspace_bytes - 1024) // 3
+        order = wf.tick_work_order(d, cus)
         cover = {(s, h): np.zeros(T, np.int32) for s in range(S + 1) if (mask >> s) & 1
                  for h in range(H)}
         for blk, item, s, h, q0, n in order:
@@ -334,7 +338,8 @@ def test_random_shapes_every_row_once(S, mask, T, H, n_hist, hf):
         assert np.all(np.diff(listed[:, 0]) >= 0)
         assert np.all(order[len(listed):, 0] == -1)
         n_blocks = int(listed[:, 0].max()) + 1 if len(listed) else 0
-        if n_blocks > 256 and n_blocks % 256 == 0 and len(set(listed[:, 0].tolist())) == n_blocks:
+        if cus == 32 and n_blocks > 256 and n_blocks % 256 == 0 and \
+                len(set(listed[:, 0].tolist())) == n_blocks:
             # packed launches of one block per CU: each covers a contiguous head range
             ranges = []
             for launch in range(n_blocks // 256):
