@@ -580,6 +580,10 @@ class Fp8Tick:
         self.o = torch.empty_like(self.q)
         self.scale = 1.0 / float(np.sqrt(D))
         self.mask = (1 << (S + 1)) - 1
+        # the run-time pool's workspace, as the bf16 tick takes it
+        nb = wfattn.workspace_bytes(S, self.mask, T, H, D, cfg.n_hist, None, P, cfg.num_pages,
+                                    k8=True, v8=v8)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         torch.cuda.synchronize()
 
     def store_live(self):
@@ -590,7 +594,7 @@ class Fp8Tick:
     def attn(self):
         self.wf.wf_attn_tick(self.q, None, None, self.o, self.cfg.S, self.mask, self.scale,
                              self.k_pool, self.v_pool, self.hist, live_pages=self.live,
-                             k_scale=self.k_scale, v_exp=self.v_exp)
+                             k_scale=self.k_scale, v_exp=self.v_exp, workspace=self.ws)
 
 
 def fp8_tier(cfg, dev, launches: int = 20, warmup: int = 3, v8: bool = False) -> dict:

@@ -317,7 +317,7 @@ typedef struct wf_tick_desc {
                           /* [64] with v_exp                                        */
   const uint8_t* v_exp;   /* device uint8 [num_pages][P/64][H] with WF_V_E4M3       */
   void* workspace;        /* device scratch (256-byte aligned), or NULL. Set, with   */
-                          /* the bf16 kernel and whole-tile sources, part of the    */
+                          /* whole-tile sources (any key format), part of the       */
                           /* work (query tiles of the heaviest slot, cut into one  */
                           /* chunk of keys each) is handed out while the launch    */
                           /* runs to whichever CU is free, and the pieces' partial  */
@@ -381,8 +381,8 @@ wf_status wf_tick_workspace_bytes(const wf_tick_desc* desc, int64_t* bytes);
  * slots' contexts nest (equal history budgets), those tiles of one head are
  * merged into tail items of eight 32-row slices that walk the heaviest such
  * slot's context with the live chunks in descending order, each slice's wave
- * stopping after its own slot's chunks (bf16 keys with whole-tile sources
- * only). Ticks whose plan does not fit the kernel's tables run one item per
+ * stopping after its own slot's chunks (whole-tile sources only, any key
+ * format). Ticks whose plan does not fit the kernel's tables run one item per
  * block instead, whole groups per XCD. Errors as wf_attn_tick's validation;
  * WF_EINVAL for a short out or a NULL n_items. */
 wf_status wf_tick_work_order(const wf_tick_desc* desc, int32_t cus_per_xcd, int32_t* out,

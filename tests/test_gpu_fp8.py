@@ -116,7 +116,14 @@ def test_store_fp8_tiny_tiles(v8):
         assert int(pg.v_exp[5, 0, 1]) == 0 and int(pg.v_exp[7, 0, 0]) == 0   # e = -127
 
 
-def _fp8_tick(S, T, H, P, n_hist, mask, seed, q_gain=1.0):
+def workspace8(S, mask, T, H, P, n_hist, num_pages, v8=False):
+    """The workspace wf_tick_workspace_bytes asks for an 8-bit tick (run-time
+    pool), or None where it takes none."""
+    nb = wfattn.workspace_bytes(S, mask, T, H, 128, n_hist, None, P, num_pages, k8=True, v8=v8)
+    return torch.empty(nb, dtype=torch.uint8, device=DEV) if nb else None
+
+
+def _fp8_tick(S, T, H, P, n_hist, mask, seed, q_gain=1.0, ws=False):
     D = 128
     cfg = inputs.TickConfig("f8", S=S, T=T, H=H, D=D, P=P, n_hist=n_hist, num_pages=1,
                             std=0.5, bf16_inputs=True, page_order="identity", seed=seed)
@@ -149,24 +156,28 @@ def _fp8_tick(S, T, H, P, n_hist, mask, seed, q_gain=1.0):
     q = inputs.to_device_bf16(q_bits, DEV)
     o = torch.full_like(q, float("nan"))
     scale = 1.0 / np.sqrt(D)
+    work = workspace8(S, mask, T, H, P, n_hist, num_pages) if ws else None
     wfattn.wf_attn_tick(q, None, None, o, S, mask, scale, pg.k_pool, pg.v_pool,
                         torch.from_numpy(np.ascontiguousarray(hist)).to(DEV) if n_hist else None,
-                        live_pages=torch.from_numpy(live).to(DEV), k_scale=pg.k_scale)
+                        live_pages=torch.from_numpy(live).to(DEV), k_scale=pg.k_scale,
+                        workspace=work)
     torch.cuda.synchronize()
     return pg, q_bits, hist, live_lists, o, scale
 
 
+@pytest.mark.parametrize("ws", [False, True])   # with a workspace: the run-time pool
 @pytest.mark.parametrize("S,T,H,P,n_hist,mask,q_gain", [
     (4, 200, 2, 64, 2, 0b11111, 1.0),
     (3, 130, 2, 128, 1, 0b1011, 1.0),     # slot 2 inactive, two scale tiles per page
-    (2, 64, 2, 64, 0, 0b111, 1.0),        # no history, one tile per chunk
-    (4, 70, 3, 64, 3, 0b10110, 1.0),      # stages 0 and 3 inactive, ragged tiles
+    (2, 64, 2, 64, 0, 0b111, 1.0),        # no history, one tile per chunk (tail items)
+    (4, 70, 3, 64, 3, 0b10110, 1.0),      # stages 0 and 3 inactive, ragged tiles (tail items)
     (2, 300, 2, 64, 1, 0b111, 4.0),       # peaked softmax: the running max is raised
+    (4, 1100, 4, 64, 3, 0b11111, 1.0),    # 8-chunk walks, 76-row last tiles: lists, tail items, pool
 ])
-def test_fp8_tick_matches_oracle(S, T, H, P, n_hist, mask, q_gain):
-    say(f"fp8 tick S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b} q_gain={q_gain}")
+def test_fp8_tick_matches_oracle(S, T, H, P, n_hist, mask, q_gain, ws):
+    say(f"fp8 tick S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b} q_gain={q_gain} ws={ws}")
     pg, q_bits, hist, live_lists, o, scale = _fp8_tick(S, T, H, P, n_hist, mask,
-                                                       seed=S * 31 + T, q_gain=q_gain)
+                                                       seed=S * 31 + T, q_gain=q_gain, ws=ws)
     for ids in list(hist) + [l for l in live_lists if l is not None]:
         pg.check(list(ids))
     want = ofp8.attention_tick_fp8(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
@@ -209,7 +220,9 @@ def test_fp8_tick_full_size_sampled_rows(name):
     wfattn.wf_attn_tick(q, None, None, o, cfg.S, mask, scale, pg.k_pool, pg.v_pool,
                         torch.from_numpy(np.ascontiguousarray(hist)).to(DEV),
                         live_pages=torch.from_numpy(np.ascontiguousarray(live)).to(DEV),
-                        k_scale=pg.k_scale)
+                        k_scale=pg.k_scale,
+                        workspace=workspace8(cfg.S, mask, cfg.T, cfg.H, cfg.P, cfg.n_hist,
+                                             cfg.num_pages))
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
     rows = sample_rows(cfg.T, seed=8)
@@ -270,7 +283,7 @@ class Fp8KvPages:
             assert np.array_equal(ve[n].astype(np.int64), we + 127), f"page {pid} exponents"
 
 
-def _fp8kv_tick(S, T, H, P, n_hist, mask, seed, q_zero=False):
+def _fp8kv_tick(S, T, H, P, n_hist, mask, seed, q_zero=False, ws=False):
     D = 128
     cfg = inputs.TickConfig("f8kv", S=S, T=T, H=H, D=D, P=P, n_hist=n_hist, num_pages=1,
                             std=0.5, bf16_inputs=True, page_order="identity", seed=seed)
@@ -300,10 +313,11 @@ def _fp8kv_tick(S, T, H, P, n_hist, mask, seed, q_zero=False):
     q = inputs.to_device_bf16(q_bits, DEV)
     o = torch.full_like(q, float("nan"))
     scale = 1.0 / np.sqrt(D)
+    work = workspace8(S, mask, T, H, P, n_hist, num_pages, v8=True) if ws else None
     wfattn.wf_attn_tick(q, None, None, o, S, mask, scale, pg.k_pool, pg.v_pool,
                         torch.from_numpy(np.ascontiguousarray(hist)).to(DEV) if n_hist else None,
                         live_pages=torch.from_numpy(live).to(DEV), k_scale=pg.k_scale,
-                        v_exp=pg.v_exp)
+                        v_exp=pg.v_exp, workspace=work)
     torch.cuda.synchronize()
     return pg, q_bits, hist, live_lists, o, scale
 
@@ -352,28 +366,32 @@ def test_store_fp8kv_matches_oracle_bits(T, H, P):
     pg.check(ids)
 
 
-@pytest.mark.parametrize("S,T,H,P,n_hist,mask", [
-    (4, 200, 2, 64, 2, 0b11111),
-    (3, 130, 2, 128, 1, 0b1011),
+@pytest.mark.parametrize("S,T,H,P,n_hist,mask,ws", [
+    (4, 200, 2, 64, 2, 0b11111, False),
+    (3, 130, 2, 128, 1, 0b1011, False),
+    (4, 1100, 4, 64, 3, 0b11111, True),    # tail items and the run-time pool's merges
 ])
-def test_fp8kv_tick_exact_p(S, T, H, P, n_hist, mask):
+def test_fp8kv_tick_exact_p(S, T, H, P, n_hist, mask, ws):
     """Zero queries make every score 0 and every P exactly 1 (an e4m3 value), so
     the output is the mean of the dequantised values: the bf16 tier's bounds."""
-    say(f"fp8 K/V tick, P = 1: S={S} T={T} H={H} P={P}")
+    say(f"fp8 K/V tick, P = 1: S={S} T={T} H={H} P={P} ws={ws}")
     pg, q_bits, hist, live_lists, o, scale = _fp8kv_tick(S, T, H, P, n_hist, mask, seed=T,
-                                                         q_zero=True)
+                                                         q_zero=True, ws=ws)
     want = ofp8.attention_tick_fp8kv(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
     compare(o, want, label="fp8 K/V, P = 1")
 
 
-@pytest.mark.parametrize("S,T,H,P,n_hist,mask", [
-    (4, 200, 2, 64, 2, 0b11111),
-    (3, 130, 2, 128, 1, 0b1011),
-    (4, 70, 3, 64, 3, 0b10110),
+@pytest.mark.parametrize("S,T,H,P,n_hist,mask,ws", [
+    (4, 200, 2, 64, 2, 0b11111, False),
+    (3, 130, 2, 128, 1, 0b1011, False),
+    (4, 70, 3, 64, 3, 0b10110, False),     # tail items
+    (4, 70, 3, 64, 3, 0b10110, True),
+    (4, 1100, 4, 64, 3, 0b11111, True),    # lists, tail items, the run-time pool
 ])
-def test_fp8kv_tick_within_p_bound(S, T, H, P, n_hist, mask):
-    say(f"fp8 K/V tick S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b}")
-    pg, q_bits, hist, live_lists, o, scale = _fp8kv_tick(S, T, H, P, n_hist, mask, seed=T + 7)
+def test_fp8kv_tick_within_p_bound(S, T, H, P, n_hist, mask, ws):
+    say(f"fp8 K/V tick S={S} T={T} H={H} P={P} n_hist={n_hist} mask={mask:b} ws={ws}")
+    pg, q_bits, hist, live_lists, o, scale = _fp8kv_tick(S, T, H, P, n_hist, mask, seed=T + 7,
+                                                         ws=ws)
     for ids in list(hist) + [l for l in live_lists if l is not None]:
         pg.check(list(ids))
     want = ofp8.attention_tick_fp8kv(q_bits, pg.store, hist.tolist(), live_lists, S, mask, scale)
@@ -406,7 +424,9 @@ def test_fp8kv_tick_full_size_sampled_rows(name):
     wfattn.wf_attn_tick(q, None, None, o, cfg.S, mask, scale, pg.k_pool, pg.v_pool,
                         torch.from_numpy(np.ascontiguousarray(hist)).to(DEV),
                         live_pages=torch.from_numpy(np.ascontiguousarray(live)).to(DEV),
-                        k_scale=pg.k_scale, v_exp=pg.v_exp)
+                        k_scale=pg.k_scale, v_exp=pg.v_exp,
+                        workspace=workspace8(cfg.S, mask, cfg.T, cfg.H, cfg.P, cfg.n_hist,
+                                             cfg.num_pages, v8=True))
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
     rows = sample_rows(cfg.T, seed=9, n_random=8)

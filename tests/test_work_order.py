@@ -261,18 +261,46 @@ def test_pool_follows_workspace_size():
         assert np.array_equal(order, plain)
 
 
-@pytest.mark.parametrize("kw", [dict(P=48), dict(k8=True)])
-def test_no_pool_where_it_does_not_apply(kw):
-    """8-bit keys and pages that are not whole 64-key tiles take no workspace."""
+def test_no_pool_where_it_does_not_apply():
+    """Pages that are not whole 64-key tiles (per-lane page lookups) take no
+    workspace."""
     S, mask, T, H, n_hist = 4, 0b11111, 4680, 12, 3
     d = desc(S, mask, T, H, n_hist)
-    if "P" in kw:
-        d.P = kw["P"]
-    if kw.get("k8"):
+    d.P = 48
+    assert wf.tick_workspace_bytes(d) == 0
+
+
+@pytest.mark.parametrize("v8", [False, True])
+@pytest.mark.parametrize("S,mask,T,H,n_hist", [(4, 0b11111, 4680, 12, 3), (4, 0b11111, 4680, 40, 3),
+                                               (2, 0b111, 300, 2, 1)])
+def test_8bit_ticks_plan_like_bf16(S, mask, T, H, n_hist, v8):
+    """The 8-bit tiers (every chunk through pages) take the same work order as
+    the bf16 tick of the same shape: tail items, the run-time pool with the
+    same workspace, launches over head ranges; every row once."""
+    def d8(ws):
+        d = desc(S, mask, T, H, n_hist)
         d.k_format = wf.K_E4M3
         d.k_scale = FAKE
         d.live_pages = FAKE
-    assert wf.tick_workspace_bytes(d) == 0
+        if v8:
+            d.v_format = wf.V_E4M3
+            d.v_exp = FAKE
+        return with_workspace(d) if ws else d
+    ref = desc(S, mask, T, H, n_hist)
+    ref.live_pages = FAKE
+    for ws in (False, True):
+        d = d8(ws)
+        want = with_workspace(ref) if ws else ref
+        assert d.workspace_bytes == want.workspace_bytes
+        order = wf.tick_work_order(d, 32)
+        assert np.array_equal(order, wf.tick_work_order(want, 32))
+        cover = {(s, h): np.zeros(T, np.int32) for s in range(S + 1) if (mask >> s) & 1
+                 for h in range(H)}
+        for blk, item, s, h, q0, n in order:
+            cover[(int(s), int(h))][q0:q0 + n] += 1
+        assert all(np.all(c == 1) for c in cover.values())
+        assert (int(np.sum(order[:, 0] == -1)) > 0) == (ws and d.workspace_bytes > 0)
+    assert d8(True).workspace_bytes > 0
 
 
 def test_pool_takes_ragged_last_tiles_without_tail_items():

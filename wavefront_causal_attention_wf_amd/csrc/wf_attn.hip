@@ -1173,7 +1173,9 @@ attn_tick_kernel(const AttnParams p) {
         for (int i = 0; i < NI; ++i) ld.emit(i, u, kn, vn, wave);
         resolve();
         __builtin_amdgcn_sched_barrier(0);
-        if (wave_active) {
+        // (a wave of a tail item stops after its own slot's chunks: the tiles
+        // past them are loaded for the other waves only)
+        if (wave_active && j < ntiles_w) {
           uint32_t kl = k_lane, vl = v_lane;
           asm volatile("" : "+v"(kl), "+v"(vl));
           const int jj = j < ntiles ? j : 0;
@@ -1708,11 +1710,11 @@ void plan_tail(const wf_tick_desc& d, const StagePlan& pl, AttnParams& p) {
 // fit, else whole (stage, head) groups dealt to XCDs, else the plain order.
 // Pool items a workspace of `bytes` holds for this tick (each item takes one
 // partial state per chunk of the heaviest slot's walk); 0 where the pool does
-// not apply (8-bit keys, per-lane page lookups, or no workspace).
+// not apply (per-lane page lookups, or no workspace).
 int pool_capacity(const wf_tick_desc& d, const StagePlan& pl, int64_t bytes) {
   const bool paged = d.n_hist > 0 || d.live_pages != nullptr || d.store_pages != nullptr;
   const bool fast = !paged || d.P % KT == 0;
-  if (!fast || d.k_format != WF_K_BF16 || pl.n_active == 0 || bytes <= kWsHeader) return 0;
+  if (!fast || pl.n_active == 0 || bytes <= kWsHeader) return 0;
   const int64_t per_item = pl.nseg[pl.order[0]] * state_bytes(d.D);
   return int(std::min<int64_t>(kMaxPool, (bytes - kWsHeader) / per_item));
 }
@@ -1723,7 +1725,7 @@ void plan_launch_uncached(const wf_tick_desc& d, const StagePlan& pl, int C, int
   p.pool_items = p.pool_pieces = p.pool_nseg = 0;
   const bool paged = d.n_hist > 0 || d.live_pages != nullptr || d.store_pages != nullptr;
   const bool fast = !paged || d.P % KT == 0;
-  if (fast && d.k_format == WF_K_BF16) plan_tail(d, pl, p);
+  if (fast) plan_tail(d, pl, p);
   blocks = int64_t(pl.n_active) * p.items_per_stage;
   // a pool leaves groups with fewer tiles, which can split into more runs
   // than the tables hold: retry with one pool item fewer (the pool takes at

@@ -608,12 +608,17 @@ def tick_workspace_bytes(desc: WfTickDesc) -> int:
 
 def workspace_bytes(S: int, active_mask: int, T: int, H: int, D: int, n_hist: int = 0,
                     hist_first: Optional[Sequence[int]] = None, P: int = 64,
-                    num_pages: int = 0, live_paged: bool = False) -> int:
-    """Workspace bytes wf_attn_tick would use for a bf16 tick of this shape."""
+                    num_pages: int = 0, live_paged: bool = False, k8: bool = False,
+                    v8: bool = False) -> int:
+    """Workspace bytes wf_attn_tick would use for a tick of this shape: bf16
+    keys, or (k8) 8-bit keys, with (v8) 8-bit values too; the 8-bit tiers read
+    every live chunk through pages."""
     fake = 16
+    live_paged = live_paged or k8
     d = make_tick_desc(S, active_mask, T, H, D, 1.0, fake, fake, fake, fake,
                        fake if (n_hist or live_paged) else None, fake if (n_hist or live_paged) else None,
                        max(num_pages, (n_hist + S + 1) * -(-T // P)) if (n_hist or live_paged) else 0,
                        P if (n_hist or live_paged) else 0, fake if n_hist else None, n_hist,
-                       hist_first, fake if live_paged else None)
+                       hist_first, fake if live_paged else None,
+                       k_scale=fake if k8 else None, v_exp=fake if (k8 and v8) else None)
     return tick_workspace_bytes(d)
