@@ -122,3 +122,45 @@ def test_noalloc_replays_in_a_graph():
         assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), f"replay {r}"
     say("  4 replays bit-identical to the eager call")
     del g
+
+
+def test_noalloc_8bit_tick():
+    """An 8-bit K/V tick (every chunk through e4m3 pages; tail items and the
+    run-time pool as the bf16 tick takes them): the allocation-free call bit
+    for bit equal to wf_attn_tick with a caller workspace of the same size."""
+    S, T, H, P, n_hist = 4, 1100, 4, 64, 3
+    D = 128
+    say(f"no-alloc 8-bit K/V: S={S} T={T} H={H} P={P} n_hist={n_hist}")
+    ppc = -(-T // P)
+    num_pages = (n_hist + S + 1) * ppc + 3
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(50)
+    k_pool = torch.zeros((num_pages, P, H, D), dtype=torch.uint8, device=dev)
+    k_scale = torch.zeros((num_pages, P // 64, H), dtype=torch.float32, device=dev)
+    v_pool = torch.zeros((num_pages, P // 64, H, D, 64), dtype=torch.uint8, device=dev)
+    v_exp = torch.zeros((num_pages, P // 64, H), dtype=torch.uint8, device=dev)
+    ids = torch.randperm(num_pages, generator=torch.Generator().manual_seed(51))[
+        :(n_hist + S + 1) * ppc].to(torch.int32).to(dev)
+    hist = ids[:n_hist * ppc].view(n_hist, ppc)
+    live = ids[n_hist * ppc:].view(S + 1, ppc)
+    kv = (torch.randn((n_hist + S + 1, T, H, D), generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+    vv = (torch.randn((n_hist + S + 1, T, H, D), generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+    wfattn.wf_store_paged_fp8_chunks(kv, vv, k_pool, k_scale, v_pool, ids.view(-1, ppc),
+                                     v_exp=v_exp)
+    q = (torch.randn((S + 1, T, H, D), generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+    mask = (1 << (S + 1)) - 1
+    scale = 1.0 / float(np.sqrt(D))
+    nb = wfattn.workspace_bytes(S, mask, T, H, D, n_hist, None, P, num_pages, k8=True, v8=True)
+    assert 0 < nb <= wfattn.NOALLOC_SCRATCH_BYTES
+    o_na = torch.full_like(q, float("nan"))
+    wfattn.wf_attn_tick_noalloc(q, None, None, o_na, S, mask, scale, k_pool, v_pool, hist,
+                                live_pages=live, k_scale=k_scale, v_exp=v_exp, scratch_bytes=nb)
+    torch.cuda.synchronize()
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    o_ws = torch.full_like(q, float("nan"))
+    wfattn.wf_attn_tick(q, None, None, o_ws, S, mask, scale, k_pool, v_pool, hist,
+                        live_pages=live, k_scale=k_scale, v_exp=v_exp, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o_na.float()).all()
+    assert torch.equal(o_na.view(torch.int16), o_ws.view(torch.int16))
+    say("  bit-identical to wf_attn_tick with a workspace")
